@@ -1,0 +1,119 @@
+"""The ring-order fold against the simulator, closed forms and library routines."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.lsq import lsq_grad, shard_grads
+from oracle.reduce import (chunk_mean, chunk_owner, owned_chunk, reduce_scatter_mean,
+                           ring_fold, shard_segments, widen)
+from oracle.ring import chunk_bounds, ring_all_reduce, ring_reduce_scatter
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+@pytest.mark.parametrize("length", [64, 67])
+def test_fold_equals_simulated_ring(n, dtype, length):
+    # Gaussian data: float addition is not associative, so only the exact
+    # order the ring uses reproduces the simulator's bits.
+    rng = np.random.default_rng(7 * n + length)
+    arrays = [rng.standard_normal(length).astype(dtype) * dtype(10.0 ** rng.integers(-3, 3))
+              for _ in range(n)]
+    owned, _ = ring_reduce_scatter(arrays)
+    bounds = chunk_bounds(length, n)
+    for r in range(n):
+        c, vals = owned[r]
+        assert c == owned_chunk(r, n) and chunk_owner(c, n) == r
+        lo, hi = bounds[c]
+        folded = ring_fold([a[lo:hi] for a in arrays], c)
+        assert folded.dtype == dtype
+        assert np.array_equal(folded, vals)
+    full, _, _ = ring_all_reduce(arrays)
+    summed = reduce_scatter_mean(arrays, "f64" if dtype == np.float64 else "f32",
+                                 [(0, length)], -1, average=False)
+    for r in range(n):
+        assert np.array_equal(full[r].astype(summed.dtype), summed)
+
+
+def test_fold_order_is_observable():
+    # The test above bites: a fold that starts at rank 0 instead of rank c
+    # disagrees with the ring on this data.
+    rng = np.random.default_rng(3)
+    n = 8
+    arrays = [rng.standard_normal(4096).astype(np.float32) for _ in range(n)]
+    c = 5
+    ring = ring_fold(arrays, c)
+    plain = arrays[0].copy()
+    for j in range(1, n):
+        plain = arrays[j] + plain
+    assert not np.array_equal(ring, plain)
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+def test_integer_data_mean_is_sum_over_n(n):
+    rng = np.random.default_rng(n)
+    arrays = [rng.integers(-50, 50, size=96).astype(np.float64) for _ in range(n)]
+    got = reduce_scatter_mean(arrays, "f64", [(0, 96)], -1)
+    assert np.array_equal(got, np.sum(np.stack(arrays), axis=0) / n)
+
+
+def test_bf16_widening_matches_torch_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = widen(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+@pytest.mark.parametrize("integer", [True, False])
+def test_equal_shard_identity_least_squares(integer):
+    # "Lab 09", s.2 and "What to implement" item 7: the mean of 8 equal-shard
+    # gradients equals X^T (X w - y) / 64; X is 64 x 32 as in the page's demo.
+    rng = np.random.default_rng(11)
+    if integer:
+        X = rng.integers(-3, 4, size=(64, 32)).astype(np.float64)
+        y = rng.integers(-3, 4, size=64).astype(np.float64)
+        w = rng.integers(-3, 4, size=32).astype(np.float64)
+    else:
+        X, y, w = rng.standard_normal((64, 32)), rng.standard_normal(64), rng.standard_normal(32)
+    full = lsq_grad(X, y, w)
+    shards = shard_grads(X, y, w, 8)
+    mean = reduce_scatter_mean(shards, "f64", [(0, 32)], -1)
+    if integer:
+        assert np.array_equal(mean, full)
+    else:
+        np.testing.assert_allclose(mean, full, rtol=1e-13, atol=1e-14 * np.abs(full).max())
+    # "Common bugs": summing is N times too large, dividing twice N times too small.
+    summed = reduce_scatter_mean(shards, "f64", [(0, 32)], -1, average=False)
+    np.testing.assert_allclose(summed, 8 * full, rtol=1e-12, atol=1e-12)
+    assert not np.allclose(summed, full)
+    twice = mean / 8
+    assert not np.allclose(twice, full)
+
+
+def test_shard_compact_layout_and_divisibility():
+    n = 4
+    buckets = [(40, 24), (0, 40)]  # processing order: the later arena range first
+    rng = np.random.default_rng(5)
+    arrays = [rng.standard_normal(64).astype(np.float32) for _ in range(n)]
+    full = reduce_scatter_mean(arrays, "f32", buckets, -1)
+    for r in range(n):
+        c = owned_chunk(r, n)
+        shard = reduce_scatter_mean(arrays, "f32", buckets, c)
+        segs = shard_segments(buckets, n, c)
+        assert [s[2] for s in segs] == [0, 6]
+        for g, length, cstart in segs:
+            assert np.array_equal(shard[cstart:cstart + length], full[g:g + length])
+        compact_in = [np.concatenate([a[g:g + l] for g, l, _ in segs]) for a in arrays]
+        again = reduce_scatter_mean(compact_in, "f32", buckets, c, compact_inputs=True)
+        assert np.array_equal(again, shard)
+    with pytest.raises(ValueError):
+        reduce_scatter_mean(arrays, "f32", [(0, 62)], 1)  # "Part 2": error out if P % N != 0
+    uneven = reduce_scatter_mean(arrays, "f32", [(0, 62)], 1, uneven=True)
+    assert uneven.shape == (16,)
+
+
+def test_single_rank_is_identity():
+    x = np.random.default_rng(1).standard_normal(33).astype(np.float32)
+    assert np.array_equal(chunk_mean([x], 0), x)

@@ -1,0 +1,190 @@
+"""Norm, clip, AdamW and bf16 rounding of the oracle against library routines,
+closed forms and the invariants the pages state."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.reduce import owned_chunk, shard_segments
+from oracle.step import (Hyper, adamw, bf16_round, bias_corrections, clip_scale,
+                         ddp_step, grad_sqnorm, lr_at, zero1_step)
+
+
+def _torch_bf16_bits(x):
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_rounding_matches_torch_dense_sample():
+    rng = np.random.default_rng(0)
+    bits = [rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)]
+    hi = rng.integers(0, 1 << 16, size=1 << 14, dtype=np.uint32) << np.uint32(16)
+    for low in (0x7FFF, 0x8000, 0x8001, 0x0000, 0xFFFF):  # ties and their neighbours
+        bits.append(hi | np.uint32(low))
+    special = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0x7F7FFFFF, 0x7F800000,
+                        0xFF800000, 0x00000001, 0x00008000, 0x00018000, 0x007FFFFF,
+                        0x80000000, 0x00000000, 0x3F808000, 0x3F818000], dtype=np.uint32)
+    bits.append(special)
+    bits.append(special | np.uint32(0x80000000))
+    x = np.concatenate(bits).view(np.float32)
+    finite_or_inf = ~np.isnan(x)
+    ours, ref = bf16_round(x), _torch_bf16_bits(x)
+    assert np.array_equal(ours[finite_or_inf], ref[finite_or_inf])
+    nan_bits = ours[~finite_or_inf]
+    assert np.all((nan_bits & 0x7F80) == 0x7F80) and np.all(nan_bits & 0x7F)
+    # Tie at the top of the range rounds to an even mantissa: infinity.
+    assert bf16_round(np.array([0x7F7F8000], dtype=np.uint32).view(np.float32))[0] == 0x7F80
+
+
+@pytest.mark.parametrize("a,p", [(0.5, 4096), (-0.25, 1 << 16), (3.0, 10)])
+def test_norm_of_constant_gradient(a, p):
+    g = np.full(p, a, dtype=np.float32)
+    sq = grad_sqnorm(g)
+    assert sq == a * a * p
+    norm = math.sqrt(sq)
+    assert math.isclose(norm, abs(a) * math.sqrt(p), rel_tol=1e-15)
+    assert clip_scale(sq, 2 * norm) == np.float32(1.0)
+    assert clip_scale(sq, norm / 4) == np.float32(0.25)
+    assert clip_scale(sq, 0.0) == np.float32(1.0)
+
+
+def test_norm_extra_partials_and_large_path():
+    rng = np.random.default_rng(2)
+    g = rng.standard_normal(1000).astype(np.float32)
+    whole = grad_sqnorm(g)
+    split = grad_sqnorm(g[:300], extra=[grad_sqnorm(g[300:700]), grad_sqnorm(g[700:])])
+    assert math.isclose(whole, split, rel_tol=1e-15)
+    exact = math.fsum(float(v) * float(v) for v in g)
+    assert whole == exact
+
+
+def test_clip_matches_torch_clip_grad_norm():
+    rng = np.random.default_rng(4)
+    g = (rng.standard_normal(50000) * 0.02).astype(np.float32)
+    for max_norm in (1.0, 0.5, 1e-3):
+        p = torch.nn.Parameter(torch.zeros(g.size, dtype=torch.float64))
+        p.grad = torch.from_numpy(g.astype(np.float64))
+        torch.nn.utils.clip_grad_norm_([p], max_norm)
+        got = clip_scale(grad_sqnorm(g), max_norm)
+        want = (p.grad / torch.from_numpy(g.astype(np.float64))).mean().item()
+        # torch divides by (norm + 1e-6); the oracle has no epsilon.
+        assert math.isclose(float(got), min(want, 1.0), rel_tol=1e-5)
+
+
+def test_adamw_matches_torch_adamw_fp64():
+    rng = np.random.default_rng(8)
+    n, steps = 4096, 10
+    h = Hyper(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=0)
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    p = torch.nn.Parameter(torch.from_numpy(master.astype(np.float64)))
+    opt = torch.optim.AdamW([p], lr=h.lr, betas=(h.beta1, h.beta2), eps=h.eps,
+                            weight_decay=h.weight_decay, foreach=False)
+    for t in range(1, steps + 1):
+        g = (rng.standard_normal(n) * 0.01).astype(np.float32)
+        master, m, v = adamw(master, m, v, g, **h.scalars(t))
+        p.grad = torch.from_numpy(g.astype(np.float64))
+        opt.step()
+    st = opt.state[p]
+    ref_master = p.detach().numpy()
+    np.testing.assert_allclose(master, ref_master, rtol=1e-6, atol=1e-6 * np.abs(ref_master).max())
+    for ours, ref in ((m, st["exp_avg"].numpy()), (v, st["exp_avg_sq"].numpy())):
+        np.testing.assert_allclose(ours, ref, rtol=1e-5, atol=1e-6 * np.sqrt(np.mean(ref ** 2)))
+    # The comparison bites: a sign error in the weight decay is far outside it.
+    bad = master + np.float32(2e-3) * np.float32(0.1) * master * steps
+    assert not np.allclose(bad, ref_master, rtol=1e-6, atol=1e-6 * np.abs(ref_master).max())
+
+
+def test_adamw_zero_gradient_is_pure_decay():
+    rng = np.random.default_rng(9)
+    master = (rng.standard_normal(512) * 0.02).astype(np.float32)
+    m = np.zeros_like(master)
+    v = np.zeros_like(master)
+    x = master.copy()
+    h = Hyper(lr=1e-2, weight_decay=0.1)
+    for t in range(1, 11):
+        x, m, v = adamw(x, m, v, np.zeros_like(x), **h.scalars(t))
+        assert np.all(m == 0) and np.all(v == 0)
+    want = master.astype(np.float64) * (1 - 1e-2 * 0.1) ** 10
+    np.testing.assert_allclose(x, want, rtol=1e-6)
+
+
+def test_adamw_first_step_closed_form():
+    rng = np.random.default_rng(10)
+    g = (rng.standard_normal(4096) * 1e-2).astype(np.float32)
+    master = (rng.standard_normal(4096) * 0.02).astype(np.float32)
+    z = np.zeros_like(master)
+    h = Hyper(lr=1e-3, weight_decay=0.1)
+    new, m, v = adamw(master, z, z, g, **h.scalars(1))
+    gd = g.astype(np.float64)
+    want = master - 1e-3 * (gd / (np.abs(gd) + 1e-8) + 0.1 * master)
+    np.testing.assert_allclose(new, want, rtol=2e-7, atol=1e-9)
+    np.testing.assert_allclose(m, 0.1 * gd, rtol=1e-6)
+    np.testing.assert_allclose(v, 0.05 * gd * gd, rtol=1e-6)
+
+
+def test_host_scalars():
+    bc1, bc2 = bias_corrections(1, 0.9, 0.95)
+    assert bc1 == np.float32(0.1) and bc2 == np.float32(0.05)
+    assert lr_at(1, 1e-4, 10) == np.float32(1e-5)
+    assert lr_at(10, 1e-4, 10) == np.float32(1e-4)
+    assert lr_at(11, 1e-4, 10) == np.float32(1e-4)
+    assert lr_at(3, 1e-3) == np.float32(1e-3)
+
+
+def _init_states(p, n, buckets, master):
+    states = []
+    for r in range(n):
+        segs = shard_segments(buckets, n, owned_chunk(r, n))
+        mm = np.concatenate([master[g:g + l] for g, l, _ in segs])
+        states.append((mm, np.zeros_like(mm), np.zeros_like(mm)))
+    return states
+
+
+@pytest.mark.parametrize("max_norm", [1.0, 0.05])
+def test_zero1_equals_ddp(max_norm):
+    # "Distributed training" (noeira), "Gates": every ZeRO stage matches DDP.
+    # With the norm summed exactly, they match with clipping too.
+    rng = np.random.default_rng(12)
+    n, p = 4, 1024
+    buckets = [(768, 256), (256, 512), (0, 256)]
+    master = (rng.standard_normal(p) * 0.02).astype(np.float32)
+    zstates = _init_states(p, n, buckets, master)
+    dstate = (master.copy(), np.zeros(p, np.float32), np.zeros(p, np.float32))
+    h = Hyper(max_norm=max_norm)
+    for t in range(1, 6):
+        grads = [(rng.standard_normal(p) * 0.01).astype(np.float32) for _ in range(n)]
+        z = zero1_step(grads, "f32", buckets, zstates, h, t)
+        d = ddp_step(grads, "f32", buckets, dstate, h, t)
+        zstates, dstate = z["states"], d["state"]
+        assert z["sqnorm"] == d["sqnorm"] and z["scale"] == d["scale"]
+        assert np.array_equal(z["arena"], d["arena"])
+    if max_norm < 0.1:
+        assert z["scale"] < 1
+
+
+def test_cross_n_identity_on_grid_exact_data():
+    # "A4", "Overview": the same answer on 1 or 4 GPUs.  On data where every
+    # sum is exact (values k * 2^-24, |k| < 2^14) the mean does not depend on
+    # N, so neither do the weights after k steps.
+    rng = np.random.default_rng(13)
+    p, steps = 1 << 12, 3
+    master = (rng.standard_normal(p) * 0.02).astype(np.float32)
+    micro = [[(rng.integers(-(1 << 13), 1 << 13, size=p) * 2.0 ** -24).astype(np.float32)
+              for _ in range(8)] for _ in range(steps)]
+    arenas = {}
+    for n in (1, 2, 4, 8):
+        buckets = [(0, p)]
+        states = _init_states(p, n, buckets, master)
+        for t in range(1, steps + 1):
+            per = 8 // n
+            grads = [np.sum(np.stack(micro[t - 1][r * per:(r + 1) * per]), axis=0)
+                     * np.float32(n / 8) for r in range(n)]
+            out = zero1_step(grads, "f32", buckets, states, Hyper(max_norm=1e-4), t)
+            states = out["states"]
+        arenas[n] = out["arena"]
+        assert out["scale"] < 1
+    for n in (2, 4, 8):
+        assert np.array_equal(arenas[n], arenas[1])
