@@ -1,0 +1,230 @@
+"""Throughput of the ZeRO-1 gradient pipeline on one MI355X.
+
+Default workload: one rank's ZeRO-1 share of a Llama-shaped 7B arena
+(6,738,415,616 parameters) at N = 8 -- rank 0 owns chunk 1, 842,301,952
+parameters.  One step:
+
+  K1 dp_reduce_scatter_mean  sum the 8 incoming bf16 chunks of the shard in
+                             ring order, fp32 mean, fp64 norm pieces
+  K2 dp_grad_sqnorm          global norm over this rank's and the received
+                             peers' pieces -> clip factor (device scalar)
+  K3 zero1_adamw_gather      clip + AdamW on fp32 master/m/v, bf16 weights
+                             written into this rank's full arena
+  AG zero1_all_gather        the 7 received peer bf16 shards into the arena
+
+Everything is resident in HBM before timing starts; every input is seeded
+and synthetic.  Prints one JSON line.  ``--gpus`` above 1 is refused: this
+build runs on one GPU (the ranks are simulated as resident buffers).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def onerank_setup(name, n, rank, device):
+    import torch  # noqa: F401
+
+    import gradient_reduce_zero_amd as grz
+    from workloads import arena, onerank_inputs
+
+    a = arena(name)
+    p = a.numel
+    buckets = grz.whole_arena(p) if name != "gpt2_124m" else grz.plan_buckets(a.numels)
+    chunk = grz.owned_chunk(rank, n)
+    shard = grz.dp_shard_numel(buckets, n, chunk)
+    npieces = grz.dp_piece_count(buckets, n)
+    inp = onerank_inputs(shard, n, rank, npieces, grz.GRZ_PIECE, device=device)
+    pipe = grz.Zero1OneRank(buckets, n, rank, inp["shard_master"], device=device, arena_numel=p)
+    pipe.norm.partials.copy_(inp["partials"])
+    return dict(arena=a, p=p, n=n, rank=rank, chunk=chunk, shard=shard, buckets=buckets,
+                npieces=npieces, inp=inp, pipe=pipe)
+
+
+def bytes_per_owned(n, grad_bytes=2):
+    """Algorithmic HBM bytes per owned parameter, per kernel of one step."""
+    return {
+        "reduce": n * grad_bytes + 4,        # N incoming chunks read, fp32 mean written
+        "adamw": 4 * 4 + 3 * 4 + 2,          # mean+master+m+v read; master+m+v+bf16 written
+        "gather": 2 * (n - 1) * grad_bytes,  # N-1 peer bf16 shards read and written
+    }
+
+
+def cpu_baseline(setup, sample, seed=0):
+    """The CPU oracle on a bounded sample of the same step (reported, not a target)."""
+    import math
+
+    import numpy as np
+    import torch
+
+    from oracle.reduce import chunk_mean, widen
+    from oracle.step import Hyper, adamw, bf16_round, clip_scale, grad_sqnorm
+    from workloads import to_bits
+
+    inp = setup["inp"]
+    n, shard, chunk = setup["n"], setup["shard"], setup["chunk"]
+    lo = (shard // 2) & ~7
+    hi = min(shard, lo + sample)
+    g = [to_bits(t[lo:hi]) for t in inp["incoming"]]
+    w = to_bits(inp["shard_master"][lo:hi])
+    peers = [None if s is None else to_bits(s[lo:hi]) for s in inp["peer_shards"]]
+    partials = to_bits(inp["partials"])
+    npieces_sample = math.ceil((hi - lo) / 4096)
+    z = np.zeros_like(w)
+    t0 = time.perf_counter()
+    mean = chunk_mean([widen(x, "bf16") for x in g], chunk)
+    sq = grad_sqnorm(mean, extra=partials[:npieces_sample * (n - 1)])
+    scale = clip_scale(sq, 1.0)
+    w1, m1, v1 = adamw(w, z, z, mean * scale, **Hyper().scalars(1))
+    arena = np.empty((n, hi - lo), np.uint16)
+    arena[chunk] = bf16_round(w1)
+    for j, s in enumerate(peers):
+        if s is not None:
+            arena[(j + 1) % n] = s
+    dt = time.perf_counter() - t0
+    del torch
+    return dict(value=(hi - lo) / dt, unit="params/s", cores=1, kind="oracle",
+                sample=f"{hi - lo} of the {shard} owned parameters (contiguous, mid-shard): "
+                       f"fold of {n} bf16 chunks, fsum norm with the matching share of peer "
+                       f"pieces, clip, fp32 AdamW, bf16 rounding, arena assembly; "
+                       f"single-threaded NumPy, {dt:.2f} s",
+                seconds=dt)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama_7b",
+                    choices=["llama_7b", "gpt2_1p5b", "gpt2_124m", "char_gpt"])
+    ap.add_argument("--nranks", type=int, default=8)
+    ap.add_argument("--cpu-sample", type=int, default=1 << 23)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the N ranks are "
+              "simulated as resident buffers on that GPU; multi-GPU runs are not part of "
+              "this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gradient_reduce_zero_amd as grz
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"setting up {args.config} one-rank share, N={args.nranks}")
+    setup = onerank_setup(args.config, args.nranks, 0, dev)
+    pipe, inp = setup["pipe"], setup["inp"]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"inputs resident: P={setup['p']}, owned={setup['shard']}, "
+        f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
+
+    t = 1
+    for _ in range(args.warmup):
+        pipe.step(inp["incoming"], inp["peer_shards"], t, stream=stream)
+        t += 1
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    names = ("reduce", "sqnorm", "adamw", "gather")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(stream)
+        pipe.reduce(inp["incoming"], stream)
+        e[1].record(stream)
+        pipe.norm.run(pipe.hyper.max_norm, stream)
+        e[2].record(stream)
+        args_t = grz.adamw_args(**grz.step_scalars(pipe.hyper, t))
+        w, m, v = pipe.state
+        grz.zero1_adamw_gather(w, m, v, pipe.mean, pipe.buckets, pipe.n, pipe.chunk,
+                               pipe.norm.scale, args_t, [pipe.arena], stream=stream)
+        e[3].record(stream)
+        pipe.gather(inp["peer_shards"], stream)
+        e[4].record(stream)
+        t += 1
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    per = {nm: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps
+           for i, nm in enumerate(names)}
+    ms = total_ms / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s); per kernel "
+        + ", ".join(f"{k} {v:.3f} ms" for k, v in per.items()))
+
+    owned, n = setup["shard"], setup["n"]
+    bpo = bytes_per_owned(n)
+    kbytes = {k: owned * v for k, v in bpo.items()}
+    step_bytes = sum(kbytes.values())
+    gbps = {k: kbytes[k] / (per[k] * 1e-3) / 1e9 for k in kbytes}
+    dominant = max(kbytes, key=lambda k: per[k])
+    step_gbps = step_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "params updated/sec + achieved HBM GB/s (% of peak), fused reduce+AdamW step",
+        "value": owned / (ms * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{setup['arena'].name} one-rank ZeRO-1 share",
+            "arena_params": setup["p"], "owned_params": owned, "nranks_simulated": n,
+            "rank": 0, "owned_chunk": setup["chunk"], "buckets": len(setup["buckets"]),
+            "grad_dtype": "bf16", "state_dtype": "fp32", "weights_dtype": "bf16",
+            "clip": 1.0,
+        },
+        "achieved_GBps": step_gbps,
+        "pct_of_peak_hbm": 100.0 * step_gbps / PEAK_HBM_GBPS,
+        "model_params_per_s": setup["p"] / (ms * 1e-3),
+        "step_bytes": step_bytes,
+        "kernels_ms": per,
+        "kernels_GBps": gbps,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dominant,
+            "achieved": gbps[dominant],
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": gbps[dominant] / PEAK_HBM_GBPS,
+            "traffic": None,
+            "bytes_per_owned_param": bpo[dominant],
+        },
+    }
+    if not args.no_cpu:
+        log(f"timing the CPU oracle on {args.cpu_sample} parameters")
+        cb = cpu_baseline(setup, args.cpu_sample)
+        out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

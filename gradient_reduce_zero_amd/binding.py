@@ -1,0 +1,209 @@
+"""Python binding of libgrz: the C entry points under the same names.
+
+Argument marshalling only.  Every function takes torch tensors for device
+memory (PyTorch provides allocation and the current HIP stream), checks that
+each buffer is on the GPU, contiguous and large enough for the plan (the C
+library sees raw pointers and cannot check extents), and calls the C entry
+point, raising ``GrzError`` on a non-zero status.  All arithmetic runs in the
+library's kernels.
+"""
+
+import ctypes
+
+import torch
+
+from . import _native as N
+from ._native import AdamWArgs, Bucket, check, lib
+
+_KIND = {torch.bfloat16: N.GRZ_BF16, torch.int16: N.GRZ_BF16, torch.uint16: N.GRZ_BF16,
+         torch.float32: N.GRZ_F32, torch.float64: N.GRZ_F64}
+_OUT = {N.GRZ_BF16: torch.float32, N.GRZ_F32: torch.float32, N.GRZ_F64: torch.float64}
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtypes=None, numel=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, not {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the plan needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _bucket_array(buckets):
+    buckets = [(int(o), int(l)) for o, l in buckets]
+    arr = (Bucket * max(len(buckets), 1))(*buckets)
+    return arr, len(buckets)
+
+
+def _extent(buckets):
+    return max((o + l for o, l in buckets), default=0)
+
+
+# -- plan helpers ------------------------------------------------------------
+
+def dp_ring_owned_chunk(rank, nranks):
+    return lib().dp_ring_owned_chunk(rank, nranks)
+
+
+def dp_ring_chunk_owner(chunk, nranks):
+    return lib().dp_ring_chunk_owner(chunk, nranks)
+
+
+def dp_chunk_range(length, nranks, chunk):
+    off, cnt = ctypes.c_int64(), ctypes.c_int64()
+    check("dp_chunk_range", lib().dp_chunk_range(length, nranks, chunk, ctypes.byref(off),
+                                                 ctypes.byref(cnt)))
+    return off.value, cnt.value
+
+
+def _neg_check(fn, value):
+    if value < 0:
+        check(fn, -value)
+    return value
+
+
+def dp_piece_count(buckets, nranks, flags=0):
+    arr, nb = _bucket_array(buckets)
+    return _neg_check("dp_piece_count", lib().dp_piece_count(arr, nb, nranks, flags))
+
+
+def dp_piece_offset(buckets, nranks, bucket, chunk, flags=0):
+    arr, nb = _bucket_array(buckets)
+    return _neg_check("dp_piece_offset",
+                      lib().dp_piece_offset(arr, nb, nranks, flags, bucket, chunk))
+
+
+def dp_shard_numel(buckets, nranks, chunk, flags=0):
+    arr, nb = _bucket_array(buckets)
+    return _neg_check("dp_shard_numel", lib().dp_shard_numel(arr, nb, nranks, chunk, flags))
+
+
+def dp_grad_sqnorm_workspace(npieces):
+    return int(lib().dp_grad_sqnorm_workspace(int(npieces)))
+
+
+# -- the pipeline --------------------------------------------------------------
+
+def dp_reduce_scatter_mean(rank_grads, buckets, chunk, mean_out, piece_sqnorm=None, flags=0,
+                           stream=None):
+    """Ring-order reduce-scatter-mean of ``rank_grads`` (one tensor per rank)."""
+    n = len(rank_grads)
+    if not 1 <= n <= N.GRZ_MAX_RANKS:
+        raise ValueError(f"{n} ranks; 1..{N.GRZ_MAX_RANKS} supported")
+    dt = rank_grads[0].dtype
+    if dt not in _KIND:
+        raise TypeError(f"gradient dtype {dt} not supported")
+    kind = _KIND[dt]
+    buckets = list(buckets)
+    if chunk >= 0:
+        shard = dp_shard_numel(buckets, n, chunk, flags & N.GRZ_UNEVEN)
+        need_in = shard if flags & N.GRZ_IN_COMPACT else _extent(buckets)
+        need_out = shard
+    else:
+        need_in = need_out = _extent(buckets)
+    same = _BF16_LIKE if kind == N.GRZ_BF16 else (dt,)
+    ptrs = (ctypes.c_void_p * n)(*[_dev(g, f"rank_grads[{j}]", same, need_in).value
+                                   for j, g in enumerate(rank_grads)])
+    out = _dev(mean_out, "mean_out", (_OUT[kind],), need_out)
+    part = None
+    if piece_sqnorm is not None:
+        part = _dev(piece_sqnorm, "piece_sqnorm", (torch.float64,),
+                    dp_piece_count(buckets, n, flags & N.GRZ_UNEVEN))
+    arr, nb = _bucket_array(buckets)
+    check("dp_reduce_scatter_mean",
+          lib().dp_reduce_scatter_mean(ptrs, n, kind, arr, nb, chunk, flags, out, part,
+                                       _stream(stream)))
+
+
+def dp_grad_sqnorm(piece_sqnorm, max_norm, workspace, sqnorm_out, clip_scale_out,
+                   npieces=None, stream=None):
+    """Fixed-order global squared norm of the piece sums and the clip factor."""
+    npieces = piece_sqnorm.numel() if npieces is None else int(npieces)
+    part = _dev(piece_sqnorm, "piece_sqnorm", (torch.float64,), npieces)
+    need = dp_grad_sqnorm_workspace(npieces)
+    ws = None
+    if need:
+        if workspace is None:
+            raise ValueError(f"dp_grad_sqnorm needs {need} bytes of workspace")
+        ws = _dev(workspace, "workspace")
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
+                             f"bytes, {need} needed")
+    sq = None if sqnorm_out is None else _dev(sqnorm_out, "sqnorm_out", (torch.float64,), 1)
+    sc = None if clip_scale_out is None else _dev(clip_scale_out, "clip_scale_out",
+                                                   (torch.float32,), 1)
+    check("dp_grad_sqnorm", lib().dp_grad_sqnorm(part, npieces, float(max_norm), ws, sq, sc,
+                                                 _stream(stream)))
+
+
+def adamw_args(lr, beta1, beta2, eps, weight_decay, bias_corr1, bias_corr2):
+    return AdamWArgs(lr, beta1, beta2, eps, weight_decay, bias_corr1, bias_corr2)
+
+
+def _state(master, m, v, mean_grad, n):
+    f32 = (torch.float32,)
+    return (_dev(master, "master", f32, n), _dev(m, "m", f32, n), _dev(v, "v", f32, n),
+            _dev(mean_grad, "mean_grad", f32, n))
+
+
+def zero1_adamw_step(master, m, v, mean_grad, clip_scale, args, bf16_out=None, n=None,
+                     stream=None):
+    """Clipped AdamW over ``n`` (default: all) shard-compact elements."""
+    n = master.numel() if n is None else int(n)
+    w, mm, vv, g = _state(master, m, v, mean_grad, n)
+    sc = None if clip_scale is None else _dev(clip_scale, "clip_scale", (torch.float32,), 1)
+    out = None if bf16_out is None else _dev(bf16_out, "bf16_out", _BF16_LIKE, n)
+    check("zero1_adamw_step", lib().zero1_adamw_step(w, mm, vv, g, n, sc, ctypes.byref(args),
+                                                     out, _stream(stream)))
+
+
+def zero1_adamw_gather(master, m, v, mean_grad, buckets, nranks, chunk, clip_scale, args,
+                       replicas, flags=0, stream=None):
+    """Clipped AdamW on the shard of ``chunk`` with the bf16 all-gather write fused in."""
+    buckets = list(buckets)
+    n = dp_shard_numel(buckets, nranks, chunk, flags) if chunk >= 0 else _extent(buckets)
+    w, mm, vv, g = _state(master, m, v, mean_grad, n)
+    sc = None if clip_scale is None else _dev(clip_scale, "clip_scale", (torch.float32,), 1)
+    ext = _extent(buckets)
+    reps = (ctypes.c_void_p * max(len(replicas), 1))(
+        *[_dev(r, f"replicas[{i}]", _BF16_LIKE, ext).value for i, r in enumerate(replicas)])
+    arr, nb = _bucket_array(buckets)
+    check("zero1_adamw_gather",
+          lib().zero1_adamw_gather(w, mm, vv, g, arr, nb, nranks, chunk, flags, sc,
+                                   ctypes.byref(args), reps, len(replicas), _stream(stream)))
+
+
+def zero1_all_gather(shards, buckets, replicas, flags=0, stream=None):
+    """Copy every rank's bf16 shard (``None`` = already in place) into every replica."""
+    buckets = list(buckets)
+    n = len(shards)
+    ext = _extent(buckets)
+    ptrs = []
+    for r, s in enumerate(shards):
+        if s is None:
+            ptrs.append(None)
+        else:
+            need = dp_shard_numel(buckets, n, (r + 1) % n, flags)
+            ptrs.append(_dev(s, f"shards[{r}]", _BF16_LIKE, need).value)
+    sp = (ctypes.c_void_p * max(n, 1))(*ptrs)
+    reps = (ctypes.c_void_p * max(len(replicas), 1))(
+        *[_dev(r, f"replicas[{i}]", _BF16_LIKE, ext).value for i, r in enumerate(replicas)])
+    arr, nb = _bucket_array(buckets)
+    check("zero1_all_gather", lib().zero1_all_gather(sp, n, arr, nb, flags, reps, len(replicas),
+                                                     _stream(stream)))
+
+
+def grz_set_max_blocks(blocks):
+    """Grid width of the grid-stride kernels (speed only; results do not change)."""
+    check("grz_set_max_blocks", lib().grz_set_max_blocks(int(blocks)))

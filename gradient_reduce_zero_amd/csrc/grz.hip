@@ -1,0 +1,829 @@
+// grz.hip -- HIP kernels and C ABI of the data-parallel / ZeRO-1 gradient
+// pipeline for AMD Instinct MI355X (gfx950, CDNA4, wave64).
+//
+// Kernels (all HBM-bandwidth bound; nothing here is a contraction, so no MFMA):
+//   rs_mean_kernel   ring-order N-way fold of 128-bit loads, fp32 (fp64) mean,
+//                    fp64 sum of squares per GRZ_PIECE-element piece
+//   sqnorm_level_kernel / sqnorm_final_kernel
+//                    fixed-shape fp64 tree over the piece sums -> norm, clip
+//   adamw_kernel     clip + AdamW on fp32 master/m/v, bf16 round-to-nearest-
+//                    even written to any number of replica arenas
+//   gather_kernel    bf16 shard copies into replica arenas (all-gather)
+//
+// The ring order of the fold and the chunk ownership follow "Lab 09 --
+// Parallelism, simulated", s.1 "Ring all-reduce" (the N = 3 schedule table)
+// and its "Tips" (reduce-scatter step t: rank r sends chunk (r - t) mod N, so
+// chunk c's partial sum starts at rank c and ends at rank c - 1, its owner).
+// The step order (reduce, clip, AdamW on the shard, all-gather) follows
+// "A4 -- Multi-GPU with NCCL and ZeRO-1", "Part 4 -- Multi-GPU Backward and
+// Update", and "Distributed training" (noeira), "Four strategies, one
+// interface".
+//
+// Build flags this file relies on: -ffp-contract=off (every a*b+c rounds
+// twice, as the fp32 reference does) and -fhip-fp32-correctly-rounded-divide-
+// sqrt (IEEE division and square root).
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "grz.h"
+
+namespace {
+
+constexpr int kThreads = 256;          // 4 waves of 64
+constexpr int kGroup = 8;              // consecutive elements a lane handles at once
+constexpr int kGroupsPerLane = GRZ_PIECE / (kThreads * kGroup);  // 2
+constexpr int kMaxSegs = 64;           // segments per launch (kernel-argument budget)
+constexpr int kReduceFan = 4096;       // values one block folds in the norm tree
+
+static_assert(kGroupsPerLane * kThreads * kGroup == GRZ_PIECE, "piece shape");
+
+int g_max_blocks = 2048;               // grid width of the grid-stride kernels
+
+// One contiguous run of work: `len` elements read at `src` and written at
+// `dst`, whose first tile is `tile0` of the launch and first norm piece is
+// `piece0` of the plan.  `chunk` is the ring chunk (fold start) for the
+// reduce kernel and the source shard for the gather kernel.  `vec` is 1 when
+// every pointer + offset of the run allows 16-byte accesses.
+struct Seg {
+  int64_t src;
+  int64_t dst;
+  int64_t len;
+  int64_t piece0;
+  int64_t tile0;
+  int32_t chunk;
+  int32_t vec;
+};
+
+__device__ __forceinline__ int find_seg(const Seg* seg, int nsegs, int64_t tile) {
+  int lo = 0, hi = nsegs - 1;
+  while (lo < hi) {  // last segment whose tile0 <= tile
+    int mid = (lo + hi + 1) >> 1;
+    if (seg[mid].tile0 <= tile) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Element access.  bf16 values are uint16 bit patterns; widening puts them in
+// the top half of a binary32, which is exact.
+
+template <typename T> struct AccOf { using type = float; };
+template <> struct AccOf<double> { using type = double; };
+
+__device__ __forceinline__ float widen1(const uint16_t* p) {
+  return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+}
+__device__ __forceinline__ float widen1(const float* p) { return *p; }
+__device__ __forceinline__ double widen1(const double* p) { return *p; }
+
+__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[kGroup]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[kGroup]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8(const double* p, double (&x)[kGroup]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double2 d = reinterpret_cast<const double2*>(p)[i];
+    x[2 * i] = d.x;
+    x[2 * i + 1] = d.y;
+  }
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[kGroup]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ void store8(double* p, const double (&x)[kGroup]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    reinterpret_cast<double2*>(p)[i] = make_double2(x[2 * i], x[2 * i + 1]);
+}
+
+// Round-to-nearest-even of a binary32 to bf16: add half an ulp of the kept
+// part (minus one when the kept part is even, so that exact ties go to the
+// even neighbour) and drop the low half.  NaN keeps its sign and becomes the
+// quiet NaN pattern; values that round past the largest finite bf16 carry
+// into the exponent and become infinities.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Sum of one double per thread over the 256-thread block, in a fixed tree:
+// a xor butterfly inside each wave (every lane ends with the same balanced
+// tree sum of its wave) then (w0 + w1) + (w2 + w3).  The shape depends on
+// nothing but the thread index, so the result is reproducible bit for bit.
+__device__ __forceinline__ double block_sum_fixed(double s, double* lds) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) s += __shfl_xor(s, m, 64);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds[wave] = s;
+  __syncthreads();
+  const double r = (lds[0] + lds[1]) + (lds[2] + lds[3]);
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// K1: reduce-scatter-mean.  One tile = one norm piece of GRZ_PIECE elements
+// of one chunk; lane l owns groups l and l + 256 (8 elements each) of it, so
+// every 16-byte load of a wave is one contiguous 1 KiB run.
+
+template <typename TIn>
+struct RsArgs {
+  const TIn* rank[GRZ_MAX_RANKS];
+  typename AccOf<TIn>::type* out;
+  double* partials;
+  int64_t ntiles;
+  int nsegs;
+  int nranks;
+  int average;   // divide the sum by N
+  int pow2;      // N is a power of two: x / N == x * (1 / N) exactly
+  Seg seg[kMaxSegs];
+};
+
+// Fold one group of 8 elements over the ranks in ring order starting at
+// rank c; NR > 0 fixes N at compile time so that every rank's load is in
+// flight before the first add.
+template <typename TIn, int NR>
+__device__ __forceinline__ void fold_vec(const RsArgs<TIn>& a, int c, int64_t off,
+                                         typename AccOf<TIn>::type (&acc)[kGroup]) {
+  using Acc = typename AccOf<TIn>::type;
+  const TIn* const* rank = a.rank;
+  if constexpr (NR > 0) {
+    Acc x[NR][kGroup];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      int r = c + j;
+      r = r >= NR ? r - NR : r;
+      load8(rank[r] + off, x[j]);
+    }
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) acc[k] = x[0][k];
+#pragma unroll
+    for (int j = 1; j < NR; ++j)
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) acc[k] = x[j][k] + acc[k];
+  } else {
+    const int n = a.nranks;
+    load8(rank[c] + off, acc);
+    for (int j = 1; j < n; ++j) {
+      int r = c + j;
+      r = r >= n ? r - n : r;
+      Acc x[kGroup];
+      load8(rank[r] + off, x);
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) acc[k] = x[k] + acc[k];
+    }
+  }
+}
+
+template <typename TIn, int NR>
+__device__ __forceinline__ typename AccOf<TIn>::type fold_one(const RsArgs<TIn>& a, int c,
+                                                              int64_t off) {
+  using Acc = typename AccOf<TIn>::type;
+  const int n = NR > 0 ? NR : a.nranks;
+  Acc acc = widen1(a.rank[c] + off);
+  for (int j = 1; j < n; ++j) {
+    int r = c + j;
+    r = r >= n ? r - n : r;
+    acc = widen1(a.rank[r] + off) + acc;
+  }
+  return acc;
+}
+
+template <typename TIn, int NR>
+__global__ __launch_bounds__(kThreads) void rs_mean_kernel(const RsArgs<TIn> a) {
+  using Acc = typename AccOf<TIn>::type;
+  __shared__ double lds[kThreads / 64];
+  const int n = NR > 0 ? NR : a.nranks;
+  const Acc nf = static_cast<Acc>(n);
+  const Acc inv = static_cast<Acc>(1) / nf;
+  const int lane = threadIdx.x;
+
+  for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const Seg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
+    const int64_t piece = tile - s.tile0;
+    const int64_t e0 = piece * GRZ_PIECE;
+    const int64_t left = s.len - e0;  // > 0
+    const int c = s.chunk;
+    double sq = 0.0;
+#pragma unroll
+    for (int gi = 0; gi < kGroupsPerLane; ++gi) {
+      const int64_t e = e0 + static_cast<int64_t>(gi * kThreads + lane) * kGroup;
+      const int64_t rel = e - e0;
+      if (s.vec && rel + kGroup <= left) {
+        Acc acc[kGroup];
+        fold_vec<TIn, NR>(a, c, s.src + e, acc);
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) {
+          if (a.average) acc[k] = a.pow2 ? acc[k] * inv : acc[k] / nf;
+          sq = __fma_rn(static_cast<double>(acc[k]), static_cast<double>(acc[k]), sq);
+        }
+        store8(a.out + s.dst + e, acc);
+      } else {
+        for (int k = 0; k < kGroup; ++k) {
+          if (rel + k >= left) break;
+          Acc v = fold_one<TIn, NR>(a, c, s.src + e + k);
+          if (a.average) v = a.pow2 ? v * inv : v / nf;
+          sq = __fma_rn(static_cast<double>(v), static_cast<double>(v), sq);
+          a.out[s.dst + e + k] = v;
+        }
+      }
+    }
+    const double tot = block_sum_fixed(sq, lds);
+    if (a.partials != nullptr && lane == 0) a.partials[s.piece0 + piece] = tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2: the fixed-order fp64 tree over piece sums.  Block j of a level folds
+// values [j*4096, (j+1)*4096): lane l adds values l, l+256, ..., l+3840 in
+// that order, then block_sum_fixed.  The tree depends only on the count.
+
+__global__ __launch_bounds__(kThreads) void sqnorm_level_kernel(const double* __restrict__ x,
+                                                                int64_t n,
+                                                                double* __restrict__ y) {
+  __shared__ double lds[kThreads / 64];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kReduceFan;
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < kReduceFan / kThreads; ++k) {
+    const int64_t i = base + k * kThreads + threadIdx.x;
+    if (i < n) s += x[i];
+  }
+  const double tot = block_sum_fixed(s, lds);
+  if (threadIdx.x == 0) y[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(kThreads) void sqnorm_final_kernel(const double* __restrict__ x,
+                                                                int64_t n, double max_norm,
+                                                                double* __restrict__ sqnorm_out,
+                                                                float* __restrict__ scale_out) {
+  __shared__ double lds[kThreads / 64];
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < kReduceFan / kThreads; ++k) {
+    const int64_t i = k * kThreads + threadIdx.x;
+    if (i < n) s += x[i];
+  }
+  const double tot = block_sum_fixed(s, lds);
+  if (threadIdx.x == 0) {
+    float scale = 1.0f;
+    if (max_norm > 0.0) {
+      const double norm = sqrt(tot);
+      if (norm > max_norm) scale = static_cast<float>(max_norm / norm);
+    }
+    if (sqnorm_out != nullptr) *sqnorm_out = tot;
+    if (scale_out != nullptr) *scale_out = scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K3: clip + AdamW over shard-compact fp32 state; the new master is rounded
+// to bf16 and written to every replica at the arena offset of its segment.
+
+struct AdamArgs {
+  float* master;
+  float* m;
+  float* v;
+  const float* grad;
+  const float* scale;   // device scalar or null (1)
+  uint16_t* rep[GRZ_MAX_RANKS];
+  int nrep;
+  int nsegs;
+  int64_t ntiles;
+  float lr, b1, b2, eps, wd, bc1, bc2;
+  Seg seg[kMaxSegs];
+};
+
+// One element, every operation rounded on its own (the file is built with
+// -ffp-contract=off; '/' and sqrtf are the IEEE ones).
+__device__ __forceinline__ void adamw1(float& w, float& m, float& v, float g, float lr,
+                                       float b1, float omb1, float b2, float omb2,
+                                       float eps, float wd, float bc1, float bc2) {
+  m = b1 * m + omb1 * g;
+  v = b2 * v + omb2 * (g * g);
+  const float mh = m / bc1;
+  const float vh = v / bc2;
+  const float u = mh / (__builtin_sqrtf(vh) + eps);
+  w = w - lr * (u + wd * w);
+}
+
+__global__ __launch_bounds__(kThreads) void adamw_kernel(const AdamArgs a) {
+  const float scale = a.scale != nullptr ? *a.scale : 1.0f;
+  const float omb1 = 1.0f - a.b1;  // exact: 1/2 <= b1 <= 1 (Sterbenz)
+  const float omb2 = 1.0f - a.b2;
+  const int lane = threadIdx.x;
+
+  for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const Seg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
+    const int64_t e0 = (tile - s.tile0) * GRZ_PIECE;
+    const int64_t left = s.len - e0;
+#pragma unroll
+    for (int gi = 0; gi < kGroupsPerLane; ++gi) {
+      const int64_t rel = static_cast<int64_t>(gi * kThreads + lane) * kGroup;
+      const int64_t e = e0 + rel;
+      if (s.vec && rel + kGroup <= left) {
+        const int64_t i = s.src + e;
+        float g[kGroup], w[kGroup], m[kGroup], v[kGroup];
+        load8(a.grad + i, g);
+        load8(a.master + i, w);
+        load8(a.m + i, m);
+        load8(a.v + i, v);
+        uint32_t b[kGroup];
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) {
+          adamw1(w[k], m[k], v[k], g[k] * scale, a.lr, a.b1, omb1, a.b2, omb2, a.eps, a.wd,
+                 a.bc1, a.bc2);
+          b[k] = bf16_rne(w[k]);
+        }
+        store8(a.master + i, w);
+        store8(a.m + i, m);
+        store8(a.v + i, v);
+        const uint4 packed = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16),
+                                        b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+        for (int r = 0; r < a.nrep; ++r)
+          *reinterpret_cast<uint4*>(a.rep[r] + s.dst + e) = packed;
+      } else {
+        for (int k = 0; k < kGroup; ++k) {
+          if (rel + k >= left) break;
+          const int64_t i = s.src + e + k;
+          float w = a.master[i], m = a.m[i], v = a.v[i];
+          adamw1(w, m, v, a.grad[i] * scale, a.lr, a.b1, omb1, a.b2, omb2, a.eps, a.wd, a.bc1,
+                 a.bc2);
+          a.master[i] = w;
+          a.m[i] = m;
+          a.v[i] = v;
+          const uint16_t b = static_cast<uint16_t>(bf16_rne(w));
+          for (int r = 0; r < a.nrep; ++r) a.rep[r][s.dst + e + k] = b;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// All-gather: copy shard segments (source shard = Seg::chunk) into replicas.
+
+struct GatherArgs {
+  const uint16_t* shard[GRZ_MAX_RANKS];
+  uint16_t* rep[GRZ_MAX_RANKS];
+  int nrep;
+  int nsegs;
+  int64_t ntiles;
+  Seg seg[kMaxSegs];
+};
+
+__global__ __launch_bounds__(kThreads) void gather_kernel(const GatherArgs a) {
+  const int lane = threadIdx.x;
+  for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const Seg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
+    const int64_t e0 = (tile - s.tile0) * GRZ_PIECE;
+    const int64_t left = s.len - e0;
+    const uint16_t* src = a.shard[s.chunk];
+#pragma unroll
+    for (int gi = 0; gi < kGroupsPerLane; ++gi) {
+      const int64_t rel = static_cast<int64_t>(gi * kThreads + lane) * kGroup;
+      const int64_t e = e0 + rel;
+      if (s.vec && rel + kGroup <= left) {
+        const uint4 u = *reinterpret_cast<const uint4*>(src + s.src + e);
+        for (int r = 0; r < a.nrep; ++r) *reinterpret_cast<uint4*>(a.rep[r] + s.dst + e) = u;
+      } else {
+        for (int k = 0; k < kGroup; ++k) {
+          if (rel + k >= left) break;
+          const uint16_t u = src[s.src + e + k];
+          for (int r = 0; r < a.nrep; ++r) a.rep[r][s.dst + e + k] = u;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: plan geometry, argument checks and launches.
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline void chunk_of(int64_t length, int n, int c, int64_t* off, int64_t* cnt) {
+  const int64_t q = length / n, rem = length % n;
+  *off = c * q + (c < rem ? c : rem);
+  *cnt = q + (c < rem ? 1 : 0);
+}
+
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+int check_plan(const grz_bucket* buckets, int nbuckets, int nranks, int chunk, int flags) {
+  if (nranks < 1 || nranks > GRZ_MAX_RANKS) return GRZ_EINVAL;
+  if (nbuckets < 0 || (nbuckets > 0 && buckets == nullptr)) return GRZ_EINVAL;
+  if (chunk < -1 || chunk >= nranks) return GRZ_EINVAL;
+  if (flags & ~(GRZ_SUM | GRZ_UNEVEN | GRZ_IN_COMPACT)) return GRZ_EINVAL;
+  for (int b = 0; b < nbuckets; ++b) {
+    if (buckets[b].offset < 0 || buckets[b].length < 0) return GRZ_ERANGE;
+    if (buckets[b].length > (INT64_MAX >> 4) - buckets[b].offset) return GRZ_ERANGE;
+    if (chunk >= 0 && !(flags & GRZ_UNEVEN) && buckets[b].length % nranks != 0)
+      return GRZ_EINDIVISIBLE;
+  }
+  return GRZ_OK;
+}
+
+// Segments of a plan: one per (bucket, chunk) processed, in plan order.
+// src/dst are filled for the reduce kernel's view; callers remap them.
+struct PlanSeg {
+  int64_t global;   // arena offset of the chunk
+  int64_t compact;  // shard-compact offset (chunk >= 0) or arena offset
+  int64_t len;
+  int64_t piece0;
+  int chunk;
+};
+
+std::vector<PlanSeg> plan_segments(const grz_bucket* buckets, int nbuckets, int n, int chunk) {
+  std::vector<PlanSeg> out;
+  int64_t piece = 0, compact = 0;
+  for (int b = 0; b < nbuckets; ++b) {
+    for (int c = 0; c < n; ++c) {
+      int64_t off, cnt;
+      chunk_of(buckets[b].length, n, c, &off, &cnt);
+      if (chunk < 0 || c == chunk) {
+        if (cnt > 0) {
+          const int64_t g = buckets[b].offset + off;
+          out.push_back({g, chunk < 0 ? g : compact, cnt, piece, c});
+        }
+        if (chunk >= 0) compact += cnt;
+      }
+      piece += ceil_div(cnt, GRZ_PIECE);
+    }
+  }
+  return out;
+}
+
+template <typename Args>
+int launch_batches(std::vector<Seg>& segs, Args& args,
+                   void (*kernel)(const Args), hipStream_t stream) {
+  (void)hipGetLastError();  // clear a stale error so the check below is ours
+  for (size_t first = 0; first < segs.size(); first += kMaxSegs) {
+    const size_t cnt = segs.size() - first < static_cast<size_t>(kMaxSegs)
+                           ? segs.size() - first : static_cast<size_t>(kMaxSegs);
+    int64_t tiles = 0;
+    for (size_t i = 0; i < cnt; ++i) {
+      args.seg[i] = segs[first + i];
+      args.seg[i].tile0 = tiles;
+      tiles += ceil_div(segs[first + i].len, GRZ_PIECE);
+    }
+    if (tiles == 0) continue;
+    args.nsegs = static_cast<int>(cnt);
+    args.ntiles = tiles;
+    const int64_t grid = tiles < g_max_blocks ? tiles : g_max_blocks;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+                       args);
+    if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
+  }
+  return GRZ_OK;
+}
+
+template <typename TIn, int NR>
+int rs_launch(std::vector<Seg>& segs, RsArgs<TIn>& args, hipStream_t stream) {
+  return launch_batches(segs, args, rs_mean_kernel<TIn, NR>, stream);
+}
+
+template <typename TIn>
+int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>& ps,
+                int flags, void* mean_out, double* partials, hipStream_t stream) {
+  using Acc = typename AccOf<TIn>::type;
+  static RsArgs<TIn> proto;  // zero-initialised template
+  RsArgs<TIn> args = proto;
+  bool vec_base = aligned(mean_out, 16);
+  for (int j = 0; j < n; ++j) {
+    if (!aligned(rank_grads[j], sizeof(TIn))) return GRZ_EALIGN;
+    vec_base = vec_base && aligned(rank_grads[j], 16);
+    args.rank[j] = static_cast<const TIn*>(rank_grads[j]);
+  }
+  args.out = static_cast<Acc*>(mean_out);
+  args.partials = partials;
+  args.nranks = n;
+  args.average = (flags & GRZ_SUM) ? 0 : 1;
+  args.pow2 = (n & (n - 1)) == 0;
+  const bool compact_in = (flags & GRZ_IN_COMPACT) != 0;
+  std::vector<Seg> segs;
+  segs.reserve(ps.size());
+  for (const PlanSeg& p : ps) {
+    Seg s{};
+    s.src = compact_in ? p.compact : p.global;
+    s.dst = p.compact;
+    s.len = p.len;
+    s.piece0 = p.piece0;
+    s.chunk = p.chunk;
+    s.vec = vec_base && (s.src * sizeof(TIn)) % 16 == 0 && (s.dst * sizeof(Acc)) % 16 == 0;
+    segs.push_back(s);
+  }
+  switch (n) {
+    case 1: return rs_launch<TIn, 1>(segs, args, stream);
+    case 2: return rs_launch<TIn, 2>(segs, args, stream);
+    case 4: return rs_launch<TIn, 4>(segs, args, stream);
+    case 8: return rs_launch<TIn, 8>(segs, args, stream);
+    default: return rs_launch<TIn, 0>(segs, args, stream);
+  }
+}
+
+int sqnorm_levels(int64_t n, int64_t* sizes, int max_levels) {
+  int levels = 0;
+  while (n > kReduceFan && levels < max_levels) {
+    n = ceil_div(n, kReduceFan);
+    sizes[levels++] = n;
+  }
+  return levels;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+
+extern "C" {
+
+int grz_version(void) { return 100; }
+
+const char* grz_strerror(int status) {
+  switch (status) {
+    case GRZ_OK: return "ok";
+    case GRZ_EINVAL: return "invalid argument";
+    case GRZ_EINDIVISIBLE: return "can't equally partition parameters: bucket length % N != 0";
+    case GRZ_EALIGN: return "device pointer not aligned to its element size";
+    case GRZ_EHIP: return "HIP launch error";
+    case GRZ_ERANGE: return "bucket or size out of range";
+    default: return "unknown status";
+  }
+}
+
+int grz_set_max_blocks(int blocks) {
+  if (blocks < 1 || blocks > (1 << 20)) return GRZ_EINVAL;
+  g_max_blocks = blocks;
+  return GRZ_OK;
+}
+
+int dp_ring_owned_chunk(int rank, int nranks) {
+  if (nranks < 1 || rank < 0 || rank >= nranks) return -1;
+  return (rank + 1) % nranks;
+}
+
+int dp_ring_chunk_owner(int chunk, int nranks) {
+  if (nranks < 1 || chunk < 0 || chunk >= nranks) return -1;
+  return (chunk + nranks - 1) % nranks;
+}
+
+int dp_chunk_range(int64_t length, int nranks, int chunk, int64_t* offset, int64_t* count) {
+  if (length < 0 || nranks < 1 || chunk < 0 || chunk >= nranks || !offset || !count)
+    return GRZ_EINVAL;
+  chunk_of(length, nranks, chunk, offset, count);
+  return GRZ_OK;
+}
+
+int64_t dp_piece_count(const grz_bucket* buckets, int nbuckets, int nranks, int flags) {
+  const int st = check_plan(buckets, nbuckets, nranks, -1, flags);
+  if (st != GRZ_OK) return -st;
+  int64_t pieces = 0;
+  for (int b = 0; b < nbuckets; ++b)
+    for (int c = 0; c < nranks; ++c) {
+      int64_t off, cnt;
+      chunk_of(buckets[b].length, nranks, c, &off, &cnt);
+      pieces += ceil_div(cnt, GRZ_PIECE);
+    }
+  return pieces;
+}
+
+int64_t dp_piece_offset(const grz_bucket* buckets, int nbuckets, int nranks, int flags,
+                        int bucket, int chunk) {
+  const int st = check_plan(buckets, nbuckets, nranks, -1, flags);
+  if (st != GRZ_OK) return -st;
+  if (bucket < 0 || bucket >= nbuckets || chunk < 0 || chunk >= nranks) return -GRZ_EINVAL;
+  int64_t pieces = 0;
+  for (int b = 0; b < nbuckets; ++b)
+    for (int c = 0; c < nranks; ++c) {
+      if (b == bucket && c == chunk) return pieces;
+      int64_t off, cnt;
+      chunk_of(buckets[b].length, nranks, c, &off, &cnt);
+      pieces += ceil_div(cnt, GRZ_PIECE);
+    }
+  return -GRZ_EINVAL;
+}
+
+int64_t dp_shard_numel(const grz_bucket* buckets, int nbuckets, int nranks, int chunk,
+                       int flags) {
+  if (chunk < 0) return -GRZ_EINVAL;
+  const int st = check_plan(buckets, nbuckets, nranks, chunk, flags);
+  if (st != GRZ_OK) return -st;
+  int64_t total = 0;
+  for (int b = 0; b < nbuckets; ++b) {
+    int64_t off, cnt;
+    chunk_of(buckets[b].length, nranks, chunk, &off, &cnt);
+    total += cnt;
+  }
+  return total;
+}
+
+int dp_reduce_scatter_mean(const void* const* rank_grads, int nranks, int dtype,
+                           const grz_bucket* buckets, int nbuckets, int chunk, int flags,
+                           void* mean_out, double* piece_sqnorm, hipStream_t stream) {
+  int st = check_plan(buckets, nbuckets, nranks, chunk, flags);
+  if (st != GRZ_OK) return st;
+  if (rank_grads == nullptr || mean_out == nullptr) return GRZ_EINVAL;
+  if ((flags & GRZ_IN_COMPACT) && chunk < 0) return GRZ_EINVAL;
+  for (int j = 0; j < nranks; ++j)
+    if (rank_grads[j] == nullptr) return GRZ_EINVAL;
+  if (piece_sqnorm != nullptr && !aligned(piece_sqnorm, 8)) return GRZ_EALIGN;
+  const std::vector<PlanSeg> ps = plan_segments(buckets, nbuckets, nranks, chunk);
+  switch (dtype) {
+    case GRZ_BF16:
+      if (!aligned(mean_out, 4)) return GRZ_EALIGN;
+      return rs_dispatch<uint16_t>(rank_grads, nranks, ps, flags, mean_out, piece_sqnorm,
+                                   stream);
+    case GRZ_F32:
+      if (!aligned(mean_out, 4)) return GRZ_EALIGN;
+      return rs_dispatch<float>(rank_grads, nranks, ps, flags, mean_out, piece_sqnorm, stream);
+    case GRZ_F64:
+      if (!aligned(mean_out, 8)) return GRZ_EALIGN;
+      return rs_dispatch<double>(rank_grads, nranks, ps, flags, mean_out, piece_sqnorm, stream);
+    default:
+      return GRZ_EINVAL;
+  }
+}
+
+size_t dp_grad_sqnorm_workspace(int64_t npieces) {
+  if (npieces <= 0) return 0;
+  int64_t sizes[8];
+  const int levels = sqnorm_levels(npieces, sizes, 8);
+  int64_t total = 0;
+  for (int i = 0; i < levels; ++i) total += sizes[i];
+  return static_cast<size_t>(total) * sizeof(double);
+}
+
+int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
+                   void* workspace, double* sqnorm_out, float* clip_scale_out,
+                   hipStream_t stream) {
+  if (npieces < 0) return GRZ_EINVAL;
+  if (npieces > 0 && piece_sqnorm == nullptr) return GRZ_EINVAL;
+  if (sqnorm_out == nullptr && clip_scale_out == nullptr) return GRZ_EINVAL;
+  if (!aligned(piece_sqnorm, 8) || !aligned(sqnorm_out, 8) || !aligned(clip_scale_out, 4) ||
+      !aligned(workspace, 8))
+    return GRZ_EALIGN;
+  if (npieces > static_cast<int64_t>(kReduceFan) * kReduceFan * kReduceFan) return GRZ_ERANGE;
+  int64_t sizes[8];
+  const int levels = sqnorm_levels(npieces, sizes, 8);
+  if (levels > 0 && workspace == nullptr) return GRZ_EINVAL;
+  (void)hipGetLastError();
+  const double* in = piece_sqnorm;
+  int64_t n = npieces;
+  double* ws = static_cast<double*>(workspace);
+  for (int i = 0; i < levels; ++i) {
+    hipLaunchKernelGGL(sqnorm_level_kernel, dim3(static_cast<unsigned>(sizes[i])),
+                       dim3(kThreads), 0, stream, in, n, ws);
+    if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
+    in = ws;
+    n = sizes[i];
+    ws += sizes[i];
+  }
+  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kThreads), 0, stream, in, n, max_norm,
+                     sqnorm_out, clip_scale_out);
+  if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
+  return GRZ_OK;
+}
+
+static int adamw_common(float* master, float* m, float* v, const float* mean_grad,
+                        const std::vector<PlanSeg>& ps, const float* clip_scale,
+                        const grz_adamw_args* args, uint16_t* const* replicas, int nreplicas,
+                        hipStream_t stream) {
+  if (!master || !m || !v || !mean_grad || !args) return GRZ_EINVAL;
+  if (nreplicas < 0 || nreplicas > GRZ_MAX_RANKS) return GRZ_EINVAL;
+  if (nreplicas > 0 && replicas == nullptr) return GRZ_EINVAL;
+  if (!aligned(master, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(mean_grad, 4) ||
+      !aligned(clip_scale, 4))
+    return GRZ_EALIGN;
+  static AdamArgs proto;
+  AdamArgs a = proto;
+  a.master = master;
+  a.m = m;
+  a.v = v;
+  a.grad = mean_grad;
+  a.scale = clip_scale;
+  bool vec_base = aligned(master, 16) && aligned(m, 16) && aligned(v, 16) &&
+                  aligned(mean_grad, 16);
+  for (int r = 0; r < nreplicas; ++r) {
+    if (replicas[r] == nullptr) return GRZ_EINVAL;
+    if (!aligned(replicas[r], 2)) return GRZ_EALIGN;
+    vec_base = vec_base && aligned(replicas[r], 16);
+    a.rep[r] = replicas[r];
+  }
+  a.nrep = nreplicas;
+  a.lr = args->lr;
+  a.b1 = args->beta1;
+  a.b2 = args->beta2;
+  a.eps = args->eps;
+  a.wd = args->weight_decay;
+  a.bc1 = args->bias_corr1;
+  a.bc2 = args->bias_corr2;
+  std::vector<Seg> segs;
+  segs.reserve(ps.size());
+  for (const PlanSeg& p : ps) {
+    Seg s{};
+    s.src = p.compact;
+    s.dst = p.global;
+    s.len = p.len;
+    s.chunk = p.chunk;
+    s.vec = vec_base && s.src % 4 == 0 && s.dst % 8 == 0;
+    segs.push_back(s);
+  }
+  return launch_batches(segs, a, adamw_kernel, stream);
+}
+
+int zero1_adamw_step(float* master, float* m, float* v, const float* mean_grad, int64_t n,
+                     const float* clip_scale, const grz_adamw_args* args, uint16_t* bf16_out,
+                     hipStream_t stream) {
+  if (n < 0) return GRZ_EINVAL;
+  if (n == 0) return GRZ_OK;
+  std::vector<PlanSeg> ps{{0, 0, n, 0, 0}};
+  uint16_t* reps[1] = {bf16_out};
+  return adamw_common(master, m, v, mean_grad, ps, clip_scale, args, reps,
+                      bf16_out ? 1 : 0, stream);
+}
+
+int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad,
+                       const grz_bucket* buckets, int nbuckets, int nranks, int chunk,
+                       int flags, const float* clip_scale, const grz_adamw_args* args,
+                       uint16_t* const* replicas, int nreplicas, hipStream_t stream) {
+  const int st = check_plan(buckets, nbuckets, nranks, chunk, flags);
+  if (st != GRZ_OK) return st;
+  if (flags & (GRZ_SUM | GRZ_IN_COMPACT)) return GRZ_EINVAL;
+  std::vector<PlanSeg> ps;
+  if (chunk >= 0) {
+    ps = plan_segments(buckets, nbuckets, nranks, chunk);
+  } else {
+    for (int b = 0; b < nbuckets; ++b)
+      if (buckets[b].length > 0)
+        ps.push_back({buckets[b].offset, buckets[b].offset, buckets[b].length, 0, 0});
+  }
+  return adamw_common(master, m, v, mean_grad, ps, clip_scale, args, replicas, nreplicas,
+                      stream);
+}
+
+int zero1_all_gather(const uint16_t* const* shards, int nranks, const grz_bucket* buckets,
+                     int nbuckets, int flags, uint16_t* const* replicas, int nreplicas,
+                     hipStream_t stream) {
+  if (flags & ~GRZ_UNEVEN) return GRZ_EINVAL;
+  if (shards == nullptr) return GRZ_EINVAL;
+  if (nreplicas < 0 || nreplicas > GRZ_MAX_RANKS) return GRZ_EINVAL;
+  if (nreplicas > 0 && replicas == nullptr) return GRZ_EINVAL;
+  for (int r = 0; r < nranks && r < GRZ_MAX_RANKS; ++r) {
+    const int st = check_plan(buckets, nbuckets, nranks, (r + 1) % nranks, flags);
+    if (st != GRZ_OK) return st;
+  }
+  const int st = check_plan(buckets, nbuckets, nranks, -1, flags);
+  if (st != GRZ_OK) return st;
+  static GatherArgs proto;
+  GatherArgs a = proto;
+  bool vec_base = true;
+  for (int r = 0; r < nreplicas; ++r) {
+    if (replicas[r] == nullptr) return GRZ_EINVAL;
+    if (!aligned(replicas[r], 2)) return GRZ_EALIGN;
+    vec_base = vec_base && aligned(replicas[r], 16);
+    a.rep[r] = replicas[r];
+  }
+  a.nrep = nreplicas;
+  if (nreplicas == 0) return GRZ_OK;
+  std::vector<Seg> segs;
+  for (int r = 0; r < nranks; ++r) {
+    a.shard[r] = shards[r];
+    if (shards[r] == nullptr) continue;
+    if (!aligned(shards[r], 2)) return GRZ_EALIGN;
+    const bool vr = vec_base && aligned(shards[r], 16);
+    for (const PlanSeg& p : plan_segments(buckets, nbuckets, nranks, (r + 1) % nranks)) {
+      Seg s{};
+      s.src = p.compact;
+      s.dst = p.global;
+      s.len = p.len;
+      s.chunk = r;
+      s.vec = vr && s.src % 8 == 0 && s.dst % 8 == 0;
+      segs.push_back(s);
+    }
+  }
+  return launch_batches(segs, a, gather_kernel, stream);
+}
+
+}  // extern "C"

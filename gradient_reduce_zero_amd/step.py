@@ -1,0 +1,165 @@
+"""One training step of the gradient pipeline, driven through the C ABI.
+
+Three views of the same step, all on one GPU with the ranks simulated as
+resident buffers ("Distributed training" (noeira), "The process group": the
+simulator runs every rank on one device with the collectives as local
+kernels):
+
+* ``Zero1AllRanks`` -- all N ranks of a ZeRO-1 step: each rank reduces the
+  chunk it owns, the norm is taken over every rank's pieces, each rank runs
+  AdamW on its shard and writes the new bf16 weights into all N replicas.
+* ``DDPStep``       -- plain data parallelism (ZeRO stage 0) as one replica
+  sees it: all-reduce-mean of every chunk, norm, AdamW over the whole arena,
+  bf16 weights into the replica.  Every replica runs the same computation.
+* ``Zero1OneRank``  -- what a single GPU of an N-GPU ZeRO-1 job does: sum the
+  N incoming chunks of its shard, combine its norm pieces with the peers'
+  (received), AdamW on its shard, then assemble its full bf16 arena from its
+  own shard and the peers' received shards.
+
+The step order is "A4 -- Multi-GPU with NCCL and ZeRO-1", "Part 4":
+reduce-scatter, AdamW on the shard, all-gather; with the clip in between as in
+"Distributed training", "Four strategies, one interface".  The host only
+enqueues kernels and fills the per-step scalars; there is no host
+synchronisation inside a step.
+"""
+
+import torch
+
+from . import binding as B
+from ._native import GRZ_IN_COMPACT, GRZ_PIECE
+from .plan import Hyper, owned_chunk, step_scalars
+
+
+def _shard_index(buckets, nranks, chunk, device):
+    """Arena indices of the shard of ``chunk``, in shard-compact order (setup only)."""
+    parts = []
+    for b, (off, length) in enumerate(buckets):
+        lo, cnt = B.dp_chunk_range(length, nranks, chunk)
+        parts.append(torch.arange(off + lo, off + lo + cnt, device=device, dtype=torch.int64))
+    return torch.cat(parts) if parts else torch.empty(0, dtype=torch.int64, device=device)
+
+
+class _Norm:
+    """Piece sums, workspace and the two device scalars of the clip."""
+
+    def __init__(self, npieces, device):
+        self.npieces = npieces
+        self.partials = torch.zeros(max(npieces, 1), dtype=torch.float64, device=device)
+        ws = B.dp_grad_sqnorm_workspace(npieces)
+        self.workspace = torch.empty(max(ws // 8, 1), dtype=torch.float64, device=device)
+        self.sqnorm = torch.zeros(1, dtype=torch.float64, device=device)
+        self.scale = torch.ones(1, dtype=torch.float32, device=device)
+
+    def run(self, max_norm, stream=None):
+        B.dp_grad_sqnorm(self.partials, max_norm, self.workspace, self.sqnorm, self.scale,
+                         npieces=self.npieces, stream=stream)
+
+
+class Zero1AllRanks:
+    """ZeRO-1 step of N simulated ranks over a bucket plan."""
+
+    def __init__(self, buckets, nranks, master, hyper=None, device="cuda"):
+        self.buckets = [(int(o), int(l)) for o, l in buckets]
+        self.n = nranks
+        self.hyper = hyper or Hyper()
+        self.numel = master.numel()
+        master = master.to(device=device, dtype=torch.float32)
+        self.chunks = [owned_chunk(r, nranks) for r in range(nranks)]
+        self.state, self.means = [], []
+        for c in self.chunks:
+            idx = _shard_index(self.buckets, nranks, c, device)
+            w = master.index_select(0, idx).contiguous()
+            self.state.append((w, torch.zeros_like(w), torch.zeros_like(w)))
+            self.means.append(torch.empty_like(w))
+        self.norm = _Norm(B.dp_piece_count(self.buckets, nranks), device)
+        self.replicas = [master.to(torch.bfloat16) for _ in range(nranks)]
+
+    def step(self, rank_grads, t, stream=None):
+        for c, mean in zip(self.chunks, self.means):
+            B.dp_reduce_scatter_mean(rank_grads, self.buckets, c, mean, self.norm.partials,
+                                     stream=stream)
+        self.norm.run(self.hyper.max_norm, stream)
+        args = B.adamw_args(**step_scalars(self.hyper, t))
+        for c, (w, m, v), mean in zip(self.chunks, self.state, self.means):
+            B.zero1_adamw_gather(w, m, v, mean, self.buckets, self.n, c, self.norm.scale, args,
+                                 self.replicas, stream=stream)
+
+
+class DDPStep:
+    """Plain data-parallel step as one replica computes it."""
+
+    def __init__(self, buckets, nranks, master, hyper=None, device="cuda"):
+        self.buckets = [(int(o), int(l)) for o, l in buckets]
+        self.n = nranks
+        self.hyper = hyper or Hyper()
+        w = master.to(device=device, dtype=torch.float32).clone()
+        self.state = (w, torch.zeros_like(w), torch.zeros_like(w))
+        self.mean = torch.zeros_like(w)
+        self.norm = _Norm(B.dp_piece_count(self.buckets, nranks), device)
+        self.replica = w.to(torch.bfloat16)
+
+    def step(self, rank_grads, t, stream=None):
+        B.dp_reduce_scatter_mean(rank_grads, self.buckets, -1, self.mean, self.norm.partials,
+                                 stream=stream)
+        self.norm.run(self.hyper.max_norm, stream)
+        args = B.adamw_args(**step_scalars(self.hyper, t))
+        w, m, v = self.state
+        B.zero1_adamw_gather(w, m, v, self.mean, self.buckets, self.n, -1, self.norm.scale,
+                             args, [self.replica], stream=stream)
+
+
+class Zero1OneRank:
+    """ZeRO-1 step of one rank; its peers' contributions arrive as inputs.
+
+    Per step the caller provides (all resident on the device):
+
+    * ``incoming[j]`` -- rank j's gradient values of this rank's chunk,
+      shard-compact (what a reduce-scatter delivers to the owner);
+    * the peers' norm pieces, written into ``self.norm.partials`` outside this
+      rank's slots (what an all-gather of the piece sums delivers);
+    * ``peer_shards[j]`` -- rank j's updated bf16 shard (``None`` at this rank),
+      what the all-gather of the weights delivers.
+    """
+
+    def __init__(self, buckets, nranks, rank, shard_master, hyper=None, device="cuda",
+                 arena_numel=None):
+        self.buckets = [(int(o), int(l)) for o, l in buckets]
+        self.n, self.rank = nranks, rank
+        self.chunk = owned_chunk(rank, nranks)
+        self.hyper = hyper or Hyper()
+        w = shard_master.to(device=device, dtype=torch.float32).contiguous()
+        if w.numel() != B.dp_shard_numel(self.buckets, nranks, self.chunk):
+            raise ValueError("shard_master does not match the plan's shard")
+        self.state = (w, torch.zeros_like(w), torch.zeros_like(w))
+        self.mean = torch.empty_like(w)
+        self.norm = _Norm(B.dp_piece_count(self.buckets, nranks), device)
+        ext = arena_numel or max(o + l for o, l in self.buckets)
+        self.arena = torch.zeros(ext, dtype=torch.bfloat16, device=device)
+
+    def own_piece_slots(self):
+        """(first, count) ranges of this rank's pieces in the norm-piece array."""
+        out = []
+        for b, (_, length) in enumerate(self.buckets):
+            first = B.dp_piece_offset(self.buckets, self.n, b, self.chunk)
+            _, cnt = B.dp_chunk_range(length, self.n, self.chunk)
+            out.append((first, -(-cnt // GRZ_PIECE)))
+        return out
+
+    def reduce(self, incoming, stream=None):
+        B.dp_reduce_scatter_mean(incoming, self.buckets, self.chunk, self.mean,
+                                 self.norm.partials, flags=GRZ_IN_COMPACT, stream=stream)
+
+    def update(self, t, stream=None):
+        self.norm.run(self.hyper.max_norm, stream)
+        args = B.adamw_args(**step_scalars(self.hyper, t))
+        w, m, v = self.state
+        B.zero1_adamw_gather(w, m, v, self.mean, self.buckets, self.n, self.chunk,
+                             self.norm.scale, args, [self.arena], stream=stream)
+
+    def gather(self, peer_shards, stream=None):
+        B.zero1_all_gather(peer_shards, self.buckets, [self.arena], stream=stream)
+
+    def step(self, incoming, peer_shards, t, stream=None):
+        self.reduce(incoming, stream)
+        self.update(t, stream)
+        self.gather(peer_shards, stream)

@@ -1,0 +1,249 @@
+/*
+ * grz.h -- C ABI of libgrz, the data-parallel / ZeRO-1 gradient pipeline on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * One step of the pipeline, for N ranks whose gradients sit in N flat arenas:
+ *
+ *   dp_reduce_scatter_mean   ring-order average of the ranks' gradients
+ *   dp_grad_sqnorm           global squared norm and clip factor
+ *   zero1_adamw_step         clipped AdamW on the owned shard (+ bf16 copy,
+ *                            optionally written straight into the replicas)
+ *   zero1_all_gather         owned bf16 shards into every replica arena
+ *
+ * Sources: "Lab 09 -- Parallelism, simulated" s.1 "Ring all-reduce" (the
+ * N = 3 schedule table; "Tips": in reduce-scatter step t rank r sends chunk
+ * (r - t) mod N and ends owning chunk (r + 1) mod N) and s.2 (sum, then
+ * divide by N); "A4 -- Multi-GPU with NCCL and ZeRO-1", "Part 2 -- Tensor
+ * Sharding", "Part 3 -- Gradient Reduction" (reduce-scatter with ncclAvg),
+ * "Part 4 -- Multi-GPU Backward and Update" (AdamW only on the shard, then
+ * all-gather); "Distributed training" (noeira), "Four strategies, one
+ * interface" (clip_grads_device, step; one flat arena per replica) and "The
+ * process group" (every rank simulated on one device).
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Memory.  Every pointer named "device" is HIP device memory owned by the
+ *    caller; the library allocates nothing and keeps no state between calls
+ *    (apart from the launch-width knob of grz_set_max_blocks), so concurrent
+ *    calls on different streams are safe when they touch disjoint buffers.
+ *    Buffers must stay alive until the stream has run the enqueued work.
+ *    Host arrays (pointer tables, bucket lists, argument structs) are read
+ *    during the call only.
+ *  - Streams.  Work is enqueued on `stream` (0 = the null stream).  No entry
+ *    point synchronises the host: results are ready when the stream is.
+ *  - Errors.  Arguments are checked before anything is enqueued; on a bad
+ *    argument nothing is launched and a GRZ_E* code is returned (see
+ *    grz_strerror).  A launch failure reported by HIP returns GRZ_EHIP.
+ *  - Buckets.  A bucket is a contiguous element range [offset, offset +
+ *    length) of the arena; buckets are listed in processing order (reverse
+ *    layer order: "Distributed training", "Overlap and graphs", plan_buckets;
+ *    "A4", "Part 4": the backward pass produces the last layer first).
+ *    Chunk c of a bucket is its c-th piece under the numpy.array_split rule
+ *    (the first length % N chunks are one element longer).
+ *  - Shards.  The ZeRO-1 shard of chunk c is chunk c of every bucket,
+ *    concatenated in processing order ("shard-compact" layout).  Rank r owns
+ *    chunk (r + 1) mod N.  Unless GRZ_UNEVEN is given, every bucket length
+ *    must be divisible by N ("Part 2 -- Tensor Sharding": error out
+ *    otherwise), else GRZ_EINDIVISIBLE.
+ *  - Pieces.  The norm is summed over pieces of GRZ_PIECE consecutive
+ *    elements of one chunk (the last piece of a chunk may be shorter).  The
+ *    pieces of a plan are numbered bucket by bucket, chunk 0..N-1 within a
+ *    bucket, piece by piece within a chunk; dp_piece_count gives their
+ *    number and dp_piece_offset where a (bucket, chunk) starts.  The same
+ *    pieces, hence the same norm bits, come out of a ZeRO-1 and a plain
+ *    data-parallel run of the same plan.
+ *  - Arithmetic.  bf16 and fp32 gradients are summed in fp32, fp64 ones in
+ *    fp64, one rounding per addition, in ring order; the mean is one IEEE
+ *    division by N.  AdamW runs in fp32 with every operation rounded on its
+ *    own (no fused multiply-add) and correctly rounded division and square
+ *    root.  bf16 outputs are round-to-nearest-even of the fp32 master.
+ */
+#ifndef GRZ_H
+#define GRZ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  GRZ_OK = 0,
+  GRZ_EINVAL = 1,        /* null pointer, bad count, bad dtype, bad flag, ... */
+  GRZ_EINDIVISIBLE = 2,  /* a bucket length is not divisible by N            */
+  GRZ_EALIGN = 3,        /* a device pointer is not aligned to its element   */
+  GRZ_EHIP = 4,          /* HIP reported an error when launching             */
+  GRZ_ERANGE = 5         /* a bucket leaves the arena or a size is too large */
+};
+
+/* Gradient element types. */
+enum { GRZ_F32 = 0, GRZ_BF16 = 1, GRZ_F64 = 2 };
+
+/* Flags of dp_reduce_scatter_mean / zero1_adamw_step / zero1_all_gather. */
+enum {
+  GRZ_SUM = 1,        /* keep the sum: skip the division by N            */
+  GRZ_UNEVEN = 2,     /* allow bucket lengths not divisible by N         */
+  GRZ_IN_COMPACT = 4  /* rank inputs hold only the reduced chunk, compact */
+};
+
+#define GRZ_MAX_RANKS 16    /* N and the number of replicas per call       */
+#define GRZ_PIECE 4096      /* elements per norm piece                      */
+
+typedef struct {
+  int64_t offset; /* first element of the bucket in the arena */
+  int64_t length; /* elements in the bucket                   */
+} grz_bucket;
+
+/* Per-step AdamW scalars, all fp32.  bias_corr1/2 are 1 - beta1^t and
+ * 1 - beta2^t for the step t (starting at 1), evaluated by the caller. */
+typedef struct {
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+  float bias_corr1;
+  float bias_corr2;
+} grz_adamw_args;
+
+/* Version of the ABI (major * 100 + minor). */
+int grz_version(void);
+
+/* Launch-width knob: the largest grid (workgroups of 256 threads) the
+ * grid-stride kernels use, default 2048 (8 per CU on 256 CUs).  It changes
+ * speed only; the piece layout, the fold order and the norm tree, hence every
+ * result bit, do not depend on it.  Process-wide; GRZ_EINVAL outside
+ * 1..2^20. */
+int grz_set_max_blocks(int blocks);
+
+/* Static description of a status code; never NULL. */
+const char* grz_strerror(int status);
+
+/* Chunk rank `rank` owns after the ring reduce-scatter: (rank + 1) mod N
+ * ("Lab 09", s.1, the "owns" row; "Tips").  -1 on a bad argument. */
+int dp_ring_owned_chunk(int rank, int nranks);
+
+/* Rank that owns chunk `chunk`: (chunk - 1) mod N.  -1 on a bad argument. */
+int dp_ring_chunk_owner(int chunk, int nranks);
+
+/* Range of chunk `chunk` of a bucket of `length` elements split over N
+ * (array_split rule): *offset within the bucket and *count elements. */
+int dp_chunk_range(int64_t length, int nranks, int chunk, int64_t* offset, int64_t* count);
+
+/* Number of norm pieces of a plan over all N chunks of every bucket, or a
+ * negative GRZ_E* code. */
+int64_t dp_piece_count(const grz_bucket* buckets, int nbuckets, int nranks, int flags);
+
+/* Index of the first piece of chunk `chunk` of bucket `bucket`, or a
+ * negative GRZ_E* code. */
+int64_t dp_piece_offset(const grz_bucket* buckets, int nbuckets, int nranks, int flags,
+                        int bucket, int chunk);
+
+/* Elements of the ZeRO-1 shard of chunk `chunk` (sum over buckets of the
+ * chunk's length), or a negative GRZ_E* code. */
+int64_t dp_shard_numel(const grz_bucket* buckets, int nbuckets, int nranks, int chunk,
+                       int flags);
+
+/*
+ * Ring-order reduce-scatter-mean ("Lab 09", s.1 and "Tips"; "A4", "Part 3",
+ * ncclReduceScatter / ncclAllReduce with ncclAvg).
+ *
+ * rank_grads  host array of N device pointers: rank j's flat gradient arena
+ *             of `dtype` elements.  With GRZ_IN_COMPACT, rank j's values of
+ *             chunk `chunk` only, in shard-compact layout (what arrives over
+ *             the wire for one owner).
+ * nranks      N, 1..GRZ_MAX_RANKS.
+ * dtype       GRZ_F32, GRZ_BF16 (uint16 bit patterns) or GRZ_F64.
+ * buckets     host array of `nbuckets` (1..) buckets in processing order.
+ * chunk       0..N-1: reduce that chunk of every bucket (ZeRO-1; mean_out is
+ *             shard-compact, dp_shard_numel elements).  -1: reduce every
+ *             chunk (plain data parallelism; mean_out is indexed like the
+ *             arena and only bucket ranges are written).
+ * flags       GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT (needs chunk >= 0).
+ * mean_out    device; fp32 for F32/BF16 input, fp64 for F64 input.
+ * piece_sqnorm device fp64 array of dp_piece_count elements, or NULL.  The
+ *             slots of the reduced chunks receive the sum of squares of the
+ *             piece's output values; other slots are left untouched.
+ *
+ * Element c-th chunk value = (((g_c + g_{c+1}) + g_{c+2}) + ... + g_{c-1}) / N
+ * with rank indices mod N: the sum starts at rank c and travels the ring.
+ */
+int dp_reduce_scatter_mean(const void* const* rank_grads, int nranks, int dtype,
+                           const grz_bucket* buckets, int nbuckets, int chunk, int flags,
+                           void* mean_out, double* piece_sqnorm, hipStream_t stream);
+
+/* Bytes of workspace dp_grad_sqnorm needs for `npieces` pieces (may be 0). */
+size_t dp_grad_sqnorm_workspace(int64_t npieces);
+
+/*
+ * Global squared norm and clip factor ("Distributed training",
+ * clip_grads_device(max_norm): clipping stays on the device).
+ *
+ * piece_sqnorm  device fp64, `npieces` partial sums in piece order.
+ * max_norm      clip threshold; <= 0 disables clipping (factor 1).
+ * workspace     device, dp_grad_sqnorm_workspace(npieces) bytes (NULL if 0).
+ * sqnorm_out    device fp64 scalar: the pieces summed in a fixed tree order
+ *               that depends only on npieces.
+ * clip_scale_out device fp32 scalar: fp32(max_norm / sqrt(sqnorm)) when
+ *               sqrt(sqnorm) > max_norm, else 1.
+ */
+int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
+                   void* workspace, double* sqnorm_out, float* clip_scale_out,
+                   hipStream_t stream);
+
+/*
+ * Clipped AdamW on one rank's shard ("A4", "Part 4": adamw_update only for
+ * this rank's shard; "Distributed training", step()).
+ *
+ * master, m, v  device fp32, `n` elements each, updated in place.
+ * mean_grad     device fp32, `n` elements (dp_reduce_scatter_mean output).
+ * clip_scale    device fp32 scalar (dp_grad_sqnorm output) or NULL for 1.
+ * args          host, the step's scalars.
+ * bf16_out      device uint16, `n` elements of RNE_bf16(new master), or NULL.
+ *
+ * Per element: g = mean*scale; m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*(g*g);
+ * master -= lr*((m/bc1) / (sqrt(v/bc2) + eps) + wd*master).
+ */
+int zero1_adamw_step(float* master, float* m, float* v, const float* mean_grad, int64_t n,
+                     const float* clip_scale, const grz_adamw_args* args, uint16_t* bf16_out,
+                     hipStream_t stream);
+
+/*
+ * zero1_adamw_step with the all-gather fused into its epilogue: the new bf16
+ * weights of the shard of chunk `chunk` go straight to their arena offsets in
+ * every replica (no shard-compact bf16 round trip).  The shard geometry is
+ * (buckets, nbuckets, nranks, chunk, flags) as in dp_reduce_scatter_mean;
+ * chunk -1 means the whole plan in arena indexing (plain data parallelism:
+ * master, m, v and mean_grad are then indexed like the arena).
+ *
+ * replicas   host array of `nreplicas` (0..GRZ_MAX_RANKS) device uint16
+ *            arenas.
+ */
+int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad,
+                       const grz_bucket* buckets, int nbuckets, int nranks, int chunk,
+                       int flags, const float* clip_scale, const grz_adamw_args* args,
+                       uint16_t* const* replicas, int nreplicas, hipStream_t stream);
+
+/*
+ * All-gather of bf16 shards ("Lab 09", s.1, all-gather rows of the N = 3
+ * table; "A4", "Part 4", ncclAllGather after the update).
+ *
+ * shards     host array of N entries: shards[r] is rank r's shard-compact
+ *            bf16 shard (chunk (r + 1) mod N of every bucket) on the device,
+ *            or NULL for a rank whose shard is already in place.
+ * replicas   host array of `nreplicas` device uint16 arenas; every non-NULL
+ *            shard is copied into each of them at its arena offsets.
+ */
+int zero1_all_gather(const uint16_t* const* shards, int nranks, const grz_bucket* buckets,
+                     int nbuckets, int flags, uint16_t* const* replicas, int nreplicas,
+                     hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRZ_H */

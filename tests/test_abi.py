@@ -1,0 +1,108 @@
+"""The C ABI loads and exports what include/grz.h declares; host-only entry
+points (index helpers, argument checks) behave as documented.  No GPU work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gradient_reduce_zero_amd as grz
+from gradient_reduce_zero_amd import _native as N
+from oracle.reduce import chunk_owner, owned_chunk
+from oracle.ring import chunk_bounds
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "grz.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z][a-z0-9_]*)\s*\(", text)) -
+                  {"defined", "if", "sizeof"})
+
+
+def test_library_exports_every_declared_symbol():
+    lib = grz.lib()
+    names = declared_functions()
+    assert "dp_reduce_scatter_mean" in names and "zero1_all_gather" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(N.SIGNATURES), "binding signatures out of step with the header"
+    assert lib.grz_version() == 100
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    assert re.search(r"#define GRZ_MAX_RANKS (\d+)", text).group(1) == str(N.GRZ_MAX_RANKS)
+    assert re.search(r"#define GRZ_PIECE (\d+)", text).group(1) == str(N.GRZ_PIECE)
+    for name in ("GRZ_SUM", "GRZ_UNEVEN", "GRZ_IN_COMPACT", "GRZ_EINDIVISIBLE", "GRZ_BF16"):
+        assert re.search(rf"{name} = (\d+)", text).group(1) == str(getattr(N, name))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
+def test_ownership_helpers_match_oracle(n):
+    for r in range(n):
+        assert grz.dp_ring_owned_chunk(r, n) == owned_chunk(r, n)
+        assert grz.dp_ring_chunk_owner(r, n) == chunk_owner(r, n)
+    assert grz.dp_ring_owned_chunk(n, n) == -1
+    assert grz.dp_ring_chunk_owner(-1, n) == -1
+
+
+@pytest.mark.parametrize("length,n", [(64, 3), (0, 4), (7, 8), (4096, 2), (10 ** 12 + 5, 7)])
+def test_chunk_range_matches_array_split(length, n):
+    for c, (lo, hi) in enumerate(chunk_bounds(length, n)):
+        assert grz.dp_chunk_range(length, n, c) == (lo, hi - lo)
+
+
+def test_piece_numbering():
+    buckets = [(10000, 9000), (0, 10000)]
+    # bucket 0: chunks of 4500 -> 2 pieces each; bucket 1: 5000 -> 2 each.
+    assert grz.dp_piece_count(buckets, 2) == 8
+    assert grz.dp_piece_offset(buckets, 2, 0, 1) == 2
+    assert grz.dp_piece_offset(buckets, 2, 1, 0) == 4
+    assert grz.dp_shard_numel(buckets, 2, 1) == 9500
+    # uneven chunks (array_split rule): 64 over 3 -> 22, 21, 21, one piece each
+    assert grz.dp_piece_count([(0, 64)], 3) == 3
+    assert grz.dp_piece_count([(0, 0)], 4) == 0
+    assert grz.dp_grad_sqnorm_workspace(0) == 0
+    assert grz.dp_grad_sqnorm_workspace(4096) == 0
+    assert grz.dp_grad_sqnorm_workspace(4097) == 16
+    assert grz.dp_grad_sqnorm_workspace(4096 * 4096 + 1) == 8 * (4097 + 2)
+
+
+def _rs(lib, ptrs, n, dtype, buckets, chunk, flags, out):
+    arr = (N.Bucket * max(len(buckets), 1))(*buckets)
+    pp = (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
+    return lib.dp_reduce_scatter_mean(pp, n, dtype, arr, len(buckets), chunk, flags, out, None,
+                                      None)
+
+
+def test_argument_errors_return_before_any_launch():
+    lib = grz.lib()
+    fake = [0x10000, 0x20000]  # never dereferenced: every call below fails validation
+    out = ctypes.c_void_p(0x30000)
+    assert _rs(lib, fake, 0, N.GRZ_F32, [(0, 64)], 0, 0, out) == N.GRZ_EINVAL
+    assert _rs(lib, fake, 2, 7, [(0, 64)], 0, 0, out) == N.GRZ_EINVAL
+    assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 63)], 1, 0, out) == N.GRZ_EINDIVISIBLE
+    assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], 2, 0, out) == N.GRZ_EINVAL
+    assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], -1, N.GRZ_IN_COMPACT, out) == N.GRZ_EINVAL
+    assert _rs(lib, fake, 2, N.GRZ_F32, [(-4, 64)], 0, 0, out) == N.GRZ_ERANGE
+    assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], 0, 64, out) == N.GRZ_EINVAL
+    assert _rs(lib, [0x10001, 0x20000], 2, N.GRZ_F32, [(0, 64)], 0, 0, out) == N.GRZ_EALIGN
+    assert _rs(lib, [0x10000, 0], 2, N.GRZ_F32, [(0, 64)], 0, 0, out) == N.GRZ_EINVAL
+    assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], 0, 0, None) == N.GRZ_EINVAL
+    assert lib.dp_grad_sqnorm(None, 5, 1.0, None, None, None, None) == N.GRZ_EINVAL
+    assert lib.dp_grad_sqnorm(ctypes.c_void_p(0x10000), 5000, 1.0, None,
+                              ctypes.c_void_p(0x20000), None, None) == N.GRZ_EINVAL
+    assert lib.grz_set_max_blocks(0) == N.GRZ_EINVAL
+    for code in range(6):
+        assert lib.grz_strerror(code)
+    assert b"partition" in lib.grz_strerror(N.GRZ_EINDIVISIBLE)
+
+
+def test_product_path_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError, match="GPU"):
+        grz.dp_reduce_scatter_mean([torch.zeros(64), torch.zeros(64)], [(0, 64)], 0,
+                                   torch.zeros(32))

@@ -1,0 +1,204 @@
+"""Parity at the full model sizes, in the launch configuration the bench times.
+
+Where the oracle can redo everything in seconds (char GPT, GPT-2 124M) it
+does; at 1.5B and 7B it recomputes sampled elements one by one from the same
+input bytes (random picks, both ends, piece and chunk boundaries) and the
+norm over the whole reduced gradient in streamed tiles.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gradient_reduce_zero_amd as grz
+from oracle.plan import plan_buckets as oracle_plan
+from oracle.reduce import chunk_mean, owned_chunk, reduce_scatter_mean, widen
+from oracle.step import Hyper as OHyper
+from oracle.step import adamw, bf16_round, clip_scale, ddp_step, zero1_step
+from parity_util import (assert_bits, chunk_of_index, gather_host, host, max_rel,
+                         oracle_mean_at, oracle_states, sample_indices)
+from workloads import arena, grad_seed, master_init, onerank_inputs, rank_grad
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _layer_spans(a, sigma=1e-3):
+    """Char GPT: sigma_l = 1e-3 * 2^(l - (L-1)/2) for block l, 1e-3 elsewhere."""
+    nl = max(layer for _, _, layer in a.tensors)
+    spans = []
+    for off, n, layer in a.spans():
+        s = sigma * 2.0 ** (layer - (nl - 1) / 2) if 0 <= layer < nl else sigma
+        spans.append((off, n, s))
+    return spans
+
+
+def test_char_gpt_all_ranks_5_steps():
+    a = arena("char_gpt")
+    p, n = a.numel, 8
+    buckets = [(0, p)]
+    master = master_init(p, device=DEV)
+    z = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    d = grz.DDPStep(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    states = oracle_states(host(master), buckets, n)
+    spans = _layer_spans(a)
+    for t in range(1, 6):
+        grads = [rank_grad(p, 1e-3, "bf16", grad_seed(t, r), DEV, spans) for r in range(n)]
+        z.step(grads, t)
+        d.step(grads, t)
+        torch.cuda.synchronize()
+        ref = zero1_step([host(g) for g in grads], "bf16", buckets, states, OHyper(), t)
+        states = ref["states"]
+        for r in range(n):
+            assert_bits(host(z.means[r]), ref["means"][r], f"t={t} mean rank {r}")
+        assert math.isclose(z.norm.sqnorm.item(), ref["sqnorm"], rel_tol=1e-13)
+        assert ref["scale"] < 1  # the char GPT's norm is above 1: the clip is active
+        assert_bits(host(z.norm.scale), np.array([ref["scale"]], np.float32), f"t={t} scale")
+        for r in range(n):
+            for k in range(3):
+                got, want = host(z.state[r][k]), ref["states"][r][k]
+                assert max_rel(got, want) <= 1e-6
+                assert_bits(got, want, f"t={t} state {k} rank {r}")
+        assert_bits(host(z.replicas[n - 1]), ref["arena"], f"t={t} replica")
+        assert_bits(host(d.replica), ref["arena"], f"t={t} DDP replica")
+
+
+def test_gpt2_124m_reverse_layer_buckets():
+    a = arena("gpt2_124m")
+    p, n = a.numel, 8
+    buckets = grz.plan_buckets(a.numels, 25 * 2 ** 20, 2)
+    assert buckets == oracle_plan(a.numels, 25 * 2 ** 20, 2) and len(buckets) == 9
+    master = master_init(p, device=DEV)
+    z = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    d = grz.DDPStep(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    grads = [rank_grad(p, 1e-3, "bf16", grad_seed(1, r), device=DEV) for r in range(n)]
+    z.step(grads, 1)
+    d.step(grads, 1)
+    torch.cuda.synchronize()
+    hg = [host(g) for g in grads]
+    dstate = (host(master), np.zeros(p, np.float32), np.zeros(p, np.float32))
+    ref = ddp_step(hg, "bf16", buckets, dstate, OHyper(), 1)
+    assert_bits(host(d.mean), ref["mean"], "DDP mean over 9 buckets")
+    for r in range(n):
+        want = reduce_scatter_mean(hg, "bf16", buckets, owned_chunk(r, n))
+        assert_bits(host(z.means[r]), want, f"ZeRO-1 shard of rank {r}")
+    assert math.isclose(z.norm.sqnorm.item(), ref["sqnorm"], rel_tol=1e-12)
+    assert_bits(host(z.norm.sqnorm), host(d.norm.sqnorm), "ZeRO-1 vs DDP sqnorm bits")
+    assert_bits(host(z.norm.scale), np.array([ref["scale"]], np.float32), "scale")
+    assert_bits(host(d.state[0]), ref["state"][0], "DDP master")
+    assert_bits(host(d.replica), ref["arena"], "DDP bf16 arena")
+    for r in range(n):
+        assert_bits(host(z.replicas[r]), ref["arena"], f"ZeRO-1 replica {r} == DDP")
+
+
+def _tiled_sqnorm(tensors_for, chunk, kind, length, tile=1 << 25):
+    """Oracle norm of the mean over [0, length) of a shard, streamed in tiles."""
+    total = []
+    for lo in range(0, length, tile):
+        hi = min(length, lo + tile)
+        contribs = [host(t[lo:hi]) for t in tensors_for]
+        mean = chunk_mean([widen(c, kind) for c in contribs], chunk)
+        total.append(np.sum(np.square(mean.astype(np.float64))))
+    return float(np.sum(total))
+
+
+def test_llama_7b_one_rank_share_sampled():
+    # The bench's configuration: rank 0 of N = 8 owns chunk 1 of the whole
+    # 6.74e9-element arena; 842,301,952 owned parameters.
+    a = arena("llama_7b")
+    p, n, rank = a.numel, 8, 0
+    buckets = grz.whole_arena(p)
+    chunk = owned_chunk(rank, n)
+    shard = grz.dp_shard_numel(buckets, n, chunk)
+    assert shard == p // n == 842_301_952
+    npieces = grz.dp_piece_count(buckets, n)
+    inp = onerank_inputs(shard, n, rank, npieces, grz.GRZ_PIECE, device=DEV)
+    pipe = grz.Zero1OneRank(buckets, n, rank, inp["shard_master"], device=DEV, arena_numel=p)
+    idx = sample_indices(shard, 200_000, 7, extra=[4095, 4096, 4097, shard - 4096 * 2])
+    w0 = gather_host(pipe.state[0], idx)
+    g_at = [gather_host(t, idx) for t in inp["incoming"]]
+    peers = host(inp["partials"])
+    own = pipe.own_piece_slots()
+    pipe.norm.partials.copy_(inp["partials"])
+    pipe.step(inp["incoming"], inp["peer_shards"], 1)
+    torch.cuda.synchronize()
+
+    # Reduced gradient, sampled, bit-exact.
+    want_mean = oracle_mean_at(g_at, np.full(idx.size, chunk), "bf16")
+    assert_bits(gather_host(pipe.mean, idx), want_mean, "7B mean (sampled)")
+    # Norm: own part recomputed in tiles from the inputs, peers' parts as received.
+    mask = np.ones(npieces, bool)
+    for first, cnt in own:
+        mask[first:first + cnt] = False
+    sq_own = _tiled_sqnorm(inp["incoming"], chunk, "bf16", shard)
+    sq = sq_own + float(np.sum(peers[mask]))
+    assert math.isclose(pipe.norm.sqnorm.item(), sq, rel_tol=1e-10)
+    scale = clip_scale(sq, 1.0)
+    assert scale < 1
+    got_scale = np.float32(pipe.norm.scale.item())
+    assert abs(float(got_scale) - float(scale)) <= float(np.spacing(scale))
+    # AdamW, sampled, on the oracle's own clip factor: bit-exact when the GPU's
+    # factor has the same bits (a 1-ulp difference can only come from the norm
+    # being summed in another order).
+    h = OHyper()
+    w1, m1, v1 = adamw(w0, np.zeros_like(w0), np.zeros_like(w0), want_mean * scale,
+                       **h.scalars(1))
+    for k, want in enumerate((w1, m1, v1)):
+        got = gather_host(pipe.state[k], idx)
+        assert max_rel(got, want) <= 1e-6
+        if got_scale == scale:
+            assert_bits(got, want, f"7B state {k} (sampled)")
+    # The rank's bf16 arena: own chunk = RNE(master); peers' chunks as received.
+    lo = chunk * shard
+    assert_bits(gather_host(pipe.arena, idx + lo), bf16_round(gather_host(pipe.state[0], idx)),
+                "own chunk of the arena")
+    for j in (2, 5, 7):
+        c = owned_chunk(j, n)
+        assert_bits(gather_host(pipe.arena, idx + c * shard),
+                    gather_host(inp["peer_shards"][j], idx), f"peer {j}'s chunk")
+
+
+def test_gpt2_1p5b_all_ranks_sampled():
+    a = arena("gpt2_1p5b")
+    p, n = a.numel, 4
+    buckets = [(0, p)]
+    hyper = grz.Hyper(lr=1e-4, warmup=10, max_norm=1.0)
+    master = master_init(p, device=DEV)
+    z = grz.Zero1AllRanks(buckets, n, master, hyper, device=DEV)
+    idx = sample_indices(p, 100_000, 11, extra=[p // 4 - 1, p // 4, p // 2, 3 * p // 4])
+    m_at = gather_host(master, idx)
+    del master
+    grads = [rank_grad(p, 1e-3, "bf16", grad_seed(1, r), device=DEV) for r in range(n)]
+    g_at = [gather_host(g, idx) for g in grads]
+    z.step(grads, 1)
+    torch.cuda.synchronize()
+    _, chunks = chunk_of_index(buckets, n, idx)
+    want_mean = oracle_mean_at(g_at, chunks, "bf16")
+    shard = p // n
+    sq = 0.0
+    for r in range(n):
+        c = owned_chunk(r, n)
+        sel = chunks == c
+        local = idx[sel] - c * shard
+        assert_bits(gather_host(z.means[r], local), want_mean[sel], f"1.5B mean rank {r}")
+        sq += _tiled_sqnorm([g[c * shard:(c + 1) * shard] for g in grads], c, "bf16", shard)
+    assert math.isclose(z.norm.sqnorm.item(), sq, rel_tol=1e-10)
+    scale = clip_scale(sq, 1.0)
+    got_scale = np.float32(z.norm.scale.item())
+    assert abs(float(got_scale) - float(scale)) <= float(np.spacing(scale))
+    s = OHyper(lr=1e-4, warmup=10).scalars(1)
+    assert s["lr"] == np.float32(1e-5)
+    w1, _, _ = adamw(m_at, np.zeros_like(m_at), np.zeros_like(m_at), want_mean * scale, **s)
+    got_all = np.empty_like(w1)
+    for r in range(n):
+        c = owned_chunk(r, n)
+        sel = chunks == c
+        got = gather_host(z.state[r][0], idx[sel] - c * shard)
+        got_all[sel] = got
+        assert max_rel(got, w1[sel]) <= 1e-6
+        if got_scale == scale:
+            assert_bits(got, w1[sel], f"1.5B master rank {r}")
+    for rep in (z.replicas[0], z.replicas[3]):
+        assert_bits(gather_host(rep, idx), bf16_round(got_all), "1.5B replicas = RNE(master)")

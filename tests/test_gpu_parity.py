@@ -1,0 +1,299 @@
+"""GPU path (C ABI -> HIP kernels) against the CPU oracle, element by element.
+
+Bars: the reduced gradient, ownership and indexing bit-exact; the norm within
+1e-13 relative (the GPU sums fixed pieces in a fixed tree, the oracle sums
+exactly); fp32 master, m and v within 1e-6 relative after 10 steps (and in
+fact bit-exact whenever the clip factor agrees, which it does here); the
+bf16 weights bit-exact against the oracle's rounding of the same masters.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gradient_reduce_zero_amd as grz
+from oracle.reduce import owned_chunk, reduce_scatter_mean
+from oracle.ring import ring_all_reduce, ring_reduce_scatter
+from oracle.step import Hyper as OHyper
+from oracle.step import all_gather, bf16_round, ddp_step, grad_sqnorm, zero1_step
+from parity_util import assert_bits, host, max_rel, oracle_states
+from workloads import arena, grad_seed, master_init, rank_grad
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _dev(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+# --- the float64 ring check: 64 values at N = 2, 3, 4, 8 ----------------------
+
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+@pytest.mark.parametrize("integer", [False, True])
+def test_f64_ring_64_values(n, integer):
+    rng = np.random.default_rng(40 + n)
+    if integer:
+        arrays = [rng.integers(-100, 100, 64).astype(np.float64) for _ in range(n)]
+    else:
+        arrays = [rng.standard_normal(64) for _ in range(n)]
+    grads = [_dev(a) for a in arrays]
+    full, _, _ = ring_all_reduce(arrays)
+    out = torch.full((64,), float("nan"), dtype=torch.float64, device=DEV)
+    grz.dp_reduce_scatter_mean(grads, [(0, 64)], -1, out, flags=grz.GRZ_SUM)
+    assert_bits(host(out), full[0], "ring sum (all-reduce)")
+    if integer:
+        assert_bits(host(out), np.sum(np.stack(arrays), axis=0), "integer sum")
+    owned, _ = ring_reduce_scatter(arrays)
+    for r in range(n):
+        c, vals = owned[r]
+        assert c == grz.dp_ring_owned_chunk(r, n)
+        shard = torch.empty(vals.size, dtype=torch.float64, device=DEV)
+        grz.dp_reduce_scatter_mean(grads, [(0, 64)], c, shard,
+                                   flags=grz.GRZ_SUM | grz.GRZ_UNEVEN)
+        assert_bits(host(shard), vals, f"owned chunk of rank {r}")
+    mean = torch.empty(64, dtype=torch.float64, device=DEV)
+    grz.dp_reduce_scatter_mean(grads, [(0, 64)], -1, mean)
+    assert_bits(host(mean), reduce_scatter_mean(arrays, "f64", [(0, 64)], -1), "f64 mean")
+
+
+# --- Tiny: 4096 fp32 parameters, N = 2, 10 steps, ZeRO-1 and DDP --------------
+
+def _tiny_run(max_norm, steps=10, p=4096, n=2, sigma=0.01):
+    buckets = [(0, p)]
+    master = master_init(p, device=DEV)
+    hyper = grz.Hyper(max_norm=max_norm)
+    ohyper = OHyper(max_norm=max_norm)
+    z = grz.Zero1AllRanks(buckets, n, master, hyper, device=DEV)
+    d = grz.DDPStep(buckets, n, master, hyper, device=DEV)
+    states = oracle_states(host(master), buckets, n)
+    dstate = (host(master), np.zeros(p, np.float32), np.zeros(p, np.float32))
+    for t in range(1, steps + 1):
+        grads = [rank_grad(p, sigma, "f32", grad_seed(t, r), device=DEV) for r in range(n)]
+        z.step(grads, t)
+        d.step(grads, t)
+        torch.cuda.synchronize()
+        hg = [host(g) for g in grads]
+        ref = zero1_step(hg, "f32", buckets, states, ohyper, t)
+        dref = ddp_step(hg, "f32", buckets, dstate, ohyper, t)
+        states, dstate = ref["states"], dref["state"]
+        for r in range(n):
+            assert_bits(host(z.means[r]), ref["means"][r], f"t={t} mean of rank {r}")
+        assert math.isclose(z.norm.sqnorm.item(), ref["sqnorm"], rel_tol=1e-13)
+        assert_bits(host(z.norm.scale), np.array([ref["scale"]], np.float32), f"t={t} scale")
+        for r in range(n):
+            for k, name in enumerate(("master", "m", "v")):
+                got, want = host(z.state[r][k]), ref["states"][r][k]
+                assert max_rel(got, want) <= 1e-6, f"t={t} {name} rank {r}"
+                assert_bits(got, want, f"t={t} {name} of rank {r}")
+        for rep in z.replicas:
+            assert_bits(host(rep), ref["arena"], f"t={t} bf16 replica")
+        # DDP: same reduced gradient, same norm bits, same weights.
+        assert_bits(host(d.mean), dref["mean"], f"t={t} DDP mean")
+        assert_bits(host(d.norm.sqnorm), host(z.norm.sqnorm), f"t={t} DDP vs ZeRO-1 sqnorm")
+        assert_bits(host(d.replica), host(z.replicas[0]), f"t={t} DDP vs ZeRO-1 weights")
+        assert_bits(host(d.state[0]), dref["state"][0], f"t={t} DDP master")
+    return z, ref
+
+
+@pytest.mark.parametrize("max_norm", [1.0, 0.1])
+def test_tiny_zero1_and_ddp_10_steps(max_norm):
+    z, ref = _tiny_run(max_norm)
+    if max_norm == 0.1:
+        assert ref["scale"] < 1  # clipping is active in this case
+    else:
+        assert ref["scale"] == 1
+
+
+def test_tiny_bf16_is_rne_of_gpu_master():
+    z, _ = _tiny_run(1.0, steps=2)
+    for r in range(2):
+        rounded = bf16_round(host(z.state[r][0]))
+        c = grz.dp_ring_owned_chunk(r, 2)
+        lo, cnt = grz.dp_chunk_range(4096, 2, c)
+        assert_bits(host(z.replicas[0])[lo:lo + cnt], rounded, "bf16 = RNE(master)")
+
+
+# --- odd shapes: ragged tails, misaligned buckets, runtime N, empty buckets ---
+
+@pytest.mark.parametrize("n,kind,buckets,p", [
+    (3, "f32", [(0, 64)], 64),                                   # uneven chunks (DDP)
+    (5, "bf16", [(9000, 1003), (4003, 4997), (0, 4003)], 10003),  # odd sizes, misaligned
+    (6, "f32", [(0, 6 * 4097 + 5)], 6 * 4097 + 5),                # ragged pieces
+    (7, "bf16", [(0, 0), (0, 70007)], 70007),                     # empty bucket, N = 7
+    (16, "bf16", [(16 * 8 * 300, 16 * 8 * 300), (0, 16 * 8 * 300)], 16 * 8 * 600),
+    (1, "f32", [(0, 12345)], 12345),                              # one rank: identity
+    (8, "f64", [(0, 8 * 4096 * 3 + 8 * 5)], 8 * 4096 * 3 + 40),
+])
+def test_ddp_reduce_odd_shapes(n, kind, buckets, p):
+    rng_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f64": torch.float64}[kind]
+    grads = [rank_grad(p, 1e-2, kind, grad_seed(3, r), device=DEV) for r in range(n)]
+    assert grads[0].dtype == rng_dt
+    out_dt = torch.float64 if kind == "f64" else torch.float32
+    out = torch.full((p,), float("nan"), dtype=out_dt, device=DEV)
+    parts = torch.full((max(grz.dp_piece_count(buckets, n), 1),), -1.0, dtype=torch.float64,
+                       device=DEV)
+    grz.dp_reduce_scatter_mean(grads, buckets, -1, out, parts)
+    hg = [host(g) for g in grads]
+    ref = reduce_scatter_mean(hg, kind, buckets, -1, arena_len=p)
+    assert_bits(host(out), ref, "DDP mean")
+    npieces = grz.dp_piece_count(buckets, n)
+    sq = float(np.sum(host(parts)[:npieces]))
+    assert math.isclose(sq, grad_sqnorm(ref[~np.isnan(ref)]), rel_tol=1e-12)
+    # ZeRO-1 (uneven allowed) per chunk, shard-compact.
+    flags = grz.GRZ_UNEVEN
+    for c in range(n):
+        cnt = grz.dp_shard_numel(buckets, n, c, flags)
+        shard = torch.empty(max(cnt, 1), dtype=out_dt, device=DEV)
+        grz.dp_reduce_scatter_mean(grads, buckets, c, shard, flags=flags)
+        want = reduce_scatter_mean(hg, kind, buckets, c, uneven=True)
+        assert_bits(host(shard)[:cnt], want, f"shard of chunk {c}")
+
+
+def test_empty_plan_is_a_no_op():
+    g = [torch.zeros(8, device=DEV) for _ in range(2)]
+    out = torch.full((8,), 3.0, device=DEV)
+    grz.dp_reduce_scatter_mean(g, [], -1, out)
+    grz.dp_reduce_scatter_mean(g, [(0, 0)], 0, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+    sq = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+    sc = torch.zeros(1, device=DEV)
+    grz.dp_grad_sqnorm(torch.zeros(1, dtype=torch.float64, device=DEV), 1.0, None, sq, sc,
+                       npieces=0)
+    torch.cuda.synchronize()
+    assert sq.item() == 0.0 and sc.item() == 1.0
+
+
+# --- invariants: grid width, repeat runs, cross-N on grid-exact data ---------
+
+def test_results_do_not_depend_on_grid_width():
+    p, n = 3 * 4096 * 8 + 8 * 77, 8
+    buckets = [(4096 * 8, p - 4096 * 8), (0, 4096 * 8)]
+    grads = [rank_grad(p, 1e-3, "bf16", grad_seed(9, r), device=DEV) for r in range(n)]
+    master = master_init(p, device=DEV)
+    outs = []
+    try:
+        for blocks in (2048, 1, 7, 64):
+            grz.grz_set_max_blocks(blocks)
+            z = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=0.01), device=DEV)
+            z.step(grads, 1)
+            z.step(grads, 2)
+            torch.cuda.synchronize()
+            outs.append((host(z.norm.partials), host(z.replicas[3]),
+                         [host(s[0]) for s in z.state]))
+    finally:
+        grz.grz_set_max_blocks(2048)
+    for o in outs[1:]:
+        assert_bits(o[0], outs[0][0], "piece sums")
+        assert_bits(o[1], outs[0][1], "replica")
+        for a, b in zip(o[2], outs[0][2]):
+            assert_bits(a, b, "master")
+
+
+def test_cross_n_identity_grid_exact():
+    # Values k * 2^-24 with |k| < 2^13: every sum is exact, so the mean, the
+    # norm and the weights cannot depend on N.
+    p, steps = 1 << 16, 3
+    rng = np.random.default_rng(21)
+    micro = [[(rng.integers(-(1 << 13), 1 << 13, p) * 2.0 ** -24).astype(np.float32)
+              for _ in range(8)] for _ in range(steps)]
+    master = master_init(p, device=DEV)
+    arenas = {}
+    for n in (1, 2, 4, 8):
+        z = grz.Zero1AllRanks([(0, p)], n, master, grz.Hyper(max_norm=1e-4), device=DEV)
+        d = grz.DDPStep([(0, p)], n, master, grz.Hyper(max_norm=1e-4), device=DEV)
+        for t in range(1, steps + 1):
+            per = 8 // n
+            grads = [_dev(np.sum(np.stack(micro[t - 1][r * per:(r + 1) * per]), axis=0)
+                          * np.float32(n / 8)) for r in range(n)]
+            z.step(grads, t)
+            d.step(grads, t)
+        torch.cuda.synchronize()
+        assert z.norm.scale.item() < 1
+        arenas[n] = host(z.replicas[0])
+        assert_bits(host(d.replica), arenas[n], f"DDP vs ZeRO-1 at N={n}")
+    for n in (2, 4, 8):
+        assert_bits(arenas[n], arenas[1], f"weights at N={n} vs N=1")
+
+
+def test_nan_in_one_rank_propagates_like_the_oracle():
+    p, n = 4096, 2
+    grads = [rank_grad(p, 0.01, "f32", grad_seed(1, r), device=DEV) for r in range(n)]
+    grads[1][100] = float("nan")
+    master = master_init(p, device=DEV)
+    z = grz.Zero1AllRanks([(0, p)], n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    z.step(grads, 1)
+    torch.cuda.synchronize()
+    ref = zero1_step([host(g) for g in grads], "f32", [(0, p)],
+                     oracle_states(host(master), [(0, p)], n), OHyper(max_norm=1.0), 1)
+    assert math.isnan(z.norm.sqnorm.item()) and math.isnan(ref["sqnorm"])
+    assert_bits(host(z.norm.scale), np.array([ref["scale"]], np.float32), "scale")
+    for r in range(n):
+        assert_bits(host(z.state[r][0]), ref["states"][r][0], "master with a NaN")
+    # The sign of a NaN produced by arithmetic is not fixed by IEEE 754: compare
+    # the NaN element by class and every other element bit for bit.
+    got, want = host(z.replicas[0]), ref["arena"]
+    nan = (want & 0x7F80) == 0x7F80
+    nan &= (want & 0x7F) != 0
+    assert nan.sum() == 1 and ((got[nan] & 0x7F80) == 0x7F80).all() and (got[nan] & 0x7F).all()
+    assert_bits(got[~nan], want[~nan], "replica with a NaN")
+
+
+# --- the unfused optimizer and the standalone all-gather ----------------------
+
+def test_unfused_adamw_and_all_gather_match_fused():
+    p, n = 8 * 4096 + 8 * 13, 4
+    buckets = [(8 * 4096, 8 * 13), (0, 8 * 4096)]
+    grads = [rank_grad(p, 1e-3, "bf16", grad_seed(5, r), device=DEV) for r in range(n)]
+    master = master_init(p, device=DEV)
+    fused = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=0.02), device=DEV)
+    fused.step(grads, 1)
+    # Same step with the optimizer writing compact bf16 shards, then all-gather.
+    plain = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=0.02), device=DEV)
+    for c, mean in zip(plain.chunks, plain.means):
+        grz.dp_reduce_scatter_mean(grads, buckets, c, mean, plain.norm.partials)
+    plain.norm.run(0.02)
+    args = grz.adamw_args(**grz.step_scalars(plain.hyper, 1))
+    shards = []
+    for (w, m, v), mean in zip(plain.state, plain.means):
+        out = torch.empty(w.numel(), dtype=torch.bfloat16, device=DEV)
+        grz.zero1_adamw_step(w, m, v, mean, plain.norm.scale, args, out)
+        shards.append(out)
+    reps = [torch.zeros(p, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    grz.zero1_all_gather(shards, buckets, reps)
+    torch.cuda.synchronize()
+    want = all_gather([host(s) for s in shards], buckets, n, p)
+    for r in reps:
+        assert_bits(host(r), want, "all-gather vs oracle")
+        assert_bits(host(r), host(fused.replicas[0]), "unfused vs fused")
+    for r in range(n):
+        assert_bits(host(shards[r]), bf16_round(host(plain.state[r][0])), "shard = RNE(master)")
+
+
+def test_negative_controls_bite():
+    # Planted mistakes, in the oracle: each must disagree with the GPU result.
+    p, n = 4096, 4
+    grads = [rank_grad(p, 0.01, "f32", grad_seed(2, r), device=DEV) for r in range(n)]
+    out = torch.empty(p // n, device=DEV)
+    c = grz.dp_ring_owned_chunk(0, n)
+    grz.dp_reduce_scatter_mean(grads, [(0, p)], c, out)
+    hg = [host(g) for g in grads]
+    got = host(out)
+    good = reduce_scatter_mean(hg, "f32", [(0, p)], c)
+    assert_bits(got, good, "mean")
+    summed = reduce_scatter_mean(hg, "f32", [(0, p)], c, average=False)
+    assert not np.allclose(got, summed)                       # sum instead of mean
+    assert not np.allclose(got, good / n)                      # divided twice
+    wrong_chunk = reduce_scatter_mean(hg, "f32", [(0, p)], (c + 1) % n)
+    assert not np.allclose(got, wrong_chunk)                   # wrong ownership
+    lo, cnt = grz.dp_chunk_range(p, n, c)
+    start0 = [a[lo:lo + cnt] for a in hg]
+    plain = start0[0].copy()
+    for j in range(1, n):
+        plain = start0[j] + plain
+    assert not np.array_equal(got, plain / np.float32(n))       # fold not in ring order

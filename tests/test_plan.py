@@ -1,0 +1,46 @@
+"""Host planning of the product against the oracle's independent versions."""
+
+import io
+
+import numpy as np
+import pytest
+
+from gradient_reduce_zero_amd.plan import Hyper, plan_buckets, step_scalars, zero_stage
+from oracle.plan import plan_buckets as oracle_plan
+from oracle.step import Hyper as OHyper
+from workloads import arena
+
+
+@pytest.mark.parametrize("name", ["tiny", "char_gpt", "gpt2_124m", "gpt2_1p5b", "llama_7b"])
+@pytest.mark.parametrize("cap", [25 * 2 ** 20, 25 * 10 ** 6, 1 << 16])
+def test_plan_buckets_matches_oracle(name, cap):
+    a = arena(name)
+    assert plan_buckets(a.numels, cap, 2) == oracle_plan(a.numels, cap, 2)
+
+
+def test_plan_small_cases_match_oracle():
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        numels = rng.integers(0, 50, size=rng.integers(0, 12)).tolist()
+        cap = int(rng.integers(1, 120))
+        assert plan_buckets(numels, cap, 1) == oracle_plan(numels, cap, 1)
+
+
+@pytest.mark.parametrize("t", [1, 2, 5, 10, 11, 100, 1000])
+def test_step_scalars_match_oracle(t):
+    ours = step_scalars(Hyper(lr=1e-4, warmup=10), t)
+    ref = OHyper(lr=1e-4, warmup=10).scalars(t)
+    assert np.float32(ours["lr"]) == ref["lr"]
+    assert np.float32(ours["bias_corr1"]) == ref["bc1"]
+    assert np.float32(ours["bias_corr2"]) == ref["bc2"]
+    assert np.float32(ours["beta1"]) == np.float32(ref["beta1"])
+    with pytest.raises(ValueError):
+        step_scalars(Hyper(), 0)
+
+
+def test_zero_stage_fallback_message():
+    log = io.StringIO()
+    assert zero_stage([(0, 64), (64, 63)], 4, 1, log) == 0
+    assert "Can't equally partition parameters" in log.getvalue()
+    assert zero_stage([(0, 64)], 4, 1, io.StringIO()) == 1
+    assert zero_stage([(0, 64)], 4, 0, io.StringIO()) == 0

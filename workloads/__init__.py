@@ -7,8 +7,9 @@ both the GPU path and the CPU oracle can be fed from it without sharing code.
 """
 
 from .shapes import ARENAS, Arena, arena, char_gpt, gpt2, llama
-from .synth import (GRAD_SEED, grad_seed, master_init, peer_partials,
+from .synth import (GRAD_SEED, grad_seed, master_init, onerank_inputs, peer_partials,
                     rank_grad, to_bits)
 
 __all__ = ["ARENAS", "Arena", "arena", "char_gpt", "gpt2", "llama", "GRAD_SEED",
-           "grad_seed", "master_init", "peer_partials", "rank_grad", "to_bits"]
+           "grad_seed", "master_init", "onerank_inputs", "peer_partials", "rank_grad",
+           "to_bits"]

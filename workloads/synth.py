@@ -62,3 +62,25 @@ def to_bits(t):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view("uint16")
     return t.numpy()
+
+
+def onerank_inputs(shard_numel, nranks, rank, npieces, piece, step=1, sigma=1e-3,
+                   device="cpu", base=GRAD_SEED):
+    """Everything one ZeRO-1 rank receives in a step, resident on ``device``.
+
+    * ``incoming[j]``: rank j's bf16 gradient values of this rank's shard;
+    * ``peer_shards[j]``: rank j's updated bf16 weight shard (None for ``rank``);
+    * ``partials``: fp64 norm pieces of the whole plan (``npieces``), standing in
+      for the peers' pieces (this rank's own slots are overwritten by its reduce);
+    * ``shard_master``: fp32 N(0, 0.02) master weights of this rank's shard.
+    """
+    incoming = [rank_grad(shard_numel, sigma, "bf16", grad_seed(step, j, base), device)
+                for j in range(nranks)]
+    peer_shards = [None if j == rank else
+                   master_init(shard_numel, seed=base + 100 + j, device=device).to(torch.bfloat16)
+                   for j in range(nranks)]
+    partials = peer_partials(npieces, piece, sigma / nranks ** 0.5, seed=base + 99,
+                             device=device)
+    shard_master = master_init(shard_numel, seed=base + 7 + rank, device=device)
+    return dict(incoming=incoming, peer_shards=peer_shards, partials=partials,
+                shard_master=shard_master)
