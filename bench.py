@@ -28,6 +28,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
+COUNTERS = os.path.join(ROOT, "profiles", "llama7b_onerank_step_counters.txt")
+KERNEL_SRC = os.path.join(ROOT, "gradient_reduce_zero_amd", "csrc", "grz.hip")
+KERNEL_NAMES = {"reduce": "rs_mean_kernel", "adamw": "adamw_kernel", "gather": "gather_kernel"}
 
 
 def log(msg):
@@ -60,6 +63,27 @@ def bytes_per_owned(n, grad_bytes=2):
         "adamw": 4 * 4 + 3 * 4 + 2,          # mean+master+m+v read; master+m+v+bf16 written
         "gather": 2 * (n - 1) * grad_bytes,  # N-1 peer bf16 shards read and written
     }
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or None
+    when the kernel source has changed since the counters were taken."""
+    import hashlib
+
+    try:
+        text = open(COUNTERS).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if "=" in line:
+            k, _, v = line.partition("=")
+            vals[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if vals.get("kernel_source_sha256") != sha or KERNEL_NAMES[kernel] not in vals:
+        return None
+    return int(vals[KERNEL_NAMES[kernel]])
 
 
 def cpu_baseline(setup, sample, seed=0):
@@ -111,8 +135,12 @@ def main():
     ap.add_argument("--config", default="llama_7b",
                     choices=["llama_7b", "gpt2_1p5b", "gpt2_124m", "char_gpt"])
     ap.add_argument("--nranks", type=int, default=8)
-    ap.add_argument("--cpu-sample", type=int, default=1 << 23)
+    ap.add_argument("--cpu-sample", type=int, default=1 << 28)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="first run a plain 2 GiB bf16 copy (the library's all-gather "
+                         "kernel with one rank and one replica) as the reference of known "
+                         "size for hardware byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -127,6 +155,16 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate:
+        numel = 1 << 30  # 2 GiB of bf16 read, 2 GiB written
+        src = torch.ones(numel, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            grz.zero1_all_gather([src], [(0, numel)], [dst])
+        torch.cuda.synchronize()
+        assert bool(torch.equal(src, dst))
+        log(f"calibration copy: 3 launches of {2 * numel} bytes read + {2 * numel} written")
+        del src, dst
     log(f"setting up {args.config} one-rank share, N={args.nranks}")
     setup = onerank_setup(args.config, args.nranks, 0, dev)
     pipe, inp = setup["pipe"], setup["inp"]
@@ -215,7 +253,10 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": gbps[dominant] / PEAK_HBM_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(dominant) if args.config == "llama_7b" and n == 8
+            else None,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                            "copy-calibrated; profiles/llama7b_onerank_step_counters.txt)",
             "bytes_per_owned_param": bpo[dominant],
         },
     }

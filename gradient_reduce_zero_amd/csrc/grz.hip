@@ -35,14 +35,14 @@
 namespace {
 
 constexpr int kThreads = 256;          // 4 waves of 64
-constexpr int kGroup = 8;              // consecutive elements a lane handles at once
-constexpr int kGroupsPerLane = GRZ_PIECE / (kThreads * kGroup);  // 2
 constexpr int kMaxSegs = 64;           // segments per launch (kernel-argument budget)
 constexpr int kReduceFan = 4096;       // values one block folds in the norm tree
 
-static_assert(kGroupsPerLane * kThreads * kGroup == GRZ_PIECE, "piece shape");
+static_assert(GRZ_PIECE % (kThreads * 8) == 0, "piece shape");
 
-int g_max_blocks = 2048;               // grid width of the grid-stride kernels
+// Grid width cap of the grid-stride kernels.  Measured on MI355X: one
+// workgroup per tile (no cap in practice) streams fastest.
+int g_max_blocks = 1 << 30;
 
 // One contiguous run of work: `len` elements read at `src` and written at
 // `dst`, whose first tile is `tile0` of the launch and first norm piece is
@@ -81,37 +81,89 @@ __device__ __forceinline__ float widen1(const uint16_t* p) {
 __device__ __forceinline__ float widen1(const float* p) { return *p; }
 __device__ __forceinline__ double widen1(const double* p) { return *p; }
 
-__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[kGroup]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+// Global accesses.  Every access instruction of a wave covers one contiguous
+// run: lane l touches bytes [w*l, w*(l+1)) of it, w = 8 or 16.  (Measured on
+// MI355X: non-temporal 16-byte stores that leave 16-byte holes between lanes,
+// to be filled by a second instruction, stream at well under half the rate
+// of contiguous ones.)  So a lane owns G consecutive fp32 (G = 4) or fp64
+// (G = 2) values of an fp32/fp64 stream per access, and the matching G bf16
+// values of a bf16 stream (8 bytes).
+//
+// Every stream is touched once per step and is far larger than the caches.
+// Each kernel picks a cache policy for its loads and stores (bit 0:
+// non-temporal loads, bit 1: non-temporal stores), chosen by measurement; it
+// changes speed only, never a result bit.
+#ifndef GRZ_RS_POLICY
+#define GRZ_RS_POLICY 3
+#endif
+#ifndef GRZ_ADAM_POLICY
+#define GRZ_ADAM_POLICY 3
+#endif
+#ifndef GRZ_AG_POLICY
+#define GRZ_AG_POLICY 3
+#endif
+constexpr int kNtLoad = 1, kNtStore = 2;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int P, typename V>
+__device__ __forceinline__ V ldv(const void* p) {
+  if constexpr ((P & kNtLoad) != 0)
+    return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  else
+    return *reinterpret_cast<const V*>(p);
+}
+
+template <int P, typename V>
+__device__ __forceinline__ void stv(void* p, V v) {
+  if constexpr ((P & kNtStore) != 0)
+    __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+  else
+    *reinterpret_cast<V*>(p) = v;
+}
+
+// Elements per lane per access for an accumulation type.
+template <typename Acc> struct Geo {
+  static constexpr int G = 16 / static_cast<int>(sizeof(Acc));
+  static constexpr int K = GRZ_PIECE / (kThreads * G);  // accesses per lane per tile
+};
+
+template <int P>
+__device__ __forceinline__ void loadg(const uint16_t* p, float (&x)[4]) {
+  const u32x2 u = ldv<P, u32x2>(p);
+  x[0] = __uint_as_float(u[0] << 16);
+  x[1] = __uint_as_float(u[0] & 0xffff0000u);
+  x[2] = __uint_as_float(u[1] << 16);
+  x[3] = __uint_as_float(u[1] & 0xffff0000u);
+}
+template <int P>
+__device__ __forceinline__ void loadg(const float* p, float (&x)[4]) {
+  const u32x4 u = ldv<P, u32x4>(p);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16);
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
+  for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(u[i]);
 }
-__device__ __forceinline__ void load8(const float* p, float (&x)[kGroup]) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0];
-  const float4 b = reinterpret_cast<const float4*>(p)[1];
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+template <int P>
+__device__ __forceinline__ void loadg(const double* p, double (&x)[2]) {
+  const u32x4 u = ldv<P, u32x4>(p);
+  x[0] = __hiloint2double(static_cast<int>(u[1]), static_cast<int>(u[0]));
+  x[1] = __hiloint2double(static_cast<int>(u[3]), static_cast<int>(u[2]));
 }
-__device__ __forceinline__ void load8(const double* p, double (&x)[kGroup]) {
+template <int P>
+__device__ __forceinline__ void storeg(float* p, const float (&x)[4]) {
+  u32x4 u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const double2 d = reinterpret_cast<const double2*>(p)[i];
-    x[2 * i] = d.x;
-    x[2 * i + 1] = d.y;
-  }
+  for (int i = 0; i < 4; ++i) u[i] = __float_as_uint(x[i]);
+  stv<P>(p, u);
 }
-__device__ __forceinline__ void store8(float* p, const float (&x)[kGroup]) {
-  reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
-  reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
-}
-__device__ __forceinline__ void store8(double* p, const double (&x)[kGroup]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    reinterpret_cast<double2*>(p)[i] = make_double2(x[2 * i], x[2 * i + 1]);
+template <int P>
+__device__ __forceinline__ void storeg(double* p, const double (&x)[2]) {
+  u32x4 u;
+  u[0] = static_cast<uint32_t>(__double2loint(x[0]));
+  u[1] = static_cast<uint32_t>(__double2hiint(x[0]));
+  u[2] = static_cast<uint32_t>(__double2loint(x[1]));
+  u[3] = static_cast<uint32_t>(__double2hiint(x[1]));
+  stv<P>(p, u);
 }
 
 // Round-to-nearest-even of a binary32 to bf16: add half an ulp of the kept
@@ -142,8 +194,9 @@ __device__ __forceinline__ double block_sum_fixed(double s, double* lds) {
 
 // ---------------------------------------------------------------------------
 // K1: reduce-scatter-mean.  One tile = one norm piece of GRZ_PIECE elements
-// of one chunk; lane l owns groups l and l + 256 (8 elements each) of it, so
-// every 16-byte load of a wave is one contiguous 1 KiB run.
+// of one chunk, one workgroup.  Access k (0 <= k < K) of lane l covers the G
+// elements at k*256*G + l*G of the tile, so each wave instruction reads one
+// contiguous run per rank and writes one contiguous run of the mean.
 
 template <typename TIn>
 struct RsArgs {
@@ -158,38 +211,38 @@ struct RsArgs {
   Seg seg[kMaxSegs];
 };
 
-// Fold one group of 8 elements over the ranks in ring order starting at
-// rank c; NR > 0 fixes N at compile time so that every rank's load is in
-// flight before the first add.
-template <typename TIn, int NR>
+// Fold one access's G elements over the ranks in ring order starting at rank
+// c; NR > 0 fixes N at compile time so that every rank's load is in flight
+// before the first add.
+template <typename TIn, int NR, typename Acc = typename AccOf<TIn>::type,
+          int G = Geo<Acc>::G>
 __device__ __forceinline__ void fold_vec(const RsArgs<TIn>& a, int c, int64_t off,
-                                         typename AccOf<TIn>::type (&acc)[kGroup]) {
-  using Acc = typename AccOf<TIn>::type;
+                                         Acc (&acc)[G]) {
   const TIn* const* rank = a.rank;
   if constexpr (NR > 0) {
-    Acc x[NR][kGroup];
+    Acc x[NR][G];
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
       int r = c + j;
       r = r >= NR ? r - NR : r;
-      load8(rank[r] + off, x[j]);
+      loadg<GRZ_RS_POLICY>(rank[r] + off, x[j]);
     }
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) acc[k] = x[0][k];
+    for (int k = 0; k < G; ++k) acc[k] = x[0][k];
 #pragma unroll
     for (int j = 1; j < NR; ++j)
 #pragma unroll
-      for (int k = 0; k < kGroup; ++k) acc[k] = x[j][k] + acc[k];
+      for (int k = 0; k < G; ++k) acc[k] = x[j][k] + acc[k];
   } else {
     const int n = a.nranks;
-    load8(rank[c] + off, acc);
+    loadg<GRZ_RS_POLICY>(rank[c] + off, acc);
     for (int j = 1; j < n; ++j) {
       int r = c + j;
       r = r >= n ? r - n : r;
-      Acc x[kGroup];
-      load8(rank[r] + off, x);
+      Acc x[G];
+      loadg<GRZ_RS_POLICY>(rank[r] + off, x);
 #pragma unroll
-      for (int k = 0; k < kGroup; ++k) acc[k] = x[k] + acc[k];
+      for (int k = 0; k < G; ++k) acc[k] = x[k] + acc[k];
     }
   }
 }
@@ -211,6 +264,8 @@ __device__ __forceinline__ typename AccOf<TIn>::type fold_one(const RsArgs<TIn>&
 template <typename TIn, int NR>
 __global__ __launch_bounds__(kThreads) void rs_mean_kernel(const RsArgs<TIn> a) {
   using Acc = typename AccOf<TIn>::type;
+  constexpr int G = Geo<Acc>::G;
+  constexpr int K = Geo<Acc>::K;
   __shared__ double lds[kThreads / 64];
   const int n = NR > 0 ? NR : a.nranks;
   const Acc nf = static_cast<Acc>(n);
@@ -225,25 +280,25 @@ __global__ __launch_bounds__(kThreads) void rs_mean_kernel(const RsArgs<TIn> a) 
     const int c = s.chunk;
     double sq = 0.0;
 #pragma unroll
-    for (int gi = 0; gi < kGroupsPerLane; ++gi) {
-      const int64_t e = e0 + static_cast<int64_t>(gi * kThreads + lane) * kGroup;
-      const int64_t rel = e - e0;
-      if (s.vec && rel + kGroup <= left) {
-        Acc acc[kGroup];
+    for (int k = 0; k < K; ++k) {
+      const int64_t rel = static_cast<int64_t>(k * kThreads + lane) * G;
+      const int64_t e = e0 + rel;
+      if (s.vec && rel + G <= left) {
+        Acc acc[G];
         fold_vec<TIn, NR>(a, c, s.src + e, acc);
 #pragma unroll
-        for (int k = 0; k < kGroup; ++k) {
-          if (a.average) acc[k] = a.pow2 ? acc[k] * inv : acc[k] / nf;
-          sq = __fma_rn(static_cast<double>(acc[k]), static_cast<double>(acc[k]), sq);
+        for (int i = 0; i < G; ++i) {
+          if (a.average) acc[i] = a.pow2 ? acc[i] * inv : acc[i] / nf;
+          sq = __fma_rn(static_cast<double>(acc[i]), static_cast<double>(acc[i]), sq);
         }
-        store8(a.out + s.dst + e, acc);
+        storeg<GRZ_RS_POLICY>(a.out + s.dst + e, acc);
       } else {
-        for (int k = 0; k < kGroup; ++k) {
-          if (rel + k >= left) break;
-          Acc v = fold_one<TIn, NR>(a, c, s.src + e + k);
+        for (int i = 0; i < G; ++i) {
+          if (rel + i >= left) break;
+          Acc v = fold_one<TIn, NR>(a, c, s.src + e + i);
           if (a.average) v = a.pow2 ? v * inv : v / nf;
           sq = __fma_rn(static_cast<double>(v), static_cast<double>(v), sq);
-          a.out[s.dst + e + k] = v;
+          a.out[s.dst + e + i] = v;
         }
       }
     }
@@ -326,7 +381,12 @@ __device__ __forceinline__ void adamw1(float& w, float& m, float& v, float g, fl
   w = w - lr * (u + wd * w);
 }
 
+// Access k (0 <= k < 4) of lane l covers the 4 elements at k*1024 + 4*l of
+// the tile: 16-byte accesses of the fp32 streams, 8-byte bf16 stores, each
+// wave instruction one contiguous run.
 __global__ __launch_bounds__(kThreads) void adamw_kernel(const AdamArgs a) {
+  constexpr int G = 4;
+  constexpr int K = GRZ_PIECE / (kThreads * G);
   const float scale = a.scale != nullptr ? *a.scale : 1.0f;
   const float omb1 = 1.0f - a.b1;  // exact: 1/2 <= b1 <= 1 (Sterbenz)
   const float omb2 = 1.0f - a.b2;
@@ -337,34 +397,34 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(const AdamArgs a) {
     const int64_t e0 = (tile - s.tile0) * GRZ_PIECE;
     const int64_t left = s.len - e0;
 #pragma unroll
-    for (int gi = 0; gi < kGroupsPerLane; ++gi) {
-      const int64_t rel = static_cast<int64_t>(gi * kThreads + lane) * kGroup;
+    for (int k = 0; k < K; ++k) {
+      const int64_t rel = static_cast<int64_t>(k * kThreads + lane) * G;
       const int64_t e = e0 + rel;
-      if (s.vec && rel + kGroup <= left) {
+      if (s.vec && rel + G <= left) {
         const int64_t i = s.src + e;
-        float g[kGroup], w[kGroup], m[kGroup], v[kGroup];
-        load8(a.grad + i, g);
-        load8(a.master + i, w);
-        load8(a.m + i, m);
-        load8(a.v + i, v);
-        uint32_t b[kGroup];
+        float g[G], w[G], m[G], v[G];
+        loadg<GRZ_ADAM_POLICY>(a.grad + i, g);
+        loadg<GRZ_ADAM_POLICY>(a.master + i, w);
+        loadg<GRZ_ADAM_POLICY>(a.m + i, m);
+        loadg<GRZ_ADAM_POLICY>(a.v + i, v);
+        uint32_t b[G];
 #pragma unroll
-        for (int k = 0; k < kGroup; ++k) {
-          adamw1(w[k], m[k], v[k], g[k] * scale, a.lr, a.b1, omb1, a.b2, omb2, a.eps, a.wd,
+        for (int j = 0; j < G; ++j) {
+          adamw1(w[j], m[j], v[j], g[j] * scale, a.lr, a.b1, omb1, a.b2, omb2, a.eps, a.wd,
                  a.bc1, a.bc2);
-          b[k] = bf16_rne(w[k]);
+          b[j] = bf16_rne(w[j]);
         }
-        store8(a.master + i, w);
-        store8(a.m + i, m);
-        store8(a.v + i, v);
-        const uint4 packed = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16),
-                                        b[4] | (b[5] << 16), b[6] | (b[7] << 16));
-        for (int r = 0; r < a.nrep; ++r)
-          *reinterpret_cast<uint4*>(a.rep[r] + s.dst + e) = packed;
+        storeg<GRZ_ADAM_POLICY>(a.master + i, w);
+        storeg<GRZ_ADAM_POLICY>(a.m + i, m);
+        storeg<GRZ_ADAM_POLICY>(a.v + i, v);
+        u32x2 packed;
+        packed[0] = b[0] | (b[1] << 16);
+        packed[1] = b[2] | (b[3] << 16);
+        for (int r = 0; r < a.nrep; ++r) stv<GRZ_ADAM_POLICY>(a.rep[r] + s.dst + e, packed);
       } else {
-        for (int k = 0; k < kGroup; ++k) {
-          if (rel + k >= left) break;
-          const int64_t i = s.src + e + k;
+        for (int j = 0; j < G; ++j) {
+          if (rel + j >= left) break;
+          const int64_t i = s.src + e + j;
           float w = a.master[i], m = a.m[i], v = a.v[i];
           adamw1(w, m, v, a.grad[i] * scale, a.lr, a.b1, omb1, a.b2, omb2, a.eps, a.wd, a.bc1,
                  a.bc2);
@@ -372,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(const AdamArgs a) {
           a.m[i] = m;
           a.v[i] = v;
           const uint16_t b = static_cast<uint16_t>(bf16_rne(w));
-          for (int r = 0; r < a.nrep; ++r) a.rep[r][s.dst + e + k] = b;
+          for (int r = 0; r < a.nrep; ++r) a.rep[r][s.dst + e + j] = b;
         }
       }
     }
@@ -391,7 +451,11 @@ struct GatherArgs {
   Seg seg[kMaxSegs];
 };
 
+// Access k (0 <= k < 2) of lane l copies the 8 elements (16 bytes) at
+// k*2048 + 8*l of the tile.
 __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherArgs a) {
+  constexpr int G = 8;
+  constexpr int K = GRZ_PIECE / (kThreads * G);
   const int lane = threadIdx.x;
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const Seg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
@@ -399,17 +463,17 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherArgs a) {
     const int64_t left = s.len - e0;
     const uint16_t* src = a.shard[s.chunk];
 #pragma unroll
-    for (int gi = 0; gi < kGroupsPerLane; ++gi) {
-      const int64_t rel = static_cast<int64_t>(gi * kThreads + lane) * kGroup;
+    for (int k = 0; k < K; ++k) {
+      const int64_t rel = static_cast<int64_t>(k * kThreads + lane) * G;
       const int64_t e = e0 + rel;
-      if (s.vec && rel + kGroup <= left) {
-        const uint4 u = *reinterpret_cast<const uint4*>(src + s.src + e);
-        for (int r = 0; r < a.nrep; ++r) *reinterpret_cast<uint4*>(a.rep[r] + s.dst + e) = u;
+      if (s.vec && rel + G <= left) {
+        const u32x4 u = ldv<GRZ_AG_POLICY, u32x4>(src + s.src + e);
+        for (int r = 0; r < a.nrep; ++r) stv<GRZ_AG_POLICY>(a.rep[r] + s.dst + e, u);
       } else {
-        for (int k = 0; k < kGroup; ++k) {
-          if (rel + k >= left) break;
-          const uint16_t u = src[s.src + e + k];
-          for (int r = 0; r < a.nrep; ++r) a.rep[r][s.dst + e + k] = u;
+        for (int j = 0; j < G; ++j) {
+          if (rel + j >= left) break;
+          const uint16_t u = src[s.src + e + j];
+          for (int r = 0; r < a.nrep; ++r) a.rep[r][s.dst + e + j] = u;
         }
       }
     }
@@ -510,10 +574,12 @@ int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>
   using Acc = typename AccOf<TIn>::type;
   static RsArgs<TIn> proto;  // zero-initialised template
   RsArgs<TIn> args = proto;
+  // One access moves G elements: 16 bytes of the mean, G * sizeof(TIn) of each input.
+  constexpr size_t in_bytes = Geo<Acc>::G * sizeof(TIn);
   bool vec_base = aligned(mean_out, 16);
   for (int j = 0; j < n; ++j) {
     if (!aligned(rank_grads[j], sizeof(TIn))) return GRZ_EALIGN;
-    vec_base = vec_base && aligned(rank_grads[j], 16);
+    vec_base = vec_base && aligned(rank_grads[j], in_bytes);
     args.rank[j] = static_cast<const TIn*>(rank_grads[j]);
   }
   args.out = static_cast<Acc*>(mean_out);
@@ -531,7 +597,7 @@ int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>
     s.len = p.len;
     s.piece0 = p.piece0;
     s.chunk = p.chunk;
-    s.vec = vec_base && (s.src * sizeof(TIn)) % 16 == 0 && (s.dst * sizeof(Acc)) % 16 == 0;
+    s.vec = vec_base && (s.src * sizeof(TIn)) % in_bytes == 0 && (s.dst * sizeof(Acc)) % 16 == 0;
     segs.push_back(s);
   }
   switch (n) {
@@ -574,7 +640,7 @@ const char* grz_strerror(int status) {
 }
 
 int grz_set_max_blocks(int blocks) {
-  if (blocks < 1 || blocks > (1 << 20)) return GRZ_EINVAL;
+  if (blocks < 1 || blocks > (1 << 30)) return GRZ_EINVAL;
   g_max_blocks = blocks;
   return GRZ_OK;
 }
@@ -728,7 +794,7 @@ static int adamw_common(float* master, float* m, float* v, const float* mean_gra
   for (int r = 0; r < nreplicas; ++r) {
     if (replicas[r] == nullptr) return GRZ_EINVAL;
     if (!aligned(replicas[r], 2)) return GRZ_EALIGN;
-    vec_base = vec_base && aligned(replicas[r], 16);
+    vec_base = vec_base && aligned(replicas[r], 8);
     a.rep[r] = replicas[r];
   }
   a.nrep = nreplicas;
@@ -747,7 +813,7 @@ static int adamw_common(float* master, float* m, float* v, const float* mean_gra
     s.dst = p.global;
     s.len = p.len;
     s.chunk = p.chunk;
-    s.vec = vec_base && s.src % 4 == 0 && s.dst % 8 == 0;
+    s.vec = vec_base && s.src % 4 == 0 && s.dst % 4 == 0;
     segs.push_back(s);
   }
   return launch_batches(segs, a, adamw_kernel, stream);
