@@ -37,7 +37,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def onerank_setup(name, n, rank, device):
+def onerank_setup(name, n, rank, device, reduce_flags=0):
     import torch  # noqa: F401
 
     import gradient_reduce_zero_amd as grz
@@ -50,7 +50,8 @@ def onerank_setup(name, n, rank, device):
     shard = grz.dp_shard_numel(buckets, n, chunk)
     npieces = grz.dp_piece_count(buckets, n)
     inp = onerank_inputs(shard, n, rank, npieces, grz.GRZ_PIECE, device=device)
-    pipe = grz.Zero1OneRank(buckets, n, rank, inp["shard_master"], device=device, arena_numel=p)
+    pipe = grz.Zero1OneRank(buckets, n, rank, inp["shard_master"], device=device, arena_numel=p,
+                            reduce_flags=reduce_flags)
     pipe.norm.partials.copy_(inp["partials"])
     return dict(arena=a, p=p, n=n, rank=rank, chunk=chunk, shard=shard, buckets=buckets,
                 npieces=npieces, inp=inp, pipe=pipe)
@@ -86,7 +87,7 @@ def measured_traffic(kernel):
     return int(vals[KERNEL_NAMES[kernel]])
 
 
-def cpu_baseline(setup, sample, seed=0):
+def cpu_baseline(setup, sample, wire=None):
     """The CPU oracle on a bounded sample of the same step (reported, not a target)."""
     import math
 
@@ -108,7 +109,7 @@ def cpu_baseline(setup, sample, seed=0):
     npieces_sample = math.ceil((hi - lo) / 4096)
     z = np.zeros_like(w)
     t0 = time.perf_counter()
-    mean = chunk_mean([widen(x, "bf16") for x in g], chunk)
+    mean = chunk_mean([widen(x, "bf16") for x in g], chunk, wire=wire)
     sq = grad_sqnorm(mean, extra=partials[:npieces_sample * (n - 1)])
     scale = clip_scale(sq, 1.0)
     w1, m1, v1 = adamw(w, z, z, mean * scale, **Hyper().scalars(1))
@@ -135,8 +136,11 @@ def main():
     ap.add_argument("--config", default="llama_7b",
                     choices=["llama_7b", "gpt2_1p5b", "gpt2_124m", "char_gpt"])
     ap.add_argument("--nranks", type=int, default=8)
-    ap.add_argument("--cpu-sample", type=int, default=1 << 28)
+    ap.add_argument("--cpu-sample", type=int, default=1 << 29)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--wire", choices=["fp32", "bf16"], default="fp32",
+                    help="precision of the ring's partial sums: fp32 accumulation (default) "
+                         "or a bf16 wire that rounds every hop")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 2 GiB bf16 copy (the library's all-gather "
                          "kernel with one rank and one replica) as the reference of known "
@@ -166,7 +170,8 @@ def main():
         log(f"calibration copy: 3 launches of {2 * numel} bytes read + {2 * numel} written")
         del src, dst
     log(f"setting up {args.config} one-rank share, N={args.nranks}")
-    setup = onerank_setup(args.config, args.nranks, 0, dev)
+    flags = grz.GRZ_BF16_WIRE if args.wire == "bf16" else 0
+    setup = onerank_setup(args.config, args.nranks, 0, dev, reduce_flags=flags)
     pipe, inp = setup["pipe"], setup["inp"]
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -238,7 +243,7 @@ def main():
             "arena_params": setup["p"], "owned_params": owned, "nranks_simulated": n,
             "rank": 0, "owned_chunk": setup["chunk"], "buckets": len(setup["buckets"]),
             "grad_dtype": "bf16", "state_dtype": "fp32", "weights_dtype": "bf16",
-            "clip": 1.0,
+            "clip": 1.0, "wire": args.wire,
         },
         "achieved_GBps": step_gbps,
         "pct_of_peak_hbm": 100.0 * step_gbps / PEAK_HBM_GBPS,
@@ -262,7 +267,7 @@ def main():
     }
     if not args.no_cpu:
         log(f"timing the CPU oracle on {args.cpu_sample} parameters")
-        cb = cpu_baseline(setup, args.cpu_sample)
+        cb = cpu_baseline(setup, args.cpu_sample, wire="bf16" if args.wire == "bf16" else None)
         out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
     print(json.dumps(out), flush=True)
 

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libgrz.so")
 
 GRZ_OK, GRZ_EINVAL, GRZ_EINDIVISIBLE, GRZ_EALIGN, GRZ_EHIP, GRZ_ERANGE = range(6)
 GRZ_F32, GRZ_BF16, GRZ_F64 = 0, 1, 2
-GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT = 1, 2, 4
+GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT, GRZ_BF16_WIRE = 1, 2, 4, 8
 GRZ_MAX_RANKS = 16
 GRZ_PIECE = 4096
 

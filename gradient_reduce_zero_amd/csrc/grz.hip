@@ -177,6 +177,11 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// The value a bf16 wire carries: x rounded to bf16 (nearest even), widened back.
+__device__ __forceinline__ float bf16_wire(float x) {
+  return __uint_as_float(bf16_rne(x) << 16);
+}
+
 // Sum of one double per thread over the 256-thread block, in a fixed tree:
 // a xor butterfly inside each wave (every lane ends with the same balanced
 // tree sum of its wave) then (w0 + w1) + (w2 + w3).  The shape depends on
@@ -214,7 +219,7 @@ struct RsArgs {
 // Fold one access's G elements over the ranks in ring order starting at rank
 // c; NR > 0 fixes N at compile time so that every rank's load is in flight
 // before the first add.
-template <typename TIn, int NR, typename Acc = typename AccOf<TIn>::type,
+template <typename TIn, int NR, bool WIRE, typename Acc = typename AccOf<TIn>::type,
           int G = Geo<Acc>::G>
 __device__ __forceinline__ void fold_vec(const RsArgs<TIn>& a, int c, int64_t off,
                                          Acc (&acc)[G]) {
@@ -232,7 +237,10 @@ __device__ __forceinline__ void fold_vec(const RsArgs<TIn>& a, int c, int64_t of
 #pragma unroll
     for (int j = 1; j < NR; ++j)
 #pragma unroll
-      for (int k = 0; k < G; ++k) acc[k] = x[j][k] + acc[k];
+      for (int k = 0; k < G; ++k) {
+        acc[k] = x[j][k] + acc[k];
+        if constexpr (WIRE) acc[k] = bf16_wire(acc[k]);
+      }
   } else {
     const int n = a.nranks;
     loadg<GRZ_RS_POLICY>(rank[c] + off, acc);
@@ -242,12 +250,15 @@ __device__ __forceinline__ void fold_vec(const RsArgs<TIn>& a, int c, int64_t of
       Acc x[G];
       loadg<GRZ_RS_POLICY>(rank[r] + off, x);
 #pragma unroll
-      for (int k = 0; k < G; ++k) acc[k] = x[k] + acc[k];
+      for (int k = 0; k < G; ++k) {
+        acc[k] = x[k] + acc[k];
+        if constexpr (WIRE) acc[k] = bf16_wire(acc[k]);
+      }
     }
   }
 }
 
-template <typename TIn, int NR>
+template <typename TIn, int NR, bool WIRE>
 __device__ __forceinline__ typename AccOf<TIn>::type fold_one(const RsArgs<TIn>& a, int c,
                                                               int64_t off) {
   using Acc = typename AccOf<TIn>::type;
@@ -257,11 +268,15 @@ __device__ __forceinline__ typename AccOf<TIn>::type fold_one(const RsArgs<TIn>&
     int r = c + j;
     r = r >= n ? r - n : r;
     acc = widen1(a.rank[r] + off) + acc;
+    if constexpr (WIRE) acc = bf16_wire(acc);
   }
   return acc;
 }
 
-template <typename TIn, int NR>
+// WIRE (bf16 gradients only) rounds every partial sum of the fold to bf16, as a
+// ring whose wire format is bf16 does once per hop ("13.5 Multi-GPU from
+// First Principles", exercise 8).
+template <typename TIn, int NR, bool WIRE>
 __global__ __launch_bounds__(kThreads) void rs_mean_kernel(const RsArgs<TIn> a) {
   using Acc = typename AccOf<TIn>::type;
   constexpr int G = Geo<Acc>::G;
@@ -285,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void rs_mean_kernel(const RsArgs<TIn> a) 
       const int64_t e = e0 + rel;
       if (s.vec && rel + G <= left) {
         Acc acc[G];
-        fold_vec<TIn, NR>(a, c, s.src + e, acc);
+        fold_vec<TIn, NR, WIRE>(a, c, s.src + e, acc);
 #pragma unroll
         for (int i = 0; i < G; ++i) {
           if (a.average) acc[i] = a.pow2 ? acc[i] * inv : acc[i] / nf;
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void rs_mean_kernel(const RsArgs<TIn> a) 
       } else {
         for (int i = 0; i < G; ++i) {
           if (rel + i >= left) break;
-          Acc v = fold_one<TIn, NR>(a, c, s.src + e + i);
+          Acc v = fold_one<TIn, NR, WIRE>(a, c, s.src + e + i);
           if (a.average) v = a.pow2 ? v * inv : v / nf;
           sq = __fma_rn(static_cast<double>(v), static_cast<double>(v), sq);
           a.out[s.dst + e + i] = v;
@@ -499,7 +514,7 @@ int check_plan(const grz_bucket* buckets, int nbuckets, int nranks, int chunk, i
   if (nranks < 1 || nranks > GRZ_MAX_RANKS) return GRZ_EINVAL;
   if (nbuckets < 0 || (nbuckets > 0 && buckets == nullptr)) return GRZ_EINVAL;
   if (chunk < -1 || chunk >= nranks) return GRZ_EINVAL;
-  if (flags & ~(GRZ_SUM | GRZ_UNEVEN | GRZ_IN_COMPACT)) return GRZ_EINVAL;
+  if (flags & ~(GRZ_SUM | GRZ_UNEVEN | GRZ_IN_COMPACT | GRZ_BF16_WIRE)) return GRZ_EINVAL;
   for (int b = 0; b < nbuckets; ++b) {
     if (buckets[b].offset < 0 || buckets[b].length < 0) return GRZ_ERANGE;
     if (buckets[b].length > (INT64_MAX >> 4) - buckets[b].offset) return GRZ_ERANGE;
@@ -564,8 +579,11 @@ int launch_batches(std::vector<Seg>& segs, Args& args,
 }
 
 template <typename TIn, int NR>
-int rs_launch(std::vector<Seg>& segs, RsArgs<TIn>& args, hipStream_t stream) {
-  return launch_batches(segs, args, rs_mean_kernel<TIn, NR>, stream);
+int rs_launch(std::vector<Seg>& segs, RsArgs<TIn>& args, bool wire, hipStream_t stream) {
+  if constexpr (sizeof(TIn) == 2) {
+    if (wire) return launch_batches(segs, args, rs_mean_kernel<TIn, NR, true>, stream);
+  }
+  return launch_batches(segs, args, rs_mean_kernel<TIn, NR, false>, stream);
 }
 
 template <typename TIn>
@@ -600,12 +618,13 @@ int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>
     s.vec = vec_base && (s.src * sizeof(TIn)) % in_bytes == 0 && (s.dst * sizeof(Acc)) % 16 == 0;
     segs.push_back(s);
   }
+  const bool wire = (flags & GRZ_BF16_WIRE) != 0;
   switch (n) {
-    case 1: return rs_launch<TIn, 1>(segs, args, stream);
-    case 2: return rs_launch<TIn, 2>(segs, args, stream);
-    case 4: return rs_launch<TIn, 4>(segs, args, stream);
-    case 8: return rs_launch<TIn, 8>(segs, args, stream);
-    default: return rs_launch<TIn, 0>(segs, args, stream);
+    case 1: return rs_launch<TIn, 1>(segs, args, wire, stream);
+    case 2: return rs_launch<TIn, 2>(segs, args, wire, stream);
+    case 4: return rs_launch<TIn, 4>(segs, args, wire, stream);
+    case 8: return rs_launch<TIn, 8>(segs, args, wire, stream);
+    default: return rs_launch<TIn, 0>(segs, args, wire, stream);
   }
 }
 
@@ -712,6 +731,7 @@ int dp_reduce_scatter_mean(const void* const* rank_grads, int nranks, int dtype,
   if (st != GRZ_OK) return st;
   if (rank_grads == nullptr || mean_out == nullptr) return GRZ_EINVAL;
   if ((flags & GRZ_IN_COMPACT) && chunk < 0) return GRZ_EINVAL;
+  if ((flags & GRZ_BF16_WIRE) && dtype != GRZ_BF16) return GRZ_EINVAL;
   for (int j = 0; j < nranks; ++j)
     if (rank_grads[j] == nullptr) return GRZ_EINVAL;
   if (piece_sqnorm != nullptr && !aligned(piece_sqnorm, 8)) return GRZ_EALIGN;
@@ -836,7 +856,7 @@ int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad
                        uint16_t* const* replicas, int nreplicas, hipStream_t stream) {
   const int st = check_plan(buckets, nbuckets, nranks, chunk, flags);
   if (st != GRZ_OK) return st;
-  if (flags & (GRZ_SUM | GRZ_IN_COMPACT)) return GRZ_EINVAL;
+  if (flags & (GRZ_SUM | GRZ_IN_COMPACT | GRZ_BF16_WIRE)) return GRZ_EINVAL;
   std::vector<PlanSeg> ps;
   if (chunk >= 0) {
     ps = plan_segments(buckets, nbuckets, nranks, chunk);

@@ -58,10 +58,11 @@ class _Norm:
 class Zero1AllRanks:
     """ZeRO-1 step of N simulated ranks over a bucket plan."""
 
-    def __init__(self, buckets, nranks, master, hyper=None, device="cuda"):
+    def __init__(self, buckets, nranks, master, hyper=None, device="cuda", reduce_flags=0):
         self.buckets = [(int(o), int(l)) for o, l in buckets]
         self.n = nranks
         self.hyper = hyper or Hyper()
+        self.reduce_flags = reduce_flags
         self.numel = master.numel()
         master = master.to(device=device, dtype=torch.float32)
         self.chunks = [owned_chunk(r, nranks) for r in range(nranks)]
@@ -77,7 +78,7 @@ class Zero1AllRanks:
     def step(self, rank_grads, t, stream=None):
         for c, mean in zip(self.chunks, self.means):
             B.dp_reduce_scatter_mean(rank_grads, self.buckets, c, mean, self.norm.partials,
-                                     stream=stream)
+                                     flags=self.reduce_flags, stream=stream)
         self.norm.run(self.hyper.max_norm, stream)
         args = B.adamw_args(**step_scalars(self.hyper, t))
         for c, (w, m, v), mean in zip(self.chunks, self.state, self.means):
@@ -88,10 +89,11 @@ class Zero1AllRanks:
 class DDPStep:
     """Plain data-parallel step as one replica computes it."""
 
-    def __init__(self, buckets, nranks, master, hyper=None, device="cuda"):
+    def __init__(self, buckets, nranks, master, hyper=None, device="cuda", reduce_flags=0):
         self.buckets = [(int(o), int(l)) for o, l in buckets]
         self.n = nranks
         self.hyper = hyper or Hyper()
+        self.reduce_flags = reduce_flags
         w = master.to(device=device, dtype=torch.float32).clone()
         self.state = (w, torch.zeros_like(w), torch.zeros_like(w))
         self.mean = torch.zeros_like(w)
@@ -100,7 +102,7 @@ class DDPStep:
 
     def step(self, rank_grads, t, stream=None):
         B.dp_reduce_scatter_mean(rank_grads, self.buckets, -1, self.mean, self.norm.partials,
-                                 stream=stream)
+                                 flags=self.reduce_flags, stream=stream)
         self.norm.run(self.hyper.max_norm, stream)
         args = B.adamw_args(**step_scalars(self.hyper, t))
         w, m, v = self.state
@@ -122,8 +124,9 @@ class Zero1OneRank:
     """
 
     def __init__(self, buckets, nranks, rank, shard_master, hyper=None, device="cuda",
-                 arena_numel=None):
+                 arena_numel=None, reduce_flags=0):
         self.buckets = [(int(o), int(l)) for o, l in buckets]
+        self.reduce_flags = reduce_flags
         self.n, self.rank = nranks, rank
         self.chunk = owned_chunk(rank, nranks)
         self.hyper = hyper or Hyper()
@@ -147,7 +150,8 @@ class Zero1OneRank:
 
     def reduce(self, incoming, stream=None):
         B.dp_reduce_scatter_mean(incoming, self.buckets, self.chunk, self.mean,
-                                 self.norm.partials, flags=GRZ_IN_COMPACT, stream=stream)
+                                 self.norm.partials, flags=GRZ_IN_COMPACT | self.reduce_flags,
+                                 stream=stream)
 
     def update(self, t, stream=None):
         self.norm.run(self.hyper.max_norm, stream)

@@ -87,7 +87,8 @@ enum { GRZ_F32 = 0, GRZ_BF16 = 1, GRZ_F64 = 2 };
 enum {
   GRZ_SUM = 1,        /* keep the sum: skip the division by N            */
   GRZ_UNEVEN = 2,     /* allow bucket lengths not divisible by N         */
-  GRZ_IN_COMPACT = 4  /* rank inputs hold only the reduced chunk, compact */
+  GRZ_IN_COMPACT = 4, /* rank inputs hold only the reduced chunk, compact */
+  GRZ_BF16_WIRE = 8   /* bf16 gradients: round every partial sum to bf16  */
 };
 
 #define GRZ_MAX_RANKS 16    /* N and the number of replicas per call       */
@@ -163,7 +164,12 @@ int64_t dp_shard_numel(const grz_bucket* buckets, int nbuckets, int nranks, int 
  *             shard-compact, dp_shard_numel elements).  -1: reduce every
  *             chunk (plain data parallelism; mean_out is indexed like the
  *             arena and only bucket ranges are written).
- * flags       GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT (needs chunk >= 0).
+ * flags       GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT (needs chunk >= 0),
+ *             GRZ_BF16_WIRE (needs GRZ_BF16): the ring's wire format is bf16,
+ *             so every partial sum of the fold -- the last one included -- is
+ *             rounded to bf16 (nearest even) before the next rank adds to it
+ *             ("13.5 Multi-GPU from First Principles", exercise 8); the mean
+ *             is that bf16 sum divided by N in fp32.
  * mean_out    device; fp32 for F32/BF16 input, fp64 for F64 input.
  * piece_sqnorm device fp64 array of dp_piece_count elements, or NULL.  The
  *             slots of the reduced chunks receive the sum of squares of the

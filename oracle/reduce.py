@@ -26,6 +26,14 @@ widened to fp32 and accumulated in fp32, rounding after every addition;
 float64 inputs stay in float64.  bf16 is the top half of an IEEE binary32, so
 widening is exact.
 
+Wire precision (the bf16-wire mode): "13.5 Multi-GPU from First Principles",
+exercise 8 ("Gradients in bf16"): a ring that sends bf16 rounds the partial sum
+to bf16 once per hop -- each reduce-scatter hop adds the incoming partial sum
+to the local chunk.  With ``wire="bf16"`` every addition of the fold is done in
+fp32 and its result rounded to bf16 (round to nearest even) before the next
+hop; the last hop's sum is rounded too, as the owner keeps it in bf16; the
+mean is then that bf16 sum divided by N in fp32.
+
 Pins (tests/test_oracle_reduce.py): the fold equals the message-passing ring
 simulator of ``oracle.ring`` bit for bit for N in {2, 3, 4, 8}; on integer
 valued data it equals ``numpy.sum``; the star example of "13.5 Multi-GPU from
@@ -37,6 +45,7 @@ full-batch gradient by a factor N).
 
 import numpy as np
 
+from .bf16 import bf16_round
 from .ring import chunk_bounds
 
 
@@ -67,23 +76,33 @@ def widen(values, kind):
     raise ValueError(f"unknown gradient kind {kind!r}")
 
 
-def ring_fold(contribs, chunk):
+def wire_round(values, wire):
+    """What one hop of a ring sends: the partial sum as is, or rounded to bf16."""
+    if wire is None:
+        return values
+    if wire == "bf16":
+        return widen(bf16_round(values), "bf16")
+    raise ValueError(f"unknown wire precision {wire!r}")
+
+
+def ring_fold(contribs, chunk, wire=None):
     """Sum of chunk ``chunk`` in ring order.
 
     ``contribs[j]`` holds rank j's (widened) values of that chunk.  The sum
     starts with rank ``chunk``'s values and adds ranks chunk+1, chunk+2, ...
-    (mod N) one at a time, rounding after each addition.
+    (mod N) one at a time, rounding after each addition (to the accumulation
+    type, then to the wire precision if one is given).
     """
     n = len(contribs)
     acc = np.array(contribs[chunk % n], copy=True)
     for j in range(1, n):
-        acc = contribs[(chunk + j) % n] + acc
+        acc = wire_round(contribs[(chunk + j) % n] + acc, wire)
     return acc
 
 
-def chunk_mean(contribs, chunk, average=True):
+def chunk_mean(contribs, chunk, average=True, wire=None):
     """Ring-order sum of one chunk, divided by N once (unless ``average`` is False)."""
-    acc = ring_fold(contribs, chunk)
+    acc = ring_fold(contribs, chunk, wire)
     if average:
         acc = acc / acc.dtype.type(len(contribs))
     return acc
@@ -109,7 +128,7 @@ def shard_segments(buckets, nranks, chunk, uneven=False):
 
 
 def reduce_scatter_mean(rank_arenas, kind, buckets, chunk, average=True,
-                        uneven=False, compact_inputs=False, arena_len=None):
+                        uneven=False, compact_inputs=False, arena_len=None, wire=None):
     """Reduce-scatter-mean of N rank arenas over a bucket plan.
 
     * ``rank_arenas[j]`` -- rank j's flat gradient arena (global layout), or,
@@ -121,7 +140,11 @@ def reduce_scatter_mean(rank_arenas, kind, buckets, chunk, average=True,
     * ``chunk == -1`` -- reduce every chunk of every bucket (all-reduce, plain
       data parallelism); returns a globally indexed array of ``arena_len``
       elements, NaN where no bucket covers it.  Chunks may be uneven here.
+    * ``wire`` -- None (sum in the accumulation type) or ``"bf16"`` (each hop's
+      partial sum rounded to bf16; bf16 inputs only).
     """
+    if wire is not None and kind != "bf16":
+        raise ValueError("the bf16 wire applies to bf16 gradients")
     n = len(rank_arenas)
     acc_dtype = np.float64 if kind == "f64" else np.float32
     if chunk >= 0:
@@ -131,7 +154,7 @@ def reduce_scatter_mean(rank_arenas, kind, buckets, chunk, average=True,
         for gstart, length, cstart in segs:
             src = cstart if compact_inputs else gstart
             contribs = [widen(a[src:src + length], kind) for a in rank_arenas]
-            out[cstart:cstart + length] = chunk_mean(contribs, chunk, average)
+            out[cstart:cstart + length] = chunk_mean(contribs, chunk, average, wire)
         return out
     if compact_inputs:
         raise ValueError("compact inputs only exist for a single chunk")
@@ -141,5 +164,5 @@ def reduce_scatter_mean(rank_arenas, kind, buckets, chunk, average=True,
     for off, length in buckets:
         for c, (lo, hi) in enumerate(chunk_bounds(length, n)):
             contribs = [widen(a[off + lo:off + hi], kind) for a in rank_arenas]
-            out[off + lo:off + hi] = chunk_mean(contribs, c, average)
+            out[off + lo:off + hi] = chunk_mean(contribs, c, average, wire)
     return out

@@ -43,7 +43,7 @@ def chunk_bounds(length, nranks):
     return out
 
 
-def ring_all_reduce(arrays, ag_start_offset=1):
+def ring_all_reduce(arrays, ag_start_offset=1, wire_round=None):
     """Run the ring all-reduce on copies of ``arrays`` (one 1-D array per rank).
 
     Returns ``(results, sent, log)``:
@@ -77,7 +77,8 @@ def ring_all_reduce(arrays, ag_start_offset=1):
             messages.append((r, (r + 1) % n, c, data[r][lo:hi].copy()))
         for src, dst, c, payload in messages:
             lo, hi = bounds[c]
-            data[dst][lo:hi] = data[dst][lo:hi] + payload
+            summed = data[dst][lo:hi] + payload
+            data[dst][lo:hi] = summed if wire_round is None else wire_round(summed)
             sent[src] += payload.nbytes
             log.append(("RS", t, src, dst, c, payload))
 

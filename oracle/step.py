@@ -42,6 +42,7 @@ import math
 
 import numpy as np
 
+from .bf16 import bf16_round  # noqa: F401  (re-exported)
 from .reduce import owned_chunk, reduce_scatter_mean, shard_segments
 
 FSUM_LIMIT = 20_000_000
@@ -100,38 +101,6 @@ def adamw(master, m, v, g, lr, beta1, beta2, eps, wd, bc1, bc2):
     return master_new, m_new, v_new
 
 
-def bf16_round(x):
-    """Round fp32 values to bf16 (nearest, ties to even); returns uint16 patterns.
-
-    Written from the definition: the two bf16 neighbours of |x| are the value
-    with the low 16 bits cleared and the next bf16 above it (for the largest
-    finite bf16 that is 2^128, which stands for infinity); both distances are
-    exact in float64 and the nearer one wins, the one with an even mantissa on
-    a tie.
-    """
-    x = np.asarray(x, dtype=np.float32)
-    bits = x.view(np.uint32)
-    sign = (bits >> np.uint32(16)) & np.uint32(0x8000)
-    mag = bits & np.uint32(0x7FFFFFFF)
-    lo_bits = mag & np.uint32(0xFFFF0000)
-    hi_bits = lo_bits + np.uint32(0x10000)
-    is_top = hi_bits == np.uint32(0x7F800000)
-    with np.errstate(over="ignore", invalid="ignore"):
-        lo = lo_bits.view(np.float32).astype(np.float64)
-        hi = np.where(is_top, 2.0 ** 128, hi_bits.view(np.float32).astype(np.float64))
-        a = mag.view(np.float32).astype(np.float64)
-        d_lo = a - lo
-        d_hi = hi - a
-    lo_odd = ((lo_bits >> np.uint32(16)) & np.uint32(1)) == 1
-    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & lo_odd)
-    out = np.where(take_hi, hi_bits >> np.uint32(16), lo_bits >> np.uint32(16))
-    is_inf = mag == np.uint32(0x7F800000)
-    is_nan = mag > np.uint32(0x7F800000)
-    out = np.where(is_inf, np.uint32(0x7F80), out)
-    out = np.where(is_nan, np.uint32(0x7FC0), out)
-    return (out | sign).astype(np.uint16)
-
-
 def all_gather(shards, buckets, nranks, arena_len, uneven=False):
     """Every replica's bf16 arena after the all-gather.
 
@@ -176,7 +145,7 @@ def _check_cover(buckets, arena_len):
         raise ValueError("buckets must tile the arena")
 
 
-def zero1_step(rank_grads, kind, buckets, states, hyper, t):
+def zero1_step(rank_grads, kind, buckets, states, hyper, t, wire=None):
     """One ZeRO-1 step of all N simulated ranks.
 
     ``states[r] = (master, m, v)``: rank r's shard-compact fp32 state for
@@ -187,7 +156,8 @@ def zero1_step(rank_grads, kind, buckets, states, hyper, t):
     n = len(rank_grads)
     arena_len = rank_grads[0].shape[0]
     _check_cover(buckets, arena_len)
-    means = [reduce_scatter_mean(rank_grads, kind, buckets, owned_chunk(r, n)) for r in range(n)]
+    means = [reduce_scatter_mean(rank_grads, kind, buckets, owned_chunk(r, n), wire=wire)
+             for r in range(n)]
     sq = grad_sqnorm(np.concatenate(means))
     scale = clip_scale(sq, hyper.max_norm)
     s = hyper.scalars(t)
@@ -202,7 +172,7 @@ def zero1_step(rank_grads, kind, buckets, states, hyper, t):
                 shards=shards, arena=arena)
 
 
-def ddp_step(rank_grads, kind, buckets, state, hyper, t):
+def ddp_step(rank_grads, kind, buckets, state, hyper, t, wire=None):
     """One plain data-parallel step (ZeRO stage 0).
 
     Every replica all-reduces the full gradient and runs the identical AdamW
@@ -211,7 +181,7 @@ def ddp_step(rank_grads, kind, buckets, state, hyper, t):
     """
     arena_len = rank_grads[0].shape[0]
     _check_cover(buckets, arena_len)
-    mean = reduce_scatter_mean(rank_grads, kind, buckets, -1, arena_len=arena_len)
+    mean = reduce_scatter_mean(rank_grads, kind, buckets, -1, arena_len=arena_len, wire=wire)
     sq = grad_sqnorm(mean)
     scale = clip_scale(sq, hyper.max_norm)
     master, m, v = adamw(*state, mean * scale, **hyper.scalars(t))

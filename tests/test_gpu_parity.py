@@ -297,3 +297,53 @@ def test_negative_controls_bite():
     for j in range(1, n):
         plain = start0[j] + plain
     assert not np.array_equal(got, plain / np.float32(n))       # fold not in ring order
+
+
+# --- the bf16 wire: every partial sum rounded to bf16 --------------------------
+
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
+def test_bf16_wire_mode_matches_oracle(n):
+    p = 3 * 4096 * n + 8 * 13 * n
+    buckets = [(4096 * n, p - 4096 * n), (0, 4096 * n)]
+    grads = [rank_grad(p, 1e-3, "bf16", grad_seed(7, r), device=DEV) for r in range(n)]
+    hg = [host(g) for g in grads]
+    out = torch.full((p,), float("nan"), device=DEV)
+    grz.dp_reduce_scatter_mean(grads, buckets, -1, out, flags=grz.GRZ_BF16_WIRE)
+    want = reduce_scatter_mean(hg, "bf16", buckets, -1, arena_len=p, wire="bf16")
+    assert_bits(host(out), want, "bf16-wire all-reduce mean")
+    plain = reduce_scatter_mean(hg, "bf16", buckets, -1, arena_len=p)
+    assert not np.array_equal(host(out), plain)  # the mode is not a no-op
+    for c in range(n):
+        shard = torch.empty(grz.dp_shard_numel(buckets, n, c), device=DEV)
+        grz.dp_reduce_scatter_mean(grads, buckets, c, shard,
+                                   flags=grz.GRZ_BF16_WIRE | grz.GRZ_SUM)
+        want = reduce_scatter_mean(hg, "bf16", buckets, c, average=False, wire="bf16")
+        assert_bits(host(shard), want, f"bf16-wire sum of chunk {c}")
+        assert np.all(host(shard).view(np.uint32) & 0xFFFF == 0)  # bf16 values
+
+
+def test_bf16_wire_zero1_step_matches_oracle():
+    p, n = 8 * 4096 * 2, 8
+    buckets = [(0, p)]
+    master = master_init(p, device=DEV)
+    z = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV,
+                          reduce_flags=grz.GRZ_BF16_WIRE)
+    states = oracle_states(host(master), buckets, n)
+    for t in (1, 2):
+        grads = [rank_grad(p, 1e-3, "bf16", grad_seed(t, r), device=DEV) for r in range(n)]
+        z.step(grads, t)
+        torch.cuda.synchronize()
+        ref = zero1_step([host(g) for g in grads], "bf16", buckets, states, OHyper(), t,
+                         wire="bf16")
+        states = ref["states"]
+        for r in range(n):
+            assert_bits(host(z.means[r]), ref["means"][r], "wire mean")
+            assert_bits(host(z.state[r][0]), ref["states"][r][0], "wire master")
+        assert_bits(host(z.replicas[0]), ref["arena"], "wire replica")
+
+
+def test_bf16_wire_needs_bf16_gradients():
+    g = [torch.zeros(64, device=DEV) for _ in range(2)]
+    with pytest.raises(grz.GrzError):
+        grz.dp_reduce_scatter_mean(g, [(0, 64)], 0, torch.empty(32, device=DEV),
+                                   flags=grz.GRZ_BF16_WIRE)

@@ -117,3 +117,79 @@ def test_shard_compact_layout_and_divisibility():
 def test_single_rank_is_identity():
     x = np.random.default_rng(1).standard_normal(33).astype(np.float32)
     assert np.array_equal(chunk_mean([x], 0), x)
+
+
+# --- the bf16 wire ("13.5 Multi-GPU from First Principles", exercise 8) -----
+
+from oracle.bf16 import bf16_round  # noqa: E402
+from oracle.reduce import wire_round  # noqa: E402
+
+
+def _bf16_vectors(rng, n, length, scale=1e-3):
+    return [bf16_round((rng.standard_normal(length) * scale).astype(np.float32))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+def test_bf16_wire_fold_equals_simulated_bf16_ring(n):
+    rng = np.random.default_rng(70 + n)
+    bits = _bf16_vectors(rng, n, 67)
+    vals = [widen(b, "bf16") for b in bits]
+    full, _, _ = ring_all_reduce(vals, wire_round=lambda x: wire_round(x, "bf16"))
+    for c, (lo, hi) in enumerate(chunk_bounds(67, n)):
+        folded = ring_fold([v[lo:hi] for v in vals], c, wire="bf16")
+        for r in range(n):
+            assert np.array_equal(full[r][lo:hi], folded)
+    assert np.all(full[0].view(np.uint32) & np.uint32(0xFFFF) == 0)  # bf16 on the wire
+    got = reduce_scatter_mean(bits, "bf16", [(0, 67)], -1, average=False, wire="bf16")
+    assert np.array_equal(got, full[0])
+
+
+def test_bf16_wire_exact_when_partial_sums_are_bf16_exact():
+    # Integers |x| < 16 summed over 8 ranks stay below 128: every partial sum
+    # is a bf16 value, so rounding per hop changes nothing.
+    rng = np.random.default_rng(71)
+    ints = [rng.integers(-15, 16, 512).astype(np.float32) for _ in range(8)]
+    bits = [bf16_round(x) for x in ints]
+    wire = reduce_scatter_mean(bits, "bf16", [(0, 512)], -1, average=False, wire="bf16")
+    assert np.array_equal(wire, np.sum(np.stack(ints), axis=0))
+
+
+def test_bf16_wire_differs_from_fp32_accumulation_on_gaussian_data():
+    rng = np.random.default_rng(72)
+    bits = _bf16_vectors(rng, 8, 4096)
+    wire = reduce_scatter_mean(bits, "bf16", [(0, 4096)], 3, wire="bf16")
+    fp32 = reduce_scatter_mean(bits, "bf16", [(0, 4096)], 3)
+    assert not np.array_equal(wire, fp32)
+    with pytest.raises(ValueError):
+        reduce_scatter_mean([np.zeros(8, np.float32)] * 2, "f32", [(0, 8)], 0, wire="bf16")
+
+
+def bf16_wire_error_study(ks=(2, 8, 64), length=1 << 16, seed=73):
+    """Relative error (2-norm) against the exact sum of fp32 gradients for
+    (a) bf16 inputs summed with a bf16 wire (rounded every hop) and (b) bf16
+    inputs summed in fp32 (rounded once, on the way in)."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for k in ks:
+        xs = [(rng.standard_normal(length) * 1e-3).astype(np.float32) for _ in range(k)]
+        exact = np.sum(np.stack(xs).astype(np.float64), axis=0)
+        bits = [bf16_round(x) for x in xs]
+        per_hop = reduce_scatter_mean(bits, "bf16", [(0, length)], -1, average=False,
+                                      wire="bf16")
+        once = reduce_scatter_mean(bits, "bf16", [(0, length)], -1, average=False)
+        nrm = np.linalg.norm(exact)
+        out[k] = (float(np.linalg.norm(per_hop - exact) / nrm),
+                  float(np.linalg.norm(once - exact) / nrm))
+    return out
+
+
+def test_bf16_wire_error_grows_with_k_and_fp32_accumulation_does_not():
+    err = bf16_wire_error_study()
+    hop = [err[k][0] for k in (2, 8, 64)]
+    once = [err[k][1] for k in (2, 8, 64)]
+    assert hop[0] < hop[1] < hop[2]                # per-hop rounding accumulates
+    assert max(once) < 2 * min(once)               # one rounding per input: flat in k
+    assert hop[2] > 3 * once[2]                    # at k = 64 the wire dominates
+    # Both are within bf16's unit roundoff scale: 2^-8 relative per rounding.
+    assert once[0] < 2 ** -8 and hop[2] < 2 ** -8 * 64
