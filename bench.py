@@ -87,7 +87,7 @@ def measured_traffic(kernel):
     return int(vals[KERNEL_NAMES[kernel]])
 
 
-def cpu_baseline(setup, sample, wire=None):
+def cpu_baseline(setup, sample, wire=None, token_counts=None):
     """The CPU oracle on a bounded sample of the same step (reported, not a target)."""
     import math
 
@@ -109,7 +109,8 @@ def cpu_baseline(setup, sample, wire=None):
     npieces_sample = math.ceil((hi - lo) / 4096)
     z = np.zeros_like(w)
     t0 = time.perf_counter()
-    mean = chunk_mean([widen(x, "bf16") for x in g], chunk, wire=wire)
+    divisor = None if token_counts is None else sum(token_counts)
+    mean = chunk_mean([widen(x, "bf16") for x in g], chunk, wire=wire, divisor=divisor)
     sq = grad_sqnorm(mean, extra=partials[:npieces_sample * (n - 1)])
     scale = clip_scale(sq, 1.0)
     w1, m1, v1 = adamw(w, z, z, mean * scale, **Hyper().scalars(1))
@@ -122,10 +123,149 @@ def cpu_baseline(setup, sample, wire=None):
     del torch
     return dict(value=(hi - lo) / dt, unit="params/s", cores=1, kind="oracle",
                 sample=f"{hi - lo} of the {shard} owned parameters (contiguous, mid-shard): "
-                       f"fold of {n} bf16 chunks, fsum norm with the matching share of peer "
+                       f"fold of {n} bf16 chunks, float64 norm with the matching share of peer "
                        f"pieces, clip, fp32 AdamW, bf16 rounding, arena assembly; "
                        f"single-threaded NumPy, {dt:.2f} s",
                 seconds=dt)
+
+
+def overlap_bench(args, dev):
+    """Bucket overlap: one JSON line with serial vs overlapped step times."""
+    import torch
+
+    import gradient_reduce_zero_amd as grz
+    from workloads import arena, master_init
+
+    a = arena("gpt2_124m")
+    p, n = a.numel, 8
+    buckets = grz.plan_buckets(a.numels)
+    d = 768
+    log(f"overlap: GPT-2 124M, N={n}, {len(buckets)} buckets")
+    master = master_init(p, device=dev)
+    pipe = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(), device=dev)
+    ov = grz.OverlappedZero1(pipe)
+    # The backward of each bucket, per simulated rank: the weight-gradient GEMM
+    # (d x T) @ (T x len/d) with T = 1024 tokens, written straight into that
+    # rank's gradient arena -- compute-bound, as a real backward is.
+    tokens = 1024
+    act_t = [torch.randn(d, tokens, device=dev, dtype=torch.bfloat16) * 0.03 for _ in range(n)]
+    dout = [[torch.randn(tokens, length // d, device=dev, dtype=torch.bfloat16) * 0.03
+             for _, length in buckets] for _ in range(n)]
+    grads = [torch.empty(p, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+
+    def produce(b):
+        off, length = buckets[b]
+        for r in range(n):
+            torch.mm(act_t[r], dout[r][b], out=grads[r][off:off + length].view(d, length // d))
+
+    def producer_only(t):
+        for b in range(len(buckets)):
+            produce(b)
+
+    def serial(t):
+        producer_only(t)
+        pipe.step(grads, t)
+
+    def overlapped(t):
+        for b in range(len(buckets)):
+            produce(b)
+            ov.bucket_ready(b, grads)
+        ov.finish(t)
+
+    def pipeline_only(t):
+        pipe.step(grads, t)
+
+    def reduce_only(t):
+        for c, mean in zip(pipe.chunks, pipe.means):
+            grz.dp_reduce_scatter_mean(grads, buckets, c, mean, pipe.norm.partials)
+
+    def timed(fn):
+        for t in range(1, args.warmup + 1):
+            fn(t)
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for t in range(1, args.steps + 1):
+            fn(t)
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    res = {k: timed(f) for k, f in (("producer_ms", producer_only), ("pipeline_ms", pipeline_only),
+                                    ("reduce_ms", reduce_only), ("serial_ms", serial),
+                                    ("overlapped_ms", overlapped))}
+    last = buckets[-1][1] / p  # the last bucket's reduce cannot overlap anything
+    hidden = (res["serial_ms"] - res["overlapped_ms"]) / res["reduce_ms"]
+    log(", ".join(f"{k} {v:.3f}" for k, v in res.items()) + f"; reduce hidden {hidden:.2f} "
+        f"(at most {1 - last:.2f}: the last bucket holds {last:.0%} of the arena)")
+    print(json.dumps({"mode": "bucket_overlap", "workload": "gpt2_124m all 8 ranks ZeRO-1",
+                      "buckets": len(buckets), "steps": args.steps, **res,
+                      "fraction_of_reduce_hidden": hidden,
+                      "max_fraction_hideable": 1 - last,
+                      "model_params_per_s_overlapped": p / (res["overlapped_ms"] * 1e-3)}),
+          flush=True)
+
+
+def stage_bench(args, dev):
+    """ZeRO-1 against ZeRO-2 on GPT-2 124M (all 8 ranks): step time and the
+    gradient bytes each keeps resident.  The same synthetic backward feeds both:
+    each bucket's gradients are copied in (to the full arenas for ZeRO-1, to
+    the one-bucket staging buffers for ZeRO-2)."""
+    import torch
+
+    import gradient_reduce_zero_amd as grz
+    from workloads import arena, grad_seed, master_init, rank_grad
+
+    a = arena("gpt2_124m")
+    p, n = a.numel, 8
+    buckets = grz.plan_buckets(a.numels)
+    master = master_init(p, device=dev)
+    src = [rank_grad(p, 1e-3, "bf16", grad_seed(1, r), device=dev) for r in range(n)]
+    z1 = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(), device=dev)
+    grads = [torch.empty_like(s) for s in src]
+    z2 = grz.Zero2AllRanks(buckets, n, master, grz.Hyper(), device=dev)
+
+    def step1(t):
+        for off, length in buckets:
+            for g, s in zip(grads, src):
+                g[off:off + length].copy_(s[off:off + length])
+        z1.step(grads, t)
+
+    def produce(b, bufs):
+        off, length = buckets[b]
+        for buf, s in zip(bufs, src):
+            buf[:length].copy_(s[off:off + length])
+
+    def step2(t):
+        z2.step(produce, t)
+
+    def timed(fn):
+        for t in range(1, args.warmup + 1):
+            fn(t)
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for t in range(1, args.steps + 1):
+            fn(t)
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    t1, t2 = timed(step1), timed(step2)
+    g1 = sum(g.numel() * g.element_size() for g in grads)
+    g2 = sum(b.numel() * b.element_size() for bufs in z2.staging for b in bufs)
+    log(f"ZeRO-1 {t1:.3f} ms, ZeRO-2 {t2:.3f} ms; gradient bytes resident "
+        f"{g1 / 1e6:.0f} MB vs {g2 / 1e6:.0f} MB")
+    print(json.dumps({"mode": "zero2_vs_zero1", "workload": "gpt2_124m all 8 ranks",
+                      "buckets": len(buckets), "steps": args.steps, "zero1_ms": t1,
+                      "zero2_ms": t2, "zero1_grad_bytes": g1, "zero2_grad_bytes": g2,
+                      "resident_bytes_per_rank": {
+                          "zero1": grz.resident_bytes(p, n, 1),
+                          "zero2": grz.resident_bytes(p, n, 2,
+                                                      longest_bucket=max(l for _, l in buckets))}}),
+          flush=True)
 
 
 def main():
@@ -141,6 +281,16 @@ def main():
     ap.add_argument("--wire", choices=["fp32", "bf16"], default="fp32",
                     help="precision of the ring's partial sums: fp32 accumulation (default) "
                          "or a bf16 wire that rounds every hop")
+    ap.add_argument("--token-weighted", action="store_true",
+                    help="ranks hold gradient sums over unequal token counts; the reduce "
+                         "divides by the global count instead of N")
+    ap.add_argument("--zero2", action="store_true",
+                    help="instead of the default workload: GPT-2 124M, all 8 simulated ranks, "
+                         "ZeRO-1 (full gradient arenas) against ZeRO-2 (one-bucket staging)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="instead of the default workload: GPT-2 124M, all 8 simulated ranks, "
+                         "9 reverse-layer buckets, reduce-scatter overlapped with a synthetic "
+                         "backward (a bf16 GEMM per bucket) on a second stream")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 2 GiB bf16 copy (the library's all-gather "
                          "kernel with one rank and one replica) as the reference of known "
@@ -159,6 +309,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.overlap:
+        overlap_bench(args, dev)
+        return
+    if args.zero2:
+        stage_bench(args, dev)
+        return
     if args.calibrate:
         numel = 1 << 30  # 2 GiB of bf16 read, 2 GiB written
         src = torch.ones(numel, dtype=torch.bfloat16, device=dev)
@@ -178,9 +334,21 @@ def main():
     log(f"inputs resident: P={setup['p']}, owned={setup['shard']}, "
         f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
 
+    # Unequal token counts (sum 8 * 4096 + 123, not a power of two: the
+    # division is a true IEEE division, not a multiply).
+    counts = ([4096 + 1000 * (j % 3) - 1000 for j in range(setup["n"])] if args.token_weighted
+              else None)
+    if counts is not None:
+        counts[0] += 123
+
+    def reduce():
+        pipe.reduce(inp["incoming"], stream, token_counts=counts)
+
     t = 1
     for _ in range(args.warmup):
-        pipe.step(inp["incoming"], inp["peer_shards"], t, stream=stream)
+        reduce()
+        pipe.update(t, stream)
+        pipe.gather(inp["peer_shards"], stream)
         t += 1
     torch.cuda.synchronize()
     log("warmup done")
@@ -196,7 +364,7 @@ def main():
     for k in range(args.steps):
         e = ev[k]
         e[0].record(stream)
-        pipe.reduce(inp["incoming"], stream)
+        reduce()
         e[1].record(stream)
         pipe.norm.run(pipe.hyper.max_norm, stream)
         e[2].record(stream)
@@ -243,7 +411,7 @@ def main():
             "arena_params": setup["p"], "owned_params": owned, "nranks_simulated": n,
             "rank": 0, "owned_chunk": setup["chunk"], "buckets": len(setup["buckets"]),
             "grad_dtype": "bf16", "state_dtype": "fp32", "weights_dtype": "bf16",
-            "clip": 1.0, "wire": args.wire,
+            "clip": 1.0, "wire": args.wire, "token_counts": counts,
         },
         "achieved_GBps": step_gbps,
         "pct_of_peak_hbm": 100.0 * step_gbps / PEAK_HBM_GBPS,
@@ -267,7 +435,8 @@ def main():
     }
     if not args.no_cpu:
         log(f"timing the CPU oracle on {args.cpu_sample} parameters")
-        cb = cpu_baseline(setup, args.cpu_sample, wire="bf16" if args.wire == "bf16" else None)
+        cb = cpu_baseline(setup, args.cpu_sample, wire="bf16" if args.wire == "bf16" else None,
+                          token_counts=counts)
         out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
     print(json.dumps(out), flush=True)
 

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libgrz.so")
 
 GRZ_OK, GRZ_EINVAL, GRZ_EINDIVISIBLE, GRZ_EALIGN, GRZ_EHIP, GRZ_ERANGE = range(6)
 GRZ_F32, GRZ_BF16, GRZ_F64 = 0, 1, 2
-GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT, GRZ_BF16_WIRE = 1, 2, 4, 8
+GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT, GRZ_BF16_WIRE, GRZ_IN_RANGE = 1, 2, 4, 8, 16
 GRZ_MAX_RANKS = 16
 GRZ_PIECE = 4096
 
@@ -45,6 +45,9 @@ SIGNATURES = {
     "dp_piece_offset": (_i64, [_BP, _i, _i, _i, _i, _i]),
     "dp_shard_numel": (_i64, [_BP, _i, _i, _i, _i]),
     "dp_reduce_scatter_mean": (_i, [_pp, _i, _i, _BP, _i, _i, _i, _vp, _vp, _vp]),
+    "dp_reduce_scatter_mean_range": (_i, [_pp, _i, _i, _BP, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "dp_reduce_scatter_weighted": (_i, [_pp, ctypes.POINTER(_i64), _i, _i, _BP, _i, _i, _i, _i,
+                                        _i, _vp, _vp, _vp]),
     "dp_grad_sqnorm_workspace": (ctypes.c_size_t, [_i64]),
     "dp_grad_sqnorm": (_i, [_vp, _i64, _d, _vp, _vp, _vp, _vp]),
     "zero1_adamw_step": (_i, [_vp, _vp, _vp, _vp, _i64, _vp, ctypes.POINTER(AdamWArgs), _vp,

@@ -96,8 +96,13 @@ def dp_grad_sqnorm_workspace(npieces):
 # -- the pipeline --------------------------------------------------------------
 
 def dp_reduce_scatter_mean(rank_grads, buckets, chunk, mean_out, piece_sqnorm=None, flags=0,
-                           stream=None):
-    """Ring-order reduce-scatter-mean of ``rank_grads`` (one tensor per rank)."""
+                           stream=None, bucket_range=None, token_counts=None):
+    """Ring-order reduce-scatter-mean of ``rank_grads`` (one tensor per rank).
+
+    ``bucket_range = (first, count)`` restricts the call to those buckets of
+    the plan (``dp_reduce_scatter_mean_range``).  ``token_counts`` (one int per
+    rank) makes it the token-weighted mean of per-rank gradient sums
+    (``dp_reduce_scatter_weighted``)."""
     n = len(rank_grads)
     if not 1 <= n <= N.GRZ_MAX_RANKS:
         raise ValueError(f"{n} ranks; 1..{N.GRZ_MAX_RANKS} supported")
@@ -112,6 +117,11 @@ def dp_reduce_scatter_mean(rank_grads, buckets, chunk, mean_out, piece_sqnorm=No
         need_out = shard
     else:
         need_in = need_out = _extent(buckets)
+    if flags & N.GRZ_IN_RANGE:
+        if bucket_range is None:
+            bucket_range = (0, len(buckets))
+        sel = [b for b in buckets[bucket_range[0]:bucket_range[0] + bucket_range[1]] if b[1] > 0]
+        need_in = _extent(sel) - min((o for o, _ in sel), default=0)
     same = _BF16_LIKE if kind == N.GRZ_BF16 else (dt,)
     ptrs = (ctypes.c_void_p * n)(*[_dev(g, f"rank_grads[{j}]", same, need_in).value
                                    for j, g in enumerate(rank_grads)])
@@ -121,9 +131,24 @@ def dp_reduce_scatter_mean(rank_grads, buckets, chunk, mean_out, piece_sqnorm=No
         part = _dev(piece_sqnorm, "piece_sqnorm", (torch.float64,),
                     dp_piece_count(buckets, n, flags & N.GRZ_UNEVEN))
     arr, nb = _bucket_array(buckets)
-    check("dp_reduce_scatter_mean",
-          lib().dp_reduce_scatter_mean(ptrs, n, kind, arr, nb, chunk, flags, out, part,
-                                       _stream(stream)))
+    if token_counts is not None:
+        if len(token_counts) != n:
+            raise ValueError("one token count per rank")
+        counts = (ctypes.c_int64 * n)(*[int(c) for c in token_counts])
+        first, count = bucket_range if bucket_range is not None else (0, nb)
+        check("dp_reduce_scatter_weighted",
+              lib().dp_reduce_scatter_weighted(ptrs, counts, n, kind, arr, nb, int(first),
+                                               int(count), chunk, flags, out, part,
+                                               _stream(stream)))
+    elif bucket_range is None:
+        check("dp_reduce_scatter_mean",
+              lib().dp_reduce_scatter_mean(ptrs, n, kind, arr, nb, chunk, flags, out, part,
+                                           _stream(stream)))
+    else:
+        first, count = (int(x) for x in bucket_range)
+        check("dp_reduce_scatter_mean_range",
+              lib().dp_reduce_scatter_mean_range(ptrs, n, kind, arr, nb, first, count, chunk,
+                                                 flags, out, part, _stream(stream)))
 
 
 def dp_grad_sqnorm(piece_sqnorm, max_norm, workspace, sqnorm_out, clip_scale_out,

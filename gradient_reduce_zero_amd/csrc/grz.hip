@@ -211,8 +211,9 @@ struct RsArgs {
   int64_t ntiles;
   int nsegs;
   int nranks;
-  int average;   // divide the sum by N
-  int pow2;      // N is a power of two: x / N == x * (1 / N) exactly
+  int average;   // divide the sum by `divisor`
+  int pow2;      // divisor is a power of two: x / d == x * (1 / d) exactly
+  double divisor;  // N, or the global token count of a token-weighted mean
   Seg seg[kMaxSegs];
 };
 
@@ -283,8 +284,9 @@ __global__ __launch_bounds__(kThreads) void rs_mean_kernel(const RsArgs<TIn> a) 
   constexpr int K = Geo<Acc>::K;
   __shared__ double lds[kThreads / 64];
   const int n = NR > 0 ? NR : a.nranks;
-  const Acc nf = static_cast<Acc>(n);
+  const Acc nf = static_cast<Acc>(a.divisor);  // exact: an integer below 2^24
   const Acc inv = static_cast<Acc>(1) / nf;
+  (void)n;
   const int lane = threadIdx.x;
 
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
@@ -514,7 +516,8 @@ int check_plan(const grz_bucket* buckets, int nbuckets, int nranks, int chunk, i
   if (nranks < 1 || nranks > GRZ_MAX_RANKS) return GRZ_EINVAL;
   if (nbuckets < 0 || (nbuckets > 0 && buckets == nullptr)) return GRZ_EINVAL;
   if (chunk < -1 || chunk >= nranks) return GRZ_EINVAL;
-  if (flags & ~(GRZ_SUM | GRZ_UNEVEN | GRZ_IN_COMPACT | GRZ_BF16_WIRE)) return GRZ_EINVAL;
+  if (flags & ~(GRZ_SUM | GRZ_UNEVEN | GRZ_IN_COMPACT | GRZ_BF16_WIRE | GRZ_IN_RANGE))
+    return GRZ_EINVAL;
   for (int b = 0; b < nbuckets; ++b) {
     if (buckets[b].offset < 0 || buckets[b].length < 0) return GRZ_ERANGE;
     if (buckets[b].length > (INT64_MAX >> 4) - buckets[b].offset) return GRZ_ERANGE;
@@ -532,19 +535,26 @@ struct PlanSeg {
   int64_t len;
   int64_t piece0;
   int chunk;
+  int bucket;
+  int64_t input;    // offset in the rank inputs when they hold a bucket range only
 };
 
-std::vector<PlanSeg> plan_segments(const grz_bucket* buckets, int nbuckets, int n, int chunk) {
+// The segments of buckets [first, first + count) of the plan; offsets and
+// piece numbers are those of the whole plan.
+std::vector<PlanSeg> plan_segments(const grz_bucket* buckets, int nbuckets, int n, int chunk,
+                                   int first = 0, int count = -1) {
+  if (count < 0) count = nbuckets - first;
   std::vector<PlanSeg> out;
   int64_t piece = 0, compact = 0;
   for (int b = 0; b < nbuckets; ++b) {
+    const bool take = b >= first && b < first + count;
     for (int c = 0; c < n; ++c) {
       int64_t off, cnt;
       chunk_of(buckets[b].length, n, c, &off, &cnt);
       if (chunk < 0 || c == chunk) {
-        if (cnt > 0) {
+        if (cnt > 0 && take) {
           const int64_t g = buckets[b].offset + off;
-          out.push_back({g, chunk < 0 ? g : compact, cnt, piece, c});
+          out.push_back({g, chunk < 0 ? g : compact, cnt, piece, c, b, g});
         }
         if (chunk >= 0) compact += cnt;
       }
@@ -588,7 +598,8 @@ int rs_launch(std::vector<Seg>& segs, RsArgs<TIn>& args, bool wire, hipStream_t 
 
 template <typename TIn>
 int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>& ps,
-                int flags, void* mean_out, double* partials, hipStream_t stream) {
+                int flags, int64_t divisor, void* mean_out, double* partials,
+                hipStream_t stream) {
   using Acc = typename AccOf<TIn>::type;
   static RsArgs<TIn> proto;  // zero-initialised template
   RsArgs<TIn> args = proto;
@@ -604,13 +615,14 @@ int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>
   args.partials = partials;
   args.nranks = n;
   args.average = (flags & GRZ_SUM) ? 0 : 1;
-  args.pow2 = (n & (n - 1)) == 0;
+  args.divisor = static_cast<double>(divisor);
+  args.pow2 = (divisor & (divisor - 1)) == 0;
   const bool compact_in = (flags & GRZ_IN_COMPACT) != 0;
   std::vector<Seg> segs;
   segs.reserve(ps.size());
   for (const PlanSeg& p : ps) {
     Seg s{};
-    s.src = compact_in ? p.compact : p.global;
+    s.src = compact_in ? p.compact : p.input;
     s.dst = p.compact;
     s.len = p.len;
     s.piece0 = p.piece0;
@@ -636,6 +648,11 @@ int sqnorm_levels(int64_t n, int64_t* sizes, int max_levels) {
   }
   return levels;
 }
+
+int reduce_entry(const void* const* rank_grads, int nranks, int64_t divisor, int dtype,
+                 const grz_bucket* buckets, int nbuckets, int bucket_first, int bucket_count,
+                 int chunk, int flags, void* mean_out, double* piece_sqnorm,
+                 hipStream_t stream);
 
 }  // namespace
 
@@ -727,30 +744,85 @@ int64_t dp_shard_numel(const grz_bucket* buckets, int nbuckets, int nranks, int 
 int dp_reduce_scatter_mean(const void* const* rank_grads, int nranks, int dtype,
                            const grz_bucket* buckets, int nbuckets, int chunk, int flags,
                            void* mean_out, double* piece_sqnorm, hipStream_t stream) {
+  return dp_reduce_scatter_mean_range(rank_grads, nranks, dtype, buckets, nbuckets, 0, nbuckets,
+                                      chunk, flags, mean_out, piece_sqnorm, stream);
+}
+
+int dp_reduce_scatter_mean_range(const void* const* rank_grads, int nranks, int dtype,
+                                 const grz_bucket* buckets, int nbuckets, int bucket_first,
+                                 int bucket_count, int chunk, int flags, void* mean_out,
+                                 double* piece_sqnorm, hipStream_t stream) {
+  return reduce_entry(rank_grads, nranks, nranks, dtype, buckets, nbuckets, bucket_first,
+                      bucket_count, chunk, flags, mean_out, piece_sqnorm, stream);
+}
+
+int dp_reduce_scatter_weighted(const void* const* rank_grads, const int64_t* token_counts,
+                               int nranks, int dtype, const grz_bucket* buckets, int nbuckets,
+                               int bucket_first, int bucket_count, int chunk, int flags,
+                               void* mean_out, double* piece_sqnorm, hipStream_t stream) {
+  if (token_counts == nullptr || nranks < 1 || nranks > GRZ_MAX_RANKS) return GRZ_EINVAL;
+  if (flags & GRZ_SUM) return GRZ_EINVAL;
+  int64_t total = 0;  // the scalar all-reduce of the token counts
+  for (int j = 0; j < nranks; ++j) {
+    if (token_counts[j] < 0) return GRZ_EINVAL;
+    total += token_counts[j];
+    if (total > (int64_t(1) << 24)) return GRZ_ERANGE;
+  }
+  if (total == 0) return GRZ_EINVAL;
+  return reduce_entry(rank_grads, nranks, total, dtype, buckets, nbuckets, bucket_first,
+                      bucket_count, chunk, flags, mean_out, piece_sqnorm, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int reduce_entry(const void* const* rank_grads, int nranks, int64_t divisor, int dtype,
+                 const grz_bucket* buckets, int nbuckets, int bucket_first, int bucket_count,
+                 int chunk, int flags, void* mean_out, double* piece_sqnorm,
+                 hipStream_t stream) {
   int st = check_plan(buckets, nbuckets, nranks, chunk, flags);
   if (st != GRZ_OK) return st;
+  if (bucket_first < 0 || bucket_count < 0 || bucket_first > nbuckets ||
+      bucket_count > nbuckets - bucket_first)
+    return GRZ_EINVAL;
   if (rank_grads == nullptr || mean_out == nullptr) return GRZ_EINVAL;
   if ((flags & GRZ_IN_COMPACT) && chunk < 0) return GRZ_EINVAL;
   if ((flags & GRZ_BF16_WIRE) && dtype != GRZ_BF16) return GRZ_EINVAL;
   for (int j = 0; j < nranks; ++j)
     if (rank_grads[j] == nullptr) return GRZ_EINVAL;
   if (piece_sqnorm != nullptr && !aligned(piece_sqnorm, 8)) return GRZ_EALIGN;
-  const std::vector<PlanSeg> ps = plan_segments(buckets, nbuckets, nranks, chunk);
+  if ((flags & GRZ_IN_RANGE) && (flags & GRZ_IN_COMPACT)) return GRZ_EINVAL;
+  std::vector<PlanSeg> ps =
+      plan_segments(buckets, nbuckets, nranks, chunk, bucket_first, bucket_count);
+  if (flags & GRZ_IN_RANGE) {
+    // Inputs hold only the range: arena index minus the range's lowest offset.
+    int64_t base = INT64_MAX;
+    for (int b = bucket_first; b < bucket_first + bucket_count; ++b)
+      if (buckets[b].length > 0 && buckets[b].offset < base) base = buckets[b].offset;
+    for (PlanSeg& p : ps) p.input = p.global - base;
+  }
   switch (dtype) {
     case GRZ_BF16:
       if (!aligned(mean_out, 4)) return GRZ_EALIGN;
-      return rs_dispatch<uint16_t>(rank_grads, nranks, ps, flags, mean_out, piece_sqnorm,
-                                   stream);
+      return rs_dispatch<uint16_t>(rank_grads, nranks, ps, flags, divisor, mean_out,
+                                   piece_sqnorm, stream);
     case GRZ_F32:
       if (!aligned(mean_out, 4)) return GRZ_EALIGN;
-      return rs_dispatch<float>(rank_grads, nranks, ps, flags, mean_out, piece_sqnorm, stream);
+      return rs_dispatch<float>(rank_grads, nranks, ps, flags, divisor, mean_out, piece_sqnorm,
+                                stream);
     case GRZ_F64:
       if (!aligned(mean_out, 8)) return GRZ_EALIGN;
-      return rs_dispatch<double>(rank_grads, nranks, ps, flags, mean_out, piece_sqnorm, stream);
+      return rs_dispatch<double>(rank_grads, nranks, ps, flags, divisor, mean_out,
+                                 piece_sqnorm, stream);
     default:
       return GRZ_EINVAL;
   }
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t dp_grad_sqnorm_workspace(int64_t npieces) {
   if (npieces <= 0) return 0;

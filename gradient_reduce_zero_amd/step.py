@@ -26,7 +26,7 @@ synchronisation inside a step.
 import torch
 
 from . import binding as B
-from ._native import GRZ_IN_COMPACT, GRZ_PIECE
+from ._native import GRZ_IN_COMPACT, GRZ_IN_RANGE, GRZ_PIECE
 from .plan import Hyper, owned_chunk, step_scalars
 
 
@@ -75,10 +75,13 @@ class Zero1AllRanks:
         self.norm = _Norm(B.dp_piece_count(self.buckets, nranks), device)
         self.replicas = [master.to(torch.bfloat16) for _ in range(nranks)]
 
-    def step(self, rank_grads, t, stream=None):
+    def step(self, rank_grads, t, stream=None, token_counts=None):
+        """One step; ``token_counts`` (one per rank) when each rank's gradient is a
+        sum over its own tokens (token-weighted mean)."""
         for c, mean in zip(self.chunks, self.means):
             B.dp_reduce_scatter_mean(rank_grads, self.buckets, c, mean, self.norm.partials,
-                                     flags=self.reduce_flags, stream=stream)
+                                     flags=self.reduce_flags, stream=stream,
+                                     token_counts=token_counts)
         self.norm.run(self.hyper.max_norm, stream)
         args = B.adamw_args(**step_scalars(self.hyper, t))
         for c, (w, m, v), mean in zip(self.chunks, self.state, self.means):
@@ -100,9 +103,10 @@ class DDPStep:
         self.norm = _Norm(B.dp_piece_count(self.buckets, nranks), device)
         self.replica = w.to(torch.bfloat16)
 
-    def step(self, rank_grads, t, stream=None):
+    def step(self, rank_grads, t, stream=None, token_counts=None):
         B.dp_reduce_scatter_mean(rank_grads, self.buckets, -1, self.mean, self.norm.partials,
-                                 flags=self.reduce_flags, stream=stream)
+                                 flags=self.reduce_flags, stream=stream,
+                                 token_counts=token_counts)
         self.norm.run(self.hyper.max_norm, stream)
         args = B.adamw_args(**step_scalars(self.hyper, t))
         w, m, v = self.state
@@ -148,10 +152,10 @@ class Zero1OneRank:
             out.append((first, -(-cnt // GRZ_PIECE)))
         return out
 
-    def reduce(self, incoming, stream=None):
+    def reduce(self, incoming, stream=None, token_counts=None):
         B.dp_reduce_scatter_mean(incoming, self.buckets, self.chunk, self.mean,
                                  self.norm.partials, flags=GRZ_IN_COMPACT | self.reduce_flags,
-                                 stream=stream)
+                                 stream=stream, token_counts=token_counts)
 
     def update(self, t, stream=None):
         self.norm.run(self.hyper.max_norm, stream)
@@ -167,3 +171,85 @@ class Zero1OneRank:
         self.reduce(incoming, stream)
         self.update(t, stream)
         self.gather(peer_shards, stream)
+
+
+class OverlappedZero1:
+    """A ``Zero1AllRanks`` step whose reduce-scatter overlaps the backward.
+
+    As each bucket's gradients become ready on the compute stream (the
+    backward produces the last layer's bucket first), ``bucket_ready`` records
+    an event there, makes the communication stream wait for it and enqueues
+    that bucket's reduce-scatter on the communication stream ("A4 -- Multi-GPU
+    with NCCL and ZeRO-1", "Part 3 -- Gradient Reduction": event record + stream
+    wait, never a host synchronisation; "Distributed training" (noeira),
+    "Overlap and graphs": buckets reduced on a second stream while the
+    backward runs).  ``finish`` runs the norm, AdamW and the all-gather on the
+    communication stream once every bucket is in, and makes the compute stream
+    wait for them.  Both streams have the default priority.  The bytes
+    produced are those of ``Zero1AllRanks.step`` (piece numbering and offsets
+    are those of the whole plan).
+    """
+
+    def __init__(self, pipe, comm_stream=None):
+        self.pipe = pipe
+        self.comm = comm_stream if comm_stream is not None else torch.cuda.Stream()
+        self.ready = [torch.cuda.Event() for _ in pipe.buckets]
+        self.done = torch.cuda.Event()
+
+    def bucket_ready(self, b, rank_grads, compute_stream=None):
+        p = self.pipe
+        cs = compute_stream if compute_stream is not None else torch.cuda.current_stream()
+        self.ready[b].record(cs)
+        self.comm.wait_event(self.ready[b])
+        for c, mean in zip(p.chunks, p.means):
+            B.dp_reduce_scatter_mean(rank_grads, p.buckets, c, mean, p.norm.partials,
+                                     flags=p.reduce_flags, stream=self.comm,
+                                     bucket_range=(b, 1))
+
+    def finish(self, t, compute_stream=None):
+        p = self.pipe
+        cs = compute_stream if compute_stream is not None else torch.cuda.current_stream()
+        p.norm.run(p.hyper.max_norm, self.comm)
+        args = B.adamw_args(**step_scalars(p.hyper, t))
+        for c, (w, m, v), mean in zip(p.chunks, p.state, p.means):
+            B.zero1_adamw_gather(w, m, v, mean, p.buckets, p.n, c, p.norm.scale, args,
+                                 p.replicas, stream=self.comm)
+        self.done.record(self.comm)
+        cs.wait_event(self.done)
+
+
+class Zero2AllRanks(Zero1AllRanks):
+    """ZeRO stage 2 of N simulated ranks: gradients are sharded as well.
+
+    No rank ever holds a full gradient arena: the backward hands each bucket's
+    gradients to ``step`` through a staging buffer the size of the largest
+    bucket (two of them, alternating), the bucket is reduce-scattered at once
+    into the ranks' fp32 gradient shards, and the buffer is reused ("Lab 09 --
+    Parallelism, simulated", s.4: stage 2 shards the gradients, 2 + 14/N bytes
+    per parameter with bf16 gradient shards; "Distributed training" (noeira),
+    ZeroSharded[2]).  The update is the ZeRO-1 one, so the results are the
+    same bits.
+    """
+
+    def __init__(self, buckets, nranks, master, hyper=None, device="cuda", reduce_flags=0,
+                 grad_dtype=torch.bfloat16):
+        super().__init__(buckets, nranks, master, hyper, device, reduce_flags)
+        longest = max((length for _, length in self.buckets), default=0)
+        self.staging = [[torch.empty(max(longest, 1), dtype=grad_dtype, device=device)
+                         for _ in range(nranks)] for _ in range(2)]
+
+    def step(self, produce, t, stream=None):
+        """``produce(b, bufs)`` writes rank r's gradients of bucket b (processing
+        order) into ``bufs[r][:length_b]`` on ``stream``."""
+        for b in range(len(self.buckets)):
+            bufs = self.staging[b % 2]
+            produce(b, bufs)
+            for c, mean in zip(self.chunks, self.means):
+                B.dp_reduce_scatter_mean(bufs, self.buckets, c, mean, self.norm.partials,
+                                         flags=self.reduce_flags | GRZ_IN_RANGE,
+                                         stream=stream, bucket_range=(b, 1))
+        self.norm.run(self.hyper.max_norm, stream)
+        args = B.adamw_args(**step_scalars(self.hyper, t))
+        for c, (w, m, v), mean in zip(self.chunks, self.state, self.means):
+            B.zero1_adamw_gather(w, m, v, mean, self.buckets, self.n, c, self.norm.scale, args,
+                                 self.replicas, stream=stream)

@@ -88,7 +88,8 @@ enum {
   GRZ_SUM = 1,        /* keep the sum: skip the division by N            */
   GRZ_UNEVEN = 2,     /* allow bucket lengths not divisible by N         */
   GRZ_IN_COMPACT = 4, /* rank inputs hold only the reduced chunk, compact */
-  GRZ_BF16_WIRE = 8   /* bf16 gradients: round every partial sum to bf16  */
+  GRZ_BF16_WIRE = 8,  /* bf16 gradients: round every partial sum to bf16  */
+  GRZ_IN_RANGE = 16   /* rank inputs hold only the reduced bucket range     */
 };
 
 #define GRZ_MAX_RANKS 16    /* N and the number of replicas per call       */
@@ -181,6 +182,48 @@ int64_t dp_shard_numel(const grz_bucket* buckets, int nbuckets, int nranks, int 
 int dp_reduce_scatter_mean(const void* const* rank_grads, int nranks, int dtype,
                            const grz_bucket* buckets, int nbuckets, int chunk, int flags,
                            void* mean_out, double* piece_sqnorm, hipStream_t stream);
+
+/*
+ * dp_reduce_scatter_mean restricted to buckets [bucket_first, bucket_first +
+ * bucket_count) of the plan: the call a bucket-overlapped backward issues as
+ * each bucket's gradients become ready ("A4", "Part 3": the reduction runs
+ * on its own stream, ordered after the compute stream by an event; "Lab 09",
+ * s.2, and "Distributed training", "Overlap and graphs": each bucket is
+ * reduced as soon as backward has produced it).  Shard-compact offsets,
+ * arena offsets and piece numbers are those of the whole plan, so reducing
+ * the buckets one call at a time, in any order, leaves exactly the bytes one
+ * call over the whole plan leaves.  GRZ_EINVAL if the range leaves the plan.
+ *
+ * With GRZ_IN_RANGE (not with GRZ_IN_COMPACT), rank_grads[j] holds only the
+ * range: arena element i is at index i - lo, lo the lowest offset of the
+ * range's buckets.  This is how a ZeRO-2 backward feeds the reduction from a
+ * staging buffer the size of one bucket instead of a full gradient arena
+ * ("Lab 09", s.4, stage 2 shards the gradients too; "Distributed training",
+ * "Four strategies, one interface", ZeroSharded[2]).
+ */
+int dp_reduce_scatter_mean_range(const void* const* rank_grads, int nranks, int dtype,
+                                 const grz_bucket* buckets, int nbuckets, int bucket_first,
+                                 int bucket_count, int chunk, int flags, void* mean_out,
+                                 double* piece_sqnorm, hipStream_t stream);
+
+/*
+ * Token-weighted reduce-scatter for shards of unequal size ("Lab 09", s.2:
+ * with variable-length sequences, sum the per-token losses and divide by the
+ * global token count; "13.5 Multi-GPU from First Principles", exercise 2:
+ * averaging the shards' means weights a token by the size of its shard, and
+ * the exact recipe needs the token counts exchanged before the update).
+ *
+ * rank_grads[j] holds rank j's gradient SUMMED over its own tokens (not
+ * divided); token_counts (host, N entries >= 0) are the ranks' token counts.
+ * The library adds the counts (the one extra scalar all-reduce) and computes
+ * (ring-order sum) / total, one IEEE division, total <= 2^24 (GRZ_ERANGE
+ * above, so that it is an exact fp32).  Everything else is
+ * dp_reduce_scatter_mean_range; GRZ_SUM is refused.
+ */
+int dp_reduce_scatter_weighted(const void* const* rank_grads, const int64_t* token_counts,
+                               int nranks, int dtype, const grz_bucket* buckets, int nbuckets,
+                               int bucket_first, int bucket_count, int chunk, int flags,
+                               void* mean_out, double* piece_sqnorm, hipStream_t stream);
 
 /* Bytes of workspace dp_grad_sqnorm needs for `npieces` pieces (may be 0). */
 size_t dp_grad_sqnorm_workspace(int64_t npieces);

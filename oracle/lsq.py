@@ -24,3 +24,21 @@ def shard_grads(X, y, w, nshards):
     rows = n // nshards
     return [lsq_grad(X[k * rows:(k + 1) * rows], y[k * rows:(k + 1) * rows], w)
             for k in range(nshards)]
+
+
+def shard_sum_grads(X, y, w, sizes):
+    """Per-shard gradients summed over the shard's rows, for row blocks of ``sizes``
+    (unequal shards; "Lab 09", s.2: with unequal shards weight by tokens --
+    sum the per-example losses and divide by the global count)."""
+    X = np.asarray(X, dtype=np.float64)
+    out, start = [], 0
+    for s in sizes:
+        Xs, ys = X[start:start + s], np.asarray(y, dtype=np.float64)[start:start + s]
+        out.append(Xs.T @ (Xs @ np.asarray(w, dtype=np.float64) - ys))
+        start += s
+    return out
+
+
+def shard_mean_grads(X, y, w, sizes):
+    """Each shard's own mean-loss gradient for row blocks of ``sizes``."""
+    return [g / s for g, s in zip(shard_sum_grads(X, y, w, sizes), sizes)]

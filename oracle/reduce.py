@@ -100,11 +100,13 @@ def ring_fold(contribs, chunk, wire=None):
     return acc
 
 
-def chunk_mean(contribs, chunk, average=True, wire=None):
-    """Ring-order sum of one chunk, divided by N once (unless ``average`` is False)."""
+def chunk_mean(contribs, chunk, average=True, wire=None, divisor=None):
+    """Ring-order sum of one chunk, divided once by N -- or by ``divisor``, the
+    global token count of a token-weighted mean -- unless ``average`` is False."""
     acc = ring_fold(contribs, chunk, wire)
     if average:
-        acc = acc / acc.dtype.type(len(contribs))
+        d = len(contribs) if divisor is None else divisor
+        acc = acc / acc.dtype.type(d)
     return acc
 
 
@@ -128,7 +130,8 @@ def shard_segments(buckets, nranks, chunk, uneven=False):
 
 
 def reduce_scatter_mean(rank_arenas, kind, buckets, chunk, average=True,
-                        uneven=False, compact_inputs=False, arena_len=None, wire=None):
+                        uneven=False, compact_inputs=False, arena_len=None, wire=None,
+                        token_counts=None):
     """Reduce-scatter-mean of N rank arenas over a bucket plan.
 
     * ``rank_arenas[j]`` -- rank j's flat gradient arena (global layout), or,
@@ -142,7 +145,12 @@ def reduce_scatter_mean(rank_arenas, kind, buckets, chunk, average=True,
       elements, NaN where no bucket covers it.  Chunks may be uneven here.
     * ``wire`` -- None (sum in the accumulation type) or ``"bf16"`` (each hop's
       partial sum rounded to bf16; bf16 inputs only).
+    * ``token_counts`` -- per-rank token counts when each rank holds the sum of
+      its per-token gradients: the result is the sum over ranks divided by the
+      total count ("Lab 09", s.2, weight by tokens; "13.5 Multi-GPU from First
+      Principles", exercise 2).
     """
+    divisor = None if token_counts is None else int(sum(int(c) for c in token_counts))
     if wire is not None and kind != "bf16":
         raise ValueError("the bf16 wire applies to bf16 gradients")
     n = len(rank_arenas)
@@ -154,7 +162,7 @@ def reduce_scatter_mean(rank_arenas, kind, buckets, chunk, average=True,
         for gstart, length, cstart in segs:
             src = cstart if compact_inputs else gstart
             contribs = [widen(a[src:src + length], kind) for a in rank_arenas]
-            out[cstart:cstart + length] = chunk_mean(contribs, chunk, average, wire)
+            out[cstart:cstart + length] = chunk_mean(contribs, chunk, average, wire, divisor)
         return out
     if compact_inputs:
         raise ValueError("compact inputs only exist for a single chunk")
@@ -164,5 +172,5 @@ def reduce_scatter_mean(rank_arenas, kind, buckets, chunk, average=True,
     for off, length in buckets:
         for c, (lo, hi) in enumerate(chunk_bounds(length, n)):
             contribs = [widen(a[off + lo:off + hi], kind) for a in rank_arenas]
-            out[off + lo:off + hi] = chunk_mean(contribs, c, average, wire)
+            out[off + lo:off + hi] = chunk_mean(contribs, c, average, wire, divisor)
     return out

@@ -145,7 +145,7 @@ def _check_cover(buckets, arena_len):
         raise ValueError("buckets must tile the arena")
 
 
-def zero1_step(rank_grads, kind, buckets, states, hyper, t, wire=None):
+def zero1_step(rank_grads, kind, buckets, states, hyper, t, wire=None, token_counts=None):
     """One ZeRO-1 step of all N simulated ranks.
 
     ``states[r] = (master, m, v)``: rank r's shard-compact fp32 state for
@@ -156,7 +156,8 @@ def zero1_step(rank_grads, kind, buckets, states, hyper, t, wire=None):
     n = len(rank_grads)
     arena_len = rank_grads[0].shape[0]
     _check_cover(buckets, arena_len)
-    means = [reduce_scatter_mean(rank_grads, kind, buckets, owned_chunk(r, n), wire=wire)
+    means = [reduce_scatter_mean(rank_grads, kind, buckets, owned_chunk(r, n), wire=wire,
+                                 token_counts=token_counts)
              for r in range(n)]
     sq = grad_sqnorm(np.concatenate(means))
     scale = clip_scale(sq, hyper.max_norm)
@@ -172,7 +173,7 @@ def zero1_step(rank_grads, kind, buckets, states, hyper, t, wire=None):
                 shards=shards, arena=arena)
 
 
-def ddp_step(rank_grads, kind, buckets, state, hyper, t, wire=None):
+def ddp_step(rank_grads, kind, buckets, state, hyper, t, wire=None, token_counts=None):
     """One plain data-parallel step (ZeRO stage 0).
 
     Every replica all-reduces the full gradient and runs the identical AdamW
@@ -181,7 +182,8 @@ def ddp_step(rank_grads, kind, buckets, state, hyper, t, wire=None):
     """
     arena_len = rank_grads[0].shape[0]
     _check_cover(buckets, arena_len)
-    mean = reduce_scatter_mean(rank_grads, kind, buckets, -1, arena_len=arena_len, wire=wire)
+    mean = reduce_scatter_mean(rank_grads, kind, buckets, -1, arena_len=arena_len, wire=wire,
+                               token_counts=token_counts)
     sq = grad_sqnorm(mean)
     scale = clip_scale(sq, hyper.max_norm)
     master, m, v = adamw(*state, mean * scale, **hyper.scalars(t))

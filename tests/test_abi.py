@@ -36,7 +36,8 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     assert re.search(r"#define GRZ_MAX_RANKS (\d+)", text).group(1) == str(N.GRZ_MAX_RANKS)
     assert re.search(r"#define GRZ_PIECE (\d+)", text).group(1) == str(N.GRZ_PIECE)
-    for name in ("GRZ_SUM", "GRZ_UNEVEN", "GRZ_IN_COMPACT", "GRZ_BF16_WIRE", "GRZ_EINDIVISIBLE",
+    for name in ("GRZ_SUM", "GRZ_UNEVEN", "GRZ_IN_COMPACT", "GRZ_BF16_WIRE", "GRZ_IN_RANGE",
+                 "GRZ_EINDIVISIBLE",
                  "GRZ_BF16"):
         assert re.search(rf"{name} = (\d+)", text).group(1) == str(getattr(N, name))
 
@@ -91,6 +92,8 @@ def test_argument_errors_return_before_any_launch():
     assert _rs(lib, fake, 2, N.GRZ_F32, [(-4, 64)], 0, 0, out) == N.GRZ_ERANGE
     assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], 0, 64, out) == N.GRZ_EINVAL
     assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], 0, N.GRZ_BF16_WIRE, out) == N.GRZ_EINVAL
+    both = N.GRZ_IN_RANGE | N.GRZ_IN_COMPACT
+    assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], 0, both, out) == N.GRZ_EINVAL
     assert _rs(lib, [0x10001, 0x20000], 2, N.GRZ_F32, [(0, 64)], 0, 0, out) == N.GRZ_EALIGN
     assert _rs(lib, [0x10000, 0], 2, N.GRZ_F32, [(0, 64)], 0, 0, out) == N.GRZ_EINVAL
     assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], 0, 0, None) == N.GRZ_EINVAL

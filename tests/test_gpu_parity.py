@@ -347,3 +347,139 @@ def test_bf16_wire_needs_bf16_gradients():
     with pytest.raises(grz.GrzError):
         grz.dp_reduce_scatter_mean(g, [(0, 64)], 0, torch.empty(32, device=DEV),
                                    flags=grz.GRZ_BF16_WIRE)
+
+
+# --- bucket-by-bucket reduction and its overlap with a backward --------------
+
+def test_bucket_range_calls_equal_one_call():
+    a = arena("char_gpt")
+    p, n = a.numel, 8
+    buckets = grz.plan_buckets(a.numels, 1 << 20, 2)  # 1 MiB cap: many buckets
+    assert len(buckets) > 5
+    grads = [rank_grad(p, 1e-3, "bf16", grad_seed(4, r), device=DEV) for r in range(n)]
+    npieces = grz.dp_piece_count(buckets, n)
+    for chunk in (-1, 3):
+        size = p if chunk < 0 else grz.dp_shard_numel(buckets, n, chunk)
+        one = torch.full((size,), float("nan"), device=DEV)
+        many = torch.full((size,), float("nan"), device=DEV)
+        p1 = torch.full((npieces,), -1.0, dtype=torch.float64, device=DEV)
+        p2 = torch.full((npieces,), -1.0, dtype=torch.float64, device=DEV)
+        grz.dp_reduce_scatter_mean(grads, buckets, chunk, one, p1)
+        for b in reversed(range(len(buckets))):  # any order
+            grz.dp_reduce_scatter_mean(grads, buckets, chunk, many, p2, bucket_range=(b, 1))
+        assert_bits(host(many), host(one), f"bucket by bucket, chunk {chunk}")
+        assert_bits(host(p2), host(p1), f"piece sums, chunk {chunk}")
+    with pytest.raises(grz.GrzError):
+        grz.dp_reduce_scatter_mean(grads, buckets, 0, many, bucket_range=(len(buckets), 1))
+
+
+def test_overlapped_step_equals_plain_step():
+    a = arena("char_gpt")
+    p, n = a.numel, 4
+    buckets = grz.plan_buckets(a.numels, 2 << 20, 2)
+    master = master_init(p, device=DEV)
+    plain = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=0.5), device=DEV)
+    ov = grz.OverlappedZero1(grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=0.5),
+                                               device=DEV))
+    src = [rank_grad(p, 1e-3, "bf16", grad_seed(1, r), device=DEV) for r in range(n)]
+    grads = [torch.zeros_like(s) for s in src]
+    x = torch.randn(1024, 1024, device=DEV)
+    for t in (1, 2):
+        plain.step(src, t)
+        for g in grads:
+            g.zero_()
+        for b, (off, length) in enumerate(buckets):  # the backward, last layer first
+            x = torch.tanh(x @ x.T * 1e-3)            # the bucket's compute
+            for g, s in zip(grads, src):
+                g[off:off + length].copy_(s[off:off + length])
+            ov.bucket_ready(b, grads)
+        ov.finish(t)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits(host(ov.pipe.means[r]), host(plain.means[r]), "overlapped mean")
+            assert_bits(host(ov.pipe.state[r][0]), host(plain.state[r][0]), "overlapped master")
+        assert_bits(host(ov.pipe.replicas[1]), host(plain.replicas[1]), "overlapped replica")
+
+
+def test_zero2_staged_step_equals_zero1_step():
+    a = arena("gpt2_124m")
+    p, n = a.numel, 8
+    buckets = grz.plan_buckets(a.numels)  # 9 buckets, reverse layer order
+    master = master_init(p, device=DEV)
+    z1 = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    z2 = grz.Zero2AllRanks(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    longest = max(length for _, length in buckets)
+    assert z2.staging[0][0].numel() == longest < p
+    for t in (1, 2):
+        grads = [rank_grad(p, 1e-3, "bf16", grad_seed(t, r), device=DEV) for r in range(n)]
+        z1.step(grads, t)
+
+        def produce(b, bufs):
+            off, length = buckets[b]
+            for buf, g in zip(bufs, grads):
+                buf[:length].copy_(g[off:off + length])
+        z2.step(produce, t)
+        torch.cuda.synchronize()
+        assert_bits(host(z2.norm.sqnorm), host(z1.norm.sqnorm), "ZeRO-2 vs ZeRO-1 sqnorm")
+        for r in (0, 5):
+            assert_bits(host(z2.means[r]), host(z1.means[r]), "ZeRO-2 gradient shard")
+            assert_bits(host(z2.state[r][0]), host(z1.state[r][0]), "ZeRO-2 master")
+        assert_bits(host(z2.replicas[7]), host(z1.replicas[7]), "ZeRO-2 replica")
+
+
+# --- token-weighted mean for shards of unequal size ---------------------------
+
+def test_token_weighted_reduce_matches_oracle():
+    n, p = 5, 3 * 4096 * 5 + 40
+    counts = [1000, 2500, 17, 4096, 300]
+    buckets = [(4096 * 5, p - 4096 * 5), (0, 4096 * 5)]
+    sums = [rank_grad(p, 1e-3 * c, "bf16", grad_seed(8, r), device=DEV)
+            for r, c in enumerate(counts)]
+    hs = [host(g) for g in sums]
+    out = torch.full((p,), float("nan"), device=DEV)
+    grz.dp_reduce_scatter_mean(sums, buckets, -1, out, token_counts=counts)
+    want = reduce_scatter_mean(hs, "bf16", buckets, -1, arena_len=p, token_counts=counts)
+    assert_bits(host(out), want, "token-weighted all-reduce")
+    for c in range(n):
+        shard = torch.empty(grz.dp_shard_numel(buckets, n, c), device=DEV)
+        grz.dp_reduce_scatter_mean(sums, buckets, c, shard, token_counts=counts)
+        assert_bits(host(shard), reduce_scatter_mean(hs, "bf16", buckets, c,
+                                                     token_counts=counts), f"chunk {c}")
+    with pytest.raises(grz.GrzError):
+        grz.dp_reduce_scatter_mean(sums, buckets, -1, out, token_counts=[1 << 23] * 5)
+    with pytest.raises(grz.GrzError):
+        grz.dp_reduce_scatter_mean(sums, buckets, -1, out, token_counts=[0] * 5)
+    with pytest.raises(grz.GrzError):
+        grz.dp_reduce_scatter_mean(sums, buckets, -1, out, flags=grz.GRZ_SUM,
+                                   token_counts=counts)
+
+
+def test_token_weighted_least_squares_65_rows_on_8_ranks():
+    from oracle.lsq import lsq_grad, shard_sum_grads
+    rng = np.random.default_rng(81)
+    sizes = [9, 8, 8, 8, 8, 8, 8, 8]
+    X = rng.integers(-3, 4, size=(65, 32)).astype(np.float64)
+    y = rng.integers(-3, 4, size=65).astype(np.float64)
+    w = rng.integers(-3, 4, size=32).astype(np.float64)
+    sums = [_dev(g) for g in shard_sum_grads(X, y, w, sizes)]
+    out = torch.empty(32, dtype=torch.float64, device=DEV)
+    grz.dp_reduce_scatter_mean(sums, [(0, 32)], -1, out, token_counts=sizes)
+    assert_bits(host(out), lsq_grad(X, y, w), "full-batch gradient")
+
+
+def test_token_weighted_zero1_step_matches_oracle():
+    p, n = 4096 * 4, 4
+    counts = [512, 2048, 1024, 100]
+    master = master_init(p, device=DEV)
+    z = grz.Zero1AllRanks([(0, p)], n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    sums = [rank_grad(p, 1e-3 * c ** 0.5, "f32", grad_seed(1, r), device=DEV)
+            for r, c in enumerate(counts)]
+    z.step(sums, 1, token_counts=counts)
+    torch.cuda.synchronize()
+    hs = [host(g) for g in sums]
+    states = oracle_states(host(master), [(0, p)], n)
+    ref = zero1_step(hs, "f32", [(0, p)], states, OHyper(max_norm=1.0), 1, token_counts=counts)
+    for r in range(n):
+        assert_bits(host(z.means[r]), ref["means"][r], f"weighted shard of rank {r}")
+        assert_bits(host(z.state[r][0]), ref["states"][r][0], f"weighted master of rank {r}")
+    assert_bits(host(z.replicas[2]), ref["arena"], "weighted replica")

@@ -193,3 +193,49 @@ def test_bf16_wire_error_grows_with_k_and_fp32_accumulation_does_not():
     assert hop[2] > 3 * once[2]                    # at k = 64 the wire dominates
     # Both are within bf16's unit roundoff scale: 2^-8 relative per rounding.
     assert once[0] < 2 ** -8 and hop[2] < 2 ** -8 * 64
+
+
+# --- token-weighted mean for unequal shards -----------------------------------
+
+from oracle.lsq import shard_mean_grads, shard_sum_grads  # noqa: E402
+
+
+@pytest.mark.parametrize("integer", [True, False])
+def test_token_weighted_mean_is_the_full_batch_gradient(integer):
+    # "Lab 09", s.2: 65 rows over 8 ranks; the plain average of the shards'
+    # means misses the full-batch gradient, weighting by tokens does not.
+    rng = np.random.default_rng(80)
+    sizes = [9, 8, 8, 8, 8, 8, 8, 8]
+    if integer:
+        X = rng.integers(-3, 4, size=(65, 32)).astype(np.float64)
+        y = rng.integers(-3, 4, size=65).astype(np.float64)
+        w = rng.integers(-3, 4, size=32).astype(np.float64)
+    else:
+        X, y, w = rng.standard_normal((65, 32)), rng.standard_normal(65), rng.standard_normal(32)
+    full = lsq_grad(X, y, w)
+    sums = shard_sum_grads(X, y, w, sizes)
+    weighted = reduce_scatter_mean(sums, "f64", [(0, 32)], -1, token_counts=sizes)
+    if integer:
+        assert np.array_equal(weighted, full)
+    else:
+        np.testing.assert_allclose(weighted, full, rtol=1e-12, atol=1e-13 * np.abs(full).max())
+    plain = reduce_scatter_mean(shard_mean_grads(X, y, w, sizes), "f64", [(0, 32)], -1)
+    miss = np.abs(plain - full).max() / np.abs(full).max()
+    assert miss > 1e-3  # the page's draw missed by 1.4% of the largest component
+
+
+def test_token_weights_of_the_two_recipes():
+    # "13.5 Multi-GPU from First Principles", exercise 2b: shards of 3000 and
+    # 1000 tokens.  Averaging the shards' means gives a token on the first
+    # shard 2/3 and one on the second 2 times its full-batch weight; the
+    # token-weighted mean gives every token weight exactly 1.
+    counts = [3000, 1000]
+    for shard in (0, 1):
+        # one unit of gradient on every token of `shard`, none on the other
+        sums = [np.array([float(counts[r] if r == shard else 0)]) for r in range(2)]
+        means = [s / c for s, c in zip(sums, counts)]
+        full = counts[shard] / sum(counts)
+        recipe_b = reduce_scatter_mean(means, "f64", [(0, 1)], -1)[0]
+        exact = reduce_scatter_mean(sums, "f64", [(0, 1)], -1, token_counts=counts)[0]
+        assert recipe_b / full == pytest.approx([2 / 3, 2.0][shard], rel=1e-15)
+        assert exact == full

@@ -44,3 +44,17 @@ def test_zero_stage_fallback_message():
     assert "Can't equally partition parameters" in log.getvalue()
     assert zero_stage([(0, 64)], 4, 1, io.StringIO()) == 1
     assert zero_stage([(0, 64)], 4, 0, io.StringIO()) == 0
+
+
+def test_resident_bytes_against_the_zero_table():
+    from gradient_reduce_zero_amd.plan import resident_bytes
+    from oracle.memory import zero_memory_bytes
+    p, n = 7e9, 8
+    # Stage 0 and 1 differ from the page's model only by the fp32 reduced
+    # gradient this pipeline keeps for the optimizer (4 bytes per kept param).
+    assert resident_bytes(p, n, 0) == zero_memory_bytes(p, n, 0) + 4 * p
+    assert resident_bytes(p, n, 1) == zero_memory_bytes(p, n, 1) + 4 * p / n
+    # Stage 2: bf16 shards of the page become fp32 shards, plus the staging.
+    longest = 25 * 2 ** 20 // 2
+    assert resident_bytes(p, n, 2, longest_bucket=longest) == \
+        zero_memory_bytes(p, n, 2) + 2 * p / n + 4 * longest
