@@ -483,3 +483,57 @@ def test_token_weighted_zero1_step_matches_oracle():
         assert_bits(host(z.means[r]), ref["means"][r], f"weighted shard of rank {r}")
         assert_bits(host(z.state[r][0]), ref["states"][r][0], f"weighted master of rank {r}")
     assert_bits(host(z.replicas[2]), ref["arena"], "weighted replica")
+
+
+# --- gates: N = 1 equals a plain optimizer step; checkpoint / resume ---------
+
+def test_single_rank_ddp_equals_plain_adamw():
+    # "Distributed training", "Gates": at N = 1 data parallelism is the plain
+    # training loop.  One rank's DDP step == the optimizer alone on its gradient.
+    p = 4096 * 3 + 100
+    master = master_init(p, device=DEV)
+    d = grz.DDPStep([(0, p)], 1, master, grz.Hyper(max_norm=0.0), device=DEV)
+    w = master.clone()
+    m, v = torch.zeros_like(w), torch.zeros_like(w)
+    out = torch.empty(p, dtype=torch.bfloat16, device=DEV)
+    for t in (1, 2, 3):
+        g = rank_grad(p, 1e-2, "f32", grad_seed(t, 0), device=DEV)
+        d.step([g], t)
+        grz.zero1_adamw_step(w, m, v, g, None, grz.adamw_args(**grz.step_scalars(d.hyper, t)),
+                             out)
+    torch.cuda.synchronize()
+    assert_bits(host(d.state[0]), host(w), "N = 1 DDP master vs plain AdamW")
+    assert_bits(host(d.replica), host(out), "N = 1 DDP weights vs plain AdamW")
+
+
+def test_checkpoint_resume_is_bit_identical():
+    # All state is caller-owned tensors plus the step counter: saving them after
+    # k steps and resuming gives the uninterrupted run's bits.
+    p, n = 8 * 4096 + 64, 4
+    buckets = [(0, p)]
+    master = master_init(p, device=DEV)
+    hyper = grz.Hyper(max_norm=0.5)
+    grads = [[rank_grad(p, 1e-2, "f32", grad_seed(t, r), device=DEV) for r in range(n)]
+             for t in range(1, 6)]
+    full = grz.Zero1AllRanks(buckets, n, master, hyper, device=DEV)
+    for t in range(1, 6):
+        full.step(grads[t - 1], t)
+    first = grz.Zero1AllRanks(buckets, n, master, hyper, device=DEV)
+    for t in range(1, 4):
+        first.step(grads[t - 1], t)
+    torch.cuda.synchronize()
+    saved = {"t": 3, "state": [[x.cpu().clone() for x in s] for s in first.state],
+             "replicas": [r.cpu().clone() for r in first.replicas]}
+    resumed = grz.Zero1AllRanks(buckets, n, master, hyper, device=DEV)
+    for dst, src in zip(resumed.state, saved["state"]):
+        for x, y in zip(dst, src):
+            x.copy_(y)
+    for dst, src in zip(resumed.replicas, saved["replicas"]):
+        dst.copy_(src)
+    for t in range(saved["t"] + 1, 6):
+        resumed.step(grads[t - 1], t)
+    torch.cuda.synchronize()
+    for a, b in zip(resumed.state, full.state):
+        for x, y in zip(a, b):
+            assert_bits(host(x), host(y), "resumed state")
+    assert_bits(host(resumed.replicas[0]), host(full.replicas[0]), "resumed weights")
