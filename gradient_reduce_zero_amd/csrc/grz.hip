@@ -104,6 +104,36 @@ __device__ __forceinline__ double widen1(const double* p) { return *p; }
 #endif
 constexpr int kNtLoad = 1, kNtStore = 2;
 
+// Occupancy caps, in waves per SIMD (0 = no cap).  Measured on MI355X at the
+// 7B one-rank share: fewer waves in flight stream faster -- the reduce at 2
+// waves per SIMD (its 8 input streams per wave) 2.75 ms against 2.90 ms
+// uncapped, the optimizer at 2 waves 4.38 ms against 4.58 ms, the all-gather
+// copy at 5 waves 3.71 ms against 3.97 ms.  Speed only, never a result bit.
+#ifndef GRZ_RS_WAVES
+#define GRZ_RS_WAVES 2
+#endif
+#ifndef GRZ_ADAM_WAVES
+#define GRZ_ADAM_WAVES 2
+#endif
+#ifndef GRZ_AG_WAVES
+#define GRZ_AG_WAVES 5
+#endif
+#if GRZ_AG_WAVES > 0
+#define GRZ_AG_ATTR __attribute__((amdgpu_waves_per_eu(GRZ_AG_WAVES, GRZ_AG_WAVES)))
+#else
+#define GRZ_AG_ATTR
+#endif
+#if GRZ_RS_WAVES > 0
+#define GRZ_RS_ATTR __attribute__((amdgpu_waves_per_eu(GRZ_RS_WAVES, GRZ_RS_WAVES)))
+#else
+#define GRZ_RS_ATTR
+#endif
+#if GRZ_ADAM_WAVES > 0
+#define GRZ_ADAM_ATTR __attribute__((amdgpu_waves_per_eu(GRZ_ADAM_WAVES, GRZ_ADAM_WAVES)))
+#else
+#define GRZ_ADAM_ATTR
+#endif
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -278,7 +308,7 @@ __device__ __forceinline__ typename AccOf<TIn>::type fold_one(const RsArgs<TIn>&
 // ring whose wire format is bf16 does once per hop ("13.5 Multi-GPU from
 // First Principles", exercise 8).
 template <typename TIn, int NR, bool WIRE>
-__global__ __launch_bounds__(kThreads) void rs_mean_kernel(const RsArgs<TIn> a) {
+__global__ __launch_bounds__(kThreads) GRZ_RS_ATTR void rs_mean_kernel(const RsArgs<TIn> a) {
   using Acc = typename AccOf<TIn>::type;
   constexpr int G = Geo<Acc>::G;
   constexpr int K = Geo<Acc>::K;
@@ -401,7 +431,7 @@ __device__ __forceinline__ void adamw1(float& w, float& m, float& v, float g, fl
 // Access k (0 <= k < 4) of lane l covers the 4 elements at k*1024 + 4*l of
 // the tile: 16-byte accesses of the fp32 streams, 8-byte bf16 stores, each
 // wave instruction one contiguous run.
-__global__ __launch_bounds__(kThreads) void adamw_kernel(const AdamArgs a) {
+__global__ __launch_bounds__(kThreads) GRZ_ADAM_ATTR void adamw_kernel(const AdamArgs a) {
   constexpr int G = 4;
   constexpr int K = GRZ_PIECE / (kThreads * G);
   const float scale = a.scale != nullptr ? *a.scale : 1.0f;
@@ -470,7 +500,7 @@ struct GatherArgs {
 
 // Access k (0 <= k < 2) of lane l copies the 8 elements (16 bytes) at
 // k*2048 + 8*l of the tile.
-__global__ __launch_bounds__(kThreads) void gather_kernel(const GatherArgs a) {
+__global__ __launch_bounds__(kThreads) GRZ_AG_ATTR void gather_kernel(const GatherArgs a) {
   constexpr int G = 8;
   constexpr int K = GRZ_PIECE / (kThreads * G);
   const int lane = threadIdx.x;
