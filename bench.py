@@ -281,6 +281,8 @@ def main():
     ap.add_argument("--wire", choices=["fp32", "bf16"], default="fp32",
                     help="precision of the ring's partial sums: fp32 accumulation (default) "
                          "or a bf16 wire that rounds every hop")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--token-weighted", action="store_true",
                     help="ranks hold gradient sums over unequal token counts; the reduce "
                          "divides by the global count instead of N")
@@ -433,6 +435,22 @@ def main():
             "bytes_per_owned_param": bpo[dominant],
         },
     }
+    if args.graph:
+        cap = grz.CapturedStep(lambda a, s: (pipe.reduce(inp["incoming"], s, token_counts=counts),
+                                             pipe.update(None, s, args=a),
+                                             pipe.gather(inp["peer_shards"], s)),
+                               pipe.hyper, t, args.warmup + args.steps)
+        for _ in range(args.warmup):
+            cap.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            cap.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        out["graph_ms_per_step"] = g0.elapsed_time(g1) / args.steps
+        log(f"graph replay: {out['graph_ms_per_step']:.3f} ms/step")
     if not args.no_cpu:
         log(f"timing the CPU oracle on {args.cpu_sample} parameters")
         cb = cpu_baseline(setup, args.cpu_sample, wire="bf16" if args.wire == "bf16" else None,

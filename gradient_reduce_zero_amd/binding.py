@@ -193,9 +193,16 @@ def zero1_adamw_step(master, m, v, mean_grad, clip_scale, args, bf16_out=None, n
                                                      out, _stream(stream)))
 
 
+ARGS_FIELDS = 7  # floats in grz_adamw_args
+
+
 def zero1_adamw_gather(master, m, v, mean_grad, buckets, nranks, chunk, clip_scale, args,
                        replicas, flags=0, stream=None):
-    """Clipped AdamW on the shard of ``chunk`` with the bf16 all-gather write fused in."""
+    """Clipped AdamW on the shard of ``chunk`` with the bf16 all-gather write fused in.
+
+    ``args`` is an ``AdamWArgs`` (host, read now) or a float32 device tensor of
+    7 values in ``grz_adamw_args`` order, read when the kernel runs
+    (``GRZ_ARGS_DEVICE``)."""
     buckets = list(buckets)
     n = dp_shard_numel(buckets, nranks, chunk, flags) if chunk >= 0 else _extent(buckets)
     w, mm, vv, g = _state(master, m, v, mean_grad, n)
@@ -204,9 +211,24 @@ def zero1_adamw_gather(master, m, v, mean_grad, buckets, nranks, chunk, clip_sca
     reps = (ctypes.c_void_p * max(len(replicas), 1))(
         *[_dev(r, f"replicas[{i}]", _BF16_LIKE, ext).value for i, r in enumerate(replicas)])
     arr, nb = _bucket_array(buckets)
+    if isinstance(args, torch.Tensor):
+        a = ctypes.cast(_dev(args, "args", (torch.float32,), ARGS_FIELDS),
+                        ctypes.POINTER(AdamWArgs))
+        flags |= N.GRZ_ARGS_DEVICE
+    else:
+        a = ctypes.byref(args)
     check("zero1_adamw_gather",
-          lib().zero1_adamw_gather(w, mm, vv, g, arr, nb, nranks, chunk, flags, sc,
-                                   ctypes.byref(args), reps, len(replicas), _stream(stream)))
+          lib().zero1_adamw_gather(w, mm, vv, g, arr, nb, nranks, chunk, flags, sc, a, reps,
+                                   len(replicas), _stream(stream)))
+
+
+def grz_step_args_next(table, counter, current, stream=None):
+    """Enqueue current = table[min(counter, rows - 1)]; counter += 1 (all on the device)."""
+    rows = table.numel() // ARGS_FIELDS
+    t = _dev(table, "table", (torch.float32,), ARGS_FIELDS)
+    c = _dev(counter, "counter", (torch.int64,), 1)
+    cur = _dev(current, "current", (torch.float32,), ARGS_FIELDS)
+    check("grz_step_args_next", lib().grz_step_args_next(t, rows, c, cur, _stream(stream)))
 
 
 def zero1_all_gather(shards, buckets, replicas, flags=0, stream=None):

@@ -407,6 +407,7 @@ struct AdamArgs {
   float* v;
   const float* grad;
   const float* scale;   // device scalar or null (1)
+  const grz_adamw_args* dargs;  // step scalars in device memory, or null (use the fields below)
   uint16_t* rep[GRZ_MAX_RANKS];
   int nrep;
   int nsegs;
@@ -435,8 +436,14 @@ __global__ __launch_bounds__(kThreads) GRZ_ADAM_ATTR void adamw_kernel(const Ada
   constexpr int G = 4;
   constexpr int K = GRZ_PIECE / (kThreads * G);
   const float scale = a.scale != nullptr ? *a.scale : 1.0f;
-  const float omb1 = 1.0f - a.b1;  // exact: 1/2 <= b1 <= 1 (Sterbenz)
-  const float omb2 = 1.0f - a.b2;
+  float lr = a.lr, b1 = a.b1, b2 = a.b2, eps = a.eps, wd = a.wd, bc1 = a.bc1, bc2 = a.bc2;
+  if (a.dargs != nullptr) {
+    const grz_adamw_args d = *a.dargs;
+    lr = d.lr; b1 = d.beta1; b2 = d.beta2; eps = d.eps; wd = d.weight_decay;
+    bc1 = d.bias_corr1; bc2 = d.bias_corr2;
+  }
+  const float omb1 = 1.0f - b1;  // exact: 1/2 <= b1 <= 1 (Sterbenz)
+  const float omb2 = 1.0f - b2;
   const int lane = threadIdx.x;
 
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
@@ -457,8 +464,7 @@ __global__ __launch_bounds__(kThreads) GRZ_ADAM_ATTR void adamw_kernel(const Ada
         uint32_t b[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-          adamw1(w[j], m[j], v[j], g[j] * scale, a.lr, a.b1, omb1, a.b2, omb2, a.eps, a.wd,
-                 a.bc1, a.bc2);
+          adamw1(w[j], m[j], v[j], g[j] * scale, lr, b1, omb1, b2, omb2, eps, wd, bc1, bc2);
           b[j] = bf16_rne(w[j]);
         }
         storeg<GRZ_ADAM_POLICY>(a.master + i, w);
@@ -473,8 +479,7 @@ __global__ __launch_bounds__(kThreads) GRZ_ADAM_ATTR void adamw_kernel(const Ada
           if (rel + j >= left) break;
           const int64_t i = s.src + e + j;
           float w = a.master[i], m = a.m[i], v = a.v[i];
-          adamw1(w, m, v, a.grad[i] * scale, a.lr, a.b1, omb1, a.b2, omb2, a.eps, a.wd, a.bc1,
-                 a.bc2);
+          adamw1(w, m, v, a.grad[i] * scale, lr, b1, omb1, b2, omb2, eps, wd, bc1, bc2);
           a.master[i] = w;
           a.m[i] = m;
           a.v[i] = v;
@@ -483,6 +488,19 @@ __global__ __launch_bounds__(kThreads) GRZ_ADAM_ATTR void adamw_kernel(const Ada
         }
       }
     }
+  }
+}
+
+// The next step's scalars for a captured (replayed) step: current =
+// table[min(counter, count - 1)], then counter += 1.  One thread.
+__global__ void args_next_kernel(const grz_adamw_args* __restrict__ table, int64_t count,
+                                 int64_t* __restrict__ counter,
+                                 grz_adamw_args* __restrict__ current) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    const int64_t c = *counter;
+    const int64_t i = c < 0 ? 0 : (c >= count ? count - 1 : c);
+    *current = table[i];
+    *counter = c + 1;
   }
 }
 
@@ -896,9 +914,10 @@ int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
 
 static int adamw_common(float* master, float* m, float* v, const float* mean_grad,
                         const std::vector<PlanSeg>& ps, const float* clip_scale,
-                        const grz_adamw_args* args, uint16_t* const* replicas, int nreplicas,
-                        hipStream_t stream) {
+                        const grz_adamw_args* args, bool args_on_device,
+                        uint16_t* const* replicas, int nreplicas, hipStream_t stream) {
   if (!master || !m || !v || !mean_grad || !args) return GRZ_EINVAL;
+  if (args_on_device && !aligned(args, 4)) return GRZ_EALIGN;
   if (nreplicas < 0 || nreplicas > GRZ_MAX_RANKS) return GRZ_EINVAL;
   if (nreplicas > 0 && replicas == nullptr) return GRZ_EINVAL;
   if (!aligned(master, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(mean_grad, 4) ||
@@ -920,13 +939,17 @@ static int adamw_common(float* master, float* m, float* v, const float* mean_gra
     a.rep[r] = replicas[r];
   }
   a.nrep = nreplicas;
-  a.lr = args->lr;
-  a.b1 = args->beta1;
-  a.b2 = args->beta2;
-  a.eps = args->eps;
-  a.wd = args->weight_decay;
-  a.bc1 = args->bias_corr1;
-  a.bc2 = args->bias_corr2;
+  if (args_on_device) {
+    a.dargs = args;
+  } else {
+    a.lr = args->lr;
+    a.b1 = args->beta1;
+    a.b2 = args->beta2;
+    a.eps = args->eps;
+    a.wd = args->weight_decay;
+    a.bc1 = args->bias_corr1;
+    a.bc2 = args->bias_corr2;
+  }
   std::vector<Seg> segs;
   segs.reserve(ps.size());
   for (const PlanSeg& p : ps) {
@@ -948,7 +971,7 @@ int zero1_adamw_step(float* master, float* m, float* v, const float* mean_grad, 
   if (n == 0) return GRZ_OK;
   std::vector<PlanSeg> ps{{0, 0, n, 0, 0}};
   uint16_t* reps[1] = {bf16_out};
-  return adamw_common(master, m, v, mean_grad, ps, clip_scale, args, reps,
+  return adamw_common(master, m, v, mean_grad, ps, clip_scale, args, false, reps,
                       bf16_out ? 1 : 0, stream);
 }
 
@@ -956,9 +979,11 @@ int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad
                        const grz_bucket* buckets, int nbuckets, int nranks, int chunk,
                        int flags, const float* clip_scale, const grz_adamw_args* args,
                        uint16_t* const* replicas, int nreplicas, hipStream_t stream) {
+  const bool dev_args = (flags & GRZ_ARGS_DEVICE) != 0;
+  flags &= ~GRZ_ARGS_DEVICE;
   const int st = check_plan(buckets, nbuckets, nranks, chunk, flags);
   if (st != GRZ_OK) return st;
-  if (flags & (GRZ_SUM | GRZ_IN_COMPACT | GRZ_BF16_WIRE)) return GRZ_EINVAL;
+  if (flags & (GRZ_SUM | GRZ_IN_COMPACT | GRZ_BF16_WIRE | GRZ_IN_RANGE)) return GRZ_EINVAL;
   std::vector<PlanSeg> ps;
   if (chunk >= 0) {
     ps = plan_segments(buckets, nbuckets, nranks, chunk);
@@ -967,8 +992,20 @@ int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad
       if (buckets[b].length > 0)
         ps.push_back({buckets[b].offset, buckets[b].offset, buckets[b].length, 0, 0});
   }
-  return adamw_common(master, m, v, mean_grad, ps, clip_scale, args, replicas, nreplicas,
-                      stream);
+  return adamw_common(master, m, v, mean_grad, ps, clip_scale, args, dev_args, replicas,
+                      nreplicas, stream);
+}
+
+int grz_step_args_next(const grz_adamw_args* table, int64_t count, int64_t* counter,
+                       grz_adamw_args* current, hipStream_t stream) {
+  if (table == nullptr || counter == nullptr || current == nullptr || count < 1)
+    return GRZ_EINVAL;
+  if (!aligned(table, 4) || !aligned(counter, 8) || !aligned(current, 4)) return GRZ_EALIGN;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(args_next_kernel, dim3(1), dim3(64), 0, stream, table, count, counter,
+                     current);
+  if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
+  return GRZ_OK;
 }
 
 int zero1_all_gather(const uint16_t* const* shards, int nranks, const grz_bucket* buckets,

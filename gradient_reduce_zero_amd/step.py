@@ -78,12 +78,16 @@ class Zero1AllRanks:
     def step(self, rank_grads, t, stream=None, token_counts=None):
         """One step; ``token_counts`` (one per rank) when each rank's gradient is a
         sum over its own tokens (token-weighted mean)."""
+        self.enqueue(rank_grads, B.adamw_args(**step_scalars(self.hyper, t)), stream,
+                     token_counts)
+
+    def enqueue(self, rank_grads, args, stream=None, token_counts=None):
+        """The step's kernels; ``args`` host ``AdamWArgs`` or a device tensor."""
         for c, mean in zip(self.chunks, self.means):
             B.dp_reduce_scatter_mean(rank_grads, self.buckets, c, mean, self.norm.partials,
                                      flags=self.reduce_flags, stream=stream,
                                      token_counts=token_counts)
         self.norm.run(self.hyper.max_norm, stream)
-        args = B.adamw_args(**step_scalars(self.hyper, t))
         for c, (w, m, v), mean in zip(self.chunks, self.state, self.means):
             B.zero1_adamw_gather(w, m, v, mean, self.buckets, self.n, c, self.norm.scale, args,
                                  self.replicas, stream=stream)
@@ -157,9 +161,12 @@ class Zero1OneRank:
                                  self.norm.partials, flags=GRZ_IN_COMPACT | self.reduce_flags,
                                  stream=stream, token_counts=token_counts)
 
-    def update(self, t, stream=None):
+    def update(self, t, stream=None, args=None):
+        """Norm, clip and AdamW with the bf16 write; ``args`` (host ``AdamWArgs`` or
+        device tensor) overrides the scalars of step ``t``."""
         self.norm.run(self.hyper.max_norm, stream)
-        args = B.adamw_args(**step_scalars(self.hyper, t))
+        if args is None:
+            args = B.adamw_args(**step_scalars(self.hyper, t))
         w, m, v = self.state
         B.zero1_adamw_gather(w, m, v, self.mean, self.buckets, self.n, self.chunk,
                              self.norm.scale, args, [self.arena], stream=stream)
@@ -170,6 +177,11 @@ class Zero1OneRank:
     def step(self, incoming, peer_shards, t, stream=None):
         self.reduce(incoming, stream)
         self.update(t, stream)
+        self.gather(peer_shards, stream)
+
+    def enqueue(self, incoming, peer_shards, args, stream=None):
+        self.reduce(incoming, stream)
+        self.update(None, stream, args=args)
         self.gather(peer_shards, stream)
 
 
@@ -253,3 +265,37 @@ class Zero2AllRanks(Zero1AllRanks):
         for c, (w, m, v), mean in zip(self.chunks, self.state, self.means):
             B.zero1_adamw_gather(w, m, v, mean, self.buckets, self.n, c, self.norm.scale, args,
                                  self.replicas, stream=stream)
+
+
+class CapturedStep:
+    """A whole step captured once in a HIP graph and replayed step after step.
+
+    "Distributed training" (noeira), "Overlap and graphs": RankGraphs captures
+    one graph per GPU and replays it.  The step's AdamW scalars change every
+    step, so they live in a device table (rows for steps ``first_t`` ..
+    ``first_t + count - 1``, filled once on the host with ``step_scalars``);
+    a one-thread kernel at the head of the graph copies the replay's row to
+    the slot the optimizer reads (``GRZ_ARGS_DEVICE``).  ``enqueue(args,
+    stream)`` must enqueue the step's kernels with ``args`` as their scalars;
+    every buffer it touches keeps its address for the graph's lifetime.  Past
+    the last row the last row is reused.  Replays produce the bits of the
+    eager steps.
+    """
+
+    def __init__(self, enqueue, hyper, first_t, count, device="cuda"):
+        rows = []
+        for t in range(first_t, first_t + count):
+            s = step_scalars(hyper, t)
+            rows.append([s["lr"], s["beta1"], s["beta2"], s["eps"], s["weight_decay"],
+                         s["bias_corr1"], s["bias_corr2"]])
+        self.table = torch.tensor(rows, dtype=torch.float32, device=device)
+        self.counter = torch.zeros(1, dtype=torch.int64, device=device)
+        self.current = torch.zeros(B.ARGS_FIELDS, dtype=torch.float32, device=device)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            s = torch.cuda.current_stream()
+            B.grz_step_args_next(self.table, self.counter, self.current, stream=s)
+            enqueue(self.current, s)
+
+    def replay(self):
+        self.graph.replay()

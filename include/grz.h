@@ -89,7 +89,8 @@ enum {
   GRZ_UNEVEN = 2,     /* allow bucket lengths not divisible by N         */
   GRZ_IN_COMPACT = 4, /* rank inputs hold only the reduced chunk, compact */
   GRZ_BF16_WIRE = 8,  /* bf16 gradients: round every partial sum to bf16  */
-  GRZ_IN_RANGE = 16   /* rank inputs hold only the reduced bucket range     */
+  GRZ_IN_RANGE = 16,  /* rank inputs hold only the reduced bucket range     */
+  GRZ_ARGS_DEVICE = 32 /* zero1_adamw_gather: `args` is a device pointer    */
 };
 
 #define GRZ_MAX_RANKS 16    /* N and the number of replicas per call       */
@@ -271,11 +272,26 @@ int zero1_adamw_step(float* master, float* m, float* v, const float* mean_grad, 
  *
  * replicas   host array of `nreplicas` (0..GRZ_MAX_RANKS) device uint16
  *            arenas.
+ * flags      GRZ_UNEVEN; GRZ_ARGS_DEVICE: `args` points to device memory and
+ *            is read by the kernel when it runs, so that a captured step
+ *            (HIP graph) can be replayed with each step's scalars
+ *            ("Distributed training", "Overlap and graphs": one graph per GPU,
+ *            replayed).
  */
 int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad,
                        const grz_bucket* buckets, int nbuckets, int nranks, int chunk,
                        int flags, const float* clip_scale, const grz_adamw_args* args,
                        uint16_t* const* replicas, int nreplicas, hipStream_t stream);
+
+/*
+ * Enqueue: *current = table[min(*counter, count - 1)]; *counter += 1.  All
+ * three are device pointers; `table` holds the per-step scalars of steps
+ * 1..count (row t-1 for step t) and `*counter` the next row.  Placed in front
+ * of a zero1_adamw_gather(..., GRZ_ARGS_DEVICE, current, ...) inside a
+ * captured step, it advances the step scalars on every replay.
+ */
+int grz_step_args_next(const grz_adamw_args* table, int64_t count, int64_t* counter,
+                       grz_adamw_args* current, hipStream_t stream);
 
 /*
  * All-gather of bf16 shards ("Lab 09", s.1, all-gather rows of the N = 3

@@ -148,6 +148,14 @@ static void argument_errors(void) {
   CHECK(zero1_all_gather(shards, 2, ok, 1, GRZ_SUM, reps, 1, NULL) == GRZ_EINVAL, "flag");
   CHECK(zero1_all_gather(shards, 0, ok, 1, 0, reps, 1, NULL) == GRZ_EINVAL, "N=0");
   CHECK(grz_set_max_blocks(0) == GRZ_EINVAL, "blocks");
+  int64_t* ctr = (int64_t*)0xC00000;
+  grz_adamw_args* table = (grz_adamw_args*)0xD00000;
+  CHECK(grz_step_args_next(NULL, 4, ctr, table, NULL) == GRZ_EINVAL, "null table");
+  CHECK(grz_step_args_next(table, 0, ctr, table, NULL) == GRZ_EINVAL, "empty table");
+  CHECK(grz_step_args_next(table, 4, (int64_t*)0xC00004, table, NULL) == GRZ_EALIGN, "counter");
+  CHECK(zero1_adamw_gather(f, f, f, f, ok, 1, 2, 0, GRZ_ARGS_DEVICE, NULL,
+                           (const grz_adamw_args*)0xE00002, reps, 1, NULL) == GRZ_EALIGN,
+        "device args alignment");
 }
 
 int main(void) {

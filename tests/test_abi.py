@@ -37,6 +37,7 @@ def test_header_constants_match_binding():
     assert re.search(r"#define GRZ_MAX_RANKS (\d+)", text).group(1) == str(N.GRZ_MAX_RANKS)
     assert re.search(r"#define GRZ_PIECE (\d+)", text).group(1) == str(N.GRZ_PIECE)
     for name in ("GRZ_SUM", "GRZ_UNEVEN", "GRZ_IN_COMPACT", "GRZ_BF16_WIRE", "GRZ_IN_RANGE",
+                 "GRZ_ARGS_DEVICE",
                  "GRZ_EINDIVISIBLE",
                  "GRZ_BF16"):
         assert re.search(rf"{name} = (\d+)", text).group(1) == str(getattr(N, name))

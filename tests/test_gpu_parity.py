@@ -537,3 +537,56 @@ def test_checkpoint_resume_is_bit_identical():
         for x, y in zip(a, b):
             assert_bits(host(x), host(y), "resumed state")
     assert_bits(host(resumed.replicas[0]), host(full.replicas[0]), "resumed weights")
+
+
+# --- a captured step, replayed ---------------------------------------------------
+
+def test_captured_one_rank_step_replays_match_eager():
+    # Graph replays, with eager work and host synchronisations in between, each
+    # compared with the eager step of the same number.
+    n, rank = 8, 0
+    p = 8 * (3 * 4096 + 520)
+    buckets = [(0, p)]
+    chunk = grz.dp_ring_owned_chunk(rank, n)
+    shard = grz.dp_shard_numel(buckets, n, chunk)
+    npieces = grz.dp_piece_count(buckets, n)
+    from workloads import onerank_inputs
+    inp = onerank_inputs(shard, n, rank, npieces, grz.GRZ_PIECE, device=DEV)
+    hyper = grz.Hyper(lr=1e-3, warmup=3, max_norm=0.05)
+    eager = grz.Zero1OneRank(buckets, n, rank, inp["shard_master"].clone(), hyper, DEV, p)
+    graphed = grz.Zero1OneRank(buckets, n, rank, inp["shard_master"].clone(), hyper, DEV, p)
+    for z in (eager, graphed):
+        z.norm.partials.copy_(inp["partials"])
+    cap = grz.CapturedStep(lambda args, s: graphed.enqueue(inp["incoming"], inp["peer_shards"],
+                                                            args, s), hyper, 1, 5)
+    junk = torch.randn(1 << 20, device=DEV)
+    for t in range(1, 8):  # steps 6 and 7 reuse the table's last row
+        eager.reduce(inp["incoming"])
+        eager.update(min(t, 5))
+        eager.gather(inp["peer_shards"])
+        cap.replay()
+        junk.mul_(0.5).add_(1.0)  # eager work between replays
+        torch.cuda.synchronize()
+        for a, b, what in ((eager.mean, graphed.mean, "mean"), (eager.state[0], graphed.state[0],
+                           "master"), (eager.state[2], graphed.state[2], "v"),
+                           (eager.arena, graphed.arena, "arena"),
+                           (eager.norm.scale, graphed.norm.scale, "scale")):
+            assert_bits(host(b), host(a), f"replay {t}: {what}")
+    assert int(cap.counter.item()) == 7
+
+
+def test_captured_all_ranks_step_replays_match_eager():
+    p, n = 4 * 4096 * 3, 4
+    buckets = [(8192, p - 8192), (0, 8192)]
+    master = master_init(p, device=DEV)
+    grads = [rank_grad(p, 1e-2, "f32", grad_seed(1, r), device=DEV) for r in range(n)]
+    eager = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=0.2), device=DEV)
+    graphed = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=0.2), device=DEV)
+    cap = grz.CapturedStep(lambda args, s: graphed.enqueue(grads, args, s), graphed.hyper, 1, 4)
+    for t in range(1, 5):
+        eager.step(grads, t)
+        cap.replay()
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert_bits(host(graphed.state[r][0]), host(eager.state[r][0]), f"replay {t} master")
+        assert_bits(host(graphed.replicas[3]), host(eager.replicas[3]), f"replay {t} replica")
