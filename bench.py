@@ -268,6 +268,43 @@ def stage_bench(args, dev):
           flush=True)
 
 
+def all_ranks_bench(args, dev):
+    """ZeRO-1 step of all N simulated ranks: one JSON line (time, bytes, GB/s)."""
+    import torch
+
+    import gradient_reduce_zero_amd as grz
+    from workloads import arena, grad_seed, master_init, rank_grad
+
+    a = arena(args.config)
+    p, n = a.numel, args.nranks
+    buckets = grz.plan_buckets(a.numels) if args.config == "gpt2_124m" else grz.whole_arena(p)
+    hyper = grz.Hyper(lr=1e-4, warmup=10) if args.config == "gpt2_1p5b" else grz.Hyper()
+    log(f"all ranks: {args.config}, N={n}, {len(buckets)} buckets")
+    master = master_init(p, device=dev)
+    pipe = grz.Zero1AllRanks(buckets, n, master, hyper, device=dev)
+    del master
+    grads = [rank_grad(p, 1e-3, "bf16", grad_seed(1, r), device=dev) for r in range(n)]
+    torch.cuda.synchronize()
+    for t in range(1, args.warmup + 1):
+        pipe.step(grads, t)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for t in range(args.warmup + 1, args.warmup + args.steps + 1):
+        pipe.step(grads, t)
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    step_bytes = p * (n * 2 + 4 + 28 + 2 * n)  # reduce N*s + mean 4; AdamW 28; N bf16 replicas
+    log(f"{ms:.3f} ms/step, {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+    print(json.dumps({"mode": "all_ranks_zero1", "workload": f"{a.name} all {n} ranks",
+                      "arena_params": p, "buckets": len(buckets), "steps": args.steps,
+                      "ms_per_step": ms, "step_bytes": step_bytes,
+                      "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
+                      "model_params_per_s": p / (ms * 1e-3)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +318,10 @@ def main():
     ap.add_argument("--wire", choices=["fp32", "bf16"], default="fp32",
                     help="precision of the ring's partial sums: fp32 accumulation (default) "
                          "or a bf16 wire that rounds every hop")
+    ap.add_argument("--all-ranks", action="store_true",
+                    help="instead of one rank's share: the ZeRO-1 step of all N simulated "
+                         "ranks of --config (every rank's reduce, AdamW and bf16 write to all "
+                         "N replicas)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--token-weighted", action="store_true",
@@ -316,6 +357,9 @@ def main():
         return
     if args.zero2:
         stage_bench(args, dev)
+        return
+    if args.all_ranks:
+        all_ranks_bench(args, dev)
         return
     if args.calibrate:
         numel = 1 << 30  # 2 GiB of bf16 read, 2 GiB written
