@@ -66,12 +66,25 @@ def bytes_per_owned(n, grad_bytes=2):
     }
 
 
+def kernel_digest():
+    """sha256 of the kernel source with comments and white space removed, and of
+    the build flags: what decides the compiled kernels."""
+    import hashlib
+    import re
+
+    from gradient_reduce_zero_amd.build import FLAGS
+
+    src = open(KERNEL_SRC).read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = re.sub(r"\s+", " ", src).strip()
+    return hashlib.sha256((src + "\n" + " ".join(FLAGS)).encode()).hexdigest()
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or None
-    when the kernel source has changed since the counters were taken."""
-    import hashlib
-
+    when the kernel code has changed since the counters were taken."""
     try:
         text = open(COUNTERS).read()
     except OSError:
@@ -81,8 +94,7 @@ def measured_traffic(kernel):
         if "=" in line:
             k, _, v = line.partition("=")
             vals[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if vals.get("kernel_source_sha256") != sha or KERNEL_NAMES[kernel] not in vals:
+    if vals.get("kernel_code_digest") != kernel_digest() or KERNEL_NAMES[kernel] not in vals:
         return None
     return int(vals[KERNEL_NAMES[kernel]])
 

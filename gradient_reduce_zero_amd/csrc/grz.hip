@@ -1,7 +1,9 @@
 // grz.hip -- HIP kernels and C ABI of the data-parallel / ZeRO-1 gradient
 // pipeline for AMD Instinct MI355X (gfx950, CDNA4, wave64).
 //
-// Kernels (all HBM-bandwidth bound; nothing here is a contraction, so no MFMA):
+// Kernels (all HBM-bandwidth bound; nothing here is a contraction, so no MFMA;
+// one 256-thread workgroup per 4096-element tile, lane-contiguous 8/16-byte
+// accesses, non-temporal hints and occupancy caps chosen by measurement):
 //   rs_mean_kernel   ring-order N-way fold of 128-bit loads, fp32 (fp64) mean,
 //                    fp64 sum of squares per GRZ_PIECE-element piece
 //   sqnorm_level_kernel / sqnorm_final_kernel
@@ -26,7 +28,6 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
-#include <string.h>
 
 #include <vector>
 
@@ -48,7 +49,9 @@ int g_max_blocks = 1 << 30;
 // `dst`, whose first tile is `tile0` of the launch and first norm piece is
 // `piece0` of the plan.  `chunk` is the ring chunk (fold start) for the
 // reduce kernel and the source shard for the gather kernel.  `vec` is 1 when
-// every pointer + offset of the run allows 16-byte accesses.
+// every pointer + offset of the run is aligned for the kernel's vector
+// accesses (8 or 16 bytes); otherwise the run goes element by element, in the
+// same lane order.
 struct Seg {
   int64_t src;
   int64_t dst;
@@ -313,10 +316,8 @@ __global__ __launch_bounds__(kThreads) GRZ_RS_ATTR void rs_mean_kernel(const RsA
   constexpr int G = Geo<Acc>::G;
   constexpr int K = Geo<Acc>::K;
   __shared__ double lds[kThreads / 64];
-  const int n = NR > 0 ? NR : a.nranks;
   const Acc nf = static_cast<Acc>(a.divisor);  // exact: an integer below 2^24
   const Acc inv = static_cast<Acc>(1) / nf;
-  (void)n;
   const int lane = threadIdx.x;
 
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
@@ -675,7 +676,8 @@ int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>
     s.len = p.len;
     s.piece0 = p.piece0;
     s.chunk = p.chunk;
-    s.vec = vec_base && (s.src * sizeof(TIn)) % in_bytes == 0 && (s.dst * sizeof(Acc)) % 16 == 0;
+    s.vec = vec_base && (s.src * sizeof(TIn)) % in_bytes == 0 &&
+            (s.dst * sizeof(Acc)) % 16 == 0;
     segs.push_back(s);
   }
   const bool wire = (flags & GRZ_BF16_WIRE) != 0;
