@@ -239,3 +239,17 @@ def test_token_weights_of_the_two_recipes():
         exact = reduce_scatter_mean(sums, "f64", [(0, 1)], -1, token_counts=counts)[0]
         assert recipe_b / full == pytest.approx([2 / 3, 2.0][shard], rel=1e-15)
         assert exact == full
+
+
+def test_least_squares_gradient_against_autograd():
+    # The closed form X^T (X w - y) / n against torch's autograd of
+    # 1/2 * mean((X w - y)^2) ("Lab 09", s.2).
+    rng = np.random.default_rng(82)
+    X, y, w = rng.standard_normal((64, 32)), rng.standard_normal(64), rng.standard_normal(32)
+    wt = torch.tensor(w, requires_grad=True)
+    loss = 0.5 * torch.mean((torch.from_numpy(X) @ wt - torch.from_numpy(y)) ** 2)
+    loss.backward()
+    np.testing.assert_allclose(lsq_grad(X, y, w), wt.grad.numpy(), rtol=1e-12, atol=1e-14)
+    sizes = [9, 8, 8, 8, 8, 8, 8, 7]
+    sums = shard_sum_grads(X, y, w, sizes)
+    np.testing.assert_allclose(np.sum(sums, axis=0) / 64, lsq_grad(X, y, w), rtol=1e-12)

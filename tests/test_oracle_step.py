@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from oracle.reduce import owned_chunk, shard_segments
-from oracle.step import (Hyper, adamw, bf16_round, bias_corrections, clip_scale,
+from oracle.step import (Hyper, adamw, all_gather, bf16_round, bias_corrections, clip_scale,
                          ddp_step, grad_sqnorm, lr_at, zero1_step)
 
 
@@ -188,3 +188,23 @@ def test_cross_n_identity_on_grid_exact_data():
         assert out["scale"] < 1
     for n in (2, 4, 8):
         assert np.array_equal(arenas[n], arenas[1])
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+def test_all_gather_equals_the_simulated_ring_all_gather(n):
+    # The oracle's all-gather places every rank's owned chunk at its arena
+    # offset; the message-passing ring ("Lab 09", s.1, all-gather rows) must
+    # leave the same vector on every rank.
+    from oracle.ring import ring_all_reduce, ring_reduce_scatter
+    rng = np.random.default_rng(90 + n)
+    length = 24 * n
+    arrays = [rng.integers(0, 1 << 15, length).astype(np.uint16).astype(np.float64)
+              for _ in range(n)]
+    owned, _ = ring_reduce_scatter(arrays)
+    shards = [None] * n
+    for r, (c, vals) in enumerate(owned):
+        shards[r] = vals.astype(np.uint16)  # small integers: exact as uint16 patterns
+    full, _, _ = ring_all_reduce(arrays)
+    gathered = all_gather(shards, [(0, length)], n, length)
+    for r in range(n):
+        assert np.array_equal(full[r].astype(np.uint16), gathered)
