@@ -590,3 +590,24 @@ def test_captured_all_ranks_step_replays_match_eager():
         for r in range(n):
             assert_bits(host(graphed.state[r][0]), host(eager.state[r][0]), f"replay {t} master")
         assert_bits(host(graphed.replicas[3]), host(eager.replicas[3]), f"replay {t} replica")
+
+
+def test_sixteen_ranks_zero1_step_matches_oracle():
+    # The largest N the library takes, with two buckets and a ragged tail.
+    p, n = 16 * (4096 + 40) + 16 * 8 * 100, 16
+    buckets = [(16 * (4096 + 40), 16 * 8 * 100), (0, 16 * (4096 + 40))]
+    master = master_init(p, device=DEV)
+    z = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=0.05), device=DEV)
+    states = oracle_states(host(master), buckets, n)
+    for t in (1, 2):
+        grads = [rank_grad(p, 1e-2, "bf16", grad_seed(t, r), device=DEV) for r in range(n)]
+        z.step(grads, t)
+        torch.cuda.synchronize()
+        ref = zero1_step([host(g) for g in grads], "bf16", buckets, states, OHyper(max_norm=0.05),
+                         t)
+        states = ref["states"]
+        assert ref["scale"] < 1
+        for r in (0, 7, 15):
+            assert_bits(host(z.means[r]), ref["means"][r], f"N=16 mean rank {r}")
+            assert_bits(host(z.state[r][0]), ref["states"][r][0], f"N=16 master rank {r}")
+        assert_bits(host(z.replicas[11]), ref["arena"], "N=16 replica")
