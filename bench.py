@@ -354,8 +354,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the N ranks are "
-              "simulated as resident buffers on that GPU; multi-GPU runs are not part of "
-              "this build", file=sys.stderr)
+              "simulated as resident buffers on that GPU, and no multi-GPU run is "
+              "implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch

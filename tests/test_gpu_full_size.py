@@ -150,10 +150,12 @@ def test_llama_7b_one_rank_share_sampled():
         assert max_rel(got, want) <= 1e-6
         if got_scale == scale:
             assert_bits(got, want, f"7B state {k} (sampled)")
-    # The rank's bf16 arena: own chunk = RNE(master); peers' chunks as received.
+    # The rank's bf16 arena: own chunk = RNE(oracle master) (when the clip
+    # factors agree, which the bit-exact masters above then show); peers'
+    # chunks as received.
     lo = chunk * shard
-    assert_bits(gather_host(pipe.arena, idx + lo), bf16_round(gather_host(pipe.state[0], idx)),
-                "own chunk of the arena")
+    if got_scale == scale:
+        assert_bits(gather_host(pipe.arena, idx + lo), bf16_round(w1), "own chunk of the arena")
     for j in (2, 5, 7):
         c = owned_chunk(j, n)
         assert_bits(gather_host(pipe.arena, idx + c * shard),
@@ -191,14 +193,13 @@ def test_gpt2_1p5b_all_ranks_sampled():
     s = OHyper(lr=1e-4, warmup=10).scalars(1)
     assert s["lr"] == np.float32(1e-5)
     w1, _, _ = adamw(m_at, np.zeros_like(m_at), np.zeros_like(m_at), want_mean * scale, **s)
-    got_all = np.empty_like(w1)
     for r in range(n):
         c = owned_chunk(r, n)
         sel = chunks == c
         got = gather_host(z.state[r][0], idx[sel] - c * shard)
-        got_all[sel] = got
         assert max_rel(got, w1[sel]) <= 1e-6
         if got_scale == scale:
             assert_bits(got, w1[sel], f"1.5B master rank {r}")
-    for rep in (z.replicas[0], z.replicas[3]):
-        assert_bits(gather_host(rep, idx), bf16_round(got_all), "1.5B replicas = RNE(master)")
+    if got_scale == scale:
+        for rep in (z.replicas[0], z.replicas[3]):
+            assert_bits(gather_host(rep, idx), bf16_round(w1), "1.5B replicas")

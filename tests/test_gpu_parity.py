@@ -109,13 +109,17 @@ def test_tiny_zero1_and_ddp_10_steps(max_norm):
         assert ref["scale"] == 1
 
 
-def test_tiny_bf16_is_rne_of_gpu_master():
-    z, _ = _tiny_run(1.0, steps=2)
+def test_tiny_bf16_weights_are_rne_of_the_masters():
+    # bf16 weights bit-exact given matching fp32 masters: the GPU masters equal
+    # the oracle's, and each rank's chunk of every replica is the oracle's
+    # rounding of them.
+    z, ref = _tiny_run(1.0, steps=2)
     for r in range(2):
-        rounded = bf16_round(host(z.state[r][0]))
+        assert_bits(host(z.state[r][0]), ref["states"][r][0], "masters match")
         c = grz.dp_ring_owned_chunk(r, 2)
         lo, cnt = grz.dp_chunk_range(4096, 2, c)
-        assert_bits(host(z.replicas[0])[lo:lo + cnt], rounded, "bf16 = RNE(master)")
+        for rep in z.replicas:
+            assert_bits(host(rep)[lo:lo + cnt], bf16_round(ref["states"][r][0]), "RNE(master)")
 
 
 # --- odd shapes: ragged tails, misaligned buckets, runtime N, empty buckets ---
@@ -246,7 +250,7 @@ def test_nan_in_one_rank_propagates_like_the_oracle():
 
 # --- the unfused optimizer and the standalone all-gather ----------------------
 
-def test_unfused_adamw_and_all_gather_match_fused():
+def test_unfused_adamw_and_all_gather_match_fused_and_oracle():
     p, n = 8 * 4096 + 8 * 13, 4
     buckets = [(8 * 4096, 8 * 13), (0, 8 * 4096)]
     grads = [rank_grad(p, 1e-3, "bf16", grad_seed(5, r), device=DEV) for r in range(n)]
@@ -267,12 +271,29 @@ def test_unfused_adamw_and_all_gather_match_fused():
     reps = [torch.zeros(p, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
     grz.zero1_all_gather(shards, buckets, reps)
     torch.cuda.synchronize()
-    want = all_gather([host(s) for s in shards], buckets, n, p)
-    for r in reps:
-        assert_bits(host(r), want, "all-gather vs oracle")
-        assert_bits(host(r), host(fused.replicas[0]), "unfused vs fused")
+    ref = zero1_step([host(g) for g in grads], "bf16", buckets,
+                     oracle_states(host(master), buckets, n), OHyper(max_norm=0.02), 1)
     for r in range(n):
-        assert_bits(host(shards[r]), bf16_round(host(plain.state[r][0])), "shard = RNE(master)")
+        assert_bits(host(shards[r]), ref["shards"][r], f"compact bf16 shard of rank {r}")
+    for rep in reps:
+        assert_bits(host(rep), ref["arena"], "unfused all-gather vs oracle")
+        assert_bits(host(rep), host(fused.replicas[0]), "unfused vs fused")
+
+
+def test_standalone_all_gather_of_synthetic_shards():
+    # Shards straight from the seeded generator (not from a GPU step): every
+    # replica must hold each rank's shard at its chunks' arena offsets.
+    p, n = 4 * (4096 * 2 + 24) + 4 * 8 * 7, 4
+    buckets = [(4 * (4096 * 2 + 24), 4 * 8 * 7), (0, 4 * (4096 * 2 + 24))]
+    shards = [master_init(grz.dp_shard_numel(buckets, n, (r + 1) % n), seed=300 + r,
+                          device=DEV).to(torch.bfloat16) for r in range(n)]
+    shards[2] = None  # already in place on its owner: not copied
+    reps = [torch.zeros(p, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    grz.zero1_all_gather(shards, buckets, reps)
+    torch.cuda.synchronize()
+    want = all_gather([None if s is None else host(s) for s in shards], buckets, n, p)
+    for rep in reps:
+        assert_bits(host(rep), want, "all-gather")
 
 
 def test_negative_controls_bite():
