@@ -203,3 +203,28 @@ def test_gpt2_1p5b_all_ranks_sampled():
     if got_scale == scale:
         for rep in (z.replicas[0], z.replicas[3]):
             assert_bits(gather_host(rep, idx), bf16_round(w1), "1.5B replicas")
+
+
+def test_char_gpt_100_steps_zero1_equals_ddp_every_step():
+    # The char GPT workload runs 100 steps.  The oracle checks the first five
+    # (test_char_gpt_all_ranks_5_steps); over all 100, ZeRO-1 and plain data
+    # parallelism must stay bit-identical (same pieces, same norm, same update)
+    # and finite.
+    a = arena("char_gpt")
+    p, n = a.numel, 8
+    buckets = [(0, p)]
+    master = master_init(p, device=DEV)
+    z = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    d = grz.DDPStep(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    spans = _layer_spans(a)
+    for t in range(1, 101):
+        grads = [rank_grad(p, 1e-3, "bf16", grad_seed(t, r), DEV, spans) for r in range(n)]
+        z.step(grads, t)
+        d.step(grads, t)
+        if t % 10 == 0 or t == 1:
+            torch.cuda.synchronize()
+            assert torch.equal(z.norm.sqnorm, d.norm.sqnorm), t
+            assert torch.equal(z.replicas[t % n].view(torch.int16), d.replica.view(torch.int16)), t
+    torch.cuda.synchronize()
+    assert torch.isfinite(d.state[0]).all()
+    assert z.norm.scale.item() < 1
