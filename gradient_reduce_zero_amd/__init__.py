@@ -10,11 +10,14 @@ call fails if the library is not built.
 
 from ._native import (GRZ_ARGS_DEVICE, GRZ_BF16, GRZ_BF16_WIRE, GRZ_F32, GRZ_F64, GRZ_IN_COMPACT, GRZ_IN_RANGE,
                       GRZ_MAX_RANKS, GRZ_PIECE, GRZ_SUM, GRZ_UNEVEN, GrzError, lib)
-from .binding import (adamw_args, dp_chunk_range, dp_grad_sqnorm, dp_grad_sqnorm_workspace,
+from .binding import (adamw_args, dp_chunk_range, dp_grad_sqnorm, dp_grad_sqnorm_of,
+                      dp_grad_sqnorm_of_workspace, dp_grad_sqnorm_workspace,
                       dp_piece_count, dp_piece_offset, dp_reduce_scatter_mean,
                       dp_ring_chunk_owner, dp_ring_owned_chunk, dp_shard_numel,
-                      grz_set_max_blocks, grz_step_args_next, zero1_adamw_gather,
-                      zero1_adamw_step, zero1_all_gather)
+                      fused_timed_out, grz_set_max_blocks, grz_set_spin_limit,
+                      grz_step_args_next, zero1_adamw_gather, zero1_adamw_step,
+                      zero1_all_gather, zero1_fused_capacity, zero1_fused_step,
+                      zero1_fused_workspace)
 from .plan import (Hyper, owned_chunk, plan_buckets, resident_bytes, step_scalars, whole_arena,
                    zero_stage)
 from .step import (CapturedStep, DDPStep, OverlappedZero1, Zero1AllRanks, Zero1OneRank,

@@ -51,12 +51,20 @@ SIGNATURES = {
                                         _i, _vp, _vp, _vp]),
     "dp_grad_sqnorm_workspace": (ctypes.c_size_t, [_i64]),
     "dp_grad_sqnorm": (_i, [_vp, _i64, _d, _vp, _vp, _vp, _vp]),
+    "dp_grad_sqnorm_of_workspace": (ctypes.c_size_t, [_i64]),
+    "dp_grad_sqnorm_of": (_i, [_vp, _i64, _d, _vp, _vp, _vp, _vp]),
     "zero1_adamw_step": (_i, [_vp, _vp, _vp, _vp, _i64, _vp, ctypes.POINTER(AdamWArgs), _vp,
                               _vp]),
     "zero1_adamw_gather": (_i, [_vp, _vp, _vp, _vp, _BP, _i, _i, _i, _i, _vp,
                                 ctypes.POINTER(AdamWArgs), _pp, _i, _vp]),
     "zero1_all_gather": (_i, [_pp, _i, _BP, _i, _i, _pp, _i, _vp]),
     "grz_step_args_next": (_i, [_vp, _i64, _vp, _vp, _vp]),
+    "grz_set_spin_limit": (_i, [ctypes.c_uint]),
+    "zero1_fused_workspace": (ctypes.c_size_t, [_i64]),
+    "zero1_fused_capacity": (_i64, [_i, _i]),
+    "zero1_fused_step": (_i, [_pp, _i, _i, _BP, _i, _i, _i, _vp, _vp, _vp,
+                              ctypes.POINTER(AdamWArgs), _d, _pp, _i, _vp, _vp, _vp, _vp, _vp,
+                              _vp]),
 }
 
 _lib = None

@@ -172,6 +172,27 @@ def dp_grad_sqnorm(piece_sqnorm, max_norm, workspace, sqnorm_out, clip_scale_out
                                                  _stream(stream)))
 
 
+def dp_grad_sqnorm_of_workspace(n):
+    return int(lib().dp_grad_sqnorm_of_workspace(int(n)))
+
+
+def dp_grad_sqnorm_of(grad, max_norm, workspace, sqnorm_out, clip_scale_out, stream=None):
+    """Global squared norm and clip factor of an fp32 gradient array."""
+    n = grad.numel()
+    g = _dev(grad, "grad", (torch.float32,))
+    need = dp_grad_sqnorm_of_workspace(n)
+    ws = None
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"dp_grad_sqnorm_of needs {need} bytes of workspace")
+        ws = _dev(workspace, "workspace")
+    sq = None if sqnorm_out is None else _dev(sqnorm_out, "sqnorm_out", (torch.float64,), 1)
+    sc = None if clip_scale_out is None else _dev(clip_scale_out, "clip_scale_out",
+                                                   (torch.float32,), 1)
+    check("dp_grad_sqnorm_of", lib().dp_grad_sqnorm_of(g, n, float(max_norm), ws, sq, sc,
+                                                       _stream(stream)))
+
+
 def adamw_args(lr, beta1, beta2, eps, weight_decay, bias_corr1, bias_corr2):
     return AdamWArgs(lr, beta1, beta2, eps, weight_decay, bias_corr1, bias_corr2)
 
@@ -249,6 +270,77 @@ def zero1_all_gather(shards, buckets, replicas, flags=0, stream=None):
     arr, nb = _bucket_array(buckets)
     check("zero1_all_gather", lib().zero1_all_gather(sp, n, arr, nb, flags, reps, len(replicas),
                                                      _stream(stream)))
+
+
+def grz_set_spin_limit(polls):
+    """Polls of a grid-wide wait in ``zero1_fused_step`` before it gives up."""
+    check("grz_set_spin_limit", lib().grz_set_spin_limit(int(polls)))
+
+
+def zero1_fused_workspace(npieces):
+    return int(lib().zero1_fused_workspace(int(npieces)))
+
+
+def zero1_fused_capacity(nranks, dtype):
+    """Pieces one fused launch holds for ``nranks`` ranks of ``dtype`` gradients."""
+    kind = _KIND[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return _neg_check("zero1_fused_capacity", lib().zero1_fused_capacity(int(nranks), kind))
+
+
+def zero1_fused_step(rank_grads, buckets, chunk, master, m, v, args, max_norm, replicas,
+                     piece_sqnorm, workspace, sqnorm_out=None, clip_scale_out=None,
+                     mean_out=None, flags=0, stream=None):
+    """Reduce-scatter-mean, norm, clip, AdamW and the bf16 write of one shard
+    (``chunk >= 0``) or of every chunk (``chunk = -1``) in one launch.
+
+    ``workspace`` (``zero1_fused_workspace`` bytes) must be zeroed before its
+    first use; ``args`` is an ``AdamWArgs`` or a device float32 tensor of 7
+    values (``GRZ_ARGS_DEVICE``)."""
+    n = len(rank_grads)
+    if not 1 <= n <= N.GRZ_MAX_RANKS:
+        raise ValueError(f"{n} ranks; 1..{N.GRZ_MAX_RANKS} supported")
+    dt = rank_grads[0].dtype
+    if dt not in (torch.float32,) + _BF16_LIKE:
+        raise TypeError(f"gradient dtype {dt} not supported by the fused step")
+    kind = _KIND[dt]
+    buckets = list(buckets)
+    ext = _extent(buckets)
+    shard = dp_shard_numel(buckets, n, chunk, flags & N.GRZ_UNEVEN) if chunk >= 0 else ext
+    need_in = shard if flags & N.GRZ_IN_COMPACT else ext
+    same = _BF16_LIKE if kind == N.GRZ_BF16 else (dt,)
+    ptrs = (ctypes.c_void_p * n)(*[_dev(g, f"rank_grads[{j}]", same, need_in).value
+                                   for j, g in enumerate(rank_grads)])
+    f32 = (torch.float32,)
+    w, mm, vv = (_dev(master, "master", f32, shard), _dev(m, "m", f32, shard),
+                 _dev(v, "v", f32, shard))
+    npieces = dp_piece_count(buckets, n, flags & N.GRZ_UNEVEN)
+    part = _dev(piece_sqnorm, "piece_sqnorm", (torch.float64,), npieces)
+    need_ws = zero1_fused_workspace(npieces)
+    if workspace.numel() * workspace.element_size() < need_ws:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
+                         f"bytes, {need_ws} needed")
+    ws = _dev(workspace, "workspace")
+    sq = None if sqnorm_out is None else _dev(sqnorm_out, "sqnorm_out", (torch.float64,), 1)
+    sc = None if clip_scale_out is None else _dev(clip_scale_out, "clip_scale_out", f32, 1)
+    mo = None if mean_out is None else _dev(mean_out, "mean_out", f32, shard)
+    reps = (ctypes.c_void_p * max(len(replicas), 1))(
+        *[_dev(r, f"replicas[{i}]", _BF16_LIKE, ext).value for i, r in enumerate(replicas)])
+    arr, nb = _bucket_array(buckets)
+    if isinstance(args, torch.Tensor):
+        a = ctypes.cast(_dev(args, "args", f32, ARGS_FIELDS), ctypes.POINTER(AdamWArgs))
+        flags |= N.GRZ_ARGS_DEVICE
+    else:
+        a = ctypes.byref(args)
+    check("zero1_fused_step",
+          lib().zero1_fused_step(ptrs, n, kind, arr, nb, chunk, flags, w, mm, vv, a,
+                                 float(max_norm), reps, len(replicas), part, ws, sq, sc, mo,
+                                 _stream(stream)))
+
+
+def fused_timed_out(workspace):
+    """True if a grid-wide wait of the last fused step on ``workspace`` gave up
+    (reads the device word: synchronises with the stream's work)."""
+    return int(workspace.view(torch.int32)[2].item()) != 0
 
 
 def grz_set_max_blocks(blocks):

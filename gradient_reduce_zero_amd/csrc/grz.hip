@@ -45,6 +45,10 @@ static_assert(GRZ_PIECE % (kThreads * 8) == 0, "piece shape");
 // workgroup per tile (no cap in practice) streams fastest.
 int g_max_blocks = 1 << 30;
 
+// Polls of a grid-barrier wait before it gives up (fused step).  Each poll
+// sleeps a few hundred cycles, so the default bounds a wait at a few seconds.
+unsigned g_spin_limit = 1u << 22;
+
 // One contiguous run of work: `len` elements read at `src` and written at
 // `dst`, whose first tile is `tile0` of the launch and first norm piece is
 // `piece0` of the plan.  `chunk` is the ring chunk (fold start) for the
@@ -62,7 +66,8 @@ struct Seg {
   int32_t vec;
 };
 
-__device__ __forceinline__ int find_seg(const Seg* seg, int nsegs, int64_t tile) {
+template <typename S>
+__device__ __forceinline__ int find_seg(const S* seg, int nsegs, int64_t tile) {
   int lo = 0, hi = nsegs - 1;
   while (lo < hi) {  // last segment whose tile0 <= tile
     int mid = (lo + hi + 1) >> 1;
@@ -255,9 +260,8 @@ struct RsArgs {
 // before the first add.
 template <typename TIn, int NR, bool WIRE, typename Acc = typename AccOf<TIn>::type,
           int G = Geo<Acc>::G>
-__device__ __forceinline__ void fold_vec(const RsArgs<TIn>& a, int c, int64_t off,
+__device__ __forceinline__ void fold_vec(const TIn* const* rank, int nranks, int c, int64_t off,
                                          Acc (&acc)[G]) {
-  const TIn* const* rank = a.rank;
   if constexpr (NR > 0) {
     Acc x[NR][G];
 #pragma unroll
@@ -276,7 +280,7 @@ __device__ __forceinline__ void fold_vec(const RsArgs<TIn>& a, int c, int64_t of
         if constexpr (WIRE) acc[k] = bf16_wire(acc[k]);
       }
   } else {
-    const int n = a.nranks;
+    const int n = nranks;
     loadg<GRZ_RS_POLICY>(rank[c] + off, acc);
     for (int j = 1; j < n; ++j) {
       int r = c + j;
@@ -293,15 +297,15 @@ __device__ __forceinline__ void fold_vec(const RsArgs<TIn>& a, int c, int64_t of
 }
 
 template <typename TIn, int NR, bool WIRE>
-__device__ __forceinline__ typename AccOf<TIn>::type fold_one(const RsArgs<TIn>& a, int c,
-                                                              int64_t off) {
+__device__ __forceinline__ typename AccOf<TIn>::type fold_one(const TIn* const* rank, int nranks,
+                                                              int c, int64_t off) {
   using Acc = typename AccOf<TIn>::type;
-  const int n = NR > 0 ? NR : a.nranks;
-  Acc acc = widen1(a.rank[c] + off);
+  const int n = NR > 0 ? NR : nranks;
+  Acc acc = widen1(rank[c] + off);
   for (int j = 1; j < n; ++j) {
     int r = c + j;
     r = r >= n ? r - n : r;
-    acc = widen1(a.rank[r] + off) + acc;
+    acc = widen1(rank[r] + off) + acc;
     if constexpr (WIRE) acc = bf16_wire(acc);
   }
   return acc;
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(kThreads) GRZ_RS_ATTR void rs_mean_kernel(const RsA
       const int64_t e = e0 + rel;
       if (s.vec && rel + G <= left) {
         Acc acc[G];
-        fold_vec<TIn, NR, WIRE>(a, c, s.src + e, acc);
+        fold_vec<TIn, NR, WIRE>(a.rank, a.nranks, c, s.src + e, acc);
 #pragma unroll
         for (int i = 0; i < G; ++i) {
           if (a.average) acc[i] = a.pow2 ? acc[i] * inv : acc[i] / nf;
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(kThreads) GRZ_RS_ATTR void rs_mean_kernel(const RsA
       } else {
         for (int i = 0; i < G; ++i) {
           if (rel + i >= left) break;
-          Acc v = fold_one<TIn, NR, WIRE>(a, c, s.src + e + i);
+          Acc v = fold_one<TIn, NR, WIRE>(a.rank, a.nranks, c, s.src + e + i);
           if (a.average) v = a.pow2 ? v * inv : v / nf;
           sq = __fma_rn(static_cast<double>(v), static_cast<double>(v), sq);
           a.out[s.dst + e + i] = v;
@@ -360,18 +364,38 @@ __global__ __launch_bounds__(kThreads) GRZ_RS_ATTR void rs_mean_kernel(const RsA
 // values [j*4096, (j+1)*4096): lane l adds values l, l+256, ..., l+3840 in
 // that order, then block_sum_fixed.  The tree depends only on the count.
 
-__global__ __launch_bounds__(kThreads) void sqnorm_level_kernel(const double* __restrict__ x,
-                                                                int64_t n,
-                                                                double* __restrict__ y) {
-  __shared__ double lds[kThreads / 64];
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kReduceFan;
+// Block fold of values [base, base + 4096) of x (those below n): lane l adds
+// values base + l, base + l + 256, ..., base + l + 3840 in that order, then
+// block_sum_fixed.
+__device__ __forceinline__ double fan_block_sum(const double* __restrict__ x, int64_t n,
+                                                int64_t base, double* lds) {
   double s = 0.0;
 #pragma unroll
   for (int k = 0; k < kReduceFan / kThreads; ++k) {
     const int64_t i = base + k * kThreads + threadIdx.x;
     if (i < n) s += x[i];
   }
-  const double tot = block_sum_fixed(s, lds);
+  return block_sum_fixed(s, lds);
+}
+
+// The clip factor: fp32(max_norm / norm) when norm = sqrt(sqnorm) exceeds
+// max_norm, else 1 (also when max_norm <= 0, and for a NaN norm, where the
+// comparison is false).
+__device__ __forceinline__ float clip_factor(double sqnorm, double max_norm) {
+  float scale = 1.0f;
+  if (max_norm > 0.0) {
+    const double norm = sqrt(sqnorm);
+    if (norm > max_norm) scale = static_cast<float>(max_norm / norm);
+  }
+  return scale;
+}
+
+__global__ __launch_bounds__(kThreads) void sqnorm_level_kernel(const double* __restrict__ x,
+                                                                int64_t n,
+                                                                double* __restrict__ y) {
+  __shared__ double lds[kThreads / 64];
+  const double tot =
+      fan_block_sum(x, n, static_cast<int64_t>(blockIdx.x) * kReduceFan, lds);
   if (threadIdx.x == 0) y[blockIdx.x] = tot;
 }
 
@@ -380,22 +404,45 @@ __global__ __launch_bounds__(kThreads) void sqnorm_final_kernel(const double* __
                                                                 double* __restrict__ sqnorm_out,
                                                                 float* __restrict__ scale_out) {
   __shared__ double lds[kThreads / 64];
-  double s = 0.0;
-#pragma unroll
-  for (int k = 0; k < kReduceFan / kThreads; ++k) {
-    const int64_t i = k * kThreads + threadIdx.x;
-    if (i < n) s += x[i];
-  }
-  const double tot = block_sum_fixed(s, lds);
+  const double tot = fan_block_sum(x, n, 0, lds);
   if (threadIdx.x == 0) {
-    float scale = 1.0f;
-    if (max_norm > 0.0) {
-      const double norm = sqrt(tot);
-      if (norm > max_norm) scale = static_cast<float>(max_norm / norm);
-    }
     if (sqnorm_out != nullptr) *sqnorm_out = tot;
-    if (scale_out != nullptr) *scale_out = scale;
+    if (scale_out != nullptr) *scale_out = clip_factor(tot, max_norm);
   }
+}
+
+// Piece sums of one fp32 array: piece p is [p*4096, (p+1)*4096), one
+// workgroup, the same lane mapping and accumulation order as the reduce
+// kernel's (access k of lane l: the 4 elements at k*1024 + 4*l, squares
+// accumulated in fp64 with one rounding each, then block_sum_fixed).
+__global__ __launch_bounds__(kThreads) void piece_sqnorm_kernel(const float* __restrict__ g,
+                                                                int64_t n, int vec,
+                                                                double* __restrict__ partials) {
+  constexpr int G = 4;
+  constexpr int K = GRZ_PIECE / (kThreads * G);
+  __shared__ double lds[kThreads / 64];
+  const int64_t e0 = static_cast<int64_t>(blockIdx.x) * GRZ_PIECE;
+  const int64_t left = n - e0;
+  double sq = 0.0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t rel = static_cast<int64_t>(k * kThreads + threadIdx.x) * G;
+    if (vec && rel + G <= left) {
+      float x[G];
+      loadg<kNtLoad>(g + e0 + rel, x);
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+        sq = __fma_rn(static_cast<double>(x[i]), static_cast<double>(x[i]), sq);
+    } else {
+      for (int i = 0; i < G; ++i) {
+        if (rel + i >= left) break;
+        const double x = g[e0 + rel + i];
+        sq = __fma_rn(x, x, sq);
+      }
+    }
+  }
+  const double tot = block_sum_fixed(sq, lds);
+  if (threadIdx.x == 0) partials[blockIdx.x] = tot;
 }
 
 // ---------------------------------------------------------------------------
@@ -540,6 +587,231 @@ __global__ __launch_bounds__(kThreads) GRZ_AG_ATTR void gather_kernel(const Gath
           if (rel + j >= left) break;
           const uint16_t u = src[s.src + e + j];
           for (int r = 0; r < a.nrep; ++r) a.rep[r][s.dst + e + j] = u;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K1 + K2 + K3 in one launch, for a shard whose mean fits in the registers of
+// the co-resident grid: the reduce keeps every mean value in registers, a
+// grid-wide barrier waits for every piece sum, each workgroup folds the norm
+// in the same tree as dp_grad_sqnorm, and the same registers feed AdamW.  The
+// mean never goes to memory (unless asked for), which saves 8 bytes per owned
+// element against the three-kernel path.  The arithmetic of every value is
+// that of rs_mean_kernel, sqnorm_*_kernel and adamw_kernel, so the results are
+// the same bits.  The launch is cooperative, which makes the runtime refuse a
+// grid that cannot be resident at once; every wait is bounded as well.
+
+constexpr int kFusedPieces = 4;   // pieces (tiles) a workgroup holds in registers
+constexpr int kFusedSegs = 32;    // segments per launch
+
+// A segment of the fused launch: offsets of one chunk of one bucket in the
+// rank inputs (`in`), in master/m/v and the optional mean (`st`) and in the
+// replica arenas (`glob`).  vec bit 0: the reduce accesses are 16/8-byte
+// aligned; bit 1: the state and replica accesses are.
+struct FSeg {
+  int64_t in;
+  int64_t st;
+  int64_t glob;
+  int64_t len;
+  int64_t piece0;
+  int64_t tile0;
+  int32_t chunk;
+  int32_t vec;
+};
+
+template <typename TIn>
+struct FusedArgs {
+  const TIn* rank[GRZ_MAX_RANKS];
+  uint16_t* rep[GRZ_MAX_RANKS];
+  float* master;
+  float* m;
+  float* v;
+  float* mean_out;                // optional copy of the mean
+  double* partials;               // piece sums of the whole plan (peers' filled in)
+  double* level;                  // first-level sums of the norm tree
+  unsigned* sync;                 // barrier words: arrivals, generation, timeout flag
+  double* sqnorm_out;
+  float* scale_out;
+  const grz_adamw_args* dargs;    // step scalars in device memory, or null
+  double max_norm;
+  double divisor;
+  int64_t ntiles;                 // pieces this launch reduces
+  int64_t npieces;                // pieces of the plan
+  int nranks;
+  int nrep;
+  int nsegs;
+  int pow2;
+  unsigned spin_limit;
+  float lr, b1, b2, eps, wd, bc1, bc2;
+  FSeg seg[kFusedSegs];
+};
+
+// Grid-wide barrier over `nblocks` co-resident workgroups.  One thread per
+// workgroup reads the generation, publishes the workgroup's writes (device-
+// scope fence), counts itself in, and either (last to arrive) resets the
+// count and advances the generation, or waits for the generation to move.
+// The wait gives up after `spin_limit` polls and raises sync[2], so a grid
+// that is not resident at once ends with a flag instead of waiting forever.
+// The count is back at zero after every completed barrier, so consecutive
+// launches reuse the words without clearing them.
+__device__ __forceinline__ void grid_barrier(unsigned* sync, unsigned nblocks,
+                                             unsigned spin_limit) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned gen = __hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __threadfence();
+    const unsigned arrived =
+        __hip_atomic_fetch_add(sync, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (arrived == nblocks - 1) {
+      __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      unsigned polls = 0;
+      while (__hip_atomic_load(sync + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+        __builtin_amdgcn_s_sleep(4);
+        if (++polls >= spin_limit) {
+          __hip_atomic_store(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    __threadfence();
+  }
+  __syncthreads();
+}
+
+// At most 128 VGPRs, so that 4 waves per SIMD (4 workgroups per CU) fit: the
+// 64 mean registers per lane plus the fold's and AdamW's working set.
+template <typename TIn, int NR, bool WIRE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void fused_step_kernel(const FusedArgs<TIn> a) {
+  constexpr int G = 4;
+  constexpr int K = GRZ_PIECE / (kThreads * G);
+  __shared__ double lds[kThreads / 64];
+  const float nf = static_cast<float>(a.divisor);
+  const float inv = 1.0f / nf;
+  const int lane = threadIdx.x;
+  float mean[kFusedPieces][K][G];
+
+  // Reduce: the pieces blockIdx.x, blockIdx.x + gridDim.x, ... of the launch.
+#pragma unroll
+  for (int p = 0; p < kFusedPieces; ++p) {
+    const int64_t tile = blockIdx.x + static_cast<int64_t>(p) * gridDim.x;
+    if (tile < a.ntiles) {
+      const FSeg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
+      const int64_t piece = tile - s.tile0;
+      const int64_t e0 = piece * GRZ_PIECE;
+      const int64_t left = s.len - e0;
+      double sq = 0.0;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t rel = static_cast<int64_t>(k * kThreads + lane) * G;
+        const int64_t e = e0 + rel;
+        if ((s.vec & 1) && rel + G <= left) {
+          fold_vec<TIn, NR, WIRE>(a.rank, a.nranks, s.chunk, s.in + e, mean[p][k]);
+#pragma unroll
+          for (int i = 0; i < G; ++i) {
+            mean[p][k][i] = a.pow2 ? mean[p][k][i] * inv : mean[p][k][i] / nf;
+            sq = __fma_rn(static_cast<double>(mean[p][k][i]),
+                          static_cast<double>(mean[p][k][i]), sq);
+          }
+          if (a.mean_out != nullptr) storeg<GRZ_RS_POLICY>(a.mean_out + s.st + e, mean[p][k]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < G; ++i) {
+            float x = 0.0f;
+            if (rel + i < left) {
+              x = fold_one<TIn, NR, WIRE>(a.rank, a.nranks, s.chunk, s.in + e + i);
+              x = a.pow2 ? x * inv : x / nf;
+              sq = __fma_rn(static_cast<double>(x), static_cast<double>(x), sq);
+              if (a.mean_out != nullptr) a.mean_out[s.st + e + i] = x;
+            }
+            mean[p][k][i] = x;
+          }
+        }
+      }
+      const double tot = block_sum_fixed(sq, lds);
+      if (lane == 0) a.partials[s.piece0 + piece] = tot;
+    }
+  }
+  grid_barrier(a.sync, gridDim.x, a.spin_limit);
+
+  // Norm: the tree of dp_grad_sqnorm (at most one level below the final fold).
+  double sqnorm;
+  if (a.npieces > kReduceFan) {
+    const int64_t nl = (a.npieces + kReduceFan - 1) / kReduceFan;
+    for (int64_t b = blockIdx.x; b < nl; b += gridDim.x) {
+      const double t = fan_block_sum(a.partials, a.npieces, b * kReduceFan, lds);
+      if (lane == 0) a.level[b] = t;
+    }
+    grid_barrier(a.sync, gridDim.x, a.spin_limit);
+    sqnorm = fan_block_sum(a.level, nl, 0, lds);
+  } else {
+    sqnorm = fan_block_sum(a.partials, a.npieces, 0, lds);
+  }
+  const float scale = clip_factor(sqnorm, a.max_norm);
+  if (blockIdx.x == 0 && lane == 0) {
+    if (a.sqnorm_out != nullptr) *a.sqnorm_out = sqnorm;
+    if (a.scale_out != nullptr) *a.scale_out = scale;
+  }
+
+  // Clip + AdamW from the registers; bf16 weights into every replica.
+  float lr = a.lr, b1 = a.b1, b2 = a.b2, eps = a.eps, wd = a.wd, bc1 = a.bc1, bc2 = a.bc2;
+  if (a.dargs != nullptr) {
+    const grz_adamw_args d = *a.dargs;
+    lr = d.lr; b1 = d.beta1; b2 = d.beta2; eps = d.eps; wd = d.weight_decay;
+    bc1 = d.bias_corr1; bc2 = d.bias_corr2;
+  }
+  const float omb1 = 1.0f - b1;
+  const float omb2 = 1.0f - b2;
+#pragma unroll
+  for (int p = 0; p < kFusedPieces; ++p) {
+    const int64_t tile = blockIdx.x + static_cast<int64_t>(p) * gridDim.x;
+    if (tile < a.ntiles) {
+      const FSeg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
+      const int64_t e0 = (tile - s.tile0) * GRZ_PIECE;
+      const int64_t left = s.len - e0;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t rel = static_cast<int64_t>(k * kThreads + lane) * G;
+        const int64_t e = e0 + rel;
+        if ((s.vec & 2) && rel + G <= left) {
+          const int64_t i = s.st + e;
+          float w[G], m[G], v[G];
+          loadg<GRZ_ADAM_POLICY>(a.master + i, w);
+          loadg<GRZ_ADAM_POLICY>(a.m + i, m);
+          loadg<GRZ_ADAM_POLICY>(a.v + i, v);
+          uint32_t b[G];
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            adamw1(w[j], m[j], v[j], mean[p][k][j] * scale, lr, b1, omb1, b2, omb2, eps, wd,
+                   bc1, bc2);
+            b[j] = bf16_rne(w[j]);
+          }
+          storeg<GRZ_ADAM_POLICY>(a.master + i, w);
+          storeg<GRZ_ADAM_POLICY>(a.m + i, m);
+          storeg<GRZ_ADAM_POLICY>(a.v + i, v);
+          u32x2 packed;
+          packed[0] = b[0] | (b[1] << 16);
+          packed[1] = b[2] | (b[3] << 16);
+          for (int r = 0; r < a.nrep; ++r) stv<GRZ_ADAM_POLICY>(a.rep[r] + s.glob + e, packed);
+        } else {
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            if (rel + j < left) {
+              const int64_t i = s.st + e + j;
+              float w = a.master[i], m = a.m[i], v = a.v[i];
+              adamw1(w, m, v, mean[p][k][j] * scale, lr, b1, omb1, b2, omb2, eps, wd, bc1, bc2);
+              a.master[i] = w;
+              a.m[i] = m;
+              a.v[i] = v;
+              const uint16_t b = static_cast<uint16_t>(bf16_rne(w));
+              for (int r = 0; r < a.nrep; ++r) a.rep[r][s.glob + e + j] = b;
+            }
+          }
         }
       }
     }
@@ -914,6 +1186,30 @@ int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
   return GRZ_OK;
 }
 
+size_t dp_grad_sqnorm_of_workspace(int64_t n) {
+  if (n <= 0) return 0;
+  const int64_t npieces = ceil_div(n, GRZ_PIECE);
+  return static_cast<size_t>(npieces) * sizeof(double) + dp_grad_sqnorm_workspace(npieces);
+}
+
+int dp_grad_sqnorm_of(const float* grad, int64_t n, double max_norm, void* workspace,
+                      double* sqnorm_out, float* clip_scale_out, hipStream_t stream) {
+  if (n < 0 || (n > 0 && (grad == nullptr || workspace == nullptr))) return GRZ_EINVAL;
+  if (sqnorm_out == nullptr && clip_scale_out == nullptr) return GRZ_EINVAL;
+  if (!aligned(grad, 4) || !aligned(workspace, 8)) return GRZ_EALIGN;
+  const int64_t npieces = ceil_div(n, GRZ_PIECE);
+  if (npieces > static_cast<int64_t>(kReduceFan) * kReduceFan * kReduceFan) return GRZ_ERANGE;
+  double* partials = static_cast<double*>(workspace);
+  if (npieces > 0) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(piece_sqnorm_kernel, dim3(static_cast<unsigned>(npieces)),
+                       dim3(kThreads), 0, stream, grad, n, aligned(grad, 16) ? 1 : 0, partials);
+    if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
+  }
+  return dp_grad_sqnorm(partials, npieces, max_norm, partials + npieces, sqnorm_out,
+                        clip_scale_out, stream);
+}
+
 static int adamw_common(float* master, float* m, float* v, const float* mean_grad,
                         const std::vector<PlanSeg>& ps, const float* clip_scale,
                         const grz_adamw_args* args, bool args_on_device,
@@ -1051,6 +1347,199 @@ int zero1_all_gather(const uint16_t* const* shards, int nranks, const grz_bucket
     }
   }
   return launch_batches(segs, a, gather_kernel, stream);
+}
+
+int grz_set_spin_limit(unsigned polls) {
+  if (polls < 1) return GRZ_EINVAL;
+  g_spin_limit = polls;
+  return GRZ_OK;
+}
+
+size_t zero1_fused_workspace(int64_t npieces) {
+  const int64_t nl = npieces > kReduceFan ? ceil_div(npieces, kReduceFan) : 0;
+  return 64 + static_cast<size_t>(nl) * sizeof(double);
+}
+
+}  // extern "C"
+
+namespace {
+
+template <typename TIn, int NR, bool WIRE>
+const void* fused_kernel_ptr() {
+  return reinterpret_cast<const void*>(&fused_step_kernel<TIn, NR, WIRE>);
+}
+
+// The fused kernel instance for (dtype, N), or null.  (The bf16-wire fold is
+// not instantiated here: its per-hop rounding does not fit the register
+// budget next to the held mean.)
+const void* fused_kernel_for(int dtype, int nranks) {
+  if (dtype == GRZ_BF16) {
+    switch (nranks) {
+      case 1: return fused_kernel_ptr<uint16_t, 1, false>();
+      case 2: return fused_kernel_ptr<uint16_t, 2, false>();
+      case 4: return fused_kernel_ptr<uint16_t, 4, false>();
+      case 8: return fused_kernel_ptr<uint16_t, 8, false>();
+      default: return fused_kernel_ptr<uint16_t, 0, false>();
+    }
+  }
+  if (dtype == GRZ_F32) {
+    switch (nranks) {
+      case 1: return fused_kernel_ptr<float, 1, false>();
+      case 2: return fused_kernel_ptr<float, 2, false>();
+      case 4: return fused_kernel_ptr<float, 4, false>();
+      case 8: return fused_kernel_ptr<float, 8, false>();
+      default: return fused_kernel_ptr<float, 0, false>();
+    }
+  }
+  return nullptr;
+}
+
+// Workgroups of `kernel` that can be resident at once on the current device.
+int fused_max_grid(const void* kernel, int* grid) {
+  int dev = 0, cus = 0, coop = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GRZ_EHIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess)
+    return GRZ_EHIP;
+  if (!coop) return GRZ_EHIP;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess)
+    return GRZ_EHIP;
+  *grid = per_cu * cus;
+  return *grid > 0 ? GRZ_OK : GRZ_EHIP;
+}
+
+template <typename TIn>
+int fused_launch(const void* kernel, const void* const* rank_grads, int nranks,
+                 const std::vector<PlanSeg>& ps, int flags, float* master, float* m, float* v,
+                 const grz_adamw_args* args, double max_norm, uint16_t* const* replicas,
+                 int nreplicas, double* piece_sqnorm, int64_t npieces, void* workspace,
+                 double* sqnorm_out, float* clip_scale_out, float* mean_out,
+                 hipStream_t stream) {
+  static FusedArgs<TIn> proto;
+  FusedArgs<TIn> a = proto;
+  constexpr size_t in_bytes = 4 * sizeof(TIn);
+  bool vin = mean_out == nullptr || aligned(mean_out, 16);
+  for (int j = 0; j < nranks; ++j) {
+    if (!aligned(rank_grads[j], sizeof(TIn))) return GRZ_EALIGN;
+    vin = vin && aligned(rank_grads[j], in_bytes);
+    a.rank[j] = static_cast<const TIn*>(rank_grads[j]);
+  }
+  bool vst = aligned(master, 16) && aligned(m, 16) && aligned(v, 16);
+  for (int r = 0; r < nreplicas; ++r) {
+    vst = vst && aligned(replicas[r], 8);
+    a.rep[r] = replicas[r];
+  }
+  const bool compact_in = (flags & GRZ_IN_COMPACT) != 0;
+  int64_t tiles = 0;
+  int nsegs = 0;
+  for (const PlanSeg& p : ps) {
+    FSeg& s = a.seg[nsegs++];
+    s.in = compact_in ? p.compact : p.input;
+    s.st = p.compact;
+    s.glob = p.global;
+    s.len = p.len;
+    s.piece0 = p.piece0;
+    s.tile0 = tiles;
+    s.chunk = p.chunk;
+    s.vec = ((vin && (s.in * sizeof(TIn)) % in_bytes == 0 && s.st % 4 == 0) ? 1 : 0) |
+            ((vst && s.st % 4 == 0 && s.glob % 4 == 0) ? 2 : 0);
+    tiles += ceil_div(p.len, GRZ_PIECE);
+  }
+  int max_grid = 0;
+  const int st = fused_max_grid(kernel, &max_grid);
+  if (st != GRZ_OK) return st;
+  if (tiles > static_cast<int64_t>(max_grid) * kFusedPieces) return GRZ_ERANGE;
+  const int grid = tiles == 0 ? 1 : static_cast<int>(tiles < max_grid ? tiles : max_grid);
+  a.master = master;
+  a.m = m;
+  a.v = v;
+  a.mean_out = mean_out;
+  a.partials = piece_sqnorm;
+  a.sync = static_cast<unsigned*>(workspace);
+  a.level = reinterpret_cast<double*>(static_cast<char*>(workspace) + 64);
+  a.sqnorm_out = sqnorm_out;
+  a.scale_out = clip_scale_out;
+  a.max_norm = max_norm;
+  a.divisor = static_cast<double>(nranks);
+  a.pow2 = (nranks & (nranks - 1)) == 0;
+  a.ntiles = tiles;
+  a.npieces = npieces;
+  a.nranks = nranks;
+  a.nrep = nreplicas;
+  a.nsegs = nsegs;
+  a.spin_limit = g_spin_limit;
+  if (flags & GRZ_ARGS_DEVICE) {
+    a.dargs = args;
+  } else {
+    a.lr = args->lr;
+    a.b1 = args->beta1;
+    a.b2 = args->beta2;
+    a.eps = args->eps;
+    a.wd = args->weight_decay;
+    a.bc1 = args->bias_corr1;
+    a.bc2 = args->bias_corr2;
+  }
+  void* params[] = {&a};
+  (void)hipGetLastError();
+  if (hipLaunchCooperativeKernel(kernel, dim3(grid), dim3(kThreads), params, 0, stream) !=
+      hipSuccess)
+    return GRZ_EHIP;
+  return hipGetLastError() == hipSuccess ? GRZ_OK : GRZ_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t zero1_fused_capacity(int nranks, int dtype) {
+  if (nranks < 1 || nranks > GRZ_MAX_RANKS) return -GRZ_EINVAL;
+  const void* kernel = fused_kernel_for(dtype, nranks);
+  if (kernel == nullptr) return -GRZ_EINVAL;
+  int grid = 0;
+  const int st = fused_max_grid(kernel, &grid);
+  if (st != GRZ_OK) return -st;
+  return static_cast<int64_t>(grid) * kFusedPieces;
+}
+
+int zero1_fused_step(const void* const* rank_grads, int nranks, int dtype,
+                     const grz_bucket* buckets, int nbuckets, int chunk, int flags,
+                     float* master, float* m, float* v, const grz_adamw_args* args,
+                     double max_norm, uint16_t* const* replicas, int nreplicas,
+                     double* piece_sqnorm, void* workspace, double* sqnorm_out,
+                     float* clip_scale_out, float* mean_out, hipStream_t stream) {
+  if (flags & ~(GRZ_UNEVEN | GRZ_IN_COMPACT | GRZ_ARGS_DEVICE)) return GRZ_EINVAL;
+  int st = check_plan(buckets, nbuckets, nranks, chunk, flags & ~GRZ_ARGS_DEVICE);
+  if (st != GRZ_OK) return st;
+  if ((flags & GRZ_IN_COMPACT) && chunk < 0) return GRZ_EINVAL;
+  const void* kernel = fused_kernel_for(dtype, nranks);
+  if (kernel == nullptr) return GRZ_EINVAL;
+  if (rank_grads == nullptr || master == nullptr || m == nullptr || v == nullptr ||
+      args == nullptr || piece_sqnorm == nullptr || workspace == nullptr)
+    return GRZ_EINVAL;
+  for (int j = 0; j < nranks; ++j)
+    if (rank_grads[j] == nullptr) return GRZ_EINVAL;
+  if (nreplicas < 0 || nreplicas > GRZ_MAX_RANKS) return GRZ_EINVAL;
+  if (nreplicas > 0 && replicas == nullptr) return GRZ_EINVAL;
+  for (int r = 0; r < nreplicas; ++r) {
+    if (replicas[r] == nullptr) return GRZ_EINVAL;
+    if (!aligned(replicas[r], 2)) return GRZ_EALIGN;
+  }
+  if (!aligned(master, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(mean_out, 4) ||
+      !aligned(piece_sqnorm, 8) || !aligned(workspace, 8) || !aligned(sqnorm_out, 8) ||
+      !aligned(clip_scale_out, 4) || !aligned(args, 4))
+    return GRZ_EALIGN;
+  const int64_t npieces = dp_piece_count(buckets, nbuckets, nranks, flags & GRZ_UNEVEN);
+  if (npieces < 0) return static_cast<int>(-npieces);
+  if (npieces > static_cast<int64_t>(kReduceFan) * kReduceFan) return GRZ_ERANGE;
+  std::vector<PlanSeg> ps = plan_segments(buckets, nbuckets, nranks, chunk);
+  if (ps.size() > static_cast<size_t>(kFusedSegs)) return GRZ_ERANGE;
+  if (dtype == GRZ_BF16)
+    return fused_launch<uint16_t>(kernel, rank_grads, nranks, ps, flags, master, m, v, args,
+                                  max_norm, replicas, nreplicas, piece_sqnorm, npieces,
+                                  workspace, sqnorm_out, clip_scale_out, mean_out, stream);
+  return fused_launch<float>(kernel, rank_grads, nranks, ps, flags, master, m, v, args,
+                             max_norm, replicas, nreplicas, piece_sqnorm, npieces, workspace,
+                             sqnorm_out, clip_scale_out, mean_out, stream);
 }
 
 }  // extern "C"

@@ -16,6 +16,9 @@ kernels):
   (received), AdamW on its shard, then assemble its full bf16 arena from its
   own shard and the peers' received shards.
 
+``Zero1OneRank`` and ``DDPStep`` take ``fused=True`` to run reduce, norm,
+clip and AdamW as one launch (``zero1_fused_step``) when the shard fits.
+
 The step order is "A4 -- Multi-GPU with NCCL and ZeRO-1", "Part 4":
 reduce-scatter, AdamW on the shard, all-gather; with the clip in between as in
 "Distributed training", "Four strategies, one interface".  The host only
@@ -53,6 +56,11 @@ class _Norm:
     def run(self, max_norm, stream=None):
         B.dp_grad_sqnorm(self.partials, max_norm, self.workspace, self.sqnorm, self.scale,
                          npieces=self.npieces, stream=stream)
+
+
+def _fused_workspace(npieces, device):
+    """Zeroed workspace of the one-launch step (barrier words + norm level)."""
+    return torch.zeros(B.zero1_fused_workspace(npieces), dtype=torch.uint8, device=device)
 
 
 class Zero1AllRanks:
@@ -94,20 +102,36 @@ class Zero1AllRanks:
 
 
 class DDPStep:
-    """Plain data-parallel step as one replica computes it."""
+    """Plain data-parallel step as one replica computes it.
 
-    def __init__(self, buckets, nranks, master, hyper=None, device="cuda", reduce_flags=0):
+    ``fused=True`` runs the step as one ``zero1_fused_step`` launch (the mean
+    stays in registers; the arena must fit ``zero1_fused_capacity``)."""
+
+    def __init__(self, buckets, nranks, master, hyper=None, device="cuda", reduce_flags=0,
+                 fused=False):
         self.buckets = [(int(o), int(l)) for o, l in buckets]
         self.n = nranks
         self.hyper = hyper or Hyper()
         self.reduce_flags = reduce_flags
+        self.fused = fused
         w = master.to(device=device, dtype=torch.float32).clone()
         self.state = (w, torch.zeros_like(w), torch.zeros_like(w))
-        self.mean = torch.zeros_like(w)
         self.norm = _Norm(B.dp_piece_count(self.buckets, nranks), device)
+        self.mean = None if fused else torch.zeros_like(w)
+        self.workspace = _fused_workspace(self.norm.npieces, device) if fused else None
         self.replica = w.to(torch.bfloat16)
 
     def step(self, rank_grads, t, stream=None, token_counts=None):
+        if self.fused:
+            if token_counts is not None:
+                raise ValueError("the fused step takes the plain mean")
+            w, m, v = self.state
+            B.zero1_fused_step(rank_grads, self.buckets, -1, w, m, v,
+                               B.adamw_args(**step_scalars(self.hyper, t)),
+                               self.hyper.max_norm, [self.replica], self.norm.partials,
+                               self.workspace, self.norm.sqnorm, self.norm.scale,
+                               flags=self.reduce_flags, stream=stream)
+            return
         B.dp_reduce_scatter_mean(rank_grads, self.buckets, -1, self.mean, self.norm.partials,
                                  flags=self.reduce_flags, stream=stream,
                                  token_counts=token_counts)
@@ -132,9 +156,10 @@ class Zero1OneRank:
     """
 
     def __init__(self, buckets, nranks, rank, shard_master, hyper=None, device="cuda",
-                 arena_numel=None, reduce_flags=0):
+                 arena_numel=None, reduce_flags=0, fused=False):
         self.buckets = [(int(o), int(l)) for o, l in buckets]
         self.reduce_flags = reduce_flags
+        self.fused = fused
         self.n, self.rank = nranks, rank
         self.chunk = owned_chunk(rank, nranks)
         self.hyper = hyper or Hyper()
@@ -142,8 +167,9 @@ class Zero1OneRank:
         if w.numel() != B.dp_shard_numel(self.buckets, nranks, self.chunk):
             raise ValueError("shard_master does not match the plan's shard")
         self.state = (w, torch.zeros_like(w), torch.zeros_like(w))
-        self.mean = torch.empty_like(w)
+        self.mean = None if fused else torch.empty_like(w)
         self.norm = _Norm(B.dp_piece_count(self.buckets, nranks), device)
+        self.workspace = _fused_workspace(self.norm.npieces, device) if fused else None
         ext = arena_numel or max(o + l for o, l in self.buckets)
         self.arena = torch.zeros(ext, dtype=torch.bfloat16, device=device)
 
@@ -174,14 +200,28 @@ class Zero1OneRank:
     def gather(self, peer_shards, stream=None):
         B.zero1_all_gather(peer_shards, self.buckets, [self.arena], stream=stream)
 
+    def fused_update(self, incoming, args, stream=None):
+        """reduce + update as one launch (the mean never leaves the registers)."""
+        w, m, v = self.state
+        B.zero1_fused_step(incoming, self.buckets, self.chunk, w, m, v, args,
+                           self.hyper.max_norm, [self.arena], self.norm.partials,
+                           self.workspace, self.norm.sqnorm, self.norm.scale,
+                           flags=GRZ_IN_COMPACT | self.reduce_flags, stream=stream)
+
     def step(self, incoming, peer_shards, t, stream=None):
-        self.reduce(incoming, stream)
-        self.update(t, stream)
+        if self.fused:
+            self.fused_update(incoming, B.adamw_args(**step_scalars(self.hyper, t)), stream)
+        else:
+            self.reduce(incoming, stream)
+            self.update(t, stream)
         self.gather(peer_shards, stream)
 
     def enqueue(self, incoming, peer_shards, args, stream=None):
-        self.reduce(incoming, stream)
-        self.update(None, stream, args=args)
+        if self.fused:
+            self.fused_update(incoming, args, stream)
+        else:
+            self.reduce(incoming, stream)
+            self.update(None, stream, args=args)
         self.gather(peer_shards, stream)
 
 

@@ -6,9 +6,11 @@
  *
  *   dp_reduce_scatter_mean   ring-order average of the ranks' gradients
  *   dp_grad_sqnorm           global squared norm and clip factor
+ *   dp_grad_sqnorm_of        the same, straight from an fp32 gradient array
  *   zero1_adamw_step         clipped AdamW on the owned shard (+ bf16 copy,
  *                            optionally written straight into the replicas)
  *   zero1_all_gather         owned bf16 shards into every replica arena
+ *   zero1_fused_step         the four above for one shard in one launch
  *
  * Sources: "Lab 09 -- Parallelism, simulated" s.1 "Ring all-reduce" (the
  * N = 3 schedule table; "Tips": in reduce-scatter step t rank r sends chunk
@@ -24,11 +26,11 @@
  *
  *  - Memory.  Every pointer named "device" is HIP device memory owned by the
  *    caller; the library allocates nothing and keeps no state between calls
- *    (apart from the launch-width knob of grz_set_max_blocks), so concurrent
- *    calls on different streams are safe when they touch disjoint buffers.
- *    Buffers must stay alive until the stream has run the enqueued work.
- *    Host arrays (pointer tables, bucket lists, argument structs) are read
- *    during the call only.
+ *    (apart from the knobs grz_set_max_blocks and grz_set_spin_limit), so
+ *    concurrent calls on different streams are safe when they touch
+ *    disjoint buffers.  Buffers must stay alive until the stream has run the
+ *    enqueued work.  Host arrays (pointer tables, bucket lists, argument
+ *    structs) are read during the call only.
  *  - Streams.  Work is enqueued on `stream` (0 = the null stream).  No entry
  *    point synchronises the host: results are ready when the stream is.
  *  - Errors.  Arguments are checked before anything is enqueued; on a bad
@@ -245,6 +247,29 @@ int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
                    void* workspace, double* sqnorm_out, float* clip_scale_out,
                    hipStream_t stream);
 
+/* Bytes of workspace dp_grad_sqnorm_of needs for `n` gradient elements. */
+size_t dp_grad_sqnorm_of_workspace(int64_t n);
+
+/*
+ * dp_grad_sqnorm over a plain fp32 gradient array that is already reduced
+ * (one chunk of one bucket): the library forms the piece sums itself, pieces
+ * of GRZ_PIECE consecutive elements summed exactly as dp_reduce_scatter_mean
+ * sums them, then combines them in the same tree.  So the result equals, bit
+ * for bit, dp_reduce_scatter_mean of a single rank (N = 1, one bucket of `n`
+ * elements) followed by dp_grad_sqnorm ("Distributed training",
+ * clip_grads_device(max_norm) on a flat fp32 arena).
+ *
+ * grad          device fp32, `n` elements (any 4-byte alignment).
+ * workspace     device, dp_grad_sqnorm_of_workspace(n) bytes, 8-byte aligned;
+ *               on return it holds the ceil(n / GRZ_PIECE) piece sums first.
+ * sqnorm_out, clip_scale_out, max_norm  as for dp_grad_sqnorm (either output
+ *               may be NULL, not both).
+ * Errors: GRZ_EINVAL for a NULL grad/workspace with n > 0, both outputs NULL
+ * or n < 0; GRZ_EALIGN; GRZ_ERANGE beyond 4096^3 pieces.
+ */
+int dp_grad_sqnorm_of(const float* grad, int64_t n, double max_norm, void* workspace,
+                      double* sqnorm_out, float* clip_scale_out, hipStream_t stream);
+
 /*
  * Clipped AdamW on one rank's shard ("A4", "Part 4": adamw_update only for
  * this rank's shard; "Distributed training", step()).
@@ -306,6 +331,76 @@ int grz_step_args_next(const grz_adamw_args* table, int64_t count, int64_t* coun
 int zero1_all_gather(const uint16_t* const* shards, int nranks, const grz_bucket* buckets,
                      int nbuckets, int flags, uint16_t* const* replicas, int nreplicas,
                      hipStream_t stream);
+
+/*
+ * Polls a grid-wide wait of zero1_fused_step makes before it gives up (>= 1;
+ * default 2^22, a few seconds).  Process-wide, like grz_set_max_blocks.
+ */
+int grz_set_spin_limit(unsigned polls);
+
+/* Bytes of workspace zero1_fused_step needs for a plan of `npieces` pieces. */
+size_t zero1_fused_workspace(int64_t npieces);
+
+/*
+ * Pieces (GRZ_PIECE-element tiles of the reduced chunks) that one
+ * zero1_fused_step launch can hold for N ranks of `dtype` gradients on the
+ * current device: 4 per workgroup that can be resident at once (1024
+ * workgroups on a 256-CU MI355X, so 4096 pieces, 16.8 M elements).  A
+ * negative value is minus a GRZ_E* code.
+ */
+int64_t zero1_fused_capacity(int nranks, int dtype);
+
+/*
+ * The whole step of one shard in one launch: reduce-scatter-mean, global
+ * norm, clip, AdamW and the bf16 write ("A4", "Part 4": reduce, update the
+ * shard, all-gather; "Distributed training", "Four strategies, one
+ * interface": clip_grads_device then step), for a shard small enough that
+ * its mean stays in registers.  Every result is bit-identical to
+ *   dp_reduce_scatter_mean -> dp_grad_sqnorm -> zero1_adamw_gather
+ * on the same inputs; the mean itself is never stored unless `mean_out` is
+ * given, which saves 8 bytes of memory traffic per owned element.  The grid
+ * synchronises internally (all pieces summed before the norm is read), so
+ * the launch is cooperative: HIP refuses it rather than start a grid that
+ * cannot be resident at once.
+ *
+ * rank_grads, nranks, dtype, buckets, nbuckets, chunk
+ *            as for dp_reduce_scatter_mean; dtype GRZ_BF16 or GRZ_F32.
+ *            chunk >= 0: one rank's ZeRO-1 shard (master/m/v and mean_out
+ *            shard-compact); chunk = -1: every chunk (plain data parallelism,
+ *            master/m/v indexed like the arena).
+ * flags      GRZ_UNEVEN, GRZ_IN_COMPACT (as for the reduce), GRZ_ARGS_DEVICE
+ *            (as for zero1_adamw_gather).  GRZ_BF16_WIRE and GRZ_SUM are
+ *            not taken (GRZ_EINVAL): use the separate entry points.
+ * master, m, v  device fp32 state, updated in place.
+ * args       the step's scalars (host, or device with GRZ_ARGS_DEVICE).
+ * max_norm   clip threshold (<= 0: no clipping).
+ * replicas   host array of `nreplicas` device bf16 arenas (0..16); each gets
+ *            the new weights of the processed chunks at their arena offsets.
+ * piece_sqnorm device fp64, dp_piece_count entries.  The kernel writes the
+ *            pieces of the processed chunks; the other entries (the peers'
+ *            pieces, when chunk >= 0) must hold their values already.
+ * workspace  device, zero1_fused_workspace(npieces) bytes, 8-byte aligned,
+ *            ZEROED before its first use.  Its first three 32-bit words are
+ *            the grid barrier's (arrival count, generation, time-out flag);
+ *            a completed call leaves the count at zero, so the workspace is
+ *            reused without clearing.  A non-zero third word means a wait
+ *            gave up (grz_set_spin_limit): that call's results are invalid
+ *            and the workspace must be zeroed again.  Calls that share a
+ *            workspace must not overlap.
+ * sqnorm_out, clip_scale_out  device scalars as for dp_grad_sqnorm, or NULL.
+ * mean_out   device fp32 copy of the mean (as dp_reduce_scatter_mean writes
+ *            it), or NULL.
+ * Errors: as dp_reduce_scatter_mean and zero1_adamw_gather; GRZ_ERANGE when
+ * the plan has more pieces than zero1_fused_capacity, more than 32 (bucket,
+ * chunk) segments, or more than 4096^2 pieces in all; GRZ_EHIP when the
+ * device cannot launch cooperatively.
+ */
+int zero1_fused_step(const void* const* rank_grads, int nranks, int dtype,
+                     const grz_bucket* buckets, int nbuckets, int chunk, int flags,
+                     float* master, float* m, float* v, const grz_adamw_args* args,
+                     double max_norm, uint16_t* const* replicas, int nreplicas,
+                     double* piece_sqnorm, void* workspace, double* sqnorm_out,
+                     float* clip_scale_out, float* mean_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -112,3 +112,36 @@ def test_product_path_refuses_cpu_tensors():
     with pytest.raises(ValueError, match="GPU"):
         grz.dp_reduce_scatter_mean([torch.zeros(64), torch.zeros(64)], [(0, 64)], 0,
                                    torch.zeros(32))
+
+
+def test_norm_and_fused_workspace_sizes():
+    assert grz.dp_grad_sqnorm_of_workspace(0) == 0
+    assert grz.dp_grad_sqnorm_of_workspace(1) == 8
+    assert grz.dp_grad_sqnorm_of_workspace(4096 * 4097) == 4097 * 8 + 2 * 8
+    assert grz.zero1_fused_workspace(0) == 64
+    assert grz.zero1_fused_workspace(4096) == 64
+    assert grz.zero1_fused_workspace(4097) == 64 + 2 * 8
+    assert grz.zero1_fused_workspace(4096 * 4096) == 64 + 4096 * 8
+
+
+def test_fused_step_refusals_before_any_launch():
+    # Checked on the host before anything touches a device: unknown flags, the
+    # sum and bf16-wire modes, a bad N, a null state pointer.
+    lib = grz.lib()
+    b = (N.Bucket * 1)((0, 64))
+    ptrs = (ctypes.c_void_p * 2)(16, 16)
+    reps = (ctypes.c_void_p * 1)(16)
+    args = N.AdamWArgs(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05)
+
+    def call(nranks=2, flags=0, master=16):
+        return lib.zero1_fused_step(ptrs, nranks, N.GRZ_BF16, b, 1, 0, flags, master, 16, 16,
+                                    ctypes.byref(args), 1.0, reps, 1, 16, 16, None, None,
+                                    None, None)
+
+    for flags in (N.GRZ_SUM, N.GRZ_BF16_WIRE, N.GRZ_IN_RANGE, 1 << 10):
+        assert call(flags=flags) == N.GRZ_EINVAL
+    assert call(nranks=17) == N.GRZ_EINVAL
+    assert call(master=None) == N.GRZ_EINVAL
+    assert lib.grz_set_spin_limit(0) == N.GRZ_EINVAL
+    assert lib.zero1_fused_capacity(0, N.GRZ_BF16) == -N.GRZ_EINVAL
+    assert lib.zero1_fused_capacity(2, N.GRZ_F64) == -N.GRZ_EINVAL

@@ -1,0 +1,282 @@
+"""The one-launch step (zero1_fused_step) against the three-kernel path and the
+oracle.
+
+The fused kernel holds the mean in registers and synchronises its grid
+between the reduce, the norm and AdamW; every value it produces must have the
+bits of dp_reduce_scatter_mean -> dp_grad_sqnorm -> zero1_adamw_gather on the
+same inputs, which the oracle pins independently.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gradient_reduce_zero_amd as grz
+from oracle.reduce import owned_chunk, reduce_scatter_mean
+from oracle.step import Hyper as OHyper
+from oracle.step import ddp_step
+from parity_util import assert_bits, host
+from workloads import arena, grad_seed, master_init, onerank_inputs, rank_grad
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _same(a, b, what):
+    assert_bits(host(a), host(b), what)
+
+
+# --- plain data parallelism in one launch, against the oracle -------------------
+
+@pytest.mark.parametrize("max_norm", [1.0, 0.1])
+def test_fused_ddp_tiny_10_steps_matches_oracle(max_norm):
+    p, n = 4096, 2
+    buckets = [(0, p)]
+    master = master_init(p, device=DEV)
+    d = grz.DDPStep(buckets, n, master, grz.Hyper(max_norm=max_norm), device=DEV, fused=True)
+    dstate = (host(master), np.zeros(p, np.float32), np.zeros(p, np.float32))
+    for t in range(1, 11):
+        grads = [rank_grad(p, 0.01, "f32", grad_seed(t, r), device=DEV) for r in range(n)]
+        d.step(grads, t)
+        torch.cuda.synchronize()
+        ref = ddp_step([host(g) for g in grads], "f32", buckets, dstate, OHyper(max_norm=max_norm),
+                       t)
+        dstate = ref["state"]
+        assert math.isclose(d.norm.sqnorm.item(), ref["sqnorm"], rel_tol=1e-13)
+        assert_bits(host(d.norm.scale), np.array([ref["scale"]], np.float32), f"t={t} scale")
+        for k, name in enumerate(("master", "m", "v")):
+            assert_bits(host(d.state[k]), ref["state"][k], f"t={t} {name}")
+        assert_bits(host(d.replica), ref["arena"], f"t={t} bf16 weights")
+    assert not grz.fused_timed_out(d.workspace)
+    assert (ref["scale"] < 1) == (max_norm == 0.1)
+
+
+def test_fused_ddp_char_gpt_equals_zero1_all_ranks():
+    # 10.77 M parameters, N = 8: 2632 pieces in 8 segments, one launch.
+    a = arena("char_gpt")
+    p, n = a.numel, 8
+    buckets = [(0, p)]
+    master = master_init(p, device=DEV)
+    z = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    d = grz.DDPStep(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV, fused=True)
+    for t in range(1, 6):
+        grads = [rank_grad(p, 1e-3, "bf16", grad_seed(t, r), device=DEV) for r in range(n)]
+        z.step(grads, t)
+        d.step(grads, t)
+        torch.cuda.synchronize()
+        _same(d.norm.partials, z.norm.partials, f"t={t} pieces")
+        _same(d.norm.sqnorm, z.norm.sqnorm, f"t={t} sqnorm")
+        _same(d.norm.scale, z.norm.scale, f"t={t} scale")
+        _same(d.replica, z.replicas[t % n], f"t={t} weights")
+    assert z.norm.scale.item() < 1
+    # The master of every shard against the fused DDP master.
+    for r in range(n):
+        c = owned_chunk(r, n)
+        lo, cnt = grz.dp_chunk_range(p, n, c)
+        _same(d.state[0][lo:lo + cnt], z.state[r][0], f"master of rank {r}")
+        _same(d.state[2][lo:lo + cnt], z.state[r][2], f"v of rank {r}")
+    assert not grz.fused_timed_out(d.workspace)
+
+
+# --- one rank's ZeRO-1 share in one launch ------------------------------------
+
+def _one_rank_pair(buckets, p, n, rank):
+    chunk = owned_chunk(rank, n)
+    shard = grz.dp_shard_numel(buckets, n, chunk)
+    npieces = grz.dp_piece_count(buckets, n)
+    inp = onerank_inputs(shard, n, rank, npieces, grz.GRZ_PIECE, device=DEV)
+    three = grz.Zero1OneRank(buckets, n, rank, inp["shard_master"].clone(), device=DEV,
+                             arena_numel=p)
+    one = grz.Zero1OneRank(buckets, n, rank, inp["shard_master"].clone(), device=DEV,
+                           arena_numel=p, fused=True)
+    for z in (three, one):
+        z.norm.partials.copy_(inp["partials"])
+    return inp, three, one
+
+
+@pytest.mark.parametrize("config", ["char_gpt", "gpt2_124m"])
+def test_fused_one_rank_equals_three_kernels(config):
+    a = arena(config)
+    p, n, rank = a.numel, 8, 3
+    buckets = grz.plan_buckets(a.numels, 25 * 2 ** 20, 2) if config == "gpt2_124m" \
+        else [(0, p)]
+    inp, three, one = _one_rank_pair(buckets, p, n, rank)
+    if config == "gpt2_124m":
+        assert one.norm.npieces > 4096  # the norm tree has a level below the final fold
+    mean_copy = torch.full_like(three.mean, float("nan"))
+    for t in (1, 2, 3):
+        three.step(inp["incoming"], inp["peer_shards"], t)
+        if t == 1:  # once with the optional copy of the mean
+            w, m, v = one.state
+            grz.zero1_fused_step(inp["incoming"], buckets, one.chunk, w, m, v,
+                                 grz.adamw_args(**grz.step_scalars(one.hyper, t)),
+                                 one.hyper.max_norm, [one.arena], one.norm.partials,
+                                 one.workspace, one.norm.sqnorm, one.norm.scale,
+                                 mean_out=mean_copy, flags=grz.GRZ_IN_COMPACT)
+            one.gather(inp["peer_shards"])
+        else:
+            one.step(inp["incoming"], inp["peer_shards"], t)
+        torch.cuda.synchronize()
+        if t == 1:
+            _same(mean_copy, three.mean, "mean")
+        for x, y, what in ((one.norm.partials, three.norm.partials, "pieces"),
+                           (one.norm.sqnorm, three.norm.sqnorm, "sqnorm"),
+                           (one.norm.scale, three.norm.scale, "scale"),
+                           (one.state[0], three.state[0], "master"),
+                           (one.state[1], three.state[1], "m"),
+                           (one.state[2], three.state[2], "v"),
+                           (one.arena, three.arena, "arena")):
+            _same(x, y, f"{config} t={t} {what}")
+    assert three.norm.scale.item() < 1
+    assert not grz.fused_timed_out(one.workspace)
+
+
+def test_fused_one_rank_mean_matches_oracle():
+    # Shard-compact inputs of rank 0 (chunk 1) with three buckets, one ragged:
+    # the fused mean copy against the oracle's fold of the same bytes.
+    n, rank = 8, 0
+    buckets = [(8 * 5000, 8 * 4096 * 2), (0, 8 * 5000), (8 * 5000 + 8 * 8192, 8 * 17)]
+    p = 8 * (5000 + 8192 + 17)
+    chunk = owned_chunk(rank, n)
+    shard = grz.dp_shard_numel(buckets, n, chunk)
+    npieces = grz.dp_piece_count(buckets, n)
+    inp = onerank_inputs(shard, n, rank, npieces, grz.GRZ_PIECE, device=DEV)
+    one = grz.Zero1OneRank(buckets, n, rank, inp["shard_master"].clone(), device=DEV,
+                           arena_numel=p, fused=True)
+    one.norm.partials.copy_(inp["partials"])
+    mean = torch.empty(shard, dtype=torch.float32, device=DEV)
+    w, m, v = one.state
+    grz.zero1_fused_step(inp["incoming"], buckets, chunk, w, m, v,
+                         grz.adamw_args(**grz.step_scalars(one.hyper, 1)), 1.0, [one.arena],
+                         one.norm.partials, one.workspace, one.norm.sqnorm, one.norm.scale,
+                         mean_out=mean, flags=grz.GRZ_IN_COMPACT)
+    torch.cuda.synchronize()
+    want = reduce_scatter_mean([host(g) for g in inp["incoming"]], "bf16", buckets, chunk,
+                               compact_inputs=True)
+    assert_bits(host(mean), want, "fused mean vs oracle")
+
+
+# --- ragged, unaligned and N = 3 ---------------------------------------------
+
+@pytest.mark.parametrize("n,kind", [(3, "f32"), (3, "bf16"), (5, "bf16"), (8, "f32")])
+def test_fused_ragged_unaligned_matches_three_kernels_and_oracle(n, kind):
+    # Uneven chunks (GRZ_UNEVEN), a bucket shorter than N, pieces with ragged
+    # tails, and every base one element past a 16-byte boundary (element-wise
+    # accesses throughout).
+    buckets = [(3 * 4096 + 11, 2 * 4096 + 7), (0, 3 * 4096 + 11), (5 * 4096 + 18, 2)]
+    p = 5 * 4096 + 20
+    flags = grz.GRZ_UNEVEN
+
+    def off(t):  # the same values, one element further along
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=DEV)
+        buf[1:] = t
+        return buf[1:]
+
+    master = master_init(p, device=DEV)
+    grads = [off(rank_grad(p, 1e-2, kind, grad_seed(1, r), device=DEV)) for r in range(n)]
+    hyper = grz.Hyper(max_norm=0.05)
+    three = grz.DDPStep(buckets, n, master, hyper, device=DEV, reduce_flags=flags)
+    one = grz.DDPStep(buckets, n, master, hyper, device=DEV, reduce_flags=flags, fused=True)
+    one.state = tuple(off(x) for x in one.state)
+    one.replica = off(one.replica)
+    dstate = (host(master), np.zeros(p, np.float32), np.zeros(p, np.float32))
+    for t in (1, 2):
+        three.step(grads, t)
+        one.step(grads, t)
+        torch.cuda.synchronize()
+        ref = ddp_step([host(g) for g in grads], kind, buckets, dstate, OHyper(max_norm=0.05), t)
+        dstate = ref["state"]
+        for k in range(3):
+            _same(one.state[k], three.state[k], f"N={n} t={t} state {k}")
+            assert_bits(host(one.state[k]), ref["state"][k], f"N={n} t={t} state {k} vs oracle")
+        _same(one.replica, three.replica, f"N={n} t={t} weights")
+        assert_bits(host(one.replica), ref["arena"], f"N={n} t={t} weights vs oracle")
+        _same(one.norm.sqnorm, three.norm.sqnorm, f"N={n} t={t} sqnorm")
+    assert ref["scale"] < 1
+
+
+# --- device-side step scalars --------------------------------------------------
+
+def test_fused_device_args_equal_host_args():
+    p, n = 8 * 4096 + 64, 4
+    buckets = [(0, p)]
+    master = master_init(p, device=DEV)
+    grads = [rank_grad(p, 1e-2, "bf16", grad_seed(2, r), device=DEV) for r in range(n)]
+    hyper = grz.Hyper(max_norm=0.3, warmup=4)
+    host_args = grz.DDPStep(buckets, n, master, hyper, device=DEV, fused=True)
+    dev_args = grz.DDPStep(buckets, n, master, hyper, device=DEV, fused=True)
+    for t in (1, 2, 3):
+        host_args.step(grads, t)
+        s = grz.step_scalars(hyper, t)
+        row = torch.tensor([s[k] for k in ("lr", "beta1", "beta2", "eps", "weight_decay",
+                                           "bias_corr1", "bias_corr2")],
+                           dtype=torch.float32, device=DEV)
+        w, m, v = dev_args.state
+        grz.zero1_fused_step(grads, buckets, -1, w, m, v, row, hyper.max_norm,
+                             [dev_args.replica], dev_args.norm.partials, dev_args.workspace)
+        torch.cuda.synchronize()
+        for k in range(3):
+            _same(dev_args.state[k], host_args.state[k], f"t={t} state {k}")
+        _same(dev_args.replica, host_args.replica, f"t={t} weights")
+
+
+# --- refusals and the bounded wait --------------------------------------------
+
+def test_fused_refuses_what_it_cannot_hold():
+    cap = grz.zero1_fused_capacity(1, torch.float32)
+    assert cap >= 4096  # 4 pieces per resident workgroup; 1024 on a 256-CU MI355X
+    p = (cap + 1) * grz.GRZ_PIECE
+    g = torch.zeros(p, device=DEV)
+    st = [torch.zeros(p, device=DEV) for _ in range(3)]
+    rep = torch.zeros(p, dtype=torch.bfloat16, device=DEV)
+    parts = torch.zeros(cap + 1, dtype=torch.float64, device=DEV)
+    ws = torch.zeros(grz.zero1_fused_workspace(cap + 1), dtype=torch.uint8, device=DEV)
+    args = grz.adamw_args(**grz.step_scalars(grz.Hyper(), 1))
+    with pytest.raises(grz.GrzError, match="out of range"):
+        grz.zero1_fused_step([g], [(0, p)], -1, *st, args, 1.0, [rep], parts, ws)
+    # More than 32 (bucket, chunk) segments.
+    buckets = [(8 * i, 8) for i in range(5)]  # 5 buckets x 8 chunks = 40 segments
+    small = [torch.zeros(40, device=DEV) for _ in range(8)]
+    st = [torch.zeros(40, device=DEV) for _ in range(3)]
+    rep = torch.zeros(40, dtype=torch.bfloat16, device=DEV)
+    parts = torch.zeros(40, dtype=torch.float64, device=DEV)
+    with pytest.raises(grz.GrzError, match="out of range"):
+        grz.zero1_fused_step(small, buckets, -1, *st, args, 1.0, [rep], parts, ws)
+    # The bf16-wire fold and the sum mode are the separate entry points' only.
+    for flag in (grz.GRZ_BF16_WIRE, grz.GRZ_SUM):
+        with pytest.raises(grz.GrzError, match="invalid"):
+            grz.zero1_fused_step([x.to(torch.bfloat16) for x in small], buckets[:1], -1, *st,
+                                 args, 1.0, [rep], parts, ws, flags=flag)
+    torch.cuda.synchronize()
+    assert not grz.fused_timed_out(ws)
+
+
+def test_fused_wait_that_gives_up_raises_the_flag():
+    # A spin limit of one poll makes every workgroup that has to wait give up
+    # at once: the call still ends (every wait is bounded), the flag is raised,
+    # and after the workspace is zeroed the next call is exact again.
+    a = arena("char_gpt")
+    p, n, rank = a.numel, 8, 5
+    inp, three, one = _one_rank_pair([(0, p)], p, n, rank)
+    try:
+        grz.grz_set_spin_limit(1)
+        one.step(inp["incoming"], inp["peer_shards"], 1)
+        torch.cuda.synchronize()
+    finally:
+        grz.grz_set_spin_limit(1 << 22)
+    assert grz.fused_timed_out(one.workspace)
+    # Start again from the same state: zero the workspace, reset the master.
+    one.workspace.zero_()
+    one.state[0].copy_(inp["shard_master"])
+    one.state[1].zero_()
+    one.state[2].zero_()
+    one.norm.partials.copy_(inp["partials"])
+    three.step(inp["incoming"], inp["peer_shards"], 1)
+    one.step(inp["incoming"], inp["peer_shards"], 1)
+    torch.cuda.synchronize()
+    assert not grz.fused_timed_out(one.workspace)
+    for k in range(3):
+        _same(one.state[k], three.state[k], f"after the reset: state {k}")
+    _same(one.arena, three.arena, "after the reset: arena")

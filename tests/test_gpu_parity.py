@@ -17,7 +17,7 @@ import gradient_reduce_zero_amd as grz
 from oracle.reduce import owned_chunk, reduce_scatter_mean
 from oracle.ring import ring_all_reduce, ring_reduce_scatter
 from oracle.step import Hyper as OHyper
-from oracle.step import all_gather, bf16_round, ddp_step, grad_sqnorm, zero1_step
+from oracle.step import all_gather, bf16_round, clip_scale, ddp_step, grad_sqnorm, zero1_step
 from parity_util import assert_bits, host, max_rel, oracle_states
 from workloads import arena, grad_seed, master_init, rank_grad
 
@@ -632,3 +632,46 @@ def test_sixteen_ranks_zero1_step_matches_oracle():
             assert_bits(host(z.means[r]), ref["means"][r], f"N=16 mean rank {r}")
             assert_bits(host(z.state[r][0]), ref["states"][r][0], f"N=16 master rank {r}")
         assert_bits(host(z.replicas[11]), ref["arena"], "N=16 replica")
+
+
+# --- dp_grad_sqnorm_of: the norm straight from an fp32 gradient array ---------
+
+@pytest.mark.parametrize("n,offset", [(1, 0), (4095, 0), (4096, 0), (4097, 1),
+                                      (3 * 4096 + 5, 0), (3 * 4096 + 5, 3),
+                                      (4096 * 4096 + 77, 0)])
+def test_grad_sqnorm_of_equals_reduce_path_and_oracle(n, offset):
+    gen = torch.Generator(device=DEV).manual_seed(900 + n)
+    buf = torch.randn(n + offset, generator=gen, device=DEV) * 1e-3
+    g = buf[offset:]  # offset 1 or 3 leaves the base 4 or 12 bytes past a 16-byte line
+    max_norm = 0.5 * math.sqrt(n) * 1e-3  # clips
+    ws = torch.empty(grz.dp_grad_sqnorm_of_workspace(n), dtype=torch.uint8, device=DEV)
+    sq, sc = (torch.empty(1, dtype=torch.float64, device=DEV),
+              torch.empty(1, dtype=torch.float32, device=DEV))
+    grz.dp_grad_sqnorm_of(g, max_norm, ws, sq, sc)
+    # The same pieces and tree as reducing one rank's single-bucket arena.
+    mean = torch.empty(n, dtype=torch.float32, device=DEV)
+    parts = torch.empty(grz.dp_piece_count([(0, n)], 1), dtype=torch.float64, device=DEV)
+    grz.dp_reduce_scatter_mean([g.clone()], [(0, n)], -1, mean, parts)
+    sq2, sc2 = torch.empty_like(sq), torch.empty_like(sc)
+    wsn = torch.empty(max(grz.dp_grad_sqnorm_workspace(parts.numel()), 8), dtype=torch.uint8,
+                      device=DEV)
+    grz.dp_grad_sqnorm(parts, max_norm, wsn, sq2, sc2)
+    torch.cuda.synchronize()
+    assert_bits(host(sq), host(sq2), "sqnorm: array vs reduce path")
+    assert_bits(host(sc), host(sc2), "clip factor: array vs reduce path")
+    assert_bits(host(ws.view(torch.float64)[:parts.numel()]), host(parts), "piece sums")
+    want = grad_sqnorm(host(g))
+    assert math.isclose(sq.item(), want, rel_tol=1e-13)
+    assert abs(sc.item() - clip_scale(want, max_norm)) <= 2 ** -23 * abs(sc.item())
+
+
+def test_grad_sqnorm_of_errors():
+    g = torch.zeros(10, device=DEV)
+    sq = torch.empty(1, dtype=torch.float64, device=DEV)
+    with pytest.raises(ValueError):
+        grz.dp_grad_sqnorm_of(g, 1.0, None, sq, None)
+    ws = torch.empty(grz.dp_grad_sqnorm_of_workspace(10), dtype=torch.uint8, device=DEV)
+    with pytest.raises(grz.GrzError):
+        grz.dp_grad_sqnorm_of(g, 1.0, ws, None, None)
+    grz.dp_grad_sqnorm_of(g, 1.0, ws, sq, None)
+    assert sq.item() == 0.0
