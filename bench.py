@@ -317,6 +317,57 @@ def all_ranks_bench(args, dev):
                       "model_params_per_s": p / (ms * 1e-3)}), flush=True)
 
 
+def fused_bench(args, setup, stream, dev):
+    """The same one-rank step with reduce + norm + clip + AdamW as one launch."""
+    import torch
+
+    import gradient_reduce_zero_amd as grz
+
+    n, inp = setup["n"], setup["inp"]
+    own_pieces = sum(-(-grz.dp_chunk_range(l, n, setup["chunk"])[1] // grz.GRZ_PIECE)
+                     for _, l in setup["buckets"])
+    cap = grz.zero1_fused_capacity(n, torch.bfloat16)
+    if own_pieces > cap or len(setup["buckets"]) > 32:
+        log(f"fused step: {own_pieces} pieces do not fit the {cap} one launch holds")
+        return {"fits": False, "pieces": own_pieces, "capacity": cap}
+    pipe = grz.Zero1OneRank(setup["buckets"], n, setup["rank"], inp["shard_master"].clone(),
+                            device=dev, arena_numel=setup["p"], fused=True)
+    pipe.norm.partials.copy_(inp["partials"])
+    t = 1
+    for _ in range(args.warmup):
+        pipe.step(inp["incoming"], inp["peer_shards"], t, stream)
+        t += 1
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        pipe.fused_update(inp["incoming"], grz.adamw_args(**grz.step_scalars(pipe.hyper, t)),
+                          stream)
+        ev[k][1].record(stream)
+        pipe.gather(inp["peer_shards"], stream)
+        ev[k][2].record(stream)
+        t += 1
+    stop.record(stream)
+    torch.cuda.synchronize()
+    if grz.fused_timed_out(pipe.workspace):
+        raise RuntimeError("a grid-wide wait of the fused step gave up")
+    ms = start.elapsed_time(stop) / args.steps
+    fused_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    gather_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    owned = setup["shard"]
+    fused_bpo = n * 2 + 12 + 14  # N bf16 chunks + master/m/v read; master/m/v + bf16 written
+    step_bytes = owned * (fused_bpo + bytes_per_owned(n)["gather"])
+    log(f"fused step: {ms:.4f} ms/step (fused launch {fused_ms:.4f} ms, gather "
+        f"{gather_ms:.4f} ms), {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+    return {"fits": True, "pieces": own_pieces, "capacity": cap, "ms_per_step": ms,
+            "value": owned / (ms * 1e-3), "fused_kernel_ms": fused_ms, "gather_ms": gather_ms,
+            "bytes_per_owned_param": fused_bpo,
+            "fused_kernel_GBps": owned * fused_bpo / (fused_ms * 1e-3) / 1e9,
+            "step_GBps": step_bytes / (ms * 1e-3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +397,9 @@ def main():
                     help="instead of the default workload: GPT-2 124M, all 8 simulated ranks, "
                          "9 reverse-layer buckets, reduce-scatter overlapped with a synthetic "
                          "backward (a bf16 GEMM per bucket) on a second stream")
+    ap.add_argument("--fused", action="store_true",
+                    help="also time the one-launch step (zero1_fused_step: reduce, norm, clip "
+                         "and AdamW with the mean kept in registers) when the shard fits")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 2 GiB bf16 copy (the library's all-gather "
                          "kernel with one rank and one replica) as the reference of known "
@@ -507,6 +561,8 @@ def main():
         torch.cuda.synchronize()
         out["graph_ms_per_step"] = g0.elapsed_time(g1) / args.steps
         log(f"graph replay: {out['graph_ms_per_step']:.3f} ms/step")
+    if args.fused:
+        out["fused"] = fused_bench(args, setup, stream, dev)
     if not args.no_cpu:
         log(f"timing the CPU oracle on {args.cpu_sample} parameters")
         cb = cpu_baseline(setup, args.cpu_sample, wire="bf16" if args.wire == "bf16" else None,

@@ -632,7 +632,7 @@ struct FusedArgs {
   float* mean_out;                // optional copy of the mean
   double* partials;               // piece sums of the whole plan (peers' filled in)
   double* level;                  // first-level sums of the norm tree
-  unsigned* sync;                 // barrier words: arrivals, generation, timeout flag
+  unsigned* sync;                 // barrier words (grid_barrier)
   double* sqnorm_out;
   float* scale_out;
   const grz_adamw_args* dargs;    // step scalars in device memory, or null
@@ -649,28 +649,53 @@ struct FusedArgs {
   FSeg seg[kFusedSegs];
 };
 
-// Grid-wide barrier over `nblocks` co-resident workgroups.  One thread per
-// workgroup reads the generation, publishes the workgroup's writes (device-
-// scope fence), counts itself in, and either (last to arrive) resets the
-// count and advances the generation, or waits for the generation to move.
-// The wait gives up after `spin_limit` polls and raises sync[2], so a grid
-// that is not resident at once ends with a flag instead of waiting forever.
-// The count is back at zero after every completed barrier, so consecutive
-// launches reuse the words without clearing them.
+// Grid-wide barrier over `nblocks` co-resident workgroups, in two levels so
+// that no memory word takes more than 32 arrivals or 32 pollers (measured on
+// MI355X: one counter shared by 1024 workgroups makes each barrier several
+// times slower).  Workgroup b belongs to group b mod 32.  One thread per
+// workgroup reads its group's generation, then counts itself in (device-scope
+// acquire-release, which publishes the workgroup's writes); the last of a
+// group resets the group count and counts the group in at the top; the last
+// group resets the top count and advances every group's generation
+// (release).  The others poll their group's generation and then take a
+// device-scope acquire fence.  The wait gives up after `spin_limit` polls and
+// raises the time-out word, so a grid that is not resident at once ends with
+// a flag instead of waiting forever.  Counts are back at zero after every
+// completed barrier, so consecutive launches reuse the words uncleared.
+//
+// Layout of `sync` (32-bit words, 256 bytes per block): block 0 word 0 the
+// top count, word 2 the time-out flag; block g + 1 words 0 and 1 the count and
+// generation of group g.
+constexpr unsigned kBarrierGroups = 32;
+constexpr unsigned kSyncStride = 64;  // words between blocks
+constexpr size_t kSyncBytes = (kBarrierGroups + 1) * kSyncStride * sizeof(unsigned);
+
 __device__ __forceinline__ void grid_barrier(unsigned* sync, unsigned nblocks,
                                              unsigned spin_limit) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned gen = __hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    const unsigned arrived =
-        __hip_atomic_fetch_add(sync, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (arrived == nblocks - 1) {
-      __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned ng = nblocks < kBarrierGroups ? nblocks : kBarrierGroups;
+    const unsigned g = blockIdx.x % ng;
+    const unsigned gsize = nblocks / ng + (g < nblocks % ng ? 1u : 0u);
+    unsigned* gw = sync + kSyncStride * (g + 1);
+    const unsigned gen = __hip_atomic_load(gw + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool last = false;
+    if (__hip_atomic_fetch_add(gw, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+        gsize - 1) {
+      __hip_atomic_store(gw, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_fetch_add(sync, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+          ng - 1) {
+        __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = true;
+      }
+    }
+    if (last) {
+      for (unsigned h = 0; h < ng; ++h)
+        __hip_atomic_fetch_add(sync + kSyncStride * (h + 1) + 1, 1u, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
     } else {
       unsigned polls = 0;
-      while (__hip_atomic_load(sync + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+      while (__hip_atomic_load(gw + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
         __builtin_amdgcn_s_sleep(4);
         if (++polls >= spin_limit) {
           __hip_atomic_store(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -678,7 +703,7 @@ __device__ __forceinline__ void grid_barrier(unsigned* sync, unsigned nblocks,
         }
       }
     }
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }
@@ -1357,7 +1382,7 @@ int grz_set_spin_limit(unsigned polls) {
 
 size_t zero1_fused_workspace(int64_t npieces) {
   const int64_t nl = npieces > kReduceFan ? ceil_div(npieces, kReduceFan) : 0;
-  return 64 + static_cast<size_t>(nl) * sizeof(double);
+  return kSyncBytes + static_cast<size_t>(nl) * sizeof(double);
 }
 
 }  // extern "C"
@@ -1456,7 +1481,7 @@ int fused_launch(const void* kernel, const void* const* rank_grads, int nranks,
   a.mean_out = mean_out;
   a.partials = piece_sqnorm;
   a.sync = static_cast<unsigned*>(workspace);
-  a.level = reinterpret_cast<double*>(static_cast<char*>(workspace) + 64);
+  a.level = reinterpret_cast<double*>(static_cast<char*>(workspace) + kSyncBytes);
   a.sqnorm_out = sqnorm_out;
   a.scale_out = clip_scale_out;
   a.max_norm = max_norm;

@@ -380,13 +380,13 @@ int64_t zero1_fused_capacity(int nranks, int dtype);
  *            pieces of the processed chunks; the other entries (the peers'
  *            pieces, when chunk >= 0) must hold their values already.
  * workspace  device, zero1_fused_workspace(npieces) bytes, 8-byte aligned,
- *            ZEROED before its first use.  Its first three 32-bit words are
- *            the grid barrier's (arrival count, generation, time-out flag);
- *            a completed call leaves the count at zero, so the workspace is
- *            reused without clearing.  A non-zero third word means a wait
- *            gave up (grz_set_spin_limit): that call's results are invalid
- *            and the workspace must be zeroed again.  Calls that share a
- *            workspace must not overlap.
+ *            ZEROED before its first use.  Its first 8448 bytes are the grid
+ *            barrier's counters; the 32-bit word at byte 8 is its time-out
+ *            flag.  A completed call leaves the counters at zero, so the
+ *            workspace is reused without clearing.  A non-zero flag means a
+ *            wait gave up (grz_set_spin_limit): that call's results are
+ *            invalid and the workspace must be zeroed again.  Calls that
+ *            share a workspace must not overlap.
  * sqnorm_out, clip_scale_out  device scalars as for dp_grad_sqnorm, or NULL.
  * mean_out   device fp32 copy of the mean (as dp_reduce_scatter_mean writes
  *            it), or NULL.

@@ -118,10 +118,11 @@ def test_norm_and_fused_workspace_sizes():
     assert grz.dp_grad_sqnorm_of_workspace(0) == 0
     assert grz.dp_grad_sqnorm_of_workspace(1) == 8
     assert grz.dp_grad_sqnorm_of_workspace(4096 * 4097) == 4097 * 8 + 2 * 8
-    assert grz.zero1_fused_workspace(0) == 64
-    assert grz.zero1_fused_workspace(4096) == 64
-    assert grz.zero1_fused_workspace(4097) == 64 + 2 * 8
-    assert grz.zero1_fused_workspace(4096 * 4096) == 64 + 4096 * 8
+    sync = 33 * 256  # barrier counters: a top block and 32 group blocks
+    assert grz.zero1_fused_workspace(0) == sync
+    assert grz.zero1_fused_workspace(4096) == sync
+    assert grz.zero1_fused_workspace(4097) == sync + 2 * 8
+    assert grz.zero1_fused_workspace(4096 * 4096) == sync + 4096 * 8
 
 
 def test_fused_step_refusals_before_any_launch():
