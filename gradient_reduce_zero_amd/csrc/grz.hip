@@ -112,6 +112,16 @@ __device__ __forceinline__ double widen1(const double* p) { return *p; }
 #endif
 constexpr int kNtLoad = 1, kNtStore = 2;
 
+// Full tiles of the reduce take a path that issues all K * N loads of the
+// tile before the first addition (the per-access path waits for each
+// access's N loads in turn).  Measured on MI355X at the 7B one-rank share:
+// the reduce 2.60-2.75 ms against 2.73-2.82 ms.  The same for the optimizer
+// (16 loads) and the all-gather copy (2 loads) measured slower, so they keep
+// the per-access path.  Speed only, never a result bit.
+#ifndef GRZ_RS_BATCH
+#define GRZ_RS_BATCH 1
+#endif
+
 // Occupancy caps, in waves per SIMD (0 = no cap).  Measured on MI355X at the
 // 7B one-rank share: fewer waves in flight stream faster -- the reduce at 2
 // waves per SIMD (its 8 input streams per wave) 2.75 ms against 2.90 ms
@@ -311,6 +321,35 @@ __device__ __forceinline__ typename AccOf<TIn>::type fold_one(const TIn* const* 
   return acc;
 }
 
+// fold_vec over the K accesses of a full tile at once: all K * NR loads are
+// issued before the first addition.  `off` is the lane's first element; the
+// fold of each element is the same sequence of additions as fold_vec's.
+template <typename TIn, int NR, bool WIRE, typename Acc = typename AccOf<TIn>::type,
+          int G = Geo<Acc>::G, int K = Geo<Acc>::K>
+__device__ __forceinline__ void fold_tile(const TIn* const* rank, int c, int64_t off,
+                                          Acc (&acc)[K][G]) {
+  Acc x[K][NR][G];
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      int r = c + j;
+      r = r >= NR ? r - NR : r;
+      loadg<GRZ_RS_POLICY>(rank[r] + off + static_cast<int64_t>(k) * kThreads * G, x[k][j]);
+    }
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      acc[k][i] = x[k][0][i];
+#pragma unroll
+      for (int j = 1; j < NR; ++j) {
+        acc[k][i] = x[k][j][i] + acc[k][i];
+        if constexpr (WIRE) acc[k][i] = bf16_wire(acc[k][i]);
+      }
+    }
+}
+
 // WIRE (bf16 gradients only) rounds every partial sum of the fold to bf16, as a
 // ring whose wire format is bf16 does once per hop ("13.5 Multi-GPU from
 // First Principles", exercise 8).
@@ -331,26 +370,45 @@ __global__ __launch_bounds__(kThreads) GRZ_RS_ATTR void rs_mean_kernel(const RsA
     const int64_t left = s.len - e0;  // > 0
     const int c = s.chunk;
     double sq = 0.0;
+    bool done = false;
+    if constexpr (GRZ_RS_BATCH && NR > 0 && sizeof(TIn) < 8) {
+      if (s.vec && left >= GRZ_PIECE) {
+        Acc acc[K][G];
+        fold_tile<TIn, NR, WIRE>(a.rank, c, s.src + e0 + lane * G, acc);
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int64_t rel = static_cast<int64_t>(k * kThreads + lane) * G;
-      const int64_t e = e0 + rel;
-      if (s.vec && rel + G <= left) {
-        Acc acc[G];
-        fold_vec<TIn, NR, WIRE>(a.rank, a.nranks, c, s.src + e, acc);
+        for (int k = 0; k < K; ++k) {
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-          if (a.average) acc[i] = a.pow2 ? acc[i] * inv : acc[i] / nf;
-          sq = __fma_rn(static_cast<double>(acc[i]), static_cast<double>(acc[i]), sq);
+          for (int i = 0; i < G; ++i) {
+            if (a.average) acc[k][i] = a.pow2 ? acc[k][i] * inv : acc[k][i] / nf;
+            sq = __fma_rn(static_cast<double>(acc[k][i]), static_cast<double>(acc[k][i]), sq);
+          }
+          storeg<GRZ_RS_POLICY>(a.out + s.dst + e0 + (k * kThreads + lane) * G, acc[k]);
         }
-        storeg<GRZ_RS_POLICY>(a.out + s.dst + e, acc);
-      } else {
-        for (int i = 0; i < G; ++i) {
-          if (rel + i >= left) break;
-          Acc v = fold_one<TIn, NR, WIRE>(a.rank, a.nranks, c, s.src + e + i);
-          if (a.average) v = a.pow2 ? v * inv : v / nf;
-          sq = __fma_rn(static_cast<double>(v), static_cast<double>(v), sq);
-          a.out[s.dst + e + i] = v;
+        done = true;
+      }
+    }
+    if (!done) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t rel = static_cast<int64_t>(k * kThreads + lane) * G;
+        const int64_t e = e0 + rel;
+        if (s.vec && rel + G <= left) {
+          Acc acc[G];
+          fold_vec<TIn, NR, WIRE>(a.rank, a.nranks, c, s.src + e, acc);
+#pragma unroll
+          for (int i = 0; i < G; ++i) {
+            if (a.average) acc[i] = a.pow2 ? acc[i] * inv : acc[i] / nf;
+            sq = __fma_rn(static_cast<double>(acc[i]), static_cast<double>(acc[i]), sq);
+          }
+          storeg<GRZ_RS_POLICY>(a.out + s.dst + e, acc);
+        } else {
+          for (int i = 0; i < G; ++i) {
+            if (rel + i >= left) break;
+            Acc v = fold_one<TIn, NR, WIRE>(a.rank, a.nranks, c, s.src + e + i);
+            if (a.average) v = a.pow2 ? v * inv : v / nf;
+            sq = __fma_rn(static_cast<double>(v), static_cast<double>(v), sq);
+            a.out[s.dst + e + i] = v;
+          }
         }
       }
     }
