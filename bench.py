@@ -317,6 +317,29 @@ def all_ranks_bench(args, dev):
                       "model_params_per_s": p / (ms * 1e-3)}), flush=True)
 
 
+def cold_bench(args, pipe, inp, stream, dev, t, step_bytes):
+    """Each step preceded by a 512 MB scrub (outside the timed events)."""
+    import torch
+
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.warmup + args.steps):
+        scrub.fill_(k & 255)
+        if k >= args.warmup:
+            ev[k - args.warmup][0].record(stream)
+        pipe.step(inp["incoming"], inp["peer_shards"], t, stream)
+        if k >= args.warmup:
+            ev[k - args.warmup][1].record(stream)
+        t += 1
+    torch.cuda.synchronize()
+    times = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    ms = sum(times) / len(times)
+    log(f"cold steps: {ms:.4f} ms/step (median {times[len(times) // 2]:.4f})")
+    return {"ms_per_step": ms, "median_ms": times[len(times) // 2],
+            "value": pipe.state[0].numel() / (ms * 1e-3),
+            "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9}
+
+
 def fused_bench(args, setup, stream, dev):
     """The same one-rank step with reduce + norm + clip + AdamW as one launch."""
     import torch
@@ -400,6 +423,10 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="also time the one-launch step (zero1_fused_step: reduce, norm, clip "
                          "and AdamW with the mean kept in registers) when the shard fits")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each step after a 512 MB write that evicts the 256 MB "
+                         "Infinity Cache and the L2s (steps whose bytes fit those caches "
+                         "otherwise run warm); the step's kernels alone are timed")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 2 GiB bf16 copy (the library's all-gather "
                          "kernel with one rank and one replica) as the reference of known "
@@ -561,6 +588,8 @@ def main():
         torch.cuda.synchronize()
         out["graph_ms_per_step"] = g0.elapsed_time(g1) / args.steps
         log(f"graph replay: {out['graph_ms_per_step']:.3f} ms/step")
+    if args.cold:
+        out["cold"] = cold_bench(args, pipe, inp, stream, dev, t, step_bytes)
     if args.fused:
         out["fused"] = fused_bench(args, setup, stream, dev)
     if not args.no_cpu:
