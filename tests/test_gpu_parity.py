@@ -318,6 +318,33 @@ def test_negative_controls_bite():
     for j in range(1, n):
         plain = start0[j] + plain
     assert not np.array_equal(got, plain / np.float32(n))       # fold not in ring order
+    # An unordered reduction (what float atomics give): each element's ranks
+    # added in an order of their own.
+    rng = np.random.default_rng(11)
+    order = np.argsort(rng.random((n, cnt)), axis=0)
+    vals = np.stack(start0)
+    shuffled = vals[order, np.arange(cnt)]
+    unordered = shuffled[0].copy()
+    for j in range(1, n):
+        unordered = shuffled[j] + unordered
+    assert not np.array_equal(got, unordered / np.float32(n))
+
+
+def test_negative_control_shard_offset_without_bucket_offset():
+    # "A4", "Common Mistakes": the ZeRO-1 offset is the bucket's (layer's)
+    # offset plus the chunk's; dropping the first reads the wrong elements.
+    n = 4
+    buckets = [(4096, 8192), (0, 4096)]
+    p = 12288
+    grads = [rank_grad(p, 0.01, "f32", grad_seed(3, r), device=DEV) for r in range(n)]
+    c = grz.dp_ring_owned_chunk(1, n)
+    out = torch.empty(grz.dp_shard_numel(buckets, n, c), device=DEV)
+    grz.dp_reduce_scatter_mean(grads, buckets, c, out)
+    hg = [host(g) for g in grads]
+    got = host(out)
+    assert_bits(got, reduce_scatter_mean(hg, "f32", buckets, c), "shard")
+    no_bucket_offset = [(0, length) for _, length in buckets]  # planted in the oracle
+    assert not np.array_equal(got, reduce_scatter_mean(hg, "f32", no_bucket_offset, c))
 
 
 # --- the bf16 wire: every partial sum rounded to bf16 --------------------------

@@ -29,7 +29,8 @@ class FakeStream:
         FakeEvent.log.append(("wait", self.name, ev.id))
 
 
-def test_overlap_orders_each_bucket_reduce_after_its_event(monkeypatch):
+def _run_schedule(monkeypatch, overlapped_cls):
+    """Run two buckets through ``overlapped_cls`` with stand-ins; return (calls, ov)."""
     FakeEvent.all, FakeEvent.log = [], []
     monkeypatch.setattr(S.torch.cuda, "Event", FakeEvent)
     calls = FakeEvent.log
@@ -51,21 +52,55 @@ def test_overlap_orders_each_bucket_reduce_after_its_event(monkeypatch):
         norm=types.SimpleNamespace(partials=None, scale=None, run=norm_run),
         hyper=S.Hyper(), state=[(0, 0, 0), (0, 0, 0)], replicas=[])
     comm, compute = FakeStream("comm"), FakeStream("compute")
-    ov = S.OverlappedZero1(pipe, comm_stream=comm)
+    ov = overlapped_cls(pipe, comm_stream=comm)
     for b in range(2):
         calls.append(("produce", "compute", b))
         ov.bucket_ready(b, [None, None], compute_stream=compute)
     ov.finish(1, compute_stream=compute)
+    return calls, ov
+
+
+def schedule_violations(calls, ov):
+    """What is out of order in a recorded schedule (empty when it is right)."""
+    bad = []
     for b in range(2):
         produced = calls.index(("produce", "compute", b))
         recorded = calls.index(("record", "compute", ov.ready[b].id))
-        waited = calls.index(("wait", "comm", ov.ready[b].id))
+        waits = [i for i, c in enumerate(calls) if c == ("wait", "comm", ov.ready[b].id)]
         reduces = [i for i, c in enumerate(calls) if c[0] == "reduce" and c[2] == (b, 1)]
-        assert len(reduces) == 2 and all(calls[i][1] == "comm" for i in reduces)
-        assert produced < recorded < waited < min(reduces)
+        if len(reduces) != 2 or any(calls[i][1] != "comm" for i in reduces):
+            bad.append(f"bucket {b}: reduces not on the communication stream")
+        if not waits or not produced < recorded < waits[0] < min(reduces):
+            bad.append(f"bucket {b}: reduce not ordered after its gradients")
     last_reduce = max(i for i, c in enumerate(calls) if c[0] == "reduce")
     norm = calls.index(("norm", "comm"))
     adam = [i for i, c in enumerate(calls) if c[0] == "adamw"]
     done = calls.index(("record", "comm", ov.done.id))
-    assert last_reduce < norm < min(adam) and max(adam) < done
-    assert calls[-1] == ("wait", "compute", ov.done.id)
+    if not (last_reduce < norm < min(adam) and max(adam) < done):
+        bad.append("update not after every reduce")
+    if calls[-1] != ("wait", "compute", ov.done.id):
+        bad.append("compute stream does not wait for the update")
+    return bad
+
+
+def test_overlap_orders_each_bucket_reduce_after_its_event(monkeypatch):
+    calls, ov = _run_schedule(monkeypatch, S.OverlappedZero1)
+    assert schedule_violations(calls, ov) == []
+
+
+def test_a_dropped_wait_is_caught(monkeypatch):
+    # Planted on the CPU: the communication stream never waits for the
+    # compute stream's event, so its reduce could read gradients that are not
+    # there yet ("A4", "Common Mistakes"; noeira's unordered naive streams).
+    class NoWait(S.OverlappedZero1):
+        def bucket_ready(self, b, rank_grads, compute_stream=None):
+            comm = self.comm
+            self.comm = types.SimpleNamespace(name=comm.name, wait_event=lambda ev: None)
+            try:
+                super().bucket_ready(b, rank_grads, compute_stream)
+            finally:
+                self.comm = comm
+
+    calls, ov = _run_schedule(monkeypatch, NoWait)
+    bad = schedule_violations(calls, ov)
+    assert any("not ordered after its gradients" in v for v in bad)
