@@ -122,16 +122,30 @@ constexpr int kNtLoad = 1, kNtStore = 2;
 #define GRZ_RS_BATCH 1
 #endif
 
+// Elements of the optimizer's and the all-gather's tiles (one workgroup
+// each; multiples of 1024 and 2048).  Measured on MI355X at the 7B one-rank
+// share: the optimizer with 1024-element tiles at 3 waves per SIMD ran
+// 4.02-4.13 ms in every repetition, against 4.13-4.48 ms with 4096-element
+// tiles at 2 waves (2048 to 16384 and 2 to 8 waves measured in between or
+// slower).  Speed only, never a result bit.
+#ifndef GRZ_ADAM_TILE
+#define GRZ_ADAM_TILE 1024
+#endif
+#ifndef GRZ_AG_TILE
+#define GRZ_AG_TILE GRZ_PIECE
+#endif
+
 // Occupancy caps, in waves per SIMD (0 = no cap).  Measured on MI355X at the
 // 7B one-rank share: fewer waves in flight stream faster -- the reduce at 2
 // waves per SIMD (its 8 input streams per wave) 2.75 ms against 2.90 ms
-// uncapped, the optimizer at 2 waves 4.38 ms against 4.58 ms, the all-gather
-// copy at 5 waves 3.71 ms against 3.97 ms.  Speed only, never a result bit.
+// uncapped, the optimizer at 3 waves (with its 1024-element tiles, below),
+// the all-gather copy at 5 waves 3.71 ms against 3.97 ms.  Speed only, never
+// a result bit.
 #ifndef GRZ_RS_WAVES
 #define GRZ_RS_WAVES 2
 #endif
 #ifndef GRZ_ADAM_WAVES
-#define GRZ_ADAM_WAVES 2
+#define GRZ_ADAM_WAVES 3
 #endif
 #ifndef GRZ_AG_WAVES
 #define GRZ_AG_WAVES 5
@@ -535,12 +549,12 @@ __device__ __forceinline__ void adamw1(float& w, float& m, float& v, float g, fl
   w = w - lr * (u + wd * w);
 }
 
-// Access k (0 <= k < 4) of lane l covers the 4 elements at k*1024 + 4*l of
-// the tile: 16-byte accesses of the fp32 streams, 8-byte bf16 stores, each
-// wave instruction one contiguous run.
+// Access k (0 <= k < GRZ_ADAM_TILE / 1024) of lane l covers the 4 elements at
+// k*1024 + 4*l of the tile: 16-byte accesses of the fp32 streams, 8-byte bf16
+// stores, each wave instruction one contiguous run.
 __global__ __launch_bounds__(kThreads) GRZ_ADAM_ATTR void adamw_kernel(const AdamArgs a) {
   constexpr int G = 4;
-  constexpr int K = GRZ_PIECE / (kThreads * G);
+  constexpr int K = GRZ_ADAM_TILE / (kThreads * G);
   const float scale = a.scale != nullptr ? *a.scale : 1.0f;
   float lr = a.lr, b1 = a.b1, b2 = a.b2, eps = a.eps, wd = a.wd, bc1 = a.bc1, bc2 = a.bc2;
   if (a.dargs != nullptr) {
@@ -554,7 +568,7 @@ __global__ __launch_bounds__(kThreads) GRZ_ADAM_ATTR void adamw_kernel(const Ada
 
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const Seg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
-    const int64_t e0 = (tile - s.tile0) * GRZ_PIECE;
+    const int64_t e0 = (tile - s.tile0) * GRZ_ADAM_TILE;
     const int64_t left = s.len - e0;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -622,15 +636,15 @@ struct GatherArgs {
   Seg seg[kMaxSegs];
 };
 
-// Access k (0 <= k < 2) of lane l copies the 8 elements (16 bytes) at
-// k*2048 + 8*l of the tile.
+// Access k (0 <= k < GRZ_AG_TILE / 2048) of lane l copies the 8 elements (16
+// bytes) at k*2048 + 8*l of the tile.
 __global__ __launch_bounds__(kThreads) GRZ_AG_ATTR void gather_kernel(const GatherArgs a) {
   constexpr int G = 8;
-  constexpr int K = GRZ_PIECE / (kThreads * G);
+  constexpr int K = GRZ_AG_TILE / (kThreads * G);
   const int lane = threadIdx.x;
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const Seg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
-    const int64_t e0 = (tile - s.tile0) * GRZ_PIECE;
+    const int64_t e0 = (tile - s.tile0) * GRZ_AG_TILE;
     const int64_t left = s.len - e0;
     const uint16_t* src = a.shard[s.chunk];
 #pragma unroll
@@ -970,7 +984,8 @@ std::vector<PlanSeg> plan_segments(const grz_bucket* buckets, int nbuckets, int 
 
 template <typename Args>
 int launch_batches(std::vector<Seg>& segs, Args& args,
-                   void (*kernel)(const Args), hipStream_t stream) {
+                   void (*kernel)(const Args), hipStream_t stream,
+                   int64_t tile_elems = GRZ_PIECE) {
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   for (size_t first = 0; first < segs.size(); first += kMaxSegs) {
     const size_t cnt = segs.size() - first < static_cast<size_t>(kMaxSegs)
@@ -979,7 +994,7 @@ int launch_batches(std::vector<Seg>& segs, Args& args,
     for (size_t i = 0; i < cnt; ++i) {
       args.seg[i] = segs[first + i];
       args.seg[i].tile0 = tiles;
-      tiles += ceil_div(segs[first + i].len, GRZ_PIECE);
+      tiles += ceil_div(segs[first + i].len, tile_elems);
     }
     if (tiles == 0) continue;
     args.nsegs = static_cast<int>(cnt);
@@ -1342,7 +1357,7 @@ static int adamw_common(float* master, float* m, float* v, const float* mean_gra
     s.vec = vec_base && s.src % 4 == 0 && s.dst % 4 == 0;
     segs.push_back(s);
   }
-  return launch_batches(segs, a, adamw_kernel, stream);
+  return launch_batches(segs, a, adamw_kernel, stream, GRZ_ADAM_TILE);
 }
 
 int zero1_adamw_step(float* master, float* m, float* v, const float* mean_grad, int64_t n,
@@ -1429,7 +1444,7 @@ int zero1_all_gather(const uint16_t* const* shards, int nranks, const grz_bucket
       segs.push_back(s);
     }
   }
-  return launch_batches(segs, a, gather_kernel, stream);
+  return launch_batches(segs, a, gather_kernel, stream, GRZ_AG_TILE);
 }
 
 int grz_set_spin_limit(unsigned polls) {
