@@ -308,13 +308,34 @@ def all_ranks_bench(args, dev):
     e1.record(s)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    # The same steps again with events between the three phases.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for k, t in enumerate(range(args.warmup + args.steps + 1, args.warmup + 2 * args.steps + 1)):
+        ev[k][0].record(s)
+        for c, mean in zip(pipe.chunks, pipe.means):
+            grz.dp_reduce_scatter_mean(grads, pipe.buckets, c, mean, pipe.norm.partials)
+        ev[k][1].record(s)
+        pipe.norm.run(pipe.hyper.max_norm, s)
+        ev[k][2].record(s)
+        args_t = grz.adamw_args(**grz.step_scalars(pipe.hyper, t))
+        for c, (w, m, v), mean in zip(pipe.chunks, pipe.state, pipe.means):
+            grz.zero1_adamw_gather(w, m, v, mean, pipe.buckets, n, c, pipe.norm.scale, args_t,
+                                   pipe.replicas)
+        ev[k][3].record(s)
+    torch.cuda.synchronize()
+    phase = {nm: sum(e[i].elapsed_time(e[i + 1]) for e in ev) / args.steps
+             for i, nm in enumerate(("reduce", "sqnorm", "adamw"))}
+    pbytes = {"reduce": p * (2 * n + 4), "adamw": p * (16 + 12 + 2 * n)}
     step_bytes = p * (n * 2 + 4 + 28 + 2 * n)  # reduce N*s + mean 4; AdamW 28; N bf16 replicas
-    log(f"{ms:.3f} ms/step, {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+    log(f"{ms:.3f} ms/step, {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s; "
+        + ", ".join(f"{k} {v:.3f} ms" for k, v in phase.items()))
     print(json.dumps({"mode": "all_ranks_zero1", "workload": f"{a.name} all {n} ranks",
                       "arena_params": p, "buckets": len(buckets), "steps": args.steps,
                       "ms_per_step": ms, "step_bytes": step_bytes,
                       "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
-                      "model_params_per_s": p / (ms * 1e-3)}), flush=True)
+                      "model_params_per_s": p / (ms * 1e-3), "phases_ms": phase,
+                      "phases_GBps": {k: pbytes[k] / (phase[k] * 1e-3) / 1e9 for k in pbytes}}),
+          flush=True)
 
 
 def cold_bench(args, pipe, inp, stream, dev, t, step_bytes):
