@@ -18,6 +18,7 @@ build runs on one GPU (the ranks are simulated as resident buffers).
 """
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -35,6 +36,15 @@ KERNEL_NAMES = {"reduce": "rs_mean_kernel", "adamw": "adamw_kernel", "gather": "
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def settle():
+    """Collect once and freeze the objects made so far: a full collection of
+    torch's many long-lived objects takes tens of ms and, landing inside a
+    timed loop whose steps are host-bound (the small arenas), would be timed
+    as GPU time."""
+    gc.collect()
+    gc.freeze()
 
 
 def onerank_setup(name, n, rank, device, reduce_flags=0):
@@ -192,6 +202,7 @@ def overlap_bench(args, dev):
             grz.dp_reduce_scatter_mean(grads, buckets, c, mean, pipe.norm.partials)
 
     def timed(fn):
+        settle()
         for t in range(1, args.warmup + 1):
             fn(t)
         torch.cuda.synchronize()
@@ -253,6 +264,7 @@ def stage_bench(args, dev):
         z2.step(produce, t)
 
     def timed(fn):
+        settle()
         for t in range(1, args.warmup + 1):
             fn(t)
         torch.cuda.synchronize()
@@ -297,6 +309,7 @@ def all_ranks_bench(args, dev):
     del master
     grads = [rank_grad(p, 1e-3, "bf16", grad_seed(1, r), device=dev) for r in range(n)]
     torch.cuda.synchronize()
+    settle()
     for t in range(1, args.warmup + 1):
         pipe.step(grads, t)
     torch.cuda.synchronize()
@@ -377,6 +390,7 @@ def fused_bench(args, setup, stream, dev):
     pipe = grz.Zero1OneRank(setup["buckets"], n, setup["rank"], inp["shard_master"].clone(),
                             device=dev, arena_numel=setup["p"], fused=True)
     pipe.norm.partials.copy_(inp["partials"])
+    settle()
     t = 1
     for _ in range(args.warmup):
         pipe.step(inp["incoming"], inp["peer_shards"], t, stream)
@@ -491,6 +505,7 @@ def main():
     pipe, inp = setup["pipe"], setup["inp"]
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
+    settle()
     log(f"inputs resident: P={setup['p']}, owned={setup['shard']}, "
         f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
 

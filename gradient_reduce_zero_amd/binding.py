@@ -9,6 +9,7 @@ library's kernels.
 """
 
 import ctypes
+import functools
 
 import torch
 
@@ -40,10 +41,18 @@ def _dev(t, name, dtypes=None, numel=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _key(buckets):
+    return tuple((int(o), int(l)) for o, l in buckets)
+
+
+@functools.lru_cache(maxsize=256)
+def _bucket_array_of(key):
+    # Read-only during each call, so one ctypes array per plan is reused.
+    return (Bucket * max(len(key), 1))(*key), len(key)
+
+
 def _bucket_array(buckets):
-    buckets = [(int(o), int(l)) for o, l in buckets]
-    arr = (Bucket * max(len(buckets), 1))(*buckets)
-    return arr, len(buckets)
+    return _bucket_array_of(_key(buckets))
 
 
 def _extent(buckets):
@@ -73,9 +82,14 @@ def _neg_check(fn, value):
     return value
 
 
-def dp_piece_count(buckets, nranks, flags=0):
-    arr, nb = _bucket_array(buckets)
+@functools.lru_cache(maxsize=1024)
+def _piece_count(key, nranks, flags):
+    arr, nb = _bucket_array_of(key)
     return _neg_check("dp_piece_count", lib().dp_piece_count(arr, nb, nranks, flags))
+
+
+def dp_piece_count(buckets, nranks, flags=0):
+    return _piece_count(_key(buckets), int(nranks), int(flags))
 
 
 def dp_piece_offset(buckets, nranks, bucket, chunk, flags=0):
@@ -84,9 +98,14 @@ def dp_piece_offset(buckets, nranks, bucket, chunk, flags=0):
                       lib().dp_piece_offset(arr, nb, nranks, flags, bucket, chunk))
 
 
-def dp_shard_numel(buckets, nranks, chunk, flags=0):
-    arr, nb = _bucket_array(buckets)
+@functools.lru_cache(maxsize=1024)
+def _shard_numel(key, nranks, chunk, flags):
+    arr, nb = _bucket_array_of(key)
     return _neg_check("dp_shard_numel", lib().dp_shard_numel(arr, nb, nranks, chunk, flags))
+
+
+def dp_shard_numel(buckets, nranks, chunk, flags=0):
+    return _shard_numel(_key(buckets), int(nranks), int(chunk), int(flags))
 
 
 def dp_grad_sqnorm_workspace(npieces):
