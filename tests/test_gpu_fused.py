@@ -280,3 +280,29 @@ def test_fused_wait_that_gives_up_raises_the_flag():
     for k in range(3):
         _same(one.state[k], three.state[k], f"after the reset: state {k}")
     _same(one.arena, three.arena, "after the reset: arena")
+
+
+def test_fused_sixteen_ranks_equals_three_kernels():
+    # The largest N (a runtime-N fold) with two buckets and ragged chunks.
+    n = 16
+    buckets = [(16 * 300, 16 * 4096 + 16 * 7), (0, 16 * 300)]
+    p = 16 * (300 + 4096 + 7)
+    master = master_init(p, device=DEV)
+    grads = [rank_grad(p, 1e-2, "bf16", grad_seed(4, r), device=DEV) for r in range(n)]
+    hyper = grz.Hyper(max_norm=0.05)
+    three = grz.DDPStep(buckets, n, master, hyper, device=DEV)
+    one = grz.DDPStep(buckets, n, master, hyper, device=DEV, fused=True)
+    inp, three_r, one_r = _one_rank_pair(buckets, p, n, 11)
+    for t in (1, 2):
+        three.step(grads, t)
+        one.step(grads, t)
+        three_r.step(inp["incoming"], inp["peer_shards"], t)
+        one_r.step(inp["incoming"], inp["peer_shards"], t)
+        torch.cuda.synchronize()
+        for k in range(3):
+            _same(one.state[k], three.state[k], f"N=16 DDP t={t} state {k}")
+            _same(one_r.state[k], three_r.state[k], f"N=16 rank 11 t={t} state {k}")
+        _same(one.replica, three.replica, f"N=16 DDP t={t} weights")
+        _same(one_r.arena, three_r.arena, f"N=16 rank 11 t={t} arena")
+        _same(one_r.norm.sqnorm, three_r.norm.sqnorm, f"N=16 rank 11 t={t} sqnorm")
+    assert three.norm.scale.item() < 1
