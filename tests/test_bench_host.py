@@ -1,0 +1,52 @@
+"""bench.py's host-side contract, checked without a GPU: the one-GPU refusal,
+the byte model behind the roofline line, and the committed counter summary
+being tied to the kernel source it was measured on."""
+
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_bytes_per_owned_element():
+    # Reduce: N bf16 chunks read + the fp32 mean written; AdamW: mean, master,
+    # m, v read and master, m, v, bf16 written; gather: N - 1 bf16 shards read
+    # and written.  78 B at N = 8: 9.75 bytes per arena element.
+    b = bench.bytes_per_owned(8)
+    assert b == {"reduce": 20, "adamw": 30, "gather": 28}
+    assert sum(b.values()) * 842_301_952 == 65_699_552_256
+    assert bench.bytes_per_owned(4)["gather"] == 12
+
+
+def test_traffic_is_reported_only_for_the_measured_source(monkeypatch):
+    # The committed counters carry the digest of the kernel source they were
+    # measured on; bench.py reports their traffic only while it matches.
+    text = open(bench.COUNTERS).read()
+    digest = [l.split("=")[1].strip() for l in text.splitlines()
+              if l.startswith("kernel_code_digest")][0]
+    monkeypatch.setattr(bench, "kernel_digest", lambda: digest)
+    for kernel in ("reduce", "adamw", "gather"):
+        assert bench.measured_traffic(kernel) > 0
+    monkeypatch.setattr(bench, "kernel_digest", lambda: "0" * 64)
+    assert bench.measured_traffic("adamw") is None
+
+
+def test_digest_ignores_comments_and_white_space(tmp_path, monkeypatch):
+    src = open(bench.KERNEL_SRC).read()
+    base = bench.kernel_digest()
+    alt = tmp_path / "grz.hip"
+    alt.write_text("// a comment\n" + src.replace("\n", "\n  ") + "\n/* another */\n")
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(alt))
+    assert bench.kernel_digest() == base
+    alt.write_text(src.replace("kThreads = 256", "kThreads = 128"))
+    assert bench.kernel_digest() != base
