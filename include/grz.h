@@ -119,10 +119,11 @@ typedef struct {
 int grz_version(void);
 
 /* Launch-width knob: the largest grid (workgroups of 256 threads) the
- * grid-stride kernels use; the default, 2^30, means one workgroup per
- * 4096-element tile.  It changes speed only; the piece layout, the fold
- * order and the norm tree, hence every result bit, do not depend on it.
- * Process-wide; GRZ_EINVAL outside 1..2^30. */
+ * grid-stride kernels use; the default, 2^30, means one workgroup per tile
+ * (4096 elements for the reduce and the all-gather, 1024 for the optimizer).
+ * It changes speed only; the piece layout, the fold order and the norm tree,
+ * hence every result bit, do not depend on it.  Process-wide; GRZ_EINVAL
+ * outside 1..2^30. */
 int grz_set_max_blocks(int blocks);
 
 /* Static description of a status code; never NULL. */
