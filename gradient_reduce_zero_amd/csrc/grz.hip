@@ -2,15 +2,20 @@
 // pipeline for AMD Instinct MI355X (gfx950, CDNA4, wave64).
 //
 // Kernels (all HBM-bandwidth bound; nothing here is a contraction, so no MFMA;
-// one 256-thread workgroup per 4096-element tile, lane-contiguous 8/16-byte
-// accesses, non-temporal hints and occupancy caps chosen by measurement):
-//   rs_mean_kernel   ring-order N-way fold of 128-bit loads, fp32 (fp64) mean,
-//                    fp64 sum of squares per GRZ_PIECE-element piece
+// one 256-thread workgroup per tile, lane-contiguous 8/16-byte accesses,
+// non-temporal hints, tile sizes and occupancy caps chosen by measurement):
+//   rs_mean_kernel   ring-order N-way fold of 64/128-bit loads, fp32 (fp64)
+//                    mean, fp64 sum of squares per GRZ_PIECE-element piece
 //   sqnorm_level_kernel / sqnorm_final_kernel
 //                    fixed-shape fp64 tree over the piece sums -> norm, clip
+//   piece_sqnorm_kernel
+//                    the piece sums of an already reduced fp32 array
 //   adamw_kernel     clip + AdamW on fp32 master/m/v, bf16 round-to-nearest-
 //                    even written to any number of replica arenas
 //   gather_kernel    bf16 shard copies into replica arenas (all-gather)
+//   fused_step_kernel
+//                    the reduce, the norm and clip + AdamW of one shard in one
+//                    cooperative launch, the mean held in registers
 //
 // The ring order of the fold and the chunk ownership follow "Lab 09 --
 // Parallelism, simulated", s.1 "Ring all-reduce" (the N = 3 schedule table)
@@ -675,6 +680,11 @@ __global__ __launch_bounds__(kThreads) GRZ_AG_ATTR void gather_kernel(const Gath
 // that of rs_mean_kernel, sqnorm_*_kernel and adamw_kernel, so the results are
 // the same bits.  The launch is cooperative, which makes the runtime refuse a
 // grid that cannot be resident at once; every wait is bounded as well.
+// Measured on MI355X it is slower than the three separate launches at the
+// sizes that fit (GPT-2 124M one-rank share: 0.22 ms against 0.14 ms of
+// kernel time): every workgroup's device-scope release and acquire at a
+// barrier write back and invalidate its XCD's L2, which costs more than the
+// mean's round trip through HBM.
 
 constexpr int kFusedPieces = 4;   // pieces (tiles) a workgroup holds in registers
 constexpr int kFusedSegs = 32;    // segments per launch
