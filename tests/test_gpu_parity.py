@@ -702,3 +702,42 @@ def test_grad_sqnorm_of_errors():
         grz.dp_grad_sqnorm_of(g, 1.0, ws, None, None)
     grz.dp_grad_sqnorm_of(g, 1.0, ws, sq, None)
     assert sq.item() == 0.0
+
+
+# --- the one-rank share is one rank of the whole job -------------------------
+
+def test_one_rank_share_equals_that_rank_of_the_all_ranks_step():
+    # Rank r's share fed what the other ranks of the same job deliver -- the
+    # chunk of every rank's gradient, every rank's norm pieces and the peers'
+    # new bf16 shards -- reproduces rank r of the all-ranks step bit for bit.
+    n, p = 8, 8 * (3 * 4096 + 136)
+    buckets = [(8 * 4096, p - 8 * 4096), (0, 8 * 4096)]
+    master = master_init(p, device=DEV)
+    hyper = grz.Hyper(max_norm=0.5)
+    full = grz.Zero1AllRanks(buckets, n, master, hyper, device=DEV)
+    grads = [rank_grad(p, 1e-2, "bf16", grad_seed(5, r), device=DEV) for r in range(n)]
+    full.step(grads, 1)
+    torch.cuda.synchronize()
+    assert full.norm.scale.item() < 1
+    for r in (0, 5):
+        c = grz.dp_ring_owned_chunk(r, n)
+        idx = torch.cat([torch.arange(o + grz.dp_chunk_range(l, n, c)[0],
+                                      o + sum(grz.dp_chunk_range(l, n, c)), device=DEV)
+                         for o, l in buckets])
+        incoming = [g.index_select(0, idx).contiguous() for g in grads]
+        one = grz.Zero1OneRank(buckets, n, r, master.index_select(0, idx), hyper, DEV, p)
+        one.norm.partials.copy_(full.norm.partials)  # every rank's pieces, as received
+        peers = []
+        for j in range(n):
+            cj = grz.dp_ring_owned_chunk(j, n)
+            ij = torch.cat([torch.arange(o + grz.dp_chunk_range(l, n, cj)[0],
+                                         o + sum(grz.dp_chunk_range(l, n, cj)), device=DEV)
+                            for o, l in buckets])
+            peers.append(None if j == r else full.replicas[0].index_select(0, ij).contiguous())
+        one.step(incoming, peers, 1)
+        torch.cuda.synchronize()
+        assert_bits(host(one.mean), host(full.means[r]), f"rank {r} mean")
+        assert_bits(host(one.norm.sqnorm), host(full.norm.sqnorm), f"rank {r} sqnorm")
+        for k in range(3):
+            assert_bits(host(one.state[k]), host(full.state[r][k]), f"rank {r} state {k}")
+        assert_bits(host(one.arena), host(full.replicas[r]), f"rank {r} bf16 arena")
