@@ -148,6 +148,40 @@ static void argument_errors(void) {
   CHECK(zero1_all_gather(shards, 2, ok, 1, GRZ_SUM, reps, 1, NULL) == GRZ_EINVAL, "flag");
   CHECK(zero1_all_gather(shards, 0, ok, 1, 0, reps, 1, NULL) == GRZ_EINVAL, "N=0");
   CHECK(grz_set_max_blocks(0) == GRZ_EINVAL, "blocks");
+  /* The norm straight from an fp32 array. */
+  CHECK(dp_grad_sqnorm_of_workspace(0) == 0, "empty workspace");
+  CHECK(dp_grad_sqnorm_of_workspace(4097) == 2 * sizeof(double), "two pieces");
+  CHECK(dp_grad_sqnorm_of(NULL, 8, 1.0, ws, (double*)0x600000, NULL, NULL) == GRZ_EINVAL,
+        "null gradient");
+  CHECK(dp_grad_sqnorm_of(f, 8, 1.0, NULL, (double*)0x600000, NULL, NULL) == GRZ_EINVAL,
+        "null workspace");
+  CHECK(dp_grad_sqnorm_of(f, -1, 1.0, ws, (double*)0x600000, NULL, NULL) == GRZ_EINVAL,
+        "negative count");
+  CHECK(dp_grad_sqnorm_of(f, 8, 1.0, ws, NULL, NULL, NULL) == GRZ_EINVAL, "no outputs");
+  CHECK(dp_grad_sqnorm_of((float*)0x800002, 8, 1.0, ws, (double*)0x600000, NULL, NULL) ==
+        GRZ_EALIGN, "misaligned gradient");
+  /* The one-launch step refuses before it looks for a device. */
+  double* parts = (double*)0xC00000;
+  void* fws = (void*)0xD00000;
+  CHECK(zero1_fused_step(r, 2, GRZ_BF16, ok, 1, 0, GRZ_SUM, f, f, f, &args, 1.0, reps, 1, parts,
+                         fws, NULL, NULL, NULL, NULL) == GRZ_EINVAL, "sum mode");
+  CHECK(zero1_fused_step(r, 2, GRZ_BF16, ok, 1, 0, GRZ_BF16_WIRE, f, f, f, &args, 1.0, reps, 1,
+                         parts, fws, NULL, NULL, NULL, NULL) == GRZ_EINVAL, "wire mode");
+  CHECK(zero1_fused_step(r, 2, GRZ_F64, ok, 1, 0, 0, f, f, f, &args, 1.0, reps, 1, parts, fws,
+                         NULL, NULL, NULL, NULL) == GRZ_EINVAL, "fp64 gradients");
+  CHECK(zero1_fused_step(r, 2, GRZ_BF16, odd, 1, 0, 0, f, f, f, &args, 1.0, reps, 1, parts, fws,
+                         NULL, NULL, NULL, NULL) == GRZ_EINDIVISIBLE, "indivisible");
+  CHECK(zero1_fused_step(r, 2, GRZ_BF16, ok, 1, -1, GRZ_IN_COMPACT, f, f, f, &args, 1.0, reps, 1,
+                         parts, fws, NULL, NULL, NULL, NULL) == GRZ_EINVAL, "compact without chunk");
+  CHECK(zero1_fused_step(r, 2, GRZ_BF16, ok, 1, 0, 0, f, f, f, &args, 1.0, reps, 1, NULL, fws,
+                         NULL, NULL, NULL, NULL) == GRZ_EINVAL, "no pieces");
+  CHECK(zero1_fused_step(r, 2, GRZ_BF16, ok, 1, 0, 0, f, f, f, &args, 1.0, reps, 1, parts, NULL,
+                         NULL, NULL, NULL, NULL) == GRZ_EINVAL, "no workspace");
+  CHECK(zero1_fused_step(r, 2, GRZ_BF16, ok, 1, 0, 0, (float*)0x800002, f, f, &args, 1.0, reps, 1,
+                         parts, fws, NULL, NULL, NULL, NULL) == GRZ_EALIGN, "misaligned master");
+  CHECK(zero1_fused_workspace(4097) > zero1_fused_workspace(4096), "level sums");
+  CHECK(zero1_fused_capacity(0, GRZ_BF16) == -GRZ_EINVAL, "capacity N=0");
+  CHECK(grz_set_spin_limit(0) == GRZ_EINVAL, "spin limit");
   int64_t* ctr = (int64_t*)0xC00000;
   grz_adamw_args* table = (grz_adamw_args*)0xD00000;
   CHECK(grz_step_args_next(NULL, 4, ctr, table, NULL) == GRZ_EINVAL, "null table");
