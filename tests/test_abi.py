@@ -146,3 +146,23 @@ def test_fused_step_refusals_before_any_launch():
     assert lib.grz_set_spin_limit(0) == N.GRZ_EINVAL
     assert lib.zero1_fused_capacity(0, N.GRZ_BF16) == -N.GRZ_EINVAL
     assert lib.zero1_fused_capacity(2, N.GRZ_F64) == -N.GRZ_EINVAL
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # No fallback of any kind: without libgrz.so every entry point raises.
+    import subprocess
+    import sys
+    code = (
+        "import gradient_reduce_zero_amd._native as N\n"
+        f"N.LIB_PATH = {str(tmp_path / 'libgrz.so')!r}\n"
+        "import gradient_reduce_zero_amd as grz\n"
+        "try:\n"
+        "    grz.dp_piece_count([(0, 64)], 2)\n"
+        "except RuntimeError as e:\n"
+        "    print('raised:', e)\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         cwd=root, timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert "raised:" in res.stdout and "no fallback" in res.stdout
