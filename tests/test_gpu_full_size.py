@@ -35,7 +35,7 @@ def _layer_spans(a, sigma=1e-3):
     return spans
 
 
-def test_char_gpt_all_ranks_5_steps():
+def test_char_gpt_all_ranks_10_steps():
     a = arena("char_gpt")
     p, n = a.numel, 8
     buckets = [(0, p)]
@@ -44,7 +44,7 @@ def test_char_gpt_all_ranks_5_steps():
     d = grz.DDPStep(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV)
     states = oracle_states(host(master), buckets, n)
     spans = _layer_spans(a)
-    for t in range(1, 6):
+    for t in range(1, 11):
         grads = [rank_grad(p, 1e-3, "bf16", grad_seed(t, r), DEV, spans) for r in range(n)]
         z.step(grads, t)
         d.step(grads, t)
@@ -206,8 +206,8 @@ def test_gpt2_1p5b_all_ranks_sampled():
 
 
 def test_char_gpt_100_steps_zero1_equals_ddp_every_step():
-    # The char GPT workload runs 100 steps.  The oracle checks the first five
-    # (test_char_gpt_all_ranks_5_steps); over all 100, ZeRO-1 and plain data
+    # The char GPT workload runs 100 steps.  The oracle checks the first ten
+    # (test_char_gpt_all_ranks_10_steps); over all 100, ZeRO-1 and plain data
     # parallelism must stay bit-identical (same pieces, same norm, same update)
     # and finite.
     a = arena("char_gpt")
