@@ -34,6 +34,7 @@
 
 #include <stdint.h>
 
+#include <atomic>
 #include <vector>
 
 #include "grz.h"
@@ -48,11 +49,12 @@ static_assert(GRZ_PIECE % (kThreads * 8) == 0, "piece shape");
 
 // Grid width cap of the grid-stride kernels.  Measured on MI355X: one
 // workgroup per tile (no cap in practice) streams fastest.
-int g_max_blocks = 1 << 30;
+// (Both knobs are atomics: a caller may set one while another thread launches.)
+std::atomic<int> g_max_blocks{1 << 30};
 
 // Polls of a grid-barrier wait before it gives up (fused step).  Each poll
 // sleeps a few hundred cycles, so the default bounds a wait at a few seconds.
-unsigned g_spin_limit = 1u << 22;
+std::atomic<unsigned> g_spin_limit{1u << 22};
 
 // One contiguous run of work: `len` elements read at `src` and written at
 // `dst`, whose first tile is `tile0` of the launch and first norm piece is
@@ -1009,7 +1011,8 @@ int launch_batches(std::vector<Seg>& segs, Args& args,
     if (tiles == 0) continue;
     args.nsegs = static_cast<int>(cnt);
     args.ntiles = tiles;
-    const int64_t grid = tiles < g_max_blocks ? tiles : g_max_blocks;
+    const int64_t cap = g_max_blocks.load(std::memory_order_relaxed);
+    const int64_t grid = tiles < cap ? tiles : cap;
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
                        args);
     if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
@@ -1107,7 +1110,7 @@ const char* grz_strerror(int status) {
 
 int grz_set_max_blocks(int blocks) {
   if (blocks < 1 || blocks > (1 << 30)) return GRZ_EINVAL;
-  g_max_blocks = blocks;
+  g_max_blocks.store(blocks, std::memory_order_relaxed);
   return GRZ_OK;
 }
 
@@ -1459,7 +1462,7 @@ int zero1_all_gather(const uint16_t* const* shards, int nranks, const grz_bucket
 
 int grz_set_spin_limit(unsigned polls) {
   if (polls < 1) return GRZ_EINVAL;
-  g_spin_limit = polls;
+  g_spin_limit.store(polls, std::memory_order_relaxed);
   return GRZ_OK;
 }
 
@@ -1575,7 +1578,7 @@ int fused_launch(const void* kernel, const void* const* rank_grads, int nranks,
   a.nranks = nranks;
   a.nrep = nreplicas;
   a.nsegs = nsegs;
-  a.spin_limit = g_spin_limit;
+  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   if (flags & GRZ_ARGS_DEVICE) {
     a.dargs = args;
   } else {
