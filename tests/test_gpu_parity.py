@@ -741,3 +741,37 @@ def test_one_rank_share_equals_that_rank_of_the_all_ranks_step():
         for k in range(3):
             assert_bits(host(one.state[k]), host(full.state[r][k]), f"rank {r} state {k}")
         assert_bits(host(one.arena), host(full.replicas[r]), f"rank {r} bf16 arena")
+
+
+def test_two_ranks_every_strategy_gives_the_same_weights():
+    # The noeira "Gates" at N = 2: data parallelism, ZeRO-1, ZeRO-2 and the
+    # one-launch forms give the same weights -- here bit for bit even with the
+    # clip on, since every strategy sums the same norm pieces in the same tree.
+    n, p = 2, 2 * (2 * 4096 + 96)
+    buckets = [(2 * 4096, p - 2 * 4096), (0, 2 * 4096)]
+    master = master_init(p, device=DEV)
+    hyper = grz.Hyper(max_norm=0.05)
+    ddp = grz.DDPStep(buckets, n, master, hyper, device=DEV)
+    ddp_fused = grz.DDPStep(buckets, n, master, hyper, device=DEV, fused=True)
+    z1 = grz.Zero1AllRanks(buckets, n, master, hyper, device=DEV)
+    z2 = grz.Zero2AllRanks(buckets, n, master, hyper, device=DEV)
+    for t in (1, 2, 3):
+        grads = [rank_grad(p, 1e-2, "bf16", grad_seed(t, r), device=DEV) for r in range(n)]
+        ddp.step(grads, t)
+        ddp_fused.step(grads, t)
+        z1.step(grads, t)
+
+        def produce(b, bufs):
+            off, length = buckets[b]
+            for buf, g in zip(bufs, grads):
+                buf[:length].copy_(g[off:off + length])
+        z2.step(produce, t)
+        torch.cuda.synchronize()
+        want = host(ddp.replica)
+        for what, rep in (("fused DDP", ddp_fused.replica), ("ZeRO-1", z1.replicas[0]),
+                          ("ZeRO-1 rank 1", z1.replicas[1]), ("ZeRO-2", z2.replicas[1])):
+            assert_bits(host(rep), want, f"t={t} {what} weights")
+        for what, sq in (("fused DDP", ddp_fused.norm.sqnorm), ("ZeRO-1", z1.norm.sqnorm),
+                         ("ZeRO-2", z2.norm.sqnorm)):
+            assert_bits(host(sq), host(ddp.norm.sqnorm), f"t={t} {what} sqnorm")
+    assert ddp.norm.scale.item() < 1
