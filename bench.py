@@ -592,6 +592,12 @@ def main():
         "pct_of_peak_hbm": 100.0 * step_gbps / PEAK_HBM_GBPS,
         "model_params_per_s": setup["p"] / (ms * 1e-3),
         "step_bytes": step_bytes,
+        # The peers' bf16 shards are read only because the ranks are simulated
+        # here (on N GPUs they arrive over the links): the step's bytes without
+        # those reads, and the rate they give over the same time.
+        "step_bytes_without_simulated_reads": step_bytes - owned * (n - 1) * 2,
+        "achieved_GBps_without_simulated_reads":
+            (step_bytes - owned * (n - 1) * 2) / (ms * 1e-3) / 1e9,
         "kernels_ms": per,
         "kernels_GBps": gbps,
         "roofline": {
