@@ -927,6 +927,14 @@ void fused_step_kernel(const FusedArgs<TIn> a) {
   }
 }
 
+// Every kernel takes its arguments by value: keep each struct within the 4 KB
+// a launch may pass.
+static_assert(sizeof(RsArgs<double>) <= 4096 && sizeof(RsArgs<uint16_t>) <= 4096,
+              "reduce arguments exceed 4 KB");
+static_assert(sizeof(AdamArgs) <= 4096, "optimizer arguments exceed 4 KB");
+static_assert(sizeof(GatherArgs) <= 4096, "all-gather arguments exceed 4 KB");
+static_assert(sizeof(FusedArgs<float>) <= 4096, "fused-step arguments exceed 4 KB");
+
 // ---------------------------------------------------------------------------
 // Host side: plan geometry, argument checks and launches.
 
