@@ -775,3 +775,24 @@ def test_two_ranks_every_strategy_gives_the_same_weights():
                          ("ZeRO-2", z2.norm.sqnorm)):
             assert_bits(host(sq), host(ddp.norm.sqnorm), f"t={t} {what} sqnorm")
     assert ddp.norm.scale.item() < 1
+
+
+@pytest.mark.parametrize("max_norm", [0.0, -1.0])
+def test_clipping_switched_off(max_norm):
+    # max_norm <= 0 disables the clip: factor exactly 1, the step the oracle
+    # takes without clipping, although the norm here is far above 1.
+    p, n = 4 * 4096 + 12, 4
+    buckets = [(0, p)]
+    master = master_init(p, device=DEV)
+    d = grz.DDPStep(buckets, n, master, grz.Hyper(max_norm=max_norm), device=DEV)
+    grads = [rank_grad(p, 1.0, "f32", grad_seed(1, r), device=DEV) for r in range(n)]
+    d.step(grads, 1)
+    torch.cuda.synchronize()
+    dstate = (host(master), np.zeros(p, np.float32), np.zeros(p, np.float32))
+    ref = ddp_step([host(g) for g in grads], "f32", buckets, dstate, OHyper(max_norm=max_norm), 1)
+    assert ref["sqnorm"] > 1 and ref["scale"] == 1
+    assert_bits(host(d.norm.scale), np.array([1.0], np.float32), "clip factor")
+    assert math.isclose(d.norm.sqnorm.item(), ref["sqnorm"], rel_tol=1e-13)
+    for k in range(3):
+        assert_bits(host(d.state[k]), ref["state"][k], f"state {k}")
+    assert_bits(host(d.replica), ref["arena"], "weights")
