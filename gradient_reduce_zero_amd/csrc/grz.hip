@@ -1108,7 +1108,7 @@ const char* grz_strerror(int status) {
   switch (status) {
     case GRZ_OK: return "ok";
     case GRZ_EINVAL: return "invalid argument";
-    case GRZ_EINDIVISIBLE: return "can't equally partition parameters: bucket length % N != 0";
+    case GRZ_EINDIVISIBLE: return "bucket length not divisible by N: no even shard split";
     case GRZ_EALIGN: return "device pointer not aligned to its element size";
     case GRZ_EHIP: return "HIP launch error";
     case GRZ_ERANGE: return "bucket or size out of range";

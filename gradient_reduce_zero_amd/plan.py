@@ -56,10 +56,12 @@ def owned_chunk(rank, nranks):
 
 
 def zero_stage(buckets, nranks, requested=1, log=sys.stderr):
-    """Stage actually used: 1 if requested and every bucket divides by N, else 0."""
+    """Stage actually used: 1 if requested and every bucket divides by N, else 0
+    ("A4", "Part 2 -- Tensor Sharding": an uneven split falls back to stage 0
+    and says so)."""
     if requested == 1 and any(length % nranks for _, length in buckets):
-        print("Can't equally partition parameters across processes; falling back to ZeRO-0",
-              file=log)
+        print(f"ZeRO-1 needs every bucket to split evenly over {nranks} ranks; "
+              "running ZeRO stage 0 (plain data parallelism) instead", file=log)
         return 0
     return 0 if requested != 1 else 1
 

@@ -45,8 +45,8 @@
  *  - Shards.  The ZeRO-1 shard of chunk c is chunk c of every bucket,
  *    concatenated in processing order ("shard-compact" layout).  Rank r owns
  *    chunk (r + 1) mod N.  Unless GRZ_UNEVEN is given, every bucket length
- *    must be divisible by N ("Part 2 -- Tensor Sharding": error out
- *    otherwise), else GRZ_EINDIVISIBLE.
+ *    must be divisible by N (an uneven count is an error in "Part 2 --
+ *    Tensor Sharding"), else GRZ_EINDIVISIBLE.
  *  - Pieces.  The norm is summed over pieces of GRZ_PIECE consecutive
  *    elements of one chunk (the last piece of a chunk may be shorter).  The
  *    pieces of a plan are numbered bucket by bucket, chunk 0..N-1 within a

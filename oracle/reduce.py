@@ -19,7 +19,7 @@ What is computed, with its sources:
   shard of rank r is chunk (r + 1) mod N of every bucket, concatenated in
   plan order ("A4", "Common Mistakes": offset into the layer first, then into
   the shard).  Sharding requires every bucket length to be divisible by N
-  ("Part 2 -- Tensor Sharding": error out otherwise).
+  ("Part 2 -- Tensor Sharding" makes an uneven split an error).
 
 Precision (a reading, the pages do not fix it): bf16 and fp32 gradients are
 widened to fp32 and accumulated in fp32, rounding after every addition;

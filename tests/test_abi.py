@@ -104,7 +104,7 @@ def test_argument_errors_return_before_any_launch():
     assert lib.grz_set_max_blocks(0) == N.GRZ_EINVAL
     for code in range(6):
         assert lib.grz_strerror(code)
-    assert b"partition" in lib.grz_strerror(N.GRZ_EINDIVISIBLE)
+    assert b"divisible" in lib.grz_strerror(N.GRZ_EINDIVISIBLE)
 
 
 def test_product_path_refuses_cpu_tensors():

@@ -109,7 +109,7 @@ def test_shard_compact_layout_and_divisibility():
         again = reduce_scatter_mean(compact_in, "f32", buckets, c, compact_inputs=True)
         assert np.array_equal(again, shard)
     with pytest.raises(ValueError):
-        reduce_scatter_mean(arrays, "f32", [(0, 62)], 1)  # "Part 2": error out if P % N != 0
+        reduce_scatter_mean(arrays, "f32", [(0, 62)], 1)  # "Part 2": an uneven split is an error
     uneven = reduce_scatter_mean(arrays, "f32", [(0, 62)], 1, uneven=True)
     assert uneven.shape == (16,)
 
