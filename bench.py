@@ -342,13 +342,28 @@ def all_ranks_bench(args, dev):
     step_bytes = p * (n * 2 + 4 + 28 + 2 * n)  # reduce N*s + mean 4; AdamW 28; N bf16 replicas
     log(f"{ms:.3f} ms/step, {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s; "
         + ", ".join(f"{k} {v:.3f} ms" for k, v in phase.items()))
-    print(json.dumps({"mode": "all_ranks_zero1", "workload": f"{a.name} all {n} ranks",
-                      "arena_params": p, "buckets": len(buckets), "steps": args.steps,
-                      "ms_per_step": ms, "step_bytes": step_bytes,
-                      "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
-                      "model_params_per_s": p / (ms * 1e-3), "phases_ms": phase,
-                      "phases_GBps": {k: pbytes[k] / (phase[k] * 1e-3) / 1e9 for k in pbytes}}),
-          flush=True)
+    out = {"mode": "all_ranks_zero1", "workload": f"{a.name} all {n} ranks",
+           "arena_params": p, "buckets": len(buckets), "steps": args.steps,
+           "ms_per_step": ms, "step_bytes": step_bytes,
+           "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
+           "model_params_per_s": p / (ms * 1e-3), "phases_ms": phase,
+           "phases_GBps": {k: pbytes[k] / (phase[k] * 1e-3) / 1e9 for k in pbytes}}
+    if args.graph:
+        first = args.warmup + 2 * args.steps + 1
+        cap = grz.CapturedStep(lambda a_, s_: pipe.enqueue(grads, a_, s_), pipe.hyper, first,
+                               args.warmup + args.steps)
+        for _ in range(args.warmup):
+            cap.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(s)
+        for _ in range(args.steps):
+            cap.replay()
+        g1.record(s)
+        torch.cuda.synchronize()
+        out["graph_ms_per_step"] = g0.elapsed_time(g1) / args.steps
+        log(f"graph replay: {out['graph_ms_per_step']:.3f} ms/step")
+    print(json.dumps(out), flush=True)
 
 
 def cold_bench(args, pipe, inp, stream, dev, t, step_bytes):
