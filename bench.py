@@ -342,12 +342,28 @@ def all_ranks_bench(args, dev):
     step_bytes = p * (n * 2 + 4 + 28 + 2 * n)  # reduce N*s + mean 4; AdamW 28; N bf16 replicas
     log(f"{ms:.3f} ms/step, {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s; "
         + ", ".join(f"{k} {v:.3f} ms" for k, v in phase.items()))
+    # The same N ranks with their shards held at arena offsets: one reduce and
+    # one optimizer launch writing all N replicas (bit-identical per element).
+    arena_pipe = grz.DDPStep(buckets, n, master_init(p, device=dev), hyper, device=dev,
+                             nreplicas=n)
+    for t in range(1, args.warmup + 1):
+        arena_pipe.step(grads, t)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(s)
+    for t in range(args.warmup + 1, args.warmup + args.steps + 1):
+        arena_pipe.step(grads, t)
+    a1.record(s)
+    torch.cuda.synchronize()
+    arena_ms = a0.elapsed_time(a1) / args.steps
+    log(f"arena layout (2 launches + norm): {arena_ms:.3f} ms/step")
     out = {"mode": "all_ranks_zero1", "workload": f"{a.name} all {n} ranks",
            "arena_params": p, "buckets": len(buckets), "steps": args.steps,
            "ms_per_step": ms, "step_bytes": step_bytes,
            "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
            "model_params_per_s": p / (ms * 1e-3), "phases_ms": phase,
-           "phases_GBps": {k: pbytes[k] / (phase[k] * 1e-3) / 1e9 for k in pbytes}}
+           "phases_GBps": {k: pbytes[k] / (phase[k] * 1e-3) / 1e9 for k in pbytes},
+           "arena_layout_ms_per_step": arena_ms}
     if args.graph:
         first = args.warmup + 2 * args.steps + 1
         cap = grz.CapturedStep(lambda a_, s_: pipe.enqueue(grads, a_, s_), pipe.hyper, first,

@@ -105,10 +105,16 @@ class DDPStep:
     """Plain data-parallel step as one replica computes it.
 
     ``fused=True`` runs the step as one ``zero1_fused_step`` launch (the mean
-    stays in registers; the arena must fit ``zero1_fused_capacity``)."""
+    stays in registers; the arena must fit ``zero1_fused_capacity``).
+
+    ``nreplicas=N`` writes the new weights into N replica arenas: then the
+    step is also every simulated rank's ZeRO-1 step at once, with each rank's
+    shard (chunk (r + 1) mod N of every bucket) held at its arena offsets in
+    the one master/m/v -- the same arithmetic per element, bit for bit, in one
+    reduce and one optimizer launch instead of N of each."""
 
     def __init__(self, buckets, nranks, master, hyper=None, device="cuda", reduce_flags=0,
-                 fused=False):
+                 fused=False, nreplicas=1):
         self.buckets = [(int(o), int(l)) for o, l in buckets]
         self.n = nranks
         self.hyper = hyper or Hyper()
@@ -119,7 +125,8 @@ class DDPStep:
         self.norm = _Norm(B.dp_piece_count(self.buckets, nranks), device)
         self.mean = None if fused else torch.zeros_like(w)
         self.workspace = _fused_workspace(self.norm.npieces, device) if fused else None
-        self.replica = w.to(torch.bfloat16)
+        self.replicas = [w.to(torch.bfloat16) for _ in range(nreplicas)]
+        self.replica = self.replicas[0]
 
     def step(self, rank_grads, t, stream=None, token_counts=None):
         if self.fused:
@@ -128,7 +135,7 @@ class DDPStep:
             w, m, v = self.state
             B.zero1_fused_step(rank_grads, self.buckets, -1, w, m, v,
                                B.adamw_args(**step_scalars(self.hyper, t)),
-                               self.hyper.max_norm, [self.replica], self.norm.partials,
+                               self.hyper.max_norm, self.replicas, self.norm.partials,
                                self.workspace, self.norm.sqnorm, self.norm.scale,
                                flags=self.reduce_flags, stream=stream)
             return
@@ -139,7 +146,7 @@ class DDPStep:
         args = B.adamw_args(**step_scalars(self.hyper, t))
         w, m, v = self.state
         B.zero1_adamw_gather(w, m, v, self.mean, self.buckets, self.n, -1, self.norm.scale,
-                             args, [self.replica], stream=stream)
+                             args, self.replicas, stream=stream)
 
 
 class Zero1OneRank:

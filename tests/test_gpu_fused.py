@@ -180,7 +180,8 @@ def test_fused_ragged_unaligned_matches_three_kernels_and_oracle(n, kind):
     three = grz.DDPStep(buckets, n, master, hyper, device=DEV, reduce_flags=flags)
     one = grz.DDPStep(buckets, n, master, hyper, device=DEV, reduce_flags=flags, fused=True)
     one.state = tuple(off(x) for x in one.state)
-    one.replica = off(one.replica)
+    one.replicas = [off(one.replica)]
+    one.replica = one.replicas[0]
     dstate = (host(master), np.zeros(p, np.float32), np.zeros(p, np.float32))
     for t in (1, 2):
         three.step(grads, t)

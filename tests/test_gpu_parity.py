@@ -796,3 +796,29 @@ def test_clipping_switched_off(max_norm):
     for k in range(3):
         assert_bits(host(d.state[k]), ref["state"][k], f"state {k}")
     assert_bits(host(d.replica), ref["arena"], "weights")
+
+
+def test_all_ranks_in_arena_layout_equal_the_shard_compact_ranks():
+    # Every simulated rank's ZeRO-1 step at once as one data-parallel step
+    # writing all N replicas: each rank's master, m and v, read at its arena
+    # offsets, equal the shard-compact ranks' bit for bit.
+    n, p = 4, 4 * (2 * 4096 + 20)
+    buckets = [(4 * 4096, p - 4 * 4096), (0, 4 * 4096)]
+    master = master_init(p, device=DEV)
+    hyper = grz.Hyper(max_norm=0.1)
+    z = grz.Zero1AllRanks(buckets, n, master, hyper, device=DEV)
+    d = grz.DDPStep(buckets, n, master, hyper, device=DEV, nreplicas=n)
+    for t in (1, 2):
+        grads = [rank_grad(p, 1e-2, "bf16", grad_seed(t, r), device=DEV) for r in range(n)]
+        z.step(grads, t)
+        d.step(grads, t)
+    torch.cuda.synchronize()
+    for r in range(n):
+        c = grz.dp_ring_owned_chunk(r, n)
+        idx = torch.cat([torch.arange(o + grz.dp_chunk_range(l, n, c)[0],
+                                      o + sum(grz.dp_chunk_range(l, n, c)), device=DEV)
+                         for o, l in buckets])
+        for k in range(3):
+            assert_bits(host(d.state[k].index_select(0, idx)), host(z.state[r][k]),
+                        f"rank {r} state {k}")
+        assert_bits(host(d.replicas[r]), host(z.replicas[r]), f"replica {r}")
