@@ -253,3 +253,27 @@ def test_least_squares_gradient_against_autograd():
     sizes = [9, 8, 8, 8, 8, 8, 8, 7]
     sums = shard_sum_grads(X, y, w, sizes)
     np.testing.assert_allclose(np.sum(sums, axis=0) / 64, lsq_grad(X, y, w), rtol=1e-12)
+
+
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
+def test_ring_fold_is_within_the_recursive_summation_bound(n):
+    # The fp32 fold in ring order against the exact sum (fp64 fsum of the
+    # widened values): recursive summation of n terms errs by at most
+    # (n - 1) u * sum|x_i| with u = 2^-24 (Higham, "Accuracy and Stability of
+    # Numerical Algorithms", s.4.2), plus the final division's half ulp.
+    import math
+    rng = np.random.default_rng(100 + n)
+    contribs = [(rng.standard_normal(4096) * 10.0 ** rng.integers(-3, 3)).astype(np.float32)
+                for _ in range(n)]
+    for chunk in (0, n - 1):
+        got = chunk_mean(contribs, chunk).astype(np.float64)
+        exact = np.array([math.fsum(float(c[i]) for c in contribs)
+                          for i in range(4096)]) / n
+        absum = np.sum(np.abs(np.stack(contribs).astype(np.float64)), axis=0) / n
+        u = 2.0 ** -24
+        bound = (n - 1) * u * absum * (1 + u) + u * np.abs(exact) + 1e-300
+        assert np.all(np.abs(got - exact) <= bound)
+        if n == 2:  # one rounding (the division by 2 is exact): the correctly rounded mean
+            assert np.array_equal(got, exact.astype(np.float32).astype(np.float64))
+        else:  # several roundings: the order shows
+            assert np.any(got != exact.astype(np.float32))
