@@ -129,24 +129,38 @@ constexpr int kNtLoad = 1, kNtStore = 2;
 #define GRZ_RS_BATCH 1
 #endif
 
-// Elements of the optimizer's and the all-gather's tiles (one workgroup
-// each; multiples of 1024 and 2048).  Measured on MI355X at the 7B one-rank
-// share: the optimizer with 1024-element tiles at 3 waves per SIMD ran
-// 4.02-4.13 ms in every repetition, against 4.13-4.48 ms with 4096-element
-// tiles at 2 waves (2048 to 16384 and 2 to 8 waves measured in between or
-// slower).  Speed only, never a result bit.
+// Workgroup sizes and tiles (elements per workgroup) of the optimizer and
+// the all-gather: one wave each, one 16-byte access per lane per stream.
+// Measured on MI355X at the 7B one-rank share, three repetitions each: the
+// optimizer with 64-thread workgroups and 256-element tiles at 3 waves per
+// SIMD 3.92-3.95 ms, against 3.99-4.07 ms with 256 threads and 1024-element
+// tiles (128 threads, 512 to 4096 elements and 2 to 8 waves measured in
+// between or slower); the all-gather copy with 64 threads and 512-element
+// tiles, uncapped, 3.57-3.62 ms, against 3.70-3.72 ms with 256 threads and
+// 4096 elements at 5 waves (it needs 8 or more waves per SIMD at this tile:
+// 4.13 ms at 5, 5.81 ms at 3).  Smaller workgroups finish and refill one by
+// one, which keeps more of each CU's memory requests in flight.  Speed
+// only, never a result bit.
+#ifndef GRZ_ADAM_THREADS
+#define GRZ_ADAM_THREADS 64
+#endif
 #ifndef GRZ_ADAM_TILE
-#define GRZ_ADAM_TILE 1024
+#define GRZ_ADAM_TILE 256
+#endif
+#ifndef GRZ_AG_THREADS
+#define GRZ_AG_THREADS 64
 #endif
 #ifndef GRZ_AG_TILE
-#define GRZ_AG_TILE GRZ_PIECE
+#define GRZ_AG_TILE 512
 #endif
+static_assert(GRZ_ADAM_TILE % (GRZ_ADAM_THREADS * 4) == 0, "optimizer tile shape");
+static_assert(GRZ_AG_TILE % (GRZ_AG_THREADS * 8) == 0, "all-gather tile shape");
 
 // Occupancy caps, in waves per SIMD (0 = no cap).  Measured on MI355X at the
-// 7B one-rank share: fewer waves in flight stream faster -- the reduce at 2
-// waves per SIMD (its 8 input streams per wave) 2.75 ms against 2.90 ms
-// uncapped, the optimizer at 3 waves (with its 1024-element tiles, below),
-// the all-gather copy at 5 waves 3.71 ms against 3.97 ms.  Speed only, never
+// 7B one-rank share: the reduce at 2 waves per SIMD (its 8 input streams per
+// wave) 2.75 ms against 2.90 ms uncapped; the optimizer at 3 waves (4.2 ms
+// at 5 or more, 4.7 ms at 2, with the workgroups above); the all-gather
+// copy of one 16-byte access per lane runs best uncapped.  Speed only, never
 // a result bit.
 #ifndef GRZ_RS_WAVES
 #define GRZ_RS_WAVES 2
@@ -155,7 +169,7 @@ constexpr int kNtLoad = 1, kNtStore = 2;
 #define GRZ_ADAM_WAVES 3
 #endif
 #ifndef GRZ_AG_WAVES
-#define GRZ_AG_WAVES 5
+#define GRZ_AG_WAVES 0
 #endif
 #if GRZ_AG_WAVES > 0
 #define GRZ_AG_ATTR __attribute__((amdgpu_waves_per_eu(GRZ_AG_WAVES, GRZ_AG_WAVES)))
@@ -556,12 +570,13 @@ __device__ __forceinline__ void adamw1(float& w, float& m, float& v, float g, fl
   w = w - lr * (u + wd * w);
 }
 
-// Access k (0 <= k < GRZ_ADAM_TILE / 1024) of lane l covers the 4 elements at
-// k*1024 + 4*l of the tile: 16-byte accesses of the fp32 streams, 8-byte bf16
-// stores, each wave instruction one contiguous run.
-__global__ __launch_bounds__(kThreads) GRZ_ADAM_ATTR void adamw_kernel(const AdamArgs a) {
+// Access k (0 <= k < K) of lane l covers the 4 elements at k*T*4 + 4*l of
+// the tile (T = GRZ_ADAM_THREADS): 16-byte accesses of the fp32 streams,
+// 8-byte bf16 stores, each wave instruction one contiguous run.
+__global__ __launch_bounds__(GRZ_ADAM_THREADS) GRZ_ADAM_ATTR void adamw_kernel(
+    const AdamArgs a) {
   constexpr int G = 4;
-  constexpr int K = GRZ_ADAM_TILE / (kThreads * G);
+  constexpr int K = GRZ_ADAM_TILE / (GRZ_ADAM_THREADS * G);
   const float scale = a.scale != nullptr ? *a.scale : 1.0f;
   float lr = a.lr, b1 = a.b1, b2 = a.b2, eps = a.eps, wd = a.wd, bc1 = a.bc1, bc2 = a.bc2;
   if (a.dargs != nullptr) {
@@ -579,7 +594,7 @@ __global__ __launch_bounds__(kThreads) GRZ_ADAM_ATTR void adamw_kernel(const Ada
     const int64_t left = s.len - e0;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int64_t rel = static_cast<int64_t>(k * kThreads + lane) * G;
+      const int64_t rel = static_cast<int64_t>(k * GRZ_ADAM_THREADS + lane) * G;
       const int64_t e = e0 + rel;
       if (s.vec && rel + G <= left) {
         const int64_t i = s.src + e;
@@ -643,11 +658,12 @@ struct GatherArgs {
   Seg seg[kMaxSegs];
 };
 
-// Access k (0 <= k < GRZ_AG_TILE / 2048) of lane l copies the 8 elements (16
-// bytes) at k*2048 + 8*l of the tile.
-__global__ __launch_bounds__(kThreads) GRZ_AG_ATTR void gather_kernel(const GatherArgs a) {
+// Access k (0 <= k < K) of lane l copies the 8 elements (16 bytes) at
+// k*T*8 + 8*l of the tile (T = GRZ_AG_THREADS).
+__global__ __launch_bounds__(GRZ_AG_THREADS) GRZ_AG_ATTR void gather_kernel(
+    const GatherArgs a) {
   constexpr int G = 8;
-  constexpr int K = GRZ_AG_TILE / (kThreads * G);
+  constexpr int K = GRZ_AG_TILE / (GRZ_AG_THREADS * G);
   const int lane = threadIdx.x;
   for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const Seg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
@@ -656,7 +672,7 @@ __global__ __launch_bounds__(kThreads) GRZ_AG_ATTR void gather_kernel(const Gath
     const uint16_t* src = a.shard[s.chunk];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int64_t rel = static_cast<int64_t>(k * kThreads + lane) * G;
+      const int64_t rel = static_cast<int64_t>(k * GRZ_AG_THREADS + lane) * G;
       const int64_t e = e0 + rel;
       if (s.vec && rel + G <= left) {
         const u32x4 u = ldv<GRZ_AG_POLICY, u32x4>(src + s.src + e);
@@ -1005,7 +1021,7 @@ std::vector<PlanSeg> plan_segments(const grz_bucket* buckets, int nbuckets, int 
 template <typename Args>
 int launch_batches(std::vector<Seg>& segs, Args& args,
                    void (*kernel)(const Args), hipStream_t stream,
-                   int64_t tile_elems = GRZ_PIECE) {
+                   int64_t tile_elems = GRZ_PIECE, int block = kThreads) {
   (void)hipGetLastError();  // clear a stale error so the check below is ours
   for (size_t first = 0; first < segs.size(); first += kMaxSegs) {
     const size_t cnt = segs.size() - first < static_cast<size_t>(kMaxSegs)
@@ -1021,7 +1037,7 @@ int launch_batches(std::vector<Seg>& segs, Args& args,
     args.ntiles = tiles;
     const int64_t cap = g_max_blocks.load(std::memory_order_relaxed);
     const int64_t grid = tiles < cap ? tiles : cap;
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(block), 0, stream,
                        args);
     if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
   }
@@ -1378,7 +1394,7 @@ static int adamw_common(float* master, float* m, float* v, const float* mean_gra
     s.vec = vec_base && s.src % 4 == 0 && s.dst % 4 == 0;
     segs.push_back(s);
   }
-  return launch_batches(segs, a, adamw_kernel, stream, GRZ_ADAM_TILE);
+  return launch_batches(segs, a, adamw_kernel, stream, GRZ_ADAM_TILE, GRZ_ADAM_THREADS);
 }
 
 int zero1_adamw_step(float* master, float* m, float* v, const float* mean_grad, int64_t n,
@@ -1465,7 +1481,7 @@ int zero1_all_gather(const uint16_t* const* shards, int nranks, const grz_bucket
       segs.push_back(s);
     }
   }
-  return launch_batches(segs, a, gather_kernel, stream, GRZ_AG_TILE);
+  return launch_batches(segs, a, gather_kernel, stream, GRZ_AG_TILE, GRZ_AG_THREADS);
 }
 
 int grz_set_spin_limit(unsigned polls) {

@@ -118,9 +118,10 @@ typedef struct {
 /* Version of the ABI (major * 100 + minor). */
 int grz_version(void);
 
-/* Launch-width knob: the largest grid (workgroups of 256 threads) the
- * grid-stride kernels use; the default, 2^30, means one workgroup per tile
- * (4096 elements for the reduce and the all-gather, 1024 for the optimizer).
+/* Launch-width knob: the largest grid (workgroups) the grid-stride kernels
+ * use; the default, 2^30, means one workgroup per tile (4096 elements and
+ * 256 threads for the reduce, 512 and 64 for the all-gather, 256 and 64 for
+ * the optimizer).
  * It changes speed only; the piece layout, the fold order and the norm tree,
  * hence every result bit, do not depend on it.  Process-wide; GRZ_EINVAL
  * outside 1..2^30. */
