@@ -161,6 +161,24 @@ def test_llama_7b_one_rank_share_sampled():
         assert_bits(gather_host(pipe.arena, idx + c * shard),
                     gather_host(inp["peer_shards"][j], idx), f"peer {j}'s chunk")
 
+    # Properties over every element (every tile edge of every kernel): each
+    # peer's chunk of the arena is its shard byte for byte, the own chunk is
+    # the master rounded to bf16, and after step 1 from m = v = 0 the moments
+    # are m = (1 - b1) * g' and v = (1 - b2) * (g' * g'), g' = mean * clip
+    # factor, each product rounded once in fp32.
+    for j in range(n):
+        if j == rank:
+            continue
+        c = owned_chunk(j, n)
+        assert torch.equal(pipe.arena[c * shard:(c + 1) * shard], inp["peer_shards"][j]), j
+    assert torch.equal(pipe.arena[lo:lo + shard], pipe.state[0].to(torch.bfloat16))
+    f32 = dict(dtype=torch.float32, device=DEV)
+    g = pipe.mean * pipe.norm.scale
+    omb1 = torch.tensor(np.float32(1) - np.float32(h.beta1), **f32)
+    omb2 = torch.tensor(np.float32(1) - np.float32(h.beta2), **f32)
+    assert torch.equal(pipe.state[1], omb1 * g)
+    assert torch.equal(pipe.state[2], omb2 * (g * g))
+
 
 def test_gpt2_1p5b_all_ranks_sampled():
     a = arena("gpt2_1p5b")
@@ -203,6 +221,21 @@ def test_gpt2_1p5b_all_ranks_sampled():
     if got_scale == scale:
         for rep in (z.replicas[0], z.replicas[3]):
             assert_bits(gather_host(rep, idx), bf16_round(w1), "1.5B replicas")
+    # Every element: all replicas hold the same bytes, chunk c of each is
+    # rank r's master rounded to bf16, and the step-1 moments are
+    # (1 - b1) * g' and (1 - b2) * (g' * g') with g' = mean * clip factor.
+    f32 = dict(dtype=torch.float32, device=DEV)
+    omb1 = torch.tensor(np.float32(1) - np.float32(s["beta1"]), **f32)
+    omb2 = torch.tensor(np.float32(1) - np.float32(s["beta2"]), **f32)
+    for rep in z.replicas[1:]:
+        assert torch.equal(rep, z.replicas[0])
+    for r in range(n):
+        c = owned_chunk(r, n)
+        w, m, v = z.state[r]
+        assert torch.equal(z.replicas[0][c * shard:(c + 1) * shard], w.to(torch.bfloat16)), r
+        g = z.means[r] * z.norm.scale
+        assert torch.equal(m, omb1 * g), r
+        assert torch.equal(v, omb2 * (g * g)), r
 
 
 def test_char_gpt_100_steps_zero1_equals_ddp_every_step():
