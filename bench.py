@@ -109,15 +109,33 @@ def measured_traffic(kernel):
     return int(vals[KERNEL_NAMES[kernel]])
 
 
-def cpu_baseline(setup, sample, wire=None, token_counts=None):
-    """The CPU oracle on a bounded sample of the same step (reported, not a target)."""
+def _oracle_onerank(g, w, peers, partials, n, chunk, wire=None, divisor=None):
+    """The oracle's one-rank step on host arrays (bf16 bits of the N incoming
+    chunks, fp32 master, peers' bf16 shards, peers' norm pieces): fold,
+    norm, clip, AdamW from zero moments, bf16 rounding, arena assembly."""
     import math
 
     import numpy as np
-    import torch
 
     from oracle.reduce import chunk_mean, widen
     from oracle.step import Hyper, adamw, bf16_round, clip_scale, grad_sqnorm
+
+    npieces = math.ceil(w.size / 4096)
+    z = np.zeros_like(w)
+    mean = chunk_mean([widen(x, "bf16") for x in g], chunk, wire=wire, divisor=divisor)
+    sq = grad_sqnorm(mean, extra=partials[:npieces * (n - 1)])
+    scale = clip_scale(sq, 1.0)
+    w1, m1, v1 = adamw(w, z, z, mean * scale, **Hyper().scalars(1))
+    arena = np.empty((n, w.size), np.uint16)
+    arena[chunk] = bf16_round(w1)
+    for j, s in enumerate(peers):
+        if s is not None:
+            arena[(j + 1) % n] = s
+    return arena
+
+
+def cpu_baseline(setup, sample, wire=None, token_counts=None):
+    """The CPU oracle on a bounded sample of the same step (reported, not a target)."""
     from workloads import to_bits
 
     inp = setup["inp"]
@@ -128,27 +146,112 @@ def cpu_baseline(setup, sample, wire=None, token_counts=None):
     w = to_bits(inp["shard_master"][lo:hi])
     peers = [None if s is None else to_bits(s[lo:hi]) for s in inp["peer_shards"]]
     partials = to_bits(inp["partials"])
-    npieces_sample = math.ceil((hi - lo) / 4096)
-    z = np.zeros_like(w)
-    t0 = time.perf_counter()
     divisor = None if token_counts is None else sum(token_counts)
-    mean = chunk_mean([widen(x, "bf16") for x in g], chunk, wire=wire, divisor=divisor)
-    sq = grad_sqnorm(mean, extra=partials[:npieces_sample * (n - 1)])
-    scale = clip_scale(sq, 1.0)
-    w1, m1, v1 = adamw(w, z, z, mean * scale, **Hyper().scalars(1))
-    arena = np.empty((n, hi - lo), np.uint16)
-    arena[chunk] = bf16_round(w1)
-    for j, s in enumerate(peers):
-        if s is not None:
-            arena[(j + 1) % n] = s
+    t0 = time.perf_counter()
+    _oracle_onerank(g, w, peers, partials, n, chunk, wire, divisor)
     dt = time.perf_counter() - t0
-    del torch
     return dict(value=(hi - lo) / dt, unit="params/s", cores=1, kind="oracle",
                 sample=f"{hi - lo} of the {shard} owned parameters (contiguous, mid-shard): "
                        f"fold of {n} bf16 chunks, float64 norm with the matching share of peer "
                        f"pieces, clip, fp32 AdamW, bf16 rounding, arena assembly; "
                        f"single-threaded NumPy, {dt:.2f} s",
-                seconds=dt)
+                seconds=dt, count=hi - lo)
+
+
+def _oracle_worker(i, count, n, rank, chunk, wire, divisor, barrier, results):
+    """One worker of the multi-process oracle timing: make a tile of the same
+    synthetic inputs (its own seeds), wait for every worker, time the step."""
+    try:
+        import torch
+
+        torch.set_num_threads(1)
+        from workloads import GRAD_SEED, onerank_inputs, to_bits
+
+        npieces = -(-count // 4096) * n
+        inp = onerank_inputs(count, n, rank, npieces, 4096, base=GRAD_SEED + 7919 * (i + 1))
+        g = [to_bits(t) for t in inp["incoming"]]
+        w = to_bits(inp["shard_master"])
+        peers = [None if s is None else to_bits(s) for s in inp["peer_shards"]]
+        partials = to_bits(inp["partials"])
+        del inp
+        barrier.wait(timeout=600)
+        t0 = time.perf_counter()
+        _oracle_onerank(g, w, peers, partials, n, chunk, wire, divisor)
+        results.put(("ok", i, count, t0, time.perf_counter()))
+    except BaseException as e:  # reported to the parent, which gives up
+        barrier.abort()
+        results.put(("error", i, repr(e), 0.0, 0.0))
+
+
+def cpu_baseline_parallel(count, n, rank, chunk, workers, wire=None, divisor=None):
+    """The same oracle step over ``count`` parameters split into ``workers``
+    disjoint tiles, one forked process each, all started together.  Runs
+    before the process touches the GPU (nothing is forked afterwards).
+    Throughput = count / (last end - first start), clocks being the system's
+    monotonic one."""
+    import multiprocessing as mp
+
+    ctx = mp.get_context("fork")
+    barrier, results = ctx.Barrier(workers), ctx.Queue()
+    sizes = [count // workers + (1 if i < count % workers else 0) for i in range(workers)]
+    procs = [ctx.Process(target=_oracle_worker,
+                         args=(i, sizes[i], n, rank, chunk, wire, divisor, barrier, results),
+                         daemon=True) for i in range(workers)]
+    for pr in procs:
+        pr.start()
+    got = []
+    try:
+        for _ in procs:
+            got.append(results.get(timeout=900))
+    finally:
+        for pr in procs:
+            pr.join(timeout=60)
+            if pr.is_alive():
+                pr.kill()
+    bad = [r for r in got if r[0] != "ok"]
+    if bad:
+        raise RuntimeError(f"oracle worker {bad[0][1]} failed: {bad[0][2]}")
+    t0, t1 = min(r[3] for r in got), max(r[4] for r in got)
+    return dict(value=count / (t1 - t0), unit="params/s", cores=workers, kind="oracle",
+                seconds=t1 - t0,
+                sample=f"{count} owned parameters in {workers} tiles of the same synthetic "
+                       f"recipe (own seeds), one forked NumPy process per tile, "
+                       f"{t1 - t0:.2f} s from the first start to the last end")
+
+
+def cpu_baseline_all_ranks(grads, buckets, n, hyper, sample):
+    """The oracle's ZeRO-1 step of all N ranks on host copies of the same
+    gradients: the whole arena when it has at most ``sample`` parameters,
+    else its first ``sample`` (a multiple of N) as one bucket."""
+    import numpy as np
+
+    from oracle.reduce import shard_segments
+    from oracle.step import Hyper, zero1_step
+    from workloads import master_init, to_bits
+
+    p = grads[0].numel()
+    if p <= sample:
+        count, plan = p, [tuple(b) for b in buckets]
+    else:
+        count = sample - sample % n
+        plan = [(0, count)]
+    host = [to_bits(g[:count]) for g in grads]
+    shard = count // n
+    master = to_bits(master_init(count))
+    states = []
+    for r in range(n):
+        w = np.concatenate([master[g0:g0 + ln]
+                            for g0, ln, _ in shard_segments(plan, n, (r + 1) % n)])
+        states.append((w, np.zeros(shard, np.float32), np.zeros(shard, np.float32)))
+    h = Hyper(lr=hyper.lr, warmup=hyper.warmup, max_norm=hyper.max_norm)
+    t0 = time.perf_counter()
+    zero1_step(host, "bf16", plan, states, h, 1)
+    dt = time.perf_counter() - t0
+    what = "the whole arena" if count == p else f"the first {count} of {p} parameters"
+    return dict(value=count / dt, unit="params/s", cores=1, kind="oracle",
+                sample=f"{what}, {len(plan)} bucket(s), all {n} ranks: ring folds, float64 "
+                       f"norm, clip, fp32 AdamW of every shard, bf16 all-gather; "
+                       f"single-threaded NumPy, {dt:.2f} s")
 
 
 def overlap_bench(args, dev):
@@ -379,6 +482,10 @@ def all_ranks_bench(args, dev):
         torch.cuda.synchronize()
         out["graph_ms_per_step"] = g0.elapsed_time(g1) / args.steps
         log(f"graph replay: {out['graph_ms_per_step']:.3f} ms/step")
+    if not args.no_cpu:
+        log("timing the CPU oracle's all-ranks step")
+        out["cpu_baseline"] = cpu_baseline_all_ranks(grads, buckets, n, hyper,
+                                                     min(args.cpu_sample, 1 << 28))
     print(json.dumps(out), flush=True)
 
 
@@ -505,6 +612,30 @@ def main():
               "implemented", file=sys.stderr)
         sys.exit(2)
 
+    # Unequal token counts (sum 8 * 4096 + 123, not a power of two: the
+    # division is a true IEEE division, not a multiply).
+    counts = ([4096 + 1000 * (j % 3) - 1000 for j in range(args.nranks)]
+              if args.token_weighted else None)
+    if counts is not None:
+        counts[0] += 123
+    wire = "bf16" if args.wire == "bf16" else None
+
+    # The oracle over several processes, forked before this process touches
+    # the GPU: the same parameter count as the single-core sample below.
+    parallel = None
+    if not (args.no_cpu or args.overlap or args.zero2 or args.all_ranks):
+        from workloads import arena
+
+        shard = arena(args.config).numel // args.nranks
+        count = min(shard - ((shard // 2) & ~7), args.cpu_sample)
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        log(f"timing the CPU oracle on {count} parameters over {workers} processes")
+        try:
+            parallel = cpu_baseline_parallel(count, args.nranks, 0, 1 % args.nranks, workers,
+                                             wire, None if counts is None else sum(counts))
+        except Exception as e:  # reported, never fatal: it is a baseline
+            log(f"multi-process oracle timing failed: {e}")
+
     import torch
 
     import gradient_reduce_zero_amd as grz
@@ -539,13 +670,6 @@ def main():
     settle()
     log(f"inputs resident: P={setup['p']}, owned={setup['shard']}, "
         f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
-
-    # Unequal token counts (sum 8 * 4096 + 123, not a power of two: the
-    # division is a true IEEE division, not a multiply).
-    counts = ([4096 + 1000 * (j % 3) - 1000 for j in range(setup["n"])] if args.token_weighted
-              else None)
-    if counts is not None:
-        counts[0] += 123
 
     def reduce():
         pipe.reduce(inp["incoming"], stream, token_counts=counts)
@@ -667,9 +791,11 @@ def main():
         out["fused"] = fused_bench(args, setup, stream, dev)
     if not args.no_cpu:
         log(f"timing the CPU oracle on {args.cpu_sample} parameters")
-        cb = cpu_baseline(setup, args.cpu_sample, wire="bf16" if args.wire == "bf16" else None,
-                          token_counts=counts)
+        cb = cpu_baseline(setup, args.cpu_sample, wire=wire, token_counts=counts)
         out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        out["cpu_baseline"]["host_cpus"] = os.cpu_count()
+        out["cpu_baseline"]["affinity_cpus"] = len(os.sched_getaffinity(0))
+        out["cpu_baseline"]["parallel"] = parallel
     print(json.dumps(out), flush=True)
 
 

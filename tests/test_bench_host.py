@@ -50,3 +50,25 @@ def test_digest_ignores_comments_and_white_space(tmp_path, monkeypatch):
     assert bench.kernel_digest() == base
     alt.write_text(src.replace("kThreads = 256", "kThreads = 128"))
     assert bench.kernel_digest() != base
+
+
+def test_multi_process_oracle_timing_runs_on_disjoint_tiles():
+    # The baseline's second line: the same oracle step over forked workers.
+    r = bench.cpu_baseline_parallel(count=20_001, n=8, rank=0, chunk=1, workers=2)
+    assert r["cores"] == 2 and r["kind"] == "oracle" and r["value"] > 0
+    assert "20001 owned parameters in 2 tiles" in r["sample"]
+
+
+def test_all_ranks_oracle_timing_whole_arena_and_prefix():
+    import torch
+
+    from gradient_reduce_zero_amd.plan import Hyper
+    from workloads import rank_grad
+
+    p, n = 8 * 4096 * 3, 8
+    grads = [rank_grad(p, 1e-3, "bf16", 11 + r) for r in range(n)]
+    whole = bench.cpu_baseline_all_ranks(grads, [(0, p // 2), (p // 2, p // 2)], n, Hyper(), p)
+    assert whole["value"] > 0 and whole["sample"].startswith("the whole arena, 2 bucket(s)")
+    part = bench.cpu_baseline_all_ranks(grads, [(0, p)], n, Hyper(), 10_007)
+    assert part["sample"].startswith(f"the first 10000 of {p} parameters")
+    assert grads[0].dtype == torch.bfloat16
