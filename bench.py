@@ -489,6 +489,116 @@ def all_ranks_bench(args, dev):
     print(json.dumps(out), flush=True)
 
 
+def ddp_bytes(p, n, grad_bytes=2):
+    """Algorithmic HBM bytes of one rank's plain data-parallel step, per phase:
+    the reduce of its chunk (N chunks of P/N read, fp32 mean chunk written),
+    the peers' fp32 mean chunks copied in (read: simulation only; written),
+    and AdamW over the full arena with the bf16 write (30 B per parameter)."""
+    peers = 4 * p * (n - 1) // n
+    return {"reduce": grad_bytes * p + 4 * p // n, "gather": 2 * peers, "adamw": 30 * p}
+
+
+def ddp_bench(args, dev):
+    """One rank's plain data-parallel (ZeRO stage 0) step: one JSON line."""
+    import torch
+
+    import gradient_reduce_zero_amd as grz
+    from workloads import arena, grad_seed, master_init, onerank_inputs, rank_grad
+
+    a = arena(args.config)
+    p, n, rank = a.numel, args.nranks, 0
+    buckets = grz.plan_buckets(a.numels) if args.config == "gpt2_124m" else grz.whole_arena(p)
+    hyper = grz.Hyper(lr=1e-4, warmup=10) if args.config == "gpt2_1p5b" else grz.Hyper()
+    chunk = grz.owned_chunk(rank, n)
+    shard = grz.dp_shard_numel(buckets, n, chunk)
+    npieces = grz.dp_piece_count(buckets, n)
+    log(f"DDP one rank: {args.config}, N={n}, {len(buckets)} buckets")
+    inp = onerank_inputs(shard, n, rank, npieces, grz.GRZ_PIECE, device=dev)
+    incoming, partials = inp["incoming"], inp["partials"]
+    del inp
+    one = grz.DDPOneRank(buckets, n, rank, master_init(p, device=dev), hyper, dev)
+    one.norm.partials.copy_(partials)
+    peer_means = [None if j == rank else
+                  rank_grad(shard, 1e-3 / n ** 0.5, "f32", grad_seed(1, 100 + j), device=dev)
+                  for j in range(n)]
+    torch.cuda.synchronize()
+    log(f"inputs resident: P={p}, {torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
+    settle()
+    s = torch.cuda.current_stream()
+    t = 1
+    for _ in range(args.warmup):
+        one.step(incoming, peer_means, t, s)
+        t += 1
+    torch.cuda.synchronize()
+    names = ("reduce", "gather", "sqnorm", "adamw")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(s)
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(s)
+        one.reduce(incoming, s)
+        e[1].record(s)
+        one.receive_means(peer_means, s)
+        e[2].record(s)
+        one.norm.run(one.hyper.max_norm, s)
+        e[3].record(s)
+        w, m, v = one.state
+        grz.zero1_adamw_gather(w, m, v, one.mean, one.buckets, n, -1, one.norm.scale,
+                               grz.adamw_args(**grz.step_scalars(one.hyper, t)), [one.arena],
+                               stream=s)
+        e[4].record(s)
+        t += 1
+    stop.record(s)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    phase = {nm: sum(e[i].elapsed_time(e[i + 1]) for e in ev) / args.steps
+             for i, nm in enumerate(names)}
+    pb = ddp_bytes(p, n)
+    step_bytes = sum(pb.values())
+    simulated = 4 * p * (n - 1) // n
+    gbps = {k: pb[k] / (phase[k] * 1e-3) / 1e9 for k in pb}
+    log(f"{ms:.3f} ms/step, {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s; "
+        + ", ".join(f"{k} {v:.3f} ms" for k, v in phase.items()))
+    out = {"mode": "ddp_one_rank", "workload": f"{a.name} one-rank plain data parallelism",
+           "arena_params": p, "nranks_simulated": n, "rank": rank, "buckets": len(buckets),
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "params_updated_per_s": p / (ms * 1e-3), "step_bytes": step_bytes,
+           "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
+           "pct_of_peak_hbm": 100.0 * step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+           "step_bytes_without_simulated_reads": step_bytes - simulated,
+           "phases_ms": phase, "phases_GBps": gbps}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_ddp(incoming, n, hyper, min(args.cpu_sample, 1 << 27))
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_ddp(incoming, n, hyper, sample):
+    """The oracle's plain data-parallel step (``oracle.step.ddp_step``: the
+    all-reduce of every chunk, clip, AdamW over the whole arena) on an arena
+    of ``sample`` parameters (a multiple of N) made of the first values of the
+    ranks' incoming gradients."""
+    import numpy as np
+
+    from oracle.step import Hyper, ddp_step
+    from workloads import master_init, to_bits
+
+    count = min(sample, incoming[0].numel())
+    count -= count % n
+    g = [to_bits(x[:count]) for x in incoming]
+    w = to_bits(master_init(count))
+    z = np.zeros_like(w)
+    h = Hyper(lr=hyper.lr, warmup=hyper.warmup, max_norm=hyper.max_norm)
+    t0 = time.perf_counter()
+    ddp_step(g, "bf16", [(0, count)], (w, z, z), h, 1)
+    dt = time.perf_counter() - t0
+    return dict(value=count / dt, unit="params/s", cores=1, kind="oracle",
+                sample=f"an arena of {count} parameters (the first values of the {n} ranks' "
+                       f"incoming gradients), one bucket: ring folds of every chunk, float64 "
+                       f"norm, clip, fp32 AdamW, bf16 rounding; single-threaded NumPy, "
+                       f"{dt:.2f} s")
+
+
 def cold_bench(args, pipe, inp, stream, dev, t, step_bytes):
     """Each step preceded by a 512 MB scrub (outside the timed events)."""
     import torch
@@ -581,6 +691,10 @@ def main():
                     help="instead of one rank's share: the ZeRO-1 step of all N simulated "
                          "ranks of --config (every rank's reduce, AdamW and bf16 write to all "
                          "N replicas)")
+    ap.add_argument("--ddp", action="store_true",
+                    help="instead of the ZeRO-1 share: one rank's plain data-parallel step "
+                         "(its chunk reduced at arena offsets, the peers' fp32 mean chunks "
+                         "copied in, clip + AdamW over the full arena)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--token-weighted", action="store_true",
@@ -623,7 +737,7 @@ def main():
     # The oracle over several processes, forked before this process touches
     # the GPU: the same parameter count as the single-core sample below.
     parallel = None
-    if not (args.no_cpu or args.overlap or args.zero2 or args.all_ranks):
+    if not (args.no_cpu or args.overlap or args.zero2 or args.all_ranks or args.ddp):
         from workloads import arena
 
         shard = arena(args.config).numel // args.nranks
@@ -650,6 +764,9 @@ def main():
         return
     if args.all_ranks:
         all_ranks_bench(args, dev)
+        return
+    if args.ddp:
+        ddp_bench(args, dev)
         return
     if args.calibrate:
         numel = 1 << 30  # 2 GiB of bf16 read, 2 GiB written

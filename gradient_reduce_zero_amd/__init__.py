@@ -8,9 +8,11 @@ points), host planning and the step drivers.  There is no CPU fallback: a
 call fails if the library is not built.
 """
 
-from ._native import (GRZ_ARGS_DEVICE, GRZ_BF16, GRZ_BF16_WIRE, GRZ_F32, GRZ_F64, GRZ_IN_COMPACT, GRZ_IN_RANGE,
-                      GRZ_MAX_RANKS, GRZ_PIECE, GRZ_SUM, GRZ_UNEVEN, GrzError, lib)
-from .binding import (adamw_args, dp_chunk_range, dp_grad_sqnorm, dp_grad_sqnorm_of,
+from ._native import (GRZ_ARGS_DEVICE, GRZ_BF16, GRZ_BF16_WIRE, GRZ_F32, GRZ_F64, GRZ_IN_COMPACT,
+                      GRZ_IN_RANGE, GRZ_MAX_RANKS, GRZ_OUT_GLOBAL, GRZ_PIECE, GRZ_SUM,
+                      GRZ_UNEVEN, GrzError, lib)
+from .binding import (adamw_args, dp_all_gather, dp_chunk_range, dp_grad_sqnorm,
+                      dp_grad_sqnorm_of,
                       dp_grad_sqnorm_of_workspace, dp_grad_sqnorm_workspace,
                       dp_piece_count, dp_piece_offset, dp_reduce_scatter_mean,
                       dp_ring_chunk_owner, dp_ring_owned_chunk, dp_shard_numel,
@@ -20,7 +22,7 @@ from .binding import (adamw_args, dp_chunk_range, dp_grad_sqnorm, dp_grad_sqnorm
                       zero1_fused_workspace)
 from .plan import (Hyper, owned_chunk, plan_buckets, resident_bytes, step_scalars, whole_arena,
                    zero_stage)
-from .step import (CapturedStep, DDPStep, OverlappedZero1, Zero1AllRanks, Zero1OneRank,
-                   Zero2AllRanks)
+from .step import (CapturedStep, DDPOneRank, DDPStep, OverlappedZero1, Zero1AllRanks,
+                   Zero1OneRank, Zero2AllRanks)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -15,8 +15,8 @@ LIB_PATH = os.path.join(HERE, "libgrz.so")
 
 GRZ_OK, GRZ_EINVAL, GRZ_EINDIVISIBLE, GRZ_EALIGN, GRZ_EHIP, GRZ_ERANGE = range(6)
 GRZ_F32, GRZ_BF16, GRZ_F64 = 0, 1, 2
-GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT, GRZ_BF16_WIRE, GRZ_IN_RANGE, GRZ_ARGS_DEVICE = (
-    1, 2, 4, 8, 16, 32)
+(GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT, GRZ_BF16_WIRE, GRZ_IN_RANGE, GRZ_ARGS_DEVICE,
+ GRZ_OUT_GLOBAL) = (1, 2, 4, 8, 16, 32, 64)
 GRZ_MAX_RANKS = 16
 GRZ_PIECE = 4096
 
@@ -58,6 +58,7 @@ SIGNATURES = {
     "zero1_adamw_gather": (_i, [_vp, _vp, _vp, _vp, _BP, _i, _i, _i, _i, _vp,
                                 ctypes.POINTER(AdamWArgs), _pp, _i, _vp]),
     "zero1_all_gather": (_i, [_pp, _i, _BP, _i, _i, _pp, _i, _vp]),
+    "dp_all_gather": (_i, [_pp, _i, _i, _BP, _i, _i, _pp, _i, _vp]),
     "grz_step_args_next": (_i, [_vp, _i64, _vp, _vp, _vp]),
     "grz_set_spin_limit": (_i, [ctypes.c_uint]),
     "zero1_fused_workspace": (ctypes.c_size_t, [_i64]),

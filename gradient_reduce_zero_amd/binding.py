@@ -133,7 +133,7 @@ def dp_reduce_scatter_mean(rank_grads, buckets, chunk, mean_out, piece_sqnorm=No
     if chunk >= 0:
         shard = dp_shard_numel(buckets, n, chunk, flags & N.GRZ_UNEVEN)
         need_in = shard if flags & N.GRZ_IN_COMPACT else _extent(buckets)
-        need_out = shard
+        need_out = _extent(buckets) if flags & N.GRZ_OUT_GLOBAL else shard
     else:
         need_in = need_out = _extent(buckets)
     if flags & N.GRZ_IN_RANGE:
@@ -289,6 +289,36 @@ def zero1_all_gather(shards, buckets, replicas, flags=0, stream=None):
     arr, nb = _bucket_array(buckets)
     check("zero1_all_gather", lib().zero1_all_gather(sp, n, arr, nb, flags, reps, len(replicas),
                                                      _stream(stream)))
+
+
+def dp_all_gather(shards, buckets, replicas, flags=0, stream=None):
+    """``zero1_all_gather`` for bf16, fp32 or fp64 shards (all of one dtype, that of
+    the replicas): rank r's shard-compact chunk (r + 1) mod N lands at its arena
+    offsets in every replica (``None`` = already in place)."""
+    buckets = list(buckets)
+    n = len(shards)
+    given = [s for s in shards if s is not None] + list(replicas)
+    if not given:
+        raise ValueError("no shard and no replica")
+    dt = given[0].dtype
+    kind = _KIND.get(dt)
+    if kind is None:
+        raise TypeError(f"dtype {dt} not supported")
+    same = _BF16_LIKE if kind == N.GRZ_BF16 else (dt,)
+    ext = _extent(buckets)
+    ptrs = []
+    for r, s in enumerate(shards):
+        if s is None:
+            ptrs.append(None)
+        else:
+            need = dp_shard_numel(buckets, n, (r + 1) % n, flags)
+            ptrs.append(_dev(s, f"shards[{r}]", same, need).value)
+    sp = (ctypes.c_void_p * max(n, 1))(*ptrs)
+    reps = (ctypes.c_void_p * max(len(replicas), 1))(
+        *[_dev(r, f"replicas[{i}]", same, ext).value for i, r in enumerate(replicas)])
+    arr, nb = _bucket_array(buckets)
+    check("dp_all_gather", lib().dp_all_gather(sp, n, kind, arr, nb, flags, reps, len(replicas),
+                                               _stream(stream)))
 
 
 def grz_set_spin_limit(polls):

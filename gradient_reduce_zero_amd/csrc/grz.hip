@@ -970,7 +970,8 @@ int check_plan(const grz_bucket* buckets, int nbuckets, int nranks, int chunk, i
   if (nranks < 1 || nranks > GRZ_MAX_RANKS) return GRZ_EINVAL;
   if (nbuckets < 0 || (nbuckets > 0 && buckets == nullptr)) return GRZ_EINVAL;
   if (chunk < -1 || chunk >= nranks) return GRZ_EINVAL;
-  if (flags & ~(GRZ_SUM | GRZ_UNEVEN | GRZ_IN_COMPACT | GRZ_BF16_WIRE | GRZ_IN_RANGE))
+  if (flags & ~(GRZ_SUM | GRZ_UNEVEN | GRZ_IN_COMPACT | GRZ_BF16_WIRE | GRZ_IN_RANGE |
+                GRZ_OUT_GLOBAL))
     return GRZ_EINVAL;
   for (int b = 0; b < nbuckets; ++b) {
     if (buckets[b].offset < 0 || buckets[b].length < 0) return GRZ_ERANGE;
@@ -1074,12 +1075,13 @@ int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>
   args.divisor = static_cast<double>(divisor);
   args.pow2 = (divisor & (divisor - 1)) == 0;
   const bool compact_in = (flags & GRZ_IN_COMPACT) != 0;
+  const bool out_global = (flags & GRZ_OUT_GLOBAL) != 0;
   std::vector<Seg> segs;
   segs.reserve(ps.size());
   for (const PlanSeg& p : ps) {
     Seg s{};
     s.src = compact_in ? p.compact : p.input;
-    s.dst = p.compact;
+    s.dst = out_global ? p.global : p.compact;
     s.len = p.len;
     s.piece0 = p.piece0;
     s.chunk = p.chunk;
@@ -1111,6 +1113,55 @@ int reduce_entry(const void* const* rank_grads, int nranks, int64_t divisor, int
                  int chunk, int flags, void* mean_out, double* piece_sqnorm,
                  hipStream_t stream);
 
+// All-gather of shards whose elements are `units` 16-bit words (1 bf16, 2
+// fp32, 4 fp64): the plan's segments in elements, copied as words by the
+// bf16 copy kernel.
+int gather_entry(const void* const* shards, int nranks, int units, const grz_bucket* buckets,
+                 int nbuckets, int flags, void* const* replicas, int nreplicas,
+                 hipStream_t stream) {
+  if (flags & ~GRZ_UNEVEN) return GRZ_EINVAL;
+  if (shards == nullptr) return GRZ_EINVAL;
+  if (nreplicas < 0 || nreplicas > GRZ_MAX_RANKS) return GRZ_EINVAL;
+  if (nreplicas > 0 && replicas == nullptr) return GRZ_EINVAL;
+  for (int r = 0; r < nranks && r < GRZ_MAX_RANKS; ++r) {
+    const int st = check_plan(buckets, nbuckets, nranks, (r + 1) % nranks, flags);
+    if (st != GRZ_OK) return st;
+  }
+  const int st = check_plan(buckets, nbuckets, nranks, -1, flags);
+  if (st != GRZ_OK) return st;
+  const size_t elem = 2 * static_cast<size_t>(units);
+  for (int b = 0; b < nbuckets; ++b)  // word offsets must stay below 2^59
+    if (buckets[b].offset + buckets[b].length > (INT64_MAX >> 4) / units) return GRZ_ERANGE;
+  static GatherArgs proto;
+  GatherArgs a = proto;
+  bool vec_base = true;
+  for (int r = 0; r < nreplicas; ++r) {
+    if (replicas[r] == nullptr) return GRZ_EINVAL;
+    if (!aligned(replicas[r], elem)) return GRZ_EALIGN;
+    vec_base = vec_base && aligned(replicas[r], 16);
+    a.rep[r] = static_cast<uint16_t*>(replicas[r]);
+  }
+  a.nrep = nreplicas;
+  if (nreplicas == 0) return GRZ_OK;
+  std::vector<Seg> segs;
+  for (int r = 0; r < nranks; ++r) {
+    a.shard[r] = static_cast<const uint16_t*>(shards[r]);
+    if (shards[r] == nullptr) continue;
+    if (!aligned(shards[r], elem)) return GRZ_EALIGN;
+    const bool vr = vec_base && aligned(shards[r], 16);
+    for (const PlanSeg& p : plan_segments(buckets, nbuckets, nranks, (r + 1) % nranks)) {
+      Seg s{};
+      s.src = p.compact * units;
+      s.dst = p.global * units;
+      s.len = p.len * units;
+      s.chunk = r;
+      s.vec = vr && s.src % 8 == 0 && s.dst % 8 == 0;
+      segs.push_back(s);
+    }
+  }
+  return launch_batches(segs, a, gather_kernel, stream, GRZ_AG_TILE, GRZ_AG_THREADS);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1118,7 +1169,7 @@ int reduce_entry(const void* const* rank_grads, int nranks, int64_t divisor, int
 
 extern "C" {
 
-int grz_version(void) { return 100; }
+int grz_version(void) { return 101; }
 
 const char* grz_strerror(int status) {
   switch (status) {
@@ -1416,7 +1467,8 @@ int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad
   flags &= ~GRZ_ARGS_DEVICE;
   const int st = check_plan(buckets, nbuckets, nranks, chunk, flags);
   if (st != GRZ_OK) return st;
-  if (flags & (GRZ_SUM | GRZ_IN_COMPACT | GRZ_BF16_WIRE | GRZ_IN_RANGE)) return GRZ_EINVAL;
+  if (flags & (GRZ_SUM | GRZ_IN_COMPACT | GRZ_BF16_WIRE | GRZ_IN_RANGE | GRZ_OUT_GLOBAL))
+    return GRZ_EINVAL;
   std::vector<PlanSeg> ps;
   if (chunk >= 0) {
     ps = plan_segments(buckets, nbuckets, nranks, chunk);
@@ -1444,44 +1496,18 @@ int grz_step_args_next(const grz_adamw_args* table, int64_t count, int64_t* coun
 int zero1_all_gather(const uint16_t* const* shards, int nranks, const grz_bucket* buckets,
                      int nbuckets, int flags, uint16_t* const* replicas, int nreplicas,
                      hipStream_t stream) {
-  if (flags & ~GRZ_UNEVEN) return GRZ_EINVAL;
-  if (shards == nullptr) return GRZ_EINVAL;
-  if (nreplicas < 0 || nreplicas > GRZ_MAX_RANKS) return GRZ_EINVAL;
-  if (nreplicas > 0 && replicas == nullptr) return GRZ_EINVAL;
-  for (int r = 0; r < nranks && r < GRZ_MAX_RANKS; ++r) {
-    const int st = check_plan(buckets, nbuckets, nranks, (r + 1) % nranks, flags);
-    if (st != GRZ_OK) return st;
-  }
-  const int st = check_plan(buckets, nbuckets, nranks, -1, flags);
-  if (st != GRZ_OK) return st;
-  static GatherArgs proto;
-  GatherArgs a = proto;
-  bool vec_base = true;
-  for (int r = 0; r < nreplicas; ++r) {
-    if (replicas[r] == nullptr) return GRZ_EINVAL;
-    if (!aligned(replicas[r], 2)) return GRZ_EALIGN;
-    vec_base = vec_base && aligned(replicas[r], 16);
-    a.rep[r] = replicas[r];
-  }
-  a.nrep = nreplicas;
-  if (nreplicas == 0) return GRZ_OK;
-  std::vector<Seg> segs;
-  for (int r = 0; r < nranks; ++r) {
-    a.shard[r] = shards[r];
-    if (shards[r] == nullptr) continue;
-    if (!aligned(shards[r], 2)) return GRZ_EALIGN;
-    const bool vr = vec_base && aligned(shards[r], 16);
-    for (const PlanSeg& p : plan_segments(buckets, nbuckets, nranks, (r + 1) % nranks)) {
-      Seg s{};
-      s.src = p.compact;
-      s.dst = p.global;
-      s.len = p.len;
-      s.chunk = r;
-      s.vec = vr && s.src % 8 == 0 && s.dst % 8 == 0;
-      segs.push_back(s);
-    }
-  }
-  return launch_batches(segs, a, gather_kernel, stream, GRZ_AG_TILE, GRZ_AG_THREADS);
+  return gather_entry(reinterpret_cast<const void* const*>(shards), nranks, 1, buckets,
+                      nbuckets, flags, reinterpret_cast<void* const*>(replicas), nreplicas,
+                      stream);
+}
+
+int dp_all_gather(const void* const* shards, int nranks, int dtype, const grz_bucket* buckets,
+                  int nbuckets, int flags, void* const* replicas, int nreplicas,
+                  hipStream_t stream) {
+  const int units = dtype == GRZ_BF16 ? 1 : dtype == GRZ_F32 ? 2 : dtype == GRZ_F64 ? 4 : 0;
+  if (units == 0) return GRZ_EINVAL;
+  return gather_entry(shards, nranks, units, buckets, nbuckets, flags, replicas, nreplicas,
+                      stream);
 }
 
 int grz_set_spin_limit(unsigned polls) {

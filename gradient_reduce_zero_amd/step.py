@@ -29,7 +29,7 @@ synchronisation inside a step.
 import torch
 
 from . import binding as B
-from ._native import GRZ_IN_COMPACT, GRZ_IN_RANGE, GRZ_PIECE
+from ._native import GRZ_IN_COMPACT, GRZ_IN_RANGE, GRZ_OUT_GLOBAL, GRZ_PIECE
 from .plan import Hyper, owned_chunk, step_scalars
 
 
@@ -230,6 +230,60 @@ class Zero1OneRank:
             self.reduce(incoming, stream)
             self.update(None, stream, args=args)
         self.gather(peer_shards, stream)
+
+
+class DDPOneRank:
+    """Plain data-parallel (ZeRO stage 0) step of one rank; its peers'
+    contributions arrive as inputs.
+
+    The all-reduce of the mean is a reduce-scatter followed by an all-gather:
+    this rank reduces its chunk ((rank + 1) mod N of every bucket) in ring
+    order straight into its arena positions of the full fp32 mean, the peers'
+    mean chunks land around it, and the rank runs clip + AdamW over its full
+    copy of the state and writes its bf16 arena.  Per step the caller
+    provides (all resident on the device):
+
+    * ``incoming[j]`` -- rank j's gradient values of this rank's chunk,
+      shard-compact;
+    * ``peer_means[j]`` -- rank j's mean of its own chunk, shard-compact (what
+      the all-gather half delivers; ``None`` at this rank);
+    * the peers' norm pieces, written into ``self.norm.partials`` outside this
+      rank's slots.
+    """
+
+    def __init__(self, buckets, nranks, rank, master, hyper=None, device="cuda"):
+        self.buckets = [(int(o), int(l)) for o, l in buckets]
+        self.n, self.rank = nranks, rank
+        self.chunk = owned_chunk(rank, nranks)
+        self.hyper = hyper or Hyper()
+        w = master.to(device=device, dtype=torch.float32).contiguous().clone()
+        self.state = (w, torch.zeros_like(w), torch.zeros_like(w))
+        self.mean = torch.zeros_like(w)
+        self.norm = _Norm(B.dp_piece_count(self.buckets, nranks), device)
+        self.arena = w.to(torch.bfloat16)
+
+    own_piece_slots = Zero1OneRank.own_piece_slots
+
+    def reduce(self, incoming, stream=None):
+        B.dp_reduce_scatter_mean(incoming, self.buckets, self.chunk, self.mean,
+                                 self.norm.partials, flags=GRZ_IN_COMPACT | GRZ_OUT_GLOBAL,
+                                 stream=stream)
+
+    def receive_means(self, peer_means, stream=None):
+        B.dp_all_gather(peer_means, self.buckets, [self.mean], stream=stream)
+
+    def update(self, t, stream=None, args=None):
+        self.norm.run(self.hyper.max_norm, stream)
+        if args is None:
+            args = B.adamw_args(**step_scalars(self.hyper, t))
+        w, m, v = self.state
+        B.zero1_adamw_gather(w, m, v, self.mean, self.buckets, self.n, -1, self.norm.scale,
+                             args, [self.arena], stream=stream)
+
+    def step(self, incoming, peer_means, t, stream=None):
+        self.reduce(incoming, stream)
+        self.receive_means(peer_means, stream)
+        self.update(t, stream)
 
 
 class OverlappedZero1:

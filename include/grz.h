@@ -10,6 +10,8 @@
  *   zero1_adamw_step         clipped AdamW on the owned shard (+ bf16 copy,
  *                            optionally written straight into the replicas)
  *   zero1_all_gather         owned bf16 shards into every replica arena
+ *   dp_all_gather            the same for fp32 / fp64 / bf16 shards (the
+ *                            second half of a plain all-reduce)
  *   zero1_fused_step         the four above for one shard in one launch
  *
  * Sources: "Lab 09 -- Parallelism, simulated" s.1 "Ring all-reduce" (the
@@ -92,7 +94,8 @@ enum {
   GRZ_IN_COMPACT = 4, /* rank inputs hold only the reduced chunk, compact */
   GRZ_BF16_WIRE = 8,  /* bf16 gradients: round every partial sum to bf16  */
   GRZ_IN_RANGE = 16,  /* rank inputs hold only the reduced bucket range     */
-  GRZ_ARGS_DEVICE = 32 /* zero1_adamw_gather: `args` is a device pointer    */
+  GRZ_ARGS_DEVICE = 32, /* zero1_adamw_gather: `args` is a device pointer   */
+  GRZ_OUT_GLOBAL = 64   /* reduce, chunk >= 0: mean_out indexed like the arena */
 };
 
 #define GRZ_MAX_RANKS 16    /* N and the number of replicas per call       */
@@ -171,6 +174,10 @@ int64_t dp_shard_numel(const grz_bucket* buckets, int nbuckets, int nranks, int 
  *             chunk (plain data parallelism; mean_out is indexed like the
  *             arena and only bucket ranges are written).
  * flags       GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT (needs chunk >= 0),
+ *             GRZ_OUT_GLOBAL (chunk >= 0: mean_out is indexed like the arena
+ *             and only the chunk's ranges are written -- the reduce-scatter
+ *             half of a plain all-reduce, whose all-gather half, dp_all_gather,
+ *             brings the other chunks; no effect with chunk -1),
  *             GRZ_BF16_WIRE (needs GRZ_BF16): the ring's wire format is bf16,
  *             so every partial sum of the fold -- the last one included -- is
  *             rounded to bf16 (nearest even) before the next rank adds to it
@@ -333,6 +340,22 @@ int grz_step_args_next(const grz_adamw_args* table, int64_t count, int64_t* coun
 int zero1_all_gather(const uint16_t* const* shards, int nranks, const grz_bucket* buckets,
                      int nbuckets, int flags, uint16_t* const* replicas, int nreplicas,
                      hipStream_t stream);
+
+/*
+ * zero1_all_gather for shards of any element type: GRZ_BF16 (2 bytes),
+ * GRZ_F32 (4) or GRZ_F64 (8).  With fp32 shards it is the all-gather half of
+ * a plain all-reduce of the mean ("Lab 09", s.1: an all-reduce is a
+ * reduce-scatter followed by an all-gather; "A4", "Part 3", ncclAllReduce):
+ * rank r's mean of chunk (r + 1) mod N, from dp_reduce_scatter_mean, lands at
+ * its arena offsets in every replica.  The copy is of bytes: the values
+ * arrive unchanged.  shards[r] is shard-compact (dp_shard_numel elements) or
+ * NULL; replicas are arenas of `dtype` elements.  Errors as zero1_all_gather,
+ * plus GRZ_EINVAL for another dtype and GRZ_EALIGN for a pointer not aligned
+ * to its element.
+ */
+int dp_all_gather(const void* const* shards, int nranks, int dtype, const grz_bucket* buckets,
+                  int nbuckets, int flags, void* const* replicas, int nreplicas,
+                  hipStream_t stream);
 
 /*
  * Polls a grid-wide wait of zero1_fused_step makes before it gives up (>= 1;

@@ -147,6 +147,16 @@ static void argument_errors(void) {
   CHECK(zero1_all_gather(shards, 2, odd, 1, 0, reps, 1, NULL) == GRZ_EINDIVISIBLE, "indivisible");
   CHECK(zero1_all_gather(shards, 2, ok, 1, GRZ_SUM, reps, 1, NULL) == GRZ_EINVAL, "flag");
   CHECK(zero1_all_gather(shards, 0, ok, 1, 0, reps, 1, NULL) == GRZ_EINVAL, "N=0");
+  const void* vshards[2] = {(void*)0xA00000, (void*)0xB00000};
+  void* vreps[1] = {(void*)0x900000};
+  void* vodd[1] = {(void*)0x900002};
+  CHECK(dp_all_gather(vshards, 2, 7, ok, 1, 0, vreps, 1, NULL) == GRZ_EINVAL, "gather dtype");
+  CHECK(dp_all_gather(vshards, 2, GRZ_F32, odd, 1, 0, vreps, 1, NULL) == GRZ_EINDIVISIBLE,
+        "indivisible fp32 gather");
+  CHECK(dp_all_gather(vshards, 2, GRZ_F32, ok, 1, 0, vodd, 1, NULL) == GRZ_EALIGN,
+        "fp32 replica off its alignment");
+  CHECK(zero1_adamw_gather(f, f, f, f, ok, 1, 2, 0, GRZ_OUT_GLOBAL, NULL, &args, reps, 1,
+                           NULL) == GRZ_EINVAL, "reduce-only flag on the optimizer");
   CHECK(grz_set_max_blocks(0) == GRZ_EINVAL, "blocks");
   /* The norm straight from an fp32 array. */
   CHECK(dp_grad_sqnorm_of_workspace(0) == 0, "empty workspace");

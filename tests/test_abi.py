@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(N.SIGNATURES), "binding signatures out of step with the header"
-    assert lib.grz_version() == 100
+    assert lib.grz_version() == 101
 
 
 def test_header_constants_match_binding():
@@ -37,7 +37,7 @@ def test_header_constants_match_binding():
     assert re.search(r"#define GRZ_MAX_RANKS (\d+)", text).group(1) == str(N.GRZ_MAX_RANKS)
     assert re.search(r"#define GRZ_PIECE (\d+)", text).group(1) == str(N.GRZ_PIECE)
     for name in ("GRZ_SUM", "GRZ_UNEVEN", "GRZ_IN_COMPACT", "GRZ_BF16_WIRE", "GRZ_IN_RANGE",
-                 "GRZ_ARGS_DEVICE",
+                 "GRZ_ARGS_DEVICE", "GRZ_OUT_GLOBAL",
                  "GRZ_EINDIVISIBLE",
                  "GRZ_BF16"):
         assert re.search(rf"{name} = (\d+)", text).group(1) == str(getattr(N, name))
@@ -91,7 +91,7 @@ def test_argument_errors_return_before_any_launch():
     assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], 2, 0, out) == N.GRZ_EINVAL
     assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], -1, N.GRZ_IN_COMPACT, out) == N.GRZ_EINVAL
     assert _rs(lib, fake, 2, N.GRZ_F32, [(-4, 64)], 0, 0, out) == N.GRZ_ERANGE
-    assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], 0, 64, out) == N.GRZ_EINVAL
+    assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], 0, 1 << 9, out) == N.GRZ_EINVAL
     assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], 0, N.GRZ_BF16_WIRE, out) == N.GRZ_EINVAL
     both = N.GRZ_IN_RANGE | N.GRZ_IN_COMPACT
     assert _rs(lib, fake, 2, N.GRZ_F32, [(0, 64)], 0, both, out) == N.GRZ_EINVAL
@@ -105,6 +105,32 @@ def test_argument_errors_return_before_any_launch():
     for code in range(6):
         assert lib.grz_strerror(code)
     assert b"divisible" in lib.grz_strerror(N.GRZ_EINDIVISIBLE)
+
+
+def test_all_gather_and_out_global_refusals_before_any_launch():
+    # dp_all_gather: a dtype outside bf16/fp32/fp64, an unknown flag, a null
+    # shard table and a pointer off its element's alignment fail on the host;
+    # the optimizer refuses the reduce-only GRZ_OUT_GLOBAL.
+    lib = grz.lib()
+    b = (N.Bucket * 1)((0, 64))
+    shards = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    reps = (ctypes.c_void_p * 1)(0x30000)
+    assert lib.dp_all_gather(shards, 2, 7, b, 1, 0, reps, 1, None) == N.GRZ_EINVAL
+    assert lib.dp_all_gather(shards, 2, N.GRZ_F32, b, 1, N.GRZ_SUM, reps, 1, None) == N.GRZ_EINVAL
+    assert lib.dp_all_gather(None, 2, N.GRZ_F32, b, 1, 0, reps, 1, None) == N.GRZ_EINVAL
+    assert lib.dp_all_gather(shards, 17, N.GRZ_F32, b, 1, 0, reps, 1, None) == N.GRZ_EINVAL
+    odd = (ctypes.c_void_p * 1)(0x30002)  # 2-byte aligned: fine for bf16, not for fp32
+    assert lib.dp_all_gather(shards, 2, N.GRZ_F32, b, 1, 0, odd, 1, None) == N.GRZ_EALIGN
+    assert lib.dp_all_gather(shards, 2, N.GRZ_F64, b, 1, 0, (ctypes.c_void_p * 1)(0x30004), 1,
+                             None) == N.GRZ_EALIGN
+    assert lib.dp_all_gather(shards, 2, N.GRZ_F32, (N.Bucket * 1)((0, 63)), 1, 0, reps, 1,
+                             None) == N.GRZ_EINDIVISIBLE
+    args = N.AdamWArgs(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05)
+    assert lib.zero1_adamw_gather(16, 16, 16, 16, b, 1, 2, 0, N.GRZ_OUT_GLOBAL, 16,
+                                  ctypes.byref(args), reps, 1, None) == N.GRZ_EINVAL
+    assert lib.zero1_fused_step((ctypes.c_void_p * 2)(16, 16), 2, N.GRZ_BF16, b, 1, 0,
+                                N.GRZ_OUT_GLOBAL, 16, 16, 16, ctypes.byref(args), 1.0, reps, 1,
+                                16, 16, None, None, None, None) == N.GRZ_EINVAL
 
 
 def test_product_path_refuses_cpu_tensors():

@@ -72,3 +72,21 @@ def test_all_ranks_oracle_timing_whole_arena_and_prefix():
     part = bench.cpu_baseline_all_ranks(grads, [(0, p)], n, Hyper(), 10_007)
     assert part["sample"].startswith(f"the first 10000 of {p} parameters")
     assert grads[0].dtype == torch.bfloat16
+
+
+def test_ddp_byte_model():
+    # sP + 4P/N (reduce) + 2 * 4P(N-1)/N (peer means read and written) + 30P:
+    # 39.5 P at N = 8 with bf16 gradients, 4P(N-1)/N of it simulation-only.
+    p = 8 * 1000
+    b = bench.ddp_bytes(p, 8)
+    assert b == {"reduce": 2 * p + p // 2, "gather": 7 * p, "adamw": 30 * p}
+    assert sum(b.values()) == 39.5 * p
+
+
+def test_ddp_oracle_timing_runs():
+    from gradient_reduce_zero_amd.plan import Hyper
+    from workloads import rank_grad
+
+    inc = [rank_grad(5000, 1e-3, "bf16", 21 + j) for j in range(8)]
+    r = bench.cpu_baseline_ddp(inc, 8, Hyper(), 4099)
+    assert r["value"] > 0 and "an arena of 4096 parameters" in r["sample"]
