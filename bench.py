@@ -174,7 +174,7 @@ def _oracle_worker(i, count, n, rank, chunk, wire, divisor, barrier, results):
         peers = [None if s is None else to_bits(s) for s in inp["peer_shards"]]
         partials = to_bits(inp["partials"])
         del inp
-        barrier.wait(timeout=600)
+        barrier.wait(timeout=240)
         t0 = time.perf_counter()
         _oracle_onerank(g, w, peers, partials, n, chunk, wire, divisor)
         results.put(("ok", i, count, t0, time.perf_counter()))
@@ -190,6 +190,7 @@ def cpu_baseline_parallel(count, n, rank, chunk, workers, wire=None, divisor=Non
     Throughput = count / (last end - first start), clocks being the system's
     monotonic one."""
     import multiprocessing as mp
+    import queue
 
     ctx = mp.get_context("fork")
     barrier, results = ctx.Barrier(workers), ctx.Queue()
@@ -199,15 +200,23 @@ def cpu_baseline_parallel(count, n, rank, chunk, workers, wire=None, divisor=Non
                          daemon=True) for i in range(workers)]
     for pr in procs:
         pr.start()
-    got = []
+    got, ok = [], False
+    deadline = time.monotonic() + 300
     try:
-        for _ in procs:
-            got.append(results.get(timeout=900))
+        while len(got) < workers:
+            try:
+                got.append(results.get(timeout=2))
+            except queue.Empty:
+                dead = [pr.exitcode for pr in procs if pr.exitcode not in (None, 0)]
+                if dead or time.monotonic() > deadline:
+                    raise RuntimeError("oracle workers " + ("exited with " + str(dead) if dead
+                                                            else "timed out"))
+        ok = True
     finally:
         for pr in procs:
+            if not ok and pr.is_alive():
+                pr.kill()  # our own children, by handle
             pr.join(timeout=60)
-            if pr.is_alive():
-                pr.kill()
     bad = [r for r in got if r[0] != "ok"]
     if bad:
         raise RuntimeError(f"oracle worker {bad[0][1]} failed: {bad[0][2]}")

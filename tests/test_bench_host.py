@@ -90,3 +90,16 @@ def test_ddp_oracle_timing_runs():
     inc = [rank_grad(5000, 1e-3, "bf16", 21 + j) for j in range(8)]
     r = bench.cpu_baseline_ddp(inc, 8, Hyper(), 4099)
     assert r["value"] > 0 and "an arena of 4096 parameters" in r["sample"]
+
+
+def test_multi_process_oracle_timing_reports_a_failed_worker_promptly():
+    # A worker that raises (here: an unknown wire precision) ends the run with
+    # an error naming it, instead of leaving the others waiting.
+    import time
+
+    import pytest
+
+    t0 = time.monotonic()
+    with pytest.raises(RuntimeError, match="unknown wire precision"):
+        bench.cpu_baseline_parallel(1000, 8, 0, 1, 2, wire="fp8")
+    assert time.monotonic() - t0 < 60
