@@ -498,6 +498,56 @@ def all_ranks_bench(args, dev):
     print(json.dumps(out), flush=True)
 
 
+def torch_reference(args, setup, stream):
+    """The same one-rank step written with PyTorch ops on the same resident
+    inputs -- the fold as an fp32 copy plus in-place adds in ring order, the
+    division, the fp64 norm with the peers' pieces, the clip, fused AdamW, the
+    bf16 copy into the arena and the peers' shard copies.  A timing reference
+    (the norm is not summed in the library's tree), not part of the product."""
+    import torch
+
+    inp, n, c, shard = setup["inp"], setup["n"], setup["chunk"], setup["shard"]
+    rows, peers = inp["incoming"], inp["peer_shards"]
+    if len(setup["buckets"]) != 1:
+        return None  # one whole-arena bucket only: each chunk is one arena range
+    arena = torch.zeros(setup["p"], dtype=torch.bfloat16, device=rows[0].device)
+    acc = torch.empty(shard, device=rows[0].device)
+    peer_sq = inp["partials"].sum()
+    param = torch.nn.Parameter(inp["shard_master"].clone())
+    opt = torch.optim.AdamW([param], lr=1e-3, betas=(0.9, 0.95), eps=1e-8, weight_decay=0.1,
+                            fused=True)
+
+    def step():
+        acc.copy_(rows[c])
+        for j in range(1, n):
+            acc.add_(rows[(c + j) % n])
+        acc.div_(n)
+        sq = torch.linalg.vector_norm(acc, dtype=torch.float64) ** 2 + peer_sq
+        scale = torch.clamp(1.0 / torch.sqrt(sq), max=1.0).to(torch.float32)
+        param.grad = acc.mul_(scale)
+        opt.step()
+        arena[c * shard:(c + 1) * shard].copy_(param.detach())
+        for j, s in enumerate(peers):
+            if s is not None:
+                cj = (j + 1) % n
+                arena[cj * shard:(cj + 1) * shard].copy_(s)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"the same step in PyTorch ops: {ms:.3f} ms/step")
+    return {"ms_per_step": ms, "value": shard / (ms * 1e-3),
+            "what": "PyTorch ops: fp32 fold by in-place adds, vector_norm, clip, "
+                    "AdamW(fused=True), bf16 and peer copies"}
+
+
 def ddp_bytes(p, n, grad_bytes=2):
     """Algorithmic HBM bytes of one rank's plain data-parallel step, per phase:
     the reduce of its chunk (N chunks of P/N read, fp32 mean chunk written),
@@ -704,6 +754,9 @@ def main():
                     help="instead of the ZeRO-1 share: one rank's plain data-parallel step "
                          "(its chunk reduced at arena offsets, the peers' fp32 mean chunks "
                          "copied in, clip + AdamW over the full arena)")
+    ap.add_argument("--torch-ref", action="store_true",
+                    help="also time the same one-rank step written with PyTorch ops "
+                         "(fused AdamW) on the same inputs, as a reference")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--token-weighted", action="store_true",
@@ -915,6 +968,8 @@ def main():
         out["cold"] = cold_bench(args, pipe, inp, stream, dev, t, step_bytes)
     if args.fused:
         out["fused"] = fused_bench(args, setup, stream, dev)
+    if args.torch_ref:
+        out["torch_reference"] = torch_reference(args, setup, stream)
     if not args.no_cpu:
         log(f"timing the CPU oracle on {args.cpu_sample} parameters")
         cb = cpu_baseline(setup, args.cpu_sample, wire=wire, token_counts=counts)
