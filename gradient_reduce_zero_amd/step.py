@@ -29,7 +29,7 @@ synchronisation inside a step.
 import torch
 
 from . import binding as B
-from ._native import GRZ_IN_COMPACT, GRZ_IN_RANGE, GRZ_OUT_GLOBAL, GRZ_PIECE
+from ._native import GRZ_IN_COMPACT, GRZ_IN_RANGE, GRZ_OUT_GLOBAL, GRZ_PIECE, GRZ_UNEVEN
 from .plan import Hyper, owned_chunk, step_scalars
 
 
@@ -249,28 +249,33 @@ class DDPOneRank:
       the all-gather half delivers; ``None`` at this rank);
     * the peers' norm pieces, written into ``self.norm.partials`` outside this
       rank's slots.
+
+    Bucket lengths need not divide by N (plain data parallelism is what runs
+    when they do not): the chunks then follow the array_split rule.
     """
 
     def __init__(self, buckets, nranks, rank, master, hyper=None, device="cuda"):
         self.buckets = [(int(o), int(l)) for o, l in buckets]
         self.n, self.rank = nranks, rank
+        self.flags = GRZ_UNEVEN if any(l % nranks for _, l in self.buckets) else 0
         self.chunk = owned_chunk(rank, nranks)
         self.hyper = hyper or Hyper()
         w = master.to(device=device, dtype=torch.float32).contiguous().clone()
         self.state = (w, torch.zeros_like(w), torch.zeros_like(w))
         self.mean = torch.zeros_like(w)
-        self.norm = _Norm(B.dp_piece_count(self.buckets, nranks), device)
+        self.norm = _Norm(B.dp_piece_count(self.buckets, nranks, self.flags), device)
         self.arena = w.to(torch.bfloat16)
 
     own_piece_slots = Zero1OneRank.own_piece_slots
 
     def reduce(self, incoming, stream=None):
         B.dp_reduce_scatter_mean(incoming, self.buckets, self.chunk, self.mean,
-                                 self.norm.partials, flags=GRZ_IN_COMPACT | GRZ_OUT_GLOBAL,
+                                 self.norm.partials,
+                                 flags=GRZ_IN_COMPACT | GRZ_OUT_GLOBAL | self.flags,
                                  stream=stream)
 
     def receive_means(self, peer_means, stream=None):
-        B.dp_all_gather(peer_means, self.buckets, [self.mean], stream=stream)
+        B.dp_all_gather(peer_means, self.buckets, [self.mean], flags=self.flags, stream=stream)
 
     def update(self, t, stream=None, args=None):
         self.norm.run(self.hyper.max_norm, stream)

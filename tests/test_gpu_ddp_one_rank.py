@@ -153,3 +153,41 @@ def test_ddp_one_rank_matches_the_oracle_and_the_all_ranks_replica():
                     for k in range(3):
                         assert_bits(host(one.state[k]), want["state"][k], f"state {k} vs oracle")
                     assert_bits(host(one.arena), want["arena"], "bf16 arena vs oracle")
+
+
+def test_ddp_one_rank_with_uneven_chunks():
+    # Plain data parallelism is what runs when bucket lengths do not divide by
+    # N: the chunks follow array_split, and each rank's step still equals the
+    # oracle's ddp_step and the all-ranks DDPStep replica.
+    n = 3
+    a, b = 3 * (4096 + 5) + 1, 3 * 4096 + 2
+    buckets = [(a, b), (0, a)]
+    p = a + b
+    master = master_init(p, device=DEV)
+    hyper = grz.Hyper(max_norm=0.5)
+    full = grz.DDPStep(buckets, n, master, hyper, device=DEV)
+    grads = [rank_grad(p, 1e-2, "bf16", grad_seed(9, r), device=DEV) for r in range(n)]
+    hg = [host(g) for g in grads]
+    full.step(grads, 1)
+    torch.cuda.synchronize()
+    w0 = host(master)
+    z = np.zeros_like(w0)
+    want = ddp_step(hg, "bf16", buckets, (w0, z, z), OHyper(max_norm=0.5), 1)
+    assert want["scale"] < 1
+    for r in range(n):
+        one = grz.DDPOneRank(buckets, n, r, master, hyper, DEV)
+        assert one.flags == grz.GRZ_UNEVEN
+        idx = _chunk_index(buckets, n, owned_chunk(r, n), uneven=True)
+        one.norm.partials.copy_(full.norm.partials)
+        peers = [None if j == r else
+                 _dev(reduce_scatter_mean(hg, "bf16", buckets, owned_chunk(j, n), uneven=True))
+                 for j in range(n)]
+        one.step([g.index_select(0, idx).contiguous() for g in grads], peers, 1)
+        torch.cuda.synchronize()
+        assert_bits(host(one.mean), want["mean"], f"rank {r} mean vs oracle")
+        assert_bits(host(one.mean), host(full.mean), f"rank {r} mean vs DDPStep")
+        for k in range(3):
+            assert_bits(host(one.state[k]), host(full.state[k]), f"rank {r} state {k}")
+            assert max_rel(host(one.state[k]), want["state"][k]) <= 1e-6
+        if np.float32(one.norm.scale.item()) == want["scale"]:
+            assert_bits(host(one.arena), want["arena"], f"rank {r} bf16 arena vs oracle")
