@@ -26,11 +26,13 @@ enqueues kernels and fills the per-step scalars; there is no host
 synchronisation inside a step.
 """
 
+import sys
+
 import torch
 
 from . import binding as B
 from ._native import GRZ_IN_COMPACT, GRZ_IN_RANGE, GRZ_OUT_GLOBAL, GRZ_PIECE, GRZ_UNEVEN
-from .plan import Hyper, owned_chunk, step_scalars
+from .plan import Hyper, owned_chunk, step_scalars, zero_stage
 
 
 def _shard_index(buckets, nranks, chunk, device):
@@ -289,6 +291,21 @@ class DDPOneRank:
         self.reduce(incoming, stream)
         self.receive_means(peer_means, stream)
         self.update(t, stream)
+
+
+def one_rank_step(buckets, nranks, rank, master, hyper=None, device="cuda", stage=1,
+                  log=None):
+    """The step rank ``rank`` runs over ``master`` (the whole fp32 arena): ZeRO-1
+    on its shard when ``stage`` is 1 and every bucket splits evenly over N,
+    otherwise plain data parallelism on the whole arena, saying so ("A4",
+    "Part 2 -- Tensor Sharding": an uneven split is an error for the sharding,
+    and the caller falls back to stage 0)."""
+    buckets = [(int(o), int(l)) for o, l in buckets]
+    if zero_stage(buckets, nranks, stage, sys.stderr if log is None else log) == 1:
+        idx = _shard_index(buckets, nranks, owned_chunk(rank, nranks), master.device)
+        return Zero1OneRank(buckets, nranks, rank, master.index_select(0, idx), hyper, device,
+                            arena_numel=master.numel())
+    return DDPOneRank(buckets, nranks, rank, master, hyper, device)
 
 
 class OverlappedZero1:

@@ -58,3 +58,24 @@ def test_resident_bytes_against_the_zero_table():
     longest = 25 * 2 ** 20 // 2
     assert resident_bytes(p, n, 2, longest_bucket=longest) == \
         zero_memory_bytes(p, n, 2) + 2 * p / n + 4 * longest
+
+
+def test_one_rank_step_falls_back_to_plain_data_parallelism(capsys):
+    # Built on the host (no kernel runs): an even plan gives the rank its ZeRO-1
+    # shard; a bucket N does not divide gives it the whole arena, with the
+    # fallback said on stderr.
+    import torch
+
+    import gradient_reduce_zero_amd as grz
+
+    master = torch.arange(8 * 40, dtype=torch.float32)
+    z = grz.one_rank_step([(0, 8 * 40)], 8, 3, master, device="cpu")
+    assert isinstance(z, grz.Zero1OneRank) and capsys.readouterr().err == ""
+    lo = grz.owned_chunk(3, 8) * 40
+    assert torch.equal(z.state[0], master[lo:lo + 40]) and z.arena.numel() == 320
+    d = grz.one_rank_step([(0, 8 * 40 - 3), (8 * 40 - 3, 3)], 8, 3, master, device="cpu")
+    assert isinstance(d, grz.DDPOneRank) and d.flags == grz.GRZ_UNEVEN
+    assert torch.equal(d.state[0], master)
+    assert "running ZeRO stage 0" in capsys.readouterr().err
+    s0 = grz.one_rank_step([(0, 8 * 40)], 8, 3, master, device="cpu", stage=0)
+    assert isinstance(s0, grz.DDPOneRank) and s0.flags == 0
