@@ -9,6 +9,7 @@ and copies bit-exact, norm within 1e-13, state and bf16 weights bit-exact when
 the clip factors agree.
 """
 
+import io
 import math
 
 import numpy as np
@@ -175,8 +176,10 @@ def test_ddp_one_rank_with_uneven_chunks():
     want = ddp_step(hg, "bf16", buckets, (w0, z, z), OHyper(max_norm=0.5), 1)
     assert want["scale"] < 1
     for r in range(n):
-        one = grz.DDPOneRank(buckets, n, r, master, hyper, DEV)
-        assert one.flags == grz.GRZ_UNEVEN
+        said = io.StringIO()
+        one = grz.one_rank_step(buckets, n, r, master, hyper, DEV, log=said)
+        assert isinstance(one, grz.DDPOneRank) and one.flags == grz.GRZ_UNEVEN
+        assert "stage 0" in said.getvalue()
         idx = _chunk_index(buckets, n, owned_chunk(r, n), uneven=True)
         one.norm.partials.copy_(full.norm.partials)
         peers = [None if j == r else
