@@ -892,6 +892,8 @@ def main():
     per = {nm: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps
            for i, nm in enumerate(names)}
     ms = total_ms / args.steps
+    per_step = sorted(ev[k][0].elapsed_time(ev[k][len(names)]) for k in range(args.steps))
+    median_ms = per_step[len(per_step) // 2]
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s); per kernel "
         + ", ".join(f"{k} {v:.3f} ms" for k, v in per.items()))
 
@@ -910,6 +912,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": median_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
