@@ -192,3 +192,50 @@ def test_missing_library_fails_loudly(tmp_path):
                          cwd=root, timeout=120)
     assert res.returncode == 0, res.stderr
     assert "raised:" in res.stdout and "no fallback" in res.stdout
+
+
+# Random plans: the library's host-side plan arithmetic against the oracle's
+# chunking (chunk_bounds, shard_segments) and the piece numbering of the norm
+# (pieces of GRZ_PIECE elements inside each chunk, numbered bucket by bucket,
+# chunk 0..N-1, piece by piece).
+from hypothesis import given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+
+@st.composite
+def _plans(draw):
+    n = draw(st.integers(1, 16))
+    even = draw(st.booleans())
+    lengths = draw(st.lists(st.integers(0, 3 * 4096 + 50), min_size=1, max_size=6))
+    if even:
+        lengths = [l - l % n for l in lengths]
+    order = draw(st.permutations(range(len(lengths))))
+    offs, pos = [0] * len(lengths), 0
+    for i in order:  # the arena layout differs from the processing order
+        offs[i] = pos
+        pos += lengths[i]
+    return n, even, list(zip(offs, lengths))
+
+
+@settings(max_examples=300, deadline=None)
+@given(_plans())
+def test_plan_helpers_match_the_oracle_on_random_plans(plan):
+    from oracle.reduce import shard_segments
+
+    n, even, buckets = plan
+    flags = 0 if even else N.GRZ_UNEVEN
+    piece = N.GRZ_PIECE
+    total = 0
+    for b, (_, length) in enumerate(buckets):
+        bounds = chunk_bounds(length, n)
+        for c, (lo, hi) in enumerate(bounds):
+            assert grz.dp_chunk_range(length, n, c) == (lo, hi - lo)
+            assert grz.dp_piece_offset(buckets, n, b, c, flags) == total
+            total += -(-(hi - lo) // piece)
+    assert grz.dp_piece_count(buckets, n, flags) == total
+    for c in range(n):
+        segs = shard_segments(buckets, n, c, uneven=not even)
+        assert grz.dp_shard_numel(buckets, n, c, flags) == sum(s[1] for s in segs)
+    if not even and any(l % n for _, l in buckets):
+        with pytest.raises(grz.GrzError):
+            grz.dp_shard_numel(buckets, n, 0, 0)
