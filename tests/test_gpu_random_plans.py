@@ -1,0 +1,97 @@
+"""The reduce on seeded random plans, against the oracle.
+
+Each case draws N (1..16), the gradient type, even or array_split chunks, a
+few buckets whose arena order differs from their processing order, a chunk to
+reduce and the output layout (shard-compact, arena offsets, or every chunk).
+The mean is compared bit for bit; each piece sum (GRZ_PIECE values of one
+chunk, numbered bucket by bucket, chunk 0..N-1, piece by piece) against the
+exact sum of the squares of the oracle's mean over the same elements.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gradient_reduce_zero_amd as grz
+from oracle.reduce import reduce_scatter_mean, shard_segments
+from oracle.ring import chunk_bounds
+from parity_util import assert_bits, host
+from workloads import rank_grad
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+PIECE = grz.GRZ_PIECE
+
+
+def _draw(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 17))
+    kind = ["bf16", "f32", "f64"][int(rng.integers(0, 3))]
+    even = bool(rng.integers(0, 2))
+    lengths = [int(x) for x in rng.integers(0, 3 * PIECE + 60, size=int(rng.integers(1, 5)))]
+    if even:
+        lengths = [l - l % n for l in lengths]
+    if sum(lengths) == 0:
+        lengths[0] = 8 * n
+    order = rng.permutation(len(lengths))
+    offs, pos = [0] * len(lengths), 0
+    for i in order:
+        offs[i] = pos
+        pos += lengths[i]
+    mode = ["compact", "global", "all"][int(rng.integers(0, 3))]
+    chunk = -1 if mode == "all" else int(rng.integers(0, n))
+    return n, kind, even, list(zip(offs, lengths)), pos, chunk, mode
+
+
+def _pieces_of(mean_global, buckets, n, chunks):
+    """Exact sum of squares per piece, in the plan's piece numbering; None for
+    pieces of chunks not reduced."""
+    out = []
+    for off, length in buckets:
+        for c, (lo, hi) in enumerate(chunk_bounds(length, n)):
+            for p0 in range(lo, hi, PIECE):
+                p1 = min(p0 + PIECE, hi)
+                if c in chunks:
+                    vals = mean_global[off + p0:off + p1].astype(np.float64)
+                    out.append(math.fsum((vals * vals).tolist()))
+                else:
+                    out.append(None)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_reduce_on_a_random_plan(seed):
+    n, kind, even, buckets, p, chunk, mode = _draw(1000 + seed)
+    flags = 0 if even else grz.GRZ_UNEVEN
+    if mode == "global":
+        flags |= grz.GRZ_OUT_GLOBAL
+    grads = [rank_grad(p, 1e-2, kind, 7000 + 31 * seed + r, device=DEV) for r in range(n)]
+    acc = np.float64 if kind == "f64" else np.float32
+    out_t = torch.float64 if kind == "f64" else torch.float32
+    npieces = grz.dp_piece_count(buckets, n, flags)
+    parts = torch.full((max(npieces, 1),), -1.0, dtype=torch.float64, device=DEV)
+    shard = grz.dp_shard_numel(buckets, n, chunk, flags) if chunk >= 0 else p
+    out = torch.full((max(shard if mode == "compact" else p, 1),), float("nan"), dtype=out_t,
+                     device=DEV)
+    grz.dp_reduce_scatter_mean(grads, buckets, chunk, out, parts, flags=flags)
+    torch.cuda.synchronize()
+    hg = [host(g) for g in grads]
+    mean_global = np.full(p, np.nan, acc)
+    chunks = range(n) if chunk < 0 else [chunk]
+    for c in chunks:
+        comp = reduce_scatter_mean(hg, kind, buckets, c, uneven=not even)
+        for g0, length, c0 in shard_segments(buckets, n, c, uneven=not even):
+            mean_global[g0:g0 + length] = comp[c0:c0 + length]
+    if mode == "compact":
+        want = reduce_scatter_mean(hg, kind, buckets, chunk, uneven=not even)
+        assert_bits(host(out)[:shard], want, f"seed {seed}: shard-compact mean")
+    else:
+        assert_bits(host(out)[:p], mean_global, f"seed {seed}: mean at arena offsets")
+    got = host(parts)
+    for i, want_i in enumerate(_pieces_of(mean_global, buckets, n, set(chunks))):
+        if want_i is None:
+            assert got[i] == -1.0, f"seed {seed}: piece {i} of a chunk not reduced was written"
+        else:
+            assert math.isclose(got[i], want_i, rel_tol=1e-13, abs_tol=0.0), (seed, i)
