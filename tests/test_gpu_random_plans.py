@@ -95,3 +95,55 @@ def test_reduce_on_a_random_plan(seed):
             assert got[i] == -1.0, f"seed {seed}: piece {i} of a chunk not reduced was written"
         else:
             assert math.isclose(got[i], want_i, rel_tol=1e-13, abs_tol=0.0), (seed, i)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_update_on_a_random_plan(seed):
+    # Clipped AdamW on the shard of a random chunk (or the whole plan) with the
+    # bf16 write into 1-3 replicas: state bit-exact against the oracle's AdamW
+    # on the same inputs, the replicas equal to the oracle's rounding at the
+    # shard's arena offsets and untouched elsewhere.
+    from oracle.bf16 import bf16_round
+    from oracle.step import Hyper as OHyper
+    from oracle.step import adamw
+
+    rng = np.random.default_rng(5000 + seed)
+    n, _, even, buckets, p, chunk, _ = _draw(2000 + seed)
+    if rng.integers(0, 4) == 0:
+        chunk = -1
+    flags = 0 if even else grz.GRZ_UNEVEN
+    t = int(rng.integers(1, 4))
+    warmup = int(rng.integers(0, 3))
+    scale = np.float32(rng.uniform(0.05, 1.0)) if rng.integers(0, 2) else np.float32(1.0)
+    nrep = int(rng.integers(1, 4))
+    if chunk >= 0:
+        segs = shard_segments(buckets, n, chunk, uneven=not even)
+        numel = sum(s[1] for s in segs)
+    else:
+        segs = [(off, length, off) for off, length in buckets]
+        numel = p
+    w = rng.standard_normal(numel).astype(np.float32) * np.float32(0.02)
+    m = rng.standard_normal(numel).astype(np.float32) * np.float32(1e-3)
+    v = np.abs(rng.standard_normal(numel)).astype(np.float32) * np.float32(1e-6)
+    g = rng.standard_normal(numel).astype(np.float32) * np.float32(1e-2)
+    hyper = grz.Hyper(lr=1e-3, warmup=warmup)
+    dev = [torch.from_numpy(a.copy()).to(DEV) for a in (w, m, v, g)]
+    if numel == 0:
+        dev = [torch.zeros(1, device=DEV) for _ in range(4)]
+    sentinel = 0x7A5C  # a bf16 bit pattern no update writes here
+    reps = [torch.full((p,), sentinel, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+            for _ in range(nrep)]
+    grz.zero1_adamw_gather(dev[0], dev[1], dev[2], dev[3], buckets, n, chunk,
+                           torch.tensor([scale], device=DEV),
+                           grz.adamw_args(**grz.step_scalars(hyper, t)), reps, flags=flags)
+    torch.cuda.synchronize()
+    s = OHyper(lr=1e-3, warmup=warmup).scalars(t)
+    w1, m1, v1 = adamw(w, m, v, g * scale, **s)
+    for k, want in enumerate((w1, m1, v1)):
+        assert_bits(host(dev[k])[:numel], want, f"seed {seed}: state {k}")
+    want_rep = np.full(p, sentinel, np.uint16)
+    b = bf16_round(w1)
+    for g0, length, c0 in segs:
+        want_rep[g0:g0 + length] = b[c0:c0 + length]
+    for r in reps:
+        assert_bits(host(r), want_rep, f"seed {seed}: replica")
