@@ -180,6 +180,85 @@ def test_llama_7b_one_rank_share_sampled():
     assert torch.equal(pipe.state[2], omb2 * (g * g))
 
 
+def test_llama_7b_ddp_one_rank_sampled():
+    # One rank of plain data parallelism at 7B: its full fp32 state holds
+    # 6.74e9 elements (beyond 2^32), its own chunk is reduced at arena offsets
+    # and the peers' fp32 mean chunks land around it.
+    a = arena("llama_7b")
+    p, n, rank = a.numel, 8, 0
+    buckets = grz.whole_arena(p)
+    chunk = owned_chunk(rank, n)
+    shard = p // n
+    npieces = grz.dp_piece_count(buckets, n)
+    inp = onerank_inputs(shard, n, rank, npieces, grz.GRZ_PIECE, device=DEV)
+    incoming, partials = inp["incoming"], inp["partials"]
+    del inp
+    master = master_init(p, device=DEV)
+    idx = sample_indices(p, 200_000, 13, extra=[shard - 1, shard, 2 * shard - 1, 2 * shard,
+                                                (1 << 32) - 1, 1 << 32, (1 << 32) + 1, p - 1])
+    w0 = gather_host(master, idx)
+    one = grz.DDPOneRank(buckets, n, rank, master, device=DEV)
+    del master
+    one.norm.partials.copy_(partials)
+    peer_means = [None if j == rank else
+                  rank_grad(shard, 1e-3 / n ** 0.5, "f32", grad_seed(1, 100 + j), device=DEV)
+                  for j in range(n)]
+    peers = host(partials)
+    own = one.own_piece_slots()
+    one.step(incoming, peer_means, 1)
+    torch.cuda.synchronize()
+
+    # The mean: the own chunk bit-exact against the oracle's fold, every peer
+    # chunk byte for byte what that peer delivered (all of it, chunk by chunk).
+    lo = chunk * shard
+    mine = (idx >= lo) & (idx < lo + shard)
+    want_own = oracle_mean_at([gather_host(g, idx[mine] - lo) for g in incoming],
+                              np.full(int(mine.sum()), chunk), "bf16")
+    assert_bits(gather_host(one.mean, idx[mine]), want_own, "7B DDP own chunk (sampled)")
+    for j in range(n):
+        if j != rank:
+            c = owned_chunk(j, n)
+            assert torch.equal(one.mean[c * shard:(c + 1) * shard], peer_means[j]), j
+    # Norm: the own pieces recomputed from the inputs, the peers' as received.
+    mask = np.ones(npieces, bool)
+    for first, cnt in own:
+        mask[first:first + cnt] = False
+    sq = _tiled_sqnorm(incoming, chunk, "bf16", shard) + float(np.sum(peers[mask]))
+    assert math.isclose(one.norm.sqnorm.item(), sq, rel_tol=1e-10)
+    scale = clip_scale(sq, 1.0)
+    got_scale = np.float32(one.norm.scale.item())
+    assert abs(float(got_scale) - float(scale)) <= float(np.spacing(scale))
+    # AdamW over the whole arena, sampled, on the oracle's mean of each element.
+    g_at = np.empty(idx.size, np.float32)
+    g_at[mine] = want_own
+    for j in range(n):  # the peers' chunks: the values they delivered
+        c = owned_chunk(j, n)
+        sel = (idx >= c * shard) & (idx < (c + 1) * shard)
+        if j != rank:
+            g_at[sel] = gather_host(peer_means[j], idx[sel] - c * shard)
+    z = np.zeros_like(w0)
+    w1, m1, v1 = adamw(w0, z, z, g_at * scale, **OHyper().scalars(1))
+    for k, want in enumerate((w1, m1, v1)):
+        got = gather_host(one.state[k], idx)
+        assert max_rel(got, want) <= 1e-6
+        if got_scale == scale:
+            assert_bits(got, want, f"7B DDP state {k} (sampled)")
+    if got_scale == scale:
+        assert_bits(gather_host(one.arena, idx), bf16_round(w1), "7B DDP arena (sampled)")
+    # Every element, one chunk at a time: the arena is the master rounded to
+    # bf16 and the step-1 moments are (1 - b1) * g' and (1 - b2) * (g' * g').
+    h = OHyper()
+    f32 = dict(dtype=torch.float32, device=DEV)
+    omb1 = torch.tensor(np.float32(1) - np.float32(h.beta1), **f32)
+    omb2 = torch.tensor(np.float32(1) - np.float32(h.beta2), **f32)
+    for c in range(n):
+        sl = slice(c * shard, (c + 1) * shard)
+        assert torch.equal(one.arena[sl], one.state[0][sl].to(torch.bfloat16)), c
+        g = one.mean[sl] * one.norm.scale
+        assert torch.equal(one.state[1][sl], omb1 * g), c
+        assert torch.equal(one.state[2][sl], omb2 * (g * g)), c
+
+
 def test_gpt2_1p5b_all_ranks_sampled():
     a = arena("gpt2_1p5b")
     p, n = a.numel, 4
