@@ -2,8 +2,9 @@
 // pipeline for AMD Instinct MI355X (gfx950, CDNA4, wave64).
 //
 // Kernels (all HBM-bandwidth bound; nothing here is a contraction, so no MFMA;
-// one 256-thread workgroup per tile, lane-contiguous 8/16-byte accesses,
-// non-temporal hints, tile sizes and occupancy caps chosen by measurement):
+// one workgroup per tile -- 256 threads for the reduce, one wave for the
+// optimizer and the copy -- lane-contiguous 8/16-byte accesses, non-temporal
+// hints, workgroup and tile sizes and occupancy caps chosen by measurement):
 //   rs_mean_kernel   ring-order N-way fold of 64/128-bit loads, fp32 (fp64)
 //                    mean, fp64 sum of squares per GRZ_PIECE-element piece
 //   sqnorm_level_kernel / sqnorm_final_kernel
@@ -12,7 +13,8 @@
 //                    the piece sums of an already reduced fp32 array
 //   adamw_kernel     clip + AdamW on fp32 master/m/v, bf16 round-to-nearest-
 //                    even written to any number of replica arenas
-//   gather_kernel    bf16 shard copies into replica arenas (all-gather)
+//   gather_kernel    shard copies into replica arenas (all-gather), in
+//                    16-bit words: bf16 elements, or fp32 / fp64 ones as 2 / 4
 //   fused_step_kernel
 //                    the reduce, the norm and clip + AdamW of one shard in one
 //                    cooperative launch, the mean held in registers
