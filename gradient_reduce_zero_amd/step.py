@@ -1,6 +1,6 @@
 """One training step of the gradient pipeline, driven through the C ABI.
 
-Three views of the same step, all on one GPU with the ranks simulated as
+Views of the same step, all on one GPU with the ranks simulated as
 resident buffers ("Distributed training" (noeira), "The process group": the
 simulator runs every rank on one device with the collectives as local
 kernels):
@@ -15,6 +15,10 @@ kernels):
   N incoming chunks of its shard, combine its norm pieces with the peers'
   (received), AdamW on its shard, then assemble its full bf16 arena from its
   own shard and the peers' received shards.
+* ``DDPOneRank``    -- a single GPU of an N-GPU plain data-parallel job: the
+  all-reduce of the mean as reduce-scatter (its chunk, at arena offsets) plus
+  all-gather (the peers' mean chunks), then AdamW over its whole copy.
+  ``one_rank_step`` picks this or ``Zero1OneRank`` from the plan.
 
 ``Zero1OneRank`` and ``DDPStep`` take ``fused=True`` to run reduce, norm,
 clip and AdamW as one launch (``zero1_fused_step``) when the shard fits.
