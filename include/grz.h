@@ -87,7 +87,12 @@ enum {
 /* Gradient element types. */
 enum { GRZ_F32 = 0, GRZ_BF16 = 1, GRZ_F64 = 2 };
 
-/* Flags of dp_reduce_scatter_mean / zero1_adamw_step / zero1_all_gather. */
+/* Flags.  An entry point returns GRZ_EINVAL for a flag it does not take:
+ * the reduce (dp_reduce_scatter_mean and its _range form) takes all but
+ * GRZ_ARGS_DEVICE, the _weighted form all but that and GRZ_SUM;
+ * zero1_adamw_gather takes GRZ_UNEVEN and GRZ_ARGS_DEVICE; the all-gathers
+ * take GRZ_UNEVEN; zero1_fused_step GRZ_UNEVEN, GRZ_IN_COMPACT and
+ * GRZ_ARGS_DEVICE.  Their meaning is in each entry point's comment. */
 enum {
   GRZ_SUM = 1,        /* keep the sum: skip the division by N            */
   GRZ_UNEVEN = 2,     /* allow bucket lengths not divisible by N         */
