@@ -627,6 +627,20 @@ def ddp_bench(args, dev):
            "pct_of_peak_hbm": 100.0 * step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
            "step_bytes_without_simulated_reads": step_bytes - simulated,
            "phases_ms": phase, "phases_GBps": gbps}
+    if args.graph:
+        cap = grz.CapturedStep(lambda a_, s_: one.enqueue(incoming, peer_means, a_, s_),
+                               one.hyper, t, args.warmup + args.steps)
+        for _ in range(args.warmup):
+            cap.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(s)
+        for _ in range(args.steps):
+            cap.replay()
+        g1.record(s)
+        torch.cuda.synchronize()
+        out["graph_ms_per_step"] = g0.elapsed_time(g1) / args.steps
+        log(f"graph replay: {out['graph_ms_per_step']:.3f} ms/step")
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_ddp(incoming, n, hyper, min(args.cpu_sample, 1 << 27))
     print(json.dumps(out), flush=True)

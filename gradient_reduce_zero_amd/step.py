@@ -296,6 +296,12 @@ class DDPOneRank:
         self.receive_means(peer_means, stream)
         self.update(t, stream)
 
+    def enqueue(self, incoming, peer_means, args, stream=None):
+        """The step's kernels; ``args`` host ``AdamWArgs`` or a device tensor."""
+        self.reduce(incoming, stream)
+        self.receive_means(peer_means, stream)
+        self.update(None, stream, args=args)
+
 
 def one_rank_step(buckets, nranks, rank, master, hyper=None, device="cuda", stage=1,
                   log=None):

@@ -194,3 +194,43 @@ def test_ddp_one_rank_with_uneven_chunks():
             assert max_rel(host(one.state[k]), want["state"][k]) <= 1e-6
         if np.float32(one.norm.scale.item()) == want["scale"]:
             assert_bits(host(one.arena), want["arena"], f"rank {r} bf16 arena vs oracle")
+
+
+def test_captured_ddp_one_rank_replays_match_eager():
+    # Graph replays of one rank's plain data-parallel step, with eager work and
+    # host synchronisations in between, each equal to the eager step of the
+    # same number (past the scalar table's end, its last row).
+    n, rank = 8, 3
+    p = 8 * (2 * 4096 + 72)
+    buckets = [(8 * 4096, p - 8 * 4096), (0, 8 * 4096)]
+    master = master_init(p, device=DEV)
+    hyper = grz.Hyper(lr=1e-3, warmup=2, max_norm=0.05)
+    c = owned_chunk(rank, n)
+    idx = _chunk_index(buckets, n, c)
+    grads = [rank_grad(p, 1e-2, "bf16", grad_seed(3, r), device=DEV) for r in range(n)]
+    incoming = [g.index_select(0, idx).contiguous() for g in grads]
+    hg = [host(g) for g in grads]
+    peers = [None if j == rank else
+             _dev(reduce_scatter_mean(hg, "bf16", buckets, owned_chunk(j, n)))
+             for j in range(n)]
+    full = grz.DDPStep(buckets, n, master, hyper, device=DEV)
+    full.step(grads, 1)
+    eager = grz.DDPOneRank(buckets, n, rank, master, hyper, DEV)
+    graphed = grz.DDPOneRank(buckets, n, rank, master, hyper, DEV)
+    for d in (eager, graphed):
+        d.norm.partials.copy_(full.norm.partials)
+    cap = grz.CapturedStep(lambda args, s: graphed.enqueue(incoming, peers, args, s), hyper, 1,
+                           4)
+    junk = torch.randn(1 << 20, device=DEV)
+    for t in range(1, 7):
+        eager.step(incoming, peers, min(t, 4))
+        cap.replay()
+        junk.mul_(0.5).add_(1.0)
+        torch.cuda.synchronize()
+        for a, b, what in ((eager.mean, graphed.mean, "mean"),
+                           (eager.state[0], graphed.state[0], "master"),
+                           (eager.state[2], graphed.state[2], "v"),
+                           (eager.arena, graphed.arena, "arena"),
+                           (eager.norm.scale, graphed.norm.scale, "scale")):
+            assert_bits(host(b), host(a), f"replay {t}: {what}")
+    assert int(cap.counter.item()) == 6
