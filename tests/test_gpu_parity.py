@@ -449,6 +449,48 @@ def test_overlapped_step_equals_plain_step():
         assert_bits(host(ov.pipe.replicas[1]), host(plain.replicas[1]), "overlapped replica")
 
 
+def test_dropped_wait_reads_gradients_not_yet_written():
+    # "A4", "Common Mistakes": without the event wait the reduction can start
+    # before the backward has written the gradients.  The compute stream runs
+    # milliseconds of GEMMs before it writes them; the ordered step reduces
+    # the written values, the one with the wait dropped reduces what was there
+    # before (zeros).  Were the two streams ever run one after the other on a
+    # device, the race could not show: then that half is skipped, not failed.
+    n, p = 2, 2 * 4096 * 16
+    buckets = [(0, p)]
+    src = [rank_grad(p, 1e-2, "bf16", grad_seed(4, r), device=DEV) for r in range(n)]
+    want = reduce_scatter_mean([host(s) for s in src], "bf16", buckets, owned_chunk(0, n))
+    master = master_init(p, device=DEV)
+    x = torch.randn(4096, 4096, device=DEV) / 64
+
+    class NoWait(grz.OverlappedZero1):
+        def bucket_ready(self, b, rank_grads, compute_stream=None):
+            q = self.pipe
+            for c, mean in zip(q.chunks, q.means):  # no record, no wait
+                grz.dp_reduce_scatter_mean(rank_grads, q.buckets, c, mean, q.norm.partials,
+                                           stream=self.comm, bucket_range=(b, 1))
+
+    def run(cls):
+        ov = cls(grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=0.0), device=DEV))
+        grads = [torch.zeros_like(s) for s in src]
+        torch.cuda.synchronize()
+        y = x
+        for _ in range(8):  # the backward's compute ahead of the write
+            y = y @ x
+        for g, s in zip(grads, src):
+            g.copy_(s)
+        ov.bucket_ready(0, grads)
+        ov.finish(1)
+        torch.cuda.synchronize()
+        return host(ov.pipe.means[0])
+
+    assert_bits(run(grz.OverlappedZero1), want, "with the wait: the written gradients")
+    raced = run(NoWait)
+    if np.array_equal(raced.view(np.uint32), want.view(np.uint32)):
+        pytest.skip("the streams ran in order here: the dropped wait could not show")
+    assert np.count_nonzero(raced.view(np.uint32) != want.view(np.uint32)) > 0
+
+
 def test_zero2_staged_step_equals_zero1_step():
     a = arena("gpt2_124m")
     p, n = a.numel, 8
