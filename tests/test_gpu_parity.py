@@ -248,6 +248,38 @@ def test_nan_in_one_rank_propagates_like_the_oracle():
     assert_bits(got[~nan], want[~nan], "replica with a NaN")
 
 
+@pytest.mark.parametrize("other", [None, "-inf"])
+def test_infinite_gradient_clips_like_the_oracle(other):
+    # +inf in one rank: the norm is infinite, the clip factor max_norm / inf is
+    # 0, finite elements take a zero gradient and the inf element turns NaN.
+    # With -inf at the same element of the other rank, the mean itself is NaN
+    # and so is the norm: the factor is then 1 (reading 7), as in the oracle.
+    p, n = 4096, 2
+    grads = [rank_grad(p, 0.01, "f32", grad_seed(2, r), device=DEV) for r in range(n)]
+    grads[1][100] = float("inf")
+    if other is not None:
+        grads[0][100] = float(other)
+    master = master_init(p, device=DEV)
+    z = grz.Zero1AllRanks([(0, p)], n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    z.step(grads, 1)
+    torch.cuda.synchronize()
+    ref = zero1_step([host(g) for g in grads], "f32", [(0, p)],
+                     oracle_states(host(master), [(0, p)], n), OHyper(max_norm=1.0), 1)
+    sq = z.norm.sqnorm.item()
+    assert (math.isinf(sq) and math.isinf(ref["sqnorm"])) if other is None else (
+        math.isnan(sq) and math.isnan(ref["sqnorm"]))
+    assert_bits(host(z.norm.scale), np.array([ref["scale"]], np.float32), "scale")
+    assert float(ref["scale"]) == (0.0 if other is None else 1.0)
+    for r in range(n):
+        assert_bits(host(z.means[r]), ref["means"][r], "mean with an infinity")
+        for k in range(3):
+            assert_bits(host(z.state[r][k]), ref["states"][r][k], f"state {k} with an infinity")
+    got, want = host(z.replicas[0]), ref["arena"]
+    nan = ((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0)
+    assert nan.sum() == 1 and ((got[nan] & 0x7F80) == 0x7F80).all() and (got[nan] & 0x7F).all()
+    assert_bits(got[~nan], want[~nan], "replica with an infinity")
+
+
 # --- the unfused optimizer and the standalone all-gather ----------------------
 
 def test_unfused_adamw_and_all_gather_match_fused_and_oracle():
