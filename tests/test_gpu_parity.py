@@ -280,6 +280,42 @@ def test_infinite_gradient_clips_like_the_oracle(other):
     assert_bits(got[~nan], want[~nan], "replica with an infinity")
 
 
+@pytest.mark.parametrize("case", ["subnormal", "zero"])
+def test_subnormal_and_zero_gradients_match_the_oracle(case):
+    # Subnormal bf16 gradients (k * 2^-133, |k| < 128, beside a few normal
+    # values) must be summed and divided without flushing to zero; all-zero
+    # gradients give a zero norm, factor 1 and a pure weight-decay update.
+    p, n = 4096 * 2 + 36, 4
+    rng = np.random.default_rng(17)
+    grads = []
+    for r in range(n):
+        if case == "zero":
+            x = np.zeros(p, np.float32)
+        else:
+            x = (rng.integers(-127, 128, size=p) * 2.0 ** -133).astype(np.float32)
+            x[::97] = rng.standard_normal(x[::97].size).astype(np.float32) * np.float32(1e-30)
+        grads.append(torch.from_numpy(x).to(DEV).to(torch.bfloat16))
+    hg = [host(g) for g in grads]
+    master = master_init(p, device=DEV)
+    z = grz.Zero1AllRanks([(0, p)], n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    z.step(grads, 1)
+    torch.cuda.synchronize()
+    ref = zero1_step(hg, "bf16", [(0, p)], oracle_states(host(master), [(0, p)], n),
+                     OHyper(max_norm=1.0), 1)
+    if case == "subnormal":
+        assert any(np.count_nonzero((m != 0) & (np.abs(m) < np.finfo(np.float32).tiny))
+                   for m in ref["means"]), "the case must hold subnormal means"
+    else:
+        assert ref["sqnorm"] == 0.0 and z.norm.sqnorm.item() == 0.0
+    assert math.isclose(z.norm.sqnorm.item(), ref["sqnorm"], rel_tol=1e-13, abs_tol=0.0)
+    assert_bits(host(z.norm.scale), np.array([ref["scale"]], np.float32), "scale")
+    for r in range(n):
+        assert_bits(host(z.means[r]), ref["means"][r], f"{case} mean rank {r}")
+        for k in range(3):
+            assert_bits(host(z.state[r][k]), ref["states"][r][k], f"{case} state {k} rank {r}")
+    assert_bits(host(z.replicas[2]), ref["arena"], f"{case} replica")
+
+
 # --- the unfused optimizer and the standalone all-gather ----------------------
 
 def test_unfused_adamw_and_all_gather_match_fused_and_oracle():
