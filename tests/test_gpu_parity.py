@@ -248,17 +248,21 @@ def test_nan_in_one_rank_propagates_like_the_oracle():
     assert_bits(got[~nan], want[~nan], "replica with a NaN")
 
 
-@pytest.mark.parametrize("other", [None, "-inf"])
+@pytest.mark.parametrize("other", [None, "-inf", "overflow"])
 def test_infinite_gradient_clips_like_the_oracle(other):
     # +inf in one rank: the norm is infinite, the clip factor max_norm / inf is
     # 0, finite elements take a zero gradient and the inf element turns NaN.
     # With -inf at the same element of the other rank, the mean itself is NaN
     # and so is the norm: the factor is then 1 (reading 7), as in the oracle.
+    # "overflow": finite 3e38 in both ranks, whose fp32 sum overflows to inf.
     p, n = 4096, 2
     grads = [rank_grad(p, 0.01, "f32", grad_seed(2, r), device=DEV) for r in range(n)]
-    grads[1][100] = float("inf")
-    if other is not None:
-        grads[0][100] = float(other)
+    if other == "overflow":
+        grads[0][100] = grads[1][100] = 3e38
+    else:
+        grads[1][100] = float("inf")
+        if other is not None:
+            grads[0][100] = float(other)
     master = master_init(p, device=DEV)
     z = grz.Zero1AllRanks([(0, p)], n, master, grz.Hyper(max_norm=1.0), device=DEV)
     z.step(grads, 1)
@@ -266,10 +270,10 @@ def test_infinite_gradient_clips_like_the_oracle(other):
     ref = zero1_step([host(g) for g in grads], "f32", [(0, p)],
                      oracle_states(host(master), [(0, p)], n), OHyper(max_norm=1.0), 1)
     sq = z.norm.sqnorm.item()
-    assert (math.isinf(sq) and math.isinf(ref["sqnorm"])) if other is None else (
-        math.isnan(sq) and math.isnan(ref["sqnorm"]))
+    assert (math.isnan(sq) and math.isnan(ref["sqnorm"])) if other == "-inf" else (
+        math.isinf(sq) and math.isinf(ref["sqnorm"]))
     assert_bits(host(z.norm.scale), np.array([ref["scale"]], np.float32), "scale")
-    assert float(ref["scale"]) == (0.0 if other is None else 1.0)
+    assert float(ref["scale"]) == (1.0 if other == "-inf" else 0.0)
     for r in range(n):
         assert_bits(host(z.means[r]), ref["means"][r], "mean with an infinity")
         for k in range(3):
