@@ -13,8 +13,10 @@ parameters.  One step:
   AG zero1_all_gather        the 7 received peer bf16 shards into the arena
 
 Everything is resident in HBM before timing starts; every input is seeded
-and synthetic.  Prints one JSON line.  ``--gpus`` above 1 is refused: this
-build runs on one GPU (the ranks are simulated as resident buffers).
+and synthetic.  Prints one JSON line.  ``--gpus`` above 1 is refused: the
+pipeline runs on one GPU (the ranks are simulated as resident buffers).
+Other modes (``--all-ranks``, ``--ddp``, ``--overlap``, ``--zero2``, ``--fused``,
+``--graph``, ``--cold``, ``--torch-ref``) are described in their --help lines.
 """
 
 import argparse
