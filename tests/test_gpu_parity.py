@@ -253,7 +253,8 @@ def test_infinite_gradient_clips_like_the_oracle(other):
     # +inf in one rank: the norm is infinite, the clip factor max_norm / inf is
     # 0, finite elements take a zero gradient and the inf element turns NaN.
     # With -inf at the same element of the other rank, the mean itself is NaN
-    # and so is the norm: the factor is then 1 (reading 7), as in the oracle.
+    # and so is the norm: the factor is then 1 (a NaN norm fails the test
+    # norm > max_norm), as in the oracle.
     # "overflow": finite 3e38 in both ranks, whose fp32 sum overflows to inf.
     p, n = 4096, 2
     grads = [rank_grad(p, 0.01, "f32", grad_seed(2, r), device=DEV) for r in range(n)]
