@@ -486,12 +486,13 @@ __device__ __forceinline__ float clip_factor(double sqnorm, double max_norm) {
 }
 
 __global__ __launch_bounds__(kThreads) void sqnorm_level_kernel(const double* __restrict__ x,
-                                                                int64_t n,
+                                                                int64_t n, int64_t nblocks,
                                                                 double* __restrict__ y) {
   __shared__ double lds[kThreads / 64];
-  const double tot =
-      fan_block_sum(x, n, static_cast<int64_t>(blockIdx.x) * kReduceFan, lds);
-  if (threadIdx.x == 0) y[blockIdx.x] = tot;
+  for (int64_t j = blockIdx.x; j < nblocks; j += gridDim.x) {
+    const double tot = fan_block_sum(x, n, j * kReduceFan, lds);
+    if (threadIdx.x == 0) y[j] = tot;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void sqnorm_final_kernel(const double* __restrict__ x,
@@ -511,33 +512,36 @@ __global__ __launch_bounds__(kThreads) void sqnorm_final_kernel(const double* __
 // kernel's (access k of lane l: the 4 elements at k*1024 + 4*l, squares
 // accumulated in fp64 with one rounding each, then block_sum_fixed).
 __global__ __launch_bounds__(kThreads) void piece_sqnorm_kernel(const float* __restrict__ g,
-                                                                int64_t n, int vec,
+                                                                int64_t n, int64_t npieces,
+                                                                int vec,
                                                                 double* __restrict__ partials) {
   constexpr int G = 4;
   constexpr int K = GRZ_PIECE / (kThreads * G);
   __shared__ double lds[kThreads / 64];
-  const int64_t e0 = static_cast<int64_t>(blockIdx.x) * GRZ_PIECE;
-  const int64_t left = n - e0;
-  double sq = 0.0;
+  for (int64_t piece = blockIdx.x; piece < npieces; piece += gridDim.x) {
+    const int64_t e0 = piece * GRZ_PIECE;
+    const int64_t left = n - e0;
+    double sq = 0.0;
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int64_t rel = static_cast<int64_t>(k * kThreads + threadIdx.x) * G;
-    if (vec && rel + G <= left) {
-      float x[G];
-      loadg<kNtLoad>(g + e0 + rel, x);
+    for (int k = 0; k < K; ++k) {
+      const int64_t rel = static_cast<int64_t>(k * kThreads + threadIdx.x) * G;
+      if (vec && rel + G <= left) {
+        float x[G];
+        loadg<kNtLoad>(g + e0 + rel, x);
 #pragma unroll
-      for (int i = 0; i < G; ++i)
-        sq = __fma_rn(static_cast<double>(x[i]), static_cast<double>(x[i]), sq);
-    } else {
-      for (int i = 0; i < G; ++i) {
-        if (rel + i >= left) break;
-        const double x = g[e0 + rel + i];
-        sq = __fma_rn(x, x, sq);
+        for (int i = 0; i < G; ++i)
+          sq = __fma_rn(static_cast<double>(x[i]), static_cast<double>(x[i]), sq);
+      } else {
+        for (int i = 0; i < G; ++i) {
+          if (rel + i >= left) break;
+          const double x = g[e0 + rel + i];
+          sq = __fma_rn(x, x, sq);
+        }
       }
     }
+    const double tot = block_sum_fixed(sq, lds);
+    if (threadIdx.x == 0) partials[piece] = tot;
   }
-  const double tot = block_sum_fixed(sq, lds);
-  if (threadIdx.x == 0) partials[blockIdx.x] = tot;
 }
 
 // ---------------------------------------------------------------------------
@@ -1021,6 +1025,17 @@ std::vector<PlanSeg> plan_segments(const grz_bucket* buckets, int nbuckets, int 
   return out;
 }
 
+// Workgroups of a grid-stride launch over `units` tiles: at most the knob and
+// at most what a dispatch can express (its grid counts work-items in 32
+// bits).  Every such kernel loops over its tiles, so any width gives the same
+// results.
+int64_t grid_for(int64_t units, int block) {
+  const int64_t cap = g_max_blocks.load(std::memory_order_relaxed);
+  const int64_t hw = static_cast<int64_t>(UINT32_MAX) / block;
+  int64_t grid = units < cap ? units : cap;
+  return grid < hw ? grid : hw;
+}
+
 template <typename Args>
 int launch_batches(std::vector<Seg>& segs, Args& args,
                    void (*kernel)(const Args), hipStream_t stream,
@@ -1038,8 +1053,7 @@ int launch_batches(std::vector<Seg>& segs, Args& args,
     if (tiles == 0) continue;
     args.nsegs = static_cast<int>(cnt);
     args.ntiles = tiles;
-    const int64_t cap = g_max_blocks.load(std::memory_order_relaxed);
-    const int64_t grid = tiles < cap ? tiles : cap;
+    const int64_t grid = grid_for(tiles, block);
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(block), 0, stream,
                        args);
     if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
@@ -1361,8 +1375,9 @@ int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
   int64_t n = npieces;
   double* ws = static_cast<double*>(workspace);
   for (int i = 0; i < levels; ++i) {
-    hipLaunchKernelGGL(sqnorm_level_kernel, dim3(static_cast<unsigned>(sizes[i])),
-                       dim3(kThreads), 0, stream, in, n, ws);
+    const unsigned grid = static_cast<unsigned>(grid_for(sizes[i], kThreads));
+    hipLaunchKernelGGL(sqnorm_level_kernel, dim3(grid), dim3(kThreads), 0, stream, in, n,
+                       sizes[i], ws);
     if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
     in = ws;
     n = sizes[i];
@@ -1390,8 +1405,9 @@ int dp_grad_sqnorm_of(const float* grad, int64_t n, double max_norm, void* works
   double* partials = static_cast<double*>(workspace);
   if (npieces > 0) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL(piece_sqnorm_kernel, dim3(static_cast<unsigned>(npieces)),
-                       dim3(kThreads), 0, stream, grad, n, aligned(grad, 16) ? 1 : 0, partials);
+    const unsigned grid = static_cast<unsigned>(grid_for(npieces, kThreads));
+    hipLaunchKernelGGL(piece_sqnorm_kernel, dim3(grid), dim3(kThreads), 0, stream, grad, n,
+                       npieces, aligned(grad, 16) ? 1 : 0, partials);
     if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
   }
   return dp_grad_sqnorm(partials, npieces, max_norm, partials + npieces, sqnorm_out,

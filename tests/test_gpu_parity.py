@@ -181,22 +181,35 @@ def test_results_do_not_depend_on_grid_width():
     grads = [rank_grad(p, 1e-3, "bf16", grad_seed(9, r), device=DEV) for r in range(n)]
     master = master_init(p, device=DEV)
     outs = []
+    # The norm of an fp32 array with more pieces than one tree level holds
+    # (4096 * 4096 + 5 elements: 4097 pieces, two levels), and a copy of fp32
+    # shards, under the same widths.
+    flat = rank_grad(4096 * 4096 + 5, 1e-2, "f32", 77, device=DEV)
+    ws = torch.empty(grz.dp_grad_sqnorm_of_workspace(flat.numel()) // 8, dtype=torch.float64,
+                     device=DEV)
     try:
-        for blocks in (2048, 1, 7, 64):
+        for blocks in (1 << 30, 1, 7, 64):
             grz.grz_set_max_blocks(blocks)
             z = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=0.01), device=DEV)
             z.step(grads, 1)
             z.step(grads, 2)
+            sq = torch.zeros(1, dtype=torch.float64, device=DEV)
+            grz.dp_grad_sqnorm_of(flat, 1.0, ws, sq, None)
+            mean = torch.zeros(p, device=DEV)
+            grz.dp_all_gather([m for m in z.means], buckets, [mean])
             torch.cuda.synchronize()
             outs.append((host(z.norm.partials), host(z.replicas[3]),
-                         [host(s[0]) for s in z.state]))
+                         [host(s[0]) for s in z.state], host(ws), host(sq), host(mean)))
     finally:
-        grz.grz_set_max_blocks(2048)
+        grz.grz_set_max_blocks(1 << 30)
     for o in outs[1:]:
         assert_bits(o[0], outs[0][0], "piece sums")
         assert_bits(o[1], outs[0][1], "replica")
         for a, b in zip(o[2], outs[0][2]):
             assert_bits(a, b, "master")
+        assert_bits(o[3], outs[0][3], "pieces and level sums of an fp32 array")
+        assert_bits(o[4], outs[0][4], "its squared norm")
+        assert_bits(o[5], outs[0][5], "fp32 all-gather")
 
 
 def test_cross_n_identity_grid_exact():
