@@ -16,12 +16,16 @@ def _torch_bf16_bits(x):
     return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def test_bf16_rounding_matches_torch_dense_sample():
+def test_bf16_rounding_matches_torch_on_every_upper_half():
     rng = np.random.default_rng(0)
     bits = [rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)]
-    hi = rng.integers(0, 1 << 16, size=1 << 14, dtype=np.uint32) << np.uint32(16)
-    for low in (0x7FFF, 0x8000, 0x8001, 0x0000, 0xFFFF):  # ties and their neighbours
+    # Every upper half (sign, exponent, top 7 mantissa bits) with the lower
+    # halves that decide the rounding: the ties and their neighbours, and a
+    # random one per upper half.
+    hi = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    for low in (0x7FFF, 0x8000, 0x8001, 0x0000, 0xFFFF, 0x0001):
         bits.append(hi | np.uint32(low))
+    bits.append(hi | rng.integers(0, 1 << 16, size=1 << 16, dtype=np.uint32))
     special = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0x7F7FFFFF, 0x7F800000,
                         0xFF800000, 0x00000001, 0x00008000, 0x00018000, 0x007FFFFF,
                         0x80000000, 0x00000000, 0x3F808000, 0x3F818000], dtype=np.uint32)
