@@ -335,6 +335,32 @@ def test_subnormal_and_zero_gradients_match_the_oracle(case):
     assert_bits(host(z.replicas[2]), ref["arena"], f"{case} replica")
 
 
+def test_bf16_rounding_on_every_upper_half():
+    # With lr = 0 and a zero gradient AdamW leaves every finite master as it
+    # is, so the kernel's bf16 output is its rounding of chosen fp32 patterns:
+    # every finite upper half (sign, exponent, top mantissa bits) with the
+    # lower halves that decide round-to-nearest-even (the tie, its
+    # neighbours, 0, 1, 0xFFFF) and a random one, against the oracle.
+    rng = np.random.default_rng(3)
+    hi = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    lows = [np.full(1 << 16, low, np.uint32) for low in (0x0000, 0x0001, 0x7FFF, 0x8000,
+                                                          0x8001, 0xFFFF)]
+    lows.append(rng.integers(0, 1 << 16, size=1 << 16, dtype=np.uint32))
+    bits = np.concatenate([hi | low for low in lows])
+    bits = bits[(bits & 0x7F800000) != 0x7F800000]  # finite only: 0 * inf is NaN
+    x = bits.view(np.float32)
+    w = _dev(x.copy())
+    zeros = torch.zeros_like(w)
+    m, v, g = zeros.clone(), zeros.clone(), zeros.clone()
+    out = torch.empty(x.size, dtype=torch.bfloat16, device=DEV)
+    args = grz.adamw_args(lr=0.0, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
+                          bias_corr1=0.1, bias_corr2=0.05)
+    grz.zero1_adamw_step(w, m, v, g, None, args, out)
+    torch.cuda.synchronize()
+    assert_bits(host(w), x, "masters unchanged at lr = 0")
+    assert_bits(host(out), bf16_round(x), "bf16 rounding of every upper half")
+
+
 # --- the unfused optimizer and the standalone all-gather ----------------------
 
 def test_unfused_adamw_and_all_gather_match_fused_and_oracle():
