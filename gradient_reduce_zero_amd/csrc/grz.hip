@@ -159,14 +159,24 @@ static_assert(GRZ_ADAM_TILE % (GRZ_ADAM_THREADS * 4) == 0, "optimizer tile shape
 static_assert(GRZ_AG_TILE % (GRZ_AG_THREADS * 8) == 0, "all-gather tile shape");
 
 // Occupancy caps, in waves per SIMD (0 = no cap).  Measured on MI355X at the
-// 7B one-rank share: the reduce at 2 waves per SIMD (its 8 input streams per
-// wave) 2.75 ms against 2.90 ms uncapped; the optimizer at 3 waves (4.2 ms
-// at 5 or more, 4.7 ms at 2, with the workgroups above); the all-gather
-// copy of one 16-byte access per lane runs best uncapped.  Speed only, never
-// a result bit.
+// 7B one-rank share: the reduce at 2 waves per SIMD for 4 to 16 input
+// streams (N = 8: 2.75 ms against 2.90 ms uncapped; N = 16: 2.47 ms against
+// 2.63 at 3 and 3.81 at 6; N = 4: 3.33 ms, 3 to 6 waves no better) and at 3
+// for one or two (N = 2: 4.37 ms against 5.16 at 2, 4.39 uncapped); the
+// optimizer at 3 waves (4.2 ms at 5 or more, 4.7 ms at 2, with the
+// workgroups above); the all-gather copy of one 16-byte access per lane runs
+// best uncapped.  Speed only, never a result bit.
 #ifndef GRZ_RS_WAVES
 #define GRZ_RS_WAVES 2
 #endif
+#ifndef GRZ_RS_WAVES_FEW
+#define GRZ_RS_WAVES_FEW 3
+#endif
+static_assert(GRZ_RS_WAVES > 0 && GRZ_RS_WAVES_FEW > 0, "the reduce's caps are per N");
+// The reduce's cap for N ranks (NR = 0: N outside the unrolled set).
+template <int NR> struct RsWaves {
+  static constexpr int value = (NR == 1 || NR == 2) ? GRZ_RS_WAVES_FEW : GRZ_RS_WAVES;
+};
 #ifndef GRZ_ADAM_WAVES
 #define GRZ_ADAM_WAVES 3
 #endif
@@ -177,11 +187,6 @@ static_assert(GRZ_AG_TILE % (GRZ_AG_THREADS * 8) == 0, "all-gather tile shape");
 #define GRZ_AG_ATTR __attribute__((amdgpu_waves_per_eu(GRZ_AG_WAVES, GRZ_AG_WAVES)))
 #else
 #define GRZ_AG_ATTR
-#endif
-#if GRZ_RS_WAVES > 0
-#define GRZ_RS_ATTR __attribute__((amdgpu_waves_per_eu(GRZ_RS_WAVES, GRZ_RS_WAVES)))
-#else
-#define GRZ_RS_ATTR
 #endif
 #if GRZ_ADAM_WAVES > 0
 #define GRZ_ADAM_ATTR __attribute__((amdgpu_waves_per_eu(GRZ_ADAM_WAVES, GRZ_ADAM_WAVES)))
@@ -358,24 +363,26 @@ __device__ __forceinline__ typename AccOf<TIn>::type fold_one(const TIn* const* 
   return acc;
 }
 
-// fold_vec over the K accesses of a full tile at once: all K * NR loads are
-// issued before the first addition.  `off` is the lane's first element; the
-// fold of each element is the same sequence of additions as fold_vec's.
-template <typename TIn, int NR, bool WIRE, typename Acc = typename AccOf<TIn>::type,
-          int G = Geo<Acc>::G, int K = Geo<Acc>::K>
-__device__ __forceinline__ void fold_tile(const TIn* const* rank, int c, int64_t off,
-                                          Acc (&acc)[K][G]) {
-  Acc x[K][NR][G];
+// fold_vec over accesses k0 .. k0 + KB - 1 of a full tile at once: all
+// KB * NR loads are issued before the first addition.  `off` is the lane's
+// first element; the fold of each element is the same sequence of additions
+// as fold_vec's.
+template <typename TIn, int NR, bool WIRE, int KB, typename Acc = typename AccOf<TIn>::type,
+          int G = Geo<Acc>::G>
+__device__ __forceinline__ void fold_tile(const TIn* const* rank, int c, int64_t off, int k0,
+                                          Acc (&acc)[KB][G]) {
+  Acc x[KB][NR][G];
 #pragma unroll
-  for (int k = 0; k < K; ++k)
+  for (int k = 0; k < KB; ++k)
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
       int r = c + j;
       r = r >= NR ? r - NR : r;
-      loadg<GRZ_RS_POLICY>(rank[r] + off + static_cast<int64_t>(k) * kThreads * G, x[k][j]);
+      loadg<GRZ_RS_POLICY>(rank[r] + off + static_cast<int64_t>(k0 + k) * kThreads * G,
+                           x[k][j]);
     }
 #pragma unroll
-  for (int k = 0; k < K; ++k)
+  for (int k = 0; k < KB; ++k)
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       acc[k][i] = x[k][0][i];
@@ -391,7 +398,9 @@ __device__ __forceinline__ void fold_tile(const TIn* const* rank, int c, int64_t
 // ring whose wire format is bf16 does once per hop ("13.5 Multi-GPU from
 // First Principles", exercise 8).
 template <typename TIn, int NR, bool WIRE>
-__global__ __launch_bounds__(kThreads) GRZ_RS_ATTR void rs_mean_kernel(const RsArgs<TIn> a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(RsWaves<NR>::value, RsWaves<NR>::value))) void rs_mean_kernel(
+    const RsArgs<TIn> a) {
   using Acc = typename AccOf<TIn>::type;
   constexpr int G = Geo<Acc>::G;
   constexpr int K = Geo<Acc>::K;
@@ -410,16 +419,26 @@ __global__ __launch_bounds__(kThreads) GRZ_RS_ATTR void rs_mean_kernel(const RsA
     bool done = false;
     if constexpr (GRZ_RS_BATCH && NR > 0 && sizeof(TIn) < 8) {
       if (s.vec && left >= GRZ_PIECE) {
-        Acc acc[K][G];
-        fold_tile<TIn, NR, WIRE>(a.rank, c, s.src + e0 + lane * G, acc);
+        // At most 32 loads in flight per lane: the whole tile for N <= 8, two
+        // accesses at a time for N = 16.  The squares are added in the same
+        // order either way.
+        constexpr int KB = NR * K <= 32 ? K : (32 / NR > 0 ? 32 / NR : 1);
+        static_assert(K % KB == 0, "batch shape");
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
+        for (int k0 = 0; k0 < K; k0 += KB) {
+          Acc acc[KB][G];
+          fold_tile<TIn, NR, WIRE, KB>(a.rank, c, s.src + e0 + lane * G, k0, acc);
 #pragma unroll
-          for (int i = 0; i < G; ++i) {
-            if (a.average) acc[k][i] = a.pow2 ? acc[k][i] * inv : acc[k][i] / nf;
-            sq = __fma_rn(static_cast<double>(acc[k][i]), static_cast<double>(acc[k][i]), sq);
+          for (int kk = 0; kk < KB; ++kk) {
+            const int k = k0 + kk;
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+              if (a.average) acc[kk][i] = a.pow2 ? acc[kk][i] * inv : acc[kk][i] / nf;
+              sq = __fma_rn(static_cast<double>(acc[kk][i]), static_cast<double>(acc[kk][i]),
+                            sq);
+            }
+            storeg<GRZ_RS_POLICY>(a.out + s.dst + e0 + (k * kThreads + lane) * G, acc[kk]);
           }
-          storeg<GRZ_RS_POLICY>(a.out + s.dst + e0 + (k * kThreads + lane) * G, acc[k]);
         }
         done = true;
       }
@@ -1111,6 +1130,7 @@ int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>
     case 2: return rs_launch<TIn, 2>(segs, args, wire, stream);
     case 4: return rs_launch<TIn, 4>(segs, args, wire, stream);
     case 8: return rs_launch<TIn, 8>(segs, args, wire, stream);
+    case 16: return rs_launch<TIn, 16>(segs, args, wire, stream);
     default: return rs_launch<TIn, 0>(segs, args, wire, stream);
   }
 }
