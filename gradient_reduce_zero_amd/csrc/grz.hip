@@ -158,11 +158,12 @@ constexpr int kNtLoad = 1, kNtStore = 2;
 static_assert(GRZ_ADAM_TILE % (GRZ_ADAM_THREADS * 4) == 0, "optimizer tile shape");
 static_assert(GRZ_AG_TILE % (GRZ_AG_THREADS * 8) == 0, "all-gather tile shape");
 
-// Occupancy caps, in waves per SIMD (0 = no cap).  Measured on MI355X at the
-// 7B one-rank share: the reduce at 2 waves per SIMD for 4 to 16 input
-// streams (N = 8: 2.75 ms against 2.90 ms uncapped; N = 16: 2.47 ms against
-// 2.63 at 3 and 3.81 at 6; N = 4: 3.33 ms, 3 to 6 waves no better) and at 3
-// for one or two (N = 2: 4.37 ms against 5.16 at 2, 4.39 uncapped); the
+// Occupancy caps, in waves per SIMD (0 = no cap).  Measured on MI355X: the
+// reduce at 2 waves per SIMD for 5 to 16 input streams (7B one-rank share,
+// N = 8: 2.75 ms against 2.90 ms uncapped; N = 16: 2.47 ms against 2.63 at 3
+// and 3.81 at 6) and at 3 for up to four (N = 2: 4.37 ms against 5.16 at 2;
+// a 134 M-element shard at N = 3: 5.8 TB/s against 4.95 at 2, at N = 4: 6.5
+// against 6.1, and the 7B share at N = 4 the same either way); the
 // optimizer at 3 waves (4.2 ms at 5 or more, 4.7 ms at 2, with the
 // workgroups above); the all-gather copy of one 16-byte access per lane runs
 // best uncapped.  Speed only, never a result bit.
@@ -175,7 +176,7 @@ static_assert(GRZ_AG_TILE % (GRZ_AG_THREADS * 8) == 0, "all-gather tile shape");
 static_assert(GRZ_RS_WAVES > 0 && GRZ_RS_WAVES_FEW > 0, "the reduce's caps are per N");
 // The reduce's cap for N ranks (NR = 0: N outside the unrolled set).
 template <int NR> struct RsWaves {
-  static constexpr int value = (NR == 1 || NR == 2) ? GRZ_RS_WAVES_FEW : GRZ_RS_WAVES;
+  static constexpr int value = (NR >= 1 && NR <= 4) ? GRZ_RS_WAVES_FEW : GRZ_RS_WAVES;
 };
 #ifndef GRZ_ADAM_WAVES
 #define GRZ_ADAM_WAVES 3
@@ -420,9 +421,9 @@ __attribute__((amdgpu_waves_per_eu(RsWaves<NR>::value, RsWaves<NR>::value))) voi
     if constexpr (GRZ_RS_BATCH && NR > 0 && sizeof(TIn) < 8) {
       if (s.vec && left >= GRZ_PIECE) {
         // At most 32 loads in flight per lane: the whole tile for N <= 8, two
-        // accesses at a time for N = 16.  The squares are added in the same
+        // accesses at a time for N = 9..16.  The squares are added in the same
         // order either way.
-        constexpr int KB = NR * K <= 32 ? K : (32 / NR > 0 ? 32 / NR : 1);
+        constexpr int KB = NR * K <= 32 ? K : (NR * (K / 2) <= 32 ? K / 2 : 1);
         static_assert(K % KB == 0, "batch shape");
 #pragma unroll
         for (int k0 = 0; k0 < K; k0 += KB) {
@@ -1125,13 +1126,26 @@ int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>
     segs.push_back(s);
   }
   const bool wire = (flags & GRZ_BF16_WIRE) != 0;
+  // Every N the library takes has its own unrolled fold.
+  static_assert(GRZ_MAX_RANKS == 16, "one case per N below");
   switch (n) {
     case 1: return rs_launch<TIn, 1>(segs, args, wire, stream);
     case 2: return rs_launch<TIn, 2>(segs, args, wire, stream);
+    case 3: return rs_launch<TIn, 3>(segs, args, wire, stream);
     case 4: return rs_launch<TIn, 4>(segs, args, wire, stream);
+    case 5: return rs_launch<TIn, 5>(segs, args, wire, stream);
+    case 6: return rs_launch<TIn, 6>(segs, args, wire, stream);
+    case 7: return rs_launch<TIn, 7>(segs, args, wire, stream);
     case 8: return rs_launch<TIn, 8>(segs, args, wire, stream);
+    case 9: return rs_launch<TIn, 9>(segs, args, wire, stream);
+    case 10: return rs_launch<TIn, 10>(segs, args, wire, stream);
+    case 11: return rs_launch<TIn, 11>(segs, args, wire, stream);
+    case 12: return rs_launch<TIn, 12>(segs, args, wire, stream);
+    case 13: return rs_launch<TIn, 13>(segs, args, wire, stream);
+    case 14: return rs_launch<TIn, 14>(segs, args, wire, stream);
+    case 15: return rs_launch<TIn, 15>(segs, args, wire, stream);
     case 16: return rs_launch<TIn, 16>(segs, args, wire, stream);
-    default: return rs_launch<TIn, 0>(segs, args, wire, stream);
+    default: return GRZ_EINVAL;
   }
 }
 

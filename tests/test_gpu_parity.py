@@ -567,8 +567,11 @@ def test_dropped_wait_reads_gradients_not_yet_written():
     # before the backward has written the gradients.  The compute stream runs
     # milliseconds of GEMMs before it writes them; the ordered step reduces
     # the written values, the one with the wait dropped reduces what was there
-    # before (zeros).  Were the two streams ever run one after the other on a
-    # device, the race could not show: then that half is skipped, not failed.
+    # before (zeros).  When the two streams share a hardware queue (HIP maps
+    # streams onto a few queues, so this depends on the streams made before)
+    # they run one after the other and the race cannot show: then that half
+    # is skipped, not failed; tests/test_overlap_schedule.py checks the
+    # ordering itself deterministically.
     n, p = 2, 2 * 4096 * 16
     buckets = [(0, p)]
     src = [rank_grad(p, 1e-2, "bf16", grad_seed(4, r), device=DEV) for r in range(n)]
