@@ -1,6 +1,7 @@
 """The library from C: a C99 consumer of include/grz.h, built with gcc against
 the regular library and with clang + AddressSanitizer against a build whose
-host code is instrumented (-Xarch_host -fsanitize=address).  Host logic only:
+host code is instrumented (-Xarch_host -fsanitize=address), and the header from
+C++.  Host logic only:
 plan helpers on pseudo-random plans and argument errors reported before any
 launch (tests/native/host_checks.c)."""
 
@@ -54,3 +55,18 @@ def test_host_code_under_address_sanitizer(tmp_path):
           "-o", str(exe)])
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0")
     assert "host checks passed" in _run([str(exe)], env=env).stdout
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="no C++ compiler")
+def test_header_compiles_as_cpp(tmp_path):
+    # A C++ consumer sees the same declarations through the header's extern "C"
+    # guard (syntax and linkage only, nothing runs).
+    src = tmp_path / "use.cpp"
+    src.write_text('#include "grz.h"\n'
+                   'static_assert(sizeof(grz_bucket) == 16, "bucket layout");\n'
+                   'static_assert(sizeof(grz_adamw_args) == 28, "args layout");\n'
+                   'int (*const reduce)(const void* const*, int, int, const grz_bucket*, int, int,'
+                   ' int, void*, double*, hipStream_t) = dp_reduce_scatter_mean;\n'
+                   'int main() { return reduce == nullptr; }\n')
+    _run(["g++", "-std=c++17", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__", f"-I{INC}",
+          f"-I{ROCM}/include", str(src)])
