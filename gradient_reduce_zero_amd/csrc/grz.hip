@@ -174,7 +174,7 @@ static_assert(GRZ_AG_TILE % (GRZ_AG_THREADS * 8) == 0, "all-gather tile shape");
 #define GRZ_RS_WAVES_FEW 3
 #endif
 static_assert(GRZ_RS_WAVES > 0 && GRZ_RS_WAVES_FEW > 0, "the reduce's caps are per N");
-// The reduce's cap for N ranks (NR = 0: N outside the unrolled set).
+// The reduce's cap for N ranks (every N from 1 to 16 has its own kernel).
 template <int NR> struct RsWaves {
   static constexpr int value = (NR >= 1 && NR <= 4) ? GRZ_RS_WAVES_FEW : GRZ_RS_WAVES;
 };
