@@ -834,6 +834,16 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate:
+        numel = 1 << 30  # 2 GiB of bf16 read, 2 GiB written
+        src = torch.ones(numel, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            grz.zero1_all_gather([src], [(0, numel)], [dst])
+        torch.cuda.synchronize()
+        assert bool(torch.equal(src, dst))
+        log(f"calibration copy: 3 launches of {2 * numel} bytes read + {2 * numel} written")
+        del src, dst
     if args.overlap:
         overlap_bench(args, dev)
         return
@@ -846,16 +856,6 @@ def main():
     if args.ddp:
         ddp_bench(args, dev)
         return
-    if args.calibrate:
-        numel = 1 << 30  # 2 GiB of bf16 read, 2 GiB written
-        src = torch.ones(numel, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            grz.zero1_all_gather([src], [(0, numel)], [dst])
-        torch.cuda.synchronize()
-        assert bool(torch.equal(src, dst))
-        log(f"calibration copy: 3 launches of {2 * numel} bytes read + {2 * numel} written")
-        del src, dst
     log(f"setting up {args.config} one-rank share, N={args.nranks}")
     flags = grz.GRZ_BF16_WIRE if args.wire == "bf16" else 0
     setup = onerank_setup(args.config, args.nranks, 0, dev, reduce_flags=flags)
