@@ -147,3 +147,111 @@ def test_update_on_a_random_plan(seed):
         want_rep[g0:g0 + length] = b[c0:c0 + length]
     for r in reps:
         assert_bits(host(r), want_rep, f"seed {seed}: replica")
+
+
+def test_a_plan_of_many_buckets_spans_several_launches():
+    # 150 buckets at N = 5 with array_split chunks: one shard has 150
+    # segments and the whole plan 750, more than one launch takes (64), so
+    # every entry point splits the plan into several launches.  The mean and
+    # the piece sums of one chunk and of every chunk, the update of one shard
+    # into two replicas, and both all-gathers, each against the oracle.
+    from oracle.bf16 import bf16_round
+    from oracle.reduce import owned_chunk
+    from oracle.step import Hyper as OHyper
+    from oracle.step import adamw, all_gather
+
+    rng = np.random.default_rng(77)
+    n, nb = 5, 150
+    lengths = [int(x) for x in rng.integers(0, 900, size=nb)]
+    lengths[::37] = [2 * PIECE + 3] * len(lengths[::37])  # a few multi-piece chunks
+    lengths[5] = 0
+    order = rng.permutation(nb)
+    offs, pos = [0] * nb, 0
+    for i in order:
+        offs[i] = pos
+        pos += lengths[i]
+    buckets, p = list(zip(offs, lengths)), pos
+    flags = grz.GRZ_UNEVEN
+    grads = [rank_grad(p, 1e-2, "bf16", 9100 + r, device=DEV) for r in range(n)]
+    hg = [host(g) for g in grads]
+    npieces = grz.dp_piece_count(buckets, n, flags)
+
+    mean_global = np.full(p, np.nan, np.float32)
+    for c in range(n):
+        comp = reduce_scatter_mean(hg, "bf16", buckets, c, uneven=True)
+        for g0, length, c0 in shard_segments(buckets, n, c, uneven=True):
+            mean_global[g0:g0 + length] = comp[c0:c0 + length]
+    for chunk in (2, -1):
+        size = grz.dp_shard_numel(buckets, n, chunk, flags) if chunk >= 0 else p
+        out = torch.full((size,), float("nan"), device=DEV)
+        parts = torch.full((npieces,), -1.0, dtype=torch.float64, device=DEV)
+        grz.dp_reduce_scatter_mean(grads, buckets, chunk, out, parts, flags=flags)
+        torch.cuda.synchronize()
+        if chunk >= 0:
+            want = reduce_scatter_mean(hg, "bf16", buckets, chunk, uneven=True)
+        else:
+            want = mean_global
+        assert_bits(host(out), want, f"mean, chunk {chunk}")
+        got = host(parts)
+        chunks = set(range(n)) if chunk < 0 else {chunk}
+        for i, want_i in enumerate(_pieces_of(mean_global, buckets, n, chunks)):
+            if want_i is None:
+                assert got[i] == -1.0, f"chunk {chunk}: piece {i} written"
+            else:
+                assert math.isclose(got[i], want_i, rel_tol=1e-13, abs_tol=0.0), (chunk, i)
+
+    # Clipped AdamW on chunk 2's shard, written into two replicas.
+    chunk = 2
+    segs = shard_segments(buckets, n, chunk, uneven=True)
+    k = sum(s[1] for s in segs)
+    w = rng.standard_normal(k).astype(np.float32) * np.float32(0.02)
+    m = rng.standard_normal(k).astype(np.float32) * np.float32(1e-3)
+    v = np.abs(rng.standard_normal(k)).astype(np.float32) * np.float32(1e-6)
+    g = reduce_scatter_mean(hg, "bf16", buckets, chunk, uneven=True)
+    scale = np.float32(0.375)
+    dev = [torch.from_numpy(a.copy()).to(DEV) for a in (w, m, v, g)]
+    sentinel = 0x7A5C
+    reps = [torch.full((p,), sentinel, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+            for _ in range(2)]
+    hyper = grz.Hyper(lr=1e-3)
+    grz.zero1_adamw_gather(dev[0], dev[1], dev[2], dev[3], buckets, n, chunk,
+                           torch.tensor([scale], device=DEV),
+                           grz.adamw_args(**grz.step_scalars(hyper, 2)), reps, flags=flags)
+    torch.cuda.synchronize()
+    w1, m1, v1 = adamw(w, m, v, g * scale, **OHyper(lr=1e-3).scalars(2))
+    for i, want in enumerate((w1, m1, v1)):
+        assert_bits(host(dev[i]), want, f"state {i}")
+    want_rep = np.full(p, sentinel, np.uint16)
+    b = bf16_round(w1)
+    for g0, length, c0 in segs:
+        want_rep[g0:g0 + length] = b[c0:c0 + length]
+    for r in reps:
+        assert_bits(host(r), want_rep, "replica after the update")
+
+    # Both all-gathers: every rank's shard (rank 1's already in place).
+    sizes = [grz.dp_shard_numel(buckets, n, owned_chunk(r, n), flags) for r in range(n)]
+    bf = [rng.integers(0, 1 << 16, size=max(s, 1), dtype=np.uint16) for s in sizes]
+    f32 = [rng.standard_normal(max(s, 1)).astype(np.float32) for s in sizes]
+    bf_t = [torch.from_numpy(a.view(np.int16).copy()).to(DEV).view(torch.bfloat16) for a in bf]
+    f32_t = [torch.from_numpy(a.copy()).to(DEV) for a in f32]
+    rep_bf = torch.full((p,), sentinel, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    rep_f32 = torch.full((p,), float("nan"), device=DEV)
+    grz.zero1_all_gather([None if r == 1 else bf_t[r] for r in range(n)], buckets, [rep_bf],
+                         flags=flags)
+    grz.dp_all_gather([None if r == 1 else f32_t[r] for r in range(n)], buckets, [rep_f32],
+                      flags=flags)
+    torch.cuda.synchronize()
+    want_bf = all_gather([None if r == 1 else bf[r][:sizes[r]] for r in range(n)], buckets, n,
+                         p, uneven=True)
+    rank1 = [(g0, length) for g0, length, _ in shard_segments(buckets, n, owned_chunk(1, n),
+                                                              uneven=True)]
+    for g0, length in rank1:
+        want_bf[g0:g0 + length] = sentinel
+    assert_bits(host(rep_bf), want_bf, "bf16 all-gather")
+    want_f32 = np.full(p, np.nan, np.float32)
+    for r in range(n):
+        if r == 1:
+            continue
+        for g0, length, c0 in shard_segments(buckets, n, owned_chunk(r, n), uneven=True):
+            want_f32[g0:g0 + length] = f32[r][c0:c0 + length]
+    assert_bits(host(rep_f32), want_f32, "fp32 all-gather")
