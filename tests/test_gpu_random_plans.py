@@ -255,3 +255,69 @@ def test_a_plan_of_many_buckets_spans_several_launches():
         for g0, length, c0 in shard_segments(buckets, n, owned_chunk(r, n), uneven=True):
             want_f32[g0:g0 + length] = f32[r][c0:c0 + length]
     assert_bits(host(rep_f32), want_f32, "fp32 all-gather")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_reduce_modes_on_a_random_plan(seed):
+    # The reduce's other modes on random plans: the sum instead of the mean,
+    # the bf16 wire (bf16 gradients), the token-weighted mean (totals that are
+    # and are not powers of two), shard-compact inputs, alone and together.
+    # Output bit-exact against the oracle; the piece sums against the exact
+    # sum of squares of the oracle's output.
+    rng = np.random.default_rng(8000 + seed)
+    n, kind, even, buckets, p, chunk, mode = _draw(3000 + seed)
+    flags = 0 if even else grz.GRZ_UNEVEN
+    if mode == "global":
+        flags |= grz.GRZ_OUT_GLOBAL
+    wire = "bf16" if kind == "bf16" and rng.integers(0, 2) else None
+    if wire:
+        flags |= grz.GRZ_BF16_WIRE
+    counts = None
+    if rng.integers(0, 3) == 0:
+        counts = [int(c) for c in rng.integers(0, 4000, size=n)]
+        if rng.integers(0, 2):
+            counts[-1] += (1 << 12) * (1 + n) - sum(counts)  # a power-of-two total
+        counts[0] = max(counts[0], 1) if sum(counts) == 0 else counts[0]
+    elif rng.integers(0, 4) == 0:
+        flags |= grz.GRZ_SUM
+    compact = chunk >= 0 and mode == "compact" and bool(rng.integers(0, 2))
+    grads = [rank_grad(p, 1e-2, kind, 9300 + 17 * seed + r, device=DEV) for r in range(n)]
+    hg = [host(g) for g in grads]
+    if compact:
+        flags |= grz.GRZ_IN_COMPACT
+        segs = shard_segments(buckets, n, chunk, uneven=not even)
+        idx = torch.tensor([i for g0, l, _ in segs for i in range(g0, g0 + l)] or [0],
+                           dtype=torch.int64, device=DEV)
+        inputs = [g[idx].contiguous() for g in grads]
+        hin = [host(g) for g in inputs]
+    else:
+        inputs, hin = grads, hg
+    acc = np.float64 if kind == "f64" else np.float32
+    out_t = torch.float64 if kind == "f64" else torch.float32
+    npieces = grz.dp_piece_count(buckets, n, flags)
+    parts = torch.full((max(npieces, 1),), -1.0, dtype=torch.float64, device=DEV)
+    shard = grz.dp_shard_numel(buckets, n, chunk, flags) if chunk >= 0 else p
+    out = torch.full((max(shard if mode == "compact" else p, 1),), float("nan"), dtype=out_t,
+                     device=DEV)
+    grz.dp_reduce_scatter_mean(inputs, buckets, chunk, out, parts, flags=flags,
+                               token_counts=counts)
+    torch.cuda.synchronize()
+    kw = dict(average=not flags & grz.GRZ_SUM, uneven=not even, wire=wire, token_counts=counts)
+    out_global = np.full(p, np.nan, acc)
+    chunks = range(n) if chunk < 0 else [chunk]
+    for c in chunks:
+        comp = reduce_scatter_mean(hg, kind, buckets, c, **kw)
+        for g0, length, c0 in shard_segments(buckets, n, c, uneven=not even):
+            out_global[g0:g0 + length] = comp[c0:c0 + length]
+    what = f"seed {seed} (n {n}, {kind}, wire {wire}, counts {counts}, flags {flags})"
+    if mode == "compact":
+        want = reduce_scatter_mean(hin, kind, buckets, chunk, compact_inputs=compact, **kw)
+        assert_bits(host(out)[:shard], want, what)
+    else:
+        assert_bits(host(out)[:p], out_global, what)
+    got = host(parts)
+    for i, want_i in enumerate(_pieces_of(out_global, buckets, n, set(chunks))):
+        if want_i is None:
+            assert got[i] == -1.0, f"{what}: piece {i} of a chunk not reduced was written"
+        else:
+            assert math.isclose(got[i], want_i, rel_tol=1e-13, abs_tol=0.0), (what, i)
