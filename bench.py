@@ -49,7 +49,7 @@ def settle():
     gc.freeze()
 
 
-def onerank_setup(name, n, rank, device, reduce_flags=0):
+def onerank_setup(name, n, rank, device, reduce_flags=0, bucket_plan="default"):
     import torch  # noqa: F401
 
     import gradient_reduce_zero_amd as grz
@@ -57,7 +57,10 @@ def onerank_setup(name, n, rank, device, reduce_flags=0):
 
     a = arena(name)
     p = a.numel
-    buckets = grz.whole_arena(p) if name != "gpt2_124m" else grz.plan_buckets(a.numels)
+    if bucket_plan == "25mb" or (bucket_plan == "default" and name == "gpt2_124m"):
+        buckets = grz.plan_buckets(a.numels)  # reverse layer order, 25 MiB of gradient
+    else:
+        buckets = grz.whole_arena(p)
     chunk = grz.owned_chunk(rank, n)
     shard = grz.dp_shard_numel(buckets, n, chunk)
     npieces = grz.dp_piece_count(buckets, n)
@@ -792,6 +795,10 @@ def main():
                     help="also time each step after a 512 MB write that evicts the 256 MB "
                          "Infinity Cache and the L2s (steps whose bytes fit those caches "
                          "otherwise run warm); the step's kernels alone are timed")
+    ap.add_argument("--bucket-plan", choices=["default", "whole", "25mb"], default="default",
+                    help="the one-rank share's bucket plan: the workload's own (one bucket "
+                         "for the whole arena, GPT-2 124M's nine 25 MiB buckets), the whole "
+                         "arena, or reverse-layer buckets of 25 MiB of gradient")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 2 GiB bf16 copy (the library's all-gather "
                          "kernel with one rank and one replica) as the reference of known "
@@ -858,7 +865,8 @@ def main():
         return
     log(f"setting up {args.config} one-rank share, N={args.nranks}")
     flags = grz.GRZ_BF16_WIRE if args.wire == "bf16" else 0
-    setup = onerank_setup(args.config, args.nranks, 0, dev, reduce_flags=flags)
+    setup = onerank_setup(args.config, args.nranks, 0, dev, reduce_flags=flags,
+                          bucket_plan=args.bucket_plan)
     pipe, inp = setup["pipe"], setup["inp"]
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()

@@ -75,14 +75,33 @@ struct Seg {
   int32_t vec;
 };
 
-template <typename S>
-__device__ __forceinline__ int find_seg(const S* seg, int nsegs, int64_t tile) {
-  int lo = 0, hi = nsegs - 1;
-  while (lo < hi) {  // last segment whose tile0 <= tile
-    int mid = (lo + hi + 1) >> 1;
-    if (seg[mid].tile0 <= tile) lo = mid; else hi = mid - 1;
+// The segment of a launch that holds `tile`: the last of the first nsegs
+// whose tile0 <= tile.  tile0 does not decrease, so those segments are a
+// prefix: count them, first by groups of 8, then inside the group, with all
+// loads of a round issued before the first comparison (two dependent rounds
+// of kernel-argument reads where a binary search over 64 takes six).
+// Measured on MI355X at the 7B one-rank share: the optimizer 3.75-3.77 ms
+// against 3.96-4.04 ms with the binary search, the all-gather copy 3.51-3.55
+// against 3.58-3.62, and with 291 reverse-layer buckets the step 10.28-10.30
+// against 10.65-10.76 ms.
+template <typename S, int M>
+__device__ __forceinline__ int find_seg(const S (&seg)[M], int nsegs, int64_t tile) {
+  static_assert(M % 8 == 0, "segment groups of 8");
+  if (nsegs <= 1) return 0;
+  int g = 0;
+#pragma unroll
+  for (int i = 1; i < M / 8; ++i) {
+    const int64_t t0 = seg[i * 8].tile0;
+    g += static_cast<int>(i * 8 < nsegs) & static_cast<int>(t0 <= tile);
   }
-  return lo;
+  int64_t t[7];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) t[i - 1] = seg[g * 8 + i].tile0;
+  int idx = g * 8;
+#pragma unroll
+  for (int i = 1; i < 8; ++i)
+    idx += static_cast<int>(g * 8 + i < nsegs) & static_cast<int>(t[i - 1] <= tile);
+  return idx;
 }
 
 // ---------------------------------------------------------------------------
@@ -583,6 +602,8 @@ struct AdamArgs {
   Seg seg[kMaxSegs];
 };
 
+typedef const __attribute__((address_space(4))) grz_adamw_args ConstArgs;
+
 // One element, every operation rounded on its own (the file is built with
 // -ffp-contract=off; '/' and sqrtf are the IEEE ones).
 __device__ __forceinline__ void adamw1(float& w, float& m, float& v, float g, float lr,
@@ -606,9 +627,12 @@ __global__ __launch_bounds__(GRZ_ADAM_THREADS) GRZ_ADAM_ATTR void adamw_kernel(
   const float scale = a.scale != nullptr ? *a.scale : 1.0f;
   float lr = a.lr, b1 = a.b1, b2 = a.b2, eps = a.eps, wd = a.wd, bc1 = a.bc1, bc2 = a.bc2;
   if (a.dargs != nullptr) {
-    const grz_adamw_args d = *a.dargs;
-    lr = d.lr; b1 = d.beta1; b2 = d.beta2; eps = d.eps; wd = d.weight_decay;
-    bc1 = d.bias_corr1; bc2 = d.bias_corr2;
+    // Read as constant memory (the scalars do not change while the kernel
+    // runs), so that they arrive through uniform loads rather than a vector
+    // load that every workgroup waits for before its first tile.
+    const ConstArgs* d = (const ConstArgs*)(a.dargs);  // an address-space cast
+    lr = d->lr; b1 = d->beta1; b2 = d->beta2; eps = d->eps; wd = d->weight_decay;
+    bc1 = d->bias_corr1; bc2 = d->bias_corr2;
   }
   const float omb1 = 1.0f - b1;  // exact: 1/2 <= b1 <= 1 (Sterbenz)
   const float omb2 = 1.0f - b2;
@@ -912,9 +936,12 @@ void fused_step_kernel(const FusedArgs<TIn> a) {
   // Clip + AdamW from the registers; bf16 weights into every replica.
   float lr = a.lr, b1 = a.b1, b2 = a.b2, eps = a.eps, wd = a.wd, bc1 = a.bc1, bc2 = a.bc2;
   if (a.dargs != nullptr) {
-    const grz_adamw_args d = *a.dargs;
-    lr = d.lr; b1 = d.beta1; b2 = d.beta2; eps = d.eps; wd = d.weight_decay;
-    bc1 = d.bias_corr1; bc2 = d.bias_corr2;
+    // Read as constant memory (the scalars do not change while the kernel
+    // runs), so that they arrive through uniform loads rather than a vector
+    // load that every workgroup waits for before its first tile.
+    const ConstArgs* d = (const ConstArgs*)(a.dargs);  // an address-space cast
+    lr = d->lr; b1 = d->beta1; b2 = d->beta2; eps = d->eps; wd = d->weight_decay;
+    bc1 = d->bias_corr1; bc2 = d->bias_corr2;
   }
   const float omb1 = 1.0f - b1;
   const float omb2 = 1.0f - b2;
