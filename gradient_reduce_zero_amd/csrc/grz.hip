@@ -80,10 +80,11 @@ struct Seg {
 // prefix: count them, first by groups of 8, then inside the group, with all
 // loads of a round issued before the first comparison (two dependent rounds
 // of kernel-argument reads where a binary search over 64 takes six).
-// Measured on MI355X at the 7B one-rank share: the optimizer 3.75-3.77 ms
-// against 3.96-4.04 ms with the binary search, the all-gather copy 3.51-3.55
-// against 3.58-3.62, and with 291 reverse-layer buckets the step 10.28-10.30
-// against 10.65-10.76 ms.
+// Measured on MI355X at the 7B one-rank share, two runs alternating with the
+// binary search: the optimizer 3.75-3.97 ms against 3.96-4.04 ms, the
+// all-gather copy 3.51-3.55 against 3.58-3.62, the step 9.94-10.21 against
+// 10.30-10.39; with 291 reverse-layer buckets the step 10.28-10.30 against
+// 10.65-10.76 ms.
 template <typename S, int M>
 __device__ __forceinline__ int find_seg(const S (&seg)[M], int nsegs, int64_t tile) {
   static_assert(M % 8 == 0, "segment groups of 8");
