@@ -155,16 +155,33 @@ def test_a_plan_of_many_buckets_spans_several_launches():
     # every entry point splits the plan into several launches.  The mean and
     # the piece sums of one chunk and of every chunk, the update of one shard
     # into two replicas, and both all-gathers, each against the oracle.
+    rng = np.random.default_rng(77)
+    lengths = [int(x) for x in rng.integers(0, 900, size=150)]
+    lengths[::37] = [2 * PIECE + 3] * len(lengths[::37])  # a few multi-piece chunks
+    lengths[5] = 0
+    _every_entry_point_on(5, lengths, rng, 9100)
+
+
+@pytest.mark.parametrize("nb", [2, 7, 8, 9, 16, 17, 63, 64, 65, 130])
+def test_segment_lookup_at_group_and_launch_edges(nb):
+    # Each kernel finds a tile's segment among up to 64 per launch by groups
+    # of 8: plans whose shards have segment counts at the edges of a group
+    # and of a launch, segments of one tile and of several, at N = 2 (a
+    # shard of nb segments, the whole plan 2 * nb), every entry point against
+    # the oracle.
+    rng = np.random.default_rng(500 + nb)
+    choices = [2, 96, 514, 2048, 2 * PIECE + 6, 3 * PIECE - 2]
+    lengths = [int(choices[i]) for i in rng.integers(0, len(choices), size=nb)]
+    _every_entry_point_on(2, lengths, rng, 9400 + nb)
+
+
+def _every_entry_point_on(n, lengths, rng, seed):
     from oracle.bf16 import bf16_round
     from oracle.reduce import owned_chunk
     from oracle.step import Hyper as OHyper
     from oracle.step import adamw, all_gather
 
-    rng = np.random.default_rng(77)
-    n, nb = 5, 150
-    lengths = [int(x) for x in rng.integers(0, 900, size=nb)]
-    lengths[::37] = [2 * PIECE + 3] * len(lengths[::37])  # a few multi-piece chunks
-    lengths[5] = 0
+    nb = len(lengths)
     order = rng.permutation(nb)
     offs, pos = [0] * nb, 0
     for i in order:
@@ -172,7 +189,7 @@ def test_a_plan_of_many_buckets_spans_several_launches():
         pos += lengths[i]
     buckets, p = list(zip(offs, lengths)), pos
     flags = grz.GRZ_UNEVEN
-    grads = [rank_grad(p, 1e-2, "bf16", 9100 + r, device=DEV) for r in range(n)]
+    grads = [rank_grad(p, 1e-2, "bf16", seed + r, device=DEV) for r in range(n)]
     hg = [host(g) for g in grads]
     npieces = grz.dp_piece_count(buckets, n, flags)
 
@@ -181,7 +198,7 @@ def test_a_plan_of_many_buckets_spans_several_launches():
         comp = reduce_scatter_mean(hg, "bf16", buckets, c, uneven=True)
         for g0, length, c0 in shard_segments(buckets, n, c, uneven=True):
             mean_global[g0:g0 + length] = comp[c0:c0 + length]
-    for chunk in (2, -1):
+    for chunk in (2 % n, -1):
         size = grz.dp_shard_numel(buckets, n, chunk, flags) if chunk >= 0 else p
         out = torch.full((size,), float("nan"), device=DEV)
         parts = torch.full((npieces,), -1.0, dtype=torch.float64, device=DEV)
@@ -200,8 +217,8 @@ def test_a_plan_of_many_buckets_spans_several_launches():
             else:
                 assert math.isclose(got[i], want_i, rel_tol=1e-13, abs_tol=0.0), (chunk, i)
 
-    # Clipped AdamW on chunk 2's shard, written into two replicas.
-    chunk = 2
+    # Clipped AdamW on one chunk's shard, written into two replicas.
+    chunk = 2 % n
     segs = shard_segments(buckets, n, chunk, uneven=True)
     k = sum(s[1] for s in segs)
     w = rng.standard_normal(k).astype(np.float32) * np.float32(0.02)
