@@ -1004,6 +1004,13 @@ def main():
         out["cpu_baseline"]["host_cpus"] = os.cpu_count()
         out["cpu_baseline"]["affinity_cpus"] = len(os.sched_getaffinity(0))
         out["cpu_baseline"]["parallel"] = parallel
+        # The same analytic bytes per owned parameter as the GPU line, and the
+        # time the oracle would take for the whole step at its sampled rate.
+        per_param = step_bytes / setup["shard"]
+        out["cpu_baseline"]["seconds_per_step"] = setup["shard"] / cb["value"]
+        out["cpu_baseline"]["GBps"] = cb["value"] * per_param / 1e9
+        if isinstance(parallel, dict) and parallel.get("value"):
+            parallel["GBps"] = parallel["value"] * per_param / 1e9
     print(json.dumps(out), flush=True)
 
 
