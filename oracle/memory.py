@@ -6,9 +6,10 @@ and k bytes of optimizer state per parameter (k = 12 for fp32 master, m and
 v); stage 1 divides the optimizer term by N, stage 2 also the gradient term,
 stage 3 also the weight term ("What to implement", item 5, and its tip).
 
-Pins (tests/test_oracle_memory.py): the page's table, 7.5e9 parameters on 64
-GPUs: 120 / 31.4 / 16.6 / 1.875 GB, and 7e9 on 8 GPUs: 112 / 38.5 / 26.25 /
-14 GB (1 GB = 1e9 bytes).
+Pins (tests/test_oracle_plan.py, test_zero_memory_table and
+test_char_gpt_arena_matches_printed_memory): the page's table, 7.5e9
+parameters on 64 GPUs: 120 / 31.4 / 16.6 / 1.875 GB, and 7e9 on 8 GPUs: 112 /
+38.5 / 26.25 / 14 GB (1 GB = 1e9 bytes).
 """
 
 

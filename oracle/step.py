@@ -30,7 +30,9 @@ Readings (the pages name these steps but do not print their formulas):
 
 Pins (tests/test_oracle_step.py): the norm against a closed form (constant
 gradient a over P elements has norm |a|*sqrt(P)) and against
-``torch.nn.utils.clip_grad_norm_``; AdamW against ``torch.optim.AdamW``
+``torch.nn.utils.clip_grad_norm_``; its numpy branch (above FSUM_LIMIT terms)
+against ``math.fsum`` with the limit lowered, and above the limit against the
+closed-form sum of squares of a grid gradient whose every partial sum is exact; AdamW against ``torch.optim.AdamW``
 (``foreach=False``, float64, CPU) over 10 steps and against two closed forms
 (all-zero gradients decay the weights by (1 - lr*wd) per step; at t = 1 the
 update is g / (|g| + eps) up to rounding); bf16 rounding against torch's CPU

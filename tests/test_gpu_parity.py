@@ -212,9 +212,11 @@ def test_results_do_not_depend_on_grid_width():
         assert_bits(o[5], outs[0][5], "fp32 all-gather")
 
 
-def test_cross_n_identity_grid_exact():
+@pytest.mark.parametrize("max_norm", [1e-4, 0.0])
+def test_cross_n_identity_grid_exact(max_norm):
     # Values k * 2^-24 with |k| < 2^13: every sum is exact, so the mean, the
-    # norm and the weights cannot depend on N.
+    # norm and the weights cannot depend on N -- with the clip active and
+    # with it switched off.  The N = 1 run is also the oracle's, bit for bit.
     p, steps = 1 << 16, 3
     rng = np.random.default_rng(21)
     micro = [[(rng.integers(-(1 << 13), 1 << 13, p) * 2.0 ** -24).astype(np.float32)
@@ -222,18 +224,28 @@ def test_cross_n_identity_grid_exact():
     master = master_init(p, device=DEV)
     arenas = {}
     for n in (1, 2, 4, 8):
-        z = grz.Zero1AllRanks([(0, p)], n, master, grz.Hyper(max_norm=1e-4), device=DEV)
-        d = grz.DDPStep([(0, p)], n, master, grz.Hyper(max_norm=1e-4), device=DEV)
+        z = grz.Zero1AllRanks([(0, p)], n, master, grz.Hyper(max_norm=max_norm), device=DEV)
+        d = grz.DDPStep([(0, p)], n, master, grz.Hyper(max_norm=max_norm), device=DEV)
+        states = oracle_states(host(master), [(0, p)], n)
         for t in range(1, steps + 1):
             per = 8 // n
-            grads = [_dev(np.sum(np.stack(micro[t - 1][r * per:(r + 1) * per]), axis=0)
-                          * np.float32(n / 8)) for r in range(n)]
+            hg = [np.sum(np.stack(micro[t - 1][r * per:(r + 1) * per]), axis=0)
+                  * np.float32(n / 8) for r in range(n)]
+            grads = [_dev(g) for g in hg]
             z.step(grads, t)
             d.step(grads, t)
+            if n in (1, 8):
+                ref = zero1_step(hg, "f32", [(0, p)], states, OHyper(max_norm=max_norm), t)
+                states = ref["states"]
         torch.cuda.synchronize()
-        assert z.norm.scale.item() < 1
+        if max_norm > 0:
+            assert z.norm.scale.item() < 1
+        else:
+            assert z.norm.scale.item() == 1.0
         arenas[n] = host(z.replicas[0])
         assert_bits(host(d.replica), arenas[n], f"DDP vs ZeRO-1 at N={n}")
+        if n in (1, 8):
+            assert_bits(arenas[n], ref["arena"], f"weights at N={n} vs the oracle")
     for n in (2, 4, 8):
         assert_bits(arenas[n], arenas[1], f"weights at N={n} vs N=1")
 

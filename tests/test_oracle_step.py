@@ -53,7 +53,10 @@ def test_norm_of_constant_gradient(a, p):
     assert clip_scale(sq, 0.0) == np.float32(1.0)
 
 
-def test_norm_extra_partials_and_large_path():
+def test_norm_with_peer_partials_equals_the_exact_whole_sum():
+    # The fsum branch (at most FSUM_LIMIT terms): the norm of a split gradient,
+    # one part as values and the others as partial sums of squares a peer
+    # computed, equals the norm of the whole; both are the exact sum rounded.
     rng = np.random.default_rng(2)
     g = rng.standard_normal(1000).astype(np.float32)
     whole = grad_sqnorm(g)
@@ -61,6 +64,52 @@ def test_norm_extra_partials_and_large_path():
     assert math.isclose(whole, split, rel_tol=1e-15)
     exact = math.fsum(float(v) * float(v) for v in g)
     assert whole == exact
+
+
+def test_norm_numpy_branch_agrees_with_fsum(monkeypatch):
+    # Above FSUM_LIMIT terms the oracle sums the float64 squares with numpy.
+    # With the limit lowered, that branch runs on a Gaussian gradient plus peer
+    # partials and must agree with the exact sum to float64 summation error
+    # (pairwise summation of 10^5 positive terms: ~1e-15).  Summing fp32
+    # squares, or dropping the peers' partials, misses by ~1e-8 or more.
+    import oracle.step as ostep
+    rng = np.random.default_rng(3)
+    g = (rng.standard_normal(100_000) * 1e-3).astype(np.float32)
+    extra = list(rng.random(7) * 1e-2)
+    exact = math.fsum([float(v) * float(v) for v in g] + extra)
+    monkeypatch.setattr(ostep, "FSUM_LIMIT", 1000)
+
+    def no_fsum(_):
+        raise AssertionError("the numpy branch must not call math.fsum")
+    monkeypatch.setattr(ostep.math, "fsum", no_fsum)
+    got = ostep.grad_sqnorm(g, extra=extra)
+    assert math.isclose(got, exact, rel_tol=1e-13)
+    assert not math.isclose(ostep.grad_sqnorm(g), exact, rel_tol=1e-13)  # extra counts
+
+
+def test_norm_numpy_branch_above_the_limit_closed_form(monkeypatch):
+    # A gradient of more than FSUM_LIMIT values on a grid where every partial
+    # sum of squares is exact in float64, so any order gives the exact value:
+    # g_i = (i mod 4096 - 2048) * 2^-10 (each square is k^2 * 2^-20 with
+    # k^2 <= 2^22, the total below 2^47 units of 2^-20).  The closed form is
+    # the sum of k^2 over the periods, in integers; the peers' partials add
+    # exactly.  Accumulating in fp32, squaring in the wrong place or dropping
+    # terms is off by many units.
+    import oracle.step as ostep
+    p = ostep.FSUM_LIMIT + 3 * 4096 + 17
+    k = (np.arange(p, dtype=np.int64) % 4096) - 2048
+    g = (k * 2.0 ** -10).astype(np.float32)
+    assert np.array_equal(g.astype(np.float64) * 2.0 ** 10, k.astype(np.float64))
+    extra = [0.5, 0.25, 2.0 ** -20]
+    period = sum(j * j for j in range(-2048, 2048))
+    q, r = divmod(p, 4096)
+    units = q * period + sum(j * j for j in range(-2048, -2048 + r))
+    want = units * 2.0 ** -20 + 0.75 + 2.0 ** -20
+
+    def no_fsum(_):
+        raise AssertionError("more than FSUM_LIMIT terms must take the numpy branch")
+    monkeypatch.setattr(ostep.math, "fsum", no_fsum)
+    assert ostep.grad_sqnorm(g, extra=extra) == want
 
 
 def test_clip_matches_torch_clip_grad_norm():
@@ -169,10 +218,12 @@ def test_zero1_equals_ddp(max_norm):
         assert z["scale"] < 1
 
 
-def test_cross_n_identity_on_grid_exact_data():
+@pytest.mark.parametrize("max_norm", [1e-4, 0.0])
+def test_cross_n_identity_on_grid_exact_data(max_norm):
     # "A4", "Overview": the same answer on 1 or 4 GPUs.  On data where every
     # sum is exact (values k * 2^-24, |k| < 2^14) the mean does not depend on
-    # N, so neither do the weights after k steps.
+    # N, so neither do the weights after k steps: with the clip on (factor
+    # below 1) and switched off (max_norm 0, factor 1).
     rng = np.random.default_rng(13)
     p, steps = 1 << 12, 3
     master = (rng.standard_normal(p) * 0.02).astype(np.float32)
@@ -186,10 +237,10 @@ def test_cross_n_identity_on_grid_exact_data():
             per = 8 // n
             grads = [np.sum(np.stack(micro[t - 1][r * per:(r + 1) * per]), axis=0)
                      * np.float32(n / 8) for r in range(n)]
-            out = zero1_step(grads, "f32", buckets, states, Hyper(max_norm=1e-4), t)
+            out = zero1_step(grads, "f32", buckets, states, Hyper(max_norm=max_norm), t)
             states = out["states"]
         arenas[n] = out["arena"]
-        assert out["scale"] < 1
+        assert (out["scale"] < 1) if max_norm > 0 else (out["scale"] == 1)
     for n in (2, 4, 8):
         assert np.array_equal(arenas[n], arenas[1])
 
