@@ -19,6 +19,7 @@ GRZ_F32, GRZ_BF16, GRZ_F64 = 0, 1, 2
  GRZ_OUT_GLOBAL) = (1, 2, 4, 8, 16, 32, 64)
 GRZ_MAX_RANKS = 16
 GRZ_PIECE = 4096
+GRZ_NOALLOC_SCRATCH_BYTES = 65536
 
 # Every symbol include/grz.h declares, with (restype, argtypes).
 _vp, _i, _i64, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
@@ -51,6 +52,7 @@ SIGNATURES = {
                                         _i, _vp, _vp, _vp]),
     "dp_grad_sqnorm_workspace": (ctypes.c_size_t, [_i64]),
     "dp_grad_sqnorm": (_i, [_vp, _i64, _d, _vp, _vp, _vp, _vp]),
+    "dp_grad_sqnorm_noalloc": (_i, [_vp, _i64, _d, _vp, _vp, _vp]),
     "dp_grad_sqnorm_of_workspace": (ctypes.c_size_t, [_i64]),
     "dp_grad_sqnorm_of": (_i, [_vp, _i64, _d, _vp, _vp, _vp, _vp]),
     "zero1_adamw_step": (_i, [_vp, _vp, _vp, _vp, _i64, _vp, ctypes.POINTER(AdamWArgs), _vp,

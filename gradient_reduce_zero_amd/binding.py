@@ -191,6 +191,19 @@ def dp_grad_sqnorm(piece_sqnorm, max_norm, workspace, sqnorm_out, clip_scale_out
                                                  _stream(stream)))
 
 
+def dp_grad_sqnorm_noalloc(piece_sqnorm, max_norm, sqnorm_out, clip_scale_out, npieces=None,
+                           stream=None):
+    """``dp_grad_sqnorm`` with the library's static per-device scratch instead of
+    a workspace (allocates nothing); calls that overlap on one device race."""
+    npieces = piece_sqnorm.numel() if npieces is None else int(npieces)
+    part = _dev(piece_sqnorm, "piece_sqnorm", (torch.float64,), npieces)
+    sq = None if sqnorm_out is None else _dev(sqnorm_out, "sqnorm_out", (torch.float64,), 1)
+    sc = None if clip_scale_out is None else _dev(clip_scale_out, "clip_scale_out",
+                                                   (torch.float32,), 1)
+    check("dp_grad_sqnorm_noalloc",
+          lib().dp_grad_sqnorm_noalloc(part, npieces, float(max_norm), sq, sc, _stream(stream)))
+
+
 def dp_grad_sqnorm_of_workspace(n):
     return int(lib().dp_grad_sqnorm_of_workspace(int(n)))
 

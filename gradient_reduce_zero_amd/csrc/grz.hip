@@ -37,6 +37,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "grz.h"
@@ -1479,6 +1480,52 @@ int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
                      sqnorm_out, clip_scale_out);
   if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
   return GRZ_OK;
+}
+
+}  // extern "C"
+
+// The middle levels of the norm tree for callers that cannot allocate: one
+// array per device, held until the process ends.  Host code never passes the
+// array's own name to a kernel (on the host it is only a stand-in for the
+// symbol); it looks the device address up once per device and uses that.
+static __device__ __align__(256) double scratch[GRZ_NOALLOC_SCRATCH_BYTES / sizeof(double)];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];  // device address of `scratch`, per device
+
+// The address of the current device's `scratch`, looked up on the first call
+// on that device (with it current) and kept.
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GRZ_EHIP;
+  if (dev < 0 || dev >= kScratchDevices) return GRZ_ERANGE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return GRZ_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GRZ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dp_grad_sqnorm_noalloc(const double* piece_sqnorm, int64_t npieces, double max_norm,
+                           double* sqnorm_out, float* clip_scale_out, hipStream_t stream) {
+  if (npieces < 0) return GRZ_EINVAL;
+  if (dp_grad_sqnorm_workspace(npieces) > GRZ_NOALLOC_SCRATCH_BYTES) return GRZ_ERANGE;
+  void* ws = nullptr;
+  const int st = scratch_for_current_device(&ws);
+  if (st != GRZ_OK) return st;
+  return dp_grad_sqnorm(piece_sqnorm, npieces, max_norm, ws, sqnorm_out, clip_scale_out,
+                        stream);
 }
 
 size_t dp_grad_sqnorm_of_workspace(int64_t n) {

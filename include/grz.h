@@ -28,9 +28,9 @@
  *
  *  - Memory.  Every pointer named "device" is HIP device memory owned by the
  *    caller; the library allocates nothing and keeps no state between calls
- *    (apart from the knobs grz_set_max_blocks and grz_set_spin_limit), so
- *    concurrent calls on different streams are safe when they touch
- *    disjoint buffers.  Buffers must stay alive until the stream has run the
+ *    (apart from the knobs grz_set_max_blocks and grz_set_spin_limit, and the
+ *    static per-device scratch of dp_grad_sqnorm_noalloc), so concurrent
+ *    calls on different streams are safe when they touch disjoint buffers.  Buffers must stay alive until the stream has run the
  *    enqueued work.  Host arrays (pointer tables, bucket lists, argument
  *    structs) are read during the call only.
  *  - Streams.  Work is enqueued on `stream` (0 = the null stream).  No entry
@@ -260,6 +260,25 @@ size_t dp_grad_sqnorm_workspace(int64_t npieces);
 int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
                    void* workspace, double* sqnorm_out, float* clip_scale_out,
                    hipStream_t stream);
+
+/*
+ * dp_grad_sqnorm without a workspace argument and without allocating, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The tree's middle
+ * levels go to a static array of GRZ_NOALLOC_SCRATCH_BYTES per device, which
+ * the library holds until the process ends; its device address is looked up
+ * on the first call on each device (the device current when the call is made,
+ * which must be the stream's).  Same arguments, results (bit for bit) and
+ * errors as dp_grad_sqnorm, plus GRZ_ERANGE when
+ * dp_grad_sqnorm_workspace(npieces) exceeds GRZ_NOALLOC_SCRATCH_BYTES (more
+ * than 33,546,240 pieces, about 1.4e11 gradient elements).  Nothing needs
+ * clearing between calls: each call writes every scratch value it reads.  All
+ * calls on one device share the array, so calls that overlap on one device
+ * (different streams, or different host threads) race: order them.
+ */
+#define GRZ_NOALLOC_SCRATCH_BYTES 65536
+int dp_grad_sqnorm_noalloc(const double* piece_sqnorm, int64_t npieces, double max_norm,
+                           double* sqnorm_out, float* clip_scale_out, hipStream_t stream);
 
 /* Bytes of workspace dp_grad_sqnorm_of needs for `n` gradient elements. */
 size_t dp_grad_sqnorm_of_workspace(int64_t n);
