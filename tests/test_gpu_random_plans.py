@@ -45,15 +45,15 @@ def _draw(seed):
     return n, kind, even, list(zip(offs, lengths)), pos, chunk, mode
 
 
-def _pieces_of(mean_global, buckets, n, chunks):
+def _pieces_of(mean_global, buckets, n, chunks, bucket_ids=None):
     """Exact sum of squares per piece, in the plan's piece numbering; None for
-    pieces of chunks not reduced."""
+    pieces of chunks not reduced (and of buckets outside ``bucket_ids``)."""
     out = []
-    for off, length in buckets:
+    for b, (off, length) in enumerate(buckets):
         for c, (lo, hi) in enumerate(chunk_bounds(length, n)):
             for p0 in range(lo, hi, PIECE):
                 p1 = min(p0 + PIECE, hi)
-                if c in chunks:
+                if c in chunks and (bucket_ids is None or b in bucket_ids):
                     vals = mean_global[off + p0:off + p1].astype(np.float64)
                     out.append(math.fsum((vals * vals).tolist()))
                 else:
@@ -278,9 +278,12 @@ def _every_entry_point_on(n, lengths, rng, seed):
 def test_reduce_modes_on_a_random_plan(seed):
     # The reduce's other modes on random plans: the sum instead of the mean,
     # the bf16 wire (bf16 gradients), the token-weighted mean (totals that are
-    # and are not powers of two), shard-compact inputs, alone and together.
-    # Output bit-exact against the oracle; the piece sums against the exact
-    # sum of squares of the oracle's output.
+    # and are not powers of two), shard-compact inputs, and a bucket range
+    # whose inputs hold only that range (GRZ_IN_RANGE, how a ZeRO-2 backward
+    # feeds the reduce from a staging buffer), alone and together.  Output
+    # bit-exact against the oracle's reduce of the whole arenas at the range's
+    # positions and untouched elsewhere; the piece sums against the exact sum
+    # of squares of the oracle's output, other pieces untouched.
     rng = np.random.default_rng(8000 + seed)
     n, kind, even, buckets, p, chunk, mode = _draw(3000 + seed)
     flags = 0 if even else grz.GRZ_UNEVEN
@@ -309,6 +312,17 @@ def test_reduce_modes_on_a_random_plan(seed):
         hin = [host(g) for g in inputs]
     else:
         inputs, hin = grads, hg
+    nb = len(buckets)
+    brange, in_range = None, set(range(nb))
+    if not compact and rng.integers(0, 2):
+        first = int(rng.integers(0, nb))
+        brange = (first, int(rng.integers(1, nb - first + 1)))
+        in_range = set(range(first, first + brange[1]))
+        sel = [buckets[b] for b in sorted(in_range) if buckets[b][1] > 0]
+        lo = min((o for o, _ in sel), default=0)
+        hi = max((o + l for o, l in sel), default=0)
+        inputs = [g[lo:max(hi, lo + 1)].contiguous() for g in grads]  # the range only
+        flags |= grz.GRZ_IN_RANGE
     acc = np.float64 if kind == "f64" else np.float32
     out_t = torch.float64 if kind == "f64" else torch.float32
     npieces = grz.dp_piece_count(buckets, n, flags)
@@ -317,23 +331,28 @@ def test_reduce_modes_on_a_random_plan(seed):
     out = torch.full((max(shard if mode == "compact" else p, 1),), float("nan"), dtype=out_t,
                      device=DEV)
     grz.dp_reduce_scatter_mean(inputs, buckets, chunk, out, parts, flags=flags,
-                               token_counts=counts)
+                               token_counts=counts, bucket_range=brange)
     torch.cuda.synchronize()
     kw = dict(average=not flags & grz.GRZ_SUM, uneven=not even, wire=wire, token_counts=counts)
     out_global = np.full(p, np.nan, acc)
     chunks = range(n) if chunk < 0 else [chunk]
     for c in chunks:
         comp = reduce_scatter_mean(hg, kind, buckets, c, **kw)
-        for g0, length, c0 in shard_segments(buckets, n, c, uneven=not even):
-            out_global[g0:g0 + length] = comp[c0:c0 + length]
-    what = f"seed {seed} (n {n}, {kind}, wire {wire}, counts {counts}, flags {flags})"
+        for b, (g0, length, c0) in enumerate(shard_segments(buckets, n, c, uneven=not even)):
+            if b in in_range:
+                out_global[g0:g0 + length] = comp[c0:c0 + length]
+    what = (f"seed {seed} (n {n}, {kind}, wire {wire}, counts {counts}, flags {flags}, "
+            f"range {brange})")
     if mode == "compact":
         want = reduce_scatter_mean(hin, kind, buckets, chunk, compact_inputs=compact, **kw)
+        for b, (_, length, c0) in enumerate(shard_segments(buckets, n, chunk, uneven=not even)):
+            if b not in in_range:
+                want[c0:c0 + length] = np.nan  # not reduced: left as it was
         assert_bits(host(out)[:shard], want, what)
     else:
         assert_bits(host(out)[:p], out_global, what)
     got = host(parts)
-    for i, want_i in enumerate(_pieces_of(out_global, buckets, n, set(chunks))):
+    for i, want_i in enumerate(_pieces_of(out_global, buckets, n, set(chunks), in_range)):
         if want_i is None:
             assert got[i] == -1.0, f"{what}: piece {i} of a chunk not reduced was written"
         else:
