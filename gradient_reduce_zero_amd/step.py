@@ -410,9 +410,11 @@ class CapturedStep:
     a one-thread kernel at the head of the graph copies the replay's row to
     the slot the optimizer reads (``GRZ_ARGS_DEVICE``).  ``enqueue(args,
     stream)`` must enqueue the step's kernels with ``args`` as their scalars;
-    every buffer it touches keeps its address for the graph's lifetime.  Past
-    the last row the last row is reused.  Replays produce the bits of the
-    eager steps.
+    every buffer it touches keeps its address for the graph's lifetime.
+    ``replay`` counts replays on the host and raises once the table's
+    ``count`` steps are used (a further replay would repeat the last row's
+    learning rate and bias corrections); capture again with a larger
+    ``count`` to run longer.  Replays produce the bits of the eager steps.
     """
 
     def __init__(self, enqueue, hyper, first_t, count, device="cuda"):
@@ -422,6 +424,8 @@ class CapturedStep:
             rows.append([s["lr"], s["beta1"], s["beta2"], s["eps"], s["weight_decay"],
                          s["bias_corr1"], s["bias_corr2"]])
         self.table = torch.tensor(rows, dtype=torch.float32, device=device)
+        self.count = count
+        self.replays = 0
         self.counter = torch.zeros(1, dtype=torch.int64, device=device)
         self.current = torch.zeros(B.ARGS_FIELDS, dtype=torch.float32, device=device)
         self.graph = torch.cuda.CUDAGraph()
@@ -431,4 +435,9 @@ class CapturedStep:
             enqueue(self.current, s)
 
     def replay(self):
+        """Run the next step; RuntimeError (nothing enqueued) past the table."""
+        if self.replays >= self.count:
+            raise RuntimeError(f"the captured step holds the scalars of {self.count} steps, "
+                               "all replayed; capture it again with a larger count")
         self.graph.replay()
+        self.replays += 1
