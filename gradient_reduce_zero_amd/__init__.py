@@ -16,7 +16,8 @@ from .binding import (adamw_args, dp_all_gather, dp_chunk_range, dp_grad_sqnorm,
                       dp_grad_sqnorm_of_workspace, dp_grad_sqnorm_workspace,
                       dp_piece_count, dp_piece_offset, dp_reduce_scatter_mean,
                       dp_ring_chunk_owner, dp_ring_owned_chunk, dp_shard_numel,
-                      fused_timed_out, grz_set_max_blocks, grz_set_spin_limit,
+                      fused_clear, fused_set_spin_limit, fused_timed_out,
+                      grz_set_max_blocks,
                       grz_step_args_next, zero1_adamw_gather, zero1_adamw_step,
                       zero1_all_gather, zero1_fused_capacity, zero1_fused_step,
                       zero1_fused_workspace)

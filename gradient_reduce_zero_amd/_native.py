@@ -62,7 +62,6 @@ SIGNATURES = {
     "zero1_all_gather": (_i, [_pp, _i, _BP, _i, _i, _pp, _i, _vp]),
     "dp_all_gather": (_i, [_pp, _i, _i, _BP, _i, _i, _pp, _i, _vp]),
     "grz_step_args_next": (_i, [_vp, _i64, _vp, _vp, _vp]),
-    "grz_set_spin_limit": (_i, [ctypes.c_uint]),
     "zero1_fused_workspace": (ctypes.c_size_t, [_i64]),
     "zero1_fused_capacity": (_i64, [_i, _i]),
     "zero1_fused_step": (_i, [_pp, _i, _i, _BP, _i, _i, _i, _vp, _vp, _vp,

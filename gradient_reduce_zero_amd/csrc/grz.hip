@@ -50,14 +50,15 @@ constexpr int kReduceFan = 4096;       // values one block folds in the norm tre
 
 static_assert(GRZ_PIECE % (kThreads * 8) == 0, "piece shape");
 
-// Grid width cap of the grid-stride kernels.  Measured on MI355X: one
-// workgroup per tile (no cap in practice) streams fastest.
-// (Both knobs are atomics: a caller may set one while another thread launches.)
-std::atomic<int> g_max_blocks{1 << 30};
+// Grid width cap of the grid-stride kernels, per calling host thread (so that
+// callers on different threads never see each other's setting).  Measured on
+// MI355X: one workgroup per tile (no cap in practice) streams fastest.
+thread_local int g_max_blocks = 1 << 30;
 
-// Polls of a grid-barrier wait before it gives up (fused step).  Each poll
-// sleeps a few hundred cycles, so the default bounds a wait at a few seconds.
-std::atomic<unsigned> g_spin_limit{1u << 22};
+// Polls of a grid-barrier wait before it gives up (fused step) when the
+// workspace does not set its own limit.  Each poll sleeps a few hundred
+// cycles, so this bounds a wait at a few seconds.
+constexpr unsigned kDefaultSpinLimit = 1u << 22;
 
 // One contiguous run of work: `len` elements read at `src` and written at
 // `dst`, whose first tile is `tile0` of the launch and first norm piece is
@@ -796,7 +797,6 @@ struct FusedArgs {
   int nrep;
   int nsegs;
   int pow2;
-  unsigned spin_limit;
   float lr, b1, b2, eps, wd, bc1, bc2;
   FSeg seg[kFusedSegs];
 };
@@ -810,22 +810,27 @@ struct FusedArgs {
 // group resets the group count and counts the group in at the top; the last
 // group resets the top count and advances every group's generation
 // (release).  The others poll their group's generation and then take a
-// device-scope acquire fence.  The wait gives up after `spin_limit` polls and
-// raises the time-out word, so a grid that is not resident at once ends with
-// a flag instead of waiting forever.  Counts are back at zero after every
-// completed barrier, so consecutive launches reuse the words uncleared.
+// device-scope acquire fence.  The wait gives up after the workspace's poll
+// limit (word 3; 0 means kDefaultSpinLimit), raises the time-out word and
+// returns false, so a grid that is not resident at once ends with a flag
+// instead of waiting forever.  Counts are back at zero after every completed
+// barrier, so consecutive launches reuse the words uncleared; after a give-up
+// they are not, and the workspace must be cleared.
 //
 // Layout of `sync` (32-bit words, 256 bytes per block): block 0 word 0 the
-// top count, word 2 the time-out flag; block g + 1 words 0 and 1 the count and
-// generation of group g.
+// top count, word 2 the time-out flag, word 3 the poll limit; block g + 1
+// words 0 and 1 the count and generation of group g.
 constexpr unsigned kBarrierGroups = 32;
 constexpr unsigned kSyncStride = 64;  // words between blocks
 constexpr size_t kSyncBytes = (kBarrierGroups + 1) * kSyncStride * sizeof(unsigned);
 
-__device__ __forceinline__ void grid_barrier(unsigned* sync, unsigned nblocks,
-                                             unsigned spin_limit) {
+// True when every workgroup arrived; false (the same in every thread of the
+// workgroup) when this workgroup's wait gave up.
+__device__ __forceinline__ bool grid_barrier(unsigned* sync, unsigned nblocks) {
+  __shared__ int gave_up;
   __syncthreads();
   if (threadIdx.x == 0) {
+    gave_up = 0;
     const unsigned ng = nblocks < kBarrierGroups ? nblocks : kBarrierGroups;
     const unsigned g = blockIdx.x % ng;
     const unsigned gsize = nblocks / ng + (g < nblocks % ng ? 1u : 0u);
@@ -846,11 +851,14 @@ __device__ __forceinline__ void grid_barrier(unsigned* sync, unsigned nblocks,
         __hip_atomic_fetch_add(sync + kSyncStride * (h + 1) + 1, 1u, __ATOMIC_RELEASE,
                                __HIP_MEMORY_SCOPE_AGENT);
     } else {
+      const unsigned set = sync[3];
+      const unsigned limit = set != 0 ? set : kDefaultSpinLimit;
       unsigned polls = 0;
       while (__hip_atomic_load(gw + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
         __builtin_amdgcn_s_sleep(4);
-        if (++polls >= spin_limit) {
+        if (++polls >= limit) {
           __hip_atomic_store(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          gave_up = 1;
           break;
         }
       }
@@ -858,6 +866,7 @@ __device__ __forceinline__ void grid_barrier(unsigned* sync, unsigned nblocks,
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
+  return gave_up == 0;
 }
 
 // At most 128 VGPRs, so that 4 waves per SIMD (4 workgroups per CU) fit: the
@@ -914,7 +923,10 @@ void fused_step_kernel(const FusedArgs<TIn> a) {
       if (lane == 0) a.partials[s.piece0 + piece] = tot;
     }
   }
-  grid_barrier(a.sync, gridDim.x, a.spin_limit);
+  // A workgroup whose wait gave up stops here: it has not seen every piece
+  // sum, so it writes nothing more (its tiles keep their old state) and
+  // arrives at no later barrier; the flag in the workspace says so.
+  if (!grid_barrier(a.sync, gridDim.x)) return;
 
   // Norm: the tree of dp_grad_sqnorm (at most one level below the final fold).
   double sqnorm;
@@ -924,7 +936,7 @@ void fused_step_kernel(const FusedArgs<TIn> a) {
       const double t = fan_block_sum(a.partials, a.npieces, b * kReduceFan, lds);
       if (lane == 0) a.level[b] = t;
     }
-    grid_barrier(a.sync, gridDim.x, a.spin_limit);
+    if (!grid_barrier(a.sync, gridDim.x)) return;
     sqnorm = fan_block_sum(a.level, nl, 0, lds);
   } else {
     sqnorm = fan_block_sum(a.partials, a.npieces, 0, lds);
@@ -1079,7 +1091,7 @@ std::vector<PlanSeg> plan_segments(const grz_bucket* buckets, int nbuckets, int 
 // bits).  Every such kernel loops over its tiles, so any width gives the same
 // results.
 int64_t grid_for(int64_t units, int block) {
-  const int64_t cap = g_max_blocks.load(std::memory_order_relaxed);
+  const int64_t cap = g_max_blocks;
   const int64_t hw = static_cast<int64_t>(UINT32_MAX) / block;
   int64_t grid = units < cap ? units : cap;
   return grid < hw ? grid : hw;
@@ -1294,7 +1306,7 @@ const char* grz_strerror(int status) {
 
 int grz_set_max_blocks(int blocks) {
   if (blocks < 1 || blocks > (1 << 30)) return GRZ_EINVAL;
-  g_max_blocks.store(blocks, std::memory_order_relaxed);
+  g_max_blocks = blocks;
   return GRZ_OK;
 }
 
@@ -1670,12 +1682,6 @@ int dp_all_gather(const void* const* shards, int nranks, int dtype, const grz_bu
                       stream);
 }
 
-int grz_set_spin_limit(unsigned polls) {
-  if (polls < 1) return GRZ_EINVAL;
-  g_spin_limit.store(polls, std::memory_order_relaxed);
-  return GRZ_OK;
-}
-
 size_t zero1_fused_workspace(int64_t npieces) {
   const int64_t nl = npieces > kReduceFan ? ceil_div(npieces, kReduceFan) : 0;
   return kSyncBytes + static_cast<size_t>(nl) * sizeof(double);
@@ -1788,7 +1794,6 @@ int fused_launch(const void* kernel, const void* const* rank_grads, int nranks,
   a.nranks = nranks;
   a.nrep = nreplicas;
   a.nsegs = nsegs;
-  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   if (flags & GRZ_ARGS_DEVICE) {
     a.dargs = args;
   } else {

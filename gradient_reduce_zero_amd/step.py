@@ -69,6 +69,17 @@ def _fused_workspace(npieces, device):
     return torch.zeros(B.zero1_fused_workspace(npieces), dtype=torch.uint8, device=device)
 
 
+def _check_fused(workspace):
+    """Raise if a grid-wide wait of the last one-launch step gave up, after
+    clearing the workspace's counters so that the next step can run.  Reads a
+    device word, so it waits for the stream's work."""
+    if workspace is not None and B.fused_timed_out(workspace):
+        B.fused_clear(workspace)
+        raise RuntimeError("a grid-wide wait of the one-launch step gave up: the tiles of the "
+                           "workgroups that gave up kept their previous state (the others were "
+                           "updated); the workspace has been cleared")
+
+
 class Zero1AllRanks:
     """ZeRO-1 step of N simulated ranks over a bucket plan."""
 
@@ -133,6 +144,11 @@ class DDPStep:
         self.workspace = _fused_workspace(self.norm.npieces, device) if fused else None
         self.replicas = [w.to(torch.bfloat16) for _ in range(nreplicas)]
         self.replica = self.replicas[0]
+
+    def check_fused(self):
+        """After the stream's work, with ``fused=True``: raise if a wait of the
+        last step gave up (see ``zero1_fused_step``)."""
+        _check_fused(self.workspace)
 
     def step(self, rank_grads, t, stream=None, token_counts=None):
         if self.fused:
@@ -212,6 +228,11 @@ class Zero1OneRank:
 
     def gather(self, peer_shards, stream=None):
         B.zero1_all_gather(peer_shards, self.buckets, [self.arena], stream=stream)
+
+    def check_fused(self):
+        """After the stream's work, with ``fused=True``: raise if a wait of the
+        last step gave up (see ``zero1_fused_step``)."""
+        _check_fused(self.workspace)
 
     def fused_update(self, incoming, args, stream=None):
         """reduce + update as one launch (the mean never leaves the registers)."""

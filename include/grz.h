@@ -28,9 +28,10 @@
  *
  *  - Memory.  Every pointer named "device" is HIP device memory owned by the
  *    caller; the library allocates nothing and keeps no state between calls
- *    (apart from the knobs grz_set_max_blocks and grz_set_spin_limit, and the
- *    static per-device scratch of dp_grad_sqnorm_noalloc), so concurrent
- *    calls on different streams are safe when they touch disjoint buffers.  Buffers must stay alive until the stream has run the
+ *    (apart from the per-thread grid cap of grz_set_max_blocks, which never
+ *    changes a result, and the static per-device scratch of
+ *    dp_grad_sqnorm_noalloc), so concurrent calls on different streams are
+ *    safe when they touch disjoint buffers.  Buffers must stay alive until the stream has run the
  *    enqueued work.  Host arrays (pointer tables, bucket lists, argument
  *    structs) are read during the call only.
  *  - Streams.  Work is enqueued on `stream` (0 = the null stream).  No entry
@@ -131,7 +132,9 @@ int grz_version(void);
  * 256 threads for the reduce, 512 and 64 for the all-gather, 256 and 64 for
  * the optimizer).
  * It changes speed only; the piece layout, the fold order and the norm tree,
- * hence every result bit, do not depend on it.  Process-wide; GRZ_EINVAL
+ * hence every result bit, do not depend on it.  It applies to the calls the
+ * calling host thread makes afterwards (each thread has its own value,
+ * starting at 2^30), so callers on other threads never see it.  GRZ_EINVAL
  * outside 1..2^30. */
 int grz_set_max_blocks(int blocks);
 
@@ -381,12 +384,6 @@ int dp_all_gather(const void* const* shards, int nranks, int dtype, const grz_bu
                   int nbuckets, int flags, void* const* replicas, int nreplicas,
                   hipStream_t stream);
 
-/*
- * Polls a grid-wide wait of zero1_fused_step makes before it gives up (>= 1;
- * default 2^22, a few seconds).  Process-wide, like grz_set_max_blocks.
- */
-int grz_set_spin_limit(unsigned polls);
-
 /* Bytes of workspace zero1_fused_step needs for a plan of `npieces` pieces. */
 size_t zero1_fused_workspace(int64_t npieces);
 
@@ -431,11 +428,18 @@ int64_t zero1_fused_capacity(int nranks, int dtype);
  * workspace  device, zero1_fused_workspace(npieces) bytes, 8-byte aligned,
  *            ZEROED before its first use.  Its first 8448 bytes are the grid
  *            barrier's counters; the 32-bit word at byte 8 is its time-out
- *            flag.  A completed call leaves the counters at zero, so the
- *            workspace is reused without clearing.  A non-zero flag means a
- *            wait gave up (grz_set_spin_limit): that call's results are
- *            invalid and the workspace must be zeroed again.  Calls that
- *            share a workspace must not overlap.
+ *            flag, and the 32-bit word at byte 12 the number of polls a wait
+ *            makes before it gives up (0, as zeroed: 2^22, a few seconds; the
+ *            caller may set it before the launch).  A completed call leaves
+ *            the counters at zero, so the workspace is reused without
+ *            clearing.  A non-zero flag means a wait gave up: a workgroup
+ *            whose wait gave up writes nothing after it (its tiles of master,
+ *            m, v, the replicas and the mean keep their previous values, and
+ *            it stores no norm), so each tile holds either its previous state
+ *            or its correct update; the call's result as a whole is then
+ *            incomplete, and the counters must be zeroed again (the poll
+ *            limit word may be kept) before the next call.  Calls that share
+ *            a workspace must not overlap.
  * sqnorm_out, clip_scale_out  device scalars as for dp_grad_sqnorm, or NULL.
  * mean_out   device fp32 copy of the mean (as dp_reduce_scatter_mean writes
  *            it), or NULL.

@@ -191,7 +191,22 @@ static void argument_errors(void) {
                          parts, fws, NULL, NULL, NULL, NULL) == GRZ_EALIGN, "misaligned master");
   CHECK(zero1_fused_workspace(4097) > zero1_fused_workspace(4096), "level sums");
   CHECK(zero1_fused_capacity(0, GRZ_BF16) == -GRZ_EINVAL, "capacity N=0");
-  CHECK(grz_set_spin_limit(0) == GRZ_EINVAL, "spin limit");
+  /* Signatures that differ from a bare "void" helper or a workspace-free
+   * norm: dp_chunk_range reports bad arguments, dp_grad_sqnorm takes a
+   * workspace sized by dp_grad_sqnorm_workspace, and its no-allocation form
+   * refuses a tree beyond its static scratch before touching a device. */
+  int64_t o = 0, c = 0;
+  CHECK(dp_chunk_range(64, 3, 3, &o, &c) == GRZ_EINVAL, "chunk index N");
+  CHECK(dp_chunk_range(-1, 3, 0, &o, &c) == GRZ_EINVAL, "negative length");
+  CHECK(dp_chunk_range(64, 3, 0, NULL, &c) == GRZ_EINVAL, "null offset");
+  CHECK(dp_grad_sqnorm_workspace(4096) == 0, "one block needs no workspace");
+  CHECK(dp_grad_sqnorm_workspace(4097) == 2 * sizeof(double), "two level sums");
+  CHECK(dp_grad_sqnorm_workspace((int64_t)8190 * 4096) == GRZ_NOALLOC_SCRATCH_BYTES,
+        "largest tree the static scratch holds");
+  CHECK(dp_grad_sqnorm_noalloc((double*)0x700000, (int64_t)8190 * 4096 + 1, 1.0,
+                               (double*)0x600000, NULL, NULL) == GRZ_ERANGE, "noalloc range");
+  CHECK(dp_grad_sqnorm_noalloc((double*)0x700000, -1, 1.0, (double*)0x600000, NULL, NULL) ==
+        GRZ_EINVAL, "noalloc count");
   int64_t* ctr = (int64_t*)0xC00000;
   grz_adamw_args* table = (grz_adamw_args*)0xD00000;
   CHECK(grz_step_args_next(NULL, 4, ctr, table, NULL) == GRZ_EINVAL, "null table");

@@ -169,7 +169,6 @@ def test_fused_step_refusals_before_any_launch():
         assert call(flags=flags) == N.GRZ_EINVAL
     assert call(nranks=17) == N.GRZ_EINVAL
     assert call(master=None) == N.GRZ_EINVAL
-    assert lib.grz_set_spin_limit(0) == N.GRZ_EINVAL
     assert lib.zero1_fused_capacity(0, N.GRZ_BF16) == -N.GRZ_EINVAL
     assert lib.zero1_fused_capacity(2, N.GRZ_F64) == -N.GRZ_EINVAL
 

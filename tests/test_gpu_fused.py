@@ -254,33 +254,58 @@ def test_fused_refuses_what_it_cannot_hold():
     assert not grz.fused_timed_out(ws)
 
 
-def test_fused_wait_that_gives_up_raises_the_flag():
-    # A spin limit of one poll makes every workgroup that has to wait give up
-    # at once: the call still ends (every wait is bounded), the flag is raised,
-    # and after the workspace is zeroed the next call is exact again.
+def test_fused_wait_that_gives_up_writes_nothing_and_is_reported():
+    # A poll limit of one makes every workgroup that has to wait give up at
+    # once.  The call still ends (every wait is bounded) and the flag is up.
+    # A workgroup that gave up writes nothing after its wait, so every
+    # 4096-element piece of the shard holds either its old state or the
+    # correct update (the three-kernel path's), never anything else; the
+    # step's check reports the give-up and clears the workspace, keeping its
+    # poll limit.  Restarted from the same state with the default limit, the
+    # next call is exact again.
     a = arena("char_gpt")
     p, n, rank = a.numel, 8, 5
     inp, three, one = _one_rank_pair([(0, p)], p, n, rank)
-    try:
-        grz.grz_set_spin_limit(1)
-        one.step(inp["incoming"], inp["peer_shards"], 1)
-        torch.cuda.synchronize()
-    finally:
-        grz.grz_set_spin_limit(1 << 22)
+    three.step(inp["incoming"], inp["peer_shards"], 1)
+    old = [host(x) for x in one.state]
+    lo = one.chunk * one.state[0].numel()
+    old_arena = host(one.arena[lo:lo + one.state[0].numel()])
+    grz.fused_set_spin_limit(one.workspace, 1)
+    one.step(inp["incoming"], inp["peer_shards"], 1)
+    torch.cuda.synchronize()
     assert grz.fused_timed_out(one.workspace)
-    # Start again from the same state: zero the workspace, reset the master.
-    one.workspace.zero_()
+    with pytest.raises(RuntimeError, match="gave up"):
+        one.check_fused()
+    assert not grz.fused_timed_out(one.workspace)
+    words = one.workspace.view(torch.int32)
+    assert int(words[3].item()) == 1 and int(words.abs().sum().item()) == 1
+    new = [host(x) for x in three.state]
+    got = [host(x) for x in one.state]
+    shard = old[0].size
+    updated = 0
+    for k0 in range(0, shard, grz.GRZ_PIECE):
+        sl = slice(k0, min(k0 + grz.GRZ_PIECE, shard))
+        same_old = all(np.array_equal(g[sl].view(np.uint32), o[sl].view(np.uint32))
+                       for g, o in zip(got, old))
+        same_new = all(np.array_equal(g[sl].view(np.uint32), w[sl].view(np.uint32))
+                       for g, w in zip(got, new))
+        assert same_old or same_new, f"piece at {k0}: neither its old state nor its update"
+        want_arena = host(three.arena[lo:lo + shard])[sl] if same_new else old_arena[sl]
+        assert np.array_equal(host(one.arena[lo:lo + shard])[sl], want_arena), k0
+        updated += same_new and not same_old
+    print(f"{updated} of {-(-shard // grz.GRZ_PIECE)} pieces updated before the give-up")
+    # Start again from the same state with the default poll limit.
+    grz.fused_set_spin_limit(one.workspace, 0)
     one.state[0].copy_(inp["shard_master"])
     one.state[1].zero_()
     one.state[2].zero_()
     one.norm.partials.copy_(inp["partials"])
-    three.step(inp["incoming"], inp["peer_shards"], 1)
     one.step(inp["incoming"], inp["peer_shards"], 1)
     torch.cuda.synchronize()
-    assert not grz.fused_timed_out(one.workspace)
+    one.check_fused()
     for k in range(3):
-        _same(one.state[k], three.state[k], f"after the reset: state {k}")
-    _same(one.arena, three.arena, "after the reset: arena")
+        _same(one.state[k], three.state[k], f"after the restart: state {k}")
+    _same(one.arena, three.arena, "after the restart: arena")
 
 
 def test_fused_sixteen_ranks_equals_three_kernels():
