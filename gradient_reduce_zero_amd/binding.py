@@ -249,6 +249,15 @@ def zero1_adamw_step(master, m, v, mean_grad, clip_scale, args, bf16_out=None, n
 ARGS_FIELDS = 7  # floats in grz_adamw_args
 
 
+def _device_args(args):
+    """(pointer, True) for step scalars in device memory (a float32 tensor of
+    7 values), (byref, False) for host ``AdamWArgs``."""
+    if isinstance(args, torch.Tensor):
+        return ctypes.cast(_dev(args, "args", (torch.float32,), ARGS_FIELDS),
+                           ctypes.POINTER(AdamWArgs)), True
+    return ctypes.byref(args), False
+
+
 def zero1_adamw_gather(master, m, v, mean_grad, buckets, nranks, chunk, clip_scale, args,
                        replicas, flags=0, stream=None):
     """Clipped AdamW on the shard of ``chunk`` with the bf16 all-gather write fused in.
@@ -264,12 +273,9 @@ def zero1_adamw_gather(master, m, v, mean_grad, buckets, nranks, chunk, clip_sca
     reps = (ctypes.c_void_p * max(len(replicas), 1))(
         *[_dev(r, f"replicas[{i}]", _BF16_LIKE, ext).value for i, r in enumerate(replicas)])
     arr, nb = _bucket_array(buckets)
-    if isinstance(args, torch.Tensor):
-        a = ctypes.cast(_dev(args, "args", (torch.float32,), ARGS_FIELDS),
-                        ctypes.POINTER(AdamWArgs))
+    a, on_device = _device_args(args)
+    if on_device:
         flags |= N.GRZ_ARGS_DEVICE
-    else:
-        a = ctypes.byref(args)
     check("zero1_adamw_gather",
           lib().zero1_adamw_gather(w, mm, vv, g, arr, nb, nranks, chunk, flags, sc, a, reps,
                                    len(replicas), _stream(stream)))
@@ -392,11 +398,9 @@ def zero1_fused_step(rank_grads, buckets, chunk, master, m, v, args, max_norm, r
     reps = (ctypes.c_void_p * max(len(replicas), 1))(
         *[_dev(r, f"replicas[{i}]", _BF16_LIKE, ext).value for i, r in enumerate(replicas)])
     arr, nb = _bucket_array(buckets)
-    if isinstance(args, torch.Tensor):
-        a = ctypes.cast(_dev(args, "args", f32, ARGS_FIELDS), ctypes.POINTER(AdamWArgs))
+    a, on_device = _device_args(args)
+    if on_device:
         flags |= N.GRZ_ARGS_DEVICE
-    else:
-        a = ctypes.byref(args)
     check("zero1_fused_step",
           lib().zero1_fused_step(ptrs, n, kind, arr, nb, chunk, flags, w, mm, vv, a,
                                  float(max_norm), reps, len(replicas), part, ws, sq, sc, mo,

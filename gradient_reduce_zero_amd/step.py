@@ -429,8 +429,10 @@ class CapturedStep:
     step, so they live in a device table (rows for steps ``first_t`` ..
     ``first_t + count - 1``, filled once on the host with ``step_scalars``);
     a one-thread kernel at the head of the graph copies the replay's row to
-    the slot the optimizer reads (``GRZ_ARGS_DEVICE``).  ``enqueue(args,
-    stream)`` must enqueue the step's kernels with ``args`` as their scalars;
+    the slot the optimizer reads (``GRZ_ARGS_DEVICE``).  (Run on a branch of
+    the graph beside the step's first kernels instead, it measured slower:
+    the join costs more than the kernel.)  ``enqueue(args, stream)`` must
+    enqueue the step's kernels with ``args`` as their scalars;
     every buffer it touches keeps its address for the graph's lifetime.
     ``replay`` counts replays on the host and raises once the table's
     ``count`` steps are used (a further replay would repeat the last row's

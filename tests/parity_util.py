@@ -86,3 +86,38 @@ def oracle_mean_at(contribs_at, chunk_ids, kind, average=True):
         sel = chunk_ids == c
         out[sel] = chunk_mean([widen(a[sel], kind) for a in contribs_at], int(c), average)
     return out
+
+
+def _fan_blocks(x):
+    """The library's block fold of each 4096 consecutive values of ``x``: lane l
+    of 256 adds values l, l + 256, ..., l + 3840 of the block in that order
+    (from +0.0, skipping values past the end), the lanes of each 64-wide wave
+    combine by an xor butterfly (every lane ends with the same bits), and the
+    four waves' sums combine as (w0 + w1) + (w2 + w3)."""
+    x = np.asarray(x, np.float64)
+    n = x.size
+    nl = max(1, -(-n // 4096))
+    pad = np.zeros(nl * 4096)
+    pad[:n] = x
+    mask = np.zeros(nl * 4096, bool)
+    mask[:n] = True
+    v = pad.reshape(nl, 16, 256)
+    m = mask.reshape(nl, 16, 256)
+    s = np.zeros((nl, 256))
+    for k in range(16):
+        s = np.where(m[:, k], s + v[:, k], s)
+    w = s.reshape(nl, 4, 64)
+    for step in (1, 2, 4, 8, 16, 32):
+        w = w + w[:, :, np.arange(64) ^ step]
+    return (w[:, 0, 0] + w[:, 1, 0]) + (w[:, 2, 0] + w[:, 3, 0])
+
+
+def fixed_tree_sum(x):
+    """The norm's fixed combine order, emulated on the host: block folds level
+    by level until at most 4096 values are left, then one last block fold.  A
+    test of the kernels' tree shape (not of the method: the oracle sums the
+    squares exactly)."""
+    x = np.asarray(x, np.float64)
+    while x.size > 4096:
+        x = _fan_blocks(x)
+    return float(_fan_blocks(x)[0])

@@ -158,6 +158,35 @@ def test_ddp_reduce_odd_shapes(n, kind, buckets, p):
         assert_bits(host(shard)[:cnt], want, f"shard of chunk {c}")
 
 
+@pytest.mark.parametrize("npieces", [1, 3000, 4096, 4097, 8 * 4096, 8 * 4096 + 5, 16 * 4096,
+                                     16 * 4096 + 1, 403 * 4096 + 7, 4096 * 4097 + 3])
+def test_norm_tree_is_the_fixed_tree_bit_for_bit(npieces):
+    # The norm's combine order is a fixed tree that depends only on the piece
+    # count: a single final block, or level-by-level launches (one or two
+    # levels) and then the final block, give the bits of the tree emulated on
+    # the host, and leave the first level's sums in the workspace.
+    from parity_util import fixed_tree_sum
+    g = torch.Generator(device=DEV).manual_seed(npieces)
+    parts = torch.rand(npieces, dtype=torch.float64, device=DEV, generator=g) * 1e-3
+    ws = torch.empty(max(grz.dp_grad_sqnorm_workspace(npieces) // 8, 1), dtype=torch.float64,
+                     device=DEV)
+    sq = torch.zeros(1, dtype=torch.float64, device=DEV)
+    sc = torch.zeros(1, dtype=torch.float32, device=DEV)
+    max_norm = 0.5
+    grz.dp_grad_sqnorm(parts, max_norm, ws, sq, sc)
+    torch.cuda.synchronize()
+    want = fixed_tree_sum(host(parts))
+    assert_bits(host(sq), np.array([want]), f"{npieces} pieces")
+    assert math.isclose(want, math.fsum(host(parts).tolist()), rel_tol=1e-13)
+    norm = math.sqrt(want)
+    factor = np.float32(max_norm / norm) if norm > max_norm else np.float32(1.0)
+    assert_bits(host(sc), np.array([factor], np.float32), f"{npieces} pieces: clip factor")
+    if npieces > 4096:  # the first level's sums are left in the workspace
+        from parity_util import _fan_blocks
+        nl = -(-npieces // 4096)
+        assert_bits(host(ws)[:nl], _fan_blocks(host(parts)), f"{npieces} pieces: level sums")
+
+
 def test_empty_plan_is_a_no_op():
     g = [torch.zeros(8, device=DEV) for _ in range(2)]
     out = torch.full((8,), 3.0, device=DEV)
