@@ -365,12 +365,23 @@ def stage_bench(args, dev):
     z1 = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(), device=dev)
     grads = [torch.empty_like(s) for s in src]
     z2 = grz.Zero2AllRanks(buckets, n, master, grz.Hyper(), device=dev)
+    # Every rank at once, each rank's shard at its arena offsets: one reduce
+    # (ZeRO-1) or one per bucket (ZeRO-2) and one optimizer launch for all.
+    z1a = grz.DDPStep(buckets, n, master, grz.Hyper(), device=dev, nreplicas=n)
+    z2a = grz.Zero2AllRanks(buckets, n, master, grz.Hyper(), device=dev, layout="arena")
 
-    def step1(t):
+    def copy_in():
         for off, length in buckets:
             for g, s in zip(grads, src):
                 g[off:off + length].copy_(s[off:off + length])
+
+    def step1(t):
+        copy_in()
         z1.step(grads, t)
+
+    def step1a(t):
+        copy_in()
+        z1a.step(grads, t)
 
     def produce(b, bufs):
         off, length = buckets[b]
@@ -379,6 +390,9 @@ def stage_bench(args, dev):
 
     def step2(t):
         z2.step(produce, t)
+
+    def step2a(t):
+        z2a.step(produce, t)
 
     def timed(fn):
         settle()
@@ -395,13 +409,17 @@ def stage_bench(args, dev):
         return e0.elapsed_time(e1) / args.steps
 
     t1, t2 = timed(step1), timed(step2)
+    t1a, t2a = timed(step1a), timed(step2a)
     g1 = sum(g.numel() * g.element_size() for g in grads)
     g2 = sum(b.numel() * b.element_size() for bufs in z2.staging for b in bufs)
-    log(f"ZeRO-1 {t1:.3f} ms, ZeRO-2 {t2:.3f} ms; gradient bytes resident "
+    log(f"ZeRO-1 {t1:.3f} ms, ZeRO-2 {t2:.3f} ms (ranks shard-compact); ZeRO-1 {t1a:.3f} ms, "
+        f"ZeRO-2 {t2a:.3f} ms (ranks in arena layout); gradient bytes resident "
         f"{g1 / 1e6:.0f} MB vs {g2 / 1e6:.0f} MB")
     print(json.dumps({"mode": "zero2_vs_zero1", "workload": "gpt2_124m all 8 ranks",
                       "buckets": len(buckets), "steps": args.steps, "zero1_ms": t1,
-                      "zero2_ms": t2, "zero1_grad_bytes": g1, "zero2_grad_bytes": g2,
+                      "zero2_ms": t2, "zero1_arena_layout_ms": t1a,
+                      "zero2_arena_layout_ms": t2a,
+                      "zero1_grad_bytes": g1, "zero2_grad_bytes": g2,
                       "resident_bytes_per_rank": {
                           "zero1": grz.resident_bytes(p, n, 1),
                           "zero2": grz.resident_bytes(p, n, 2,

@@ -395,11 +395,35 @@ class Zero2AllRanks(Zero1AllRanks):
     per parameter with bf16 gradient shards; "Distributed training" (noeira),
     ZeroSharded[2]).  The update is the ZeRO-1 one, so the results are the
     same bits.
+
+    ``layout="shards"`` keeps each rank's gradient shard and state
+    shard-compact (N reduce launches per bucket, N optimizer launches);
+    ``layout="arena"`` holds every rank's shard at its arena offsets in one
+    fp32 gradient array and one master/m/v (each rank still owns only its
+    chunk of every bucket), so that each bucket is one reduce launch over all
+    N chunks and the update one optimizer launch writing all N replicas --
+    the same arithmetic per element, as ``DDPStep(nreplicas=N)`` is for ZeRO-1.
     """
 
     def __init__(self, buckets, nranks, master, hyper=None, device="cuda", reduce_flags=0,
-                 grad_dtype=torch.bfloat16):
-        super().__init__(buckets, nranks, master, hyper, device, reduce_flags)
+                 grad_dtype=torch.bfloat16, layout="shards"):
+        if layout not in ("shards", "arena"):
+            raise ValueError("layout is 'shards' or 'arena'")
+        self.layout = layout
+        if layout == "shards":
+            super().__init__(buckets, nranks, master, hyper, device, reduce_flags)
+        else:
+            self.buckets = [(int(o), int(l)) for o, l in buckets]
+            self.n = nranks
+            self.hyper = hyper or Hyper()
+            self.reduce_flags = reduce_flags
+            self.numel = master.numel()
+            w = master.to(device=device, dtype=torch.float32).clone()
+            self.chunks = [owned_chunk(r, nranks) for r in range(nranks)]
+            self.state = (w, torch.zeros_like(w), torch.zeros_like(w))
+            self.mean = torch.zeros_like(w)  # rank r's shard at its arena offsets, every r
+            self.norm = _Norm(B.dp_piece_count(self.buckets, nranks), device)
+            self.replicas = [w.to(torch.bfloat16) for _ in range(nranks)]
         longest = max((length for _, length in self.buckets), default=0)
         self.staging = [[torch.empty(max(longest, 1), dtype=grad_dtype, device=device)
                          for _ in range(nranks)] for _ in range(2)]
@@ -407,18 +431,37 @@ class Zero2AllRanks(Zero1AllRanks):
     def step(self, produce, t, stream=None):
         """``produce(b, bufs)`` writes rank r's gradients of bucket b (processing
         order) into ``bufs[r][:length_b]`` on ``stream``."""
+        arena = self.layout == "arena"
         for b in range(len(self.buckets)):
             bufs = self.staging[b % 2]
             produce(b, bufs)
-            for c, mean in zip(self.chunks, self.means):
-                B.dp_reduce_scatter_mean(bufs, self.buckets, c, mean, self.norm.partials,
-                                         flags=self.reduce_flags | GRZ_IN_RANGE,
-                                         stream=stream, bucket_range=(b, 1))
+            flags = self.reduce_flags | GRZ_IN_RANGE
+            if arena:
+                B.dp_reduce_scatter_mean(bufs, self.buckets, -1, self.mean, self.norm.partials,
+                                         flags=flags, stream=stream, bucket_range=(b, 1))
+            else:
+                for c, mean in zip(self.chunks, self.means):
+                    B.dp_reduce_scatter_mean(bufs, self.buckets, c, mean, self.norm.partials,
+                                             flags=flags, stream=stream, bucket_range=(b, 1))
         self.norm.run(self.hyper.max_norm, stream)
         args = B.adamw_args(**step_scalars(self.hyper, t))
+        if arena:
+            w, m, v = self.state
+            B.zero1_adamw_gather(w, m, v, self.mean, self.buckets, self.n, -1, self.norm.scale,
+                                 args, self.replicas, stream=stream)
+            return
         for c, (w, m, v), mean in zip(self.chunks, self.state, self.means):
             B.zero1_adamw_gather(w, m, v, mean, self.buckets, self.n, c, self.norm.scale, args,
                                  self.replicas, stream=stream)
+
+    def rank_view(self, rank):
+        """Rank ``rank``'s gradient shard and (master, m, v), shard-compact (a copy
+        gathered from the arena layout, or the held tensors)."""
+        if self.layout == "shards":
+            return self.means[rank], self.state[rank]
+        idx = _shard_index(self.buckets, self.n, self.chunks[rank], self.mean.device)
+        return (self.mean.index_select(0, idx),
+                tuple(x.index_select(0, idx) for x in self.state))
 
 
 class CapturedStep:

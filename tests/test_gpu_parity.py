@@ -579,9 +579,11 @@ def _check_all_ranks_against_oracle(pipe, ref, what):
     """Every rank's mean, norm, clip factor, master/m/v and every replica of an
     all-ranks step against the oracle's zero1_step."""
     for r in range(pipe.n):
-        assert_bits(host(pipe.means[r]), ref["means"][r], f"{what}: mean of rank {r}")
+        mean, state = pipe.rank_view(r) if hasattr(pipe, "rank_view") else \
+            (pipe.means[r], pipe.state[r])
+        assert_bits(host(mean), ref["means"][r], f"{what}: mean of rank {r}")
         for k, name in enumerate(("master", "m", "v")):
-            assert_bits(host(pipe.state[r][k]), ref["states"][r][k], f"{what}: {name} of rank {r}")
+            assert_bits(host(state[k]), ref["states"][r][k], f"{what}: {name} of rank {r}")
     assert math.isclose(pipe.norm.sqnorm.item(), ref["sqnorm"], rel_tol=1e-13), what
     assert_bits(host(pipe.norm.scale), np.array([ref["scale"]], np.float32), f"{what}: scale")
     for i, rep in enumerate(pipe.replicas):
@@ -665,18 +667,21 @@ def test_dropped_wait_reads_gradients_not_yet_written():
     assert np.count_nonzero(raced.view(np.uint32) != want.view(np.uint32)) > 0
 
 
-def test_zero2_staged_step_matches_oracle():
+@pytest.mark.parametrize("layout", ["shards", "arena"])
+def test_zero2_staged_step_matches_oracle(layout):
     # ZeRO-2 at GPT-2 124M (9 reverse-layer buckets, N = 8): each bucket's
     # gradients arrive in a staging buffer the size of the longest bucket and
     # are reduce-scattered from it at once (GRZ_IN_RANGE); no full gradient
     # arena is kept.  Gradient shards, norm, clip factor, master/m/v and every
     # replica against the oracle's ZeRO-1 step (the update is the same), bit
-    # for bit, over two steps.
+    # for bit, over two steps -- with the ranks' shards held shard-compact, and
+    # at their arena offsets (one reduce launch per bucket for all ranks).
     a = arena("gpt2_124m")
     p, n = a.numel, 8
     buckets = grz.plan_buckets(a.numels)  # 9 buckets, reverse layer order
     master = master_init(p, device=DEV)
-    z2 = grz.Zero2AllRanks(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV)
+    z2 = grz.Zero2AllRanks(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV,
+                           layout=layout)
     longest = max(length for _, length in buckets)
     assert len(buckets) == 9 and z2.staging[0][0].numel() == longest < p
     states = oracle_states(host(master), buckets, n)
@@ -987,6 +992,7 @@ def test_two_ranks_every_strategy_gives_the_same_weights():
     ddp_fused = grz.DDPStep(buckets, n, master, hyper, device=DEV, fused=True)
     z1 = grz.Zero1AllRanks(buckets, n, master, hyper, device=DEV)
     z2 = grz.Zero2AllRanks(buckets, n, master, hyper, device=DEV)
+    z2a = grz.Zero2AllRanks(buckets, n, master, hyper, device=DEV, layout="arena")
     for t in (1, 2, 3):
         grads = [rank_grad(p, 1e-2, "bf16", grad_seed(t, r), device=DEV) for r in range(n)]
         ddp.step(grads, t)
@@ -998,13 +1004,15 @@ def test_two_ranks_every_strategy_gives_the_same_weights():
             for buf, g in zip(bufs, grads):
                 buf[:length].copy_(g[off:off + length])
         z2.step(produce, t)
+        z2a.step(produce, t)
         torch.cuda.synchronize()
         want = host(ddp.replica)
         for what, rep in (("fused DDP", ddp_fused.replica), ("ZeRO-1", z1.replicas[0]),
-                          ("ZeRO-1 rank 1", z1.replicas[1]), ("ZeRO-2", z2.replicas[1])):
+                          ("ZeRO-1 rank 1", z1.replicas[1]), ("ZeRO-2", z2.replicas[1]),
+                          ("ZeRO-2 in arena layout", z2a.replicas[1])):
             assert_bits(host(rep), want, f"t={t} {what} weights")
         for what, sq in (("fused DDP", ddp_fused.norm.sqnorm), ("ZeRO-1", z1.norm.sqnorm),
-                         ("ZeRO-2", z2.norm.sqnorm)):
+                         ("ZeRO-2", z2.norm.sqnorm), ("ZeRO-2 in arena layout", z2a.norm.sqnorm)):
             assert_bits(host(sq), host(ddp.norm.sqnorm), f"t={t} {what} sqnorm")
     assert ddp.norm.scale.item() < 1
 
