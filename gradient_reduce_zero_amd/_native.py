@@ -53,6 +53,7 @@ SIGNATURES = {
     "dp_grad_sqnorm_workspace": (ctypes.c_size_t, [_i64]),
     "dp_grad_sqnorm": (_i, [_vp, _i64, _d, _vp, _vp, _vp, _vp]),
     "dp_grad_sqnorm_noalloc": (_i, [_vp, _i64, _d, _vp, _vp, _vp]),
+    "dp_grad_sqnorm_step_args": (_i, [_vp, _i64, _d, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
     "dp_grad_sqnorm_of_workspace": (ctypes.c_size_t, [_i64]),
     "dp_grad_sqnorm_of": (_i, [_vp, _i64, _d, _vp, _vp, _vp, _vp]),
     "zero1_adamw_step": (_i, [_vp, _vp, _vp, _vp, _i64, _vp, ctypes.POINTER(AdamWArgs), _vp,

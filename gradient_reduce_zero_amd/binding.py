@@ -170,9 +170,25 @@ def dp_reduce_scatter_mean(rank_grads, buckets, chunk, mean_out, piece_sqnorm=No
                                                  flags, out, part, _stream(stream)))
 
 
+class StepScalars:
+    """The AdamW scalars of a captured step in device memory: ``table`` (rows of
+    7 float32 values, one per step), ``counter`` (int64, the next row) and
+    ``current`` (the row the optimizer reads).  The first call of a step that
+    needs ``current`` advances it -- the norm in its own last launch
+    (``dp_grad_sqnorm_step_args``), else the optimizer's entry point with a
+    ``grz_step_args_next`` launch before its own; ``advanced`` records that it
+    was done for the step being enqueued."""
+
+    def __init__(self, table, counter, current):
+        self.table, self.counter, self.current = table, counter, current
+        self.advanced = False
+
+
 def dp_grad_sqnorm(piece_sqnorm, max_norm, workspace, sqnorm_out, clip_scale_out,
-                   npieces=None, stream=None):
-    """Fixed-order global squared norm of the piece sums and the clip factor."""
+                   npieces=None, stream=None, step_args=None):
+    """Fixed-order global squared norm of the piece sums and the clip factor;
+    with ``step_args`` (a ``StepScalars`` not yet advanced for this step) the
+    same launch advances the step's scalars."""
     npieces = piece_sqnorm.numel() if npieces is None else int(npieces)
     part = _dev(piece_sqnorm, "piece_sqnorm", (torch.float64,), npieces)
     need = dp_grad_sqnorm_workspace(npieces)
@@ -187,6 +203,17 @@ def dp_grad_sqnorm(piece_sqnorm, max_norm, workspace, sqnorm_out, clip_scale_out
     sq = None if sqnorm_out is None else _dev(sqnorm_out, "sqnorm_out", (torch.float64,), 1)
     sc = None if clip_scale_out is None else _dev(clip_scale_out, "clip_scale_out",
                                                    (torch.float32,), 1)
+    if step_args is not None and not step_args.advanced:
+        rows = step_args.table.numel() // ARGS_FIELDS
+        check("dp_grad_sqnorm_step_args",
+              lib().dp_grad_sqnorm_step_args(
+                  part, npieces, float(max_norm), ws, sq, sc,
+                  _dev(step_args.table, "table", (torch.float32,), ARGS_FIELDS),
+                  rows, _dev(step_args.counter, "counter", (torch.int64,), 1),
+                  _dev(step_args.current, "current", (torch.float32,), ARGS_FIELDS),
+                  _stream(stream)))
+        step_args.advanced = True
+        return
     check("dp_grad_sqnorm", lib().dp_grad_sqnorm(part, npieces, float(max_norm), ws, sq, sc,
                                                  _stream(stream)))
 
@@ -249,9 +276,15 @@ def zero1_adamw_step(master, m, v, mean_grad, clip_scale, args, bf16_out=None, n
 ARGS_FIELDS = 7  # floats in grz_adamw_args
 
 
-def _device_args(args):
+def _device_args(args, stream):
     """(pointer, True) for step scalars in device memory (a float32 tensor of
-    7 values), (byref, False) for host ``AdamWArgs``."""
+    7 values, or a ``StepScalars``, advanced first if nothing did it yet for
+    this step), (byref, False) for host ``AdamWArgs``."""
+    if isinstance(args, StepScalars):
+        if not args.advanced:
+            grz_step_args_next(args.table, args.counter, args.current, stream=stream)
+            args.advanced = True
+        args = args.current
     if isinstance(args, torch.Tensor):
         return ctypes.cast(_dev(args, "args", (torch.float32,), ARGS_FIELDS),
                            ctypes.POINTER(AdamWArgs)), True
@@ -273,7 +306,7 @@ def zero1_adamw_gather(master, m, v, mean_grad, buckets, nranks, chunk, clip_sca
     reps = (ctypes.c_void_p * max(len(replicas), 1))(
         *[_dev(r, f"replicas[{i}]", _BF16_LIKE, ext).value for i, r in enumerate(replicas)])
     arr, nb = _bucket_array(buckets)
-    a, on_device = _device_args(args)
+    a, on_device = _device_args(args, stream)
     if on_device:
         flags |= N.GRZ_ARGS_DEVICE
     check("zero1_adamw_gather",
@@ -398,7 +431,7 @@ def zero1_fused_step(rank_grads, buckets, chunk, master, m, v, args, max_norm, r
     reps = (ctypes.c_void_p * max(len(replicas), 1))(
         *[_dev(r, f"replicas[{i}]", _BF16_LIKE, ext).value for i, r in enumerate(replicas)])
     arr, nb = _bucket_array(buckets)
-    a, on_device = _device_args(args)
+    a, on_device = _device_args(args, stream)
     if on_device:
         flags |= N.GRZ_ARGS_DEVICE
     check("zero1_fused_step",

@@ -537,15 +537,34 @@ __global__ __launch_bounds__(kThreads) void sqnorm_level_kernel(const double* __
   }
 }
 
+// The step scalars of a captured step, advanced by the norm's last launch
+// (see dp_grad_sqnorm_step_args): current = table[min(counter, count - 1)],
+// then counter += 1.  `table` null: nothing to advance.
+struct StepArgsNext {
+  const grz_adamw_args* table;
+  int64_t count;
+  int64_t* counter;
+  grz_adamw_args* current;
+};
+
+__device__ __forceinline__ void step_args_next(const StepArgsNext& a) {
+  const int64_t c = *a.counter;
+  const int64_t i = c < 0 ? 0 : (c >= a.count ? a.count - 1 : c);
+  *a.current = a.table[i];
+  *a.counter = c + 1;
+}
+
 __global__ __launch_bounds__(kThreads) void sqnorm_final_kernel(const double* __restrict__ x,
                                                                 int64_t n, double max_norm,
                                                                 double* __restrict__ sqnorm_out,
-                                                                float* __restrict__ scale_out) {
+                                                                float* __restrict__ scale_out,
+                                                                const StepArgsNext next) {
   __shared__ double lds[kThreads / 64];
   const double tot = fan_block_sum(x, n, 0, lds);
   if (threadIdx.x == 0) {
     if (sqnorm_out != nullptr) *sqnorm_out = tot;
     if (scale_out != nullptr) *scale_out = clip_factor(tot, max_norm);
+    if (next.table != nullptr) step_args_next(next);
   }
 }
 
@@ -688,15 +707,8 @@ __global__ __launch_bounds__(GRZ_ADAM_THREADS) GRZ_ADAM_ATTR void adamw_kernel(
 
 // The next step's scalars for a captured (replayed) step: current =
 // table[min(counter, count - 1)], then counter += 1.  One thread.
-__global__ void args_next_kernel(const grz_adamw_args* __restrict__ table, int64_t count,
-                                 int64_t* __restrict__ counter,
-                                 grz_adamw_args* __restrict__ current) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    const int64_t c = *counter;
-    const int64_t i = c < 0 ? 0 : (c >= count ? count - 1 : c);
-    *current = table[i];
-    *counter = c + 1;
-  }
+__global__ void args_next_kernel(const StepArgsNext next) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) step_args_next(next);
 }
 
 // ---------------------------------------------------------------------------
@@ -1462,9 +1474,21 @@ size_t dp_grad_sqnorm_workspace(int64_t npieces) {
   return static_cast<size_t>(total) * sizeof(double);
 }
 
-int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
-                   void* workspace, double* sqnorm_out, float* clip_scale_out,
-                   hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int check_step_args(const grz_adamw_args* table, int64_t count, const int64_t* counter,
+                    const grz_adamw_args* current) {
+  if (table == nullptr || counter == nullptr || current == nullptr || count < 1)
+    return GRZ_EINVAL;
+  if (!aligned(table, 4) || !aligned(counter, 8) || !aligned(current, 4)) return GRZ_EALIGN;
+  return GRZ_OK;
+}
+
+int sqnorm_entry(const double* piece_sqnorm, int64_t npieces, double max_norm,
+                 void* workspace, double* sqnorm_out, float* clip_scale_out,
+                 const StepArgsNext& next, hipStream_t stream) {
   if (npieces < 0) return GRZ_EINVAL;
   if (npieces > 0 && piece_sqnorm == nullptr) return GRZ_EINVAL;
   if (sqnorm_out == nullptr && clip_scale_out == nullptr) return GRZ_EINVAL;
@@ -1489,9 +1513,30 @@ int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
     ws += sizes[i];
   }
   hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kThreads), 0, stream, in, n, max_norm,
-                     sqnorm_out, clip_scale_out);
+                     sqnorm_out, clip_scale_out, next);
   if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
   return GRZ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
+                   void* workspace, double* sqnorm_out, float* clip_scale_out,
+                   hipStream_t stream) {
+  return sqnorm_entry(piece_sqnorm, npieces, max_norm, workspace, sqnorm_out, clip_scale_out,
+                      StepArgsNext{}, stream);
+}
+
+int dp_grad_sqnorm_step_args(const double* piece_sqnorm, int64_t npieces, double max_norm,
+                             void* workspace, double* sqnorm_out, float* clip_scale_out,
+                             const grz_adamw_args* table, int64_t count, int64_t* counter,
+                             grz_adamw_args* current, hipStream_t stream) {
+  const int st = check_step_args(table, count, counter, current);
+  if (st != GRZ_OK) return st;
+  return sqnorm_entry(piece_sqnorm, npieces, max_norm, workspace, sqnorm_out, clip_scale_out,
+                      StepArgsNext{table, count, counter, current}, stream);
 }
 
 }  // extern "C"
@@ -1655,12 +1700,11 @@ int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad
 
 int grz_step_args_next(const grz_adamw_args* table, int64_t count, int64_t* counter,
                        grz_adamw_args* current, hipStream_t stream) {
-  if (table == nullptr || counter == nullptr || current == nullptr || count < 1)
-    return GRZ_EINVAL;
-  if (!aligned(table, 4) || !aligned(counter, 8) || !aligned(current, 4)) return GRZ_EALIGN;
+  const int st = check_step_args(table, count, counter, current);
+  if (st != GRZ_OK) return st;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(args_next_kernel, dim3(1), dim3(64), 0, stream, table, count, counter,
-                     current);
+  hipLaunchKernelGGL(args_next_kernel, dim3(1), dim3(64), 0, stream,
+                     StepArgsNext{table, count, counter, current});
   if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
   return GRZ_OK;
 }

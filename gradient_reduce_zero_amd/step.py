@@ -59,9 +59,13 @@ class _Norm:
         self.sqnorm = torch.zeros(1, dtype=torch.float64, device=device)
         self.scale = torch.ones(1, dtype=torch.float32, device=device)
 
-    def run(self, max_norm, stream=None):
+    def run(self, max_norm, stream=None, args=None):
+        """The norm and the clip factor; ``args`` (the step's scalars, as handed to
+        an ``enqueue``) are advanced in the same launch when they are a
+        captured step's ``StepScalars``."""
         B.dp_grad_sqnorm(self.partials, max_norm, self.workspace, self.sqnorm, self.scale,
-                         npieces=self.npieces, stream=stream)
+                         npieces=self.npieces, stream=stream,
+                         step_args=args if isinstance(args, B.StepScalars) else None)
 
 
 def _fused_workspace(npieces, device):
@@ -112,7 +116,7 @@ class Zero1AllRanks:
             B.dp_reduce_scatter_mean(rank_grads, self.buckets, c, mean, self.norm.partials,
                                      flags=self.reduce_flags, stream=stream,
                                      token_counts=token_counts)
-        self.norm.run(self.hyper.max_norm, stream)
+        self.norm.run(self.hyper.max_norm, stream, args)
         for c, (w, m, v), mean in zip(self.chunks, self.state, self.means):
             B.zero1_adamw_gather(w, m, v, mean, self.buckets, self.n, c, self.norm.scale, args,
                                  self.replicas, stream=stream)
@@ -219,7 +223,7 @@ class Zero1OneRank:
     def update(self, t, stream=None, args=None):
         """Norm, clip and AdamW with the bf16 write; ``args`` (host ``AdamWArgs`` or
         device tensor) overrides the scalars of step ``t``."""
-        self.norm.run(self.hyper.max_norm, stream)
+        self.norm.run(self.hyper.max_norm, stream, args)
         if args is None:
             args = B.adamw_args(**step_scalars(self.hyper, t))
         w, m, v = self.state
@@ -305,7 +309,7 @@ class DDPOneRank:
         B.dp_all_gather(peer_means, self.buckets, [self.mean], flags=self.flags, stream=stream)
 
     def update(self, t, stream=None, args=None):
-        self.norm.run(self.hyper.max_norm, stream)
+        self.norm.run(self.hyper.max_norm, stream, args)
         if args is None:
             args = B.adamw_args(**step_scalars(self.hyper, t))
         w, m, v = self.state
@@ -471,11 +475,11 @@ class CapturedStep:
     one graph per GPU and replays it.  The step's AdamW scalars change every
     step, so they live in a device table (rows for steps ``first_t`` ..
     ``first_t + count - 1``, filled once on the host with ``step_scalars``);
-    a one-thread kernel at the head of the graph copies the replay's row to
-    the slot the optimizer reads (``GRZ_ARGS_DEVICE``).  (Run on a branch of
-    the graph beside the step's first kernels instead, it measured slower:
-    the join costs more than the kernel.)  ``enqueue(args, stream)`` must
-    enqueue the step's kernels with ``args`` as their scalars;
+    each replay copies its row to the slot the optimizer reads
+    (``GRZ_ARGS_DEVICE``) in the norm's last launch (``StepScalars``; a step
+    without a norm launch of its own, the one-launch step, gets a one-thread
+    kernel before its launch instead).  ``enqueue(args, stream)`` must enqueue
+    the step's kernels with ``args`` as their scalars;
     every buffer it touches keeps its address for the graph's lifetime.
     ``replay`` counts replays on the host and raises once the table's
     ``count`` steps are used (a further replay would repeat the last row's
@@ -494,11 +498,10 @@ class CapturedStep:
         self.replays = 0
         self.counter = torch.zeros(1, dtype=torch.int64, device=device)
         self.current = torch.zeros(B.ARGS_FIELDS, dtype=torch.float32, device=device)
+        self.scalars = B.StepScalars(self.table, self.counter, self.current)
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
-            s = torch.cuda.current_stream()
-            B.grz_step_args_next(self.table, self.counter, self.current, stream=s)
-            enqueue(self.current, s)
+            enqueue(self.scalars, torch.cuda.current_stream())
 
     def replay(self):
         """Run the next step; RuntimeError (nothing enqueued) past the table."""

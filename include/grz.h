@@ -283,6 +283,19 @@ int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
 int dp_grad_sqnorm_noalloc(const double* piece_sqnorm, int64_t npieces, double max_norm,
                            double* sqnorm_out, float* clip_scale_out, hipStream_t stream);
 
+/*
+ * dp_grad_sqnorm, and in its last launch the work of grz_step_args_next:
+ * *current = table[min(*counter, count - 1)]; *counter += 1 (all device
+ * memory).  A captured step ("Distributed training", "Overlap and graphs": one
+ * graph per GPU, replayed) needs both before its optimizer runs; done by the
+ * norm's single-workgroup launch they cost one launch fewer per replay.
+ * Arguments and errors as dp_grad_sqnorm and grz_step_args_next.
+ */
+int dp_grad_sqnorm_step_args(const double* piece_sqnorm, int64_t npieces, double max_norm,
+                             void* workspace, double* sqnorm_out, float* clip_scale_out,
+                             const grz_adamw_args* table, int64_t count, int64_t* counter,
+                             grz_adamw_args* current, hipStream_t stream);
+
 /* Bytes of workspace dp_grad_sqnorm_of needs for `n` gradient elements. */
 size_t dp_grad_sqnorm_of_workspace(int64_t n);
 

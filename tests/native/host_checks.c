@@ -207,6 +207,13 @@ static void argument_errors(void) {
                                (double*)0x600000, NULL, NULL) == GRZ_ERANGE, "noalloc range");
   CHECK(dp_grad_sqnorm_noalloc((double*)0x700000, -1, 1.0, (double*)0x600000, NULL, NULL) ==
         GRZ_EINVAL, "noalloc count");
+  CHECK(dp_grad_sqnorm_step_args((double*)0x700000, 5, 1.0, NULL, (double*)0x600000, NULL,
+                                 NULL, 4, (int64_t*)0xC00000, (grz_adamw_args*)0xD00000,
+                                 NULL) == GRZ_EINVAL, "step-args norm without a table");
+  CHECK(dp_grad_sqnorm_step_args((double*)0x700000, 5, 1.0, NULL, (double*)0x600000, NULL,
+                                 (grz_adamw_args*)0xD00000, 4, (int64_t*)0xC00004,
+                                 (grz_adamw_args*)0xD00000, NULL) == GRZ_EALIGN,
+        "step-args norm, counter off its alignment");
   int64_t* ctr = (int64_t*)0xC00000;
   grz_adamw_args* table = (grz_adamw_args*)0xD00000;
   CHECK(grz_step_args_next(NULL, 4, ctr, table, NULL) == GRZ_EINVAL, "null table");

@@ -187,6 +187,45 @@ def test_norm_tree_is_the_fixed_tree_bit_for_bit(npieces):
         assert_bits(host(ws)[:nl], _fan_blocks(host(parts)), f"{npieces} pieces: level sums")
 
 
+@pytest.mark.parametrize("npieces", [3000, 30416])
+def test_norm_that_also_advances_the_step_scalars(npieces):
+    # dp_grad_sqnorm_step_args, through the C ABI: the norm and clip factor of
+    # dp_grad_sqnorm bit for bit, and the work of grz_step_args_next in the
+    # same launch (the row at the counter, clamped to the table, copied to
+    # `current`; the counter advanced) -- with one tree level and with none.
+    import ctypes
+    from gradient_reduce_zero_amd import _native as N
+
+    def ptr(t):
+        return ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    g = torch.Generator(device=DEV).manual_seed(npieces)
+    parts = torch.rand(npieces, dtype=torch.float64, device=DEV, generator=g) * 1e-3
+    ws = torch.empty(max(grz.dp_grad_sqnorm_workspace(npieces) // 8, 1), dtype=torch.float64,
+                     device=DEV)
+    table = torch.arange(3 * 7, dtype=torch.float32, device=DEV) + 0.5
+    counter = torch.zeros(1, dtype=torch.int64, device=DEV)
+    current = torch.zeros(7, dtype=torch.float32, device=DEV)
+    want_sq = torch.zeros(1, dtype=torch.float64, device=DEV)
+    want_sc = torch.zeros(1, dtype=torch.float32, device=DEV)
+    assert grz.lib().dp_grad_sqnorm(ptr(parts), npieces, 0.25, ptr(ws), ptr(want_sq),
+                                    ptr(want_sc), stream) == N.GRZ_OK
+    for step in range(4):  # rows 0, 1, 2, then the last row again
+        sq = torch.zeros(1, dtype=torch.float64, device=DEV)
+        sc = torch.zeros(1, dtype=torch.float32, device=DEV)
+        assert grz.lib().dp_grad_sqnorm_step_args(
+            ptr(parts), npieces, 0.25, ptr(ws), ptr(sq), ptr(sc), ptr(table), 3, ptr(counter),
+            ptr(current), stream) == N.GRZ_OK
+        torch.cuda.synchronize()
+        assert_bits(host(sq), host(want_sq), f"step {step}: sqnorm")
+        assert_bits(host(sc), host(want_sc), f"step {step}: clip factor")
+        assert_bits(host(current), host(table.view(3, 7)[min(step, 2)]), f"step {step}: row")
+        assert int(counter.item()) == step + 1
+    assert grz.lib().dp_grad_sqnorm_step_args(ptr(parts), npieces, 0.25, ptr(ws), ptr(sq),
+                                              ptr(sc), None, 3, ptr(counter), ptr(current),
+                                              stream) == N.GRZ_EINVAL
+
+
 def test_empty_plan_is_a_no_op():
     g = [torch.zeros(8, device=DEV) for _ in range(2)]
     out = torch.full((8,), 3.0, device=DEV)
