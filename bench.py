@@ -427,8 +427,9 @@ def stage_bench(args, dev):
           flush=True)
 
 
-def all_ranks_bench(args, dev):
-    """ZeRO-1 step of all N simulated ranks: one JSON line (time, bytes, GB/s)."""
+def all_ranks_bench(args, dev, emit=True):
+    """ZeRO-1 step of all N simulated ranks: one JSON line (time, bytes, GB/s),
+    also returned as a dict."""
     import torch
 
     import gradient_reduce_zero_amd as grz
@@ -498,7 +499,9 @@ def all_ranks_bench(args, dev):
            "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
            "model_params_per_s": p / (ms * 1e-3), "phases_ms": phase,
            "phases_GBps": {k: pbytes[k] / (phase[k] * 1e-3) / 1e9 for k in pbytes},
-           "arena_layout_ms_per_step": arena_ms}
+           "arena_layout_ms_per_step": arena_ms,
+           "arena_layout_frac_of_peak": step_bytes / (arena_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+           "ms_at_70pct_of_peak": step_bytes / (0.7 * PEAK_HBM_GBPS * 1e9) * 1e3}
     if args.graph:
         first = args.warmup + 2 * args.steps + 1
         cap = grz.CapturedStep(lambda a_, s_: pipe.enqueue(grads, a_, s_), pipe.hyper, first,
@@ -518,7 +521,9 @@ def all_ranks_bench(args, dev):
         log("timing the CPU oracle's all-ranks step")
         out["cpu_baseline"] = cpu_baseline_all_ranks(grads, buckets, n, hyper,
                                                      min(args.cpu_sample, 1 << 28))
-    print(json.dumps(out), flush=True)
+    if emit:
+        print(json.dumps(out), flush=True)
+    return out
 
 
 def torch_reference(args, setup, stream):
@@ -580,8 +585,9 @@ def ddp_bytes(p, n, grad_bytes=2):
     return {"reduce": grad_bytes * p + 4 * p // n, "gather": 2 * peers, "adamw": 30 * p}
 
 
-def ddp_bench(args, dev):
-    """One rank's plain data-parallel (ZeRO stage 0) step: one JSON line."""
+def ddp_bench(args, dev, emit=True):
+    """One rank's plain data-parallel (ZeRO stage 0) step: one JSON line, also
+    returned as a dict."""
     import torch
 
     import gradient_reduce_zero_amd as grz
@@ -649,6 +655,7 @@ def ddp_bench(args, dev):
            "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
            "pct_of_peak_hbm": 100.0 * step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
            "step_bytes_without_simulated_reads": step_bytes - simulated,
+           "ms_at_70pct_of_peak": step_bytes / (0.7 * PEAK_HBM_GBPS * 1e9) * 1e3,
            "phases_ms": phase, "phases_GBps": gbps}
     if args.graph:
         cap = grz.CapturedStep(lambda a_, s_: one.enqueue(incoming, peer_means, a_, s_),
@@ -666,7 +673,9 @@ def ddp_bench(args, dev):
         log(f"graph replay: {out['graph_ms_per_step']:.3f} ms/step")
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_ddp(incoming, n, hyper, min(args.cpu_sample, 1 << 27))
-    print(json.dumps(out), flush=True)
+    if emit:
+        print(json.dumps(out), flush=True)
+    return out
 
 
 def cpu_baseline_ddp(incoming, n, hyper, sample):
@@ -787,6 +796,28 @@ def other_configs_bench(args, dev):
     return out
 
 
+def other_modes_bench(args, dev):
+    """The step in its other modes, as ``--all-ranks`` and ``--ddp`` run them
+    (without the CPU oracle): every simulated rank of the char GPT, GPT-2 124M
+    (each also as a graph) and GPT-2 1.5B, and one rank's plain data-parallel
+    step at 7B (10 steps)."""
+    import torch
+
+    out = {}
+    runs = [("all_ranks", "char_gpt", 8, True), ("all_ranks", "gpt2_124m", 8, True),
+            ("all_ranks", "gpt2_1p5b", 4, False), ("ddp_one_rank", "llama_7b", 8, False)]
+    for mode, cfg, n, graph in runs:
+        sub = argparse.Namespace(**vars(args))
+        sub.config, sub.nranks, sub.graph, sub.no_cpu = cfg, n, graph, True
+        if cfg == "llama_7b":
+            sub.steps, sub.warmup = min(args.steps, 10), min(args.warmup, 2)
+        fn = all_ranks_bench if mode == "all_ranks" else ddp_bench
+        out[f"{cfg}_{mode}"] = fn(sub, dev, emit=False)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def fused_bench(args, setup, stream, dev):
     """The same one-rank step with reduce + norm + clip + AdamW as one launch."""
     import torch
@@ -886,9 +917,10 @@ def main():
                          "for the whole arena, GPT-2 124M's nine 25 MiB buckets), the whole "
                          "arena, or reverse-layer buckets of 25 MiB of gradient")
     ap.add_argument("--no-other-configs", action="store_true",
-                    help="skip the smaller one-rank shares (char GPT, GPT-2 124M and 1.5B, "
-                         "as graph replays, warm and cold) the default run times after the "
-                         "headline workload")
+                    help="skip what the default run times after the headline workload: the "
+                         "smaller one-rank shares (char GPT, GPT-2 124M and 1.5B, as graph "
+                         "replays, warm and cold), every simulated rank of those three "
+                         "arenas, and one rank's plain data-parallel step at 7B")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 2 GiB bf16 copy (the library's all-gather "
                          "kernel with one rank and one replica) as the reference of known "
@@ -1107,6 +1139,7 @@ def main():
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         out["other_configs"] = other_configs_bench(args, dev)
+        out["other_modes"] = other_modes_bench(args, dev)
     print(json.dumps(out), flush=True)
 
 
