@@ -189,16 +189,34 @@ static_assert(GRZ_AG_TILE % (GRZ_AG_THREADS * 8) == 0, "all-gather tile shape");
 // optimizer at 3 waves (4.2 ms at 5 or more, 4.7 ms at 2, with the
 // workgroups above); the all-gather copy of one 16-byte access per lane runs
 // best uncapped.  Speed only, never a result bit.
+//
+// A small launch of the reduce runs better at 3 waves for every N: with few
+// tiles per CU, more of them resident shortens the ramp and the tail.  At
+// N = 8 (3 against 2 waves): GPT-2 124M one-rank share (3,802 tiles) 0.056
+// against 0.062 ms; the 124M ranks' reduces of all 8 ranks 0.446 against
+// 0.483 ms, the char GPT's 0.115 against 0.124 ms; one launch of 30,416
+// tiles the same either way; the 1.5B share at N = 8 (47,534 tiles) 0.638
+// against 0.618 ms and the 7B share (205,641 tiles) 2.85 against 2.79 ms.
+// So launches of at most kRsSmallTiles tiles take the small-launch cap.
 #ifndef GRZ_RS_WAVES
 #define GRZ_RS_WAVES 2
 #endif
 #ifndef GRZ_RS_WAVES_FEW
 #define GRZ_RS_WAVES_FEW 3
 #endif
-static_assert(GRZ_RS_WAVES > 0 && GRZ_RS_WAVES_FEW > 0, "the reduce's caps are per N");
-// The reduce's cap for N ranks (every N from 1 to 16 has its own kernel).
-template <int NR> struct RsWaves {
-  static constexpr int value = (NR >= 1 && NR <= 4) ? GRZ_RS_WAVES_FEW : GRZ_RS_WAVES;
+#ifndef GRZ_RS_WAVES_SMALL
+#define GRZ_RS_WAVES_SMALL 3
+#endif
+static_assert(GRZ_RS_WAVES > 0 && GRZ_RS_WAVES_FEW > 0 && GRZ_RS_WAVES_SMALL > 0,
+              "the reduce's caps are per N");
+constexpr int64_t kRsSmallTiles = 16384;
+// The reduce's cap for N ranks (every N from 1 to 16 has its own kernel),
+// for a large launch or a small one.  Up to four ranks it is the same cap
+// either way (so the same kernel).
+template <int NR, bool SMALL> struct RsWaves {
+  static constexpr int value = (NR >= 1 && NR <= 4) ? GRZ_RS_WAVES_FEW
+                               : SMALL               ? GRZ_RS_WAVES_SMALL
+                                                     : GRZ_RS_WAVES;
 };
 #ifndef GRZ_ADAM_WAVES
 #define GRZ_ADAM_WAVES 3
@@ -420,10 +438,9 @@ __device__ __forceinline__ void fold_tile(const TIn* const* rank, int c, int64_t
 // WIRE (bf16 gradients only) rounds every partial sum of the fold to bf16, as a
 // ring whose wire format is bf16 does once per hop ("13.5 Multi-GPU from
 // First Principles", exercise 8).
-template <typename TIn, int NR, bool WIRE>
+template <typename TIn, int NR, bool WIRE, int WAVES>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(RsWaves<NR>::value, RsWaves<NR>::value))) void rs_mean_kernel(
-    const RsArgs<TIn> a) {
+__attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void rs_mean_kernel(const RsArgs<TIn> a) {
   using Acc = typename AccOf<TIn>::type;
   constexpr int G = Geo<Acc>::G;
   constexpr int K = Geo<Acc>::K;
@@ -1136,10 +1153,17 @@ int launch_batches(std::vector<Seg>& segs, Args& args,
 
 template <typename TIn, int NR>
 int rs_launch(std::vector<Seg>& segs, RsArgs<TIn>& args, bool wire, hipStream_t stream) {
+  int64_t tiles = 0;
+  for (const Seg& s : segs) tiles += ceil_div(s.len, GRZ_PIECE);
+  const bool small = tiles <= kRsSmallTiles;
+  constexpr int WL = RsWaves<NR, false>::value, WS = RsWaves<NR, true>::value;
   if constexpr (sizeof(TIn) == 2) {
-    if (wire) return launch_batches(segs, args, rs_mean_kernel<TIn, NR, true>, stream);
+    if (wire)
+      return small ? launch_batches(segs, args, rs_mean_kernel<TIn, NR, true, WS>, stream)
+                   : launch_batches(segs, args, rs_mean_kernel<TIn, NR, true, WL>, stream);
   }
-  return launch_batches(segs, args, rs_mean_kernel<TIn, NR, false>, stream);
+  return small ? launch_batches(segs, args, rs_mean_kernel<TIn, NR, false, WS>, stream)
+               : launch_batches(segs, args, rs_mean_kernel<TIn, NR, false, WL>, stream);
 }
 
 template <typename TIn>
