@@ -332,3 +332,31 @@ def test_fused_sixteen_ranks_equals_three_kernels():
         _same(one_r.arena, three_r.arena, f"N=16 rank 11 t={t} arena")
         _same(one_r.norm.sqnorm, three_r.norm.sqnorm, f"N=16 rank 11 t={t} sqnorm")
     assert three.norm.scale.item() < 1
+
+
+def test_captured_fused_step_replays_match_eager_fused_steps():
+    # The one-launch step captured in a HIP graph: it has no norm launch of its
+    # own, so each replay advances the step scalars with grz_step_args_next
+    # ahead of the fused launch (GRZ_ARGS_DEVICE); every replay equals the
+    # eager fused step of the same number, which equals the three kernels.
+    a = arena("char_gpt")
+    p, n, rank = a.numel, 8, 2
+    inp, three, eager = _one_rank_pair([(0, p)], p, n, rank)
+    graphed = grz.Zero1OneRank([(0, p)], n, rank, inp["shard_master"].clone(), device=DEV,
+                               arena_numel=p, fused=True)
+    graphed.norm.partials.copy_(inp["partials"])
+    cap = grz.CapturedStep(lambda args, s: graphed.enqueue(inp["incoming"], inp["peer_shards"],
+                                                            args, s), graphed.hyper, 1, 3)
+    for t in (1, 2, 3):
+        three.step(inp["incoming"], inp["peer_shards"], t)
+        eager.step(inp["incoming"], inp["peer_shards"], t)
+        cap.replay()
+        torch.cuda.synchronize()
+        eager.check_fused()
+        graphed.check_fused()
+        for k in range(3):
+            _same(graphed.state[k], eager.state[k], f"replay {t}: state {k}")
+            _same(eager.state[k], three.state[k], f"eager fused t={t}: state {k}")
+        _same(graphed.arena, eager.arena, f"replay {t}: arena")
+        _same(graphed.norm.sqnorm, three.norm.sqnorm, f"replay {t}: sqnorm")
+    assert int(cap.counter.item()) == 3
