@@ -10,7 +10,7 @@ from oracle.reduce import (chunk_mean, chunk_owner, owned_chunk, reduce_scatter_
 from oracle.ring import chunk_bounds, ring_all_reduce, ring_reduce_scatter
 
 
-@pytest.mark.parametrize("n", [2, 3, 4, 8])
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 8, 13, 16])
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 @pytest.mark.parametrize("length", [64, 67])
 def test_fold_equals_simulated_ring(n, dtype, length):
@@ -49,7 +49,7 @@ def test_fold_order_is_observable():
     assert not np.array_equal(ring, plain)
 
 
-@pytest.mark.parametrize("n", [2, 3, 4, 8])
+@pytest.mark.parametrize("n", [2, 3, 4, 8, 16])
 def test_integer_data_mean_is_sum_over_n(n):
     rng = np.random.default_rng(n)
     arrays = [rng.integers(-50, 50, size=96).astype(np.float64) for _ in range(n)]
@@ -130,7 +130,7 @@ def _bf16_vectors(rng, n, length, scale=1e-3):
             for _ in range(n)]
 
 
-@pytest.mark.parametrize("n", [2, 3, 4, 8])
+@pytest.mark.parametrize("n", [2, 3, 4, 8, 16])
 def test_bf16_wire_fold_equals_simulated_bf16_ring(n):
     rng = np.random.default_rng(70 + n)
     bits = _bf16_vectors(rng, n, 67)

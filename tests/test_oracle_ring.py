@@ -67,7 +67,7 @@ def test_eq_13_5_1_bytes(k):
     assert all(s * k == 2 * (k - 1) * nbytes for s in sent)
 
 
-@pytest.mark.parametrize("n", [2, 3, 4, 8])
+@pytest.mark.parametrize("n", [2, 3, 4, 8, 16])
 def test_integer_data_equals_numpy_sum(n):
     rng = np.random.default_rng(100 + n)
     arrays = [rng.integers(-1000, 1000, size=64).astype(np.float64) for _ in range(n)]
