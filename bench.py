@@ -745,12 +745,13 @@ def other_configs_bench(args, dev):
     stream = torch.cuda.current_stream()
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     out = {}
+    steps = max(args.steps, 100)  # replays of a few µs to ms: time enough of them
     for name, n in OTHER_CONFIGS:
         setup = onerank_setup(name, n, 0, dev)
         pipe, inp = setup["pipe"], setup["inp"]
         owned = setup["shard"]
         step_bytes = owned * sum(bytes_per_owned(n).values())
-        count = 2 * (args.warmup + args.steps)
+        count = 2 * (args.warmup + steps)
         cap = grz.CapturedStep(lambda a, s: (pipe.reduce(inp["incoming"], s),
                                              pipe.update(None, s, args=a),
                                              pipe.gather(inp["peer_shards"], s)),
@@ -761,13 +762,13 @@ def other_configs_bench(args, dev):
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(steps):
             cap.replay()
         g1.record(stream)
         torch.cuda.synchronize()
-        warm = g0.elapsed_time(g1) / args.steps
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for k in range(args.warmup + args.steps):
+        warm = g0.elapsed_time(g1) / steps
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for k in range(args.warmup + steps):
             scrub.fill_(k & 255)
             if k >= args.warmup:
                 ev[k - args.warmup][0].record(stream)
@@ -775,12 +776,12 @@ def other_configs_bench(args, dev):
             if k >= args.warmup:
                 ev[k - args.warmup][1].record(stream)
         torch.cuda.synchronize()
-        cold = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+        cold = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
         target = step_bytes / (0.7 * PEAK_HBM_GBPS * 1e9) * 1e3
         out[name] = {
             "workload": f"{setup['arena'].name} one-rank ZeRO-1 share",
             "arena_params": setup["p"], "owned_params": owned, "nranks_simulated": n,
-            "buckets": len(setup["buckets"]), "step_bytes": step_bytes,
+            "buckets": len(setup["buckets"]), "step_bytes": step_bytes, "replays": steps,
             "graph_ms_per_step": warm, "cold_graph_ms_per_step": cold,
             "params_per_s": owned / (warm * 1e-3),
             "achieved_GBps": step_bytes / (warm * 1e-3) / 1e9,
