@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import gradient_reduce_zero_amd as grz
-from oracle.reduce import owned_chunk, reduce_scatter_mean
+from oracle.reduce import owned_chunk, reduce_scatter_mean, shard_segments
 from oracle.step import Hyper as OHyper
 from oracle.step import ddp_step
 from parity_util import assert_bits, host
@@ -254,22 +254,24 @@ def test_fused_refuses_what_it_cannot_hold():
     assert not grz.fused_timed_out(ws)
 
 
-def test_fused_wait_that_gives_up_writes_nothing_and_is_reported():
+@pytest.mark.parametrize("config", ["char_gpt", "gpt2_124m"])
+def test_fused_wait_that_gives_up_writes_nothing_and_is_reported(config):
     # A poll limit of one makes every workgroup that has to wait give up at
     # once.  The call still ends (every wait is bounded) and the flag is up.
-    # A workgroup that gave up writes nothing after its wait, so every
-    # 4096-element piece of the shard holds either its old state or the
-    # correct update (the three-kernel path's), never anything else; the
-    # step's check reports the give-up and clears the workspace, keeping its
-    # poll limit.  Restarted from the same state with the default limit, the
-    # next call is exact again.
-    a = arena("char_gpt")
+    # A workgroup that gave up writes nothing after its wait, so every piece
+    # of the shard holds either its old state or the correct update (the
+    # three-kernel path's), never anything else; the step's check reports the
+    # give-up and clears the workspace, keeping its poll limit.  Restarted
+    # from the same state with the default limit, the next call is exact
+    # again.  The char GPT's plan has one grid barrier; GPT-2 124M's (30,416
+    # pieces, 9 buckets) two, either of which can give up.
+    a = arena(config)
     p, n, rank = a.numel, 8, 5
-    inp, three, one = _one_rank_pair([(0, p)], p, n, rank)
+    buckets = grz.plan_buckets(a.numels) if config == "gpt2_124m" else [(0, p)]
+    inp, three, one = _one_rank_pair(buckets, p, n, rank)
     three.step(inp["incoming"], inp["peer_shards"], 1)
     old = [host(x) for x in one.state]
-    lo = one.chunk * one.state[0].numel()
-    old_arena = host(one.arena[lo:lo + one.state[0].numel()])
+    old_arena = host(one.arena)
     grz.fused_set_spin_limit(one.workspace, 1)
     one.step(inp["incoming"], inp["peer_shards"], 1)
     torch.cuda.synchronize()
@@ -281,19 +283,22 @@ def test_fused_wait_that_gives_up_writes_nothing_and_is_reported():
     assert int(words[3].item()) == 1 and int(words.abs().sum().item()) == 1
     new = [host(x) for x in three.state]
     got = [host(x) for x in one.state]
-    shard = old[0].size
-    updated = 0
-    for k0 in range(0, shard, grz.GRZ_PIECE):
-        sl = slice(k0, min(k0 + grz.GRZ_PIECE, shard))
-        same_old = all(np.array_equal(g[sl].view(np.uint32), o[sl].view(np.uint32))
-                       for g, o in zip(got, old))
-        same_new = all(np.array_equal(g[sl].view(np.uint32), w[sl].view(np.uint32))
-                       for g, w in zip(got, new))
-        assert same_old or same_new, f"piece at {k0}: neither its old state nor its update"
-        want_arena = host(three.arena[lo:lo + shard])[sl] if same_new else old_arena[sl]
-        assert np.array_equal(host(one.arena[lo:lo + shard])[sl], want_arena), k0
-        updated += same_new and not same_old
-    print(f"{updated} of {-(-shard // grz.GRZ_PIECE)} pieces updated before the give-up")
+    got_arena, new_arena = host(one.arena), host(three.arena)
+    updated = pieces = 0
+    for g0, length, c0 in shard_segments(buckets, n, one.chunk):
+        for k0 in range(0, length, grz.GRZ_PIECE):  # the pieces (tiles) of this segment
+            k1 = min(k0 + grz.GRZ_PIECE, length)
+            sl, asl = slice(c0 + k0, c0 + k1), slice(g0 + k0, g0 + k1)
+            same_old = all(np.array_equal(x[sl].view(np.uint32), o[sl].view(np.uint32))
+                           for x, o in zip(got, old))
+            same_new = all(np.array_equal(x[sl].view(np.uint32), w[sl].view(np.uint32))
+                           for x, w in zip(got, new))
+            assert same_old or same_new, f"piece at {c0 + k0}: neither old state nor update"
+            want = new_arena[asl] if same_new else old_arena[asl]
+            assert np.array_equal(got_arena[asl], want), f"arena piece at {g0 + k0}"
+            updated += same_new and not same_old
+            pieces += 1
+    print(f"{updated} of {pieces} pieces updated before the give-up")
     # Start again from the same state with the default poll limit.
     grz.fused_set_spin_limit(one.workspace, 0)
     one.state[0].copy_(inp["shard_master"])
