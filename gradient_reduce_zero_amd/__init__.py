@@ -24,6 +24,6 @@ from .binding import (StepScalars, adamw_args, dp_all_gather, dp_chunk_range, dp
 from .plan import (Hyper, owned_chunk, plan_buckets, resident_bytes, step_scalars, whole_arena,
                    zero_stage)
 from .step import (CapturedStep, DDPOneRank, DDPStep, OverlappedZero1, Zero1AllRanks,
-                   Zero1OneRank, Zero2AllRanks, one_rank_step)
+                   Zero1OneRank, Zero2AllRanks, one_rank_step, placed_zeros, state_phase)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -79,3 +79,39 @@ def test_one_rank_step_falls_back_to_plain_data_parallelism(capsys):
     assert "running ZeRO stage 0" in capsys.readouterr().err
     s0 = grz.one_rank_step([(0, 8 * 40)], 8, 3, master, device="cpu", stage=0)
     assert isinstance(s0, grz.DDPOneRank) and s0.flags == 0
+
+
+def test_shard_state_sits_at_the_phase_of_its_arena_position():
+    # GPT-2 1.5B at N = 4: chunks 1 and 3 start 16 elements past a 32-element
+    # boundary of the arena, so their fp32 state goes 16 elements (64 bytes)
+    # into a 128-byte line; chunks 0 and 2 and the DDP layout stay at 0.
+    import torch
+
+    import gradient_reduce_zero_amd as grz
+
+    p = arena("gpt2_1p5b").numel
+    assert [grz.state_phase(grz.whole_arena(p), 4, c) for c in range(4)] == [0, 16, 0, 16]
+    assert grz.state_phase(grz.whole_arena(p), 4, -1) == 0
+    # Two buckets at N = 4, chunk 1: the first has d = 64 - 0 = 0 (mod 32) over
+    # 64 elements, the second d = 256 + 1000 - 64 = 8 over 1000: the longer wins.
+    assert grz.state_phase([(0, 256), (256, 4000)], 4, 1) == 8
+    # d = 9 would leave the arrays off their 16-byte alignment: phase 0.
+    assert grz.state_phase([(0, 256), (256, 4004)], 4, 1) == 0
+    for phase in (0, 4, 16, 28):
+        t = grz.placed_zeros(1000, phase, "cpu")
+        assert t.numel() == 1000 and (t.data_ptr() // 4) % 32 == phase
+        assert not t.any()
+    master = torch.arange(4 * 48, dtype=torch.float32)
+    shard = master[48:96]
+    z = grz.Zero1OneRank(grz.whole_arena(4 * 48), 4, 0, shard, device="cpu")
+    for x in (*z.state, z.mean):
+        assert (x.data_ptr() // 4) % 32 == 16 and x.numel() == 48
+    assert torch.equal(z.state[0], shard) and not z.state[1].any()
+    assert z.state[0].data_ptr() != shard.data_ptr()  # the step holds a copy
+    zf = grz.Zero1OneRank(grz.whole_arena(4 * 48), 4, 0, shard, device="cpu", fused=True)
+    assert zf.mean is None
+    za = grz.Zero1AllRanks(grz.whole_arena(4 * 48), 4, master, device="cpu")
+    for c, (w, m, v), mean in zip(za.chunks, za.state, za.means):
+        want = 16 if c % 2 else 0
+        assert all((x.data_ptr() // 4) % 32 == want for x in (w, m, v, mean))
+        assert torch.equal(w, master[c * 48:(c + 1) * 48])
