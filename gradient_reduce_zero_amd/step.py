@@ -202,12 +202,17 @@ class DDPStep:
         _check_fused(self.workspace)
 
     def step(self, rank_grads, t, stream=None, token_counts=None):
+        self.enqueue(rank_grads, B.adamw_args(**step_scalars(self.hyper, t)), stream,
+                     token_counts)
+
+    def enqueue(self, rank_grads, args, stream=None, token_counts=None):
+        """The step's kernels; ``args`` host ``AdamWArgs``, a device tensor or a
+        captured step's ``StepScalars``."""
+        w, m, v = self.state
         if self.fused:
             if token_counts is not None:
                 raise ValueError("the fused step takes the plain mean")
-            w, m, v = self.state
-            B.zero1_fused_step(rank_grads, self.buckets, -1, w, m, v,
-                               B.adamw_args(**step_scalars(self.hyper, t)),
+            B.zero1_fused_step(rank_grads, self.buckets, -1, w, m, v, args,
                                self.hyper.max_norm, self.replicas, self.norm.partials,
                                self.workspace, self.norm.sqnorm, self.norm.scale,
                                flags=self.reduce_flags, stream=stream)
@@ -215,9 +220,7 @@ class DDPStep:
         B.dp_reduce_scatter_mean(rank_grads, self.buckets, -1, self.mean, self.norm.partials,
                                  flags=self.reduce_flags, stream=stream,
                                  token_counts=token_counts)
-        self.norm.run(self.hyper.max_norm, stream)
-        args = B.adamw_args(**step_scalars(self.hyper, t))
-        w, m, v = self.state
+        self.norm.run(self.hyper.max_norm, stream, args)
         B.zero1_adamw_gather(w, m, v, self.mean, self.buckets, self.n, -1, self.norm.scale,
                              args, self.replicas, stream=stream)
 

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import gradient_reduce_zero_amd as grz
-from oracle.reduce import owned_chunk, reduce_scatter_mean
+from oracle.reduce import owned_chunk, reduce_scatter_mean, shard_segments
 from oracle.ring import ring_all_reduce, ring_reduce_scatter
 from oracle.step import Hyper as OHyper
 from oracle.step import all_gather, bf16_round, clip_scale, ddp_step, grad_sqnorm, zero1_step
@@ -914,6 +914,38 @@ def test_captured_all_ranks_step_replays_match_eager():
         for r in range(n):
             assert_bits(host(graphed.state[r][0]), host(eager.state[r][0]), f"replay {t} master")
         assert_bits(host(graphed.replicas[3]), host(eager.replicas[3]), f"replay {t} replica")
+
+
+def test_captured_arena_layout_step_replays_match_eager():
+    # Every rank in arena layout (DDPStep with N replicas: one reduce, the norm,
+    # one optimizer launch) captured once and replayed; each replay against the
+    # eager step of the same number, and the eager steps against the oracle.
+    p, n = 8 * (4096 + 40) + 8 * 300, 8
+    buckets = [(8 * (4096 + 40), 8 * 300), (0, 8 * (4096 + 40))]
+    master = master_init(p, device=DEV)
+    hyper = grz.Hyper(max_norm=0.05)
+    eager = grz.DDPStep(buckets, n, master, hyper, device=DEV, nreplicas=n)
+    graphed = grz.DDPStep(buckets, n, master, hyper, device=DEV, nreplicas=n)
+    grads = [rank_grad(p, 1e-2, "bf16", grad_seed(1, r), device=DEV) for r in range(n)]
+    cap = grz.CapturedStep(lambda args, s: graphed.enqueue(grads, args, s), hyper, 1, 3)
+    states = oracle_states(host(master), buckets, n)
+    for t in range(1, 4):
+        eager.step(grads, t)
+        cap.replay()
+        torch.cuda.synchronize()
+        ref = zero1_step([host(g) for g in grads], "bf16", buckets, states, OHyper(max_norm=0.05),
+                         t)
+        states = ref["states"]
+        for j in range(3):
+            assert_bits(host(graphed.state[j]), host(eager.state[j]), f"replay {t} state {j}")
+        for r in (0, 5):
+            assert_bits(host(graphed.replicas[r]), host(eager.replicas[r]), f"replay {t} rep {r}")
+        assert_bits(host(eager.replicas[7]), ref["arena"], f"step {t} arena vs oracle")
+        w = host(eager.state[0])
+        for r in range(n):
+            segs = shard_segments(buckets, n, owned_chunk(r, n))
+            mine = np.concatenate([w[g:g + length] for g, length, _ in segs])
+            assert_bits(mine, ref["states"][r][0], f"step {t} rank {r} master vs oracle")
 
 
 def test_sixteen_ranks_zero1_step_matches_oracle():
