@@ -1245,20 +1245,23 @@ int reduce_entry(const void* const* rank_grads, int nranks, int64_t divisor, int
 // destination of element 0 of the segment, `elem` = destination element
 // bytes, `g` = elements per vector access): a store run that starts inside a
 // block turns every block it covers into two partial writes at the memory
-// side.  `keep` (bytes per element of other streams the kernel writes at the
-// source offsets, 0 for none) refuses a head that would move those off their
-// blocks.  Measured on MI355X, GPT-2 1.5B: the optimizer's bf16 writes into
-// a chunk 32 bytes off a block boundary ran 2.8 ms against 2.2 ms on one (at
-// N = 4); a head that moved its fp32 master, m and v 32 bytes off instead
-// ran 1.07 ms against 0.94 (at N = 8), hence `keep`.  For the optimizer and
-// the copy only, whose tiles carry no meaning; every element's result is the
-// same.
+// side.  `keep` (the byte addresses, at the segment's element 0, of the
+// `nkeep` other streams the kernel writes, `keep_elem` bytes per element)
+// refuses a head that would move one of them off its blocks.  Measured on
+// MI355X, GPT-2 1.5B: the optimizer's bf16 writes into a chunk 32 bytes off a
+// block boundary ran 2.8 ms against 2.2 ms on one (at N = 4); a head that
+// moved its fp32 master, m and v 32 bytes off instead ran 1.07 ms against
+// 0.94 (at N = 8), hence `keep`.  For the optimizer and the copy only, whose
+// tiles carry no meaning; every element's result is the same.
 void push_block_aligned(std::vector<Seg>& segs, Seg s, uintptr_t dst0, int elem, int g,
-                        int keep) {
+                        const uintptr_t* keep, int nkeep, int keep_elem) {
   const int64_t mis = static_cast<int64_t>(dst0 % 64);
   if (s.vec && mis % (elem * g) == 0 && mis != 0) {
     const int64_t head = (64 - mis) / elem;  // a multiple of g
-    if (head < s.len && (head * keep) % 64 == 0) {
+    bool ok = head < s.len;
+    for (int k = 0; k < nkeep && ok; ++k)
+      ok = keep[k] % 64 != 0 || (keep[k] + head * keep_elem) % 64 == 0;
+    if (ok) {
       Seg h = s;
       h.len = head;
       segs.push_back(h);
@@ -1313,7 +1316,8 @@ int gather_entry(const void* const* shards, int nranks, int units, const grz_buc
       s.len = p.len * units;
       s.chunk = r;
       s.vec = vr && s.src % 8 == 0 && s.dst % 8 == 0;
-      push_block_aligned(segs, s, reinterpret_cast<uintptr_t>(a.rep[0] + s.dst), 2, 8, 0);
+      push_block_aligned(segs, s, reinterpret_cast<uintptr_t>(a.rep[0] + s.dst), 2, 8, nullptr,
+                         0, 0);
     }
   }
   return launch_batches(segs, a, gather_kernel, stream, GRZ_AG_TILE, GRZ_AG_THREADS);
@@ -1579,10 +1583,15 @@ void* g_scratch_ptr[kScratchDevices];  // device address of `scratch`, per devic
 
 // The address of the current device's `scratch`, looked up on the first call
 // on that device (with it current) and kept.
-int scratch_for_current_device(void** out) {
+int scratch_for_current_device(hipStream_t stream, void** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GRZ_EHIP;
   if (dev < 0 || dev >= kScratchDevices) return GRZ_ERANGE;
+  if (stream != nullptr) {  // another device's stream would get this device's address
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return GRZ_EHIP;
+    if (sdev != dev) return GRZ_EINVAL;
+  }
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (g_scratch_ptr[dev] == nullptr) {
     void* ptr = nullptr;
@@ -1603,7 +1612,7 @@ int dp_grad_sqnorm_noalloc(const double* piece_sqnorm, int64_t npieces, double m
   if (npieces < 0) return GRZ_EINVAL;
   if (dp_grad_sqnorm_workspace(npieces) > GRZ_NOALLOC_SCRATCH_BYTES) return GRZ_ERANGE;
   void* ws = nullptr;
-  const int st = scratch_for_current_device(&ws);
+  const int st = scratch_for_current_device(stream, &ws);
   if (st != GRZ_OK) return st;
   return dp_grad_sqnorm(piece_sqnorm, npieces, max_norm, ws, sqnorm_out, clip_scale_out,
                         stream);
@@ -1681,9 +1690,13 @@ static int adamw_common(float* master, float* m, float* v, const float* mean_gra
     s.len = p.len;
     s.chunk = p.chunk;
     s.vec = vec_base && s.src % 4 == 0 && s.dst % 4 == 0;
-    if (nreplicas > 0)
-      push_block_aligned(segs, s, reinterpret_cast<uintptr_t>(replicas[0] + s.dst), 2, 4, 4);
-    else
+    if (nreplicas > 0) {
+      const uintptr_t keep[3] = {reinterpret_cast<uintptr_t>(master + s.src),
+                                 reinterpret_cast<uintptr_t>(m + s.src),
+                                 reinterpret_cast<uintptr_t>(v + s.src)};
+      push_block_aligned(segs, s, reinterpret_cast<uintptr_t>(replicas[0] + s.dst), 2, 4, keep,
+                         3, 4);
+    } else
       segs.push_back(s);
   }
   return launch_batches(segs, a, adamw_kernel, stream, GRZ_ADAM_TILE, GRZ_ADAM_THREADS);

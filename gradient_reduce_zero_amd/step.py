@@ -58,11 +58,9 @@ def state_phase(buckets, nranks, chunk):
     brings their reads onto whole 128-byte lines.  (GPT-2 1.5B at N = 4, chunk
     1, d = 16: the optimizer 1.97-2.07 ms at phase 0 against 1.87-1.89 ms at
     phase 16 on MI355X.)  Of the buckets' d_b mod 32 the one covering the most
-    owned elements is taken if it is 0 or 16: the optimizer takes a head only
-    when it moves the fp32 streams by a multiple of 64 bytes (16 elements), so
-    at another phase the arrays would stay off their lines and the bf16 stores
-    off their blocks.  0 for the DDP layout (``chunk`` -1), whose arrays are
-    arena-indexed."""
+    owned elements is taken, and only a multiple of 4, so that the arrays keep
+    the 16-byte alignment of the kernels' vector accesses; 0 for the DDP
+    layout (``chunk`` -1), whose arrays are arena-indexed."""
     if chunk < 0:
         return 0
     cover, shard = {}, 0
@@ -72,7 +70,7 @@ def state_phase(buckets, nranks, chunk):
         cover[d] = cover.get(d, 0) + cnt
         shard += cnt
     best = max(sorted(cover), key=lambda d: cover[d], default=0)
-    return best if best % 16 == 0 else 0
+    return best if best % 4 == 0 else 0
 
 
 def placed_zeros(numel, phase, device, dtype=torch.float32):

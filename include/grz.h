@@ -274,7 +274,8 @@ int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
  * which must be the stream's).  Same arguments, results (bit for bit) and
  * errors as dp_grad_sqnorm, plus GRZ_ERANGE when
  * dp_grad_sqnorm_workspace(npieces) exceeds GRZ_NOALLOC_SCRATCH_BYTES (more
- * than 33,546,240 pieces, about 1.4e11 gradient elements).  Nothing needs
+ * than 33,546,240 pieces, about 1.4e11 gradient elements) and GRZ_EINVAL when
+ * a non-null stream belongs to another device than the current one.  Nothing needs
  * clearing between calls: each call writes every scratch value it reads.  All
  * calls on one device share the array, so calls that overlap on one device
  * (different streams, or different host threads) race: order them.

@@ -948,6 +948,38 @@ def test_captured_arena_layout_step_replays_match_eager():
             assert_bits(mine, ref["states"][r][0], f"step {t} rank {r} master vs oracle")
 
 
+def test_zero1_state_placed_at_each_arena_phase_matches_oracle():
+    # Chunks of the long bucket land d = 24, 28, 0, 4 elements past a
+    # 32-element arena boundary (shard offset 8, chunk length 8196): each
+    # rank's state sits at that phase of its lines, so the optimizer's head
+    # brings its bf16 stores and its fp32 streams onto whole blocks together.
+    n = 4
+    buckets = [(0, 4 * 8), (4 * 8, 4 * 8196)]
+    p = 4 * 8 + 4 * 8196
+    master = master_init(p, device=DEV)
+    z = grz.Zero1AllRanks(buckets, n, master, grz.Hyper(max_norm=0.05), device=DEV)
+    phases = [grz.state_phase(buckets, n, c) for c in z.chunks]
+    assert phases == [28, 0, 4, 24]  # chunks 1, 2, 3, 0
+    for ph, (w, m, v), mean in zip(phases, z.state, z.means):
+        assert all((x.data_ptr() // 4) % 32 == ph for x in (w, m, v, mean))
+    states = oracle_states(host(master), buckets, n)
+    for t in (1, 2):
+        grads = [rank_grad(p, 1e-2, "bf16", grad_seed(t, r), device=DEV) for r in range(n)]
+        z.step(grads, t)
+        torch.cuda.synchronize()
+        ref = zero1_step([host(g) for g in grads], "bf16", buckets, states, OHyper(max_norm=0.05),
+                         t)
+        states = ref["states"]
+        assert ref["scale"] < 1
+        for r in range(n):
+            assert_bits(host(z.means[r]), ref["means"][r], f"phase test mean rank {r}")
+            for j in range(3):
+                assert_bits(host(z.state[r][j]), ref["states"][r][j],
+                            f"phase test state {j} rank {r}")
+        for r in range(n):
+            assert_bits(host(z.replicas[r]), ref["arena"], f"phase test replica {r}")
+
+
 def test_sixteen_ranks_zero1_step_matches_oracle():
     # The largest N the library takes, with two buckets and a ragged tail.
     p, n = 16 * (4096 + 40) + 16 * 8 * 100, 16

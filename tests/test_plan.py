@@ -96,8 +96,8 @@ def test_shard_state_sits_at_the_phase_of_its_arena_position():
     # 64 elements, the second d = 256 + 1008 - 64 = 16 over 1008: the longer wins.
     assert grz.state_phase([(0, 256), (256, 4032)], 4, 1) == 16
     assert grz.state_phase([(0, 4 * 2048), (4 * 2048, 4032)], 4, 1) == 0  # 2048 at d = 0
-    # d = 8 (the optimizer takes no head there) and d = 9: phase 0.
-    assert grz.state_phase([(0, 256), (256, 4000)], 4, 1) == 0
+    assert grz.state_phase([(0, 256), (256, 4000)], 4, 1) == 8  # d = 8 over 1000
+    # d = 9 would leave the arrays off their 16-byte alignment: phase 0.
     assert grz.state_phase([(0, 256), (256, 4004)], 4, 1) == 0
     for phase in (0, 4, 16, 28):
         t = grz.placed_zeros(1000, phase, "cpu")
