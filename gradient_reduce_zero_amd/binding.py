@@ -171,17 +171,25 @@ def dp_reduce_scatter_mean(rank_grads, buckets, chunk, mean_out, piece_sqnorm=No
 
 
 class StepScalars:
-    """The AdamW scalars of a captured step in device memory: ``table`` (rows of
-    7 float32 values, one per step), ``counter`` (int64, the next row) and
+    """The AdamW scalars of a step in device memory: ``table`` (rows of 7
+    float32 values, one per step), ``counter`` (int64, the next row) and
     ``current`` (the row the optimizer reads).  The first call of a step that
     needs ``current`` advances it -- the norm in its own last launch
     (``dp_grad_sqnorm_step_args``), else the optimizer's entry point with a
     ``grz_step_args_next`` launch before its own; ``advanced`` records that it
-    was done for the step being enqueued."""
+    was done for the step being enqueued.
+
+    One object stands for one enqueued step: a captured step enqueues once and
+    each replay advances the scalars again; eager steps take ``next()`` (the
+    same tensors, not yet advanced) for each further step."""
 
     def __init__(self, table, counter, current):
         self.table, self.counter, self.current = table, counter, current
         self.advanced = False
+
+    def next(self):
+        """The scalars of the following step (same device tensors)."""
+        return StepScalars(self.table, self.counter, self.current)
 
 
 def dp_grad_sqnorm(piece_sqnorm, max_norm, workspace, sqnorm_out, clip_scale_out,

@@ -916,6 +916,35 @@ def test_captured_all_ranks_step_replays_match_eager():
         assert_bits(host(graphed.replicas[3]), host(eager.replicas[3]), f"replay {t} replica")
 
 
+def test_device_step_scalars_advance_once_per_eager_step():
+    # Eager steps fed from a device table: each step's StepScalars object
+    # advances the row once (the norm's last launch), next() gives the
+    # following step's; the same bits as host scalars step by step.
+    p, n = 4 * 4096 * 2 + 4 * 40, 4
+    buckets = [(0, p)]
+    master = master_init(p, device=DEV)
+    hyper = grz.Hyper(max_norm=0.05, warmup=3)
+    host_args = grz.Zero1AllRanks(buckets, n, master, hyper, device=DEV)
+    dev_args = grz.Zero1AllRanks(buckets, n, master, hyper, device=DEV)
+    rows = [[s["lr"], s["beta1"], s["beta2"], s["eps"], s["weight_decay"], s["bias_corr1"],
+             s["bias_corr2"]] for s in (grz.step_scalars(hyper, t) for t in range(1, 4))]
+    sc = grz.StepScalars(torch.tensor(rows, dtype=torch.float32, device=DEV),
+                         torch.zeros(1, dtype=torch.int64, device=DEV),
+                         torch.zeros(7, dtype=torch.float32, device=DEV))
+    for t in range(1, 4):
+        grads = [rank_grad(p, 1e-2, "bf16", grad_seed(t, r), device=DEV) for r in range(n)]
+        host_args.step(grads, t)
+        dev_args.enqueue(grads, sc)
+        assert sc.advanced
+        sc = sc.next()
+        torch.cuda.synchronize()
+        assert int(sc.counter.item()) == t
+        for r in range(n):
+            for j in range(3):
+                assert_bits(host(dev_args.state[r][j]), host(host_args.state[r][j]),
+                            f"step {t} rank {r} state {j}")
+
+
 def test_captured_arena_layout_step_replays_match_eager():
     # Every rank in arena layout (DDPStep with N replicas: one reduce, the norm,
     # one optimizer launch) captured once and replayed; each replay against the
