@@ -1126,11 +1126,25 @@ int64_t grid_for(int64_t units, int block) {
   return grid < hw ? grid : hw;
 }
 
+template <typename T> struct NoDeduce { using type = T; };
+
+// Launches `kernel` and returns the status of this launch alone (the return
+// value of hipLaunchKernel): an error the caller has not collected yet stays
+// in the runtime's last-error slot, neither cleared nor taken for ours.  The
+// argument types are the kernel's own, so each params entry points at an
+// object of exactly its parameter's type.
+template <typename... A>
+int launch(void (*kernel)(A...), dim3 grid, dim3 block, hipStream_t stream,
+           typename NoDeduce<A>::type... a) {
+  void* params[] = {static_cast<void*>(&a)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, params, 0,
+                         stream) == hipSuccess ? GRZ_OK : GRZ_EHIP;
+}
+
 template <typename Args>
 int launch_batches(std::vector<Seg>& segs, Args& args,
                    void (*kernel)(const Args), hipStream_t stream,
                    int64_t tile_elems = GRZ_PIECE, int block = kThreads) {
-  (void)hipGetLastError();  // clear a stale error so the check below is ours
   for (size_t first = 0; first < segs.size(); first += kMaxSegs) {
     const size_t cnt = segs.size() - first < static_cast<size_t>(kMaxSegs)
                            ? segs.size() - first : static_cast<size_t>(kMaxSegs);
@@ -1144,9 +1158,8 @@ int launch_batches(std::vector<Seg>& segs, Args& args,
     args.nsegs = static_cast<int>(cnt);
     args.ntiles = tiles;
     const int64_t grid = grid_for(tiles, block);
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(block), 0, stream,
-                       args);
-    if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
+    const int st = launch(kernel, dim3(static_cast<unsigned>(grid)), dim3(block), stream, args);
+    if (st != GRZ_OK) return st;
   }
   return GRZ_OK;
 }
@@ -1527,23 +1540,20 @@ int sqnorm_entry(const double* piece_sqnorm, int64_t npieces, double max_norm,
   int64_t sizes[8];
   const int levels = sqnorm_levels(npieces, sizes, 8);
   if (levels > 0 && workspace == nullptr) return GRZ_EINVAL;
-  (void)hipGetLastError();
   const double* in = piece_sqnorm;
   int64_t n = npieces;
   double* ws = static_cast<double*>(workspace);
   for (int i = 0; i < levels; ++i) {
     const unsigned grid = static_cast<unsigned>(grid_for(sizes[i], kThreads));
-    hipLaunchKernelGGL(sqnorm_level_kernel, dim3(grid), dim3(kThreads), 0, stream, in, n,
-                       sizes[i], ws);
-    if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
+    const int st = launch(sqnorm_level_kernel, dim3(grid), dim3(kThreads), stream, in, n,
+                          sizes[i], ws);
+    if (st != GRZ_OK) return st;
     in = ws;
     n = sizes[i];
     ws += sizes[i];
   }
-  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kThreads), 0, stream, in, n, max_norm,
-                     sqnorm_out, clip_scale_out, next);
-  if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
-  return GRZ_OK;
+  return launch(sqnorm_final_kernel, dim3(1), dim3(kThreads), stream, in, n, max_norm,
+                sqnorm_out, clip_scale_out, next);
 }
 
 }  // namespace
@@ -1633,11 +1643,10 @@ int dp_grad_sqnorm_of(const float* grad, int64_t n, double max_norm, void* works
   if (npieces > static_cast<int64_t>(kReduceFan) * kReduceFan * kReduceFan) return GRZ_ERANGE;
   double* partials = static_cast<double*>(workspace);
   if (npieces > 0) {
-    (void)hipGetLastError();
     const unsigned grid = static_cast<unsigned>(grid_for(npieces, kThreads));
-    hipLaunchKernelGGL(piece_sqnorm_kernel, dim3(grid), dim3(kThreads), 0, stream, grad, n,
-                       npieces, aligned(grad, 16) ? 1 : 0, partials);
-    if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
+    const int st = launch(piece_sqnorm_kernel, dim3(grid), dim3(kThreads), stream, grad, n,
+                          npieces, aligned(grad, 16) ? 1 : 0, partials);
+    if (st != GRZ_OK) return st;
   }
   return dp_grad_sqnorm(partials, npieces, max_norm, partials + npieces, sqnorm_out,
                         clip_scale_out, stream);
@@ -1739,11 +1748,8 @@ int grz_step_args_next(const grz_adamw_args* table, int64_t count, int64_t* coun
                        grz_adamw_args* current, hipStream_t stream) {
   const int st = check_step_args(table, count, counter, current);
   if (st != GRZ_OK) return st;
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(args_next_kernel, dim3(1), dim3(64), 0, stream,
-                     StepArgsNext{table, count, counter, current});
-  if (hipGetLastError() != hipSuccess) return GRZ_EHIP;
-  return GRZ_OK;
+  return launch(args_next_kernel, dim3(1), dim3(64), stream,
+                StepArgsNext{table, count, counter, current});
 }
 
 int zero1_all_gather(const uint16_t* const* shards, int nranks, const grz_bucket* buckets,
@@ -1887,11 +1893,8 @@ int fused_launch(const void* kernel, const void* const* rank_grads, int nranks,
     a.bc2 = args->bias_corr2;
   }
   void* params[] = {&a};
-  (void)hipGetLastError();
-  if (hipLaunchCooperativeKernel(kernel, dim3(grid), dim3(kThreads), params, 0, stream) !=
-      hipSuccess)
-    return GRZ_EHIP;
-  return hipGetLastError() == hipSuccess ? GRZ_OK : GRZ_EHIP;
+  return hipLaunchCooperativeKernel(kernel, dim3(grid), dim3(kThreads), params, 0, stream) ==
+                 hipSuccess ? GRZ_OK : GRZ_EHIP;
 }
 
 }  // namespace
