@@ -130,15 +130,23 @@ def test_gpt2_124m_reverse_layer_buckets_10_steps():
     assert ref["scale"] < 1
 
 
-def _tiled_sqnorm(tensors_for, chunk, kind, length, tile=1 << 25):
-    """Oracle norm of the mean over [0, length) of a shard, streamed in tiles."""
-    total = []
-    for lo in range(0, length, tile):
+def _tiled_sqnorm(tensors_for, chunk, kind, length, wire=None, divisor=None, tile=1 << 24,
+                  workers=8):
+    """Oracle norm of the mean (with a wire precision or a divisor, if given)
+    over [0, length) of a shard: tiles folded by the oracle in worker threads
+    (NumPy releases the interpreter lock inside its loops), the tile sums
+    added in tile order."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def part(lo):
         hi = min(length, lo + tile)
-        contribs = [host(t[lo:hi]) for t in tensors_for]
-        mean = chunk_mean([widen(c, kind) for c in contribs], chunk)
-        total.append(np.sum(np.square(mean.astype(np.float64))))
-    return float(np.sum(total))
+        m = chunk_mean([widen(host(t[lo:hi]), kind) for t in tensors_for], chunk, True, wire,
+                       divisor)
+        return float(np.sum(np.square(m.astype(np.float64))))
+
+    with ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(part, range(0, length, tile)))
+    return float(np.sum(parts))
 
 
 def _clip_factor_bits_agree(got_scale, scale, what):
@@ -236,6 +244,58 @@ def test_llama_7b_one_rank_share_sampled(n):
         c = owned_chunk(j, n)
         assert torch.equal(pipe.arena[c * shard:(c + 1) * shard], inp["peer_shards"][j]), j
     assert torch.equal(pipe.arena[lo:lo + shard], pipe.state[0].to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("mode", ["bf16_wire", "token_weighted"])
+def test_llama_7b_one_rank_share_modes_sampled(mode):
+    # The 7B share (N = 8, rank 0, one bucket) as `bench.py --wire bf16` and
+    # `--token-weighted` run it, one step: the mean at 200 k samples against the
+    # oracle's fold (each hop's partial sum rounded to bf16, or the sum divided
+    # by the global token count), the norm against the oracle's over the whole
+    # shard in tiles, AdamW on the samples and the own chunk of the arena bit
+    # for bit.
+    a = arena("llama_7b")
+    p, n, rank = a.numel, 8, 0
+    buckets = grz.whole_arena(p)
+    chunk = owned_chunk(rank, n)
+    shard = p // n
+    npieces = grz.dp_piece_count(buckets, n)
+    inp = onerank_inputs(shard, n, rank, npieces, grz.GRZ_PIECE, device=DEV)
+    wire, counts = None, None
+    if mode == "bf16_wire":
+        wire = "bf16"
+    else:  # the bench's counts: unequal, their sum not a power of two
+        counts = [4096 + 1000 * (j % 3) - 1000 for j in range(n)]
+        counts[0] += 123
+    divisor = None if counts is None else sum(counts)
+    pipe = grz.Zero1OneRank(buckets, n, rank, inp["shard_master"], device=DEV, arena_numel=p,
+                            reduce_flags=grz.GRZ_BF16_WIRE if wire else 0)
+    idx = sample_indices(shard, 200_000, 11, extra=[4095, 4096, 4097, (1 << 31) - 1, 1 << 31])
+    w = gather_host(pipe.state[0], idx)
+    peers = host(inp["partials"])
+    mask = np.ones(npieces, bool)
+    for first, cnt in pipe.own_piece_slots():
+        mask[first:first + cnt] = False
+    pipe.norm.partials.copy_(inp["partials"])
+    pipe.reduce(inp["incoming"], token_counts=counts)
+    pipe.update(1)
+    pipe.gather(inp["peer_shards"])
+    torch.cuda.synchronize()
+    want = chunk_mean([widen(gather_host(t, idx), "bf16") for t in inp["incoming"]], chunk,
+                      True, wire, divisor)
+    assert_bits(gather_host(pipe.mean, idx), want, f"7B {mode} mean (sampled)")
+    sq = _tiled_sqnorm(inp["incoming"], chunk, "bf16", shard, wire, divisor)
+    sq += float(np.sum(peers[mask]))
+    assert math.isclose(pipe.norm.sqnorm.item(), sq, rel_tol=1e-10), mode
+    scale = clip_scale(sq, 1.0)
+    assert scale < 1
+    _clip_factor_bits_agree(pipe.norm.scale.item(), scale, f"7B {mode}")
+    z = np.zeros_like(w)
+    w1, m1, v1 = adamw(w, z, z, want * scale, **OHyper().scalars(1))
+    for j, x in enumerate((w1, m1, v1)):
+        assert_bits(gather_host(pipe.state[j], idx), x, f"7B {mode} state {j} (sampled)")
+    assert_bits(gather_host(pipe.arena, idx + chunk * shard), bf16_round(w1),
+                f"7B {mode} own chunk")
 
 
 def test_llama_7b_ddp_one_rank_sampled():
