@@ -49,7 +49,7 @@ def settle():
     gc.freeze()
 
 
-def onerank_setup(name, n, rank, device, reduce_flags=0, bucket_plan="default"):
+def onerank_setup(name, n, rank, device, reduce_flags=0, bucket_plan="default", recv="tiled"):
     import torch  # noqa: F401
 
     import gradient_reduce_zero_amd as grz
@@ -68,8 +68,12 @@ def onerank_setup(name, n, rank, device, reduce_flags=0, bucket_plan="default"):
     pipe = grz.Zero1OneRank(buckets, n, rank, inp["shard_master"], device=device, arena_numel=p,
                             reduce_flags=reduce_flags)
     pipe.norm.partials.copy_(inp["partials"])
+    # What the reduce reads: the N ranks' chunks in one tiled receive buffer,
+    # or as N separate tensors.
+    inp["recv"] = (grz.tiled_receive(inp["incoming"], buckets, n, chunk) if recv == "tiled"
+                   else inp["incoming"])
     return dict(arena=a, p=p, n=n, rank=rank, chunk=chunk, shard=shard, buckets=buckets,
-                npieces=npieces, inp=inp, pipe=pipe)
+                npieces=npieces, inp=inp, pipe=pipe, recv=recv)
 
 
 def bytes_per_owned(n, grad_bytes=2):
@@ -746,7 +750,7 @@ def cold_bench(args, pipe, inp, stream, dev, t, step_bytes):
         scrub.fill_(k & 255)
         if k >= args.warmup:
             ev[k - args.warmup][0].record(stream)
-        pipe.step(inp["incoming"], inp["peer_shards"], t, stream)
+        pipe.step(inp["recv"], inp["peer_shards"], t, stream)
         if k >= args.warmup:
             ev[k - args.warmup][1].record(stream)
         t += 1
@@ -784,7 +788,7 @@ def other_configs_bench(args, dev):
         owned = setup["shard"]
         step_bytes = owned * sum(bytes_per_owned(n).values())
         count = 2 * (args.warmup + steps)
-        cap = grz.CapturedStep(lambda a, s: (pipe.reduce(inp["incoming"], s),
+        cap = grz.CapturedStep(lambda a, s: (pipe.reduce(inp["recv"], s),
                                              pipe.update(None, s, args=a),
                                              pipe.gather(inp["peer_shards"], s)),
                                pipe.hyper, 1, count)
@@ -813,7 +817,8 @@ def other_configs_bench(args, dev):
         out[name] = {
             "workload": f"{setup['arena'].name} one-rank ZeRO-1 share",
             "arena_params": setup["p"], "owned_params": owned, "nranks_simulated": n,
-            "buckets": len(setup["buckets"]), "step_bytes": step_bytes, "replays": steps,
+            "buckets": len(setup["buckets"]), "recv_layout": setup["recv"],
+            "step_bytes": step_bytes, "replays": steps,
             "graph_ms_per_step": warm, "cold_graph_ms_per_step": cold,
             "params_per_s": owned / (warm * 1e-3),
             "achieved_GBps": step_bytes / (warm * 1e-3) / 1e9,
@@ -949,6 +954,10 @@ def main():
                     help="the one-rank share's bucket plan: the workload's own (one bucket "
                          "for the whole arena, GPT-2 124M's nine 25 MiB buckets), the whole "
                          "arena, or reverse-layer buckets of 25 MiB of gradient")
+    ap.add_argument("--recv", choices=["tiled", "ranks"], default="tiled",
+                    help="how the one-rank share's reduce reads the N ranks' chunks: one "
+                         "receive buffer with each piece's N values side by side (the "
+                         "default), or N separate shard-compact tensors")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip what the default run times after the headline workload: the "
                          "smaller one-rank shares (char GPT, GPT-2 124M and 1.5B, as graph "
@@ -1021,7 +1030,7 @@ def main():
     log(f"setting up {args.config} one-rank share, N={args.nranks}")
     flags = grz.GRZ_BF16_WIRE if args.wire == "bf16" else 0
     setup = onerank_setup(args.config, args.nranks, 0, dev, reduce_flags=flags,
-                          bucket_plan=args.bucket_plan)
+                          bucket_plan=args.bucket_plan, recv=args.recv)
     pipe, inp = setup["pipe"], setup["inp"]
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -1030,7 +1039,7 @@ def main():
         f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
 
     def reduce():
-        pipe.reduce(inp["incoming"], stream, token_counts=counts)
+        pipe.reduce(inp["recv"], stream, token_counts=counts)
 
     t = 1
     for _ in range(args.warmup):
@@ -1103,6 +1112,7 @@ def main():
             "rank": 0, "owned_chunk": setup["chunk"], "buckets": len(setup["buckets"]),
             "grad_dtype": "bf16", "state_dtype": "fp32", "weights_dtype": "bf16",
             "clip": 1.0, "wire": args.wire, "token_counts": counts,
+            "recv_layout": setup["recv"],
         },
         "achieved_GBps": step_gbps,
         "pct_of_peak_hbm": 100.0 * step_gbps / PEAK_HBM_GBPS,
@@ -1131,7 +1141,7 @@ def main():
         },
     }
     if args.graph:
-        cap = grz.CapturedStep(lambda a, s: (pipe.reduce(inp["incoming"], s, token_counts=counts),
+        cap = grz.CapturedStep(lambda a, s: (pipe.reduce(inp["recv"], s, token_counts=counts),
                                              pipe.update(None, s, args=a),
                                              pipe.gather(inp["peer_shards"], s)),
                                pipe.hyper, t, args.warmup + args.steps)

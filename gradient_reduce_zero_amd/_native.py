@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libgrz.so")
 GRZ_OK, GRZ_EINVAL, GRZ_EINDIVISIBLE, GRZ_EALIGN, GRZ_EHIP, GRZ_ERANGE = range(6)
 GRZ_F32, GRZ_BF16, GRZ_F64 = 0, 1, 2
 (GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT, GRZ_BF16_WIRE, GRZ_IN_RANGE, GRZ_ARGS_DEVICE,
- GRZ_OUT_GLOBAL) = (1, 2, 4, 8, 16, 32, 64)
+ GRZ_OUT_GLOBAL, GRZ_IN_TILED) = (1, 2, 4, 8, 16, 32, 64, 128)
 GRZ_MAX_RANKS = 16
 GRZ_PIECE = 4096
 GRZ_NOALLOC_SCRATCH_BYTES = 65536
@@ -46,6 +46,7 @@ SIGNATURES = {
     "dp_piece_count": (_i64, [_BP, _i, _i, _i]),
     "dp_piece_offset": (_i64, [_BP, _i, _i, _i, _i, _i]),
     "dp_shard_numel": (_i64, [_BP, _i, _i, _i, _i]),
+    "dp_tiled_numel": (_i64, [_BP, _i, _i, _i, _i]),
     "dp_reduce_scatter_mean": (_i, [_pp, _i, _i, _BP, _i, _i, _i, _vp, _vp, _vp]),
     "dp_reduce_scatter_mean_range": (_i, [_pp, _i, _i, _BP, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "dp_reduce_scatter_weighted": (_i, [_pp, ctypes.POINTER(_i64), _i, _i, _BP, _i, _i, _i, _i,

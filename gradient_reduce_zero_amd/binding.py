@@ -108,6 +108,28 @@ def dp_shard_numel(buckets, nranks, chunk, flags=0):
     return _shard_numel(_key(buckets), int(nranks), int(chunk), int(flags))
 
 
+@functools.lru_cache(maxsize=1024)
+def _tiled_numel(key, nranks, chunk, flags):
+    arr, nb = _bucket_array_of(key)
+    return _neg_check("dp_tiled_numel", lib().dp_tiled_numel(arr, nb, nranks, chunk, flags))
+
+
+def dp_tiled_numel(buckets, nranks, chunk, flags=0):
+    """Elements of chunk ``chunk``'s ``GRZ_IN_TILED`` receive buffer."""
+    return _tiled_numel(_key(buckets), int(nranks), int(chunk), int(flags))
+
+
+class Tiled:
+    """The N ranks' values of one chunk in one receive buffer (``GRZ_IN_TILED``):
+    the chunk's pieces in plan order, each piece's slot holding the N ranks'
+    values side by side, ``GRZ_PIECE`` elements apiece (``dp_tiled_numel``
+    elements).  Passed to ``dp_reduce_scatter_mean`` in place of the list of
+    N rank tensors; the call then adds ``GRZ_IN_COMPACT | GRZ_IN_TILED``."""
+
+    def __init__(self, buffer, nranks):
+        self.buffer, self.nranks = buffer, int(nranks)
+
+
 def dp_grad_sqnorm_workspace(npieces):
     return int(lib().dp_grad_sqnorm_workspace(int(npieces)))
 
@@ -116,20 +138,26 @@ def dp_grad_sqnorm_workspace(npieces):
 
 def dp_reduce_scatter_mean(rank_grads, buckets, chunk, mean_out, piece_sqnorm=None, flags=0,
                            stream=None, bucket_range=None, token_counts=None):
-    """Ring-order reduce-scatter-mean of ``rank_grads`` (one tensor per rank).
+    """Ring-order reduce-scatter-mean of ``rank_grads`` (one tensor per rank, or
+    a ``Tiled`` receive buffer).
 
     ``bucket_range = (first, count)`` restricts the call to those buckets of
     the plan (``dp_reduce_scatter_mean_range``).  ``token_counts`` (one int per
     rank) makes it the token-weighted mean of per-rank gradient sums
     (``dp_reduce_scatter_weighted``)."""
-    n = len(rank_grads)
+    tiled = isinstance(rank_grads, Tiled)
+    n = rank_grads.nranks if tiled else len(rank_grads)
     if not 1 <= n <= N.GRZ_MAX_RANKS:
         raise ValueError(f"{n} ranks; 1..{N.GRZ_MAX_RANKS} supported")
-    dt = rank_grads[0].dtype
+    dt = rank_grads.buffer.dtype if tiled else rank_grads[0].dtype
     if dt not in _KIND:
         raise TypeError(f"gradient dtype {dt} not supported")
     kind = _KIND[dt]
     buckets = list(buckets)
+    if tiled:
+        if chunk < 0 or flags & N.GRZ_IN_RANGE:
+            raise ValueError("a tiled receive buffer holds one chunk (chunk >= 0, no GRZ_IN_RANGE)")
+        flags |= N.GRZ_IN_COMPACT | N.GRZ_IN_TILED
     if chunk >= 0:
         shard = dp_shard_numel(buckets, n, chunk, flags & N.GRZ_UNEVEN)
         need_in = shard if flags & N.GRZ_IN_COMPACT else _extent(buckets)
@@ -142,8 +170,15 @@ def dp_reduce_scatter_mean(rank_grads, buckets, chunk, mean_out, piece_sqnorm=No
         sel = [b for b in buckets[bucket_range[0]:bucket_range[0] + bucket_range[1]] if b[1] > 0]
         need_in = _extent(sel) - min((o for o, _ in sel), default=0)
     same = _BF16_LIKE if kind == N.GRZ_BF16 else (dt,)
-    ptrs = (ctypes.c_void_p * n)(*[_dev(g, f"rank_grads[{j}]", same, need_in).value
-                                   for j, g in enumerate(rank_grads)])
+    if tiled:
+        buf = rank_grads.buffer
+        base = _dev(buf, "receive buffer", same,
+                    dp_tiled_numel(buckets, n, chunk, flags & N.GRZ_UNEVEN)).value
+        step = N.GRZ_PIECE * buf.element_size()
+        ptrs = (ctypes.c_void_p * n)(*[base + j * step for j in range(n)])
+    else:
+        ptrs = (ctypes.c_void_p * n)(*[_dev(g, f"rank_grads[{j}]", same, need_in).value
+                                       for j, g in enumerate(rank_grads)])
     out = _dev(mean_out, "mean_out", (_OUT[kind],), need_out)
     part = None
     if piece_sqnorm is not None:

@@ -337,6 +337,12 @@ __device__ __forceinline__ double block_sum_fixed(double s, double* lds) {
 template <typename TIn>
 struct RsArgs {
   const TIn* rank[GRZ_MAX_RANKS];
+  // 0: rank j's values of a segment start at rank[j] + src.  Otherwise
+  // (GRZ_IN_TILED) piece k of a segment sits at rank[j] + src + k * tstride:
+  // one receive buffer holding, piece by piece, the N ranks' values of each
+  // piece side by side (rank[j] = buffer + j * GRZ_PIECE, tstride = N *
+  // GRZ_PIECE), so that a tile's loads are one contiguous run.
+  int64_t tstride;
   typename AccOf<TIn>::type* out;
   double* partials;
   int64_t ntiles;
@@ -455,6 +461,7 @@ __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void rs_mean_kernel(const RsA
     const int64_t e0 = piece * GRZ_PIECE;
     const int64_t left = s.len - e0;  // > 0
     const int c = s.chunk;
+    const int64_t ib = a.tstride ? s.src + piece * a.tstride : s.src + e0;  // tile's input
     double sq = 0.0;
     bool done = false;
     if constexpr (GRZ_RS_BATCH && NR > 0 && sizeof(TIn) < 8) {
@@ -467,7 +474,7 @@ __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void rs_mean_kernel(const RsA
 #pragma unroll
         for (int k0 = 0; k0 < K; k0 += KB) {
           Acc acc[KB][G];
-          fold_tile<TIn, NR, WIRE, KB>(a.rank, c, s.src + e0 + lane * G, k0, acc);
+          fold_tile<TIn, NR, WIRE, KB>(a.rank, c, ib + lane * G, k0, acc);
 #pragma unroll
           for (int kk = 0; kk < KB; ++kk) {
             const int k = k0 + kk;
@@ -490,7 +497,7 @@ __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void rs_mean_kernel(const RsA
         const int64_t e = e0 + rel;
         if (s.vec && rel + G <= left) {
           Acc acc[G];
-          fold_vec<TIn, NR, WIRE>(a.rank, a.nranks, c, s.src + e, acc);
+          fold_vec<TIn, NR, WIRE>(a.rank, a.nranks, c, ib + rel, acc);
 #pragma unroll
           for (int i = 0; i < G; ++i) {
             if (a.average) acc[i] = a.pow2 ? acc[i] * inv : acc[i] / nf;
@@ -500,7 +507,7 @@ __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void rs_mean_kernel(const RsA
         } else {
           for (int i = 0; i < G; ++i) {
             if (rel + i >= left) break;
-            Acc v = fold_one<TIn, NR, WIRE>(a.rank, a.nranks, c, s.src + e + i);
+            Acc v = fold_one<TIn, NR, WIRE>(a.rank, a.nranks, c, ib + rel + i);
             if (a.average) v = a.pow2 ? v * inv : v / nf;
             sq = __fma_rn(static_cast<double>(v), static_cast<double>(v), sq);
             a.out[s.dst + e + i] = v;
@@ -1067,7 +1074,7 @@ int check_plan(const grz_bucket* buckets, int nbuckets, int nranks, int chunk, i
   if (nbuckets < 0 || (nbuckets > 0 && buckets == nullptr)) return GRZ_EINVAL;
   if (chunk < -1 || chunk >= nranks) return GRZ_EINVAL;
   if (flags & ~(GRZ_SUM | GRZ_UNEVEN | GRZ_IN_COMPACT | GRZ_BF16_WIRE | GRZ_IN_RANGE |
-                GRZ_OUT_GLOBAL))
+                GRZ_OUT_GLOBAL | GRZ_IN_TILED))
     return GRZ_EINVAL;
   for (int b = 0; b < nbuckets; ++b) {
     if (buckets[b].offset < 0 || buckets[b].length < 0) return GRZ_ERANGE;
@@ -1088,6 +1095,7 @@ struct PlanSeg {
   int chunk;
   int bucket;
   int64_t input;    // offset in the rank inputs when they hold a bucket range only
+  int64_t lpiece0;  // (chunk >= 0) pieces of the chunk in the buckets before this one
 };
 
 // The segments of buckets [first, first + count) of the plan; offsets and
@@ -1096,7 +1104,7 @@ std::vector<PlanSeg> plan_segments(const grz_bucket* buckets, int nbuckets, int 
                                    int first = 0, int count = -1) {
   if (count < 0) count = nbuckets - first;
   std::vector<PlanSeg> out;
-  int64_t piece = 0, compact = 0;
+  int64_t piece = 0, compact = 0, lpiece = 0;
   for (int b = 0; b < nbuckets; ++b) {
     const bool take = b >= first && b < first + count;
     for (int c = 0; c < n; ++c) {
@@ -1105,9 +1113,12 @@ std::vector<PlanSeg> plan_segments(const grz_bucket* buckets, int nbuckets, int 
       if (chunk < 0 || c == chunk) {
         if (cnt > 0 && take) {
           const int64_t g = buckets[b].offset + off;
-          out.push_back({g, chunk < 0 ? g : compact, cnt, piece, c, b, g});
+          out.push_back({g, chunk < 0 ? g : compact, cnt, piece, c, b, g, lpiece});
         }
-        if (chunk >= 0) compact += cnt;
+        if (chunk >= 0) {
+          compact += cnt;
+          lpiece += ceil_div(cnt, GRZ_PIECE);
+        }
       }
       piece += ceil_div(cnt, GRZ_PIECE);
     }
@@ -1202,11 +1213,12 @@ int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>
   args.pow2 = (divisor & (divisor - 1)) == 0;
   const bool compact_in = (flags & GRZ_IN_COMPACT) != 0;
   const bool out_global = (flags & GRZ_OUT_GLOBAL) != 0;
+  args.tstride = (flags & GRZ_IN_TILED) ? static_cast<int64_t>(n) * GRZ_PIECE : 0;
   std::vector<Seg> segs;
   segs.reserve(ps.size());
   for (const PlanSeg& p : ps) {
     Seg s{};
-    s.src = compact_in ? p.compact : p.input;
+    s.src = args.tstride ? p.lpiece0 * args.tstride : compact_in ? p.compact : p.input;
     s.dst = out_global ? p.global : p.compact;
     s.len = p.len;
     s.piece0 = p.piece0;
@@ -1343,7 +1355,7 @@ int gather_entry(const void* const* shards, int nranks, int units, const grz_buc
 
 extern "C" {
 
-int grz_version(void) { return 101; }
+int grz_version(void) { return 102; }
 
 const char* grz_strerror(int status) {
   switch (status) {
@@ -1423,6 +1435,21 @@ int64_t dp_shard_numel(const grz_bucket* buckets, int nbuckets, int nranks, int 
   return total;
 }
 
+int64_t dp_tiled_numel(const grz_bucket* buckets, int nbuckets, int nranks, int chunk,
+                       int flags) {
+  if (chunk < 0) return -GRZ_EINVAL;
+  const int st = check_plan(buckets, nbuckets, nranks, chunk, flags);
+  if (st != GRZ_OK) return -st;
+  int64_t pieces = 0;
+  for (int b = 0; b < nbuckets; ++b) {
+    int64_t off, cnt;
+    chunk_of(buckets[b].length, nranks, chunk, &off, &cnt);
+    pieces += ceil_div(cnt, GRZ_PIECE);
+  }
+  if (pieces > (INT64_MAX >> 4) / (static_cast<int64_t>(nranks) * GRZ_PIECE)) return -GRZ_ERANGE;
+  return pieces * nranks * GRZ_PIECE;
+}
+
 int dp_reduce_scatter_mean(const void* const* rank_grads, int nranks, int dtype,
                            const grz_bucket* buckets, int nbuckets, int chunk, int flags,
                            void* mean_out, double* piece_sqnorm, hipStream_t stream) {
@@ -1475,6 +1502,17 @@ int reduce_entry(const void* const* rank_grads, int nranks, int64_t divisor, int
     if (rank_grads[j] == nullptr) return GRZ_EINVAL;
   if (piece_sqnorm != nullptr && !aligned(piece_sqnorm, 8)) return GRZ_EALIGN;
   if ((flags & GRZ_IN_RANGE) && (flags & GRZ_IN_COMPACT)) return GRZ_EINVAL;
+  if (flags & GRZ_IN_TILED) {
+    // One receive buffer: rank j's pointer is the buffer + j pieces.
+    if (!(flags & GRZ_IN_COMPACT)) return GRZ_EINVAL;
+    const int64_t esz = dtype == GRZ_BF16 ? 2 : dtype == GRZ_F32 ? 4 : dtype == GRZ_F64 ? 8 : 0;
+    if (esz == 0) return GRZ_EINVAL;
+    const uintptr_t base = reinterpret_cast<uintptr_t>(rank_grads[0]);
+    for (int j = 1; j < nranks; ++j)
+      if (reinterpret_cast<uintptr_t>(rank_grads[j]) !=
+          base + static_cast<uintptr_t>(j) * GRZ_PIECE * esz)
+        return GRZ_EINVAL;
+  }
   std::vector<PlanSeg> ps =
       plan_segments(buckets, nbuckets, nranks, chunk, bucket_first, bucket_count);
   if (flags & GRZ_IN_RANGE) {
@@ -1730,7 +1768,8 @@ int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad
   flags &= ~GRZ_ARGS_DEVICE;
   const int st = check_plan(buckets, nbuckets, nranks, chunk, flags);
   if (st != GRZ_OK) return st;
-  if (flags & (GRZ_SUM | GRZ_IN_COMPACT | GRZ_BF16_WIRE | GRZ_IN_RANGE | GRZ_OUT_GLOBAL))
+  if (flags & (GRZ_SUM | GRZ_IN_COMPACT | GRZ_BF16_WIRE | GRZ_IN_RANGE | GRZ_OUT_GLOBAL |
+               GRZ_IN_TILED))
     return GRZ_EINVAL;
   std::vector<PlanSeg> ps;
   if (chunk >= 0) {

@@ -92,6 +92,34 @@ def _shard_state(src, phase, with_mean=True):
     return state, (placed_zeros(n, phase, dev) if with_mean else None)
 
 
+def tiled_receive(incoming, buckets, nranks, chunk):
+    """The ranks' shard-compact values of chunk ``chunk`` (``incoming[j]``, rank
+    j's) laid out as one ``GRZ_IN_TILED`` receive buffer: piece k of the chunk
+    (in plan order) in slot k, its N ranks' values side by side.  Device
+    copies only; on N GPUs each peer writes its pieces into the owner's slots
+    itself, here the simulation packs them once."""
+    buckets = [(int(o), int(l)) for o, l in buckets]
+    n = nranks
+    flags = GRZ_UNEVEN if any(length % n for _, length in buckets) else 0
+    x0 = incoming[0]
+    buf = torch.zeros(B.dp_tiled_numel(buckets, n, chunk, flags), dtype=x0.dtype,
+                      device=x0.device)
+    slots = buf.view(-1, n, GRZ_PIECE)
+    comp = piece = 0
+    for _, length in buckets:
+        _, cnt = B.dp_chunk_range(length, n, chunk)
+        full, tail = divmod(cnt, GRZ_PIECE)
+        for j, x in enumerate(incoming):
+            if full:
+                slots[piece:piece + full, j].copy_(x[comp:comp + full * GRZ_PIECE]
+                                                   .view(full, GRZ_PIECE))
+            if tail:
+                slots[piece + full, j, :tail].copy_(x[comp + full * GRZ_PIECE:comp + cnt])
+        comp += cnt
+        piece += -(-cnt // GRZ_PIECE)
+    return B.Tiled(buf, n)
+
+
 class _Norm:
     """Piece sums, workspace and the two device scalars of the clip."""
 
@@ -229,7 +257,8 @@ class Zero1OneRank:
     Per step the caller provides (all resident on the device):
 
     * ``incoming[j]`` -- rank j's gradient values of this rank's chunk,
-      shard-compact (what a reduce-scatter delivers to the owner);
+      shard-compact (what a reduce-scatter delivers to the owner), or all N
+      ranks' values in one ``Tiled`` receive buffer (``tiled_receive``);
     * the peers' norm pieces, written into ``self.norm.partials`` outside this
       rank's slots (what an all-gather of the piece sums delivers);
     * ``peer_shards[j]`` -- rank j's updated bf16 shard (``None`` at this rank),

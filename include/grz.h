@@ -101,7 +101,9 @@ enum {
   GRZ_BF16_WIRE = 8,  /* bf16 gradients: round every partial sum to bf16  */
   GRZ_IN_RANGE = 16,  /* rank inputs hold only the reduced bucket range     */
   GRZ_ARGS_DEVICE = 32, /* zero1_adamw_gather: `args` is a device pointer   */
-  GRZ_OUT_GLOBAL = 64   /* reduce, chunk >= 0: mean_out indexed like the arena */
+  GRZ_OUT_GLOBAL = 64,  /* reduce, chunk >= 0: mean_out indexed like the arena */
+  GRZ_IN_TILED = 128    /* with GRZ_IN_COMPACT: one receive buffer, the N ranks'
+                           values of each piece side by side               */
 };
 
 #define GRZ_MAX_RANKS 16    /* N and the number of replicas per call       */
@@ -166,6 +168,12 @@ int64_t dp_piece_offset(const grz_bucket* buckets, int nbuckets, int nranks, int
 int64_t dp_shard_numel(const grz_bucket* buckets, int nbuckets, int nranks, int chunk,
                        int flags);
 
+/* Elements of the GRZ_IN_TILED receive buffer of chunk `chunk`: the chunk's
+ * pieces (GRZ_PIECE elements each, the last piece of each bucket's chunk
+ * possibly shorter) times N times GRZ_PIECE, or a negative GRZ_E* code. */
+int64_t dp_tiled_numel(const grz_bucket* buckets, int nbuckets, int nranks, int chunk,
+                       int flags);
+
 /*
  * Ring-order reduce-scatter-mean ("Lab 09", s.1 and "Tips"; "A4", "Part 3",
  * ncclReduceScatter / ncclAllReduce with ncclAvg).
@@ -173,7 +181,18 @@ int64_t dp_shard_numel(const grz_bucket* buckets, int nbuckets, int nranks, int 
  * rank_grads  host array of N device pointers: rank j's flat gradient arena
  *             of `dtype` elements.  With GRZ_IN_COMPACT, rank j's values of
  *             chunk `chunk` only, in shard-compact layout (what arrives over
- *             the wire for one owner).
+ *             the wire for one owner).  With GRZ_IN_COMPACT | GRZ_IN_TILED,
+ *             the N ranks' values arrive in one receive buffer of
+ *             dp_tiled_numel elements: number the chunk's pieces k = 0, 1, ...
+ *             in plan order (bucket by bucket, GRZ_PIECE elements each, the
+ *             last piece of each bucket's chunk possibly shorter); rank j's
+ *             values of piece k start at element (k * N + j) * GRZ_PIECE
+ *             (the rest of a short piece's slot is not read).  rank_grads[j]
+ *             must then be the buffer + j * GRZ_PIECE elements (GRZ_EINVAL
+ *             otherwise).  A tile's loads are then one contiguous run instead
+ *             of N runs in N buffers, which MI355X's HBM streams faster (the
+ *             7B share's reduce 2.62-2.65 ms against 2.76-2.77 ms); the
+ *             results are the same bits.
  * nranks      N, 1..GRZ_MAX_RANKS.
  * dtype       GRZ_F32, GRZ_BF16 (uint16 bit patterns) or GRZ_F64.
  * buckets     host array of `nbuckets` (1..) buckets in processing order.
@@ -182,6 +201,7 @@ int64_t dp_shard_numel(const grz_bucket* buckets, int nbuckets, int nranks, int 
  *             chunk (plain data parallelism; mean_out is indexed like the
  *             arena and only bucket ranges are written).
  * flags       GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT (needs chunk >= 0),
+ *             GRZ_IN_TILED (needs GRZ_IN_COMPACT),
  *             GRZ_OUT_GLOBAL (chunk >= 0: mean_out is indexed like the arena
  *             and only the chunk's ranges are written -- the reduce-scatter
  *             half of a plain all-reduce, whose all-gather half, dp_all_gather,
@@ -210,7 +230,8 @@ int dp_reduce_scatter_mean(const void* const* rank_grads, int nranks, int dtype,
  * on its own stream, ordered after the compute stream by an event; "Lab 09",
  * s.2, and "Distributed training", "Overlap and graphs": each bucket is
  * reduced as soon as backward has produced it).  Shard-compact offsets,
- * arena offsets and piece numbers are those of the whole plan, so reducing
+ * arena offsets, piece numbers and GRZ_IN_TILED slots are those of the whole
+ * plan (only the range's slots are read), so reducing
  * the buckets one call at a time, in any order, leaves exactly the bytes one
  * call over the whole plan leaves.  GRZ_EINVAL if the range leaves the plan.
  *

@@ -67,15 +67,22 @@ static void random_plans(int rounds) {
       CHECK(expect_off == lens[i], "chunks cover the bucket");
     }
     CHECK(dp_piece_count(b, nb, n, 0) == pieces, "piece count");
+    int64_t tiled_pieces = 0;
     for (int c = 0; c < n; ++c) {
       const int64_t s = dp_shard_numel(b, nb, n, c, 0);
       const int64_t su = dp_shard_numel(b, nb, n, c, GRZ_UNEVEN);
+      /* the tiled receive buffer: one N-piece slot per piece of the chunk */
+      const int64_t tu = dp_tiled_numel(b, nb, n, c, GRZ_UNEVEN);
+      CHECK(tu >= 0 && tu % ((int64_t)n * GRZ_PIECE) == 0, "tiled receive size");
+      CHECK(tu / n >= su, "a slot holds every value of its piece");
+      tiled_pieces += tu / ((int64_t)n * GRZ_PIECE);
       if (divisible) CHECK(s == su, "shard size");
       else CHECK(s == -GRZ_EINDIVISIBLE, "indivisible shard must fail");
       shard_total += su;
       CHECK(dp_ring_chunk_owner(dp_ring_owned_chunk(c, n), n) == c, "owner of owned chunk");
     }
     CHECK(shard_total == pos, "shards partition the arena");
+    CHECK(tiled_pieces == pieces, "the chunks' tiled slots are the plan's pieces");
     CHECK(dp_piece_offset(b, nb, n, 0, nb, 0) < 0, "bucket out of range");
     CHECK(dp_piece_count(b, nb, GRZ_MAX_RANKS + 1, 0) < 0, "too many ranks");
   }

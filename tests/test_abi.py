@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(N.SIGNATURES), "binding signatures out of step with the header"
-    assert lib.grz_version() == 101
+    assert lib.grz_version() == 102
 
 
 def test_header_constants_match_binding():
@@ -37,7 +37,7 @@ def test_header_constants_match_binding():
     assert re.search(r"#define GRZ_MAX_RANKS (\d+)", text).group(1) == str(N.GRZ_MAX_RANKS)
     assert re.search(r"#define GRZ_PIECE (\d+)", text).group(1) == str(N.GRZ_PIECE)
     for name in ("GRZ_SUM", "GRZ_UNEVEN", "GRZ_IN_COMPACT", "GRZ_BF16_WIRE", "GRZ_IN_RANGE",
-                 "GRZ_ARGS_DEVICE", "GRZ_OUT_GLOBAL",
+                 "GRZ_ARGS_DEVICE", "GRZ_OUT_GLOBAL", "GRZ_IN_TILED",
                  "GRZ_EINDIVISIBLE",
                  "GRZ_BF16"):
         assert re.search(rf"{name} = (\d+)", text).group(1) == str(getattr(N, name))
@@ -131,6 +131,40 @@ def test_all_gather_and_out_global_refusals_before_any_launch():
     assert lib.zero1_fused_step((ctypes.c_void_p * 2)(16, 16), 2, N.GRZ_BF16, b, 1, 0,
                                 N.GRZ_OUT_GLOBAL, 16, 16, 16, ctypes.byref(args), 1.0, reps, 1,
                                 16, 16, None, None, None, None) == N.GRZ_EINVAL
+
+
+def test_tiled_receive_buffer_size_and_refusals():
+    # GRZ_IN_TILED: one slot of N * GRZ_PIECE elements per piece of the chunk
+    # (array_split chunks, the last piece of each bucket's chunk short); only
+    # with GRZ_IN_COMPACT, rank pointers exactly one piece apart; refused by
+    # the optimizer and the one-launch step.  No call below reaches a launch.
+    T = N.GRZ_PIECE
+    for buckets, n in (([(10000, 9000), (0, 10000)], 2), ([(0, 64)], 3), ([(0, 0)], 4),
+                       ([(5, 3 * T + 1), (0, 5)], 3), ([(0, 16 * 7 * T)], 16)):
+        uneven = N.GRZ_UNEVEN if any(length % n for _, length in buckets) else 0
+        for c in range(n):
+            pieces = sum(-(-(hi - lo) // T) for _, length in buckets
+                         for lo, hi in [chunk_bounds(length, n)[c]])
+            assert grz.dp_tiled_numel(buckets, n, c, uneven) == pieces * n * T
+    lib = grz.lib()
+    arr = (N.Bucket * 1)((0, 64))
+    assert lib.dp_tiled_numel(arr, 1, 2, -1, 0) == -N.GRZ_EINVAL
+    assert lib.dp_tiled_numel(arr, 1, 3, 0, 0) == -N.GRZ_EINDIVISIBLE
+    out = ctypes.c_void_p(0x30000)
+    tiled = N.GRZ_IN_TILED | N.GRZ_IN_COMPACT
+    apart = [0x100000, 0x100000 + 4 * T]  # fp32: one piece apart
+    assert _rs(lib, apart, 2, N.GRZ_F32, [(0, 64)], 0, N.GRZ_IN_TILED, out) == N.GRZ_EINVAL
+    assert _rs(lib, [0x100000, 0x100000 + 2 * T], 2, N.GRZ_F32, [(0, 64)], 0, tiled,
+               out) == N.GRZ_EINVAL
+    assert _rs(lib, [0x100000, 0x200000], 2, N.GRZ_BF16, [(0, 64)], 0, tiled,
+               out) == N.GRZ_EINVAL
+    args = N.AdamWArgs(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05)
+    reps = (ctypes.c_void_p * 1)(0x30000)
+    assert lib.zero1_adamw_gather(16, 16, 16, 16, arr, 1, 2, 0, N.GRZ_IN_TILED, 16,
+                                  ctypes.byref(args), reps, 1, None) == N.GRZ_EINVAL
+    assert lib.zero1_fused_step((ctypes.c_void_p * 2)(16, 16), 2, N.GRZ_BF16, arr, 1, 0, tiled,
+                                16, 16, 16, ctypes.byref(args), 1.0, reps, 1, 16, 16, None,
+                                None, None, None) == N.GRZ_EINVAL
 
 
 def test_product_path_refuses_cpu_tensors():

@@ -1,7 +1,7 @@
 """The smaller one-rank shares the bench records, in the launch configuration
-it times them: set up by the bench's own helper (the same seeded inputs), the
-step captured once in a HIP graph and replayed, against the oracle over two
-replays.  Char GPT and GPT-2 124M are checked on every element; GPT-2 1.5B
+it times them: set up by the bench's own helper (the same seeded inputs, the
+reduce reading them from the tiled receive buffer), the step captured once in
+a HIP graph and replayed, against the oracle over two replays.  Char GPT and GPT-2 124M are checked on every element; GPT-2 1.5B
 (389 M owned parameters at N = 4) on sampled elements, with the norm over the
 whole shard in streamed tiles."""
 
@@ -52,6 +52,7 @@ def _tiled_own_sqnorm(incoming, chunk, length, tile=1 << 25):
 def test_bench_one_rank_share_as_a_graph_matches_oracle(config, n):
     setup = bench.onerank_setup(config, n, 0, DEV)
     one, inp = setup["pipe"], setup["inp"]
+    assert isinstance(inp["recv"], grz.Tiled)
     chunk, shard, buckets = setup["chunk"], setup["shard"], setup["buckets"]
     whole = shard <= 1 << 25
     idx = np.arange(shard) if whole else sample_indices(shard, 100_000, 3)
@@ -68,7 +69,7 @@ def test_bench_one_rank_share_as_a_graph_matches_oracle(config, n):
         peers = host(inp["partials"])[_peer_mask(one)]
         sq = _tiled_own_sqnorm(inp["incoming"], chunk, shard) + float(np.sum(peers))
     scale = clip_scale(sq, 1.0)
-    cap = grz.CapturedStep(lambda a, s: (one.reduce(inp["incoming"], s),
+    cap = grz.CapturedStep(lambda a, s: (one.reduce(inp["recv"], s),
                                          one.update(None, s, args=a),
                                          one.gather(inp["peer_shards"], s)),
                            one.hyper, 1, 2)

@@ -168,7 +168,9 @@ def test_llama_7b_one_rank_share_sampled(n):
     # computed once per set; the oracle carries master, m and v on 200 k
     # sampled elements through all 10 steps.  At N = 2 (one step) the shard
     # holds 3.37e9 elements (indices beyond 2^31 in every shard-compact
-    # array); N = 16 (one step) folds each tile's loads in two batches.
+    # array); N = 16 (one step) folds each tile's loads in two batches.  At
+    # N = 8 and 16 the reduce reads the tiled receive buffer, as the bench
+    # does; at N = 2 the N separate tensors.
     a = arena("llama_7b")
     p, rank = a.numel, 0
     steps = 10 if n == 8 else 1
@@ -192,6 +194,7 @@ def test_llama_7b_one_rank_share_sampled(n):
     if steps > 1:
         sets.append([rank_grad(shard, 1e-3, "bf16", grad_seed(2, j), device=DEV)
                      for j in range(n)])
+    recvs = sets if n == 2 else [grz.tiled_receive(x, buckets, n, chunk) for x in sets]
     # Per set: the oracle's mean at the samples and its norm (own part
     # recomputed in tiles from the inputs, the peers' pieces as received).
     want_means, sqs = [], []
@@ -204,7 +207,7 @@ def test_llama_7b_one_rank_share_sampled(n):
     lo = chunk * shard
     for t in range(1, steps + 1):
         k = (t - 1) % len(sets)
-        pipe.step(sets[k], inp["peer_shards"], t)
+        pipe.step(recvs[k], inp["peer_shards"], t)
         torch.cuda.synchronize()
         what = f"7B N={n} t={t}"
         assert_bits(gather_host(pipe.mean, idx), want_means[k], f"{what} mean (sampled)")
@@ -248,8 +251,9 @@ def test_llama_7b_one_rank_share_sampled(n):
 
 @pytest.mark.parametrize("mode", ["bf16_wire", "token_weighted"])
 def test_llama_7b_one_rank_share_modes_sampled(mode):
-    # The 7B share (N = 8, rank 0, one bucket) as `bench.py --wire bf16` and
-    # `--token-weighted` run it, one step: the mean at 200 k samples against the
+    # The 7B share (N = 8, rank 0, one bucket, the tiled receive buffer) as
+    # `bench.py --wire bf16` and `--token-weighted` run it, one step: the mean
+    # at 200 k samples against the
     # oracle's fold (each hop's partial sum rounded to bf16, or the sum divided
     # by the global token count), the norm against the oracle's over the whole
     # shard in tiles, AdamW on the samples and the own chunk of the arena bit
@@ -277,7 +281,7 @@ def test_llama_7b_one_rank_share_modes_sampled(mode):
     for first, cnt in pipe.own_piece_slots():
         mask[first:first + cnt] = False
     pipe.norm.partials.copy_(inp["partials"])
-    pipe.reduce(inp["incoming"], token_counts=counts)
+    pipe.reduce(grz.tiled_receive(inp["incoming"], buckets, n, chunk), token_counts=counts)
     pipe.update(1)
     pipe.gather(inp["peer_shards"])
     torch.cuda.synchronize()

@@ -357,3 +357,100 @@ def test_reduce_modes_on_a_random_plan(seed):
             assert got[i] == -1.0, f"{what}: piece {i} of a chunk not reduced was written"
         else:
             assert math.isclose(got[i], want_i, rel_tol=1e-13, abs_tol=0.0), (what, i)
+
+
+def _nan_fill(kind):
+    return {"bf16": np.uint16(0x7FC0), "f32": np.float32("nan"), "f64": np.float64("nan")}[kind]
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_tiled_receive_on_a_random_plan(seed):
+    # The reduce reading the N ranks' values of its chunk from one tiled
+    # receive buffer (GRZ_IN_TILED), built here from the oracle's chunk
+    # bounds with NaN wherever no value belongs (the rest of a short piece's
+    # slot), on random plans with the reduce's modes (sum, bf16 wire, token
+    # weights, arena-indexed output, a bucket range): bit for bit against the
+    # oracle and against the same call on N separate shard-compact tensors;
+    # the piece sums against the exact sums of squares; `tiled_receive` packs
+    # the same buffer.
+    rng = np.random.default_rng(12000 + seed)
+    n, kind, even, buckets, p, chunk, mode = _draw(5000 + seed)
+    if chunk < 0:
+        chunk = int(rng.integers(0, n))
+    flags = 0 if even else grz.GRZ_UNEVEN
+    out_global = bool(rng.integers(0, 3) == 0)
+    if out_global:
+        flags |= grz.GRZ_OUT_GLOBAL
+    wire = "bf16" if kind == "bf16" and rng.integers(0, 2) else None
+    if wire:
+        flags |= grz.GRZ_BF16_WIRE
+    counts = None
+    if rng.integers(0, 3) == 0:
+        counts = [int(c) + 1 for c in rng.integers(0, 4000, size=n)]
+    elif rng.integers(0, 4) == 0:
+        flags |= grz.GRZ_SUM
+    nb = len(buckets)
+    brange, in_range = None, set(range(nb))
+    if rng.integers(0, 2):
+        first = int(rng.integers(0, nb))
+        brange = (first, int(rng.integers(1, nb - first + 1)))
+        in_range = set(range(first, first + brange[1]))
+    grads = [rank_grad(p, 1e-2, kind, 15000 + 17 * seed + r, device=DEV) for r in range(n)]
+    hg = [host(g) for g in grads]
+    segs = shard_segments(buckets, n, chunk, uneven=not even)
+    hin = [np.concatenate([h[g0:g0 + length] for g0, length, _ in segs]) for h in hg]
+    npc = sum(-(-length // PIECE) for _, length, _ in segs)
+    buf = np.full((max(npc, 1), n, PIECE), _nan_fill(kind), dtype=hg[0].dtype)
+    filled = np.zeros(buf.shape, bool)
+    k = 0
+    for g0, length, _ in segs:
+        for a in range(0, length, PIECE):
+            e = min(length, a + PIECE)
+            for j in range(n):
+                buf[k, j, :e - a] = hg[j][g0 + a:g0 + e]
+            filled[k, :, :e - a] = True
+            k += 1
+    assert npc * n * PIECE == grz.dp_tiled_numel(buckets, n, chunk, flags & grz.GRZ_UNEVEN)
+    dev_t = {"bf16": torch.int16, "f32": torch.float32, "f64": torch.float64}[kind]
+    flat = buf.reshape(-1)
+    recv = torch.from_numpy(flat.view(np.int16) if kind == "bf16" else flat).to(DEV)
+    compact = [torch.from_numpy(h.view(np.int16) if kind == "bf16" else h).to(DEV) for h in hin]
+    packed = grz.tiled_receive(compact, buckets, n, chunk)
+    got_buf = host(packed.buffer).view(buf.dtype).reshape(buf.shape)
+    assert np.array_equal(got_buf[filled], buf[filled])
+    out_t = torch.float64 if kind == "f64" else torch.float32
+    shard = grz.dp_shard_numel(buckets, n, chunk, flags & grz.GRZ_UNEVEN)
+    npieces = grz.dp_piece_count(buckets, n, flags & grz.GRZ_UNEVEN)
+    outs, parts = [], []
+    for inputs, extra in ((grz.Tiled(recv, n), 0), (compact, grz.GRZ_IN_COMPACT)):
+        o = torch.full((max(p if out_global else shard, 1),), float("nan"), dtype=out_t,
+                       device=DEV)
+        q = torch.full((max(npieces, 1),), -1.0, dtype=torch.float64, device=DEV)
+        grz.dp_reduce_scatter_mean(inputs, buckets, chunk, o, q, flags=flags | extra,
+                                   token_counts=counts, bucket_range=brange)
+        outs.append(o)
+        parts.append(q)
+    torch.cuda.synchronize()
+    what = (f"seed {seed} (n {n}, {kind}, chunk {chunk}, wire {wire}, counts {counts}, "
+            f"flags {flags}, range {brange})")
+    assert_bits(host(outs[0]), host(outs[1]), f"{what}: tiled against separate tensors")
+    assert_bits(host(parts[0]), host(parts[1]), f"{what}: piece sums, tiled against separate")
+    acc = np.float64 if kind == "f64" else np.float32
+    kw = dict(average=not flags & grz.GRZ_SUM, uneven=not even, wire=wire, token_counts=counts)
+    comp = reduce_scatter_mean(hin, kind, buckets, chunk, compact_inputs=True, **kw)
+    full = np.full(p, np.nan, acc)
+    for b, (g0, length, c0) in enumerate(segs):
+        if b in in_range:
+            full[g0:g0 + length] = comp[c0:c0 + length]
+        else:
+            comp[c0:c0 + length] = np.nan  # not reduced: left as it was
+    if out_global:
+        assert_bits(host(outs[0])[:p], full, what)
+    else:
+        assert_bits(host(outs[0])[:shard], comp, what)
+    got = host(parts[0])
+    for i, want_i in enumerate(_pieces_of(full, buckets, n, {chunk}, in_range)):
+        if want_i is None:
+            assert got[i] == -1.0, f"{what}: piece {i} of a chunk not reduced was written"
+        else:
+            assert math.isclose(got[i], want_i, rel_tol=1e-13, abs_tol=0.0), (what, i)
