@@ -624,6 +624,7 @@ def ddp_bench(args, dev, emit=True):
     inp = onerank_inputs(shard, n, rank, npieces, grz.GRZ_PIECE, device=dev)
     incoming, partials = inp["incoming"], inp["partials"]
     del inp
+    recv = grz.tiled_receive(incoming, buckets, n, chunk) if args.recv == "tiled" else incoming
     one = grz.DDPOneRank(buckets, n, rank, master_init(p, device=dev), hyper, dev)
     one.norm.partials.copy_(partials)
     peer_means = [None if j == rank else
@@ -635,7 +636,7 @@ def ddp_bench(args, dev, emit=True):
     s = torch.cuda.current_stream()
     t = 1
     for _ in range(args.warmup):
-        one.step(incoming, peer_means, t, s)
+        one.step(recv, peer_means, t, s)
         t += 1
     torch.cuda.synchronize()
     names = ("reduce", "gather", "sqnorm", "adamw")
@@ -645,7 +646,7 @@ def ddp_bench(args, dev, emit=True):
     for k in range(args.steps):
         e = ev[k]
         e[0].record(s)
-        one.reduce(incoming, s)
+        one.reduce(recv, s)
         e[1].record(s)
         one.receive_means(peer_means, s)
         e[2].record(s)
@@ -670,6 +671,7 @@ def ddp_bench(args, dev, emit=True):
         + ", ".join(f"{k} {v:.3f} ms" for k, v in phase.items()))
     out = {"mode": "ddp_one_rank", "workload": f"{a.name} one-rank plain data parallelism",
            "arena_params": p, "nranks_simulated": n, "rank": rank, "buckets": len(buckets),
+           "recv_layout": args.recv,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
            "params_updated_per_s": p / (ms * 1e-3), "step_bytes": step_bytes,
            "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
@@ -678,7 +680,7 @@ def ddp_bench(args, dev, emit=True):
            "ms_at_70pct_of_peak": step_bytes / (0.7 * PEAK_HBM_GBPS * 1e9) * 1e3,
            "phases_ms": phase, "phases_GBps": gbps}
     if args.graph:
-        cap = grz.CapturedStep(lambda a_, s_: one.enqueue(incoming, peer_means, a_, s_),
+        cap = grz.CapturedStep(lambda a_, s_: one.enqueue(recv, peer_means, a_, s_),
                                one.hyper, t, args.warmup + args.steps)
         for _ in range(args.warmup):
             cap.replay()

@@ -107,11 +107,13 @@ def test_all_gather_of_any_element_size(dtype):
         assert_bits(host(rep), want, f"{dtype} all-gather")
 
 
-def test_ddp_one_rank_matches_the_oracle_and_the_all_ranks_replica():
-    # Rank r fed what its peers deliver -- its chunk of every rank's gradient,
-    # the peers' mean chunks (the oracle's, as inputs) and every rank's norm
-    # pieces -- reproduces the oracle's ddp_step and, over two steps, the
-    # replica DDPStep computes from the full arenas, bit for bit.
+@pytest.mark.parametrize("recv", ["ranks", "tiled"])
+def test_ddp_one_rank_matches_the_oracle_and_the_all_ranks_replica(recv):
+    # Rank r fed what its peers deliver -- its chunk of every rank's gradient
+    # (as N tensors, or in one tiled receive buffer), the peers' mean chunks
+    # (the oracle's, as inputs) and every rank's norm pieces -- reproduces the
+    # oracle's ddp_step and, over two steps, the replica DDPStep computes from
+    # the full arenas, bit for bit.
     n, p = 8, 8 * (3 * 4096 + 136)
     buckets = [(8 * 4096, p - 8 * 4096), (0, 8 * 4096)]
     master = master_init(p, device=DEV)
@@ -134,8 +136,10 @@ def test_ddp_one_rank_matches_the_oracle_and_the_all_ranks_replica():
             c = owned_chunk(r, n)
             idx = _chunk_index(buckets, n, c)
             one.norm.partials.copy_(full.norm.partials)  # every rank's pieces, as received
-            one.step([g.index_select(0, idx).contiguous() for g in grads],
-                     [None if j == r else peer_mean[j] for j in range(n)], t)
+            mine = [g.index_select(0, idx).contiguous() for g in grads]
+            if recv == "tiled":
+                mine = grz.tiled_receive(mine, buckets, n, c)
+            one.step(mine, [None if j == r else peer_mean[j] for j in range(n)], t)
             torch.cuda.synchronize()
             assert_bits(host(one.mean), host(full.mean), f"rank {r} step {t} mean")
             assert_bits(host(one.norm.sqnorm), host(full.norm.sqnorm), f"rank {r} sqnorm")
