@@ -693,22 +693,6 @@ def ddp_bench(args, dev, emit=True):
         torch.cuda.synchronize()
         out["graph_ms_per_step"] = g0.elapsed_time(g1) / args.steps
         log(f"graph replay: {out['graph_ms_per_step']:.3f} ms/step")
-        # The arena layout captured too: its three launches back to back.
-        reps = max(args.steps, 100)
-        acap = grz.CapturedStep(lambda a_, s_: arena_pipe.enqueue(grads, a_, s_), hyper,
-                                args.warmup + args.steps + 1, args.warmup + reps)
-        for _ in range(args.warmup):
-            acap.replay()
-        torch.cuda.synchronize()
-        g0.record(s)
-        for _ in range(reps):
-            acap.replay()
-        g1.record(s)
-        torch.cuda.synchronize()
-        ams = g0.elapsed_time(g1) / reps
-        out["arena_layout_graph_ms_per_step"] = ams
-        out["arena_layout_graph_frac_of_peak"] = step_bytes / (ams * 1e-3) / 1e9 / PEAK_HBM_GBPS
-        log(f"arena layout as a graph: {ams:.4f} ms/step over {reps} replays")
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_ddp(incoming, n, hyper, min(args.cpu_sample, 1 << 27))
     if emit:
@@ -1158,22 +1142,6 @@ def main():
         torch.cuda.synchronize()
         out["graph_ms_per_step"] = g0.elapsed_time(g1) / args.steps
         log(f"graph replay: {out['graph_ms_per_step']:.3f} ms/step")
-        # The arena layout captured too: its three launches back to back.
-        reps = max(args.steps, 100)
-        acap = grz.CapturedStep(lambda a_, s_: arena_pipe.enqueue(grads, a_, s_), hyper,
-                                args.warmup + args.steps + 1, args.warmup + reps)
-        for _ in range(args.warmup):
-            acap.replay()
-        torch.cuda.synchronize()
-        g0.record(s)
-        for _ in range(reps):
-            acap.replay()
-        g1.record(s)
-        torch.cuda.synchronize()
-        ams = g0.elapsed_time(g1) / reps
-        out["arena_layout_graph_ms_per_step"] = ams
-        out["arena_layout_graph_frac_of_peak"] = step_bytes / (ams * 1e-3) / 1e9 / PEAK_HBM_GBPS
-        log(f"arena layout as a graph: {ams:.4f} ms/step over {reps} replays")
     if args.cold:
         out["cold"] = cold_bench(args, pipe, inp, stream, dev, t, step_bytes)
     if args.fused:
