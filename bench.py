@@ -824,12 +824,13 @@ def other_modes_bench(args, dev):
     """The step in its other modes, as ``--all-ranks`` and ``--ddp`` run them
     (without the CPU oracle): every simulated rank of the char GPT, GPT-2 124M
     (each also as a graph) and GPT-2 1.5B, and one rank's plain data-parallel
-    step at 7B (10 steps)."""
+    step at GPT-2 124M (also as a graph) and at 7B (10 steps)."""
     import torch
 
     out = {}
     runs = [("all_ranks", "char_gpt", 8, True), ("all_ranks", "gpt2_124m", 8, True),
-            ("all_ranks", "gpt2_1p5b", 4, False), ("ddp_one_rank", "llama_7b", 8, False)]
+            ("all_ranks", "gpt2_1p5b", 4, False), ("ddp_one_rank", "gpt2_124m", 8, True),
+            ("ddp_one_rank", "llama_7b", 8, False)]
     for mode, cfg, n, graph in runs:
         sub = argparse.Namespace(**vars(args))
         sub.config, sub.nranks, sub.graph, sub.no_cpu = cfg, n, graph, True
@@ -948,7 +949,8 @@ def main():
                     help="skip what the default run times after the headline workload: the "
                          "smaller one-rank shares (char GPT, GPT-2 124M and 1.5B, as graph "
                          "replays, warm and cold), every simulated rank of those three "
-                         "arenas, and one rank's plain data-parallel step at 7B")
+                         "arenas, and one rank's plain data-parallel step at GPT-2 124M "
+                         "and 7B")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 2 GiB bf16 copy (the library's all-gather "
                          "kernel with one rank and one replica) as the reference of known "
