@@ -605,31 +605,48 @@ def ddp_bytes(p, n, grad_bytes=2):
     return {"reduce": grad_bytes * p + 4 * p // n, "gather": 2 * peers, "adamw": 30 * p}
 
 
+def ddp_setup(name, n, rank, device, recv="tiled"):
+    """One rank's plain data-parallel step over a workload arena with seeded
+    inputs resident: the rank's chunk of every rank's gradient (``recv``: one
+    tiled receive buffer, or N tensors), the peers' fp32 mean chunks and the
+    peers' norm pieces (standing in for what the collectives deliver)."""
+    import gradient_reduce_zero_amd as grz
+    from workloads import arena, grad_seed, master_init, onerank_inputs, rank_grad
+
+    a = arena(name)
+    p = a.numel
+    buckets = grz.plan_buckets(a.numels) if name == "gpt2_124m" else grz.whole_arena(p)
+    hyper = grz.Hyper(lr=1e-4, warmup=10) if name == "gpt2_1p5b" else grz.Hyper()
+    chunk = grz.owned_chunk(rank, n)
+    shard = grz.dp_shard_numel(buckets, n, chunk)
+    npieces = grz.dp_piece_count(buckets, n)
+    inp = onerank_inputs(shard, n, rank, npieces, grz.GRZ_PIECE, device=device)
+    incoming, partials = inp["incoming"], inp["partials"]
+    del inp
+    one = grz.DDPOneRank(buckets, n, rank, master_init(p, device=device), hyper, device)
+    one.norm.partials.copy_(partials)
+    peer_means = [None if j == rank else
+                  rank_grad(shard, 1e-3 / n ** 0.5, "f32", grad_seed(1, 100 + j), device=device)
+                  for j in range(n)]
+    return dict(arena=a, p=p, n=n, rank=rank, chunk=chunk, shard=shard, buckets=buckets,
+                hyper=hyper, incoming=incoming, partials=partials, one=one,
+                peer_means=peer_means,
+                recv=(grz.tiled_receive(incoming, buckets, n, chunk) if recv == "tiled"
+                      else incoming))
+
+
 def ddp_bench(args, dev, emit=True):
     """One rank's plain data-parallel (ZeRO stage 0) step: one JSON line, also
     returned as a dict."""
     import torch
 
     import gradient_reduce_zero_amd as grz
-    from workloads import arena, grad_seed, master_init, onerank_inputs, rank_grad
 
-    a = arena(args.config)
-    p, n, rank = a.numel, args.nranks, 0
-    buckets = grz.plan_buckets(a.numels) if args.config == "gpt2_124m" else grz.whole_arena(p)
-    hyper = grz.Hyper(lr=1e-4, warmup=10) if args.config == "gpt2_1p5b" else grz.Hyper()
-    chunk = grz.owned_chunk(rank, n)
-    shard = grz.dp_shard_numel(buckets, n, chunk)
-    npieces = grz.dp_piece_count(buckets, n)
-    log(f"DDP one rank: {args.config}, N={n}, {len(buckets)} buckets")
-    inp = onerank_inputs(shard, n, rank, npieces, grz.GRZ_PIECE, device=dev)
-    incoming, partials = inp["incoming"], inp["partials"]
-    del inp
-    recv = grz.tiled_receive(incoming, buckets, n, chunk) if args.recv == "tiled" else incoming
-    one = grz.DDPOneRank(buckets, n, rank, master_init(p, device=dev), hyper, dev)
-    one.norm.partials.copy_(partials)
-    peer_means = [None if j == rank else
-                  rank_grad(shard, 1e-3 / n ** 0.5, "f32", grad_seed(1, 100 + j), device=dev)
-                  for j in range(n)]
+    log(f"DDP one rank: {args.config}, N={args.nranks}")
+    d = ddp_setup(args.config, args.nranks, 0, dev, args.recv)
+    a, p, n, rank, buckets, hyper = d["arena"], d["p"], d["n"], d["rank"], d["buckets"], d["hyper"]
+    incoming, recv, one, peer_means = d["incoming"], d["recv"], d["one"], d["peer_means"]
+    log(f"{len(buckets)} buckets")
     torch.cuda.synchronize()
     log(f"inputs resident: P={p}, {torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
     settle()

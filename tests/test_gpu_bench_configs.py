@@ -94,3 +94,37 @@ def test_bench_one_rank_share_as_a_graph_matches_oracle(config, n):
             assert_bits(gather_host(one.arena, _arena_positions(psegs, idx)),
                         gather_host(inp["peer_shards"][j], idx), f"{what}: peer {j}'s shard")
     assert scale < 1
+
+
+def test_bench_ddp_one_rank_gpt2_124m_matches_oracle():
+    # The bench's GPT-2 124M DDP rank (9 reverse-layer buckets, N = 8, rank 0,
+    # set up by the bench's own helper, the tiled receive buffer), one step,
+    # every element against the oracle: the own chunk's mean (ring fold), the
+    # peers' mean chunks as received, the norm over the own chunk plus the
+    # peers' pieces as received, clipped AdamW over the whole arena and its
+    # bf16 rounding.
+    d = bench.ddp_setup("gpt2_124m", 8, 0, DEV)
+    one, n, buckets, chunk, p = d["one"], d["n"], d["buckets"], d["chunk"], d["p"]
+    assert isinstance(d["recv"], grz.Tiled)
+    w0 = host(one.state[0])
+    one.step(d["recv"], d["peer_means"], 1)
+    torch.cuda.synchronize()
+    own = chunk_mean([widen(host(t), "bf16") for t in d["incoming"]], chunk)
+    want = np.empty(p, np.float32)
+    for g0, length, c0 in shard_segments(buckets, n, chunk):
+        want[g0:g0 + length] = own[c0:c0 + length]
+    for j in range(n):
+        if j != d["rank"]:
+            peer = host(d["peer_means"][j])
+            for g0, length, c0 in shard_segments(buckets, n, (j + 1) % n):
+                want[g0:g0 + length] = peer[c0:c0 + length]
+    assert_bits(host(one.mean), want, "DDP 124M mean")
+    sq = grad_sqnorm(own, extra=host(d["partials"])[_peer_mask(one)])
+    assert math.isclose(one.norm.sqnorm.item(), sq, rel_tol=1e-12)
+    scale = clip_scale(sq, 1.0)
+    assert scale < 1 and np.float32(one.norm.scale.item()) == scale
+    z = np.zeros_like(w0)
+    w, m, v = adamw(w0, z, z, want * scale, **OHyper().scalars(1))
+    for k, x in enumerate((w, m, v)):
+        assert_bits(host(one.state[k]), x, f"DDP 124M state {k}")
+    assert_bits(host(one.arena), bf16_round(w), "DDP 124M bf16 arena")
