@@ -303,7 +303,8 @@ def test_llama_7b_one_rank_share_modes_sampled(mode):
 
 
 def test_llama_7b_ddp_one_rank_sampled():
-    # One rank of plain data parallelism at 7B: its full fp32 state holds
+    # One rank of plain data parallelism at 7B, as the bench runs it (its
+    # chunk's inputs in the tiled receive buffer): its full fp32 state holds
     # 6.74e9 elements (beyond 2^32), its own chunk is reduced at arena offsets
     # and the peers' fp32 mean chunks land around it.
     a = arena("llama_7b")
@@ -327,7 +328,7 @@ def test_llama_7b_ddp_one_rank_sampled():
                   for j in range(n)]
     peers = host(partials)
     own = one.own_piece_slots()
-    one.step(incoming, peer_means, 1)
+    one.step(grz.tiled_receive(incoming, buckets, n, chunk), peer_means, 1)
     torch.cuda.synchronize()
 
     # The mean: the own chunk bit-exact against the oracle's fold, every peer
