@@ -145,6 +145,15 @@ def _fused_workspace(npieces, device):
     return torch.zeros(B.zero1_fused_workspace(npieces), dtype=torch.uint8, device=device)
 
 
+def _arenas(rank_grads):
+    """The N ranks' full gradient arenas a step over every chunk reads; a tiled
+    receive buffer holds one chunk only."""
+    if isinstance(rank_grads, B.Tiled):
+        raise TypeError("this step reads every rank's full gradient arena; a tiled receive "
+                        "buffer holds one rank's chunk (Zero1OneRank, DDPOneRank)")
+    return rank_grads
+
+
 def _check_fused(workspace):
     """Raise if a grid-wide wait of the last one-launch step gave up, after
     clearing the workspace's counters so that the next step can run.  Reads a
@@ -185,6 +194,7 @@ class Zero1AllRanks:
 
     def enqueue(self, rank_grads, args, stream=None, token_counts=None):
         """The step's kernels; ``args`` host ``AdamWArgs`` or a device tensor."""
+        rank_grads = _arenas(rank_grads)
         for c, mean in zip(self.chunks, self.means):
             B.dp_reduce_scatter_mean(rank_grads, self.buckets, c, mean, self.norm.partials,
                                      flags=self.reduce_flags, stream=stream,
@@ -234,6 +244,7 @@ class DDPStep:
     def enqueue(self, rank_grads, args, stream=None, token_counts=None):
         """The step's kernels; ``args`` host ``AdamWArgs``, a device tensor or a
         captured step's ``StepScalars``."""
+        rank_grads = _arenas(rank_grads)
         w, m, v = self.state
         if self.fused:
             if token_counts is not None:
@@ -448,6 +459,7 @@ class OverlappedZero1:
         self.done = torch.cuda.Event()
 
     def bucket_ready(self, b, rank_grads, compute_stream=None):
+        rank_grads = _arenas(rank_grads)
         p = self.pipe
         cs = compute_stream if compute_stream is not None else torch.cuda.current_stream()
         self.ready[b].record(cs)

@@ -117,3 +117,21 @@ def test_shard_state_sits_at_the_phase_of_its_arena_position():
         want = 16 if c % 2 else 0
         assert all((x.data_ptr() // 4) % 32 == want for x in (w, m, v, mean))
         assert torch.equal(w, master[c * 48:(c + 1) * 48])
+
+
+def test_steps_over_every_chunk_refuse_a_tiled_receive_buffer():
+    # A tiled receive buffer holds one rank's chunk: the all-ranks steps, which
+    # read every rank's full arena, refuse it before any call into the library.
+    import torch
+
+    import gradient_reduce_zero_amd as grz
+
+    master = torch.zeros(4 * 64)
+    tiled = grz.Tiled(torch.zeros(4 * 4 * grz.GRZ_PIECE), 4)
+    z = grz.Zero1AllRanks([(0, 4 * 64)], 4, master, device="cpu")
+    d = grz.DDPStep([(0, 4 * 64)], 4, master, device="cpu", nreplicas=4)
+    for step in (z, d):
+        with pytest.raises(TypeError, match="tiled receive buffer"):
+            step.enqueue(tiled, grz.adamw_args(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05))
+    with pytest.raises(TypeError, match="tiled receive buffer"):
+        grz.OverlappedZero1.bucket_ready(type("P", (), {"pipe": z})(), 0, tiled)
