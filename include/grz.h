@@ -31,8 +31,8 @@
  *    (apart from the per-thread grid cap of grz_set_max_blocks, which never
  *    changes a result, and the static per-device scratch of
  *    dp_grad_sqnorm_noalloc), so concurrent calls on different streams are
- *    safe when they touch disjoint buffers.  Buffers must stay alive until the stream has run the
- *    enqueued work.  Host arrays (pointer tables, bucket lists, argument
+ *    safe when they touch disjoint buffers.  Buffers must stay alive until
+ *    the stream has run the enqueued work.  Host arrays (pointer tables, bucket lists, argument
  *    structs) are read during the call only.
  *  - Streams.  Work is enqueued on `stream` (0 = the null stream).  No entry
  *    point synchronises the host: results are ready when the stream is.
@@ -296,10 +296,10 @@ int dp_grad_sqnorm(const double* piece_sqnorm, int64_t npieces, double max_norm,
  * errors as dp_grad_sqnorm, plus GRZ_ERANGE when
  * dp_grad_sqnorm_workspace(npieces) exceeds GRZ_NOALLOC_SCRATCH_BYTES (more
  * than 33,546,240 pieces, about 1.4e11 gradient elements) and GRZ_EINVAL when
- * a non-null stream belongs to another device than the current one.  Nothing needs
- * clearing between calls: each call writes every scratch value it reads.  All
- * calls on one device share the array, so calls that overlap on one device
- * (different streams, or different host threads) race: order them.
+ * a non-null stream belongs to another device than the current one.  Nothing
+ * needs clearing between calls: each call writes every scratch value it
+ * reads.  All calls on one device share the array, so calls that overlap on
+ * one device (different streams, or different host threads) race: order them.
  */
 #define GRZ_NOALLOC_SCRATCH_BYTES 65536
 int dp_grad_sqnorm_noalloc(const double* piece_sqnorm, int64_t npieces, double max_norm,
@@ -450,8 +450,9 @@ int64_t zero1_fused_capacity(int nranks, int dtype);
  *            shard-compact); chunk = -1: every chunk (plain data parallelism,
  *            master/m/v indexed like the arena).
  * flags      GRZ_UNEVEN, GRZ_IN_COMPACT (as for the reduce), GRZ_ARGS_DEVICE
- *            (as for zero1_adamw_gather).  GRZ_BF16_WIRE and GRZ_SUM are
- *            not taken (GRZ_EINVAL): use the separate entry points.
+ *            (as for zero1_adamw_gather).  GRZ_BF16_WIRE, GRZ_SUM and
+ *            GRZ_IN_TILED are not taken (GRZ_EINVAL): use the separate entry
+ *            points.
  * master, m, v  device fp32 state, updated in place.
  * args       the step's scalars (host, or device with GRZ_ARGS_DEVICE).
  * max_norm   clip threshold (<= 0: no clipping).
