@@ -135,3 +135,41 @@ def test_steps_over_every_chunk_refuse_a_tiled_receive_buffer():
             step.enqueue(tiled, grz.adamw_args(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05))
     with pytest.raises(TypeError, match="tiled receive buffer"):
         grz.OverlappedZero1.bucket_ready(type("P", (), {"pipe": z})(), 0, tiled)
+
+
+@pytest.mark.parametrize("n,lengths", [(8, [8 * 5000, 8 * 4096]), (3, [64, 3 * 4096 + 2, 0]),
+                                       (16, [16 * 4096 * 3])])
+def test_tiled_receive_layout(n, lengths):
+    # On the host (no kernel runs): piece k of the chunk (in plan order, the
+    # array_split chunk rule) lands in slot k with rank j's values at j * 4096;
+    # the rest of a short piece's slot stays zero.
+    import torch
+
+    import gradient_reduce_zero_amd as grz
+    from oracle.reduce import shard_segments
+
+    T = grz.GRZ_PIECE
+    offs, pos = [], 0
+    for length in lengths:
+        offs.append(pos)
+        pos += length
+    buckets = list(zip(offs, lengths))
+    uneven = any(length % n for length in lengths)
+    for chunk in (0, n - 1):
+        segs = shard_segments(buckets, n, chunk, uneven=uneven)
+        shard = sum(length for _, length, _ in segs)
+        rng = np.random.default_rng(chunk)
+        incoming = [torch.from_numpy(rng.standard_normal(shard).astype(np.float32) + 1)
+                    for _ in range(n)]
+        t = grz.tiled_receive(incoming, buckets, n, chunk)
+        got = t.buffer.numpy().reshape(-1, n, T)
+        want = np.zeros_like(got)
+        k = 0
+        for _, length, c0 in segs:
+            for a in range(0, length, T):
+                e = min(length, a + T)
+                for j in range(n):
+                    want[k, j, :e - a] = incoming[j].numpy()[c0 + a:c0 + e]
+                k += 1
+        assert k * n * T == t.buffer.numel() and t.nranks == n
+        assert np.array_equal(got, want)
