@@ -5,7 +5,9 @@
 // one workgroup per tile -- 256 threads for the reduce, one wave for the
 // optimizer and the copy -- lane-contiguous 8/16-byte accesses, non-temporal
 // hints, workgroup and tile sizes and occupancy caps chosen by measurement):
-//   rs_mean_kernel   ring-order N-way fold of 64/128-bit loads, fp32 (fp64)
+//   rs_mean_kernel   ring-order N-way fold of 64/128-bit loads (from N
+//                    buffers, or one tiled receive buffer that holds each
+//                    piece's N contributions side by side), fp32 (fp64)
 //                    mean, fp64 sum of squares per GRZ_PIECE-element piece
 //   sqnorm_level_kernel / sqnorm_final_kernel
 //                    fixed-shape fp64 tree over the piece sums -> norm, clip
