@@ -1071,8 +1071,7 @@ def main():
         pipe.norm.run(pipe.hyper.max_norm, stream)
         e[2].record(stream)
         args_t = grz.adamw_args(**grz.step_scalars(pipe.hyper, t))
-        w, m, v = pipe.state
-        grz.zero1_adamw_gather(w, m, v, pipe.mean, pipe.buckets, pipe.n, pipe.chunk,
+        grz.zero1_adamw_gather(*pipe.state, pipe.mean, pipe.buckets, pipe.n, pipe.chunk,
                                pipe.norm.scale, args_t, [pipe.arena], stream=stream)
         e[3].record(stream)
         pipe.gather(inp["peer_shards"], stream)

@@ -38,7 +38,6 @@
 
 #include <stdint.h>
 
-#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -1756,7 +1755,7 @@ int zero1_adamw_step(float* master, float* m, float* v, const float* mean_grad, 
                      hipStream_t stream) {
   if (n < 0) return GRZ_EINVAL;
   if (n == 0) return GRZ_OK;
-  std::vector<PlanSeg> ps{{0, 0, n, 0, 0}};
+  std::vector<PlanSeg> ps{{0, 0, n, 0, 0, 0, 0, 0}};
   uint16_t* reps[1] = {bf16_out};
   return adamw_common(master, m, v, mean_grad, ps, clip_scale, args, false, reps,
                       bf16_out ? 1 : 0, stream);
@@ -1779,7 +1778,8 @@ int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad
   } else {
     for (int b = 0; b < nbuckets; ++b)
       if (buckets[b].length > 0)
-        ps.push_back({buckets[b].offset, buckets[b].offset, buckets[b].length, 0, 0});
+        ps.push_back({buckets[b].offset, buckets[b].offset, buckets[b].length, 0, 0, b,
+                      buckets[b].offset, 0});
   }
   return adamw_common(master, m, v, mean_grad, ps, clip_scale, args, dev_args, replicas,
                       nreplicas, stream);
