@@ -5,7 +5,9 @@ Default workload: one rank's ZeRO-1 share of a Llama-shaped 7B arena
 parameters.  One step:
 
   K1 dp_reduce_scatter_mean  sum the 8 incoming bf16 chunks of the shard in
-                             ring order, fp32 mean, fp64 norm pieces
+                             ring order (read from one tiled receive buffer,
+                             ``--recv ranks``: 8 tensors), fp32 mean, fp64
+                             norm pieces
   K2 dp_grad_sqnorm          global norm over this rank's and the received
                              peers' pieces -> clip factor (device scalar)
   K3 zero1_adamw_gather      clip + AdamW on fp32 master/m/v, bf16 weights
