@@ -363,7 +363,7 @@ def _nan_fill(kind):
     return {"bf16": np.uint16(0x7FC0), "f32": np.float32("nan"), "f64": np.float64("nan")}[kind]
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(48))
 def test_tiled_receive_on_a_random_plan(seed):
     # The reduce reading the N ranks' values of its chunk from one tiled
     # receive buffer (GRZ_IN_TILED), built here from the oracle's chunk
