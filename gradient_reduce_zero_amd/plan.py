@@ -89,18 +89,23 @@ def step_scalars(hyper, t):
                 bias_corr2=float(f(1.0 - hyper.beta2 ** t)))
 
 
-def resident_bytes(numel, nranks, stage, grad_bytes=2, longest_bucket=0):
+def resident_bytes(numel, nranks, stage, grad_bytes=2, longest_bucket=0, shard_bytes=4):
     """Bytes one rank of this pipeline keeps resident for the model state.
 
     bf16 weights (2 per parameter); the gradient arena (``grad_bytes`` per
     parameter) below stage 2, or two staging buffers of the longest bucket at
-    stage 2; the reduced fp32 gradient (4 per parameter, sharded from stage 1);
-    fp32 master, m and v (12 per parameter, sharded from stage 1).  Compare
-    "Lab 09 -- Parallelism, simulated", s.4 (2 + 2 + 12 bytes per parameter,
-    stage 2 keeping bf16 gradient shards): this pipeline keeps its gradient
-    shard in fp32 for the optimizer, 2 bytes more per owned parameter.
+    stage 2; the reduced gradient it holds for the optimizer (``shard_bytes``
+    per parameter, sharded from stage 1: 4 for the fp32 mean, 2 with the
+    gradient shard held in bf16); fp32 master, m and v (12 per parameter,
+    sharded from stage 1).  Compare "Lab 09 -- Parallelism, simulated", s.4
+    (2 + 2 + 12 bytes per parameter, stage 2 keeping bf16 gradient shards):
+    with ``shard_bytes=2`` and the staging left out, stage 2 is the page's
+    2 + 14/N bytes per parameter; the fp32 shard holds 2 bytes more per owned
+    parameter.
     """
+    if shard_bytes not in (2, 4):
+        raise ValueError("the gradient shard is held in fp32 (4) or bf16 (2)")
     p, n = float(numel), float(nranks)
     shard = p / n if stage >= 1 else p
     grads = grad_bytes * p if stage < 2 else 2.0 * grad_bytes * longest_bucket
-    return 2.0 * p + grads + 4.0 * shard + 12.0 * shard
+    return 2.0 * p + grads + float(shard_bytes) * shard + 12.0 * shard

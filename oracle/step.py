@@ -27,6 +27,14 @@ Readings (the pages name these steps but do not print their formulas):
   with bc1 = fp32(1 - b1^t), bc2 = fp32(1 - b2^t) evaluated in float64.
 * bf16: round to nearest, ties to even mantissa; a value beyond the largest
   bf16 by half an ulp or more becomes an infinity; NaN stays a (quiet) NaN.
+* The gradient shard an owner keeps between the reduce-scatter and the
+  update: by default in fp32, the type the ring accumulates in, so that every
+  ZeRO stage sees the same values as plain data parallelism ("Distributed
+  training", "Gates": the stages agree bit for bit with DDP when nothing is
+  clipped).  With ``grad_shard="bf16"`` it is held in bf16 as "Lab 09", s.4
+  counts it (2 bytes of bf16 gradients per parameter, divided by N from
+  stage 2 on): each mean value is rounded once to bf16 (nearest even), and
+  the norm, the clip and AdamW all take the rounded value, widened exactly.
 
 Pins (tests/test_oracle_step.py): the norm against a closed form (constant
 gradient a over P elements has norm |a|*sqrt(P)) and against
@@ -37,7 +45,11 @@ closed-form sum of squares of a grid gradient whose every partial sum is exact; 
 (all-zero gradients decay the weights by (1 - lr*wd) per step; at t = 1 the
 update is g / (|g| + eps) up to rounding); bf16 rounding against torch's CPU
 ``.to(torch.bfloat16)`` on a dense sample of binary32 patterns (ties, subnormals,
-the overflow boundary, infinities, NaN).
+the overflow boundary, infinities, NaN).  The bf16 gradient shard: on means
+that are bf16 values already the step is the fp32-shard step bit for bit; on
+means just off bf16 values (below, above and exactly at half a bf16 ulp) it
+is the fp32-shard step on the hand-rounded means, and the norm is the closed
+form of those rounded values.
 """
 
 import math
@@ -45,7 +57,7 @@ import math
 import numpy as np
 
 from .bf16 import bf16_round  # noqa: F401  (re-exported)
-from .reduce import owned_chunk, reduce_scatter_mean, shard_segments
+from .reduce import owned_chunk, reduce_scatter_mean, shard_segments, widen
 
 FSUM_LIMIT = 20_000_000
 
@@ -147,19 +159,39 @@ def _check_cover(buckets, arena_len):
         raise ValueError("buckets must tile the arena")
 
 
-def zero1_step(rank_grads, kind, buckets, states, hyper, t, wire=None, token_counts=None):
+def held_gradient(mean, grad_shard=None):
+    """The gradient shard as its owner holds it until the update.
+
+    ``None``: the fp32 mean itself.  ``"bf16"``: the mean rounded once to bf16
+    (nearest even) and widened back to fp32, which is exact ("Lab 09", s.4:
+    2 bytes of bf16 gradients per parameter).
+    """
+    if grad_shard is None:
+        return mean
+    if grad_shard == "bf16":
+        if mean.dtype != np.float32:
+            raise ValueError("a bf16 gradient shard holds the mean of fp32 or bf16 gradients")
+        return widen(bf16_round(mean), "bf16")
+    raise ValueError(f"unknown gradient shard type {grad_shard!r}")
+
+
+def zero1_step(rank_grads, kind, buckets, states, hyper, t, wire=None, token_counts=None,
+               grad_shard=None):
     """One ZeRO-1 step of all N simulated ranks.
 
     ``states[r] = (master, m, v)``: rank r's shard-compact fp32 state for
     chunk (r + 1) mod N of every bucket.  Returns a dict with the per-rank
-    mean shards, the global sqnorm and clip scale, the new states, the
-    per-rank bf16 shards and the gathered bf16 arena (equal on all ranks).
+    mean shards (as held, see ``held_gradient``), the global sqnorm and clip
+    scale, the new states, the per-rank bf16 shards and the gathered bf16
+    arena (equal on all ranks).  With ``grad_shard="bf16"`` it is the step of
+    ZeRO-2 as "Lab 09", s.4 counts its bytes.
     """
     n = len(rank_grads)
     arena_len = rank_grads[0].shape[0]
     _check_cover(buckets, arena_len)
-    means = [reduce_scatter_mean(rank_grads, kind, buckets, owned_chunk(r, n), wire=wire,
-                                 token_counts=token_counts)
+    means = [held_gradient(reduce_scatter_mean(rank_grads, kind, buckets, owned_chunk(r, n),
+                                               wire=wire, token_counts=token_counts),
+                           grad_shard)
              for r in range(n)]
     sq = grad_sqnorm(np.concatenate(means))
     scale = clip_scale(sq, hyper.max_norm)

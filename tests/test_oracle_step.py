@@ -245,6 +245,79 @@ def test_cross_n_identity_on_grid_exact_data(max_norm):
         assert np.array_equal(arenas[n], arenas[1])
 
 
+@pytest.mark.parametrize("max_norm", [1e-3, 0.0])
+def test_bf16_gradient_shard_on_bf16_exact_means_is_the_fp32_shard_step(max_norm):
+    # "Lab 09", s.4 holds the gradient shard in bf16.  Where every mean is a
+    # bf16 value already (rank values k * 2^-12 with |k| <= 15: sums of four
+    # need at most 6 significant bits, and the division by 4 is exact),
+    # rounding it changes nothing, so the step -- norm, clip factor, state
+    # and weights -- is the fp32-shard step bit for bit, the clip on (its
+    # factor below 1, so that mean * scale is not a bf16 value) and off.
+    rng = np.random.default_rng(14)
+    n, p = 4, 1024
+    buckets = [(512, 512), (0, 512)]
+    master = (rng.standard_normal(p) * 0.02).astype(np.float32)
+    a = _init_states(p, n, buckets, master)
+    b = [tuple(x.copy() for x in st) for st in a]
+    h = Hyper(max_norm=max_norm)
+    for t in range(1, 4):
+        grads = [bf16_round((rng.integers(-15, 16, size=p) * 2.0 ** -12).astype(np.float32))
+                 for _ in range(n)]
+        x = zero1_step(grads, "bf16", buckets, a, h, t, grad_shard="bf16")
+        y = zero1_step(grads, "bf16", buckets, b, h, t)
+        for mu in y["means"]:
+            assert np.array_equal(bf16_round(mu).astype(np.uint32) << 16, mu.view(np.uint32))
+        assert x["sqnorm"] == y["sqnorm"] and x["scale"] == y["scale"]
+        for sa, sb in zip(x["states"], y["states"]):
+            for u, w in zip(sa, sb):
+                assert np.array_equal(u.view(np.uint32), w.view(np.uint32))
+        assert np.array_equal(x["arena"], y["arena"])
+        a, b = x["states"], y["states"]
+    assert (x["scale"] < 1) if max_norm > 0 else (x["scale"] == 1)
+
+
+def test_bf16_gradient_shard_rounds_each_mean_once_to_nearest_even():
+    # Means just off bf16 values.  bf16 keeps 8 significant bits, so next to
+    # 1 its values are 2^-7 apart and half an ulp is 2^-8 (times 2^-10 here):
+    #   1 + 2^-9      below half an ulp       -> 1
+    #   1 + 3 * 2^-9  above half an ulp       -> 1 + 2^-7
+    #   1 + 2^-8      a tie, 1 is even        -> 1
+    #   1 + 3 * 2^-8  a tie, 1 + 2^-7 is odd  -> 1 + 2^-6
+    # and the same with the sign flipped.  Both ranks hold the value, so the
+    # mean is the value exactly.  The step must be the fp32-shard step run on
+    # the hand-rounded means, and its norm the closed form of those.
+    off = [2.0 ** -9, 3 * 2.0 ** -9, 2.0 ** -8, 3 * 2.0 ** -8]
+    held = [0.0, 2.0 ** -7, 0.0, 2.0 ** -6]
+    reps = 512
+    x_vals, y_vals = [], []
+    for sign in (1.0, -1.0):
+        for o, h in zip(off, held):
+            x_vals += [sign * (1 + o) * 2.0 ** -10] * reps
+            y_vals += [sign * (1 + h) * 2.0 ** -10] * reps
+    x = np.array(x_vals, dtype=np.float32)
+    y = np.array(y_vals, dtype=np.float32)
+    p, n = x.size, 2
+    buckets = [(0, p)]
+    rng = np.random.default_rng(15)
+    master = (rng.standard_normal(p) * 0.02).astype(np.float32)
+    h = Hyper(max_norm=0.01)
+    got = zero1_step([x, x], "f32", buckets, _init_states(p, n, buckets, master), h, 1,
+                     grad_shard="bf16")
+    want = zero1_step([y, y], "f32", buckets, _init_states(p, n, buckets, master), h, 1)
+    exact = sum(2 * reps * ((1 + hh) * 2.0 ** -10) ** 2 for hh in held)
+    assert got["sqnorm"] == exact == want["sqnorm"]
+    assert got["sqnorm"] != sum(2 * reps * ((1 + o) * 2.0 ** -10) ** 2 for o in off)
+    assert got["scale"] == want["scale"] < 1
+    for r in range(n):
+        assert np.array_equal(got["means"][r], want["means"][r])
+        for u, w in zip(got["states"][r], want["states"][r]):
+            assert np.array_equal(u.view(np.uint32), w.view(np.uint32))
+    assert np.array_equal(got["arena"], want["arena"])
+    with pytest.raises(ValueError):
+        zero1_step([x, x], "f32", buckets, _init_states(p, n, buckets, master), h, 1,
+                   grad_shard="fp8")
+
+
 @pytest.mark.parametrize("n", [2, 3, 4, 8])
 def test_all_gather_equals_the_simulated_ring_all_gather(n):
     # The oracle's all-gather places every rank's owned chunk at its arena

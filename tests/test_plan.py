@@ -58,6 +58,13 @@ def test_resident_bytes_against_the_zero_table():
     longest = 25 * 2 ** 20 // 2
     assert resident_bytes(p, n, 2, longest_bucket=longest) == \
         zero_memory_bytes(p, n, 2) + 2 * p / n + 4 * longest
+    # With the gradient shard held in bf16 the stage-2 state is the page's
+    # 2 + 14/N bytes per parameter (26.25 GB for 7e9 on 8), the staging on top.
+    assert resident_bytes(p, n, 2, shard_bytes=2) == zero_memory_bytes(p, n, 2) == 26.25e9
+    assert resident_bytes(p, n, 2, longest_bucket=longest, shard_bytes=2) == \
+        zero_memory_bytes(p, n, 2) + 4 * longest
+    with pytest.raises(ValueError):
+        resident_bytes(p, n, 2, shard_bytes=1)
 
 
 def test_one_rank_step_falls_back_to_plain_data_parallelism(capsys):
