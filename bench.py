@@ -375,6 +375,10 @@ def stage_bench(args, dev):
     # (ZeRO-1) or one per bucket (ZeRO-2) and one optimizer launch for all.
     z1a = grz.DDPStep(buckets, n, master, grz.Hyper(), device=dev, nreplicas=n)
     z2a = grz.Zero2AllRanks(buckets, n, master, grz.Hyper(), device=dev, layout="arena")
+    # The gradient shards held in bf16 (2 bytes per owned parameter).
+    z2b = grz.Zero2AllRanks(buckets, n, master, grz.Hyper(), device=dev, grad_shard="bf16")
+    z2ab = grz.Zero2AllRanks(buckets, n, master, grz.Hyper(), device=dev, layout="arena",
+                             grad_shard="bf16")
 
     def copy_in():
         for off, length in buckets:
@@ -400,6 +404,12 @@ def stage_bench(args, dev):
     def step2a(t):
         z2a.step(produce, t)
 
+    def step2b(t):
+        z2b.step(produce, t)
+
+    def step2ab(t):
+        z2ab.step(produce, t)
+
     def timed(fn):
         settle()
         for t in range(1, args.warmup + 1):
@@ -416,20 +426,32 @@ def stage_bench(args, dev):
 
     t1, t2 = timed(step1), timed(step2)
     t1a, t2a = timed(step1a), timed(step2a)
+    t2b, t2ab = timed(step2b), timed(step2ab)
     g1 = sum(g.numel() * g.element_size() for g in grads)
     g2 = sum(b.numel() * b.element_size() for bufs in z2.staging for b in bufs)
+    s32 = sum(mu.numel() * mu.element_size() for mu in z2.means)
+    s16 = sum(mu.numel() * mu.element_size() for mu in z2b.means)
     log(f"ZeRO-1 {t1:.3f} ms, ZeRO-2 {t2:.3f} ms (ranks shard-compact); ZeRO-1 {t1a:.3f} ms, "
         f"ZeRO-2 {t2a:.3f} ms (ranks in arena layout); gradient bytes resident "
         f"{g1 / 1e6:.0f} MB vs {g2 / 1e6:.0f} MB")
+    log(f"ZeRO-2, gradient shards held in bf16: {t2b:.3f} ms (ranks shard-compact), "
+        f"{t2ab:.3f} ms (arena layout); the 8 ranks' gradient shards {s16 / 1e6:.0f} MB "
+        f"against {s32 / 1e6:.0f} MB in fp32")
+    longest = max(l for _, l in buckets)
     print(json.dumps({"mode": "zero2_vs_zero1", "workload": "gpt2_124m all 8 ranks",
                       "buckets": len(buckets), "steps": args.steps, "zero1_ms": t1,
                       "zero2_ms": t2, "zero1_arena_layout_ms": t1a,
                       "zero2_arena_layout_ms": t2a,
+                      "zero2_bf16_shard_ms": t2b, "zero2_bf16_shard_arena_layout_ms": t2ab,
                       "zero1_grad_bytes": g1, "zero2_grad_bytes": g2,
+                      "zero2_grad_shard_bytes": {"f32": s32, "bf16": s16},
                       "resident_bytes_per_rank": {
                           "zero1": grz.resident_bytes(p, n, 1),
-                          "zero2": grz.resident_bytes(p, n, 2,
-                                                      longest_bucket=max(l for _, l in buckets))}}),
+                          "zero2": grz.resident_bytes(p, n, 2, longest_bucket=longest),
+                          "zero2_bf16_shard": grz.resident_bytes(p, n, 2, longest_bucket=longest,
+                                                                 shard_bytes=2),
+                          "zero2_bf16_shard_without_staging": grz.resident_bytes(
+                              p, n, 2, shard_bytes=2)}}),
           flush=True)
 
 

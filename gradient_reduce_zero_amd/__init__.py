@@ -9,8 +9,9 @@ call fails if the library is not built.
 """
 
 from ._native import (GRZ_ARGS_DEVICE, GRZ_BF16, GRZ_BF16_WIRE, GRZ_F32, GRZ_F64, GRZ_IN_COMPACT,
-                      GRZ_IN_RANGE, GRZ_IN_TILED, GRZ_MAX_RANKS, GRZ_OUT_GLOBAL, GRZ_PIECE,
-                      GRZ_SUM, GRZ_UNEVEN, GrzError, lib)
+                      GRZ_IN_RANGE, GRZ_IN_TILED, GRZ_MAX_RANKS, GRZ_MEAN_BF16,
+                      GRZ_NOALLOC_SCRATCH_BYTES, GRZ_OUT_GLOBAL, GRZ_PIECE, GRZ_SUM, GRZ_UNEVEN,
+                      GrzError, lib)
 from .binding import (StepScalars, Tiled, adamw_args, dp_all_gather, dp_chunk_range,
                       dp_grad_sqnorm,
                       dp_grad_sqnorm_noalloc, dp_grad_sqnorm_of,

@@ -144,7 +144,8 @@ def dp_reduce_scatter_mean(rank_grads, buckets, chunk, mean_out, piece_sqnorm=No
     ``bucket_range = (first, count)`` restricts the call to those buckets of
     the plan (``dp_reduce_scatter_mean_range``).  ``token_counts`` (one int per
     rank) makes it the token-weighted mean of per-rank gradient sums
-    (``dp_reduce_scatter_weighted``)."""
+    (``dp_reduce_scatter_weighted``).  A bf16 ``mean_out`` holds the mean
+    rounded to bf16 (``GRZ_MEAN_BF16``)."""
     tiled = isinstance(rank_grads, Tiled)
     n = rank_grads.nranks if tiled else len(rank_grads)
     if not 1 <= n <= N.GRZ_MAX_RANKS:
@@ -179,7 +180,10 @@ def dp_reduce_scatter_mean(rank_grads, buckets, chunk, mean_out, piece_sqnorm=No
     else:
         ptrs = (ctypes.c_void_p * n)(*[_dev(g, f"rank_grads[{j}]", same, need_in).value
                                        for j, g in enumerate(rank_grads)])
-    out = _dev(mean_out, "mean_out", (_OUT[kind],), need_out)
+    if isinstance(mean_out, torch.Tensor) and mean_out.dtype in _BF16_LIKE:
+        flags |= N.GRZ_MEAN_BF16
+    out = _dev(mean_out, "mean_out",
+               _BF16_LIKE if flags & N.GRZ_MEAN_BF16 else (_OUT[kind],), need_out)
     part = None
     if piece_sqnorm is not None:
         part = _dev(piece_sqnorm, "piece_sqnorm", (torch.float64,),
@@ -299,10 +303,10 @@ def adamw_args(lr, beta1, beta2, eps, weight_decay, bias_corr1, bias_corr2):
     return AdamWArgs(lr, beta1, beta2, eps, weight_decay, bias_corr1, bias_corr2)
 
 
-def _state(master, m, v, mean_grad, n):
+def _state(master, m, v, mean_grad, n, grad_types=(torch.float32,)):
     f32 = (torch.float32,)
     return (_dev(master, "master", f32, n), _dev(m, "m", f32, n), _dev(v, "v", f32, n),
-            _dev(mean_grad, "mean_grad", f32, n))
+            _dev(mean_grad, "mean_grad", grad_types, n))
 
 
 def zero1_adamw_step(master, m, v, mean_grad, clip_scale, args, bf16_out=None, n=None,
@@ -340,10 +344,15 @@ def zero1_adamw_gather(master, m, v, mean_grad, buckets, nranks, chunk, clip_sca
 
     ``args`` is an ``AdamWArgs`` (host, read now) or a float32 device tensor of
     7 values in ``grz_adamw_args`` order, read when the kernel runs
-    (``GRZ_ARGS_DEVICE``)."""
+    (``GRZ_ARGS_DEVICE``).  A bf16 ``mean_grad`` is a gradient shard held in
+    bf16 (``GRZ_MEAN_BF16``)."""
     buckets = list(buckets)
-    n = dp_shard_numel(buckets, nranks, chunk, flags) if chunk >= 0 else _extent(buckets)
-    w, mm, vv, g = _state(master, m, v, mean_grad, n)
+    if isinstance(mean_grad, torch.Tensor) and mean_grad.dtype in _BF16_LIKE:
+        flags |= N.GRZ_MEAN_BF16
+    plan_flags = flags & ~N.GRZ_MEAN_BF16
+    n = dp_shard_numel(buckets, nranks, chunk, plan_flags) if chunk >= 0 else _extent(buckets)
+    w, mm, vv, g = _state(master, m, v, mean_grad, n,
+                          _BF16_LIKE if flags & N.GRZ_MEAN_BF16 else (torch.float32,))
     sc = None if clip_scale is None else _dev(clip_scale, "clip_scale", (torch.float32,), 1)
     ext = _extent(buckets)
     reps = (ctypes.c_void_p * max(len(replicas), 1))(

@@ -314,6 +314,16 @@ __device__ __forceinline__ float bf16_wire(float x) {
   return __uint_as_float(bf16_rne(x) << 16);
 }
 
+// Stores 4 values that are bf16 values already (their low halves are zero) as
+// 4 bf16 patterns, one 8-byte access.
+template <int P>
+__device__ __forceinline__ void store_bf16(uint16_t* p, const float (&x)[4]) {
+  u32x2 u;
+  u[0] = (__float_as_uint(x[0]) >> 16) | (__float_as_uint(x[1]) & 0xffff0000u);
+  u[1] = (__float_as_uint(x[2]) >> 16) | (__float_as_uint(x[3]) & 0xffff0000u);
+  stv<P>(p, u);
+}
+
 // Sum of one double per thread over the 256-thread block, in a fixed tree:
 // a xor butterfly inside each wave (every lane ends with the same balanced
 // tree sum of its wave) then (w0 + w1) + (w2 + w3).  The shape depends on
@@ -345,6 +355,9 @@ struct RsArgs {
   // GRZ_PIECE), so that a tile's loads are one contiguous run.
   int64_t tstride;
   typename AccOf<TIn>::type* out;
+  // GRZ_MEAN_BF16: the mean rounded to bf16 (nearest even) goes here instead
+  // of `out`, and the piece sums are those of the rounded values.
+  uint16_t* outb;
   double* partials;
   int64_t ntiles;
   int nsegs;
@@ -445,10 +458,11 @@ __device__ __forceinline__ void fold_tile(const TIn* const* rank, int c, int64_t
 // WIRE (bf16 gradients only) rounds every partial sum of the fold to bf16, as a
 // ring whose wire format is bf16 does once per hop ("13.5 Multi-GPU from
 // First Principles", exercise 8).
-template <typename TIn, int NR, bool WIRE, int WAVES>
+template <typename TIn, int NR, bool WIRE, int WAVES, bool OB>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void rs_mean_kernel(const RsArgs<TIn> a) {
   using Acc = typename AccOf<TIn>::type;
+  static_assert(!OB || sizeof(Acc) == 4, "a bf16 mean is the rounding of an fp32 one");
   constexpr int G = Geo<Acc>::G;
   constexpr int K = Geo<Acc>::K;
   __shared__ double lds[kThreads / 64];
@@ -482,10 +496,15 @@ __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void rs_mean_kernel(const RsA
 #pragma unroll
             for (int i = 0; i < G; ++i) {
               if (a.average) acc[kk][i] = a.pow2 ? acc[kk][i] * inv : acc[kk][i] / nf;
+              if constexpr (OB) acc[kk][i] = bf16_wire(acc[kk][i]);
               sq = __fma_rn(static_cast<double>(acc[kk][i]), static_cast<double>(acc[kk][i]),
                             sq);
             }
-            storeg<GRZ_RS_POLICY>(a.out + s.dst + e0 + (k * kThreads + lane) * G, acc[kk]);
+            const int64_t o = s.dst + e0 + (k * kThreads + lane) * G;
+            if constexpr (OB)
+              store_bf16<GRZ_RS_POLICY>(a.outb + o, acc[kk]);
+            else
+              storeg<GRZ_RS_POLICY>(a.out + o, acc[kk]);
           }
         }
         done = true;
@@ -502,16 +521,24 @@ __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void rs_mean_kernel(const RsA
 #pragma unroll
           for (int i = 0; i < G; ++i) {
             if (a.average) acc[i] = a.pow2 ? acc[i] * inv : acc[i] / nf;
+            if constexpr (OB) acc[i] = bf16_wire(acc[i]);
             sq = __fma_rn(static_cast<double>(acc[i]), static_cast<double>(acc[i]), sq);
           }
-          storeg<GRZ_RS_POLICY>(a.out + s.dst + e, acc);
+          if constexpr (OB)
+            store_bf16<GRZ_RS_POLICY>(a.outb + s.dst + e, acc);
+          else
+            storeg<GRZ_RS_POLICY>(a.out + s.dst + e, acc);
         } else {
           for (int i = 0; i < G; ++i) {
             if (rel + i >= left) break;
             Acc v = fold_one<TIn, NR, WIRE>(a.rank, a.nranks, c, ib + rel + i);
             if (a.average) v = a.pow2 ? v * inv : v / nf;
+            if constexpr (OB) v = bf16_wire(v);
             sq = __fma_rn(static_cast<double>(v), static_cast<double>(v), sq);
-            a.out[s.dst + e + i] = v;
+            if constexpr (OB)
+              a.outb[s.dst + e + i] = static_cast<uint16_t>(__float_as_uint(v) >> 16);
+            else
+              a.out[s.dst + e + i] = v;
           }
         }
       }
@@ -639,6 +666,7 @@ struct AdamArgs {
   float* m;
   float* v;
   const float* grad;
+  const uint16_t* gradb;  // GRZ_MEAN_BF16: the mean as bf16 patterns (`grad` unused)
   const float* scale;   // device scalar or null (1)
   const grz_adamw_args* dargs;  // step scalars in device memory, or null (use the fields below)
   uint16_t* rep[GRZ_MAX_RANKS];
@@ -666,7 +694,9 @@ __device__ __forceinline__ void adamw1(float& w, float& m, float& v, float g, fl
 
 // Access k (0 <= k < K) of lane l covers the 4 elements at k*T*4 + 4*l of
 // the tile (T = GRZ_ADAM_THREADS): 16-byte accesses of the fp32 streams,
-// 8-byte bf16 stores, each wave instruction one contiguous run.
+// 8-byte bf16 stores (and loads of a bf16 mean, GB), each wave instruction
+// one contiguous run.
+template <bool GB>
 __global__ __launch_bounds__(GRZ_ADAM_THREADS) GRZ_ADAM_ATTR void adamw_kernel(
     const AdamArgs a) {
   constexpr int G = 4;
@@ -696,7 +726,10 @@ __global__ __launch_bounds__(GRZ_ADAM_THREADS) GRZ_ADAM_ATTR void adamw_kernel(
       if (s.vec && rel + G <= left) {
         const int64_t i = s.src + e;
         float g[G], w[G], m[G], v[G];
-        loadg<GRZ_ADAM_POLICY>(a.grad + i, g);
+        if constexpr (GB)
+          loadg<GRZ_ADAM_POLICY>(a.gradb + i, g);
+        else
+          loadg<GRZ_ADAM_POLICY>(a.grad + i, g);
         loadg<GRZ_ADAM_POLICY>(a.master + i, w);
         loadg<GRZ_ADAM_POLICY>(a.m + i, m);
         loadg<GRZ_ADAM_POLICY>(a.v + i, v);
@@ -718,7 +751,8 @@ __global__ __launch_bounds__(GRZ_ADAM_THREADS) GRZ_ADAM_ATTR void adamw_kernel(
           if (rel + j >= left) break;
           const int64_t i = s.src + e + j;
           float w = a.master[i], m = a.m[i], v = a.v[i];
-          adamw1(w, m, v, a.grad[i] * scale, lr, b1, omb1, b2, omb2, eps, wd, bc1, bc2);
+          const float g = GB ? widen1(a.gradb + i) : a.grad[i];
+          adamw1(w, m, v, g * scale, lr, b1, omb1, b2, omb2, eps, wd, bc1, bc2);
           a.master[i] = w;
           a.m[i] = m;
           a.v[i] = v;
@@ -1075,7 +1109,7 @@ int check_plan(const grz_bucket* buckets, int nbuckets, int nranks, int chunk, i
   if (nbuckets < 0 || (nbuckets > 0 && buckets == nullptr)) return GRZ_EINVAL;
   if (chunk < -1 || chunk >= nranks) return GRZ_EINVAL;
   if (flags & ~(GRZ_SUM | GRZ_UNEVEN | GRZ_IN_COMPACT | GRZ_BF16_WIRE | GRZ_IN_RANGE |
-                GRZ_OUT_GLOBAL | GRZ_IN_TILED))
+                GRZ_OUT_GLOBAL | GRZ_IN_TILED | GRZ_MEAN_BF16))
     return GRZ_EINVAL;
   for (int b = 0; b < nbuckets; ++b) {
     if (buckets[b].offset < 0 || buckets[b].length < 0) return GRZ_ERANGE;
@@ -1176,19 +1210,29 @@ int launch_batches(std::vector<Seg>& segs, Args& args,
   return GRZ_OK;
 }
 
+template <typename TIn, int NR, bool WIRE, bool OB>
+int rs_launch_shape(std::vector<Seg>& segs, RsArgs<TIn>& args, bool small,
+                    hipStream_t stream) {
+  constexpr int WL = RsWaves<NR, false>::value, WS = RsWaves<NR, true>::value;
+  return small ? launch_batches(segs, args, rs_mean_kernel<TIn, NR, WIRE, WS, OB>, stream)
+               : launch_batches(segs, args, rs_mean_kernel<TIn, NR, WIRE, WL, OB>, stream);
+}
+
 template <typename TIn, int NR>
 int rs_launch(std::vector<Seg>& segs, RsArgs<TIn>& args, bool wire, hipStream_t stream) {
   int64_t tiles = 0;
   for (const Seg& s : segs) tiles += ceil_div(s.len, GRZ_PIECE);
   const bool small = tiles <= kRsSmallTiles;
-  constexpr int WL = RsWaves<NR, false>::value, WS = RsWaves<NR, true>::value;
+  const bool ob = args.outb != nullptr;
   if constexpr (sizeof(TIn) == 2) {
     if (wire)
-      return small ? launch_batches(segs, args, rs_mean_kernel<TIn, NR, true, WS>, stream)
-                   : launch_batches(segs, args, rs_mean_kernel<TIn, NR, true, WL>, stream);
+      return ob ? rs_launch_shape<TIn, NR, true, true>(segs, args, small, stream)
+                : rs_launch_shape<TIn, NR, true, false>(segs, args, small, stream);
   }
-  return small ? launch_batches(segs, args, rs_mean_kernel<TIn, NR, false, WS>, stream)
-               : launch_batches(segs, args, rs_mean_kernel<TIn, NR, false, WL>, stream);
+  if constexpr (sizeof(TIn) < 8) {
+    if (ob) return rs_launch_shape<TIn, NR, false, true>(segs, args, small, stream);
+  }
+  return rs_launch_shape<TIn, NR, false, false>(segs, args, small, stream);
 }
 
 template <typename TIn>
@@ -1198,15 +1242,20 @@ int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>
   using Acc = typename AccOf<TIn>::type;
   static RsArgs<TIn> proto;  // zero-initialised template
   RsArgs<TIn> args = proto;
-  // One access moves G elements: 16 bytes of the mean, G * sizeof(TIn) of each input.
+  // One access moves G elements: G * out_esz bytes of the mean (16, or 8 for a
+  // bf16 mean), G * sizeof(TIn) of each input.
   constexpr size_t in_bytes = Geo<Acc>::G * sizeof(TIn);
-  bool vec_base = aligned(mean_out, 16);
+  const bool ob = (flags & GRZ_MEAN_BF16) != 0;
+  const size_t out_esz = ob ? 2 : sizeof(Acc);
+  const size_t out_bytes = Geo<Acc>::G * out_esz;
+  bool vec_base = aligned(mean_out, out_bytes);
   for (int j = 0; j < n; ++j) {
     if (!aligned(rank_grads[j], sizeof(TIn))) return GRZ_EALIGN;
     vec_base = vec_base && aligned(rank_grads[j], in_bytes);
     args.rank[j] = static_cast<const TIn*>(rank_grads[j]);
   }
-  args.out = static_cast<Acc*>(mean_out);
+  args.out = ob ? nullptr : static_cast<Acc*>(mean_out);
+  args.outb = ob ? static_cast<uint16_t*>(mean_out) : nullptr;
   args.partials = partials;
   args.nranks = n;
   args.average = (flags & GRZ_SUM) ? 0 : 1;
@@ -1225,7 +1274,7 @@ int rs_dispatch(const void* const* rank_grads, int n, const std::vector<PlanSeg>
     s.piece0 = p.piece0;
     s.chunk = p.chunk;
     s.vec = vec_base && (s.src * sizeof(TIn)) % in_bytes == 0 &&
-            (s.dst * sizeof(Acc)) % 16 == 0;
+            (s.dst * out_esz) % out_bytes == 0;
     segs.push_back(s);
   }
   const bool wire = (flags & GRZ_BF16_WIRE) != 0;
@@ -1356,7 +1405,7 @@ int gather_entry(const void* const* shards, int nranks, int units, const grz_buc
 
 extern "C" {
 
-int grz_version(void) { return 102; }
+int grz_version(void) { return 103; }
 
 const char* grz_strerror(int status) {
   switch (status) {
@@ -1499,6 +1548,7 @@ int reduce_entry(const void* const* rank_grads, int nranks, int64_t divisor, int
   if (rank_grads == nullptr || mean_out == nullptr) return GRZ_EINVAL;
   if ((flags & GRZ_IN_COMPACT) && chunk < 0) return GRZ_EINVAL;
   if ((flags & GRZ_BF16_WIRE) && dtype != GRZ_BF16) return GRZ_EINVAL;
+  if ((flags & GRZ_MEAN_BF16) && dtype != GRZ_BF16 && dtype != GRZ_F32) return GRZ_EINVAL;
   for (int j = 0; j < nranks; ++j)
     if (rank_grads[j] == nullptr) return GRZ_EINVAL;
   if (piece_sqnorm != nullptr && !aligned(piece_sqnorm, 8)) return GRZ_EALIGN;
@@ -1525,11 +1575,11 @@ int reduce_entry(const void* const* rank_grads, int nranks, int64_t divisor, int
   }
   switch (dtype) {
     case GRZ_BF16:
-      if (!aligned(mean_out, 4)) return GRZ_EALIGN;
+      if (!aligned(mean_out, (flags & GRZ_MEAN_BF16) ? 2 : 4)) return GRZ_EALIGN;
       return rs_dispatch<uint16_t>(rank_grads, nranks, ps, flags, divisor, mean_out,
                                    piece_sqnorm, stream);
     case GRZ_F32:
-      if (!aligned(mean_out, 4)) return GRZ_EALIGN;
+      if (!aligned(mean_out, (flags & GRZ_MEAN_BF16) ? 2 : 4)) return GRZ_EALIGN;
       return rs_dispatch<float>(rank_grads, nranks, ps, flags, divisor, mean_out, piece_sqnorm,
                                 stream);
     case GRZ_F64:
@@ -1691,15 +1741,17 @@ int dp_grad_sqnorm_of(const float* grad, int64_t n, double max_norm, void* works
                         clip_scale_out, stream);
 }
 
-static int adamw_common(float* master, float* m, float* v, const float* mean_grad,
-                        const std::vector<PlanSeg>& ps, const float* clip_scale,
+// `mean_grad` holds fp32 values, or bf16 patterns when `grad_bf16`.
+static int adamw_common(float* master, float* m, float* v, const void* mean_grad,
+                        bool grad_bf16, const std::vector<PlanSeg>& ps, const float* clip_scale,
                         const grz_adamw_args* args, bool args_on_device,
                         uint16_t* const* replicas, int nreplicas, hipStream_t stream) {
   if (!master || !m || !v || !mean_grad || !args) return GRZ_EINVAL;
   if (args_on_device && !aligned(args, 4)) return GRZ_EALIGN;
   if (nreplicas < 0 || nreplicas > GRZ_MAX_RANKS) return GRZ_EINVAL;
   if (nreplicas > 0 && replicas == nullptr) return GRZ_EINVAL;
-  if (!aligned(master, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(mean_grad, 4) ||
+  const size_t gsz = grad_bf16 ? 2 : 4;
+  if (!aligned(master, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(mean_grad, gsz) ||
       !aligned(clip_scale, 4))
     return GRZ_EALIGN;
   static AdamArgs proto;
@@ -1707,10 +1759,11 @@ static int adamw_common(float* master, float* m, float* v, const float* mean_gra
   a.master = master;
   a.m = m;
   a.v = v;
-  a.grad = mean_grad;
+  a.grad = grad_bf16 ? nullptr : static_cast<const float*>(mean_grad);
+  a.gradb = grad_bf16 ? static_cast<const uint16_t*>(mean_grad) : nullptr;
   a.scale = clip_scale;
   bool vec_base = aligned(master, 16) && aligned(m, 16) && aligned(v, 16) &&
-                  aligned(mean_grad, 16);
+                  aligned(mean_grad, 4 * gsz);
   for (int r = 0; r < nreplicas; ++r) {
     if (replicas[r] == nullptr) return GRZ_EINVAL;
     if (!aligned(replicas[r], 2)) return GRZ_EALIGN;
@@ -1747,7 +1800,10 @@ static int adamw_common(float* master, float* m, float* v, const float* mean_gra
     } else
       segs.push_back(s);
   }
-  return launch_batches(segs, a, adamw_kernel, stream, GRZ_ADAM_TILE, GRZ_ADAM_THREADS);
+  return grad_bf16 ? launch_batches(segs, a, adamw_kernel<true>, stream, GRZ_ADAM_TILE,
+                                    GRZ_ADAM_THREADS)
+                   : launch_batches(segs, a, adamw_kernel<false>, stream, GRZ_ADAM_TILE,
+                                    GRZ_ADAM_THREADS);
 }
 
 int zero1_adamw_step(float* master, float* m, float* v, const float* mean_grad, int64_t n,
@@ -1757,16 +1813,17 @@ int zero1_adamw_step(float* master, float* m, float* v, const float* mean_grad, 
   if (n == 0) return GRZ_OK;
   std::vector<PlanSeg> ps{{0, 0, n, 0, 0, 0, 0, 0}};
   uint16_t* reps[1] = {bf16_out};
-  return adamw_common(master, m, v, mean_grad, ps, clip_scale, args, false, reps,
+  return adamw_common(master, m, v, mean_grad, false, ps, clip_scale, args, false, reps,
                       bf16_out ? 1 : 0, stream);
 }
 
-int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad,
+int zero1_adamw_gather(float* master, float* m, float* v, const void* mean_grad,
                        const grz_bucket* buckets, int nbuckets, int nranks, int chunk,
                        int flags, const float* clip_scale, const grz_adamw_args* args,
                        uint16_t* const* replicas, int nreplicas, hipStream_t stream) {
   const bool dev_args = (flags & GRZ_ARGS_DEVICE) != 0;
-  flags &= ~GRZ_ARGS_DEVICE;
+  const bool grad_bf16 = (flags & GRZ_MEAN_BF16) != 0;
+  flags &= ~(GRZ_ARGS_DEVICE | GRZ_MEAN_BF16);
   const int st = check_plan(buckets, nbuckets, nranks, chunk, flags);
   if (st != GRZ_OK) return st;
   if (flags & (GRZ_SUM | GRZ_IN_COMPACT | GRZ_BF16_WIRE | GRZ_IN_RANGE | GRZ_OUT_GLOBAL |
@@ -1781,8 +1838,8 @@ int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad
         ps.push_back({buckets[b].offset, buckets[b].offset, buckets[b].length, 0, 0, b,
                       buckets[b].offset, 0});
   }
-  return adamw_common(master, m, v, mean_grad, ps, clip_scale, args, dev_args, replicas,
-                      nreplicas, stream);
+  return adamw_common(master, m, v, mean_grad, grad_bf16, ps, clip_scale, args, dev_args,
+                      replicas, nreplicas, stream);
 }
 
 int grz_step_args_next(const grz_adamw_args* table, int64_t count, int64_t* counter,

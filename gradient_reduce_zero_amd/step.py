@@ -487,11 +487,15 @@ class Zero2AllRanks(Zero1AllRanks):
     No rank ever holds a full gradient arena: the backward hands each bucket's
     gradients to ``step`` through a staging buffer the size of the largest
     bucket (two of them, alternating), the bucket is reduce-scattered at once
-    into the ranks' fp32 gradient shards, and the buffer is reused ("Lab 09 --
+    into the ranks' gradient shards, and the buffer is reused ("Lab 09 --
     Parallelism, simulated", s.4: stage 2 shards the gradients, 2 + 14/N bytes
     per parameter with bf16 gradient shards; "Distributed training" (noeira),
-    ZeroSharded[2]).  The update is the ZeRO-1 one, so the results are the
-    same bits.
+    ZeroSharded[2]).  With ``grad_shard="f32"`` the shards hold the fp32 mean
+    and the update is the ZeRO-1 one, so the results are the same bits (as
+    the noeira gates have every stage match plain data parallelism); with
+    ``grad_shard="bf16"`` each shard holds the mean rounded once to bf16
+    (``GRZ_MEAN_BF16``), 2 bytes per owned parameter as the page counts them,
+    and the norm, the clip and AdamW take the rounded values.
 
     ``layout="shards"`` keeps each rank's gradient shard and state
     shard-compact (N reduce launches per bucket, N optimizer launches);
@@ -503,12 +507,20 @@ class Zero2AllRanks(Zero1AllRanks):
     """
 
     def __init__(self, buckets, nranks, master, hyper=None, device="cuda", reduce_flags=0,
-                 grad_dtype=torch.bfloat16, layout="shards"):
+                 grad_dtype=torch.bfloat16, layout="shards", grad_shard="f32"):
         if layout not in ("shards", "arena"):
             raise ValueError("layout is 'shards' or 'arena'")
+        if grad_shard not in ("f32", "bf16"):
+            raise ValueError("grad_shard is 'f32' or 'bf16'")
         self.layout = layout
+        self.grad_shard = grad_shard
+        shard_dtype = torch.float32 if grad_shard == "f32" else torch.bfloat16
         if layout == "shards":
             super().__init__(buckets, nranks, master, hyper, device, reduce_flags)
+            if grad_shard == "bf16":
+                self.means = [placed_zeros(mu.numel(), state_phase(self.buckets, nranks, c),
+                                           mu.device, dtype=shard_dtype)
+                              for c, mu in zip(self.chunks, self.means)]
         else:
             self.buckets = [(int(o), int(l)) for o, l in buckets]
             self.n = nranks
@@ -518,7 +530,8 @@ class Zero2AllRanks(Zero1AllRanks):
             w = master.to(device=device, dtype=torch.float32).clone()
             self.chunks = [owned_chunk(r, nranks) for r in range(nranks)]
             self.state = (w, torch.zeros_like(w), torch.zeros_like(w))
-            self.mean = torch.zeros_like(w)  # rank r's shard at its arena offsets, every r
+            # rank r's gradient shard at its arena offsets, every r
+            self.mean = torch.zeros(w.numel(), dtype=shard_dtype, device=w.device)
             self.norm = _Norm(B.dp_piece_count(self.buckets, nranks), device)
             self.replicas = [w.to(torch.bfloat16) for _ in range(nranks)]
         longest = max((length for _, length in self.buckets), default=0)

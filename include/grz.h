@@ -91,9 +91,9 @@ enum { GRZ_F32 = 0, GRZ_BF16 = 1, GRZ_F64 = 2 };
 /* Flags.  An entry point returns GRZ_EINVAL for a flag it does not take:
  * the reduce (dp_reduce_scatter_mean and its _range form) takes all but
  * GRZ_ARGS_DEVICE, the _weighted form all but that and GRZ_SUM;
- * zero1_adamw_gather takes GRZ_UNEVEN and GRZ_ARGS_DEVICE; the all-gathers
- * take GRZ_UNEVEN; zero1_fused_step GRZ_UNEVEN, GRZ_IN_COMPACT and
- * GRZ_ARGS_DEVICE.  Their meaning is in each entry point's comment. */
+ * zero1_adamw_gather takes GRZ_UNEVEN, GRZ_ARGS_DEVICE and GRZ_MEAN_BF16; the
+ * all-gathers take GRZ_UNEVEN; zero1_fused_step GRZ_UNEVEN, GRZ_IN_COMPACT
+ * and GRZ_ARGS_DEVICE.  Their meaning is in each entry point's comment. */
 enum {
   GRZ_SUM = 1,        /* keep the sum: skip the division by N            */
   GRZ_UNEVEN = 2,     /* allow bucket lengths not divisible by N         */
@@ -102,8 +102,9 @@ enum {
   GRZ_IN_RANGE = 16,  /* rank inputs hold only the reduced bucket range     */
   GRZ_ARGS_DEVICE = 32, /* zero1_adamw_gather: `args` is a device pointer   */
   GRZ_OUT_GLOBAL = 64,  /* reduce, chunk >= 0: mean_out indexed like the arena */
-  GRZ_IN_TILED = 128    /* with GRZ_IN_COMPACT: one receive buffer, the N ranks'
+  GRZ_IN_TILED = 128,   /* with GRZ_IN_COMPACT: one receive buffer, the N ranks'
                            values of each piece side by side               */
+  GRZ_MEAN_BF16 = 256   /* the mean (gradient shard) is held in bf16         */
 };
 
 #define GRZ_MAX_RANKS 16    /* N and the number of replicas per call       */
@@ -211,10 +212,16 @@ int64_t dp_tiled_numel(const grz_bucket* buckets, int nbuckets, int nranks, int 
  *             rounded to bf16 (nearest even) before the next rank adds to it
  *             ("13.5 Multi-GPU from First Principles", exercise 8); the mean
  *             is that bf16 sum divided by N in fp32.
- * mean_out    device; fp32 for F32/BF16 input, fp64 for F64 input.
+ *             GRZ_MEAN_BF16 (F32 or BF16 input): the owner holds its gradient
+ *             shard in bf16, as "Lab 09", s.4 counts a ZeRO-2 rank's bytes
+ *             (2 per parameter, divided by N): the fp32 mean is rounded once
+ *             to bf16 (nearest even) and written as uint16 bit patterns.
+ * mean_out    device; fp32 for F32/BF16 input (uint16 bf16 patterns with
+ *             GRZ_MEAN_BF16), fp64 for F64 input.
  * piece_sqnorm device fp64 array of dp_piece_count elements, or NULL.  The
  *             slots of the reduced chunks receive the sum of squares of the
- *             piece's output values; other slots are left untouched.
+ *             piece's output values (with GRZ_MEAN_BF16, of the rounded
+ *             values); other slots are left untouched.
  *
  * Element c-th chunk value = (((g_c + g_{c+1}) + g_{c+2}) + ... + g_{c-1}) / N
  * with rank indices mod N: the sum starts at rank c and travels the ring.
@@ -366,15 +373,18 @@ int zero1_adamw_step(float* master, float* m, float* v, const float* mean_grad, 
  * chunk -1 means the whole plan in arena indexing (plain data parallelism:
  * master, m, v and mean_grad are then indexed like the arena).
  *
+ * mean_grad  device; fp32 values, or with GRZ_MEAN_BF16 the bf16 patterns
+ *            the reduce wrote with that flag (each widened exactly to fp32
+ *            before the clip factor multiplies it).
  * replicas   host array of `nreplicas` (0..GRZ_MAX_RANKS) device uint16
  *            arenas.
- * flags      GRZ_UNEVEN; GRZ_ARGS_DEVICE: `args` points to device memory and
- *            is read by the kernel when it runs, so that a captured step
- *            (HIP graph) can be replayed with each step's scalars
- *            ("Distributed training", "Overlap and graphs": one graph per GPU,
- *            replayed).
+ * flags      GRZ_UNEVEN; GRZ_MEAN_BF16; GRZ_ARGS_DEVICE: `args` points to
+ *            device memory and is read by the kernel when it runs, so that a
+ *            captured step (HIP graph) can be replayed with each step's
+ *            scalars ("Distributed training", "Overlap and graphs": one graph
+ *            per GPU, replayed).
  */
-int zero1_adamw_gather(float* master, float* m, float* v, const float* mean_grad,
+int zero1_adamw_gather(float* master, float* m, float* v, const void* mean_grad,
                        const grz_bucket* buckets, int nbuckets, int nranks, int chunk,
                        int flags, const float* clip_scale, const grz_adamw_args* args,
                        uint16_t* const* replicas, int nreplicas, hipStream_t stream);

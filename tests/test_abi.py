@@ -29,7 +29,13 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(N.SIGNATURES), "binding signatures out of step with the header"
-    assert lib.grz_version() == 102
+    assert lib.grz_version() == 103
+
+
+def test_package_exports_every_flag_and_type_constant():
+    for name in dir(N):
+        if name.startswith("GRZ_") and not name.startswith("GRZ_E") and name != "GRZ_OK":
+            assert getattr(grz, name) == getattr(N, name), name
 
 
 def test_header_constants_match_binding():
@@ -37,7 +43,7 @@ def test_header_constants_match_binding():
     assert re.search(r"#define GRZ_MAX_RANKS (\d+)", text).group(1) == str(N.GRZ_MAX_RANKS)
     assert re.search(r"#define GRZ_PIECE (\d+)", text).group(1) == str(N.GRZ_PIECE)
     for name in ("GRZ_SUM", "GRZ_UNEVEN", "GRZ_IN_COMPACT", "GRZ_BF16_WIRE", "GRZ_IN_RANGE",
-                 "GRZ_ARGS_DEVICE", "GRZ_OUT_GLOBAL", "GRZ_IN_TILED",
+                 "GRZ_ARGS_DEVICE", "GRZ_OUT_GLOBAL", "GRZ_IN_TILED", "GRZ_MEAN_BF16",
                  "GRZ_EINDIVISIBLE",
                  "GRZ_BF16"):
         assert re.search(rf"{name} = (\d+)", text).group(1) == str(getattr(N, name))
@@ -165,6 +171,30 @@ def test_tiled_receive_buffer_size_and_refusals():
     assert lib.zero1_fused_step((ctypes.c_void_p * 2)(16, 16), 2, N.GRZ_BF16, arr, 1, 0, tiled,
                                 16, 16, 16, ctypes.byref(args), 1.0, reps, 1, 16, 16, None,
                                 None, None, None) == N.GRZ_EINVAL
+
+
+def test_bf16_mean_refusals():
+    # GRZ_MEAN_BF16: the rounding of an fp32 mean, so refused for fp64
+    # gradients; a bf16 mean needs 2-byte alignment only; refused by the
+    # all-gathers and the one-launch step.  No call below reaches a launch.
+    lib = grz.lib()
+    arr = (N.Bucket * 1)((0, 64))
+    out = ctypes.c_void_p(0x30000)
+    f = N.GRZ_MEAN_BF16
+    assert _rs(lib, [0x100000, 0x200000], 2, N.GRZ_F64, [(0, 64)], 0, f, out) == N.GRZ_EINVAL
+    assert _rs(lib, [0x100000, 0x200000], 2, N.GRZ_BF16, [(0, 64)], 0, f,
+               ctypes.c_void_p(0x30001)) == N.GRZ_EALIGN
+    assert _rs(lib, [0x100000, 0x200000], 2, N.GRZ_BF16, [(0, 64)], 0, 0,
+               ctypes.c_void_p(0x30002)) == N.GRZ_EALIGN
+    args = N.AdamWArgs(1e-3, 0.9, 0.95, 1e-8, 0.1, 0.1, 0.05)
+    reps = (ctypes.c_void_p * 1)(0x30000)
+    assert lib.zero1_adamw_gather(16, 16, 16, 0x30001, arr, 1, 2, 0, f, 16,
+                                  ctypes.byref(args), reps, 1, None) == N.GRZ_EALIGN
+    assert lib.zero1_all_gather((ctypes.c_void_p * 2)(16, 16), 2, arr, 1, f, reps, 1,
+                                None) == N.GRZ_EINVAL
+    assert lib.zero1_fused_step((ctypes.c_void_p * 2)(16, 16), 2, N.GRZ_BF16, arr, 1, 0,
+                                f | N.GRZ_IN_COMPACT, 16, 16, 16, ctypes.byref(args), 1.0, reps,
+                                1, 16, 16, None, None, None, None) == N.GRZ_EINVAL
 
 
 def test_product_path_refuses_cpu_tensors():

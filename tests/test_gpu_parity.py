@@ -620,7 +620,10 @@ def _check_all_ranks_against_oracle(pipe, ref, what):
     for r in range(pipe.n):
         mean, state = pipe.rank_view(r) if hasattr(pipe, "rank_view") else \
             (pipe.means[r], pipe.state[r])
-        assert_bits(host(mean), ref["means"][r], f"{what}: mean of rank {r}")
+        want = ref["means"][r]
+        if mean.dtype == torch.bfloat16:  # a gradient shard held in bf16
+            want = bf16_round(want)
+        assert_bits(host(mean), want, f"{what}: mean of rank {r}")
         for k, name in enumerate(("master", "m", "v")):
             assert_bits(host(state[k]), ref["states"][r][k], f"{what}: {name} of rank {r}")
     assert math.isclose(pipe.norm.sqnorm.item(), ref["sqnorm"], rel_tol=1e-13), what
@@ -706,21 +709,26 @@ def test_dropped_wait_reads_gradients_not_yet_written():
     assert np.count_nonzero(raced.view(np.uint32) != want.view(np.uint32)) > 0
 
 
+@pytest.mark.parametrize("grad_shard", ["f32", "bf16"])
 @pytest.mark.parametrize("layout", ["shards", "arena"])
-def test_zero2_staged_step_matches_oracle(layout):
+def test_zero2_staged_step_matches_oracle(layout, grad_shard):
     # ZeRO-2 at GPT-2 124M (9 reverse-layer buckets, N = 8): each bucket's
     # gradients arrive in a staging buffer the size of the longest bucket and
     # are reduce-scattered from it at once (GRZ_IN_RANGE); no full gradient
     # arena is kept.  Gradient shards, norm, clip factor, master/m/v and every
     # replica against the oracle's ZeRO-1 step (the update is the same), bit
     # for bit, over two steps -- with the ranks' shards held shard-compact, and
-    # at their arena offsets (one reduce launch per bucket for all ranks).
+    # at their arena offsets (one reduce launch per bucket for all ranks); the
+    # gradient shards held in fp32, and in bf16 ("Lab 09", s.4's 2 bytes per
+    # owned parameter: the oracle's step with grad_shard="bf16").
     a = arena("gpt2_124m")
     p, n = a.numel, 8
     buckets = grz.plan_buckets(a.numels)  # 9 buckets, reverse layer order
     master = master_init(p, device=DEV)
     z2 = grz.Zero2AllRanks(buckets, n, master, grz.Hyper(max_norm=1.0), device=DEV,
-                           layout=layout)
+                           layout=layout, grad_shard=grad_shard)
+    shard_t = torch.float32 if grad_shard == "f32" else torch.bfloat16
+    assert all(mu.dtype == shard_t for mu in ([z2.mean] if layout == "arena" else z2.means))
     longest = max(length for _, length in buckets)
     assert len(buckets) == 9 and z2.staging[0][0].numel() == longest < p
     states = oracle_states(host(master), buckets, n)
@@ -736,10 +744,11 @@ def test_zero2_staged_step_matches_oracle(layout):
         torch.cuda.synchronize()
         hg = [host(g) for g in grads]
         del grads
-        ref = zero1_step(hg, "bf16", buckets, states, OHyper(max_norm=1.0), t)
+        ref = zero1_step(hg, "bf16", buckets, states, OHyper(max_norm=1.0), t,
+                         grad_shard=None if grad_shard == "f32" else "bf16")
         del hg
         states = ref["states"]
-        _check_all_ranks_against_oracle(z2, ref, f"ZeRO-2 t={t}")
+        _check_all_ranks_against_oracle(z2, ref, f"ZeRO-2 ({grad_shard} shards) t={t}")
     assert ref["scale"] < 1
 
 

@@ -15,8 +15,10 @@ import pytest
 import torch
 
 import gradient_reduce_zero_amd as grz
+from oracle.bf16 import bf16_round
 from oracle.reduce import reduce_scatter_mean, shard_segments
 from oracle.ring import chunk_bounds
+from oracle.step import held_gradient
 from parity_util import assert_bits, host
 from workloads import rank_grad
 
@@ -97,13 +99,14 @@ def test_reduce_on_a_random_plan(seed):
             assert math.isclose(got[i], want_i, rel_tol=1e-13, abs_tol=0.0), (seed, i)
 
 
+@pytest.mark.parametrize("held", ["f32", "bf16"])
 @pytest.mark.parametrize("seed", range(16))
-def test_update_on_a_random_plan(seed):
+def test_update_on_a_random_plan(seed, held):
     # Clipped AdamW on the shard of a random chunk (or the whole plan) with the
     # bf16 write into 1-3 replicas: state bit-exact against the oracle's AdamW
     # on the same inputs, the replicas equal to the oracle's rounding at the
-    # shard's arena offsets and untouched elsewhere.
-    from oracle.bf16 import bf16_round
+    # shard's arena offsets and untouched elsewhere.  held="bf16": the mean
+    # gradient is a shard held in bf16 (GRZ_MEAN_BF16), widened exactly.
     from oracle.step import Hyper as OHyper
     from oracle.step import adamw
 
@@ -130,6 +133,11 @@ def test_update_on_a_random_plan(seed):
     dev = [torch.from_numpy(a.copy()).to(DEV) for a in (w, m, v, g)]
     if numel == 0:
         dev = [torch.zeros(1, device=DEV) for _ in range(4)]
+    if held == "bf16":
+        gb = bf16_round(g)
+        g = held_gradient(g, "bf16")
+        dev[3] = torch.from_numpy(gb.view(np.int16).copy()).to(DEV).view(torch.bfloat16) \
+            if numel else torch.zeros(1, dtype=torch.bfloat16, device=DEV)
     sentinel = 0x7A5C  # a bf16 bit pattern no update writes here
     reps = [torch.full((p,), sentinel, dtype=torch.int16, device=DEV).view(torch.bfloat16)
             for _ in range(nrep)]
@@ -274,8 +282,9 @@ def _every_entry_point_on(n, lengths, rng, seed):
     assert_bits(host(rep_f32), want_f32, "fp32 all-gather")
 
 
+@pytest.mark.parametrize("held", ["f32", "bf16"])
 @pytest.mark.parametrize("seed", range(24))
-def test_reduce_modes_on_a_random_plan(seed):
+def test_reduce_modes_on_a_random_plan(seed, held):
     # The reduce's other modes on random plans: the sum instead of the mean,
     # the bf16 wire (bf16 gradients), the token-weighted mean (totals that are
     # and are not powers of two), shard-compact inputs, and a bucket range
@@ -283,10 +292,17 @@ def test_reduce_modes_on_a_random_plan(seed):
     # feeds the reduce from a staging buffer), alone and together.  Output
     # bit-exact against the oracle's reduce of the whole arenas at the range's
     # positions and untouched elsewhere; the piece sums against the exact sum
-    # of squares of the oracle's output, other pieces untouched.
+    # of squares of the oracle's output, other pieces untouched.  With
+    # held="bf16" the output is the gradient shard held in bf16
+    # (GRZ_MEAN_BF16): the oracle's mean rounded once, piece sums of the
+    # rounded values (fp64 gradients, which have no such mode, become fp32).
     rng = np.random.default_rng(8000 + seed)
     n, kind, even, buckets, p, chunk, mode = _draw(3000 + seed)
+    if held == "bf16" and kind == "f64":
+        kind = "f32"
     flags = 0 if even else grz.GRZ_UNEVEN
+    if held == "bf16":
+        flags |= grz.GRZ_MEAN_BF16
     if mode == "global":
         flags |= grz.GRZ_OUT_GLOBAL
     wire = "bf16" if kind == "bf16" and rng.integers(0, 2) else None
@@ -325,6 +341,8 @@ def test_reduce_modes_on_a_random_plan(seed):
         flags |= grz.GRZ_IN_RANGE
     acc = np.float64 if kind == "f64" else np.float32
     out_t = torch.float64 if kind == "f64" else torch.float32
+    if held == "bf16":
+        out_t = torch.bfloat16
     npieces = grz.dp_piece_count(buckets, n, flags)
     parts = torch.full((max(npieces, 1),), -1.0, dtype=torch.float64, device=DEV)
     shard = grz.dp_shard_numel(buckets, n, chunk, flags) if chunk >= 0 else p
@@ -342,15 +360,18 @@ def test_reduce_modes_on_a_random_plan(seed):
             if b in in_range:
                 out_global[g0:g0 + length] = comp[c0:c0 + length]
     what = (f"seed {seed} (n {n}, {kind}, wire {wire}, counts {counts}, flags {flags}, "
-            f"range {brange})")
+            f"range {brange}, held {held})")
+    as_held = (lambda x: bf16_round(x)) if held == "bf16" else (lambda x: x)
     if mode == "compact":
         want = reduce_scatter_mean(hin, kind, buckets, chunk, compact_inputs=compact, **kw)
         for b, (_, length, c0) in enumerate(shard_segments(buckets, n, chunk, uneven=not even)):
             if b not in in_range:
                 want[c0:c0 + length] = np.nan  # not reduced: left as it was
-        assert_bits(host(out)[:shard], want, what)
+        assert_bits(host(out)[:shard], as_held(want), what)
     else:
-        assert_bits(host(out)[:p], out_global, what)
+        assert_bits(host(out)[:p], as_held(out_global), what)
+    if held == "bf16":
+        out_global = held_gradient(out_global, "bf16")
     got = host(parts)
     for i, want_i in enumerate(_pieces_of(out_global, buckets, n, set(chunks), in_range)):
         if want_i is None:
