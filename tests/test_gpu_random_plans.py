@@ -384,8 +384,9 @@ def _nan_fill(kind):
     return {"bf16": np.uint16(0x7FC0), "f32": np.float32("nan"), "f64": np.float64("nan")}[kind]
 
 
+@pytest.mark.parametrize("held", ["f32", "bf16"])
 @pytest.mark.parametrize("seed", range(48))
-def test_tiled_receive_on_a_random_plan(seed):
+def test_tiled_receive_on_a_random_plan(seed, held):
     # The reduce reading the N ranks' values of its chunk from one tiled
     # receive buffer (GRZ_IN_TILED), built here from the oracle's chunk
     # bounds with NaN wherever no value belongs (the rest of a short piece's
@@ -393,12 +394,17 @@ def test_tiled_receive_on_a_random_plan(seed):
     # weights, arena-indexed output, a bucket range): bit for bit against the
     # oracle and against the same call on N separate shard-compact tensors;
     # the piece sums against the exact sums of squares; `tiled_receive` packs
-    # the same buffer.
+    # the same buffer.  held="bf16": the mean written as a bf16 gradient shard
+    # (GRZ_MEAN_BF16; fp64 gradients, which have no such mode, become fp32).
     rng = np.random.default_rng(12000 + seed)
     n, kind, even, buckets, p, chunk, mode = _draw(5000 + seed)
+    if held == "bf16" and kind == "f64":
+        kind = "f32"
     if chunk < 0:
         chunk = int(rng.integers(0, n))
     flags = 0 if even else grz.GRZ_UNEVEN
+    if held == "bf16":
+        flags |= grz.GRZ_MEAN_BF16
     out_global = bool(rng.integers(0, 3) == 0)
     if out_global:
         flags |= grz.GRZ_OUT_GLOBAL
@@ -440,6 +446,8 @@ def test_tiled_receive_on_a_random_plan(seed):
     got_buf = host(packed.buffer).view(buf.dtype).reshape(buf.shape)
     assert np.array_equal(got_buf[filled], buf[filled])
     out_t = torch.float64 if kind == "f64" else torch.float32
+    if held == "bf16":
+        out_t = torch.bfloat16
     shard = grz.dp_shard_numel(buckets, n, chunk, flags & grz.GRZ_UNEVEN)
     npieces = grz.dp_piece_count(buckets, n, flags & grz.GRZ_UNEVEN)
     outs, parts = [], []
@@ -453,7 +461,7 @@ def test_tiled_receive_on_a_random_plan(seed):
         parts.append(q)
     torch.cuda.synchronize()
     what = (f"seed {seed} (n {n}, {kind}, chunk {chunk}, wire {wire}, counts {counts}, "
-            f"flags {flags}, range {brange})")
+            f"flags {flags}, range {brange}, held {held})")
     assert_bits(host(outs[0]), host(outs[1]), f"{what}: tiled against separate tensors")
     assert_bits(host(parts[0]), host(parts[1]), f"{what}: piece sums, tiled against separate")
     acc = np.float64 if kind == "f64" else np.float32
@@ -465,10 +473,13 @@ def test_tiled_receive_on_a_random_plan(seed):
             full[g0:g0 + length] = comp[c0:c0 + length]
         else:
             comp[c0:c0 + length] = np.nan  # not reduced: left as it was
+    as_held = (lambda x: bf16_round(x)) if held == "bf16" else (lambda x: x)
     if out_global:
-        assert_bits(host(outs[0])[:p], full, what)
+        assert_bits(host(outs[0])[:p], as_held(full), what)
     else:
-        assert_bits(host(outs[0])[:shard], comp, what)
+        assert_bits(host(outs[0])[:shard], as_held(comp), what)
+    if held == "bf16":
+        full = held_gradient(full, "bf16")
     got = host(parts[0])
     for i, want_i in enumerate(_pieces_of(full, buckets, n, {chunk}, in_range)):
         if want_i is None:
