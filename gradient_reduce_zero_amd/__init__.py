@@ -8,7 +8,8 @@ points), host planning and the step drivers.  There is no CPU fallback: a
 call fails if the library is not built.
 """
 
-from ._native import (GRZ_ARGS_DEVICE, GRZ_BF16, GRZ_BF16_WIRE, GRZ_F32, GRZ_F64, GRZ_IN_COMPACT,
+from ._native import (GRZ_ARGS_DEVICE, GRZ_BF16, GRZ_BF16_WIRE, GRZ_COOPERATIVE, GRZ_F32,
+                      GRZ_F64, GRZ_IN_COMPACT,
                       GRZ_IN_RANGE, GRZ_IN_TILED, GRZ_MAX_RANKS, GRZ_MEAN_BF16,
                       GRZ_NOALLOC_SCRATCH_BYTES, GRZ_OUT_GLOBAL, GRZ_PIECE, GRZ_SUM, GRZ_UNEVEN,
                       GrzError, lib)

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(HERE, "libgrz.so")
 GRZ_OK, GRZ_EINVAL, GRZ_EINDIVISIBLE, GRZ_EALIGN, GRZ_EHIP, GRZ_ERANGE = range(6)
 GRZ_F32, GRZ_BF16, GRZ_F64 = 0, 1, 2
 (GRZ_SUM, GRZ_UNEVEN, GRZ_IN_COMPACT, GRZ_BF16_WIRE, GRZ_IN_RANGE, GRZ_ARGS_DEVICE,
- GRZ_OUT_GLOBAL, GRZ_IN_TILED, GRZ_MEAN_BF16) = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+ GRZ_OUT_GLOBAL, GRZ_IN_TILED, GRZ_MEAN_BF16, GRZ_COOPERATIVE) = (1, 2, 4, 8, 16, 32, 64, 128,
+                                                                 256, 512)
 GRZ_MAX_RANKS = 16
 GRZ_PIECE = 4096
 GRZ_NOALLOC_SCRATCH_BYTES = 65536

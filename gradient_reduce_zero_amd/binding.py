@@ -426,9 +426,9 @@ def dp_all_gather(shards, buckets, replicas, flags=0, stream=None):
 
 
 def fused_set_spin_limit(workspace, polls):
-    """Polls a grid-wide wait of ``zero1_fused_step`` on ``workspace`` makes
-    before it gives up (the workspace's 32-bit word at byte 12; 0 restores the
-    library's default).  Enqueued on the current stream like any write."""
+    """Polls a wait of ``zero1_fused_step`` on ``workspace`` makes before it
+    gives up (the workspace's 32-bit word at byte 12; 0 restores the library's
+    default).  Enqueued on the current stream like any write."""
     if not 0 <= int(polls) < 2 ** 31:
         raise ValueError("polls must be in [0, 2^31)")
     workspace.view(torch.int32)[3].fill_(int(polls))
@@ -493,14 +493,15 @@ def zero1_fused_step(rank_grads, buckets, chunk, master, m, v, args, max_norm, r
 
 
 def fused_timed_out(workspace):
-    """True if a grid-wide wait of the last fused step on ``workspace`` gave up
-    (reads the device word: synchronises with the stream's work)."""
+    """True if a wait of a fused step on ``workspace`` gave up, or a step with
+    another piece count was refused (reads the device word: synchronises with
+    the stream's work)."""
     return int(workspace.view(torch.int32)[2].item()) != 0
 
 
 def fused_clear(workspace):
-    """Zero the barrier counters and the time-out flag of a fused-step
-    workspace after a wait gave up, keeping its poll limit."""
+    """Zero a fused-step workspace after a wait gave up (the flag, the launch
+    counter and the published piece sums), keeping its poll limit."""
     words = workspace.view(torch.int32)
     limit = words[3].clone()
     workspace.zero_()

@@ -56,9 +56,9 @@ static_assert(GRZ_PIECE % (kThreads * 8) == 0, "piece shape");
 // MI355X: one workgroup per tile (no cap in practice) streams fastest.
 thread_local int g_max_blocks = 1 << 30;
 
-// Polls of a grid-barrier wait before it gives up (fused step) when the
-// workspace does not set its own limit.  Each poll sleeps a few hundred
-// cycles, so this bounds a wait at a few seconds.
+// Polls of a wait of the fused step before it gives up, when the workspace
+// does not set its own limit.  Each poll sleeps about a hundred cycles, so
+// this bounds a wait at well under a second.
 constexpr unsigned kDefaultSpinLimit = 1u << 22;
 
 // One contiguous run of work: `len` elements read at `src` and written at
@@ -820,13 +820,8 @@ __global__ __launch_bounds__(GRZ_AG_THREADS) GRZ_AG_ATTR void gather_kernel(
 // mean never goes to memory (unless asked for), which saves 8 bytes per owned
 // element against the three-kernel path.  The arithmetic of every value is
 // that of rs_mean_kernel, sqnorm_*_kernel and adamw_kernel, so the results are
-// the same bits.  The launch is cooperative, which makes the runtime refuse a
-// grid that cannot be resident at once; every wait is bounded as well.
-// Measured on MI355X it is slower than the three separate launches at the
-// sizes that fit (GPT-2 124M one-rank share: 0.22 ms against 0.14 ms of
-// kernel time): every workgroup's device-scope release and acquire at a
-// barrier write back and invalidate its XCD's L2, which costs more than the
-// mean's round trip through HBM.
+// the same bits.  The grid is sized to be resident at once, and every wait is
+// bounded.
 
 constexpr int kFusedPieces = 4;   // pieces (tiles) a workgroup holds in registers
 constexpr int kFusedSegs = 32;    // segments per launch
@@ -855,8 +850,10 @@ struct FusedArgs {
   float* v;
   float* mean_out;                // optional copy of the mean
   double* partials;               // piece sums of the whole plan (peers' filled in)
-  double* level;                  // first-level sums of the norm tree
-  unsigned* sync;                 // barrier words (grid_barrier)
+  unsigned* ctl;                  // control words of the workspace (see kCtlBytes)
+  uint64_t* slots;                // published piece sums, one per piece of the plan
+  uint64_t* lslots;               // published first-level sums of the norm tree
+  uint64_t* total;                // the published norm
   double* sqnorm_out;
   float* scale_out;
   const grz_adamw_args* dargs;    // step scalars in device memory, or null
@@ -864,6 +861,7 @@ struct FusedArgs {
   double divisor;
   int64_t ntiles;                 // pieces this launch reduces
   int64_t npieces;                // pieces of the plan
+  int nred;                       // workgroups that reduce; the others fold the norm
   int nranks;
   int nrep;
   int nsegs;
@@ -872,72 +870,109 @@ struct FusedArgs {
   FSeg seg[kFusedSegs];
 };
 
-// Grid-wide barrier over `nblocks` co-resident workgroups, in two levels so
-// that no memory word takes more than 32 arrivals or 32 pollers (measured on
-// MI355X: one counter shared by 1024 workgroups makes each barrier several
-// times slower).  Workgroup b belongs to group b mod 32.  One thread per
-// workgroup reads its group's generation, then counts itself in (device-scope
-// acquire-release, which publishes the workgroup's writes); the last of a
-// group resets the group count and counts the group in at the top; the last
-// group resets the top count and advances every group's generation
-// (release).  The others poll their group's generation and then take a
-// device-scope acquire fence.  The wait gives up after the workspace's poll
-// limit (word 3; 0 means kDefaultSpinLimit), raises the time-out word and
-// returns false, so a grid that is not resident at once ends with a flag
-// instead of waiting forever.  Counts are back at zero after every completed
-// barrier, so consecutive launches reuse the words uncleared; after a give-up
-// they are not, and the workspace must be cleared.
+// The norm of the one-launch step needs every piece sum of the plan before
+// any workgroup may clip, and no grid-wide barrier: each sum is published in
+// a slot of the workspace that says by itself whether it belongs to this
+// launch.  A sum of squares is never negative, so bit 63 of its fp64 pattern
+// is free; a launch stores its sums with bit 63 set to its parity (one plus
+// the low bit of the launch counter in the workspace), and a reader polls
+// the slot with device-scope loads until the bit matches.  The value is its
+// own flag, so nothing else has to be ordered: no counter, no fence, and none
+// of the L2 write-back and invalidation that a device-scope release and
+// acquire cost on this chip (with a two-level barrier the launch took 0.24 ms
+// at the GPT-2 124M one-rank share).  The tree is dp_grad_sqnorm's: level
+// block j (more than 4096 pieces) is folded by workgroup j and published in
+// its own slot, workgroup 0 folds the level slots (or the pieces) into the
+// norm, publishes it and advances the launch counter, and every workgroup
+// waits for that one slot.  A NaN sum is published as the one quiet NaN.
 //
-// Layout of `sync` (32-bit words, 256 bytes per block): block 0 word 0 the
-// top count, word 2 the time-out flag, word 3 the poll limit; block g + 1
-// words 0 and 1 the count and generation of group g.
-constexpr unsigned kBarrierGroups = 32;
-constexpr unsigned kSyncStride = 64;  // words between blocks
-constexpr size_t kSyncBytes = (kBarrierGroups + 1) * kSyncStride * sizeof(unsigned);
+// Control words (32-bit, the first kCtlBytes of the workspace): word 2 the
+// time-out flag, word 3 the poll limit (0 means kDefaultSpinLimit), word 4
+// the launch counter, word 5 the piece count of the last launch plus one.
+// Every launch rewrites every slot of its plan, so a slot holds the last
+// launch's parity as long as the piece count stays the same; a launch with
+// another piece count raises the flag instead of reading slots that older
+// launches may have left at its parity.  A wait that reaches the limit
+// raises the flag and its workgroup stops; a launch that finds the flag
+// raised does nothing at all, so a workspace whose last call gave up stays
+// stopped until it is cleared (zeroed, which also makes every slot stale).
+constexpr size_t kCtlBytes = 256;
+constexpr uint64_t kSignBit = 1ull << 63;
 
-// True when every workgroup arrived; false (the same in every thread of the
-// workgroup) when this workgroup's wait gave up.
-__device__ __forceinline__ bool grid_barrier(unsigned* sync, unsigned nblocks) {
-  __shared__ int gave_up;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    gave_up = 0;
-    const unsigned ng = nblocks < kBarrierGroups ? nblocks : kBarrierGroups;
-    const unsigned g = blockIdx.x % ng;
-    const unsigned gsize = nblocks / ng + (g < nblocks % ng ? 1u : 0u);
-    unsigned* gw = sync + kSyncStride * (g + 1);
-    const unsigned gen = __hip_atomic_load(gw + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bool last = false;
-    if (__hip_atomic_fetch_add(gw, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-        gsize - 1) {
-      __hip_atomic_store(gw, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__hip_atomic_fetch_add(sync, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-          ng - 1) {
-        __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = true;
-      }
+__device__ __forceinline__ void publish(uint64_t* slot, double x, uint64_t parity) {
+  uint64_t u = static_cast<uint64_t>(__double_as_longlong(x)) & ~kSignBit;
+  if (u > 0x7ff0000000000000ull) u = 0x7ff8000000000000ull;
+  __hip_atomic_store(slot, u | (parity << 63), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polls `slot` until it holds this launch's value (true) or `limit` polls
+// have passed (false).
+__device__ __forceinline__ bool collect(uint64_t* slot, uint64_t parity, unsigned limit,
+                                        double* x) {
+  for (unsigned polls = 0;;) {
+    const uint64_t u = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((u >> 63) == parity) {
+      *x = __longlong_as_double(static_cast<long long>(u & ~kSignBit));
+      return true;
     }
-    if (last) {
-      for (unsigned h = 0; h < ng; ++h)
-        __hip_atomic_fetch_add(sync + kSyncStride * (h + 1) + 1, 1u, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      const unsigned set = sync[3];
-      const unsigned limit = set != 0 ? set : kDefaultSpinLimit;
-      unsigned polls = 0;
-      while (__hip_atomic_load(gw + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        __builtin_amdgcn_s_sleep(4);
-        if (++polls >= limit) {
-          __hip_atomic_store(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          gave_up = 1;
-          break;
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (++polls >= limit) return false;
+    __builtin_amdgcn_s_sleep(2);
   }
-  __syncthreads();
-  return gave_up == 0;
+}
+
+// fan_block_sum over published slots [base, base + 4096) (those below n): the
+// same additions in the same order, each value taken once it is published.
+// A lane loads all its 16 slots at once and polls again only those that
+// were not published yet.  False (in every thread) when a wait of any thread
+// gave up.
+__device__ __forceinline__ bool fan_block_collect(uint64_t* slots, int64_t n, int64_t base,
+                                                  uint64_t parity, unsigned limit,
+                                                  double* lds, double* out) {
+  constexpr int kPer = kReduceFan / kThreads;
+  constexpr int kBatch = kPer;
+  double s = 0.0;
+  bool ok = true;
+#pragma unroll
+  for (int k0 = 0; k0 < kPer; k0 += kBatch) {
+    uint64_t u[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int64_t i = base + (k0 + k) * kThreads + threadIdx.x;
+      u[k] = i < n ? __hip_atomic_load(slots + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : parity << 63;
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int64_t i = base + (k0 + k) * kThreads + threadIdx.x;
+      if (i < n && ok) {
+        double x;
+        if ((u[k] >> 63) == parity)
+          x = __longlong_as_double(static_cast<long long>(u[k] & ~kSignBit));
+        else
+          ok = collect(slots + i, parity, limit, &x);
+        if (ok) s += x;
+      }
+    }
+  }
+  const bool all_ok = __syncthreads_and(ok) != 0;
+  *out = block_sum_fixed(s, lds);
+  return all_ok;
+}
+
+// fan_block_sum of n <= 256 published values (value l in lane l alone), as
+// fan_block_collect computes it, with one load per lane.
+__device__ __forceinline__ bool small_collect(uint64_t* slots, int64_t n, uint64_t parity,
+                                              unsigned limit, double* lds, double* out) {
+  double s = 0.0;
+  bool ok = true;
+  if (threadIdx.x < n) {
+    double x;
+    ok = collect(slots + threadIdx.x, parity, limit, &x);
+    if (ok) s += x;
+  }
+  const bool all_ok = __syncthreads_and(ok) != 0;
+  *out = block_sum_fixed(s, lds);
+  return all_ok;
 }
 
 // At most 128 VGPRs, so that 4 waves per SIMD (4 workgroups per CU) fit: the
@@ -947,16 +982,69 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 void fused_step_kernel(const FusedArgs<TIn> a) {
   constexpr int G = 4;
   constexpr int K = GRZ_PIECE / (kThreads * G);
+  static_assert(K % 2 == 0, "the update takes two accesses at a time");
   __shared__ double lds[kThreads / 64];
+  __shared__ double norm_lds;
   const float nf = static_cast<float>(a.divisor);
   const float inv = 1.0f / nf;
   const int lane = threadIdx.x;
   float mean[kFusedPieces][K][G];
 
-  // Reduce: the pieces blockIdx.x, blockIdx.x + gridDim.x, ... of the launch.
+  // The control words, read once per workgroup.  A workspace whose last call
+  // gave up, or that served a plan of another piece count (whose slots would
+  // not all have been rewritten by the last launch), does nothing until it is
+  // cleared; a plan of another piece count also raises the flag.
+  __shared__ unsigned ctl_lds[2];
+  if (lane == 0) {
+    const unsigned flag = __hip_atomic_load(a.ctl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned plan = __hip_atomic_load(a.ctl + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool other_plan = plan != 0 && plan != static_cast<unsigned>(a.npieces + 1);
+    if (other_plan && flag == 0)
+      __hip_atomic_store(a.ctl + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ctl_lds[0] = (flag != 0 || other_plan) ? 1u : 0u;
+    ctl_lds[1] = __hip_atomic_load(a.ctl + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (ctl_lds[0] != 0) return;
+  const unsigned launch_no = ctl_lds[1];
+  const uint64_t parity = (launch_no + 1u) & 1u;
+  const unsigned set = a.ctl[3];
+  const unsigned limit = set != 0 ? set : kDefaultSpinLimit;
+
+  // Publish the pieces this launch does not reduce (the peers'), as given.
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + lane; i < a.npieces;
+       i += static_cast<int64_t>(gridDim.x) * kThreads) {
+    bool own = false;
+    for (int j = 0; j < a.nsegs; ++j) {
+      const FSeg& s = a.seg[j];
+      own = own || (i >= s.piece0 && i < s.piece0 + (s.len + GRZ_PIECE - 1) / GRZ_PIECE);
+    }
+    if (!own) publish(a.slots + i, a.partials[i], parity);
+  }
+
+  // The workgroups after the first nred fold the norm and hold no mean: with
+  // a level below the final fold, workgroup nred + j folds level block j;
+  // without, workgroup nred folds the pieces into the norm.  Each publishes
+  // its sum.  (Workgroup 0 is a folder only when the launch reduces nothing;
+  // it then goes on to take the norm like the others.)
+  const int64_t nl = a.npieces > kReduceFan ? (a.npieces + kReduceFan - 1) / kReduceFan : 0;
+  if (static_cast<int>(blockIdx.x) >= a.nred) {
+    const int64_t f = blockIdx.x - a.nred;
+    double t;
+    const bool ok = fan_block_collect(a.slots, a.npieces, nl > 0 ? f * kReduceFan : 0, parity,
+                                      limit, lds, &t);
+    if (!ok) {
+      if (lane == 0) __hip_atomic_store(a.ctl + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    if (lane == 0) publish(nl > 0 ? a.lslots + f : a.total, t, parity);
+    if (blockIdx.x != 0) return;
+  }
+
+  // Reduce: the pieces blockIdx.x, blockIdx.x + nred, ... of the launch.
 #pragma unroll
   for (int p = 0; p < kFusedPieces; ++p) {
-    const int64_t tile = blockIdx.x + static_cast<int64_t>(p) * gridDim.x;
+    const int64_t tile = blockIdx.x + static_cast<int64_t>(p) * a.nred;
     if (tile < a.ntiles) {
       const FSeg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
       const int64_t piece = tile - s.tile0;
@@ -991,31 +1079,62 @@ void fused_step_kernel(const FusedArgs<TIn> a) {
         }
       }
       const double tot = block_sum_fixed(sq, lds);
-      if (lane == 0) a.partials[s.piece0 + piece] = tot;
+      if (lane == 0) {
+        a.partials[s.piece0 + piece] = tot;
+        publish(a.slots + s.piece0 + piece, tot, parity);
+      }
     }
   }
-  // A workgroup whose wait gave up stops here: it has not seen every piece
-  // sum, so it writes nothing more (its tiles keep their old state) and
-  // arrives at no later barrier; the flag in the workspace says so.
-  if (!grid_barrier(a.sync, gridDim.x)) return;
 
-  // Norm: the tree of dp_grad_sqnorm (at most one level below the final fold).
-  double sqnorm;
-  if (a.npieces > kReduceFan) {
-    const int64_t nl = (a.npieces + kReduceFan - 1) / kReduceFan;
-    for (int64_t b = blockIdx.x; b < nl; b += gridDim.x) {
-      const double t = fan_block_sum(a.partials, a.npieces, b * kReduceFan, lds);
-      if (lane == 0) a.level[b] = t;
+  // The first two accesses of the first piece's state, loaded before the
+  // norm is known (the state is this workgroup's alone), so that they are in
+  // flight while it waits.
+  float pw[2][G], pm[2][G], pv[2][G];
+  bool pre = false;
+  if (blockIdx.x < a.ntiles) {
+    const FSeg& s = a.seg[find_seg(a.seg, a.nsegs, blockIdx.x)];
+    const int64_t e0 = (blockIdx.x - s.tile0) * GRZ_PIECE;
+    if ((s.vec & 2) && static_cast<int64_t>(kThreads + lane) * G + G <= s.len - e0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t i = s.st + e0 + static_cast<int64_t>(j * kThreads + lane) * G;
+        loadg<GRZ_ADAM_POLICY>(a.master + i, pw[j]);
+        loadg<GRZ_ADAM_POLICY>(a.m + i, pm[j]);
+        loadg<GRZ_ADAM_POLICY>(a.v + i, pv[j]);
+      }
+      pre = true;
     }
-    if (!grid_barrier(a.sync, gridDim.x)) return;
-    sqnorm = fan_block_sum(a.level, nl, 0, lds);
-  } else {
-    sqnorm = fan_block_sum(a.partials, a.npieces, 0, lds);
   }
+
+  // Norm: the tree of dp_grad_sqnorm (at most one level below the final
+  // fold), from the folders' published sums.  With a level, every workgroup
+  // folds the level sums itself (the same tree, so the same bits
+  // everywhere); without, it takes the norm the folder published.  A
+  // workgroup whose wait gives up has not seen every piece sum, so it writes
+  // nothing more (its tiles keep their old state) and raises the flag.
+  bool ok = true;
+  {
+    double t = 0.0;
+    if (nl > 0)
+      ok = small_collect(a.lslots, nl, parity, limit, lds, &t);
+    else if (lane == 0)
+      ok = collect(a.total, parity, limit, &t);
+    if (lane == 0) norm_lds = t;
+  }
+  if (__syncthreads_or(!ok) != 0) {
+    if (lane == 0) __hip_atomic_store(a.ctl + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const double sqnorm = norm_lds;
   const float scale = clip_factor(sqnorm, a.max_norm);
   if (blockIdx.x == 0 && lane == 0) {
     if (a.sqnorm_out != nullptr) *a.sqnorm_out = sqnorm;
     if (a.scale_out != nullptr) *a.scale_out = scale;
+    // Every workgroup has read the launch counter (each published a piece
+    // after reading it), so the next launch's parity can be set.
+    __hip_atomic_store(a.ctl + 4, launch_no + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.ctl + 5, static_cast<unsigned>(a.npieces + 1), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // Clip + AdamW from the registers; bf16 weights into every replica.
@@ -1032,47 +1151,70 @@ void fused_step_kernel(const FusedArgs<TIn> a) {
   const float omb2 = 1.0f - b2;
 #pragma unroll
   for (int p = 0; p < kFusedPieces; ++p) {
-    const int64_t tile = blockIdx.x + static_cast<int64_t>(p) * gridDim.x;
+    const int64_t tile = blockIdx.x + static_cast<int64_t>(p) * a.nred;
     if (tile < a.ntiles) {
       const FSeg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
       const int64_t e0 = (tile - s.tile0) * GRZ_PIECE;
       const int64_t left = s.len - e0;
+      // Two accesses at a time: both accesses' loads are in flight before
+      // the first update.
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int64_t rel = static_cast<int64_t>(k * kThreads + lane) * G;
-        const int64_t e = e0 + rel;
-        if ((s.vec & 2) && rel + G <= left) {
-          const int64_t i = s.st + e;
-          float w[G], m[G], v[G];
-          loadg<GRZ_ADAM_POLICY>(a.master + i, w);
-          loadg<GRZ_ADAM_POLICY>(a.m + i, m);
-          loadg<GRZ_ADAM_POLICY>(a.v + i, v);
-          uint32_t b[G];
+      for (int kb = 0; kb < K; kb += 2) {
+        float w[2][G], m[2][G], v[2][G];
+        bool vec[2];
 #pragma unroll
-          for (int j = 0; j < G; ++j) {
-            adamw1(w[j], m[j], v[j], mean[p][k][j] * scale, lr, b1, omb1, b2, omb2, eps, wd,
-                   bc1, bc2);
-            b[j] = bf16_rne(w[j]);
+        for (int j = 0; j < 2; ++j) {
+          const int64_t rel = static_cast<int64_t>((kb + j) * kThreads + lane) * G;
+          vec[j] = (s.vec & 2) && rel + G <= left;
+          if (p == 0 && kb == 0 && pre) {
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+              w[j][q] = pw[j][q];
+              m[j][q] = pm[j][q];
+              v[j][q] = pv[j][q];
+            }
+          } else if (vec[j]) {
+            const int64_t i = s.st + e0 + rel;
+            loadg<GRZ_ADAM_POLICY>(a.master + i, w[j]);
+            loadg<GRZ_ADAM_POLICY>(a.m + i, m[j]);
+            loadg<GRZ_ADAM_POLICY>(a.v + i, v[j]);
           }
-          storeg<GRZ_ADAM_POLICY>(a.master + i, w);
-          storeg<GRZ_ADAM_POLICY>(a.m + i, m);
-          storeg<GRZ_ADAM_POLICY>(a.v + i, v);
-          u32x2 packed;
-          packed[0] = b[0] | (b[1] << 16);
-          packed[1] = b[2] | (b[3] << 16);
-          for (int r = 0; r < a.nrep; ++r) stv<GRZ_ADAM_POLICY>(a.rep[r] + s.glob + e, packed);
-        } else {
+        }
 #pragma unroll
-          for (int j = 0; j < G; ++j) {
-            if (rel + j < left) {
-              const int64_t i = s.st + e + j;
-              float w = a.master[i], m = a.m[i], v = a.v[i];
-              adamw1(w, m, v, mean[p][k][j] * scale, lr, b1, omb1, b2, omb2, eps, wd, bc1, bc2);
-              a.master[i] = w;
-              a.m[i] = m;
-              a.v[i] = v;
-              const uint16_t b = static_cast<uint16_t>(bf16_rne(w));
-              for (int r = 0; r < a.nrep; ++r) a.rep[r][s.glob + e + j] = b;
+        for (int j = 0; j < 2; ++j) {
+          const int k = kb + j;
+          const int64_t rel = static_cast<int64_t>(k * kThreads + lane) * G;
+          const int64_t e = e0 + rel;
+          if (vec[j]) {
+            const int64_t i = s.st + e;
+            uint32_t b[G];
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+              adamw1(w[j][q], m[j][q], v[j][q], mean[p][k][q] * scale, lr, b1, omb1, b2,
+                     omb2, eps, wd, bc1, bc2);
+              b[q] = bf16_rne(w[j][q]);
+            }
+            storeg<GRZ_ADAM_POLICY>(a.master + i, w[j]);
+            storeg<GRZ_ADAM_POLICY>(a.m + i, m[j]);
+            storeg<GRZ_ADAM_POLICY>(a.v + i, v[j]);
+            u32x2 packed;
+            packed[0] = b[0] | (b[1] << 16);
+            packed[1] = b[2] | (b[3] << 16);
+            for (int r = 0; r < a.nrep; ++r) stv<GRZ_ADAM_POLICY>(a.rep[r] + s.glob + e, packed);
+          } else {
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+              if (rel + q < left) {
+                const int64_t i = s.st + e + q;
+                float ws = a.master[i], ms = a.m[i], vs = a.v[i];
+                adamw1(ws, ms, vs, mean[p][k][q] * scale, lr, b1, omb1, b2, omb2, eps, wd, bc1,
+                       bc2);
+                a.master[i] = ws;
+                a.m[i] = ms;
+                a.v[i] = vs;
+                const uint16_t bb = static_cast<uint16_t>(bf16_rne(ws));
+                for (int r = 0; r < a.nrep; ++r) a.rep[r][s.glob + e + q] = bb;
+              }
             }
           }
         }
@@ -1868,8 +2010,9 @@ int dp_all_gather(const void* const* shards, int nranks, int dtype, const grz_bu
 }
 
 size_t zero1_fused_workspace(int64_t npieces) {
+  if (npieces < 0) npieces = 0;
   const int64_t nl = npieces > kReduceFan ? ceil_div(npieces, kReduceFan) : 0;
-  return kSyncBytes + static_cast<size_t>(nl) * sizeof(double);
+  return kCtlBytes + static_cast<size_t>(npieces + nl + 1) * sizeof(uint64_t);
 }
 
 }  // extern "C"
@@ -1960,15 +2103,25 @@ int fused_launch(const void* kernel, const void* const* rank_grads, int nranks,
   int max_grid = 0;
   const int st = fused_max_grid(kernel, &max_grid);
   if (st != GRZ_OK) return st;
-  if (tiles > static_cast<int64_t>(max_grid) * kFusedPieces) return GRZ_ERANGE;
-  const int grid = tiles == 0 ? 1 : static_cast<int>(tiles < max_grid ? tiles : max_grid);
+  // One folding workgroup per level block of the norm tree (one without a
+  // level); the rest of the resident grid reduces.
+  const int64_t nl = npieces > kReduceFan ? ceil_div(npieces, kReduceFan) : 0;
+  const int64_t nfold = nl > 0 ? nl : 1;
+  if (nl > kThreads || nfold >= max_grid) return GRZ_ERANGE;
+  const int64_t nred_max = max_grid - nfold;
+  if (tiles > nred_max * kFusedPieces) return GRZ_ERANGE;
+  const int64_t nred = tiles < nred_max ? tiles : nred_max;
+  const int grid = static_cast<int>(nred + nfold);
+  a.nred = static_cast<int>(nred);
   a.master = master;
   a.m = m;
   a.v = v;
   a.mean_out = mean_out;
   a.partials = piece_sqnorm;
-  a.sync = static_cast<unsigned*>(workspace);
-  a.level = reinterpret_cast<double*>(static_cast<char*>(workspace) + kSyncBytes);
+  a.ctl = static_cast<unsigned*>(workspace);
+  a.slots = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kCtlBytes);
+  a.lslots = a.slots + npieces;
+  a.total = a.lslots + (npieces > kReduceFan ? ceil_div(npieces, kReduceFan) : 0);
   a.sqnorm_out = sqnorm_out;
   a.scale_out = clip_scale_out;
   a.max_norm = max_norm;
@@ -1991,8 +2144,17 @@ int fused_launch(const void* kernel, const void* const* rank_grads, int nranks,
     a.bc2 = args->bias_corr2;
   }
   void* params[] = {&a};
-  return hipLaunchCooperativeKernel(kernel, dim3(grid), dim3(kThreads), params, 0, stream) ==
-                 hipSuccess ? GRZ_OK : GRZ_EHIP;
+  // The grid is what the occupancy allows resident at once, so on a device
+  // that runs nothing else every workgroup is dispatched at once; the waits
+  // are bounded besides, so a grid that is not resident ends with the flag
+  // up rather than waiting for ever.  A cooperative launch has HIP guarantee
+  // residency, at a cost (MI355X: 147 against 130 us per launch at the GPT-2
+  // 124M one-rank share, 41 against 24 us at the char GPT).
+  const hipError_t e =
+      (flags & GRZ_COOPERATIVE)
+          ? hipLaunchCooperativeKernel(kernel, dim3(grid), dim3(kThreads), params, 0, stream)
+          : hipLaunchKernel(kernel, dim3(grid), dim3(kThreads), params, 0, stream);
+  return e == hipSuccess ? GRZ_OK : GRZ_EHIP;
 }
 
 }  // namespace
@@ -2006,7 +2168,7 @@ int64_t zero1_fused_capacity(int nranks, int dtype) {
   int grid = 0;
   const int st = fused_max_grid(kernel, &grid);
   if (st != GRZ_OK) return -st;
-  return static_cast<int64_t>(grid) * kFusedPieces;
+  return static_cast<int64_t>(grid - 1) * kFusedPieces;  // one workgroup folds the norm
 }
 
 int zero1_fused_step(const void* const* rank_grads, int nranks, int dtype,
@@ -2015,8 +2177,10 @@ int zero1_fused_step(const void* const* rank_grads, int nranks, int dtype,
                      double max_norm, uint16_t* const* replicas, int nreplicas,
                      double* piece_sqnorm, void* workspace, double* sqnorm_out,
                      float* clip_scale_out, float* mean_out, hipStream_t stream) {
-  if (flags & ~(GRZ_UNEVEN | GRZ_IN_COMPACT | GRZ_ARGS_DEVICE)) return GRZ_EINVAL;
-  int st = check_plan(buckets, nbuckets, nranks, chunk, flags & ~GRZ_ARGS_DEVICE);
+  if (flags & ~(GRZ_UNEVEN | GRZ_IN_COMPACT | GRZ_ARGS_DEVICE | GRZ_COOPERATIVE))
+    return GRZ_EINVAL;
+  int st = check_plan(buckets, nbuckets, nranks, chunk,
+                      flags & ~(GRZ_ARGS_DEVICE | GRZ_COOPERATIVE));
   if (st != GRZ_OK) return st;
   if ((flags & GRZ_IN_COMPACT) && chunk < 0) return GRZ_EINVAL;
   const void* kernel = fused_kernel_for(dtype, nranks);

@@ -92,8 +92,9 @@ enum { GRZ_F32 = 0, GRZ_BF16 = 1, GRZ_F64 = 2 };
  * the reduce (dp_reduce_scatter_mean and its _range form) takes all but
  * GRZ_ARGS_DEVICE, the _weighted form all but that and GRZ_SUM;
  * zero1_adamw_gather takes GRZ_UNEVEN, GRZ_ARGS_DEVICE and GRZ_MEAN_BF16; the
- * all-gathers take GRZ_UNEVEN; zero1_fused_step GRZ_UNEVEN, GRZ_IN_COMPACT
- * and GRZ_ARGS_DEVICE.  Their meaning is in each entry point's comment. */
+ * all-gathers take GRZ_UNEVEN; zero1_fused_step GRZ_UNEVEN, GRZ_IN_COMPACT,
+ * GRZ_ARGS_DEVICE and GRZ_COOPERATIVE.  Their meaning is in each entry
+ * point's comment. */
 enum {
   GRZ_SUM = 1,        /* keep the sum: skip the division by N            */
   GRZ_UNEVEN = 2,     /* allow bucket lengths not divisible by N         */
@@ -104,7 +105,8 @@ enum {
   GRZ_OUT_GLOBAL = 64,  /* reduce, chunk >= 0: mean_out indexed like the arena */
   GRZ_IN_TILED = 128,   /* with GRZ_IN_COMPACT: one receive buffer, the N ranks'
                            values of each piece side by side               */
-  GRZ_MEAN_BF16 = 256   /* the mean (gradient shard) is held in bf16         */
+  GRZ_MEAN_BF16 = 256,  /* the mean (gradient shard) is held in bf16         */
+  GRZ_COOPERATIVE = 512 /* zero1_fused_step: a cooperative launch            */
 };
 
 #define GRZ_MAX_RANKS 16    /* N and the number of replicas per call       */
@@ -435,9 +437,11 @@ size_t zero1_fused_workspace(int64_t npieces);
 /*
  * Pieces (GRZ_PIECE-element tiles of the reduced chunks) that one
  * zero1_fused_step launch can hold for N ranks of `dtype` gradients on the
- * current device: 4 per workgroup that can be resident at once (1024
- * workgroups on a 256-CU MI355X, so 4096 pieces, 16.8 M elements).  A
- * negative value is minus a GRZ_E* code.
+ * current device: 4 per workgroup that can be resident at once, less one
+ * workgroup that folds the norm (1024 resident on a 256-CU MI355X, so 4092
+ * pieces, 16.76 M elements).  A plan of more than 4096 pieces in all (the
+ * peers' included) takes one more folding workgroup per 4096 pieces, so 4
+ * pieces less each.  A negative value is minus a GRZ_E* code.
  */
 int64_t zero1_fused_capacity(int nranks, int dtype);
 
@@ -450,9 +454,16 @@ int64_t zero1_fused_capacity(int nranks, int dtype);
  *   dp_reduce_scatter_mean -> dp_grad_sqnorm -> zero1_adamw_gather
  * on the same inputs; the mean itself is never stored unless `mean_out` is
  * given, which saves 8 bytes of memory traffic per owned element.  The grid
- * synchronises internally (all pieces summed before the norm is read), so
- * the launch is cooperative: HIP refuses it rather than start a grid that
- * cannot be resident at once.
+ * synchronises internally (all pieces summed before the norm is read: each
+ * piece sum is published in a workspace slot that carries the launch's
+ * parity, and the readers poll it), so its workgroups must be resident at
+ * once.  The grid is sized to what the occupancy allows resident, so on a
+ * device that runs nothing else at the same time they are; with
+ * GRZ_COOPERATIVE the launch is cooperative and HIP guarantees it (or
+ * refuses the launch), at about 17 us more per call on MI355X.  Without it,
+ * kernels of other streams that hold compute units for longer than the
+ * poll limit make the waits give up (see `workspace`): the call then
+ * reports it and no tile holds anything but its old state or its update.
  *
  * rank_grads, nranks, dtype, buckets, nbuckets, chunk
  *            as for dp_reduce_scatter_mean; dtype GRZ_BF16 or GRZ_F32.
@@ -460,7 +471,7 @@ int64_t zero1_fused_capacity(int nranks, int dtype);
  *            shard-compact); chunk = -1: every chunk (plain data parallelism,
  *            master/m/v indexed like the arena).
  * flags      GRZ_UNEVEN, GRZ_IN_COMPACT (as for the reduce), GRZ_ARGS_DEVICE
- *            (as for zero1_adamw_gather).  GRZ_BF16_WIRE, GRZ_SUM and
+ *            (as for zero1_adamw_gather), GRZ_COOPERATIVE (above).  GRZ_BF16_WIRE, GRZ_SUM and
  *            GRZ_IN_TILED are not taken (GRZ_EINVAL): use the separate entry
  *            points.
  * master, m, v  device fp32 state, updated in place.
@@ -472,27 +483,34 @@ int64_t zero1_fused_capacity(int nranks, int dtype);
  *            pieces of the processed chunks; the other entries (the peers'
  *            pieces, when chunk >= 0) must hold their values already.
  * workspace  device, zero1_fused_workspace(npieces) bytes, 8-byte aligned,
- *            ZEROED before its first use.  Its first 8448 bytes are the grid
- *            barrier's counters; the 32-bit word at byte 8 is its time-out
- *            flag, and the 32-bit word at byte 12 the number of polls a wait
- *            makes before it gives up (0, as zeroed: 2^22, a few seconds; the
- *            caller may set it before the launch).  A completed call leaves
- *            the counters at zero, so the workspace is reused without
- *            clearing.  A non-zero flag means a wait gave up: a workgroup
- *            whose wait gave up writes nothing after it (its tiles of master,
- *            m, v, the replicas and the mean keep their previous values, and
- *            it stores no norm), so each tile holds either its previous state
- *            or its correct update; the call's result as a whole is then
- *            incomplete, and the counters must be zeroed again (the poll
- *            limit word may be kept) before the next call.  Calls that share
- *            a workspace must not overlap.
+ *            ZEROED before its first use.  Its first 256 bytes are control
+ *            words: the 32-bit word at byte 8 is the time-out flag, the word
+ *            at byte 12 the number of polls a wait makes before it gives up
+ *            (0, as zeroed: 2^22, well under a second; the caller may set it
+ *            before the launch), the words at bytes 16 and 20 a launch
+ *            counter and the piece count of the last launch.  The rest holds
+ *            the published piece sums.  A completed call leaves the workspace
+ *            ready for the next call of a plan with the same piece count; a
+ *            call with another piece count raises the flag and writes
+ *            nothing.  A non-zero flag means a wait gave up (or the piece
+ *            count changed): a workgroup whose wait gave up writes nothing
+ *            after it (its tiles of master, m, v, the replicas and the mean
+ *            keep their previous values, and it stores no norm), so each tile
+ *            holds either its previous state or its correct update; the
+ *            call's result as a whole is then incomplete, and while the flag
+ *            is up every further call on the workspace returns at once
+ *            without writing anything.  Zero the workspace (the poll limit
+ *            word may be kept) before the next call.  Calls that share a
+ *            workspace must not overlap.  The peers' entries of piece_sqnorm
+ *            are sums of squares: non-negative (a NaN is carried as NaN).
  * sqnorm_out, clip_scale_out  device scalars as for dp_grad_sqnorm, or NULL.
  * mean_out   device fp32 copy of the mean (as dp_reduce_scatter_mean writes
  *            it), or NULL.
  * Errors: as dp_reduce_scatter_mean and zero1_adamw_gather; GRZ_ERANGE when
- * the plan has more pieces than zero1_fused_capacity, more than 32 (bucket,
- * chunk) segments, or more than 4096^2 pieces in all; GRZ_EHIP when the
- * device cannot launch cooperatively.
+ * the plan has more pieces than zero1_fused_capacity (less its folding
+ * workgroups), more than 32 (bucket, chunk) segments, or more than 2^20
+ * pieces in all; GRZ_EHIP when the launch fails (with GRZ_COOPERATIVE, also
+ * when the device cannot launch cooperatively).
  */
 int zero1_fused_step(const void* const* rank_grads, int nranks, int dtype,
                      const grz_bucket* buckets, int nbuckets, int chunk, int flags,

@@ -44,6 +44,7 @@ def test_header_constants_match_binding():
     assert re.search(r"#define GRZ_PIECE (\d+)", text).group(1) == str(N.GRZ_PIECE)
     for name in ("GRZ_SUM", "GRZ_UNEVEN", "GRZ_IN_COMPACT", "GRZ_BF16_WIRE", "GRZ_IN_RANGE",
                  "GRZ_ARGS_DEVICE", "GRZ_OUT_GLOBAL", "GRZ_IN_TILED", "GRZ_MEAN_BF16",
+                 "GRZ_COOPERATIVE",
                  "GRZ_EINDIVISIBLE",
                  "GRZ_BF16"):
         assert re.search(rf"{name} = (\d+)", text).group(1) == str(getattr(N, name))
@@ -208,11 +209,11 @@ def test_norm_and_fused_workspace_sizes():
     assert grz.dp_grad_sqnorm_of_workspace(0) == 0
     assert grz.dp_grad_sqnorm_of_workspace(1) == 8
     assert grz.dp_grad_sqnorm_of_workspace(4096 * 4097) == 4097 * 8 + 2 * 8
-    sync = 33 * 256  # barrier counters: a top block and 32 group blocks
-    assert grz.zero1_fused_workspace(0) == sync
-    assert grz.zero1_fused_workspace(4096) == sync
-    assert grz.zero1_fused_workspace(4097) == sync + 2 * 8
-    assert grz.zero1_fused_workspace(4096 * 4096) == sync + 4096 * 8
+    ctl = 256  # control words; then one published slot per piece, per level sum, the norm
+    assert grz.zero1_fused_workspace(0) == ctl + 8
+    assert grz.zero1_fused_workspace(4096) == ctl + (4096 + 1) * 8
+    assert grz.zero1_fused_workspace(4097) == ctl + (4097 + 2 + 1) * 8
+    assert grz.zero1_fused_workspace(4096 * 4096) == ctl + (4096 * 4096 + 4096 + 1) * 8
 
 
 def test_fused_step_refusals_before_any_launch():

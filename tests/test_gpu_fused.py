@@ -108,13 +108,14 @@ def test_fused_one_rank_equals_three_kernels(config):
     mean_copy = torch.full_like(three.mean, float("nan"))
     for t in (1, 2, 3):
         three.step(inp["incoming"], inp["peer_shards"], t)
-        if t == 1:  # once with the optional copy of the mean
+        if t == 1:  # once with the optional copy of the mean, launched cooperatively
             w, m, v = one.state
             grz.zero1_fused_step(inp["incoming"], buckets, one.chunk, w, m, v,
                                  grz.adamw_args(**grz.step_scalars(one.hyper, t)),
                                  one.hyper.max_norm, [one.arena], one.norm.partials,
                                  one.workspace, one.norm.sqnorm, one.norm.scale,
-                                 mean_out=mean_copy, flags=grz.GRZ_IN_COMPACT)
+                                 mean_out=mean_copy,
+                                 flags=grz.GRZ_IN_COMPACT | grz.GRZ_COOPERATIVE)
             one.gather(inp["peer_shards"])
         else:
             one.step(inp["incoming"], inp["peer_shards"], t)
@@ -227,7 +228,9 @@ def test_fused_device_args_equal_host_args():
 
 def test_fused_refuses_what_it_cannot_hold():
     cap = grz.zero1_fused_capacity(1, torch.float32)
-    assert cap >= 4096  # 4 pieces per resident workgroup; 1024 on a 256-CU MI355X
+    # 4 pieces per resident workgroup but the one that folds the norm: 1023 on
+    # a 256-CU MI355X.
+    assert cap >= 4092
     p = (cap + 1) * grz.GRZ_PIECE
     g = torch.zeros(p, device=DEV)
     st = [torch.zeros(p, device=DEV) for _ in range(3)]
@@ -263,8 +266,9 @@ def test_fused_wait_that_gives_up_writes_nothing_and_is_reported(config):
     # three-kernel path's), never anything else; the step's check reports the
     # give-up and clears the workspace, keeping its poll limit.  Restarted
     # from the same state with the default limit, the next call is exact
-    # again.  The char GPT's plan has one grid barrier; GPT-2 124M's (30,416
-    # pieces, 9 buckets) two, either of which can give up.
+    # again.  The char GPT's plan (fewer than 4096 pieces) has one level of
+    # waits (workgroup 0 for the pieces, everyone for the norm); GPT-2 124M's
+    # (30,416 pieces, 9 buckets) two, any of which can give up.
     a = arena(config)
     p, n, rank = a.numel, 8, 5
     buckets = grz.plan_buckets(a.numels) if config == "gpt2_124m" else [(0, p)]
@@ -311,6 +315,49 @@ def test_fused_wait_that_gives_up_writes_nothing_and_is_reported(config):
     for k in range(3):
         _same(one.state[k], three.state[k], f"after the restart: state {k}")
     _same(one.arena, three.arena, "after the restart: arena")
+
+
+def test_fused_workspace_refuses_a_plan_of_another_piece_count():
+    # A workspace's published piece sums carry the parity of the launch that
+    # wrote them; they alternate launch by launch only while every launch
+    # rewrites all of them.  A call whose plan has another piece count than
+    # the last call's raises the flag and writes nothing; once the workspace
+    # is cleared the same call equals the three-kernel step.
+    n = 4
+    small, big = [(0, n * 4096 * 3)], [(0, n * 4096 * 5)]
+    p = big[0][1]
+    master = master_init(p, device=DEV)
+    grads = [rank_grad(p, 1e-2, "bf16", grad_seed(5, r), device=DEV) for r in range(n)]
+    hyper = grz.Hyper(max_norm=0.5)
+    args = grz.adamw_args(**grz.step_scalars(hyper, 1))
+    ws = torch.zeros(grz.zero1_fused_workspace(grz.dp_piece_count(big, n)), dtype=torch.uint8,
+                     device=DEV)
+    q = small[0][1]
+    s1 = [master[:q].clone(), torch.zeros(q, device=DEV), torch.zeros(q, device=DEV)]
+    r1 = torch.zeros(q, dtype=torch.bfloat16, device=DEV)
+    parts1 = torch.zeros(grz.dp_piece_count(small, n), dtype=torch.float64, device=DEV)
+    grz.zero1_fused_step([g[:q] for g in grads], small, -1, *s1, args, hyper.max_norm, [r1],
+                         parts1, ws)
+    torch.cuda.synchronize()
+    assert not grz.fused_timed_out(ws)
+    s2 = [master.clone(), torch.zeros(p, device=DEV), torch.zeros(p, device=DEV)]
+    r2 = torch.zeros(p, dtype=torch.bfloat16, device=DEV)
+    parts2 = torch.zeros(grz.dp_piece_count(big, n), dtype=torch.float64, device=DEV)
+    grz.zero1_fused_step(grads, big, -1, *s2, args, hyper.max_norm, [r2], parts2, ws)
+    torch.cuda.synchronize()
+    assert grz.fused_timed_out(ws)
+    _same(s2[0], master, "refused call: master untouched")
+    assert not s2[1].any() and not s2[2].any() and not r2.view(torch.int16).any()
+    assert not parts2.any()
+    grz.fused_clear(ws)
+    grz.zero1_fused_step(grads, big, -1, *s2, args, hyper.max_norm, [r2], parts2, ws)
+    three = grz.DDPStep(big, n, master, hyper, device=DEV)
+    three.step(grads, 1)
+    torch.cuda.synchronize()
+    assert not grz.fused_timed_out(ws)
+    for k in range(3):
+        _same(s2[k], three.state[k], f"after the clear: state {k}")
+    _same(r2, three.replica, "after the clear: weights")
 
 
 def test_fused_sixteen_ranks_equals_three_kernels():
