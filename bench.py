@@ -855,6 +855,46 @@ def other_configs_bench(args, dev):
         }
         log(f"{name} one-rank share as a graph: warm {warm:.4f} ms, cold {cold:.4f} ms "
             f"(70 % of peak: {target:.4f} ms)")
+        own_pieces, fcap = fused_fit(setup)
+        if own_pieces <= fcap and len(setup["buckets"]) <= 32:
+            # The same step as one launch (reduce + norm + clip + AdamW) and the
+            # peers' copy, captured and replayed the same way.
+            fpipe = grz.Zero1OneRank(setup["buckets"], n, 0, inp["shard_master"].clone(),
+                                     device=dev, arena_numel=setup["p"], fused=True)
+            fpipe.norm.partials.copy_(inp["partials"])
+            fcapt = grz.CapturedStep(lambda a, s: (fpipe.fused_update(inp["incoming"], a, s),
+                                                   fpipe.gather(inp["peer_shards"], s)),
+                                     fpipe.hyper, 1, count)
+            settle()
+            for _ in range(args.warmup):
+                fcapt.replay()
+            torch.cuda.synchronize()
+            g0.record(stream)
+            for _ in range(steps):
+                fcapt.replay()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            fwarm = g0.elapsed_time(g1) / steps
+            for k in range(args.warmup + steps):
+                scrub.fill_(k & 255)
+                if k >= args.warmup:
+                    ev[k - args.warmup][0].record(stream)
+                fcapt.replay()
+                if k >= args.warmup:
+                    ev[k - args.warmup][1].record(stream)
+            torch.cuda.synchronize()
+            fpipe.check_fused()  # raises if a wait of any replay gave up
+            fcold = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+            fbytes = owned * (n * 2 + 12 + 14 + bytes_per_owned(n)["gather"])
+            out[name].update({
+                "fused_graph_ms_per_step": fwarm, "fused_cold_graph_ms_per_step": fcold,
+                "fused_step_bytes": fbytes,
+                "fused_params_per_s": owned / (fwarm * 1e-3),
+                "fused_frac_of_peak": fbytes / (fwarm * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            })
+            log(f"{name} one-rank share, one launch + copy as a graph: warm {fwarm:.4f} ms, "
+                f"cold {fcold:.4f} ms")
+            del fpipe, fcapt
         del setup, pipe, inp, cap
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
@@ -884,6 +924,22 @@ def other_modes_bench(args, dev):
     return out
 
 
+def fused_fit(setup):
+    """(own pieces, pieces one launch holds for this plan): the launch's
+    resident workgroups hold 4 pieces each, less one folding workgroup per
+    4096 pieces of the plan (at least one)."""
+    import torch
+
+    import gradient_reduce_zero_amd as grz
+
+    n = setup["n"]
+    own = sum(-(-grz.dp_chunk_range(l, n, setup["chunk"])[1] // grz.GRZ_PIECE)
+              for _, l in setup["buckets"])
+    cap = grz.zero1_fused_capacity(n, torch.bfloat16)  # with one folding workgroup
+    nl = -(-setup["npieces"] // 4096) if setup["npieces"] > 4096 else 0
+    return own, cap - 4 * (max(nl, 1) - 1)
+
+
 def fused_bench(args, setup, stream, dev):
     """The same one-rank step with reduce + norm + clip + AdamW as one launch."""
     import torch
@@ -891,9 +947,7 @@ def fused_bench(args, setup, stream, dev):
     import gradient_reduce_zero_amd as grz
 
     n, inp = setup["n"], setup["inp"]
-    own_pieces = sum(-(-grz.dp_chunk_range(l, n, setup["chunk"])[1] // grz.GRZ_PIECE)
-                     for _, l in setup["buckets"])
-    cap = grz.zero1_fused_capacity(n, torch.bfloat16)
+    own_pieces, cap = fused_fit(setup)
     if own_pieces > cap or len(setup["buckets"]) > 32:
         log(f"fused step: {own_pieces} pieces do not fit the {cap} one launch holds")
         return {"fits": False, "pieces": own_pieces, "capacity": cap}
@@ -919,7 +973,7 @@ def fused_bench(args, setup, stream, dev):
         t += 1
     stop.record(stream)
     torch.cuda.synchronize()
-    pipe.check_fused()  # raises if a grid-wide wait gave up
+    pipe.check_fused()  # raises if a wait of a launch gave up
     ms = start.elapsed_time(stop) / args.steps
     fused_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     gather_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps

@@ -155,14 +155,16 @@ def _arenas(rank_grads):
 
 
 def _check_fused(workspace):
-    """Raise if a grid-wide wait of the last one-launch step gave up, after
-    clearing the workspace's counters so that the next step can run.  Reads a
-    device word, so it waits for the stream's work."""
+    """Raise if a wait of the last one-launch step gave up (or the workspace
+    last served a plan of another piece count), after clearing the workspace
+    so that the next step can run.  Reads a device word, so it waits for the
+    stream's work."""
     if workspace is not None and B.fused_timed_out(workspace):
         B.fused_clear(workspace)
-        raise RuntimeError("a grid-wide wait of the one-launch step gave up: the tiles of the "
-                           "workgroups that gave up kept their previous state (the others were "
-                           "updated); the workspace has been cleared")
+        raise RuntimeError("a wait of the one-launch step gave up, or its workspace served a "
+                           "plan of another piece count: the tiles of the workgroups that gave "
+                           "up kept their previous state (the others were updated); the "
+                           "workspace has been cleared")
 
 
 class Zero1AllRanks:
