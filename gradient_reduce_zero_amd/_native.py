@@ -70,6 +70,8 @@ SIGNATURES = {
     "zero1_fused_step": (_i, [_pp, _i, _i, _BP, _i, _i, _i, _vp, _vp, _vp,
                               ctypes.POINTER(AdamWArgs), _d, _pp, _i, _vp, _vp, _vp, _vp, _vp,
                               _vp]),
+    "zero1_fused_step_args": (_i, [_pp, _i, _i, _BP, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _vp,
+                                   _vp, _d, _pp, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None

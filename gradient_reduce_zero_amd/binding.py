@@ -214,7 +214,8 @@ class StepScalars:
     float32 values, one per step), ``counter`` (int64, the next row) and
     ``current`` (the row the optimizer reads).  The first call of a step that
     needs ``current`` advances it -- the norm in its own last launch
-    (``dp_grad_sqnorm_step_args``), else the optimizer's entry point with a
+    (``dp_grad_sqnorm_step_args``), the one-launch step in its launch
+    (``zero1_fused_step_args``), else the optimizer's entry point with a
     ``grz_step_args_next`` launch before its own; ``advanced`` records that it
     was done for the step being enqueued.
 
@@ -451,8 +452,9 @@ def zero1_fused_step(rank_grads, buckets, chunk, master, m, v, args, max_norm, r
     (``chunk >= 0``) or of every chunk (``chunk = -1``) in one launch.
 
     ``workspace`` (``zero1_fused_workspace`` bytes) must be zeroed before its
-    first use; ``args`` is an ``AdamWArgs`` or a device float32 tensor of 7
-    values (``GRZ_ARGS_DEVICE``)."""
+    first use; ``args`` is an ``AdamWArgs``, a device float32 tensor of 7
+    values (``GRZ_ARGS_DEVICE``), or a ``StepScalars`` whose row the launch
+    takes and advances itself (``zero1_fused_step_args``)."""
     n = len(rank_grads)
     if not 1 <= n <= N.GRZ_MAX_RANKS:
         raise ValueError(f"{n} ranks; 1..{N.GRZ_MAX_RANKS} supported")
@@ -483,6 +485,17 @@ def zero1_fused_step(rank_grads, buckets, chunk, master, m, v, args, max_norm, r
     reps = (ctypes.c_void_p * max(len(replicas), 1))(
         *[_dev(r, f"replicas[{i}]", _BF16_LIKE, ext).value for i, r in enumerate(replicas)])
     arr, nb = _bucket_array(buckets)
+    if isinstance(args, StepScalars) and not args.advanced:
+        # One launch takes the step's row of the table and advances it.
+        check("zero1_fused_step_args",
+              lib().zero1_fused_step_args(
+                  ptrs, n, kind, arr, nb, chunk, flags, w, mm, vv,
+                  _dev(args.table, "table", (torch.float32,)), args.table.shape[0],
+                  _dev(args.counter, "counter", (torch.int64,), 1),
+                  _dev(args.current, "current", (torch.float32,), ARGS_FIELDS),
+                  float(max_norm), reps, len(replicas), part, ws, sq, sc, mo, _stream(stream)))
+        args.advanced = True
+        return
     a, on_device = _device_args(args, stream)
     if on_device:
         flags |= N.GRZ_ARGS_DEVICE

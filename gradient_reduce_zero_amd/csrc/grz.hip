@@ -481,10 +481,14 @@ __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void rs_mean_kernel(const RsA
     bool done = false;
     if constexpr (GRZ_RS_BATCH && NR > 0 && sizeof(TIn) < 8) {
       if (s.vec && left >= GRZ_PIECE) {
-        // At most 32 loads in flight per lane: the whole tile for N <= 8, two
-        // accesses at a time for N = 9..16.  The squares are added in the same
-        // order either way.
-        constexpr int KB = NR * K <= 32 ? K : (NR * (K / 2) <= 32 ? K / 2 : 1);
+        // At most 64 registers of loads in flight per lane (32 bf16 loads of
+        // 8 bytes, 16 fp32 loads of 16 bytes): for bf16 the whole tile for
+        // N <= 8 and two accesses at a time for N = 9..16, for fp32 the whole
+        // tile for N <= 4 and two accesses for N = 5..8.  Beyond that the
+        // three-wave shape of small launches spilled.  The squares are added
+        // in the same order either way.
+        constexpr int LW = static_cast<int>(sizeof(TIn)) * G / 4;  // registers per load
+        constexpr int KB = NR * K * LW <= 64 ? K : (NR * (K / 2) * LW <= 64 ? K / 2 : 1);
         static_assert(K % KB == 0, "batch shape");
 #pragma unroll
         for (int k0 = 0; k0 < K; k0 += KB) {
@@ -857,6 +861,7 @@ struct FusedArgs {
   double* sqnorm_out;
   float* scale_out;
   const grz_adamw_args* dargs;    // step scalars in device memory, or null
+  StepArgsNext next;              // or the launch takes them from a table and advances it
   double max_norm;
   double divisor;
   int64_t ntiles;                 // pieces this launch reduces
@@ -995,7 +1000,10 @@ void fused_step_kernel(const FusedArgs<TIn> a) {
   // not all have been rewritten by the last launch), does nothing until it is
   // cleared; a plan of another piece count also raises the flag.
   __shared__ unsigned ctl_lds[2];
+  __shared__ int64_t step_lds;  // the step counter, with a table of step scalars
   if (lane == 0) {
+    if (a.next.table != nullptr)
+      step_lds = __hip_atomic_load(a.next.counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned flag = __hip_atomic_load(a.ctl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned plan = __hip_atomic_load(a.ctl + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool other_plan = plan != 0 && plan != static_cast<unsigned>(a.npieces + 1);
@@ -1130,16 +1138,29 @@ void fused_step_kernel(const FusedArgs<TIn> a) {
   if (blockIdx.x == 0 && lane == 0) {
     if (a.sqnorm_out != nullptr) *a.sqnorm_out = sqnorm;
     if (a.scale_out != nullptr) *a.scale_out = scale;
-    // Every workgroup has read the launch counter (each published a piece
-    // after reading it), so the next launch's parity can be set.
+    // Every workgroup has read the launch counter and the step counter (each
+    // published a piece after reading them), so both can advance.
     __hip_atomic_store(a.ctl + 4, launch_no + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(a.ctl + 5, static_cast<unsigned>(a.npieces + 1), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+    if (a.next.table != nullptr) {
+      const int64_t c = step_lds;
+      *a.next.current = a.next.table[c < 0 ? 0 : (c >= a.next.count ? a.next.count - 1 : c)];
+      __hip_atomic_store(a.next.counter, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   // Clip + AdamW from the registers; bf16 weights into every replica.
   float lr = a.lr, b1 = a.b1, b2 = a.b2, eps = a.eps, wd = a.wd, bc1 = a.bc1, bc2 = a.bc2;
-  if (a.dargs != nullptr) {
+  if (a.next.table != nullptr) {
+    // Row min(counter, count - 1) of the table: the step scalars
+    // grz_step_args_next would have copied to `current`.
+    const int64_t c = step_lds;
+    const ConstArgs* d = (const ConstArgs*)(a.next.table +
+                                            (c < 0 ? 0 : (c >= a.next.count ? a.next.count - 1 : c)));
+    lr = d->lr; b1 = d->beta1; b2 = d->beta2; eps = d->eps; wd = d->weight_decay;
+    bc1 = d->bias_corr1; bc2 = d->bias_corr2;
+  } else if (a.dargs != nullptr) {
     // Read as constant memory (the scalars do not change while the kernel
     // runs), so that they arrive through uniform loads rather than a vector
     // load that every workgroup waits for before its first tile.
@@ -2066,7 +2087,8 @@ int fused_max_grid(const void* kernel, int* grid) {
 template <typename TIn>
 int fused_launch(const void* kernel, const void* const* rank_grads, int nranks,
                  const std::vector<PlanSeg>& ps, int flags, float* master, float* m, float* v,
-                 const grz_adamw_args* args, double max_norm, uint16_t* const* replicas,
+                 const grz_adamw_args* args, const StepArgsNext& next, double max_norm,
+                 uint16_t* const* replicas,
                  int nreplicas, double* piece_sqnorm, int64_t npieces, void* workspace,
                  double* sqnorm_out, float* clip_scale_out, float* mean_out,
                  hipStream_t stream) {
@@ -2132,7 +2154,9 @@ int fused_launch(const void* kernel, const void* const* rank_grads, int nranks,
   a.nranks = nranks;
   a.nrep = nreplicas;
   a.nsegs = nsegs;
-  if (flags & GRZ_ARGS_DEVICE) {
+  if (next.table != nullptr) {
+    a.next = next;
+  } else if (flags & GRZ_ARGS_DEVICE) {
     a.dargs = args;
   } else {
     a.lr = args->lr;
@@ -2171,12 +2195,16 @@ int64_t zero1_fused_capacity(int nranks, int dtype) {
   return static_cast<int64_t>(grid - 1) * kFusedPieces;  // one workgroup folds the norm
 }
 
-int zero1_fused_step(const void* const* rank_grads, int nranks, int dtype,
-                     const grz_bucket* buckets, int nbuckets, int chunk, int flags,
-                     float* master, float* m, float* v, const grz_adamw_args* args,
-                     double max_norm, uint16_t* const* replicas, int nreplicas,
-                     double* piece_sqnorm, void* workspace, double* sqnorm_out,
-                     float* clip_scale_out, float* mean_out, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int fused_entry(const void* const* rank_grads, int nranks, int dtype,
+                const grz_bucket* buckets, int nbuckets, int chunk, int flags, float* master,
+                float* m, float* v, const grz_adamw_args* args, const StepArgsNext& next,
+                double max_norm, uint16_t* const* replicas, int nreplicas,
+                double* piece_sqnorm, void* workspace, double* sqnorm_out,
+                float* clip_scale_out, float* mean_out, hipStream_t stream) {
   if (flags & ~(GRZ_UNEVEN | GRZ_IN_COMPACT | GRZ_ARGS_DEVICE | GRZ_COOPERATIVE))
     return GRZ_EINVAL;
   int st = check_plan(buckets, nbuckets, nranks, chunk,
@@ -2207,11 +2235,42 @@ int zero1_fused_step(const void* const* rank_grads, int nranks, int dtype,
   if (ps.size() > static_cast<size_t>(kFusedSegs)) return GRZ_ERANGE;
   if (dtype == GRZ_BF16)
     return fused_launch<uint16_t>(kernel, rank_grads, nranks, ps, flags, master, m, v, args,
-                                  max_norm, replicas, nreplicas, piece_sqnorm, npieces,
+                                  next, max_norm, replicas, nreplicas, piece_sqnorm, npieces,
                                   workspace, sqnorm_out, clip_scale_out, mean_out, stream);
-  return fused_launch<float>(kernel, rank_grads, nranks, ps, flags, master, m, v, args,
+  return fused_launch<float>(kernel, rank_grads, nranks, ps, flags, master, m, v, args, next,
                              max_norm, replicas, nreplicas, piece_sqnorm, npieces, workspace,
                              sqnorm_out, clip_scale_out, mean_out, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int zero1_fused_step(const void* const* rank_grads, int nranks, int dtype,
+                     const grz_bucket* buckets, int nbuckets, int chunk, int flags,
+                     float* master, float* m, float* v, const grz_adamw_args* args,
+                     double max_norm, uint16_t* const* replicas, int nreplicas,
+                     double* piece_sqnorm, void* workspace, double* sqnorm_out,
+                     float* clip_scale_out, float* mean_out, hipStream_t stream) {
+  return fused_entry(rank_grads, nranks, dtype, buckets, nbuckets, chunk, flags, master, m, v,
+                     args, StepArgsNext{}, max_norm, replicas, nreplicas, piece_sqnorm,
+                     workspace, sqnorm_out, clip_scale_out, mean_out, stream);
+}
+
+int zero1_fused_step_args(const void* const* rank_grads, int nranks, int dtype,
+                          const grz_bucket* buckets, int nbuckets, int chunk, int flags,
+                          float* master, float* m, float* v, const grz_adamw_args* table,
+                          int64_t count, int64_t* counter, grz_adamw_args* current,
+                          double max_norm, uint16_t* const* replicas, int nreplicas,
+                          double* piece_sqnorm, void* workspace, double* sqnorm_out,
+                          float* clip_scale_out, float* mean_out, hipStream_t stream) {
+  if (flags & GRZ_ARGS_DEVICE) return GRZ_EINVAL;  // implied
+  const int st = check_step_args(table, count, counter, current);
+  if (st != GRZ_OK) return st;
+  return fused_entry(rank_grads, nranks, dtype, buckets, nbuckets, chunk, flags, master, m, v,
+                     table, StepArgsNext{table, count, counter, current}, max_norm, replicas,
+                     nreplicas, piece_sqnorm, workspace, sqnorm_out, clip_scale_out, mean_out,
+                     stream);
 }
 
 }  // extern "C"

@@ -141,7 +141,8 @@ class _Norm:
 
 
 def _fused_workspace(npieces, device):
-    """Zeroed workspace of the one-launch step (barrier words + norm level)."""
+    """Zeroed workspace of the one-launch step (control words and the slots
+    its workgroups publish the norm's sums in)."""
     return torch.zeros(B.zero1_fused_workspace(npieces), dtype=torch.uint8, device=device)
 
 
@@ -584,9 +585,9 @@ class CapturedStep:
     step, so they live in a device table (rows for steps ``first_t`` ..
     ``first_t + count - 1``, filled once on the host with ``step_scalars``);
     each replay copies its row to the slot the optimizer reads
-    (``GRZ_ARGS_DEVICE``) in the norm's last launch (``StepScalars``; a step
-    without a norm launch of its own, the one-launch step, gets a one-thread
-    kernel before its launch instead).  ``enqueue(args, stream)`` must enqueue
+    (``GRZ_ARGS_DEVICE``) in the norm's last launch (``StepScalars``; the
+    one-launch step, which has no norm launch of its own, does it in its
+    launch).  ``enqueue(args, stream)`` must enqueue
     the step's kernels with ``args`` as their scalars;
     every buffer it touches keeps its address for the graph's lifetime.
     ``replay`` counts replays on the host and raises once the table's

@@ -519,6 +519,26 @@ int zero1_fused_step(const void* const* rank_grads, int nranks, int dtype,
                      double* piece_sqnorm, void* workspace, double* sqnorm_out,
                      float* clip_scale_out, float* mean_out, hipStream_t stream);
 
+/*
+ * zero1_fused_step whose step scalars come from a table and advance in the
+ * same launch, for a captured step replayed once per step ("Distributed
+ * training", "Overlap and graphs": one graph per GPU, replayed): the launch
+ * uses row min(*counter, count - 1) of `table` (rows as for
+ * grz_step_args_next), copies it to *current and adds one to *counter, as
+ * grz_step_args_next followed by zero1_fused_step with GRZ_ARGS_DEVICE would,
+ * without the extra launch.  table, counter and current are device pointers;
+ * GRZ_ARGS_DEVICE is implied (passing it: GRZ_EINVAL).  A call that writes
+ * nothing (a wait gave up, see zero1_fused_step) leaves the counter as it was.
+ * Everything else is zero1_fused_step.
+ */
+int zero1_fused_step_args(const void* const* rank_grads, int nranks, int dtype,
+                          const grz_bucket* buckets, int nbuckets, int chunk, int flags,
+                          float* master, float* m, float* v, const grz_adamw_args* table,
+                          int64_t count, int64_t* counter, grz_adamw_args* current,
+                          double max_norm, uint16_t* const* replicas, int nreplicas,
+                          double* piece_sqnorm, void* workspace, double* sqnorm_out,
+                          float* clip_scale_out, float* mean_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -234,6 +234,20 @@ def test_fused_step_refusals_before_any_launch():
         assert call(flags=flags) == N.GRZ_EINVAL
     assert call(nranks=17) == N.GRZ_EINVAL
     assert call(master=None) == N.GRZ_EINVAL
+
+    # The form that takes its step scalars from a table: GRZ_ARGS_DEVICE is
+    # implied, and the table, its size and the counter are checked.
+    def call_args(flags=0, table=0x20000, count=4, counter=0x30000, current=0x40000):
+        return lib.zero1_fused_step_args(ptrs, 2, N.GRZ_BF16, b, 1, 0, flags, 16, 16, 16, table,
+                                         count, counter, current, 1.0, reps, 1, 16, 16, None,
+                                         None, None, None)
+
+    assert call_args(flags=N.GRZ_ARGS_DEVICE) == N.GRZ_EINVAL
+    assert call_args(flags=N.GRZ_SUM) == N.GRZ_EINVAL
+    assert call_args(table=None) == N.GRZ_EINVAL
+    assert call_args(count=0) == N.GRZ_EINVAL
+    assert call_args(counter=None) == N.GRZ_EINVAL
+    assert call_args(counter=0x30004) == N.GRZ_EALIGN
     assert lib.zero1_fused_capacity(0, N.GRZ_BF16) == -N.GRZ_EINVAL
     assert lib.zero1_fused_capacity(2, N.GRZ_F64) == -N.GRZ_EINVAL
 
