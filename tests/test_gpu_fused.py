@@ -317,6 +317,41 @@ def test_fused_wait_that_gives_up_writes_nothing_and_is_reported(config):
     _same(one.arena, three.arena, "after the restart: arena")
 
 
+@pytest.mark.parametrize("bad", ["nan", "inf", "peer_nan"])
+def test_fused_non_finite_gradient_equals_three_kernels(bad):
+    # A NaN or an infinity in one rank's gradient (or a NaN among the peers'
+    # piece sums): the norm is NaN or +Inf, the clip factor 1 (NaN) or 0
+    # (Inf, max_norm / Inf), and the update propagates it.  The published slot
+    # carries a NaN as the one quiet NaN, so only the NaN's payload in the
+    # norm may differ; master, m, v and the arena equal the three kernels'
+    # bit for bit (NaN where the three kernels have NaN).
+    a = arena("char_gpt")
+    p, n, rank = a.numel, 8, 4
+    buckets = [(0, p)]
+    inp, three, one = _one_rank_pair(buckets, p, n, rank)
+    if bad == "peer_nan":
+        slot = next(i for i in range(one.norm.npieces)
+                    if all(not (f <= i < f + c) for f, c in one.own_piece_slots()))
+        for z in (three, one):
+            z.norm.partials[slot] = float("nan")
+    else:
+        g = inp["incoming"][5].view(torch.int16)
+        g[1234] = 0x7FC0 if bad == "nan" else 0x7F80  # bf16 NaN / +Inf
+    three.step(inp["incoming"], inp["peer_shards"], 1)
+    one.step(inp["incoming"], inp["peer_shards"], 1)
+    torch.cuda.synchronize()
+    one.check_fused()
+    s3, s1 = three.norm.sqnorm.item(), one.norm.sqnorm.item()
+    if bad == "inf":
+        assert s3 == s1 == float("inf")
+    else:
+        assert math.isnan(s3) and math.isnan(s1)
+    _same(one.norm.scale, three.norm.scale, "clip factor")
+    for k in range(3):
+        _same(one.state[k], three.state[k], f"{bad}: state {k}")
+    _same(one.arena, three.arena, f"{bad}: arena")
+
+
 def test_fused_workspace_refuses_a_plan_of_another_piece_count():
     # A workspace's published piece sums carry the parity of the launch that
     # wrote them; they alternate launch by launch only while every launch
