@@ -885,11 +885,13 @@ struct FusedArgs {
 // own flag, so nothing else has to be ordered: no counter, no fence, and none
 // of the L2 write-back and invalidation that a device-scope release and
 // acquire cost on this chip (with a two-level barrier the launch took 0.24 ms
-// at the GPT-2 124M one-rank share).  The tree is dp_grad_sqnorm's: level
-// block j (more than 4096 pieces) is folded by workgroup j and published in
-// its own slot, workgroup 0 folds the level slots (or the pieces) into the
-// norm, publishes it and advances the launch counter, and every workgroup
-// waits for that one slot.  A NaN sum is published as the one quiet NaN.
+// at the GPT-2 124M one-rank share).  The tree is dp_grad_sqnorm's, folded by
+// workgroups after the reducing ones, which hold no mean: with more than 4096
+// pieces, folder j folds level block j and publishes it in its own slot and
+// every reducing workgroup folds the level slots itself; with fewer, the one
+// folder folds the pieces and publishes the norm, which every reducing
+// workgroup waits for.  Workgroup 0 advances the launch counter once it has
+// the norm.  A NaN sum is published as the one quiet NaN.
 //
 // Control words (32-bit, the first kCtlBytes of the workspace): word 2 the
 // time-out flag, word 3 the poll limit (0 means kDefaultSpinLimit), word 4
@@ -927,9 +929,10 @@ __device__ __forceinline__ bool collect(uint64_t* slot, uint64_t parity, unsigne
 
 // fan_block_sum over published slots [base, base + 4096) (those below n): the
 // same additions in the same order, each value taken once it is published.
-// A lane loads all its 16 slots at once and polls again only those that
-// were not published yet.  False (in every thread) when a wait of any thread
-// gave up.
+// A lane loads its 16 slots kBatch at a time (all at once: the folders hold
+// no mean, so the registers are there) and polls again only those that were
+// not published yet.  False (in every thread) when a wait of any thread gave
+// up.
 __device__ __forceinline__ bool fan_block_collect(uint64_t* slots, int64_t n, int64_t base,
                                                   uint64_t parity, unsigned limit,
                                                   double* lds, double* out) {
