@@ -128,3 +128,45 @@ def test_bench_ddp_one_rank_gpt2_124m_matches_oracle():
     for k, x in enumerate((w, m, v)):
         assert_bits(host(one.state[k]), x, f"DDP 124M state {k}")
     assert_bits(host(one.arena), bf16_round(w), "DDP 124M bf16 arena")
+
+
+def test_bench_char_gpt_share_100_steps_matches_oracle():
+    # The char GPT workload runs 100 steps.  The bench's char GPT one-rank
+    # share (N = 8, rank 0, the tiled receive buffer), captured and replayed
+    # 100 times, as three kernels and as one launch (zero1_fused_step_args):
+    # master, m, v and the own shard in the arena against the oracle's AdamW
+    # after every 10th step, bit for bit (the same received gradients every
+    # step, so the oracle's mean and norm are computed once).
+    setup = bench.onerank_setup("char_gpt", 8, 0, DEV)
+    one, inp = setup["pipe"], setup["inp"]
+    chunk, shard, buckets, n = setup["chunk"], setup["shard"], setup["buckets"], setup["n"]
+    fused = grz.Zero1OneRank(buckets, n, 0, inp["shard_master"].clone(), device=DEV,
+                             arena_numel=setup["p"], fused=True)
+    fused.norm.partials.copy_(inp["partials"])
+    mean = chunk_mean([widen(host(t), "bf16") for t in inp["incoming"]], chunk)
+    scale = clip_scale(grad_sqnorm(mean, extra=host(inp["partials"])[_peer_mask(one)]), 1.0)
+    assert scale < 1
+    steps = 100
+    three_cap = grz.CapturedStep(lambda a, s: (one.reduce(inp["recv"], s),
+                                               one.update(None, s, args=a),
+                                               one.gather(inp["peer_shards"], s)),
+                                 one.hyper, 1, steps)
+    fused_cap = grz.CapturedStep(lambda a, s: (fused.fused_update(inp["incoming"], a, s),
+                                               fused.gather(inp["peer_shards"], s)),
+                                 fused.hyper, 1, steps)
+    w = host(one.state[0])
+    m, v = np.zeros_like(w), np.zeros_like(w)
+    g = mean * scale
+    h = OHyper()
+    own = _arena_positions(shard_segments(buckets, n, chunk), np.arange(shard))
+    for t in range(1, steps + 1):
+        three_cap.replay()
+        fused_cap.replay()
+        w, m, v = adamw(w, m, v, g, **h.scalars(t))
+        if t % 10 == 0:
+            torch.cuda.synchronize()
+            fused.check_fused()
+            for pipe, name in ((one, "three kernels"), (fused, "one launch")):
+                for k, want in enumerate((w, m, v)):
+                    assert_bits(host(pipe.state[k]), want, f"{name} t={t}: state {k}")
+                assert_bits(host(pipe.arena)[own], bf16_round(w), f"{name} t={t}: own shard")
