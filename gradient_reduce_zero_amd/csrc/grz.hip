@@ -57,8 +57,8 @@ static_assert(GRZ_PIECE % (kThreads * 8) == 0, "piece shape");
 thread_local int g_max_blocks = 1 << 30;
 
 // Polls of a wait of the fused step before it gives up, when the workspace
-// does not set its own limit.  Each poll sleeps about a hundred cycles, so
-// this bounds a wait at well under a second.
+// does not set its own limit.  Each poll is a device-scope load (about a
+// microsecond) and a short sleep, so this bounds a wait at a few seconds.
 constexpr unsigned kDefaultSpinLimit = 1u << 22;
 
 // One contiguous run of work: `len` elements read at `src` and written at

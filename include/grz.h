@@ -486,7 +486,7 @@ int64_t zero1_fused_capacity(int nranks, int dtype);
  *            ZEROED before its first use.  Its first 256 bytes are control
  *            words: the 32-bit word at byte 8 is the time-out flag, the word
  *            at byte 12 the number of polls a wait makes before it gives up
- *            (0, as zeroed: 2^22, well under a second; the caller may set it
+ *            (0, as zeroed: 2^22, a few seconds; the caller may set it
  *            before the launch), the words at bytes 16 and 20 a launch
  *            counter and the piece count of the last launch.  The rest holds
  *            the published piece sums.  A completed call leaves the workspace
