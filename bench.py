@@ -561,6 +561,31 @@ def all_ranks_bench(args, dev, emit=True):
         out["arena_layout_graph_ms_per_step"] = ams
         out["arena_layout_graph_frac_of_peak"] = step_bytes / (ams * 1e-3) / 1e9 / PEAK_HBM_GBPS
         log(f"arena layout as a graph: {ams:.4f} ms/step over {reps} replays")
+        # The arena layout as one launch (reduce + norm + clip + AdamW with the
+        # bf16 write into all N replicas) where the whole plan fits one.
+        npieces = grz.dp_piece_count(buckets, n)
+        nl = -(-npieces // 4096) if npieces > 4096 else 0
+        fit = grz.zero1_fused_capacity(n, torch.bfloat16) - 4 * (max(nl, 1) - 1)
+        if npieces <= fit and len(buckets) * n <= 32:
+            fpipe = grz.DDPStep(buckets, n, master_init(p, device=dev), hyper, device=dev,
+                                nreplicas=n, fused=True)
+            fcap = grz.CapturedStep(lambda a_, s_: fpipe.enqueue(grads, a_, s_), hyper,
+                                    args.warmup + args.steps + 1, args.warmup + reps)
+            for _ in range(args.warmup):
+                fcap.replay()
+            torch.cuda.synchronize()
+            g0.record(s)
+            for _ in range(reps):
+                fcap.replay()
+            g1.record(s)
+            torch.cuda.synchronize()
+            fpipe.check_fused()
+            fms = g0.elapsed_time(g1) / reps
+            fbytes = p * (n * 2 + 28 + 2 * n)  # no mean written or read
+            out["arena_layout_one_launch_graph_ms_per_step"] = fms
+            out["arena_layout_one_launch_graph_frac_of_peak"] = (
+                fbytes / (fms * 1e-3) / 1e9 / PEAK_HBM_GBPS)
+            log(f"arena layout as one launch, as a graph: {fms:.4f} ms/step over {reps} replays")
     if not args.no_cpu:
         log("timing the CPU oracle's all-ranks step")
         out["cpu_baseline"] = cpu_baseline_all_ranks(grads, buckets, n, hyper,
