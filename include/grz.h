@@ -471,9 +471,9 @@ int64_t zero1_fused_capacity(int nranks, int dtype);
  *            shard-compact); chunk = -1: every chunk (plain data parallelism,
  *            master/m/v indexed like the arena).
  * flags      GRZ_UNEVEN, GRZ_IN_COMPACT (as for the reduce), GRZ_ARGS_DEVICE
- *            (as for zero1_adamw_gather), GRZ_COOPERATIVE (above).  GRZ_BF16_WIRE, GRZ_SUM and
- *            GRZ_IN_TILED are not taken (GRZ_EINVAL): use the separate entry
- *            points.
+ *            (as for zero1_adamw_gather), GRZ_COOPERATIVE (above).
+ *            GRZ_BF16_WIRE, GRZ_SUM, GRZ_IN_TILED and GRZ_MEAN_BF16 are not
+ *            taken (GRZ_EINVAL): use the separate entry points.
  * master, m, v  device fp32 state, updated in place.
  * args       the step's scalars (host, or device with GRZ_ARGS_DEVICE).
  * max_norm   clip threshold (<= 0: no clipping).
@@ -527,8 +527,10 @@ int zero1_fused_step(const void* const* rank_grads, int nranks, int dtype,
  * grz_step_args_next), copies it to *current and adds one to *counter, as
  * grz_step_args_next followed by zero1_fused_step with GRZ_ARGS_DEVICE would,
  * without the extra launch.  table, counter and current are device pointers;
- * GRZ_ARGS_DEVICE is implied (passing it: GRZ_EINVAL).  A call that writes
- * nothing (a wait gave up, see zero1_fused_step) leaves the counter as it was.
+ * GRZ_ARGS_DEVICE is implied (passing it: GRZ_EINVAL).  A call refused at its
+ * start (the workspace's flag up, or another piece count; see
+ * zero1_fused_step) leaves the counter as it was; after a wait gave up it
+ * may have advanced (workgroup 0 advances it once it has the norm).
  * Everything else is zero1_fused_step.
  */
 int zero1_fused_step_args(const void* const* rank_grads, int nranks, int dtype,
