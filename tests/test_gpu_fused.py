@@ -161,11 +161,14 @@ def test_fused_one_rank_mean_matches_oracle():
 
 # --- ragged, unaligned and N = 3 ---------------------------------------------
 
-@pytest.mark.parametrize("n,kind", [(3, "f32"), (3, "bf16"), (5, "bf16"), (8, "f32")])
+@pytest.mark.parametrize("n,kind", [(1, "f32"), (1, "bf16"), (2, "f32"), (2, "bf16"),
+                                    (3, "f32"), (3, "bf16"), (4, "f32"), (4, "bf16"),
+                                    (5, "bf16"), (8, "f32"), (8, "bf16")])
 def test_fused_ragged_unaligned_matches_three_kernels_and_oracle(n, kind):
     # Uneven chunks (GRZ_UNEVEN), a bucket shorter than N, pieces with ragged
     # tails, and every base one element past a 16-byte boundary (element-wise
-    # accesses throughout).
+    # accesses throughout).  N = 1, 2, 4 and 8 have their own kernel instances
+    # (a fold unrolled for that N), the others share the one that loops.
     buckets = [(3 * 4096 + 11, 2 * 4096 + 7), (0, 3 * 4096 + 11), (5 * 4096 + 18, 2)]
     p = 5 * 4096 + 20
     flags = grz.GRZ_UNEVEN
