@@ -818,9 +818,10 @@ __global__ __launch_bounds__(GRZ_AG_THREADS) GRZ_AG_ATTR void gather_kernel(
 
 // ---------------------------------------------------------------------------
 // K1 + K2 + K3 in one launch, for a shard whose mean fits in the registers of
-// the co-resident grid: the reduce keeps every mean value in registers, a
-// grid-wide barrier waits for every piece sum, each workgroup folds the norm
-// in the same tree as dp_grad_sqnorm, and the same registers feed AdamW.  The
+// the co-resident grid: the reduce keeps every mean value in registers, the
+// piece sums go through self-flagging workspace slots (below) to the
+// workgroups that fold the norm in the same tree as dp_grad_sqnorm, and the
+// same registers feed AdamW once the norm is known.  The
 // mean never goes to memory (unless asked for), which saves 8 bytes per owned
 // element against the three-kernel path.  The arithmetic of every value is
 // that of rs_mean_kernel, sqnorm_*_kernel and adamw_kernel, so the results are
