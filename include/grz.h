@@ -90,8 +90,9 @@ enum { GRZ_F32 = 0, GRZ_BF16 = 1, GRZ_F64 = 2 };
 
 /* Flags.  An entry point returns GRZ_EINVAL for a flag it does not take:
  * the reduce (dp_reduce_scatter_mean and its _range form) takes all but
- * GRZ_ARGS_DEVICE, the _weighted form all but that and GRZ_SUM;
- * zero1_adamw_gather takes GRZ_UNEVEN, GRZ_ARGS_DEVICE and GRZ_MEAN_BF16; the
+ * GRZ_ARGS_DEVICE and GRZ_COOPERATIVE, the _weighted form all but those and
+ * GRZ_SUM; zero1_adamw_gather takes GRZ_UNEVEN, GRZ_ARGS_DEVICE and
+ * GRZ_MEAN_BF16; the
  * all-gathers take GRZ_UNEVEN; zero1_fused_step GRZ_UNEVEN, GRZ_IN_COMPACT,
  * GRZ_ARGS_DEVICE and GRZ_COOPERATIVE.  Their meaning is in each entry
  * point's comment. */

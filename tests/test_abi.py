@@ -198,6 +198,23 @@ def test_bf16_mean_refusals():
                                 1, 16, 16, None, None, None, None) == N.GRZ_EINVAL
 
 
+def test_reduce_refuses_the_flags_of_other_entry_points():
+    # The reduce (and its _range and _weighted forms) takes neither
+    # GRZ_ARGS_DEVICE nor GRZ_COOPERATIVE; refused before any launch.
+    lib = grz.lib()
+    arr = (N.Bucket * 1)((0, 64))
+    pp = (ctypes.c_void_p * 2)(0x100000, 0x200000)
+    out = ctypes.c_void_p(0x30000)
+    counts = (ctypes.c_int64 * 2)(3, 5)
+    for f in (N.GRZ_ARGS_DEVICE, N.GRZ_COOPERATIVE, 1 << 12):
+        assert _rs(lib, [0x100000, 0x200000], 2, N.GRZ_BF16, [(0, 64)], 0, f, out) == \
+            N.GRZ_EINVAL
+        assert lib.dp_reduce_scatter_mean_range(pp, 2, N.GRZ_BF16, arr, 1, 0, 1, 0, f, out,
+                                                None, None) == N.GRZ_EINVAL
+        assert lib.dp_reduce_scatter_weighted(pp, counts, 2, N.GRZ_BF16, arr, 1, 0, 1, 0, f,
+                                              out, None, None) == N.GRZ_EINVAL
+
+
 def test_product_path_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError, match="GPU"):
