@@ -198,6 +198,44 @@ def test_bf16_mean_refusals():
                                 1, 16, 16, None, None, None, None) == N.GRZ_EINVAL
 
 
+C_CALLER = r"""
+#include <stdio.h>
+#include "grz.h"
+int main(void) {
+  grz_bucket b[1] = {{0, 64}};
+  int64_t off = -1, n = -1;
+  dp_chunk_range(10, 3, 1, &off, &n);
+  printf("%d %d %d %lld %lld %lld\n", grz_version(), dp_ring_owned_chunk(0, 8),
+         dp_ring_chunk_owner(0, 8), (long long)off, (long long)n,
+         (long long)dp_piece_count(b, 1, 2, 0));
+  return 0;
+}
+"""
+
+
+def test_header_is_c_and_a_c_program_links_the_library(tmp_path):
+    # The boundary is a C ABI: grz.h compiles as C11 with warnings as errors,
+    # and a C program linked against libgrz.so calls its host-only helpers
+    # (no device work): ring ownership (rank r owns chunk r + 1 mod N), an
+    # array_split chunk (10 over 3: chunk 1 is [4, 7)), one piece per chunk.
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src, exe = tmp_path / "caller.c", tmp_path / "caller"
+    src.write_text(C_CALLER)
+    libdir = os.path.dirname(N.LIB_PATH)
+    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           f"-I{os.path.dirname(HEADER)}", "-I/opt/rocm/include", str(src),
+           f"-L{libdir}", "-lgrz", f"-Wl,-rpath,{libdir}", "-o", str(exe)]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == [str(grz.lib().grz_version()), "1", "7", "4", "3", "2"]
+
+
 def test_reduce_refuses_the_flags_of_other_entry_points():
     # The reduce (and its _range and _weighted forms) takes neither
     # GRZ_ARGS_DEVICE nor GRZ_COOPERATIVE; refused before any launch.
