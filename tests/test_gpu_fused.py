@@ -1,10 +1,12 @@
 """The one-launch step (zero1_fused_step) against the three-kernel path and the
 oracle.
 
-The fused kernel holds the mean in registers and synchronises its grid
-between the reduce, the norm and AdamW; every value it produces must have the
-bits of dp_reduce_scatter_mean -> dp_grad_sqnorm -> zero1_adamw_gather on the
-same inputs, which the oracle pins independently.
+The fused kernel holds the mean in registers and passes the piece sums
+between its workgroups through self-flagging workspace slots (no grid
+barrier), so that every workgroup can clip once the norm is known; every
+value it produces must have the bits of dp_reduce_scatter_mean ->
+dp_grad_sqnorm -> zero1_adamw_gather on the same inputs, which the oracle
+pins independently.
 """
 
 import math
