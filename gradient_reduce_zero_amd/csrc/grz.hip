@@ -985,19 +985,25 @@ __device__ __forceinline__ bool small_collect(uint64_t* slots, int64_t n, uint64
 }
 
 // At most 128 VGPRs, so that 4 waves per SIMD (4 workgroups per CU) fit: the
-// 64 mean registers per lane plus the fold's and AdamW's working set.
-template <typename TIn, int NR, bool WIRE>
+// mean registers per lane (16 per piece held) plus the fold's and AdamW's
+// working set.  PIECES: the pieces a workgroup can hold (kFusedPieces, or 1
+// for a launch whose pieces fit one per reducing workgroup).  The update
+// takes B accesses at a time and the first B accesses' state is loaded
+// before the norm is known: two with four pieces held, the whole piece
+// (12 loads) with one, which the registers then have room for.
+template <typename TIn, int NR, bool WIRE, int PIECES>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void fused_step_kernel(const FusedArgs<TIn> a) {
   constexpr int G = 4;
   constexpr int K = GRZ_PIECE / (kThreads * G);
-  static_assert(K % 2 == 0, "the update takes two accesses at a time");
+  constexpr int B = PIECES == 1 ? K : 2;
+  static_assert(K % B == 0, "the update's batches");
   __shared__ double lds[kThreads / 64];
   __shared__ double norm_lds;
   const float nf = static_cast<float>(a.divisor);
   const float inv = 1.0f / nf;
   const int lane = threadIdx.x;
-  float mean[kFusedPieces][K][G];
+  float mean[PIECES][K][G];
 
   // The control words, read once per workgroup.  A workspace whose last call
   // gave up, or that served a plan of another piece count (whose slots would
@@ -1055,7 +1061,7 @@ void fused_step_kernel(const FusedArgs<TIn> a) {
 
   // Reduce: the pieces blockIdx.x, blockIdx.x + nred, ... of the launch.
 #pragma unroll
-  for (int p = 0; p < kFusedPieces; ++p) {
+  for (int p = 0; p < PIECES; ++p) {
     const int64_t tile = blockIdx.x + static_cast<int64_t>(p) * a.nred;
     if (tile < a.ntiles) {
       const FSeg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
@@ -1098,17 +1104,17 @@ void fused_step_kernel(const FusedArgs<TIn> a) {
     }
   }
 
-  // The first two accesses of the first piece's state, loaded before the
+  // The first B accesses of the first piece's state, loaded before the
   // norm is known (the state is this workgroup's alone), so that they are in
   // flight while it waits.
-  float pw[2][G], pm[2][G], pv[2][G];
+  float pw[B][G], pm[B][G], pv[B][G];
   bool pre = false;
   if (blockIdx.x < a.ntiles) {
     const FSeg& s = a.seg[find_seg(a.seg, a.nsegs, blockIdx.x)];
     const int64_t e0 = (blockIdx.x - s.tile0) * GRZ_PIECE;
-    if ((s.vec & 2) && static_cast<int64_t>(kThreads + lane) * G + G <= s.len - e0) {
+    if ((s.vec & 2) && static_cast<int64_t>((B - 1) * kThreads + lane) * G + G <= s.len - e0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < B; ++j) {
         const int64_t i = s.st + e0 + static_cast<int64_t>(j * kThreads + lane) * G;
         loadg<GRZ_ADAM_POLICY>(a.master + i, pw[j]);
         loadg<GRZ_ADAM_POLICY>(a.m + i, pm[j]);
@@ -1175,20 +1181,20 @@ void fused_step_kernel(const FusedArgs<TIn> a) {
   const float omb1 = 1.0f - b1;
   const float omb2 = 1.0f - b2;
 #pragma unroll
-  for (int p = 0; p < kFusedPieces; ++p) {
+  for (int p = 0; p < PIECES; ++p) {
     const int64_t tile = blockIdx.x + static_cast<int64_t>(p) * a.nred;
     if (tile < a.ntiles) {
       const FSeg& s = a.seg[find_seg(a.seg, a.nsegs, tile)];
       const int64_t e0 = (tile - s.tile0) * GRZ_PIECE;
       const int64_t left = s.len - e0;
-      // Two accesses at a time: both accesses' loads are in flight before
-      // the first update.
+      // B accesses at a time: all their loads are in flight before the
+      // first update.
 #pragma unroll
-      for (int kb = 0; kb < K; kb += 2) {
-        float w[2][G], m[2][G], v[2][G];
-        bool vec[2];
+      for (int kb = 0; kb < K; kb += B) {
+        float w[B][G], m[B][G], v[B][G];
+        bool vec[B];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < B; ++j) {
           const int64_t rel = static_cast<int64_t>((kb + j) * kThreads + lane) * G;
           vec[j] = (s.vec & 2) && rel + G <= left;
           if (p == 0 && kb == 0 && pre) {
@@ -1206,7 +1212,7 @@ void fused_step_kernel(const FusedArgs<TIn> a) {
           }
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < B; ++j) {
           const int k = kb + j;
           const int64_t rel = static_cast<int64_t>(k * kThreads + lane) * G;
           const int64_t e = e0 + rel;
@@ -2045,30 +2051,32 @@ size_t zero1_fused_workspace(int64_t npieces) {
 namespace {
 
 template <typename TIn, int NR, bool WIRE>
-const void* fused_kernel_ptr() {
-  return reinterpret_cast<const void*>(&fused_step_kernel<TIn, NR, WIRE>);
+const void* fused_kernel_ptr(bool one_piece) {
+  return one_piece ? reinterpret_cast<const void*>(&fused_step_kernel<TIn, NR, WIRE, 1>)
+                   : reinterpret_cast<const void*>(&fused_step_kernel<TIn, NR, WIRE, kFusedPieces>);
 }
 
-// The fused kernel instance for (dtype, N), or null.  (The bf16-wire fold is
-// not instantiated here: its per-hop rounding does not fit the register
-// budget next to the held mean.)
-const void* fused_kernel_for(int dtype, int nranks) {
+// The fused kernel instance for (dtype, N) that holds kFusedPieces pieces
+// per workgroup, or one, or null.  (The bf16-wire fold is not instantiated
+// here: its per-hop rounding does not fit the register budget next to the
+// held mean.)
+const void* fused_kernel_for(int dtype, int nranks, bool one_piece = false) {
   if (dtype == GRZ_BF16) {
     switch (nranks) {
-      case 1: return fused_kernel_ptr<uint16_t, 1, false>();
-      case 2: return fused_kernel_ptr<uint16_t, 2, false>();
-      case 4: return fused_kernel_ptr<uint16_t, 4, false>();
-      case 8: return fused_kernel_ptr<uint16_t, 8, false>();
-      default: return fused_kernel_ptr<uint16_t, 0, false>();
+      case 1: return fused_kernel_ptr<uint16_t, 1, false>(one_piece);
+      case 2: return fused_kernel_ptr<uint16_t, 2, false>(one_piece);
+      case 4: return fused_kernel_ptr<uint16_t, 4, false>(one_piece);
+      case 8: return fused_kernel_ptr<uint16_t, 8, false>(one_piece);
+      default: return fused_kernel_ptr<uint16_t, 0, false>(one_piece);
     }
   }
   if (dtype == GRZ_F32) {
     switch (nranks) {
-      case 1: return fused_kernel_ptr<float, 1, false>();
-      case 2: return fused_kernel_ptr<float, 2, false>();
-      case 4: return fused_kernel_ptr<float, 4, false>();
-      case 8: return fused_kernel_ptr<float, 8, false>();
-      default: return fused_kernel_ptr<float, 0, false>();
+      case 1: return fused_kernel_ptr<float, 1, false>(one_piece);
+      case 2: return fused_kernel_ptr<float, 2, false>(one_piece);
+      case 4: return fused_kernel_ptr<float, 4, false>(one_piece);
+      case 8: return fused_kernel_ptr<float, 8, false>(one_piece);
+      default: return fused_kernel_ptr<float, 0, false>(one_piece);
     }
   }
   return nullptr;
@@ -2089,7 +2097,8 @@ int fused_max_grid(const void* kernel, int* grid) {
 }
 
 template <typename TIn>
-int fused_launch(const void* kernel, const void* const* rank_grads, int nranks,
+int fused_launch(const void* kernel, const void* kernel1, const void* const* rank_grads,
+                 int nranks,
                  const std::vector<PlanSeg>& ps, int flags, float* master, float* m, float* v,
                  const grz_adamw_args* args, const StepArgsNext& next, double max_norm,
                  uint16_t* const* replicas,
@@ -2139,6 +2148,14 @@ int fused_launch(const void* kernel, const void* const* rank_grads, int nranks,
   const int64_t nred = tiles < nred_max ? tiles : nred_max;
   const int grid = static_cast<int>(nred + nfold);
   a.nred = static_cast<int>(nred);
+  // When every reducing workgroup holds at most one piece, the instance that
+  // holds one (the same arithmetic; room to load a whole piece's state while
+  // the norm is pending), provided as many of its workgroups are resident.
+  const void* run = kernel;
+  if (tiles <= nred_max) {
+    int max1 = 0;
+    if (fused_max_grid(kernel1, &max1) == GRZ_OK && grid <= max1) run = kernel1;
+  }
   a.master = master;
   a.m = m;
   a.v = v;
@@ -2180,8 +2197,8 @@ int fused_launch(const void* kernel, const void* const* rank_grads, int nranks,
   // 124M one-rank share, 41 against 24 us at the char GPT).
   const hipError_t e =
       (flags & GRZ_COOPERATIVE)
-          ? hipLaunchCooperativeKernel(kernel, dim3(grid), dim3(kThreads), params, 0, stream)
-          : hipLaunchKernel(kernel, dim3(grid), dim3(kThreads), params, 0, stream);
+          ? hipLaunchCooperativeKernel(run, dim3(grid), dim3(kThreads), params, 0, stream)
+          : hipLaunchKernel(run, dim3(grid), dim3(kThreads), params, 0, stream);
   return e == hipSuccess ? GRZ_OK : GRZ_EHIP;
 }
 
@@ -2216,7 +2233,8 @@ int fused_entry(const void* const* rank_grads, int nranks, int dtype,
   if (st != GRZ_OK) return st;
   if ((flags & GRZ_IN_COMPACT) && chunk < 0) return GRZ_EINVAL;
   const void* kernel = fused_kernel_for(dtype, nranks);
-  if (kernel == nullptr) return GRZ_EINVAL;
+  const void* kernel1 = fused_kernel_for(dtype, nranks, true);
+  if (kernel == nullptr || kernel1 == nullptr) return GRZ_EINVAL;
   if (rank_grads == nullptr || master == nullptr || m == nullptr || v == nullptr ||
       args == nullptr || piece_sqnorm == nullptr || workspace == nullptr)
     return GRZ_EINVAL;
@@ -2238,12 +2256,13 @@ int fused_entry(const void* const* rank_grads, int nranks, int dtype,
   std::vector<PlanSeg> ps = plan_segments(buckets, nbuckets, nranks, chunk);
   if (ps.size() > static_cast<size_t>(kFusedSegs)) return GRZ_ERANGE;
   if (dtype == GRZ_BF16)
-    return fused_launch<uint16_t>(kernel, rank_grads, nranks, ps, flags, master, m, v, args,
-                                  next, max_norm, replicas, nreplicas, piece_sqnorm, npieces,
-                                  workspace, sqnorm_out, clip_scale_out, mean_out, stream);
-  return fused_launch<float>(kernel, rank_grads, nranks, ps, flags, master, m, v, args, next,
-                             max_norm, replicas, nreplicas, piece_sqnorm, npieces, workspace,
-                             sqnorm_out, clip_scale_out, mean_out, stream);
+    return fused_launch<uint16_t>(kernel, kernel1, rank_grads, nranks, ps, flags, master, m, v,
+                                  args, next, max_norm, replicas, nreplicas, piece_sqnorm,
+                                  npieces, workspace, sqnorm_out, clip_scale_out, mean_out,
+                                  stream);
+  return fused_launch<float>(kernel, kernel1, rank_grads, nranks, ps, flags, master, m, v, args,
+                             next, max_norm, replicas, nreplicas, piece_sqnorm, npieces,
+                             workspace, sqnorm_out, clip_scale_out, mean_out, stream);
 }
 
 }  // namespace
